@@ -1,0 +1,222 @@
+"""CPU oracle for the colibri quantized matmul and MoE block -- TEST INFRASTRUCTURE.
+
+The arithmetic lives in ``coli_oracle.c`` (plain C, f64).  This module only
+compiles it with gcc and marshals numpy arrays through ctypes.  It shares no
+code with the GPU library; only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it.
+
+Every function here states the passage it follows in the C source; the
+readings taken where the pages are silent are listed there as well.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "coli_oracle.c")
+LIB = os.path.join(HERE, "libcoli_oracle.so")
+
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+          "-ffp-contract=off", "-fopenmp", "-Wall", "-Wextra"]
+
+
+def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc into a shared library; returns its path."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class OracleQT(C.Structure):
+    """Mirror of the oracle's own ``oracle_qt`` record (one expert stack)."""
+    _fields_ = [("fmt", C.c_int32), ("O", C.c_int32), ("I", C.c_int32),
+                ("gs", C.c_int32), ("ng", C.c_int32), ("pad_", C.c_int32),
+                ("q_stride", C.c_int64), ("s_stride", C.c_int64),
+                ("q", C.c_void_p), ("s", C.c_void_p)]
+
+
+def row_bytes(fmt: int, I: int) -> int:
+    return {1: I, 2: (I + 1) // 2, 4: (I + 1) // 2, 3: (I + 3) // 4}[fmt]
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+@dataclass
+class QMat:
+    """A quantized matrix (or stack of n matrices) held in host memory.
+
+    q: uint8 [n][O][row_bytes] (int8 bytes for fmt 1 are stored as uint8)
+    s: float32 [n][O][ng] for fmt 4, [n][O] for fmt 1-3.
+    """
+    fmt: int
+    O: int
+    I: int
+    gs: int
+    q: np.ndarray
+    s: np.ndarray
+
+    @property
+    def ng(self) -> int:
+        return -(-self.I // self.gs) if self.fmt == 4 else 1
+
+    @property
+    def n(self) -> int:
+        return self.q.shape[0] if self.q.ndim == 3 else 1
+
+    def qt(self) -> OracleQT:
+        q = np.ascontiguousarray(self.q.view(np.uint8))
+        s = np.ascontiguousarray(self.s, dtype=np.float32)
+        self._keep = (q, s)
+        return OracleQT(self.fmt, self.O, self.I, self.gs if self.fmt == 4 else 0,
+                        self.ng, 0, self.O * row_bytes(self.fmt, self.I),
+                        self.O * self.ng, q.ctypes.data, s.ctypes.data)
+
+    def expert(self, e: int) -> "QMat":
+        if self.q.ndim == 2:
+            assert e == 0
+            return self
+        return QMat(self.fmt, self.O, self.I, self.gs, self.q[e], self.s[e])
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, lib_path: str | None = None, nthreads: int = 1):
+        path = lib_path or LIB
+        if lib_path is None and (not os.path.exists(path)
+                                 or os.path.getmtime(path) < os.path.getmtime(SRC)):
+            build()
+        self.lib = C.CDLL(path)
+        self.nthreads = nthreads
+        L = self.lib
+        i64, i32, vp, dbl = C.c_int64, C.c_int, C.c_void_p, C.c_double
+        L.oracle_row_bytes.restype = i64
+        L.oracle_row_bytes.argtypes = [i32, i64]
+        L.oracle_shape_ok.restype = i32
+        L.oracle_shape_ok.argtypes = [i32, i64, i64, i64, i64]
+        L.oracle_decode_codes.argtypes = [i32, i64, i64, vp, vp]
+        L.oracle_dequant_f32.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp]
+        L.oracle_dequant_f64.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp]
+        L.oracle_qmatmul.argtypes = [i32, i64, i64, i64, i64, vp, vp, i64, vp, vp, vp, i32]
+        L.oracle_qmatmul_f64in.argtypes = [i32, i64, i64, i64, i64, vp, vp, i64, vp, vp, vp, i32]
+        L.oracle_silu.restype = dbl
+        L.oracle_silu.argtypes = [dbl]
+        L.oracle_moe_route.restype = i64
+        L.oracle_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+        L.oracle_moe_block.restype = i64
+        L.oracle_moe_block.argtypes = [C.POINTER(OracleQT)] * 3 + [
+            i64, vp, i64, vp, vp, i64] + [C.POINTER(OracleQT)] * 3 + [
+            i64, vp, vp, vp, vp, vp, vp, vp, i32]
+
+    # --- formats -----------------------------------------------------------
+    def row_bytes(self, fmt: int, I: int) -> int:
+        return int(self.lib.oracle_row_bytes(fmt, I))
+
+    def shape_ok(self, fmt, O, I, gs, ng) -> bool:
+        return bool(self.lib.oracle_shape_ok(fmt, O, I, gs, ng))
+
+    def decode_codes(self, W: QMat) -> np.ndarray:
+        q = np.ascontiguousarray(W.q.view(np.uint8))
+        v = np.zeros((W.O, W.I), dtype=np.int32)
+        self.lib.oracle_decode_codes(W.fmt, W.O, W.I, _p(q), _p(v))
+        return v
+
+    def dequant_f32(self, W: QMat) -> np.ndarray:
+        q = np.ascontiguousarray(W.q.view(np.uint8))
+        s = np.ascontiguousarray(W.s, dtype=np.float32)
+        w = np.zeros((W.O, W.I), dtype=np.float32)
+        self.lib.oracle_dequant_f32(W.fmt, W.O, W.I, W.gs, W.ng, _p(q), _p(s), _p(w))
+        return w
+
+    def dequant_f64(self, W: QMat) -> np.ndarray:
+        q = np.ascontiguousarray(W.q.view(np.uint8))
+        s = np.ascontiguousarray(W.s, dtype=np.float32)
+        w = np.zeros((W.O, W.I), dtype=np.float64)
+        self.lib.oracle_dequant_f64(W.fmt, W.O, W.I, W.gs, W.ng, _p(q), _p(s), _p(w))
+        return w
+
+    # --- matmul --------------------------------------------------------------
+    def qmatmul(self, W: QMat, x: np.ndarray):
+        """y[s][o] = sum_i w(o,i) x[s][i] in f64; returns (y, A) with A the
+        magnitude sum_i |w||x| per output."""
+        x = np.ascontiguousarray(np.atleast_2d(x))
+        S = x.shape[0]
+        q = np.ascontiguousarray(W.q.view(np.uint8))
+        s = np.ascontiguousarray(W.s, dtype=np.float32)
+        y = np.zeros((S, W.O), dtype=np.float64)
+        A = np.zeros((S, W.O), dtype=np.float64)
+        if x.dtype == np.float64:
+            fn = self.lib.oracle_qmatmul_f64in
+        else:
+            assert x.dtype == np.float32
+            fn = self.lib.oracle_qmatmul
+        fn(W.fmt, W.O, W.I, W.gs, W.ng, _p(q), _p(s), S, _p(x), _p(y), _p(A),
+           self.nthreads)
+        return y, A
+
+    # --- MoE -----------------------------------------------------------------
+    def silu(self, z: float) -> float:
+        return float(self.lib.oracle_silu(float(z)))
+
+    def moe_route(self, ids: np.ndarray, E: int):
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        S, K = ids.shape
+        counts = np.zeros(E, dtype=np.int32)
+        offsets = np.zeros(E + 1, dtype=np.int32)
+        perm = np.full(S * K, -1, dtype=np.int32)
+        bad = self.lib.oracle_moe_route(_p(ids), S, K, E, _p(counts), _p(offsets), _p(perm))
+        return counts, offsets, perm, int(bad)
+
+    def moe_block(self, gate: QMat, up: QMat, down: QMat, x: np.ndarray,
+                  ids: np.ndarray, w: np.ndarray, shared=None, rows=None,
+                  intermediates: bool = False):
+        """Returns out [S][D or len(rows)] f64 (and a dict of per-pair g, u, h,
+        Ag, Au [P][F] when intermediates=True)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        S, K = ids.shape
+        E = gate.n
+        F = gate.O
+        qg, qu, qd = gate.qt(), up.qt(), down.qt()
+        sh = [None, None, None]
+        if shared is not None:
+            sh = [C.pointer(m.qt()) for m in shared]
+        P = S * K + (S if shared is not None else 0)
+        nout = len(rows) if rows is not None else down.O
+        rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+        out = np.zeros((S, nout), dtype=np.float64)
+        inter = {k: np.zeros((P, F), dtype=np.float64) for k in ("g", "u", "h", "Ag", "Au")} \
+            if intermediates else {}
+        bad = self.lib.oracle_moe_block(
+            C.pointer(qg), C.pointer(qu), C.pointer(qd), E, _p(x), S, _p(ids), _p(w), K,
+            sh[0], sh[1], sh[2], nout if rows is not None else 0, _p(rows_arr), _p(out),
+            *(_p(inter.get(k)) for k in ("g", "u", "h", "Ag", "Au")), self.nthreads)
+        self._keep = (shared,)
+        if intermediates:
+            inter["bad"] = int(bad)
+            return out, inter
+        return out
+
+
+_default: Oracle | None = None
+
+
+def get(nthreads: int = 1) -> Oracle:
+    """The default oracle instance (built on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    _default.nthreads = nthreads
+    return _default

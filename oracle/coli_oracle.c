@@ -1,0 +1,381 @@
+/*
+ * coli_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, double-precision CPU statement of what the colibri quantized
+ * weight matmul and batched MoE expert block compute.  It exists so that the
+ * GPU library can be checked against something that is obviously correct.
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load it; the GPU library never calls it, and the two share no code.
+ *
+ * Sources (pages describing the colibri engine):
+ *   [P4-cuda]   colibri PR #298, commit adding fmt=4 to the CUDA backend:
+ *               grouped int4 keeps the fmt=2 nibble layout and carries one f32
+ *               scale per gs inputs along I, applied per group during the
+ *               accumulation; the scale buffer holds O*ceil(I/gs) floats.
+ *   [P4-test]   colibri PR #298, commit adding the matmul_i4_grouped test:
+ *               the double-precision reference dequantises nibble -> (v-8)
+ *               times scale[i/gs] and accumulates in double; nibbles are
+ *               offset-encoded (0x0 -> -8, 0xF -> +7); the last group may be
+ *               partial; the error is judged against the sum of |terms|.
+ *   [P4-metal]  colibri PR #298, commit adding fmt=4 to the Metal mm_gemv:
+ *               fmt 1-3 apply one per-row scale after the full dot product,
+ *               fmt 4 folds its group scale in per group.
+ *   [P4-addrow] colibri PR #298, commit making qt_addrow/qt_matvec_rows refuse
+ *               unknown formats: fmt=1 raw bytes, fmt=3 row stride (I+3)/4,
+ *               one scale per row for fmt 1/2/3.
+ *   [P3-moe]    colibri-strix commit log, commit "metal: batched moe_block +
+ *               zero-copy slab registry": gate/up -> SiLU -> down per expert,
+ *               per-row ragged routing, weighted scatter-add of the results.
+ *   [P3-shared] colibri-strix commit log, commit "zero-copy attention weights +
+ *               fuse shared expert into GPU block": the shared expert is an
+ *               extra expert with routing weight 1.0 over every row.
+ *
+ * Readings where the pages are silent (each also listed with the design notes):
+ *   - element 2j of a byte pair is the LOW nibble, 2j+1 the high nibble;
+ *   - each row starts on a byte boundary (strides I, ceil(I/2), ceil(I/4));
+ *   - fmt 3 packs four 2-bit codes per byte, lowest bits first, value code-2;
+ *   - fmt 1 bytes are two's-complement int8;
+ *   - fmt 4 scales are row-major [O][ng], ng = ceil(I/gs), the last group
+ *     holds I-(ng-1)*gs inputs;
+ *   - SiLU(z) = z / (1 + exp(-z)); the gate feeds SiLU, the up projection is
+ *     linear; routing weights are used exactly as given;
+ *   - an expert id outside [0,E) contributes nothing and is counted.
+ *
+ * Arithmetic: every weight is s*v with s an f32 and |v| <= 128, so the f64
+ * product is exact; every product with an f32 (or f64-held f32) input is exact
+ * in f64 as well.  Sums run sequentially over the input index in f64.
+ *
+ * Parallelism: the optional OpenMP pragmas only split independent output rows
+ * (or independent routed pairs) across threads; they change no arithmetic.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* Formats                                                             */
+/* ------------------------------------------------------------------ */
+
+/* Bytes per weight row: fmt 1 one byte per input, fmt 2/4 two nibbles per
+ * byte, fmt 3 four 2-bit codes per byte ([P4-addrow] gives (I+3)/4). */
+int64_t oracle_row_bytes(int fmt, int64_t I)
+{
+    switch (fmt) {
+    case 1: return I;
+    case 2: case 4: return (I + 1) / 2;
+    case 3: return (I + 3) / 4;
+    default: return -1;
+    }
+}
+
+/* 1 when (fmt, O, I, gs, ng) is a shape the oracle understands. */
+int oracle_shape_ok(int fmt, int64_t O, int64_t I, int64_t gs, int64_t ng)
+{
+    if (fmt < 1 || fmt > 4 || O < 0 || I < 0)
+        return 0;
+    if (fmt == 4) {
+        if (gs < 1) return 0;
+        if (ng != (I + gs - 1) / gs) return 0;
+    }
+    return 1;
+}
+
+/* Integer code of weight (o, i): the stored value with its offset removed. */
+static int weight_code(int fmt, const uint8_t *q, int64_t rb, int64_t o, int64_t i)
+{
+    const uint8_t *row = q + o * rb;
+    if (fmt == 1)
+        return (int)(int8_t)row[i];
+    if (fmt == 2 || fmt == 4) {
+        uint8_t b = row[i / 2];
+        int nib = (i % 2 == 0) ? (b & 0x0F) : (b >> 4);
+        return nib - 8;
+    }
+    /* fmt 3 */
+    {
+        uint8_t b = row[i / 4];
+        int code = (b >> (2 * (i % 4))) & 0x3;
+        return code - 2;
+    }
+}
+
+/* Scale that multiplies weight (o, i): per row for fmt 1-3, per group of gs
+ * inputs for fmt 4 ([P4-cuda], [P4-test]). */
+static double weight_scale(int fmt, const float *s, int64_t ng, int64_t gs,
+                           int64_t o, int64_t i)
+{
+    if (fmt == 4)
+        return (double)s[o * ng + i / gs];
+    return (double)s[o];
+}
+
+/* Exact weight value s * v. */
+static double weight_value(int fmt, const uint8_t *q, const float *s, int64_t rb,
+                           int64_t ng, int64_t gs, int64_t o, int64_t i)
+{
+    return weight_scale(fmt, s, ng, gs, o, i) * (double)weight_code(fmt, q, rb, o, i);
+}
+
+/* Integer codes of a whole [O][I] matrix. */
+void oracle_decode_codes(int fmt, int64_t O, int64_t I, const uint8_t *q, int32_t *v)
+{
+    int64_t rb = oracle_row_bytes(fmt, I);
+    for (int64_t o = 0; o < O; o++)
+        for (int64_t i = 0; i < I; i++)
+            v[o * I + i] = weight_code(fmt, q, rb, o, i);
+}
+
+/* Dequantised weights rounded once to f32: (float)((double)s * v). */
+void oracle_dequant_f32(int fmt, int64_t O, int64_t I, int64_t gs, int64_t ng,
+                        const uint8_t *q, const float *s, float *w)
+{
+    int64_t rb = oracle_row_bytes(fmt, I);
+    for (int64_t o = 0; o < O; o++)
+        for (int64_t i = 0; i < I; i++)
+            w[o * I + i] = (float)weight_value(fmt, q, s, rb, ng, gs, o, i);
+}
+
+/* Dequantised weights kept exact in f64. */
+void oracle_dequant_f64(int fmt, int64_t O, int64_t I, int64_t gs, int64_t ng,
+                        const uint8_t *q, const float *s, double *w)
+{
+    int64_t rb = oracle_row_bytes(fmt, I);
+    for (int64_t o = 0; o < O; o++)
+        for (int64_t i = 0; i < I; i++)
+            w[o * I + i] = weight_value(fmt, q, s, rb, ng, gs, o, i);
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantized matmul: y[s][o] = sum_i w(o,i) * x[s][i]                  */
+/* ------------------------------------------------------------------ */
+
+/* One output: the plain sequential sum over i in f64, plus the magnitude
+ * A = sum_i |w(o,i)| * |x[i]| that tolerances are measured against
+ * ([P4-test]: cancellation makes |result|-relative checks misfire). */
+static void dot_row(int fmt, const uint8_t *q, const float *s, int64_t rb,
+                    int64_t ng, int64_t gs, int64_t I, int64_t o,
+                    const double *x, double *y, double *A)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t i = 0; i < I; i++) {
+        double w = weight_value(fmt, q, s, rb, ng, gs, o, i);
+        acc += w * x[i];
+        mag += fabs(w) * fabs(x[i]);
+    }
+    *y = acc;
+    *A = mag;
+}
+
+/* y, A: [S][O] in f64 (A may be NULL).  x: [S][I] f64 inputs. */
+void oracle_qmatmul_f64in(int fmt, int64_t O, int64_t I, int64_t gs, int64_t ng,
+                          const uint8_t *q, const float *s, int64_t S,
+                          const double *x, double *y, double *A, int nthreads)
+{
+    int64_t rb = oracle_row_bytes(fmt, I);
+    (void)nthreads;
+    for (int64_t t = 0; t < S; t++) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+        for (int64_t o = 0; o < O; o++) {
+            double yy, aa;
+            dot_row(fmt, q, s, rb, ng, gs, I, o, x + t * I, &yy, &aa);
+            y[t * O + o] = yy;
+            if (A)
+                A[t * O + o] = aa;
+        }
+    }
+}
+
+/* Same with f32 inputs x: [S][I]; every f32 is exact in f64. */
+void oracle_qmatmul(int fmt, int64_t O, int64_t I, int64_t gs, int64_t ng,
+                    const uint8_t *q, const float *s, int64_t S, const float *x,
+                    double *y, double *A, int nthreads)
+{
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(S * I > 0 ? S * I : 1));
+    for (int64_t k = 0; k < S * I; k++)
+        xd[k] = (double)x[k];
+    oracle_qmatmul_f64in(fmt, O, I, gs, ng, q, s, S, xd, y, A, nthreads);
+    free(xd);
+}
+
+/* ------------------------------------------------------------------ */
+/* MoE expert block                                                    */
+/* ------------------------------------------------------------------ */
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)) in f64. */
+double oracle_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* Routing table ([P3-moe] "per-row ragged expert routing"):
+ *   counts[e]  = number of (s,k) with ids[s][k] == e,
+ *   offsets[e] = exclusive prefix sum of counts (offsets[E] = valid pairs),
+ *   perm       = every valid pair index p = s*K + k, grouped by expert in
+ *                ascending e, ascending p inside each expert.
+ * Returns the number of pairs whose id lies outside [0,E) (left out). */
+int64_t oracle_moe_route(const int32_t *ids, int64_t S, int64_t K, int64_t E,
+                         int32_t *counts, int32_t *offsets, int32_t *perm)
+{
+    int64_t bad = 0;
+    for (int64_t e = 0; e < E; e++)
+        counts[e] = 0;
+    for (int64_t p = 0; p < S * K; p++) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= E)
+            bad++;
+        else
+            counts[e]++;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; e++)
+        offsets[e + 1] = offsets[e] + counts[e];
+    /* stable placement: walk pairs in ascending p, append to their expert */
+    {
+        int32_t *fill = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+        for (int64_t e = 0; e < E; e++)
+            fill[e] = offsets[e];
+        for (int64_t p = 0; p < S * K; p++) {
+            int32_t e = ids[p];
+            if (e >= 0 && e < E)
+                perm[fill[e]++] = (int32_t)p;
+        }
+        free(fill);
+    }
+    return bad;
+}
+
+/* One quantized matrix inside a stack of experts. */
+typedef struct oracle_qt {
+    int32_t fmt;
+    int32_t O, I;
+    int32_t gs, ng;
+    int32_t pad_;
+    int64_t q_stride; /* bytes between consecutive experts' codes   */
+    int64_t s_stride; /* floats between consecutive experts' scales */
+    const uint8_t *q;
+    const float *s;
+} oracle_qt;
+
+static const uint8_t *qt_q(const oracle_qt *t, int64_t e) { return t->q + e * t->q_stride; }
+static const float *qt_s(const oracle_qt *t, int64_t e) { return t->s + e * t->s_stride; }
+
+/* One expert MLP on one input row ([P3-moe]):
+ *   g = G x, u = U x, h_j = silu(g_j) * u_j, y = D h.
+ * x is f64 [D_in]; g, u, h, Ag, Au are [F]; y is evaluated only at the
+ * requested output rows (all rows when rows == NULL). */
+static void expert_mlp(const oracle_qt *G, const oracle_qt *U, const oracle_qt *Dn,
+                       int64_t e, const double *x, double *g, double *u, double *h,
+                       double *Ag, double *Au, int64_t nrows, const int32_t *rows,
+                       double *y)
+{
+    int64_t F = G->O, Din = G->I, Dout = Dn->O;
+    int64_t rbg = oracle_row_bytes(G->fmt, Din);
+    int64_t rbu = oracle_row_bytes(U->fmt, Din);
+    int64_t rbd = oracle_row_bytes(Dn->fmt, F);
+    for (int64_t j = 0; j < F; j++) {
+        dot_row(G->fmt, qt_q(G, e), qt_s(G, e), rbg, G->ng, G->gs, Din, j, x, &g[j], &Ag[j]);
+        dot_row(U->fmt, qt_q(U, e), qt_s(U, e), rbu, U->ng, U->gs, Din, j, x, &u[j], &Au[j]);
+        h[j] = oracle_silu(g[j]) * u[j];
+    }
+    int64_t n = rows ? nrows : Dout;
+    for (int64_t r = 0; r < n; r++) {
+        int64_t o = rows ? rows[r] : r;
+        double a;
+        dot_row(Dn->fmt, qt_q(Dn, e), qt_s(Dn, e), rbd, Dn->ng, Dn->gs, F, o, h, &y[r], &a);
+    }
+}
+
+/* The batched expert block:
+ *   out[s] = sum_k w[s][k] * MLP_{ids[s][k]}(x[s])  (+ 1.0 * MLP_shared(x[s]))
+ * gate/up: stacks of E matrices [F][D]; down: E matrices [D][F]; the shared
+ * triple (all three NULL or none) holds one matrix each.
+ * x: f32 [S][D].  ids, w: [S][K].  out: f64 [S][nout] where nout = nrows when
+ * rows != NULL (only those output rows are evaluated) else D.
+ * Optional per-pair intermediates, each [P][F] with P = S*K (+S when a shared
+ * expert is given; routed pair p = s*K+k first, then shared row s at S*K+s):
+ * g, u, h, Ag, Au.  An id outside [0,E) contributes nothing; the count of such
+ * pairs is returned. */
+int64_t oracle_moe_block(const oracle_qt *gate, const oracle_qt *up, const oracle_qt *down,
+                         int64_t E, const float *x, int64_t S, const int32_t *ids,
+                         const float *w, int64_t K, const oracle_qt *sh_gate,
+                         const oracle_qt *sh_up, const oracle_qt *sh_down,
+                         int64_t nrows, const int32_t *rows, double *out,
+                         double *g_out, double *u_out, double *h_out, double *Ag_out,
+                         double *Au_out, int nthreads)
+{
+    int64_t F = gate->O, D = gate->I;
+    int64_t nout = rows ? nrows : down->O;
+    int64_t has_shared = (sh_gate && sh_up && sh_down) ? 1 : 0;
+    int64_t P = S * K + (has_shared ? S : 0);
+    int64_t bad = 0;
+    (void)nthreads;
+
+    double *ybuf = (double *)malloc(sizeof(double) * (size_t)((P > 0 ? P : 1) * (nout > 0 ? nout : 1)));
+    int8_t *valid = (int8_t *)calloc((size_t)(P > 0 ? P : 1), 1);
+
+    for (int64_t p = 0; p < S * K; p++) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= E)
+            bad++;
+        else
+            valid[p] = 1;
+    }
+    for (int64_t p = S * K; p < P; p++)
+        valid[p] = 1;
+
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+    for (int64_t p = 0; p < P; p++) {
+        if (!valid[p])
+            continue;
+        int64_t s = (p < S * K) ? p / K : p - S * K;
+        const oracle_qt *G = gate, *U = up, *Dn = down;
+        int64_t e;
+        if (p < S * K) {
+            e = ids[p];
+        } else {
+            G = sh_gate; U = sh_up; Dn = sh_down;
+            e = 0;
+        }
+        double *xd = (double *)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+        double *g = (double *)malloc(sizeof(double) * (size_t)(F > 0 ? F : 1) * 5);
+        double *u = g + F, *h = u + F, *Ag = h + F, *Au = Ag + F;
+        for (int64_t i = 0; i < D; i++)
+            xd[i] = (double)x[s * D + i];
+        expert_mlp(G, U, Dn, e, xd, g, u, h, Ag, Au, nrows, rows, ybuf + p * nout);
+        if (g_out) memcpy(g_out + p * F, g, sizeof(double) * (size_t)F);
+        if (u_out) memcpy(u_out + p * F, u, sizeof(double) * (size_t)F);
+        if (h_out) memcpy(h_out + p * F, h, sizeof(double) * (size_t)F);
+        if (Ag_out) memcpy(Ag_out + p * F, Ag, sizeof(double) * (size_t)F);
+        if (Au_out) memcpy(Au_out + p * F, Au, sizeof(double) * (size_t)F);
+        free(g);
+        free(xd);
+    }
+
+    /* weighted combine in ascending k, then the shared expert with weight 1 */
+    for (int64_t s = 0; s < S; s++) {
+        for (int64_t r = 0; r < nout; r++) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                int64_t p = s * K + k;
+                if (valid[p])
+                    acc += (double)w[p] * ybuf[p * nout + r];
+            }
+            if (has_shared)
+                acc += ybuf[(S * K + s) * nout + r];
+            out[s * nout + r] = acc;
+        }
+    }
+    free(valid);
+    free(ybuf);
+    return bad;
+}

@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with what the pages or the mathematics fix:
+  - values the pages print (the nibble extremes),
+  - closed forms (group sums with power-of-two scales, ramps),
+  - invariants (one-hot inputs, zero codes, scale doubling, row independence),
+  - special cases that reduce to another format or to a library routine
+    (scipy's logistic function, numpy's f64 matmul on an independently
+    written decoder),
+  - brute force on tiny inputs (routing by sorting).
+The same functions run against deliberately broken copies of the oracle in
+``test_oracle_mutations.py`` to show that they bite.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+from scipy.special import expit
+
+import synthdata as sd
+from oracle import QMat
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# An independent decoder: vectorised bit slicing with numpy (a different
+# construction from the oracle's per-element function).
+# ---------------------------------------------------------------------------
+
+def ref_codes(fmt: int, q: np.ndarray, I: int) -> np.ndarray:
+    q = q.view(np.uint8)
+    O = q.shape[0]
+    if fmt == 1:
+        return q.view(np.int8).astype(np.int64)[:, :I]
+    if fmt in (2, 4):
+        both = np.stack([q & 0x0F, q >> 4], axis=-1).reshape(O, -1)
+        return both[:, :I].astype(np.int64) - 8
+    if fmt == 3:
+        shifts = np.array([0, 2, 4, 6], dtype=np.uint8)
+        crumbs = (q[:, :, None] >> shifts[None, None, :]) & 0x3
+        return crumbs.reshape(O, -1)[:, :I].astype(np.int64) - 2
+    raise ValueError(fmt)
+
+
+def ref_dense(W: QMat) -> np.ndarray:
+    """Exact f64 weights from the independent decoder."""
+    v = ref_codes(W.fmt, W.q, W.I).astype(np.float64)
+    if W.fmt == 4:
+        col_scale = np.repeat(W.s.astype(np.float64), W.gs, axis=1)[:, :W.I]
+        return v * col_scale
+    return v * W.s.astype(np.float64)[:, None]
+
+
+def make(fmt, O, I, gs=64, seed=0, S=1):
+    r = sd.rng(seed)
+    x = sd.gen_x(r, S, I)
+    q, s = sd.gen_matrix(r, fmt, O, I, gs)
+    return QMat(fmt, O, I, gs if fmt == 4 else 0, q, s), x
+
+
+# The shape matrix of the grouped-int4 test commit (PR #298): I a multiple of
+# gs, a partial last group, odd I, gs > I, gs = 16/64/128, S > 1; plus the
+# per-row formats on odd / non-multiple-of-4 widths.
+SHAPES = [
+    (4, 8, 128, 64, 1), (4, 5, 130, 64, 1), (4, 3, 129, 64, 2), (4, 4, 37, 64, 1),
+    (4, 6, 96, 16, 3), (4, 4, 256, 128, 1), (4, 2, 1, 16, 1), (4, 7, 200, 32, 4),
+    (2, 5, 130, 0, 2), (2, 3, 33, 0, 1), (1, 4, 70, 0, 3), (1, 2, 5, 0, 1),
+    (3, 5, 130, 0, 2), (3, 3, 7, 0, 1), (3, 2, 66, 0, 1),
+]
+
+
+def _assert_close_A(y, y_ref, A, rel):
+    err = np.abs(y - y_ref)
+    bound = rel * A + 1e-300
+    assert np.all(err <= bound), f"max err/A = {np.max(err / np.maximum(A, 1e-300)):.3e}"
+
+
+# ---------------------------------------------------------------------------
+# Format pins
+# ---------------------------------------------------------------------------
+
+def pin_golden_nibble_extremes(orc):
+    """Page-printed values: 0x00 -> -8, 0xFF -> +7 (offset encoding)."""
+    with open(os.path.join(GOLDEN, "nibble_extremes.json")) as f:
+        g = json.load(f)
+    for fmt in (2, 4):
+        for case in g["cases"]:
+            q = np.array([[case["byte"]]], dtype=np.uint8)
+            v = orc.decode_codes(QMat(fmt, 1, 2, 2 if fmt == 4 else 0, q,
+                                      np.ones((1, 1) if fmt == 4 else (1,), np.float32)))
+            assert v.tolist() == [case["values"]], (fmt, case, v)
+
+
+def pin_midpoint_and_order(orc):
+    """Nibble 8 is zero; byte 0x9F holds 15 in its low nibble (element 0,
+    value +7) and 9 in its high nibble (element 1, value +1)."""
+    q = np.array([[0x88, 0x9F]], dtype=np.uint8)
+    v = orc.decode_codes(QMat(2, 1, 4, 0, q, np.ones(1, np.float32)))
+    assert v.tolist() == [[0, 0, 7, 1]], v
+    # fmt 3: byte 0b11_10_01_00 holds codes 0,1,2,3 from the lowest bits up
+    q3 = np.array([[0b11100100]], dtype=np.uint8)
+    v3 = orc.decode_codes(QMat(3, 1, 4, 0, q3, np.ones(1, np.float32)))
+    assert v3.tolist() == [[-2, -1, 0, 1]], v3
+    # fmt 1: two's complement bytes
+    q1 = np.array([[0x7F, 0x80, 0xFF, 0x01]], dtype=np.uint8)
+    v1 = orc.decode_codes(QMat(1, 1, 4, 0, q1, np.ones(1, np.float32)))
+    assert v1.tolist() == [[127, -128, -1, 1]], v1
+
+
+def pin_decoder_matches_independent(orc):
+    for fmt, O, I, gs, _ in SHAPES:
+        W, _ = make(fmt, O, I, gs, seed=fmt * 100 + I)
+        assert np.array_equal(orc.decode_codes(W), ref_codes(fmt, W.q, I)), (fmt, O, I)
+
+
+def pin_dequant_single_rounding(orc):
+    """f32 dequant equals one rounding of the exact product s*v."""
+    for fmt, O, I, gs, _ in SHAPES:
+        W, _ = make(fmt, O, I, gs, seed=7 + I)
+        exact = ref_dense(W)
+        assert np.array_equal(orc.dequant_f64(W), exact), (fmt, O, I)
+        assert np.array_equal(orc.dequant_f32(W).view(np.uint32),
+                              exact.astype(np.float32).view(np.uint32)), (fmt, O, I)
+
+
+# ---------------------------------------------------------------------------
+# Matmul pins
+# ---------------------------------------------------------------------------
+
+def pin_bruteforce_dense(orc):
+    """Dequantise with the independent decoder, then numpy's f64 matmul."""
+    for fmt, O, I, gs, S in SHAPES:
+        W, x = make(fmt, O, I, gs, seed=11 + I + fmt, S=S)
+        y, A = orc.qmatmul(W, x)
+        Wd = ref_dense(W)
+        y_ref = x.astype(np.float64) @ Wd.T
+        A_ref = np.abs(x.astype(np.float64)) @ np.abs(Wd).T
+        _assert_close_A(y, y_ref, A_ref, 1e-12)
+        assert np.allclose(A, A_ref, rtol=1e-12, atol=0), (fmt, O, I)
+
+
+def pin_closed_form_group_sums(orc):
+    """x = 1, every nibble 15 (value +7), group scales 2^g:
+    y = 7 * sum_g 2^g * len_g with the last group holding I - (ng-1)*gs."""
+    for I, gs in [(130, 64), (129, 64), (37, 64), (96, 16), (200, 32), (64, 64), (1, 16)]:
+        ng = -(-I // gs)
+        q = np.full((2, (I + 1) // 2), 0xFF, dtype=np.uint8)
+        s = np.tile(np.array([2.0 ** g for g in range(ng)], dtype=np.float32), (2, 1))
+        s[1] *= 0.5
+        W = QMat(4, 2, I, gs, q, s)
+        y, _ = orc.qmatmul(W, np.ones((1, I), np.float32))
+        lens = [gs] * (ng - 1) + [I - (ng - 1) * gs]
+        expect = 7.0 * sum((2.0 ** g) * lens[g] for g in range(ng))
+        assert y[0, 0] == expect and y[0, 1] == expect / 2, (I, gs, y, expect)
+
+
+def pin_closed_form_ramp(orc):
+    """x_i = i, nibbles alternate 0 / 15 (values -8 / +7), scale 1 per row:
+    y = sum_even(-8 i) + sum_odd(7 i)."""
+    for I in (8, 9, 130, 257):
+        q = np.full((1, (I + 1) // 2), 0xF0, dtype=np.uint8)  # low nibble 0, high 15
+        W = QMat(2, 1, I, 0, q, np.ones(1, np.float32))
+        x = np.arange(I, dtype=np.float32)[None, :]
+        y, _ = orc.qmatmul(W, x)
+        expect = sum(-8 * i for i in range(0, I, 2)) + sum(7 * i for i in range(1, I, 2))
+        assert y[0, 0] == expect, (I, y, expect)
+
+
+def pin_one_hot_columns(orc):
+    for fmt, O, I, gs, _ in SHAPES:
+        W, _ = make(fmt, O, I, gs, seed=5 + I)
+        Wd = ref_dense(W)
+        for i in sorted({0, I // 2, I - 1}):
+            x = np.zeros((1, I), np.float32)
+            x[0, i] = 1.0
+            y, _ = orc.qmatmul(W, x)
+            assert np.array_equal(y[0], Wd[:, i]), (fmt, I, i)
+
+
+def pin_zero_and_unit(orc):
+    for I in (1, 7, 64, 130):
+        # all nibbles 8 -> every weight 0
+        W = QMat(4, 3, I, 16, np.full((3, (I + 1) // 2), 0x88, np.uint8),
+                 np.full((3, -(-I // 16)), 0.37, np.float32))
+        y, _ = orc.qmatmul(W, np.ones((1, I), np.float32))
+        assert np.all(y == 0.0)
+        # scale 1, value +1 (nibble 9), x = 1 -> y = I
+        W1 = QMat(4, 2, I, 16, np.full((2, (I + 1) // 2), 0x99, np.uint8),
+                  np.ones((2, -(-I // 16)), np.float32))
+        y1, _ = orc.qmatmul(W1, np.ones((1, I), np.float32))
+        assert np.all(y1 == I), (I, y1)
+
+
+def pin_scale_doubling_and_rows(orc):
+    W, x = make(4, 6, 200, 64, seed=3, S=3)
+    y, _ = orc.qmatmul(W, x)
+    W2 = QMat(4, 6, 200, 64, W.q, W.s * 2)
+    y2, _ = orc.qmatmul(W2, x)
+    assert np.array_equal(y2, 2 * y)
+    for t in range(3):
+        yt, _ = orc.qmatmul(W, x[t:t + 1])
+        assert np.array_equal(yt[0], y[t])
+
+
+def pin_cross_format(orc):
+    r = sd.rng(21)
+    O = 4
+    for I in (64, 130, 37):
+        x = sd.gen_x(r, 2, I)
+        q = sd.gen_codes(r, 2, O, I)
+        s = sd.gen_scales(r, 2, O, I, 0)
+        y2, _ = orc.qmatmul(QMat(2, O, I, 0, q, s), x)
+        # fmt 4 with gs = I, and with gs > I, equals fmt 2 with s[o]
+        for gs in (I, I + 5, 4 * I):
+            y4, _ = orc.qmatmul(QMat(4, O, I, gs, q, s[:, None].copy()), x)
+            assert np.array_equal(y4, y2), (I, gs)
+        # equal group scales along a row equal fmt 2
+        ng = -(-I // 16)
+        y4e, _ = orc.qmatmul(QMat(4, O, I, 16, q, np.repeat(s[:, None], ng, axis=1)), x)
+        _assert_close_A(y4e, y2, np.abs(y2) + 1, 1e-13)
+        # values in -2..1 give the same result in fmt 1 / 2 / 3
+        v = r.integers(-2, 2, size=(O, I))
+        q1 = v.astype(np.int8).view(np.uint8)
+        nib = (v + 8).astype(np.uint8)
+        nib = np.pad(nib, ((0, 0), (0, (-I) % 2)), constant_values=8)
+        q2 = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        cr = (v + 2).astype(np.uint8)
+        cr = np.pad(cr, ((0, 0), (0, (-I) % 4)), constant_values=2)
+        q3 = (cr[:, 0::4] | (cr[:, 1::4] << 2) | (cr[:, 2::4] << 4) | (cr[:, 3::4] << 6)).astype(np.uint8)
+        ya, _ = orc.qmatmul(QMat(1, O, I, 0, q1, s), x)
+        yb, _ = orc.qmatmul(QMat(2, O, I, 0, q2, s), x)
+        yc, _ = orc.qmatmul(QMat(3, O, I, 0, q3, s), x)
+        assert np.array_equal(ya, yb) and np.array_equal(yb, yc), I
+
+
+# ---------------------------------------------------------------------------
+# SiLU and routing pins
+# ---------------------------------------------------------------------------
+
+def pin_silu(orc):
+    assert orc.silu(0.0) == 0.0
+    for z in (0.1, 0.5, 1.0, 3.0, 10.0):
+        assert abs(orc.silu(-z) - (orc.silu(z) - z)) <= 1e-15 * (1 + z)
+    for z in np.linspace(-30, 30, 121):
+        ref = float(z) * float(expit(z))
+        assert abs(orc.silu(float(z)) - ref) <= 1e-15 * (1 + abs(ref)), z
+
+
+def pin_route_bruteforce(orc):
+    r = sd.rng(4)
+    for S, K, E in [(1, 8, 256), (3, 2, 5), (7, 3, 4), (16, 4, 64), (5, 1, 1), (0, 8, 16)]:
+        ids = r.integers(0, E, size=(S, K)).astype(np.int32)
+        counts, offsets, perm, bad = orc.moe_route(ids, E)
+        assert bad == 0
+        pairs = sorted(range(S * K), key=lambda p: (int(ids.flat[p]), p))
+        assert perm.tolist() == pairs
+        assert counts.tolist() == [int(np.sum(ids == e)) for e in range(E)]
+        assert offsets.tolist() == [0] + list(np.cumsum(counts))
+        assert offsets[-1] == S * K
+    ids = np.array([[0, 9, 2], [-1, 2, 2]], dtype=np.int32)
+    counts, offsets, perm, bad = orc.moe_route(ids, 4)
+    assert bad == 2 and counts.tolist() == [1, 0, 3, 0]
+    assert perm[:4].tolist() == [0, 2, 4, 5]
+
+
+# ---------------------------------------------------------------------------
+# MoE block pins
+# ---------------------------------------------------------------------------
+
+def _moe_case(seed, S, K, E, D, F, gs=32, shared=False):
+    r = sd.rng(seed)
+    x = sd.gen_x(r, S, D)
+    gq, gs_ = sd.gen_matrix(r, 4, F, D, gs, n=E)
+    uq, us = sd.gen_matrix(r, 4, F, D, gs, n=E)
+    dq, ds = sd.gen_matrix(r, 4, D, F, gs, n=E)
+    ids, w = sd.gen_routing_uniform(r, S, K, E)
+    G, U, Dn = QMat(4, F, D, gs, gq, gs_), QMat(4, F, D, gs, uq, us), QMat(4, D, F, gs, dq, ds)
+    sh = None
+    if shared:
+        a, b = sd.gen_matrix(r, 4, F, D, gs)
+        c, d = sd.gen_matrix(r, 4, F, D, gs)
+        e_, f_ = sd.gen_matrix(r, 4, D, F, gs)
+        sh = (QMat(4, F, D, gs, a, b), QMat(4, F, D, gs, c, d), QMat(4, D, F, gs, e_, f_))
+    return G, U, Dn, x, ids, w, sh
+
+
+def _mlp_dense(G, U, Dn, xs):
+    g = ref_dense(G) @ xs
+    u = ref_dense(U) @ xs
+    h = g * expit(g) * u
+    return ref_dense(Dn) @ h, np.abs(ref_dense(Dn)) @ np.abs(h)
+
+
+def pin_moe_bruteforce(orc):
+    """Dense numpy expert MLPs on the independent decoder, weighted by w."""
+    for seed, S, K, E, D, F, shared in [(1, 1, 1, 1, 64, 32, False), (2, 3, 2, 5, 70, 40, True),
+                                        (3, 2, 4, 6, 96, 33, False)]:
+        G, U, Dn, x, ids, w, sh = _moe_case(seed, S, K, E, D, F, shared=shared)
+        out = orc.moe_block(G, U, Dn, x, ids, w, shared=sh)
+        for s in range(S):
+            ref = np.zeros(D)
+            mag = np.zeros(D)
+            xs = x[s].astype(np.float64)
+            for k in range(K):
+                e = int(ids[s, k])
+                y, m = _mlp_dense(G.expert(e), U.expert(e), Dn.expert(e), xs)
+                ref += float(w[s, k]) * y
+                mag += abs(float(w[s, k])) * m
+            if sh is not None:
+                y, m = _mlp_dense(*sh, xs)
+                ref += y
+                mag += m
+            _assert_close_A(out[s], ref, mag, 1e-12)
+
+
+def pin_moe_invariants(orc):
+    G, U, Dn, x, ids, w, sh = _moe_case(9, 3, 3, 7, 64, 48, shared=True)
+    out = orc.moe_block(G, U, Dn, x, ids, w)
+    # zero weights give zero
+    assert np.all(orc.moe_block(G, U, Dn, x, ids, np.zeros_like(w)) == 0.0)
+    # doubling w doubles the output exactly
+    assert np.array_equal(orc.moe_block(G, U, Dn, x, ids, 2 * w), 2 * out)
+    # relabelling the experts (permuting the stack and the ids) changes nothing
+    perm = np.array([3, 0, 6, 1, 5, 2, 4])
+    inv = np.argsort(perm)
+    Gp = QMat(4, G.O, G.I, G.gs, G.q[perm], G.s[perm])
+    Up = QMat(4, U.O, U.I, U.gs, U.q[perm], U.s[perm])
+    Dp = QMat(4, Dn.O, Dn.I, Dn.gs, Dn.q[perm], Dn.s[perm])
+    assert np.array_equal(orc.moe_block(Gp, Up, Dp, x, inv[ids].astype(np.int32), w), out)
+    # each row of a batch equals the same row run alone
+    for s in range(3):
+        assert np.array_equal(orc.moe_block(G, U, Dn, x[s:s + 1], ids[s:s + 1], w[s:s + 1])[0], out[s])
+    # the shared expert equals an extra routed expert with weight 1 on every row
+    with_sh = orc.moe_block(G, U, Dn, x, ids, w, shared=sh)
+    Ge = QMat(4, G.O, G.I, G.gs, np.concatenate([G.q, sh[0].q[None]]), np.concatenate([G.s, sh[0].s[None]]))
+    Ue = QMat(4, U.O, U.I, U.gs, np.concatenate([U.q, sh[1].q[None]]), np.concatenate([U.s, sh[1].s[None]]))
+    De = QMat(4, Dn.O, Dn.I, Dn.gs, np.concatenate([Dn.q, sh[2].q[None]]), np.concatenate([Dn.s, sh[2].s[None]]))
+    ids_e = np.concatenate([ids, np.full((3, 1), 7, np.int32)], axis=1)
+    w_e = np.concatenate([w, np.ones((3, 1), np.float32)], axis=1)
+    assert np.array_equal(orc.moe_block(Ge, Ue, De, x, ids_e, w_e), with_sh)
+    # sampled output rows equal the full evaluation at those rows
+    rows = np.array([0, 5, 63, 17], dtype=np.int32)
+    assert np.array_equal(orc.moe_block(G, U, Dn, x, ids, w, shared=sh, rows=rows), with_sh[:, rows])
+
+
+def pin_moe_invalid_ids(orc):
+    G, U, Dn, x, ids, w, _ = _moe_case(12, 2, 3, 4, 32, 16)
+    bad = ids.copy()
+    bad[0, 1] = 4
+    bad[1, 2] = -3
+    out, inter = orc.moe_block(G, U, Dn, x, bad, w, intermediates=True)
+    assert inter["bad"] == 2
+    w0 = w.copy()
+    w0[0, 1] = 0
+    w0[1, 2] = 0
+    ids0 = ids.copy()
+    ids0[0, 1] = 0
+    ids0[1, 2] = 0
+    ref = orc.moe_block(G, U, Dn, x, ids0, w0)
+    assert np.allclose(out, ref, rtol=0, atol=1e-12 * (1 + np.abs(ref).max()))
+
+
+def pin_moe_intermediates(orc):
+    G, U, Dn, x, ids, w, sh = _moe_case(13, 2, 2, 3, 64, 40, shared=True)
+    _, inter = orc.moe_block(G, U, Dn, x, ids, w, shared=sh, intermediates=True)
+    for p in range(2 * 2 + 2):
+        s = p // 2 if p < 4 else p - 4
+        if p < 4:
+            e = int(ids.flat[p])
+            Gm, Um = G.expert(e), U.expert(e)
+        else:
+            Gm, Um = sh[0], sh[1]
+        g_ref = ref_dense(Gm) @ x[s].astype(np.float64)
+        u_ref = ref_dense(Um) @ x[s].astype(np.float64)
+        assert np.allclose(inter["g"][p], g_ref, rtol=0, atol=1e-12 * inter["Ag"][p].max())
+        assert np.allclose(inter["u"][p], u_ref, rtol=0, atol=1e-12 * inter["Au"][p].max())
+        h_ref = g_ref * expit(g_ref) * u_ref
+        tol = 1e-12 * (1.1 * np.abs(u_ref) * inter["Ag"][p]
+                       + np.abs(g_ref * expit(g_ref)) * inter["Au"][p]) + 1e-15 * np.abs(h_ref)
+        assert np.all(np.abs(inter["h"][p] - h_ref) <= tol)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
