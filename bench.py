@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the colibri quantized-matmul hot path on one MI355X.
+
+A step is one decode MoE block (S=1) on fresh routing: 8 of 256 experts, each
+gate/up 2048x6144 and down 6144x2048 in grouped int4 (fmt 4, gs 64, f32 scales
+U[0.001,0.02]), hidden N(0,1) of 6144, softmax routing weights -- route,
+dual gate/up + SiLU, down + weighted combine, all inside coli_moe_block.  The
+routing changes every step (64 precomputed uniform draws), so the 170 MB the
+block touches does not sit in the 256 MB last-level cache.
+
+value = algorithmic HBM bytes per block / block time (GB/s).  Per-kernel
+durations come from HIP events the library records on the launch stream
+around each kernel inside the timed region.  Side measurements ("extra")
+cover the single fmt-4 GEMV and the 6144x6144 format sweep.
+
+Prints ONE JSON line.  N > 1 GPUs is not supported (one-GPU build).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fmt4 GEMV+MoE-block HBM GB/s (S=1) and prefill TFLOP/s (S=544), %roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+E, D, F, K, GS = 256, 6144, 2048, 8, 64
+
+
+def qbytes(fmt, O, I, gs):
+    rb = {1: I, 2: (I + 1) // 2, 4: (I + 1) // 2, 3: (I + 3) // 4}[fmt]
+    ng = -(-I // gs) if fmt == 4 else 1
+    return O * rb + O * ng * 4
+
+
+def src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = ["bit_gemv_coli_amd/csrc/gemv.hip", "bit_gemv_coli_amd/csrc/common.h"]
+
+
+def traffic_from_profiles(kernel_tag):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_decode_moe_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != src_hash(KERNEL_SOURCES):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_gemv_coli_amd as coli
+    import synthdata as sd
+
+    dev = "cuda"
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---- inputs ----------------------------------------------------------
+    log("drawing the 256-expert fmt-4 pool on the device")
+    gq, gsc = sd.pool_on_device(100, 4, E, F, D, GS)
+    uq, usc = sd.pool_on_device(101, 4, E, F, D, GS)
+    dq, dsc = sd.pool_on_device(102, 4, E, D, F, GS)
+    tg = coli.QTensor(4, gq, gsc, F, D, GS)
+    tu = coli.QTensor(4, uq, usc, F, D, GS)
+    td = coli.QTensor(4, dq, dsc, D, F, GS)
+    r = sd.rng(0)
+    x = sd.gen_x(r, 1, D)
+    NR = 64
+    routes = [sd.gen_routing_uniform(r, 1, K, E) for _ in range(NR)]
+    ids_d = torch.from_numpy(np.stack([a for a, _ in routes])).to(dev)      # [NR][1][K]
+    w_d = torch.from_numpy(np.stack([b for _, b in routes])).to(dev)
+    x_d = torch.from_numpy(x).to(dev)
+    out = torch.empty((1, D), device=dev)
+    wsb = coli.coli_moe_workspace_bytes(E, 1, K, F, D, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    expert_bytes = qbytes(4, F, D, GS) * 2 + qbytes(4, D, F, GS)
+    block_bytes = K * expert_bytes + x.nbytes + out.numel() * 4 + K * 8
+    gateup_bytes = K * 2 * qbytes(4, F, D, GS) + x.nbytes + K * F * 4
+
+    def step(i):
+        rc = coli.coli_moe_block(tg, tu, td, x_d, 1, ids_d[i % NR], w_d[i % NR], K, None, None,
+                                 None, out, ws, wsb, stream)
+        if rc != coli.COLI_OK:
+            coli.check(rc, "coli_moe_block")
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    log(f"timed {args.steps} steps")
+    coli.coli_prof_reset()
+    coli.coli_prof_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    coli.coli_prof_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = block_bytes / (ms * 1e-3) / 1e9
+    kern = {}
+    for tag in coli.coli_prof_tags():
+        n, tot = coli.coli_prof_read(tag)
+        if n > 0:
+            kern[tag] = {"launches": n, "avg_us": tot / n * 1e3}
+    log(f"block {ms * 1e3:.2f} us  {value:.1f} GB/s  kernels {kern}")
+
+    dom = "moe_gateup_decode"
+    dom_us = kern.get(dom, {}).get("avg_us")
+    achieved = gateup_bytes / (dom_us * 1e-6) / 1e9 if dom_us else None
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                "traffic": traffic_from_profiles(dom),
+                "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": dom_us}
+
+    # ---- side measurements --------------------------------------------------
+    extra = {"block_us": ms * 1e3, "kernels": kern, "wall_s_timed": wall}
+    if not args.no_extra:
+        extra.update(side_measurements(coli, sd, np, torch, log))
+
+    # ---- CPU oracle baseline -------------------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(coli, sd, np, torch, gq, gsc, uq, usc, dq, dsc, x, routes,
+                           block_bytes, args.cpu_seconds, log)
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode MoE block S=1: 8 of 256 experts (uniform, fresh routing "
+                               "each step), gate/up 2048x6144 + down 6144x2048, fmt4 gs64",
+                   "E": E, "D": D, "F": F, "K": K, "gs": GS, "S": 1,
+                   "bytes_per_step": block_bytes},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def side_measurements(coli, sd, np, torch, log):
+    """Single fmt-4 GEMV (1024x2048, latency) and the 6144x6144 format sweep
+    (ring of distinct copies >= 1 GiB so each launch streams from HBM)."""
+    out = {}
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a.record(st)
+        for i in range(n):
+            fn(i)
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3  # us
+
+    # config 1: one matrix, back-to-back launches (cache-resident; latency)
+    q, s = sd.pool_on_device(7, 4, 1, 1024, 2048, 64)
+    T = coli.QTensor(4, q, s, 1024, 2048, 64)
+    x = torch.randn((1, 2048), device=dev)
+    y = torch.empty((1, 1024), device=dev)
+    us = timed(lambda i: coli.coli_qmatmul(T, x, y, 1, st), 200)
+    out["gemv_1024x2048_g64_us"] = us
+    log(f"gemv 1024x2048 g64: {us:.2f} us/call")
+
+    sweep = {}
+    for fmt, gs in ((4, 64), (4, 128), (2, 0), (1, 0), (3, 0)):
+        for S in (1, 4):
+            mb = qbytes(fmt, 6144, 6144, gs)
+            ncopy = max(2, -(-(1 << 30) // mb))
+            q, s = sd.pool_on_device(11 + fmt, fmt, ncopy, 6144, 6144, gs)
+            Ts = [coli.QTensor(fmt, q[c], s[c], 6144, 6144, gs, n=1) for c in range(ncopy)]
+            x = torch.randn((S, 6144), device=dev)
+            y = torch.empty((S, 6144), device=dev)
+            us = timed(lambda i: coli.coli_qmatmul(Ts[i % ncopy], x, y, S, st), 4 * ncopy)
+            gbs = (mb + S * 6144 * 8) / (us * 1e-6) / 1e9
+            key = f"fmt{fmt}" + (f"_g{gs}" if fmt == 4 else "") + f"_S{S}"
+            sweep[key] = {"us": us, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+            log(f"sweep {key}: {us:.2f} us  {gbs:.0f} GB/s")
+            del Ts, q, s
+    out["gemv_6144x6144_ring"] = sweep
+    return out
+
+
+def cpu_baseline(coli, sd, np, torch, gq, gsc, uq, usc, dq, dsc, x, routes, block_bytes,
+                 seconds, log):
+    """The oracle (plain f64 C, OpenMP over routed pairs) on decode blocks of
+    the same workload, run until `seconds` of CPU time have been spent."""
+    import oracle
+    from oracle import QMat
+    nthreads = len(os.sched_getaffinity(0))
+    orc = oracle.get(nthreads=nthreads)
+    done, spent = 0, 0.0
+    for ids, w in routes:
+        sel = torch.from_numpy(ids[0].astype(np.int64)).cuda()
+        G = QMat(4, F, D, GS, gq[sel].cpu().numpy(), gsc[sel].cpu().numpy())
+        U = QMat(4, F, D, GS, uq[sel].cpu().numpy(), usc[sel].cpu().numpy())
+        Dn = QMat(4, D, F, GS, dq[sel].cpu().numpy(), dsc[sel].cpu().numpy())
+        local = np.arange(K, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        orc.moe_block(G, U, Dn, x, local, w)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= seconds:
+            break
+    gbs = done * block_bytes / spent / 1e9
+    log(f"cpu oracle: {done} blocks in {spent:.1f} s -> {gbs:.3f} GB/s ({min(nthreads, K)} threads)")
+    return {"value": gbs, "unit": "GB/s", "cores": min(nthreads, K), "kind": "oracle",
+            "sample": f"{done} decode MoE blocks (S=1, 8 routed experts, full shapes), "
+                      f"{spent:.1f} s of oracle time; OpenMP over the 8 routed pairs",
+            "us_per_block": spent / done * 1e6}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+"""Python binding of libcoli -- the MI355X (gfx950) quantized-weight matmul
+and MoE-block library.
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name in ``libcoli.so`` (declared in ``include/coli.h``).  Device
+memory and streams come from PyTorch: pass tensors (their ``data_ptr()`` is
+used) or raw integer device pointers.  There is no CPU fallback: if the
+library is missing, importing a compute function raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcoli.so")
+
+COLI_OK, COLI_DECLINED, COLI_HIP_ERROR = 1, 0, -1
+
+
+class coli_qtensor(C.Structure):
+    """Mirror of ``coli_qtensor`` in include/coli.h."""
+    _fields_ = [("fmt", C.c_int32), ("n", C.c_int32), ("O", C.c_int32), ("I", C.c_int32),
+                ("gs", C.c_int32), ("ng", C.c_int32), ("row_bytes", C.c_int64),
+                ("q_stride", C.c_int64), ("s_stride", C.c_int64), ("q", C.c_void_p),
+                ("s", C.c_void_p), ("magic", C.c_uint32), ("flags", C.c_uint32)]
+
+
+_lib = None
+
+
+class ColiError(RuntimeError):
+    pass
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ColiError(f"libcoli.so is not built ({LIB_PATH}); run "
+                        "`python -m bit_gemv_coli_amd.build` (hipcc, gfx950)")
+    try:  # bind to the HIP runtime torch already loaded (one runtime per process)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    QP = C.POINTER(coli_qtensor)
+    sig = {
+        "coli_tensor_upload": (i32, [QP, i32, i32, i32, i32, i32, i32, vp, vp]),
+        "coli_qmatmul": (i32, [QP, vp, vp, i32, vp]),
+        "coli_gemv_max_rows": (i32, []),
+        "coli_set_gemv_max_rows": (i32, [i32]),
+        "coli_dequantize": (i32, [QP, vp, vp]),
+        "coli_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "coli_moe_block": (i32, [QP, QP, QP, vp, i32, vp, vp, i32, QP, QP, QP, vp, vp, sz, vp]),
+        "coli_moe_hidden": (i32, [QP, QP, vp, i32, vp, i32, QP, QP, vp, vp, sz, vp]),
+        "coli_moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "coli_last_reason": (C.c_char_p, []),
+        "coli_last_error": (C.c_char_p, []),
+        "coli_stats": (None, [vp, vp, vp]),
+        "coli_set_fail_after": (None, [i64]),
+        "coli_prof_enable": (None, [i32]),
+        "coli_prof_reset": (None, []),
+        "coli_prof_read": (i64, [C.c_char_p, vp]),
+        "coli_prof_tag": (C.c_char_p, [i32]),
+        "coli_version": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def exported_symbols():
+    """Names the binding expects libcoli to export."""
+    return ["coli_tensor_upload", "coli_qmatmul", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
+            "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
+            "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
+            "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
+            "coli_prof_tag", "coli_version"]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _qp(t):
+    if t is None:
+        return None
+    return C.byref(t.desc if isinstance(t, QTensor) else t)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def coli_tensor_upload(desc: coli_qtensor, fmt, n, O, I, gs, ng, q, s) -> int:
+    return _load().coli_tensor_upload(C.byref(desc), fmt, n, O, I, gs, ng, _ptr(q), _ptr(s))
+
+
+def coli_qmatmul(W, x, y, S, stream=None) -> int:
+    return _load().coli_qmatmul(_qp(W), _ptr(x), _ptr(y), S, _stream(stream))
+
+
+def coli_gemv_max_rows() -> int:
+    return _load().coli_gemv_max_rows()
+
+
+def coli_set_gemv_max_rows(s: int) -> int:
+    return _load().coli_set_gemv_max_rows(s)
+
+
+def coli_dequantize(W, w_out, stream=None) -> int:
+    return _load().coli_dequantize(_qp(W), _ptr(w_out), _stream(stream))
+
+
+def coli_moe_route(ids, S, K, E, counts, offsets, perm, n_bad, stream=None) -> int:
+    return _load().coli_moe_route(_ptr(ids), S, K, E, _ptr(counts), _ptr(offsets), _ptr(perm),
+                                  _ptr(n_bad), _stream(stream))
+
+
+def coli_moe_block(gate, up, down, x, S, ids, w, K, sh_gate, sh_up, sh_down, out, workspace,
+                   ws_bytes, stream=None) -> int:
+    return _load().coli_moe_block(_qp(gate), _qp(up), _qp(down), _ptr(x), S, _ptr(ids), _ptr(w),
+                                  K, _qp(sh_gate), _qp(sh_up), _qp(sh_down), _ptr(out),
+                                  _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def coli_moe_hidden(gate, up, x, S, ids, K, sh_gate, sh_up, h_out, workspace, ws_bytes,
+                    stream=None) -> int:
+    return _load().coli_moe_hidden(_qp(gate), _qp(up), _ptr(x), S, _ptr(ids), K, _qp(sh_gate),
+                                   _qp(sh_up), _ptr(h_out), _ptr(workspace), ws_bytes,
+                                   _stream(stream))
+
+
+def coli_moe_workspace_bytes(E, S, K, F, Dm, has_shared) -> int:
+    return _load().coli_moe_workspace_bytes(E, S, K, F, Dm, int(bool(has_shared)))
+
+
+def coli_last_reason() -> str:
+    return _load().coli_last_reason().decode()
+
+
+def coli_last_error() -> str:
+    return _load().coli_last_error().decode()
+
+
+def coli_stats():
+    a, b, c = C.c_uint64(), C.c_uint64(), C.c_uint64()
+    _load().coli_stats(C.addressof(a), C.addressof(b), C.addressof(c))
+    return a.value, b.value, c.value
+
+
+def coli_set_fail_after(n: int) -> None:
+    _load().coli_set_fail_after(n)
+
+
+def coli_prof_enable(on: bool) -> None:
+    _load().coli_prof_enable(int(bool(on)))
+
+
+def coli_prof_reset() -> None:
+    _load().coli_prof_reset()
+
+
+def coli_prof_read(tag: str):
+    ms = C.c_double()
+    n = _load().coli_prof_read(tag.encode(), C.addressof(ms))
+    return int(n), ms.value
+
+
+def coli_prof_tags():
+    out, i = [], 0
+    while True:
+        t = _load().coli_prof_tag(i)
+        if t is None:
+            return out
+        out.append(t.decode())
+        i += 1
+
+
+def coli_version() -> str:
+    return _load().coli_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# Small conveniences (still marshalling only)
+# ---------------------------------------------------------------------------
+
+class QTensor:
+    """A coli_qtensor record plus the device tensors it refers to (kept alive)."""
+
+    def __init__(self, fmt, q, s, O, I, gs=0, n=None):
+        self.q, self.s = q, s
+        n = n if n is not None else (q.shape[0] if q.dim() == 3 else 1)
+        ng = -(-I // gs) if fmt == 4 else 1
+        self.desc = coli_qtensor()
+        rc = coli_tensor_upload(self.desc, fmt, n, O, I, gs if fmt == 4 else 0, ng, q, s)
+        if rc != COLI_OK:
+            raise ColiError(f"coli_tensor_upload declined: {coli_last_reason()}")
+
+    @property
+    def fmt(self):
+        return self.desc.fmt
+
+
+def check(rc: int, what: str = "call") -> None:
+    """Raise unless rc == COLI_OK, naming the library's reason."""
+    if rc == COLI_OK:
+        return
+    if rc == COLI_DECLINED:
+        raise ColiError(f"{what} declined: {coli_last_reason()}")
+    raise ColiError(f"{what} failed: {coli_last_error()}")

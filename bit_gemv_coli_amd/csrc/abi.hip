@@ -1,0 +1,444 @@
+// abi.hip -- the extern "C" entry points of libcoli: validation, dispatch,
+// diagnostics.  Conventions (colibri PR #298, commit making the CUDA ABI return
+// 0 for fmt=4: "a fallback, never a wrong answer"; issue #585 thread: silent
+// fallbacks mislead, so every refusal names its reason; colibri PR #298, HIP
+// single-source merge: a fault-injection control proves GPU calls executed):
+//   * every entry validates everything it can see on the host before enqueuing
+//     any work; a refusal returns COLI_DECLINED, writes nothing, and records
+//     the reason (coli_last_reason, and on stderr when COLI_NOTICE=1);
+//   * COLI_FAIL_AFTER=n makes every compute call after the first n decline.
+#include <atomic>
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace coli {
+
+static thread_local char g_reason[512];
+static thread_local char g_error[512];
+static std::atomic<uint64_t> g_calls{0}, g_declined{0}, g_launches{0};
+static std::atomic<int64_t> g_fail_after{-2};  // -2: not read from env yet
+static std::atomic<int> g_gemv_max{0};
+static int g_notice = -1;
+
+static void notice(const char *what, const char *msg) {
+    if (g_notice < 0) {
+        const char *e = getenv("COLI_NOTICE");
+        g_notice = (e && atoi(e) > 0) ? 1 : 0;
+    }
+    if (g_notice)
+        fprintf(stderr, "[coli] %s: %s\n", what, msg);
+}
+
+int decline(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_reason, sizeof g_reason, fmt, ap);
+    va_end(ap);
+    g_declined.fetch_add(1);
+    notice("declined", g_reason);
+    return COLI_DECLINED;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+    snprintf(g_error, sizeof g_error, "%s: %s", where, hipGetErrorString(e));
+    notice("hip error", g_error);
+    return COLI_HIP_ERROR;
+}
+
+int after_launch(const char *tag) {
+    g_launches.fetch_add(1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, tag);
+    return COLI_OK;
+}
+
+// --- profiling -------------------------------------------------------------
+
+struct ProfRec {
+    std::string tag;
+    hipEvent_t a, b;
+};
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof;       // recorded launches
+static std::vector<hipEvent_t> g_evpool;  // free events
+static std::vector<std::string> g_tags;   // distinct tags seen
+
+static hipEvent_t take_event() {
+    if (!g_evpool.empty()) {
+        hipEvent_t e = g_evpool.back();
+        g_evpool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+ProfScope::ProfScope(const char *tag, hipStream_t s) : slot(-1), stream(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on)
+        return;
+    ProfRec r;
+    r.tag = tag;
+    r.a = take_event();
+    r.b = take_event();
+    if (!r.a || !r.b)
+        return;
+    bool known = false;
+    for (auto &t : g_tags) known |= (t == r.tag);
+    if (!known) g_tags.push_back(r.tag);
+    (void)hipEventRecord(r.a, s);
+    slot = (int)g_prof.size();
+    g_prof.push_back(r);
+}
+
+ProfScope::~ProfScope() {
+    if (slot < 0)
+        return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (slot < (int)g_prof.size())
+        (void)hipEventRecord(g_prof[slot].b, stream);
+}
+
+static bool gate_call() {
+    g_calls.fetch_add(1);
+    int64_t f = g_fail_after.load();
+    if (f == -2) {
+        const char *e = getenv("COLI_FAIL_AFTER");
+        int64_t v = e ? atoll(e) : -1;
+        int64_t expect = -2;
+        g_fail_after.compare_exchange_strong(expect, v);
+        f = g_fail_after.load();
+    }
+    if (f < 0)
+        return true;
+    if (f == 0) {
+        decline("fault injection (COLI_FAIL_AFTER) tripped");
+        return false;
+    }
+    g_fail_after.fetch_sub(1);
+    return true;
+}
+
+// --- validation ------------------------------------------------------------
+
+static int check_qt(const coli_qtensor *t, const char *name) {
+    if (!t)
+        return decline("%s: NULL tensor", name);
+    if (t->magic != QT_MAGIC)
+        return decline("%s: not filled by coli_tensor_upload", name);
+    return COLI_OK;
+}
+
+static bool dev_aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace coli
+
+using namespace coli;
+
+extern "C" {
+
+const char *coli_version(void) { return "libcoli 0.1 (gfx950)"; }
+
+const char *coli_last_reason(void) { return g_reason; }
+const char *coli_last_error(void) { return g_error; }
+
+void coli_stats(uint64_t *calls, uint64_t *declined, uint64_t *launches) {
+    if (calls) *calls = g_calls.load();
+    if (declined) *declined = g_declined.load();
+    if (launches) *launches = g_launches.load();
+}
+
+void coli_set_fail_after(int64_t n) { g_fail_after.store(n < 0 ? -1 : n); }
+
+int coli_gemv_max_rows(void) {
+    int v = g_gemv_max.load();
+    if (v == 0) {
+        const char *e = getenv("COLI_GEMV_MAX_ROWS");
+        v = e ? atoi(e) : 4;
+        if (v < 1 || v > 4) v = 4;
+        int z = 0;
+        g_gemv_max.compare_exchange_strong(z, v);
+        v = g_gemv_max.load();
+    }
+    return v;
+}
+
+int coli_set_gemv_max_rows(int s) {
+    if (s < 1 || s > 4)
+        return 0;
+    const int old = coli_gemv_max_rows();
+    g_gemv_max.store(s);
+    return old;
+}
+
+void coli_prof_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = on != 0;
+}
+
+void coli_prof_reset(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto &r : g_prof) {
+        g_evpool.push_back(r.a);
+        g_evpool.push_back(r.b);
+    }
+    g_prof.clear();
+}
+
+int64_t coli_prof_read(const char *tag, double *total_ms) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!tag)
+        return -1;
+    double sum = 0.0;
+    int64_t n = 0;
+    for (auto &r : g_prof) {
+        if (r.tag != tag)
+            continue;
+        if (hipEventQuery(r.b) != hipSuccess)
+            continue;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            continue;
+        sum += ms;
+        ++n;
+    }
+    if (total_ms) *total_ms = sum;
+    return n;
+}
+
+const char *coli_prof_tag(int i) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (i < 0 || i >= (int)g_tags.size())
+        return nullptr;
+    return g_tags[i].c_str();
+}
+
+int coli_tensor_upload(coli_qtensor *t, int fmt, int n, int O, int I, int gs, int ng,
+                       const void *q_dev, const float *s_dev) {
+    if (!t)
+        return decline("tensor_upload: NULL record");
+    if (fmt < 1 || fmt > 4)
+        return decline("tensor_upload: unknown fmt %d (supported: 1 int8/row, 2 int4/row, "
+                       "3 int2/row, 4 grouped int4)", fmt);
+    if (n < 1 || O < 1 || I < 1)
+        return decline("tensor_upload: bad shape n=%d O=%d I=%d", n, O, I);
+    if ((int64_t)n * O > (int64_t)INT32_MAX / 2)
+        return decline("tensor_upload: n*O=%lld too large", (long long)n * O);
+    if (!q_dev || !s_dev)
+        return decline("tensor_upload: NULL codes or scales");
+    if (!dev_aligned(s_dev, 4))
+        return decline("tensor_upload: scales not 4-byte aligned");
+    if (fmt == 4) {
+        if (gs < 1)
+            return decline("tensor_upload: fmt 4 needs gs >= 1 (got %d)", gs);
+        const int want = (int)(((int64_t)I + gs - 1) / gs);
+        if (ng != want)
+            return decline("tensor_upload: ng=%d but ceil(I/gs)=%d (I=%d gs=%d)", ng, want, I, gs);
+    } else {
+        if (gs != 0)
+            return decline("tensor_upload: fmt %d has per-row scales; gs must be 0 (got %d)",
+                           fmt, gs);
+        if (ng != 1)
+            return decline("tensor_upload: fmt %d has per-row scales; ng must be 1 (got %d)",
+                           fmt, ng);
+    }
+    coli_qtensor r;
+    memset(&r, 0, sizeof r);
+    r.fmt = fmt;
+    r.n = n;
+    r.O = O;
+    r.I = I;
+    r.gs = gs;
+    r.ng = ng;
+    r.row_bytes = fmt == 1 ? I : (fmt == 3 ? ((int64_t)I + 3) / 4 : ((int64_t)I + 1) / 2);
+    r.q_stride = (int64_t)O * r.row_bytes;
+    r.s_stride = (int64_t)O * ng;
+    r.q = q_dev;
+    r.s = s_dev;
+    r.magic = QT_MAGIC;
+    const int pb = packet_bytes(fmt), pc = packet_cols(fmt);
+    if (I % pc == 0 && r.row_bytes % pb == 0 && dev_aligned(q_dev, pb))
+        r.flags |= QF_FAST;
+    if (fmt == 4) {
+        if (gs % 32 == 0)
+            r.flags |= QF_GROUP32;
+        else if (gs % 16 == 0)
+            r.flags |= QF_GROUP16;
+    }
+    *t = r;
+    return COLI_OK;
+}
+
+int coli_dequantize(const coli_qtensor *W, float *w_out, void *stream) {
+    if (check_qt(W, "dequantize") != COLI_OK)
+        return COLI_DECLINED;
+    if (!w_out)
+        return decline("dequantize: NULL output");
+    if (!gate_call())
+        return COLI_DECLINED;
+    return launch_dequant(W, w_out, (hipStream_t)stream);
+}
+
+int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *stream) {
+    if (check_qt(W, "qmatmul") != COLI_OK)
+        return COLI_DECLINED;
+    if (!x || !y)
+        return decline("qmatmul: NULL x or y");
+    if (S < 1)
+        return decline("qmatmul: S=%d < 1", S);
+    if (!dev_aligned(x, 4) || !dev_aligned(y, 4))
+        return decline("qmatmul: x or y not 4-byte aligned");
+    if (!gate_call())
+        return COLI_DECLINED;
+    if (S <= coli_gemv_max_rows())
+        return launch_gemv(W, x, y, S, (hipStream_t)stream);
+    return launch_gemm(W, x, y, S, nullptr, 0, (hipStream_t)stream);
+}
+
+int coli_moe_route(const int32_t *ids, int S, int K, int E, int32_t *counts, int32_t *offsets,
+                   int32_t *perm, int32_t *n_bad, void *stream) {
+    if (!ids || !counts || !offsets || !perm || !n_bad)
+        return decline("moe_route: NULL pointer");
+    if (S < 0 || K < 1 || E < 1 || E > 4096)
+        return decline("moe_route: bad S=%d K=%d E=%d (E must be 1..4096)", S, K, E);
+    if ((int64_t)S * K > INT32_MAX / 4)
+        return decline("moe_route: S*K too large");
+    if (!gate_call())
+        return COLI_DECLINED;
+    return launch_route(ids, S, K, E, counts, offsets, perm, n_bad, nullptr, nullptr, nullptr, 0,
+                        0, (hipStream_t)stream);
+}
+
+size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shared) {
+    if (E < 1 || S < 1 || K < 1 || F < 1 || Dm < 1)
+        return 0;
+    if (S <= coli_gemv_max_rows())
+        return moe_decode_ws_bytes(S, K, F, has_shared);
+    return moe_prefill_ws_bytes(E, S, K, F, Dm, has_shared);
+}
+
+static int check_moe(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                     const float *x, int S, const int32_t *ids, int K,
+                     const coli_qtensor *sg, const coli_qtensor *su, const coli_qtensor *sd,
+                     const char *who) {
+    // down / sd may be NULL for the hidden-only entry point
+    if (gate == nullptr || gate->magic != QT_MAGIC) return decline("%s: bad gate tensor", who);
+    if (up == nullptr || up->magic != QT_MAGIC) return decline("%s: bad up tensor", who);
+    if (down != nullptr && down->magic != QT_MAGIC) return decline("%s: bad down tensor", who);
+    if (!x || !ids)
+        return decline("%s: NULL x or ids", who);
+    if (S < 1 || K < 1 || K > 64)
+        return decline("%s: bad S=%d K=%d (K must be 1..64)", who, S, K);
+    const int E = gate->n, F = gate->O, D = gate->I;
+    if (E > 4096)
+        return decline("%s: E=%d > 4096", who, E);
+    if (up->n != E || up->O != F || up->I != D)
+        return decline("%s: up [%d][%d][%d] != gate [%d][%d][%d]", who, up->n, up->O, up->I, E, F, D);
+    if (down && (down->n != E || down->O != D || down->I != F))
+        return decline("%s: down [%d][%d][%d] must be [%d][%d][%d]", who, down->n, down->O,
+                       down->I, E, D, F);
+    const coli_qtensor *all[6] = {gate, up, down, sg, su, sd};
+    const int nsh = (sg != nullptr) + (su != nullptr) + (sd != nullptr || !down);
+    if (nsh != 0 && nsh != 3)
+        return decline("%s: shared expert needs all of its matrices", who);
+    for (int i = 0; i < 6; ++i) {
+        const coli_qtensor *t = all[i];
+        if (!t) continue;
+        if (t->magic != QT_MAGIC)
+            return decline("%s: tensor %d not filled by coli_tensor_upload", who, i);
+        if (t->fmt != gate->fmt)
+            return decline("%s: tensor %d has fmt %d, gate has fmt %d (one format per block)",
+                           who, i, t->fmt, gate->fmt);
+        if (t->gs != gate->gs)
+            return decline("%s: tensor %d has gs %d, gate has gs %d (mixed group sizes in one "
+                           "block)", who, i, t->gs, gate->gs);
+        if (!(t->flags & QF_FAST))
+            return decline("%s: tensor %d layout unsupported by the block kernels (needs rows "
+                           "of whole 16-byte packets: I %% %d == 0, aligned codes)", who, i,
+                           packet_cols(t->fmt));
+        if (t->fmt == 4 && !(t->flags & (QF_GROUP32 | QF_GROUP16)))
+            return decline("%s: tensor %d gs=%d; the block kernels need gs %% 16 == 0", who, i,
+                           t->gs);
+    }
+    if (nsh == 3) {
+        if (sg->n != 1 || su->n != 1 || (sd && sd->n != 1))
+            return decline("%s: shared tensors must hold one matrix each", who);
+        if (sg->O != F || sg->I != D || su->O != F || su->I != D ||
+            (sd && (sd->O != D || sd->I != F)))
+            return decline("%s: shared expert shapes differ from the routed experts", who);
+    }
+    if (!dev_aligned(x, 16))
+        return decline("%s: x must be 16-byte aligned", who);
+    return COLI_OK;
+}
+
+int coli_moe_block(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                   const float *x, int S, const int32_t *ids, const float *w, int K,
+                   const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                   const coli_qtensor *sh_down, float *out, void *workspace, size_t ws_bytes,
+                   void *stream) {
+    if (check_moe(gate, up, down, x, S, ids, K, sh_gate, sh_up, sh_down, "moe_block") != COLI_OK)
+        return COLI_DECLINED;
+    if (!w || !out)
+        return decline("moe_block: NULL w or out");
+    if (!workspace || !dev_aligned(workspace, 256))
+        return decline("moe_block: workspace NULL or not 256-byte aligned");
+    const int has_sh = sh_gate != nullptr;
+    const size_t need = coli_moe_workspace_bytes(gate->n, S, K, gate->O, gate->I, has_sh);
+    if (ws_bytes < need)
+        return decline("moe_block: workspace %zu bytes < %zu needed", ws_bytes, need);
+    if (!gate_call())
+        return COLI_DECLINED;
+    MoeArgs a;
+    a.gate = gate; a.up = up; a.down = down;
+    a.sg = sh_gate; a.su = sh_up; a.sd = sh_down;
+    a.x = x; a.S = S; a.K = K; a.E = gate->n; a.F = gate->O; a.D = gate->I;
+    a.ids = ids; a.w = w; a.out = out; a.h_out = nullptr;
+    a.ws = workspace; a.ws_bytes = ws_bytes; a.st = (hipStream_t)stream;
+    if (S <= coli_gemv_max_rows())
+        return launch_moe_decode(a);
+    return launch_moe_prefill(a);
+}
+
+int coli_moe_hidden(const coli_qtensor *gate, const coli_qtensor *up, const float *x, int S,
+                    const int32_t *ids, int K, const coli_qtensor *sh_gate,
+                    const coli_qtensor *sh_up, float *h_out, void *workspace, size_t ws_bytes,
+                    void *stream) {
+    if ((sh_gate == nullptr) != (sh_up == nullptr))
+        return decline("moe_hidden: shared expert needs both gate and up");
+    if (check_moe(gate, up, nullptr, x, S, ids, K, sh_gate, sh_up, nullptr,
+                  "moe_hidden") != COLI_OK)
+        return COLI_DECLINED;
+    if (!h_out || !dev_aligned(h_out, 16))
+        return decline("moe_hidden: h_out NULL or not 16-byte aligned");
+    if (!workspace || !dev_aligned(workspace, 256))
+        return decline("moe_hidden: workspace NULL or not 256-byte aligned");
+    const int has_sh = sh_gate != nullptr;
+    const size_t need = coli_moe_workspace_bytes(gate->n, S, K, gate->O, gate->I, has_sh);
+    if (ws_bytes < need)
+        return decline("moe_hidden: workspace %zu bytes < %zu needed", ws_bytes, need);
+    if (!gate_call())
+        return COLI_DECLINED;
+    MoeArgs a;
+    a.gate = gate; a.up = up; a.down = nullptr;
+    a.sg = sh_gate; a.su = sh_up; a.sd = nullptr;
+    a.x = x; a.S = S; a.K = K; a.E = gate->n; a.F = gate->O; a.D = gate->I;
+    a.ids = ids; a.w = nullptr; a.out = nullptr; a.h_out = h_out;
+    a.ws = workspace; a.ws_bytes = ws_bytes; a.st = (hipStream_t)stream;
+    if (S <= coli_gemv_max_rows())
+        return launch_moe_decode(a);
+    return launch_moe_prefill(a);
+}
+
+}  // extern "C"

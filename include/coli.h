@@ -1,0 +1,228 @@
+/*
+ * coli.h -- C ABI of the MI355X (gfx950) quantized-weight matmul library
+ * (libcoli.so): the colibri engine's quantized matmul and batched MoE expert
+ * block, as hand-written HIP kernels.
+ *
+ * Sources (pages describing the colibri engine; cited as in every file):
+ *   colibri PR #298, commit adding fmt=4 to the CUDA backend  -- grouped int4:
+ *       fmt=2 nibble layout plus one f32 scale per gs inputs along I, folded in
+ *       per group during accumulation; tensor upload takes gs and sizes the
+ *       scale buffer O*ceil(I/gs).
+ *   colibri PR #298, commit adding the matmul_i4_grouped test -- offset
+ *       nibbles (0x0 -> -8, 0xF -> +7), partial last group, tolerances judged
+ *       against the sum of |terms|.
+ *   colibri PR #298, commit adding fmt=4 to the Metal mm_gemv -- fmt 1-3 scale
+ *       once per row after the dot product; fmt 4 per group.
+ *   colibri PR #298, commit making the CUDA ABI return 0 for fmt=4 -- an entry
+ *       that cannot honour its input returns 0: a fallback, never a wrong answer.
+ *   colibri-strix commit log, "metal: batched moe_block + zero-copy slab
+ *       registry" -- gate/up -> SiLU -> down for a whole expert block in one
+ *       submission, ragged per-row routing, weighted scatter-add.
+ *   colibri-strix commit log, "fuse shared expert into GPU block" -- the shared
+ *       expert joins the block as an extra expert with weight 1.0 on every row.
+ *   colibri-strix commit log, "route large row-batch matmul_qt GEMMs to the GPU"
+ *       -- large row batches (prefill) take a GEMM path, small ones a GEMV.
+ *
+ * Conventions shared by every entry point
+ *   Return value: COLI_OK (1) work validated and enqueued on `stream`;
+ *   COLI_DECLINED (0) the call cannot be honoured (unknown or unsupported
+ *   format, group size, shape, NULL or misaligned pointer, workspace too small,
+ *   fault injection tripped): NOTHING was written or enqueued, and
+ *   coli_last_reason() says why; COLI_HIP_ERROR (-1) the HIP runtime reported
+ *   an error (coli_last_error()).
+ *   Memory: every data pointer is a DEVICE pointer owned by the caller (for
+ *   example a torch tensor's data_ptr()); the library allocates and frees no
+ *   device memory in these calls and keeps no pointer past the call, except
+ *   that enqueued kernels read/write the buffers until they complete.
+ *   Streams: `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *   asynchronous; the caller synchronises.
+ *   Layouts are row-major and dense.  Activations and outputs are f32.
+ *   Reentrancy: calls on different streams may overlap; a workspace must not be
+ *   shared by two calls that may run at the same time.
+ */
+#ifndef COLI_H
+#define COLI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COLI_OK 1
+#define COLI_DECLINED 0
+#define COLI_HIP_ERROR (-1)
+
+/* Weight formats (colibri's QT fmt codes). */
+#define COLI_FMT_I8_ROW 1  /* int8 two's complement, one f32 scale per row      */
+#define COLI_FMT_I4_ROW 2  /* int4 offset (nibble-8), one f32 scale per row     */
+#define COLI_FMT_I2_ROW 3  /* int2 offset (code-2), one f32 scale per row       */
+#define COLI_FMT_I4_GRP 4  /* int4 offset, one f32 scale per gs inputs (groups) */
+
+/*
+ * A quantized matrix, or a stack of n equally shaped matrices (experts).
+ * Filled and validated by coli_tensor_upload; treat the fields as read-only.
+ *
+ * Codes q: bytes [n][O][row_bytes], each row starting on a byte boundary:
+ *   fmt 1: row_bytes = I,         byte i = int8 value v
+ *   fmt 2/4: row_bytes = ceil(I/2), element i in byte i/2, LOW nibble for even
+ *            i, high nibble for odd i; v = nibble - 8 (0x0 -> -8, 0xF -> +7)
+ *   fmt 3: row_bytes = ceil(I/4), element i in byte i/4 at bits 2*(i%4)..+1;
+ *          v = code - 2
+ * Scales s: f32 [n][O] for fmt 1-3; f32 [n][O][ng] for fmt 4 with
+ *   ng = ceil(I/gs), group g covering inputs [g*gs, min((g+1)*gs, I)).
+ * Weight value: w(o,i) = s[o] * v (fmt 1-3), s[o][i/gs] * v (fmt 4).
+ */
+typedef struct coli_qtensor {
+    int32_t fmt;
+    int32_t n;         /* matrices in the stack, >= 1                       */
+    int32_t O, I;      /* rows (outputs) and inputs of each matrix          */
+    int32_t gs;        /* fmt 4: inputs per scale group; fmt 1-3: 0         */
+    int32_t ng;        /* fmt 4: ceil(I/gs); fmt 1-3: 1                     */
+    int64_t row_bytes; /* bytes per row of codes                            */
+    int64_t q_stride;  /* bytes between matrices   = O * row_bytes          */
+    int64_t s_stride;  /* floats between matrices  = O * ng                 */
+    const void *q;     /* device codes                                      */
+    const float *s;    /* device scales                                     */
+    uint32_t magic;    /* set by coli_tensor_upload                         */
+    uint32_t flags;    /* internal: which kernel paths the layout allows    */
+} coli_qtensor;
+
+/*
+ * coli_tensor_upload -- describe caller-owned device codes and scales as a
+ * quantized tensor (colibri PR #298, CUDA fmt=4 commit: the grouped upload
+ * takes gs and allocates O*ceil(I/gs) scales; the per-row upload is gs=0).
+ *   t      host record to fill (written only on success)
+ *   fmt    1..4;  n >= 1;  O, I >= 1
+ *   gs     fmt 4: group size >= 1 (any value; multiples of 16 take the fast
+ *          kernels, others a slower exact path); fmt 1-3: must be 0
+ *   ng     fmt 4: must equal ceil(I/gs); fmt 1-3: must be 1
+ *   q_dev, s_dev  device pointers (non-NULL); nothing is copied -- the record
+ *          refers to the caller's buffers, which must outlive its use.
+ * Returns COLI_OK or COLI_DECLINED (bad fmt, gs, ng, shape or NULL pointer).
+ * Launches nothing.
+ */
+int coli_tensor_upload(coli_qtensor *t, int fmt, int n, int O, int I, int gs, int ng,
+                       const void *q_dev, const float *s_dev);
+
+/*
+ * coli_qmatmul -- y = W x for every matrix of the stack
+ * (colibri PR #298 commits: fmt 4 folds the group scale in per group, fmt 1-3
+ * scale once per row; colibri-strix "route large row-batch matmul_qt GEMMs to
+ * the GPU": large row batches take the GEMM path).
+ *   W   tensor from coli_tensor_upload (n matrices [O][I])
+ *   x   device f32 [S][I]          y   device f32 [n][S][O]
+ *   S   >= 1 input rows.  S <= coli_gemv_max_rows() (default 4) runs the
+ *       fp32 GEMV kernels (error <= 1e-5 * sum_i |w||x| per output); larger S
+ *       runs the bf16 matrix-core GEMM (weights and x rounded to bf16, fp32
+ *       accumulation; error <= 4e-3 * sum_i |w||x|).
+ * x and y must not overlap.  Returns COLI_OK / COLI_DECLINED / COLI_HIP_ERROR.
+ */
+int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *stream);
+
+/* Largest S served by the fp32 GEMV path (env COLI_GEMV_MAX_ROWS, 1..4). */
+int coli_gemv_max_rows(void);
+/* Set it (1..4); returns the previous value, or 0 if the value is refused. */
+int coli_set_gemv_max_rows(int s);
+
+/*
+ * coli_dequantize -- w_out[e][o][i] = (float)(s * v), the exact product
+ * rounded once to f32 (test hook; bit-exact with the oracle).
+ *   w_out  device f32 [n][O][I].  Returns COLI_OK / COLI_DECLINED / -1.
+ */
+int coli_dequantize(const coli_qtensor *W, float *w_out, void *stream);
+
+/*
+ * coli_moe_route -- the block's routing table (colibri-strix "batched
+ * moe_block": per-row ragged expert routing).
+ *   ids     device int32 [S][K] expert ids; ids outside [0,E) are left out
+ *   counts  device int32 [E]     pairs routed to each expert
+ *   offsets device int32 [E+1]   exclusive prefix sum; offsets[E] = valid pairs
+ *   perm    device int32 [S*K]   valid pair indices p = s*K+k grouped by
+ *           ascending expert, ascending p within an expert; entries past
+ *           offsets[E] are set to -1
+ *   n_bad   device int32 [1]     number of ids outside [0,E)
+ * Limits: 1 <= E <= 4096, K >= 1, S >= 0.  Bit-exact with the oracle.
+ */
+int coli_moe_route(const int32_t *ids, int S, int K, int E, int32_t *counts,
+                   int32_t *offsets, int32_t *perm, int32_t *n_bad, void *stream);
+
+/*
+ * coli_moe_block -- the batched MoE expert block in one submission
+ * (colibri-strix "batched moe_block": gate/up -> SiLU -> down per expert, then
+ * the weighted combine; "fuse shared expert": the shared expert adds with
+ * weight 1.0 on every row):
+ *   out[s] = sum_k w[s][k] * D_e (silu(G_e x_s) * (U_e x_s)),  e = ids[s][k]
+ *            + D_sh (silu(G_sh x_s) * (U_sh x_s))            (if given)
+ *   gate, up   stacks of E matrices [F][Dm]   (same fmt and gs)
+ *   down       stack of E matrices [Dm][F]
+ *   x          device f32 [S][Dm];  ids device int32 [S][K];  w device f32 [S][K]
+ *   sh_gate, sh_up, sh_down  all NULL, or one matrix each with the routed
+ *              stacks' shapes, fmt and gs (a group-size mix is declined)
+ *   out        device f32 [S][Dm] (overwritten)
+ *   workspace  device buffer of at least coli_moe_workspace_bytes(...) bytes,
+ *              256-byte aligned
+ * Routing weights are used as given (no renormalisation).  Pairs whose id lies
+ * outside [0,E) contribute nothing (their count is reported by
+ * coli_moe_route); duplicate ids in a row are independent terms.  The combine
+ * adds k in ascending order with no atomics, so reruns are bit-identical.
+ * S <= coli_gemv_max_rows() runs fp32 GEMV kernels; larger S runs bf16
+ * matrix-core grouped GEMMs over the routing table.
+ * Limits: 1 <= E <= 4096, 1 <= K <= 64, S >= 1.
+ */
+int coli_moe_block(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                   const float *x, int S, const int32_t *ids, const float *w, int K,
+                   const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                   const coli_qtensor *sh_down, float *out, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * coli_moe_hidden -- the first half of coli_moe_block on its own (test hook):
+ * h[p] = silu(G_e x_s) * (U_e x_s) for routed pair p = s*K+k (zero when the id
+ * is out of range), then h[S*K+s] for the shared expert when given.
+ *   h_out  device f32 [S*K (+S)][F].  Same kernels, precision and workspace
+ *          rules as coli_moe_block with the same S.
+ */
+int coli_moe_hidden(const coli_qtensor *gate, const coli_qtensor *up, const float *x, int S,
+                    const int32_t *ids, int K, const coli_qtensor *sh_gate,
+                    const coli_qtensor *sh_up, float *h_out, void *workspace,
+                    size_t ws_bytes, void *stream);
+
+/* Workspace bytes coli_moe_block / coli_moe_hidden need (0 on bad input). */
+size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shared);
+
+/* ---------------------------------------------------------------------- */
+/* Diagnostics (colibri PR #298, HIP single-source merge: a fault-injection */
+/* control proves GPU calls really executed; issue #585: fallbacks must be  */
+/* loud).                                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Why the last call on this thread returned COLI_DECLINED ("" if none). */
+const char *coli_last_reason(void);
+/* Last HIP error text on this thread ("" if none). */
+const char *coli_last_error(void);
+/* Counters since load: compute calls, declined calls, kernel launches. */
+void coli_stats(uint64_t *calls, uint64_t *declined, uint64_t *launches);
+/* Fault injection: after n more successful compute calls every compute call
+ * returns COLI_DECLINED and writes nothing; n < 0 disables.  The environment
+ * variable COLI_FAIL_AFTER sets the initial value. */
+void coli_set_fail_after(int64_t n);
+
+/* Kernel timing with HIP events recorded around every launch while enabled
+ * (on the launch stream).  coli_prof_read sums completed launches whose kernel
+ * tag equals `tag` (e.g. "moe_gateup_decode"); returns the count or -1. */
+void coli_prof_enable(int on);
+void coli_prof_reset(void);
+int64_t coli_prof_read(const char *tag, double *total_ms);
+/* Tag of the i-th distinct kernel seen by the profiler (NULL past the end). */
+const char *coli_prof_tag(int i);
+
+/* Library version string. */
+const char *coli_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLI_H */

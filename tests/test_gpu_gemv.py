@@ -1,0 +1,193 @@
+"""GPU parity of coli_dequantize (bit-exact) and coli_qmatmul against the
+oracle, through the C ABI.
+
+The shape matrix follows the grouped-int4 test commit of colibri PR #298
+(I a multiple of gs, partial last group, odd I, gs > I, gs = 16/64/128,
+S > 1, nibble extremes) and the Metal commits' tails (non-multiple-of-8
+rows/columns, I <= 64), plus the full sizes of the decode workloads."""
+import numpy as np
+import pytest
+import torch
+
+import bit_gemv_coli_amd as coli
+import synthdata as sd
+from gpu_util import (TOL_BF16, TOL_FP32, assert_within, gpu_qmatmul, make_case, need_gpu,
+                      qtensor, to_dev)
+from oracle import QMat
+
+pytestmark = pytest.mark.gpu
+
+# (fmt, O, I, gs, S, n)
+SMALL = [
+    (4, 8, 128, 64, 1, 1), (4, 5, 130, 64, 1, 1), (4, 3, 129, 64, 2, 1), (4, 4, 37, 64, 1, 1),
+    (4, 6, 96, 16, 3, 1), (4, 4, 256, 128, 1, 1), (4, 2, 1, 16, 1, 1), (4, 7, 200, 32, 4, 1),
+    (4, 9, 96, 48, 2, 1), (4, 3, 96, 24, 1, 1), (4, 33, 4096 + 64, 64, 4, 1),
+    (4, 70, 2048, 64, 1, 3), (4, 17, 6144, 128, 3, 2), (4, 5, 32, 32, 1, 1), (4, 5, 32, 64, 2, 1),
+    (2, 5, 130, 0, 2, 1), (2, 3, 33, 0, 1, 1), (2, 41, 2048 + 32, 0, 4, 1), (2, 9, 64, 0, 1, 2),
+    (1, 4, 70, 0, 3, 1), (1, 2, 5, 0, 1, 1), (1, 33, 1040, 0, 2, 1), (1, 8, 4096, 0, 4, 2),
+    (3, 5, 130, 0, 2, 1), (3, 3, 7, 0, 1, 1), (3, 2, 66, 0, 1, 1), (3, 19, 2080, 0, 4, 1),
+    (3, 12, 64, 0, 3, 2),
+]
+
+
+def _id(c):
+    return "fmt{}-O{}-I{}-gs{}-S{}-n{}".format(*c)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+def test_dequant_bit_exact(orc, case):
+    need_gpu()
+    fmt, O, I, gs, S, n = case
+    W, _ = make_case(fmt, O, I, gs, S, seed=hash(case) % 1000, n=n if n > 1 else None)
+    T = qtensor(W)
+    w = torch.full((n, O, I), float("nan"), device="cuda")
+    coli.check(coli.coli_dequantize(T, w), "coli_dequantize")
+    got = w.cpu().numpy()
+    for e in range(n):
+        ref = orc.dequant_f32(W.expert(e))
+        assert np.array_equal(got[e].view(np.uint32), ref.view(np.uint32)), (case, e)
+
+
+def test_dequant_subnormal_and_extreme_scales(orc):
+    need_gpu()
+    # products that land in the f32 subnormal range and near the top of it
+    q = np.array([[0x00, 0xFF, 0x19, 0x91]], dtype=np.uint8)
+    s = np.array([[1e-41, 3.0e38]], dtype=np.float32)
+    W = QMat(4, 1, 8, 4, q, s)
+    T = qtensor(W)
+    w = torch.zeros((1, 1, 8), device="cuda")
+    coli.check(coli.coli_dequantize(T, w))
+    assert np.array_equal(w.cpu().numpy()[0].view(np.uint32), orc.dequant_f32(W).view(np.uint32))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+def test_qmatmul_small(orc, case):
+    need_gpu()
+    fmt, O, I, gs, S, n = case
+    W, x = make_case(fmt, O, I, gs, S, seed=1 + hash(case) % 1000, n=n if n > 1 else None)
+    T = qtensor(W)
+    y = gpu_qmatmul(T, x, n)
+    tol = TOL_FP32 if S <= coli.coli_gemv_max_rows() else TOL_BF16
+    for e in range(n):
+        y_ref, A = orc.qmatmul(W.expert(e), x)
+        assert_within(y[e], y_ref, A, tol, f"{case} expert {e}")
+
+
+def test_qmatmul_nibble_extremes_and_outliers(orc):
+    """Rows of all 0x00 / all 0xFF bytes (-8 / +7), zero rows (0x88), and
+    outlier-heavy rows (one large group scale), S = 1..4."""
+    need_gpu()
+    r = sd.rng(77)
+    O, I, gs = 8, 2048, 64
+    q = sd.gen_codes(r, 4, O, I)
+    q[0] = 0x00
+    q[1] = 0xFF
+    q[2] = 0x88
+    q[3, : I // 4] = 0x88
+    s = sd.gen_scales(r, 4, O, I, gs)
+    s[4, 7] = 50.0
+    s[5, :] = 1e-3
+    s[5, 3] = 1e3
+    W = QMat(4, O, I, gs, q, s)
+    T = qtensor(W)
+    for S in (1, 2, 3, 4):
+        x = sd.gen_x(r, S, I)
+        x[:, 100] = 1e4
+        y = gpu_qmatmul(T, x)[0]
+        y_ref, A = orc.qmatmul(W, x)
+        assert_within(y, y_ref, A, TOL_FP32, f"extremes S={S}")
+        assert np.all(y[:, 2] == 0.0)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_qmatmul_one_hot_columns_exact(orc, S):
+    """x = e_i picks column i: the GPU result equals s*v exactly."""
+    need_gpu()
+    W, _ = make_case(4, 64, 2048, 64, 1, seed=5)
+    T = qtensor(W)
+    cols = [0, 31, 32, 1000, 2047][:S]
+    x = np.zeros((S, 2048), np.float32)
+    for t, c in enumerate(cols):
+        x[t, c] = 1.0
+    y = gpu_qmatmul(T, x)[0]
+    w = orc.dequant_f32(W)
+    for t, c in enumerate(cols):
+        assert np.array_equal(y[t], w[:, c]), (S, c)
+
+
+def test_qmatmul_config1_full(orc):
+    """Single fmt-4 GEMV: O=1024, I=2048, gs=64, S=1, seed 0."""
+    need_gpu()
+    W, x = make_case(4, 1024, 2048, 64, 1, seed=0)
+    y = gpu_qmatmul(qtensor(W), x)[0]
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(y, y_ref, A, TOL_FP32, "config 1")
+
+
+SWEEP = [(1, 0), (2, 0), (3, 0), (4, 64), (4, 128)]
+
+
+@pytest.mark.parametrize("fmt,gs", SWEEP, ids=[f"fmt{f}-gs{g}" for f, g in SWEEP])
+@pytest.mark.parametrize("S", [1, 4])
+def test_qmatmul_format_sweep_full(orc, fmt, gs, S):
+    """Format sweep at full size: O = I = 6144, S in {1, 4}."""
+    need_gpu()
+    W, x = make_case(fmt, 6144, 6144, gs, S, seed=10 + fmt + gs + S)
+    y = gpu_qmatmul(qtensor(W), x)[0]
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(y, y_ref, A, TOL_FP32, f"sweep fmt {fmt} gs {gs} S {S}")
+
+
+@pytest.mark.parametrize("O,I", [(1536, 6144), (16384, 1536), (576, 6144), (6144, 16384)])
+def test_qmatmul_attention_projection_shapes(orc, O, I):
+    """The decode layer's projections (q_a, q_b, kv_a, o_proj), fmt 4 g64."""
+    need_gpu()
+    W, x = make_case(4, O, I, 64, 1, seed=O + I)
+    y = gpu_qmatmul(qtensor(W), x)[0]
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(y, y_ref, A, TOL_FP32, f"proj {O}x{I}")
+
+
+def test_qmatmul_repeatable_bitwise(orc):
+    need_gpu()
+    W, x = make_case(4, 3000, 6144, 64, 3, seed=9)
+    T = qtensor(W)
+    a = gpu_qmatmul(T, x)
+    b = gpu_qmatmul(T, x)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_qmatmul_unaligned_x_and_stream(orc):
+    """An x view at a 4-byte (not 16-byte) offset takes the exact fallback;
+    work on a side stream is ordered on that stream."""
+    need_gpu()
+    W, x = make_case(4, 40, 256, 64, 2, seed=3)
+    T = qtensor(W)
+    buf = torch.zeros(2 * 256 + 1, device="cuda")
+    buf[1:].copy_(torch.from_numpy(x.reshape(-1)))
+    xv = buf[1:]
+    y = torch.zeros((2, 40), device="cuda")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        coli.check(coli.coli_qmatmul(T, xv, y, 2, st))
+    st.synchronize()
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(y.cpu().numpy(), y_ref, A, TOL_FP32, "unaligned x")
+
+
+def test_fault_injection_writes_nothing(orc):
+    need_gpu()
+    W, x = make_case(4, 16, 128, 64, 1, seed=4)
+    T = qtensor(W)
+    xd = to_dev(x)
+    y = torch.full((1, 16), 123.0, device="cuda")
+    coli.coli_set_fail_after(1)
+    try:
+        assert coli.coli_qmatmul(T, xd, y, 1) == coli.COLI_OK
+        torch.cuda.synchronize()
+        y.fill_(123.0)
+        assert coli.coli_qmatmul(T, xd, y, 1) == coli.COLI_DECLINED
+        torch.cuda.synchronize()
+        assert torch.all(y == 123.0)
+    finally:
+        coli.coli_set_fail_after(-1)

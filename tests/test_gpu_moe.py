@@ -1,0 +1,238 @@
+"""GPU parity of the MoE routing table (bit-exact) and the expert block
+(colibri-strix commit log, "metal: batched moe_block": gate/up -> SiLU ->
+down per routed expert, weighted combine; "fuse shared expert": the shared
+expert adds with weight 1.0 on every row) against the oracle.
+
+Checks per case:
+  * hidden h = silu(G x) * (U x) against the oracle within
+    eps_j = tau * (1.1 |u_j| A_g,j + |silu(g_j)| A_u,j)  (1.1 >= max |silu'|);
+  * stagewise: out against sum_k w_k D_e h_gpu (+ shared), recomputed by the
+    oracle from the GPU's own h, within tau * sum_k |w_k| A_D;
+  * end to end: |out - out_ref| <= sum_k |w_k| (|D| eps + tau |D| (|h| + eps)).
+tau = 1e-5 for the fp32 decode path (S <= 4), 4e-3 for the bf16 prefill path."""
+import numpy as np
+import pytest
+import torch
+
+import bit_gemv_coli_amd as coli
+import synthdata as sd
+from gpu_util import TOL_BF16, TOL_FP32, assert_within, need_gpu, qtensor, to_dev
+from oracle import QMat
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe_inputs(seed, fmt, S, K, E, D, F, gs, shared, routing="uniform"):
+    r = sd.rng(seed)
+    x = sd.gen_x(r, S, D)
+    gq, gsc = sd.gen_matrix(r, fmt, F, D, gs, n=E)
+    uq, usc = sd.gen_matrix(r, fmt, F, D, gs, n=E)
+    dq, dsc = sd.gen_matrix(r, fmt, D, F, gs, n=E)
+    g = 0 if fmt != 4 else gs
+    G, U, Dn = QMat(fmt, F, D, g, gq, gsc), QMat(fmt, F, D, g, uq, usc), QMat(fmt, D, F, g, dq, dsc)
+    sh = None
+    if shared:
+        a = sd.gen_matrix(r, fmt, F, D, gs)
+        b = sd.gen_matrix(r, fmt, F, D, gs)
+        c = sd.gen_matrix(r, fmt, D, F, gs)
+        sh = (QMat(fmt, F, D, g, *a), QMat(fmt, F, D, g, *b), QMat(fmt, D, F, g, *c))
+    if routing == "zipf":
+        ids, w = sd.gen_routing_zipf(r, S, K, E, 1.1)
+    else:
+        ids, w = sd.gen_routing_uniform(r, S, K, E)
+    return G, U, Dn, sh, x, ids, w
+
+
+def _run_gpu(G, U, Dn, sh, x, ids, w, hidden=True):
+    S, K = ids.shape
+    E, F, D = G.n, G.O, G.I
+    tg, tu, td = qtensor(G), qtensor(U), qtensor(Dn)
+    ts = [qtensor(m) for m in sh] if sh is not None else [None, None, None]
+    xd, idd, wd = to_dev(x), to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32))
+    ws_bytes = coli.coli_moe_workspace_bytes(E, S, K, F, D, sh is not None)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((S, D), float("nan"), device="cuda")
+    coli.check(coli.coli_moe_block(tg, tu, td, xd, S, idd, wd, K, ts[0], ts[1], ts[2], out, ws,
+                                   ws_bytes), "coli_moe_block")
+    h = None
+    if hidden:
+        P = S * K + (S if sh is not None else 0)
+        h = torch.full((P, F), float("nan"), device="cuda")
+        coli.check(coli.coli_moe_hidden(tg, tu, xd, S, idd, K, ts[0], ts[1], h, ws, ws_bytes),
+                   "coli_moe_hidden")
+        h = h.cpu().numpy()
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), h
+
+
+def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None):
+    S, K = ids.shape
+    E = G.n
+    D = Dn.O
+    out_ref, inter = orc.moe_block(G, U, Dn, x, ids, w, shared=sh, rows=rows, intermediates=True)
+    g, u, h, Ag, Au = (inter[k] for k in ("g", "u", "h", "Ag", "Au"))
+    sil = g / (1.0 + np.exp(-g))
+    eps = tau * (1.1 * np.abs(u) * Ag + np.abs(sil) * Au) + 1e-6 * np.abs(h) + 1e-30
+    P = S * K + (S if sh is not None else 0)
+    valid = np.ones(P, bool)
+    valid[:S * K] = (ids.reshape(-1) >= 0) & (ids.reshape(-1) < E)
+    # 1. hidden vectors
+    if h_gpu is not None:
+        err = np.abs(h_gpu.astype(np.float64) - h)
+        assert np.all(err[valid] <= eps[valid]), \
+            f"hidden: max err/eps = {np.max(err[valid] / eps[valid]):.3e}"
+        assert np.all(h_gpu[~valid] == 0.0)
+    out_rows = out if rows is None else out[:, rows]
+    # 2. stagewise down + combine from the GPU's own h (f32 exactly as stored)
+    if h_gpu is not None:
+        sel = np.arange(D) if rows is None else np.asarray(rows)
+        y_st = np.zeros((S, len(sel)))
+        A_st = np.zeros((S, len(sel)))
+        for p in range(P):
+            if not valid[p]:
+                continue
+            if p < S * K:
+                s, wk, Dm = p // K, float(w.flat[p]), Dn.expert(int(ids.flat[p]))
+            else:
+                s, wk, Dm = p - S * K, 1.0, sh[2]
+            Dsel = QMat(Dm.fmt, len(sel), Dm.I, Dm.gs, np.ascontiguousarray(Dm.q[sel]),
+                        np.ascontiguousarray(Dm.s[sel]))
+            yk, Ak = orc.qmatmul(Dsel, h_gpu[p:p + 1].astype(np.float32))
+            y_st[s] += wk * yk[0]
+            A_st[s] += abs(wk) * Ak[0]
+        assert_within(out_rows, y_st, A_st, tau, "stagewise down+combine")
+    # 3. end to end
+    sel = np.arange(D) if rows is None else np.asarray(rows)
+    bound = np.zeros((S, len(sel)))
+    for p in range(P):
+        if not valid[p]:
+            continue
+        if p < S * K:
+            s, wk, Dm = p // K, float(w.flat[p]), Dn.expert(int(ids.flat[p]))
+        else:
+            s, wk, Dm = p - S * K, 1.0, sh[2]
+        Dsel = QMat(Dm.fmt, len(sel), Dm.I, Dm.gs, np.ascontiguousarray(Dm.q[sel]),
+                    np.ascontiguousarray(Dm.s[sel]))
+        Dabs = np.abs(orc.dequant_f64(Dsel))
+        bound[s] += abs(wk) * (Dabs @ eps[p] + tau * (Dabs @ (np.abs(h[p]) + eps[p])))
+    err = np.abs(out_rows.astype(np.float64) - out_ref)
+    assert np.all(err <= bound + 1e-30), f"end to end: max err/bound = {np.max(err / bound):.3e}"
+
+
+DECODE = [  # (fmt, S, K, E, D, F, gs, shared)
+    (4, 1, 8, 16, 256, 128, 64, False),
+    (4, 1, 8, 16, 256, 128, 64, True),
+    (4, 2, 4, 6, 192, 96, 32, True),
+    (4, 3, 2, 5, 128, 64, 16, False),
+    (4, 4, 8, 12, 2048 + 64, 64, 64, True),
+    (4, 4, 3, 9, 96, 2048 + 96, 32, False),
+    (4, 1, 1, 1, 64, 32, 128, False),
+    (2, 2, 3, 7, 128, 96, 0, True),
+    (1, 1, 4, 6, 64, 48, 0, False),
+    (1, 3, 2, 4, 160, 64, 0, True),
+    (3, 2, 4, 6, 128, 64, 0, True),
+    (3, 4, 2, 3, 96, 160, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=["fmt{}-S{}-K{}-E{}-D{}-F{}-gs{}-sh{}".format(*c) for c in DECODE])
+def test_moe_decode_small(orc, case):
+    need_gpu()
+    fmt, S, K, E, D, F, gs, shared = case
+    G, U, Dn, sh, x, ids, w = _moe_inputs(hash(case) % 997, fmt, S, K, E, D, F, gs, shared)
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
+
+
+def test_moe_decode_duplicates_invalid_and_zero_weights(orc):
+    need_gpu()
+    G, U, Dn, sh, x, ids, w = _moe_inputs(31, 4, 3, 4, 8, 128, 64, 64, True)
+    ids = ids.copy()
+    w = w.copy()
+    ids[0, 1] = ids[0, 0]      # duplicate expert in one row: two independent terms
+    ids[1, 2] = 8              # out of range: left out
+    ids[2, 0] = -5             # out of range: left out
+    w[2, 3] = 0.0              # zero weight
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
+
+
+def test_moe_decode_repeatable_bitwise(orc):
+    need_gpu()
+    G, U, Dn, sh, x, ids, w = _moe_inputs(5, 4, 4, 8, 16, 512, 256, 64, True)
+    a, _ = _run_gpu(G, U, Dn, sh, x, ids, w, hidden=False)
+    b, _ = _run_gpu(G, U, Dn, sh, x, ids, w, hidden=False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_moe_decode_config2_full(orc):
+    """Decode MoE block at its real shape: hidden 6144, 256 experts with gate/up
+    2048x6144 and down 6144x2048, fmt 4 gs 64, 8 routed experts chosen
+    uniformly, softmax weights.  The expert pool is drawn on the device with a
+    seeded generator; the 8 routed experts are copied back for the oracle;
+    the oracle evaluates 384 sampled output rows."""
+    need_gpu()
+    E, D, F, gs, K = 256, 6144, 2048, 64, 8
+    r = sd.rng(2)
+    x = sd.gen_x(r, 1, D)
+    ids, w = sd.gen_routing_uniform(r, 1, K, E)
+    gq, gsc = sd.pool_on_device(100, 4, E, F, D, gs)
+    uq, usc = sd.pool_on_device(101, 4, E, F, D, gs)
+    dq, dsc = sd.pool_on_device(102, 4, E, D, F, gs)
+    tg = coli.QTensor(4, gq, gsc, F, D, gs)
+    tu = coli.QTensor(4, uq, usc, F, D, gs)
+    td = coli.QTensor(4, dq, dsc, D, F, gs)
+    xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+    ws_bytes = coli.coli_moe_workspace_bytes(E, 1, K, F, D, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((1, D), float("nan"), device="cuda")
+    h = torch.full((K, F), float("nan"), device="cuda")
+    coli.check(coli.coli_moe_block(tg, tu, td, xd, 1, idd, wd, K, None, None, None, out, ws,
+                                   ws_bytes))
+    coli.check(coli.coli_moe_hidden(tg, tu, xd, 1, idd, K, None, None, h, ws, ws_bytes))
+    torch.cuda.synchronize()
+    # the routed experts, relabelled 0..7, on the host
+    sel = torch.from_numpy(ids[0].astype(np.int64)).cuda()
+    G = QMat(4, F, D, gs, gq[sel].cpu().numpy(), gsc[sel].cpu().numpy())
+    U = QMat(4, F, D, gs, uq[sel].cpu().numpy(), usc[sel].cpu().numpy())
+    Dn = QMat(4, D, F, gs, dq[sel].cpu().numpy(), dsc[sel].cpu().numpy())
+    local = np.arange(K, dtype=np.int32)[None, :]
+    rows = np.sort(sd.rng(3).choice(D, 384, replace=False)).astype(np.int32)
+    _check_moe(orc, G, U, Dn, None, x, local, w, out.cpu().numpy(), h.cpu().numpy(), TOL_FP32,
+               rows=rows)
+
+
+ROUTE = [(1, 8, 256), (3, 2, 5), (7, 3, 4), (16, 4, 64), (5, 1, 1), (544, 8, 256),
+         (100, 8, 4096), (2000, 2, 37), (4, 64, 300)]
+
+
+@pytest.mark.parametrize("S,K,E", ROUTE)
+def test_route_bit_exact(orc, S, K, E):
+    need_gpu()
+    r = sd.rng(S * 7 + K + E)
+    if S == 544:
+        ids, _ = sd.gen_routing_zipf(r, S, K, E, 1.1)
+    else:
+        ids = r.integers(0, E, size=(S, K)).astype(np.int32)
+    _route_compare(orc, ids, E)
+
+
+def test_route_invalid_ids(orc):
+    need_gpu()
+    ids = sd.rng(1).integers(-3, 12, size=(50, 4)).astype(np.int32)
+    _route_compare(orc, ids, 9)
+
+
+def _route_compare(orc, ids, E):
+    S, K = ids.shape
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((max(S * K, 1),), -7, dtype=torch.int32, device="cuda")
+    bad = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    coli.check(coli.coli_moe_route(to_dev(ids), S, K, E, counts, offsets, perm, bad))
+    torch.cuda.synchronize()
+    c_ref, o_ref, p_ref, b_ref = orc.moe_route(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(perm.cpu().numpy()[:S * K], p_ref)
+    assert int(bad.item()) == b_ref
