@@ -349,7 +349,8 @@ static int check_moe(const coli_qtensor *gate, const coli_qtensor *up, const col
         return decline("%s: down [%d][%d][%d] must be [%d][%d][%d]", who, down->n, down->O,
                        down->I, E, D, F);
     const coli_qtensor *all[6] = {gate, up, down, sg, su, sd};
-    const int nsh = (sg != nullptr) + (su != nullptr) + (sd != nullptr || !down);
+    // without a down stack (hidden-only) the shared down matrix is not needed
+    const int nsh = (sg != nullptr) + (su != nullptr) + (down ? (sd != nullptr) : (sg != nullptr));
     if (nsh != 0 && nsh != 3)
         return decline("%s: shared expert needs all of its matrices", who);
     for (int i = 0; i < 6; ++i) {

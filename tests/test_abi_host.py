@@ -190,3 +190,16 @@ def test_fault_injection_declines(lib):
         assert l1 == l0
     finally:
         coli.coli_set_fail_after(-1)
+
+
+def test_moe_hidden_validation(lib):
+    g, u, d = _moe_tensors()
+    ws = coli.coli_moe_workspace_bytes(4, 1, 2, 64, 128, 0)
+    # no shared expert: validation reaches the output check
+    assert coli.coli_moe_hidden(g, u, FAKE_S, 1, FAKE_S, 2, None, None, None, FAKE_Q, ws, 0) == 0
+    assert "h_out" in coli.coli_last_reason(), coli.coli_last_reason()
+    sg, su, _ = _moe_tensors(E=1)
+    assert coli.coli_moe_hidden(g, u, FAKE_S, 1, FAKE_S, 2, sg, None, FAKE_S, FAKE_Q, ws, 0) == 0
+    assert "shared" in coli.coli_last_reason()
+    assert coli.coli_moe_hidden(g, u, FAKE_S, 1, FAKE_S, 2, sg, su, None, FAKE_Q, ws, 0) == 0
+    assert "h_out" in coli.coli_last_reason(), coli.coli_last_reason()
