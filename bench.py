@@ -133,8 +133,6 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timed {args.steps} steps")
-    coli.coli_prof_reset()
-    coli.coli_prof_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -144,9 +142,18 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    coli.coli_prof_enable(False)
     ms = ev0.elapsed_time(ev1) / args.steps
     value = block_bytes / (ms * 1e-3) / 1e9
+
+    # the same steps again with HIP events recorded by the library around
+    # every kernel launch (on the launch stream): per-kernel durations
+    log(f"profiled {args.steps} steps")
+    coli.coli_prof_reset()
+    coli.coli_prof_enable(True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    coli.coli_prof_enable(False)
     kern = {}
     for tag in coli.coli_prof_tags():
         n, tot = coli.coli_prof_read(tag)

@@ -324,7 +324,7 @@ size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shar
     if (E < 1 || S < 1 || K < 1 || F < 1 || Dm < 1)
         return 0;
     if (S <= coli_gemv_max_rows())
-        return moe_decode_ws_bytes(S, K, F, has_shared);
+        return moe_decode_ws_bytes(S, K, F, Dm, has_shared);
     return moe_prefill_ws_bytes(E, S, K, F, Dm, has_shared);
 }
 

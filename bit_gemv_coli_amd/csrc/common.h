@@ -67,7 +67,7 @@ struct MoeArgs {
 };
 int launch_moe_decode(const MoeArgs &a);
 int launch_moe_prefill(const MoeArgs &a);
-size_t moe_decode_ws_bytes(int S, int K, int F, int has_shared);
+size_t moe_decode_ws_bytes(int S, int K, int F, int D, int has_shared);
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared);
 
 // ---------------------------------------------------------------------------
@@ -110,6 +110,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Pointers into global memory (address space 1), so loads through them are
+// global_load (vector-memory counter only) rather than flat loads, which
+// would also hold up the LDS counter.
+#define COLI_GLOBAL __attribute__((address_space(1)))
+
+template <typename T>
+__device__ __forceinline__ T gload(const void *p) {
+    return *(const COLI_GLOBAL T *)(p);
+}
+
 // Packet of codes as loaded by one lane (streamed once: non-temporal loads).
 template <int FMT>
 struct Packet { u32x4 v; };
@@ -119,13 +129,13 @@ struct Packet<3> { u32x2 v; };
 template <int FMT>
 __device__ __forceinline__ Packet<FMT> load_packet(const uint8_t *p) {
     Packet<FMT> k;
-    k.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    k.v = __builtin_nontemporal_load((const COLI_GLOBAL u32x4 *)p);
     return k;
 }
 template <>
 __device__ __forceinline__ Packet<3> load_packet<3>(const uint8_t *p) {
     Packet<3> k;
-    k.v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    k.v = __builtin_nontemporal_load((const COLI_GLOBAL u32x2 *)p);
     return k;
 }
 

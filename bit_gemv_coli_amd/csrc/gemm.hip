@@ -13,8 +13,8 @@ int launch_gemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws
 }
 
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared) {
-    (void)E; (void)D;
-    return moe_decode_ws_bytes(S, K, F, has_shared);
+    (void)E;
+    return moe_decode_ws_bytes(S, K, F, D, has_shared);
 }
 
 int launch_moe_prefill(const MoeArgs &a) {
