@@ -1,0 +1,145 @@
+"""GPU parity of the prefill path (S > 4 input rows): the bf16 matrix-core
+GEMM for coli_qmatmul and the ragged MoE block (routing table, gathered
+inputs, dual gate/up + SiLU, down, combine), against the oracle with the
+bf16 tolerance 4e-3 * sum |w||x| (colibri-strix commit log, "route large
+row-batch matmul_qt GEMMs to the GPU": prefill-sized row batches take a GEMM
+path)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_gemv_coli_amd as coli
+import synthdata as sd
+from gpu_util import TOL_BF16, assert_within, gpu_qmatmul, make_case, need_gpu, qtensor, to_dev
+from oracle import QMat
+from test_gpu_moe import _check_moe, _moe_inputs, _run_gpu
+
+pytestmark = pytest.mark.gpu
+
+# (fmt, O, I, gs, S, n)
+GEMM = [
+    (4, 128, 256, 64, 5, 1), (4, 130, 96, 32, 17, 1), (4, 64, 6144, 128, 33, 1),
+    (4, 200, 320, 64, 64, 2), (4, 48, 512, 256, 100, 1), (4, 257, 2048, 64, 65, 1),
+    (4, 32, 160, 160, 9, 1),
+    (2, 100, 256, 0, 7, 1), (2, 64, 96, 0, 129, 1),
+    (1, 90, 128, 0, 12, 1), (1, 33, 96, 0, 70, 2),
+    (3, 77, 256, 0, 6, 1), (3, 128, 160, 0, 40, 1),
+]
+
+
+@pytest.mark.parametrize("case", GEMM, ids=["fmt{}-O{}-I{}-gs{}-S{}-n{}".format(*c) for c in GEMM])
+def test_qmatmul_prefill(orc, case):
+    need_gpu()
+    fmt, O, I, gs, S, n = case
+    W, x = make_case(fmt, O, I, gs, S, seed=200 + hash(case) % 1000, n=n if n > 1 else None)
+    T = qtensor(W)
+    y = gpu_qmatmul(T, x, n)
+    for e in range(n):
+        y_ref, A = orc.qmatmul(W.expert(e), x)
+        assert_within(y[e], y_ref, A, TOL_BF16, f"{case} expert {e}")
+
+
+def test_qmatmul_prefill_fallback_layouts(orc):
+    """Layouts the matrix cores do not take (odd I, gs % 32 != 0) run the exact
+    fp32 path and still meet the bound."""
+    need_gpu()
+    for fmt, O, I, gs, S in [(4, 20, 130, 64, 9), (4, 16, 96, 16, 6), (2, 9, 33, 0, 12)]:
+        W, x = make_case(fmt, O, I, gs, S, seed=O + I)
+        y = gpu_qmatmul(qtensor(W), x)[0]
+        y_ref, A = orc.qmatmul(W, x)
+        assert_within(y, y_ref, A, TOL_BF16, f"fallback {fmt} {I} {gs}")
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+def test_qmatmul_prefill_dense_544_full(orc, gs):
+    """S = 544 x 6144 x 6144 fmt 4: every output of 24 sampled input rows."""
+    need_gpu()
+    W, x = make_case(4, 6144, 6144, gs, 544, seed=544 + gs)
+    y = gpu_qmatmul(qtensor(W), x)[0]
+    rows = np.sort(sd.rng(1).choice(544, 24, replace=False))
+    y_ref, A = orc.qmatmul(W, x[rows])
+    assert_within(y[rows], y_ref, A, TOL_BF16, f"dense 544 g{gs}")
+    assert np.all(np.isfinite(y))
+
+
+PREFILL = [  # (fmt, S, K, E, D, F, gs, shared)
+    (4, 5, 2, 6, 128, 64, 32, False),
+    (4, 9, 4, 7, 256, 128, 64, True),
+    (4, 40, 8, 16, 192, 160, 32, True),
+    (4, 33, 3, 3, 128, 96, 128, False),
+    (2, 12, 2, 5, 128, 64, 0, True),
+    (1, 7, 3, 4, 96, 64, 0, False),
+    (3, 20, 2, 6, 128, 96, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=["fmt{}-S{}-K{}-E{}-D{}-F{}-gs{}-sh{}".format(*c) for c in PREFILL])
+def test_moe_prefill_small(orc, case):
+    need_gpu()
+    fmt, S, K, E, D, F, gs, shared = case
+    G, U, Dn, sh, x, ids, w = _moe_inputs(300 + hash(case) % 997, fmt, S, K, E, D, F, gs, shared)
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_BF16)
+
+
+def test_moe_prefill_ragged_zipf_invalid(orc):
+    """Zipf-skewed routing (some experts with many rows, many with one or
+    none), out-of-range ids and duplicates."""
+    need_gpu()
+    G, U, Dn, sh, x, ids, w = _moe_inputs(41, 4, 70, 4, 12, 256, 128, 64, True, routing="zipf")
+    ids = ids.copy()
+    ids[3, 1] = 12
+    ids[5, 0] = -1
+    ids[7, 2] = ids[7, 1]
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_BF16)
+
+
+def test_moe_prefill_repeatable_bitwise(orc):
+    need_gpu()
+    G, U, Dn, sh, x, ids, w = _moe_inputs(42, 4, 50, 8, 16, 256, 128, 64, True, routing="zipf")
+    a, _ = _run_gpu(G, U, Dn, sh, x, ids, w, hidden=False)
+    b, _ = _run_gpu(G, U, Dn, sh, x, ids, w, hidden=False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_moe_prefill_config4_full(orc):
+    """Prefill MoE at its real shape: S = 544 tokens, 256 experts, top-8 with
+    Zipf(1.1) popularity, gate/up 2048x6144 and down 6144x2048 fmt 4 gs 128.
+    The pool is drawn on the device; the oracle evaluates 6 sampled tokens
+    (each token's output depends only on its own input and routing) at 256
+    sampled output rows, with the experts those tokens use copied back."""
+    need_gpu()
+    E, D, F, gs, K, S = 256, 6144, 2048, 128, 8, 544
+    r = sd.rng(4)
+    x = sd.gen_x(r, S, D)
+    ids, w = sd.gen_routing_zipf(r, S, K, E, 1.1)
+    gq, gsc = sd.pool_on_device(200, 4, E, F, D, gs)
+    uq, usc = sd.pool_on_device(201, 4, E, F, D, gs)
+    dq, dsc = sd.pool_on_device(202, 4, E, D, F, gs)
+    tg = coli.QTensor(4, gq, gsc, F, D, gs)
+    tu = coli.QTensor(4, uq, usc, F, D, gs)
+    td = coli.QTensor(4, dq, dsc, D, F, gs)
+    xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+    ws_bytes = coli.coli_moe_workspace_bytes(E, S, K, F, D, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((S, D), float("nan"), device="cuda")
+    coli.check(coli.coli_moe_block(tg, tu, td, xd, S, idd, wd, K, None, None, None, out, ws,
+                                   ws_bytes))
+    h = torch.full((S * K, F), float("nan"), device="cuda")
+    coli.check(coli.coli_moe_hidden(tg, tu, xd, S, idd, K, None, None, h, ws, ws_bytes))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    h = h.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    toks = np.sort(sd.rng(5).choice(S, 6, replace=False))
+    used = np.unique(ids[toks])
+    remap = {int(e): i for i, e in enumerate(used)}
+    sel = torch.from_numpy(used.astype(np.int64)).cuda()
+    G = QMat(4, F, D, gs, gq[sel].cpu().numpy(), gsc[sel].cpu().numpy())
+    U = QMat(4, F, D, gs, uq[sel].cpu().numpy(), usc[sel].cpu().numpy())
+    Dn = QMat(4, D, F, gs, dq[sel].cpu().numpy(), dsc[sel].cpu().numpy())
+    local = np.vectorize(remap.get)(ids[toks]).astype(np.int32)
+    rows = np.sort(sd.rng(6).choice(D, 256, replace=False)).astype(np.int32)
+    hsel = h.reshape(S, K, F)[toks].reshape(-1, F)
+    _check_moe(orc, G, U, Dn, None, x[toks], local, w[toks], out[toks], hsel, TOL_BF16, rows=rows)
