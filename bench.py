@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 5 times (reference for the "
+                         "HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -86,6 +89,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     import bit_gemv_coli_amd as coli
     import synthdata as sd
@@ -237,7 +250,145 @@ def side_measurements(coli, sd, np, torch, log):
             log(f"sweep {key}: {us:.2f} us  {gbs:.0f} GB/s")
             del Ts, q, s
     out["gemv_6144x6144_ring"] = sweep
+    out.update(prefill_measurements(coli, sd, np, torch, log, timed))
+    out.update(layer_stream(coli, sd, np, torch, log))
     return out
+
+
+def prefill_measurements(coli, sd, np, torch, log, timed):
+    """S = 544 prefill: the dense 6144x6144 fmt-4 GEMM (compute-bound) and the
+    Zipf(1.1)-routed 256-expert MoE block with gs 128 (HBM-bound: the routed
+    union covers ~250 experts)."""
+    out = {}
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    S = 544
+    for gs in (128, 64):
+        q, s = sd.pool_on_device(30 + gs, 4, 1, 6144, 6144, gs)
+        T = coli.QTensor(4, q[0], s[0], 6144, 6144, gs, n=1)
+        x = torch.randn((S, 6144), device=dev)
+        y = torch.empty((S, 6144), device=dev)
+        us = timed(lambda i: coli.coli_qmatmul(T, x, y, S, st), 20)
+        tf = 2.0 * S * 6144 * 6144 / (us * 1e-6) / 1e12
+        out[f"prefill_dense_544x6144x6144_g{gs}"] = {
+            "us": us, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS}
+        log(f"prefill dense g{gs}: {us:.1f} us  {tf:.1f} TFLOP/s ({100 * tf / BF16_PEAK_TFLOPS:.1f}% of bf16 peak)")
+        del T, q, s
+
+    gs = 128
+    r = sd.rng(4)
+    xh = sd.gen_x(r, S, D)
+    ids, w = sd.gen_routing_zipf(r, S, K, E, 1.1)
+    gq, gsc = sd.pool_on_device(200, 4, E, F, D, gs)
+    uq, usc = sd.pool_on_device(201, 4, E, F, D, gs)
+    dq, dsc = sd.pool_on_device(202, 4, E, D, F, gs)
+    tg = coli.QTensor(4, gq, gsc, F, D, gs)
+    tu = coli.QTensor(4, uq, usc, F, D, gs)
+    td = coli.QTensor(4, dq, dsc, D, F, gs)
+    xd = torch.from_numpy(xh).to(dev)
+    idd = torch.from_numpy(ids).to(dev)
+    wd = torch.from_numpy(w).to(dev)
+    outb = torch.empty((S, D), device=dev)
+    wsb = coli.coli_moe_workspace_bytes(E, S, K, F, D, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    us = timed(lambda i: coli.check(coli.coli_moe_block(tg, tu, td, xd, S, idd, wd, K, None, None,
+                                                        None, outb, ws, wsb, st)), 10)
+    union = int(np.unique(ids).size)
+    flops = 2.0 * S * K * 3 * F * D
+    nbytes = union * (2 * qbytes(4, F, D, gs) + qbytes(4, D, F, gs)) + 2 * S * D * 4 + S * K * 8
+    tf = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    ideal_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)) * 1e6
+    out["prefill_moe_544_zipf1.1_g128"] = {
+        "us": us, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "GBps": gbs,
+        "frac_hbm": gbs / HBM_PEAK_GBS, "union_experts": union, "roofline_us": ideal_us,
+        "frac_roofline": ideal_us / us}
+    log(f"prefill MoE 544 zipf: {us:.1f} us  {tf:.1f} TFLOP/s  {gbs:.0f} GB/s  union {union}  "
+        f"({100 * ideal_us / us:.1f}% of max(F/P, B/BW))")
+    del tg, tu, td, gq, gsc, uq, usc, dq, dsc, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):
+    """75 decode layers (S = 1) back to back in one HIP graph: per layer the
+    q_a 1536x6144, q_b 16384x1536, kv_a 576x6144 and o_proj 6144x16384 GEMVs
+    (each fed a fixed N(0,1) input of its length) and the MoE block with 8
+    routed experts (drawn from a resident pool of 20 per layer) plus one
+    shared expert, all fmt 4 gs 64 -- about 40 GB resident."""
+    dev = "cuda"
+    gs = 64
+    log(f"layer stream: drawing {layers} layers")
+    projs = [(1536, 6144), (16384, 1536), (576, 6144), (6144, 16384)]
+    L = []
+    for l in range(layers):
+        P = [sd.pool_on_device(1000 + 10 * l + i, 4, 1, o, i_, gs) for i, (o, i_) in enumerate(projs)]
+        TP = [coli.QTensor(4, q[0], s[0], o, i_, gs, n=1) for (q, s), (o, i_) in zip(P, projs)]
+        mg = sd.pool_on_device(5000 + 4 * l, 4, pool + 1, F, D, gs)
+        mu = sd.pool_on_device(5001 + 4 * l, 4, pool + 1, F, D, gs)
+        md = sd.pool_on_device(5002 + 4 * l, 4, pool + 1, D, F, gs)
+        tg = coli.QTensor(4, mg[0][:pool], mg[1][:pool], F, D, gs)
+        tu = coli.QTensor(4, mu[0][:pool], mu[1][:pool], F, D, gs)
+        td = coli.QTensor(4, md[0][:pool], md[1][:pool], D, F, gs)
+        sg = coli.QTensor(4, mg[0][pool], mg[1][pool], F, D, gs, n=1)
+        su = coli.QTensor(4, mu[0][pool], mu[1][pool], F, D, gs, n=1)
+        sdn = coli.QTensor(4, md[0][pool], md[1][pool], D, F, gs, n=1)
+        L.append((P, TP, mg, mu, md, tg, tu, td, sg, su, sdn))
+    r = sd.rng(75)
+    routes = [sd.gen_routing_uniform(r, 1, K, pool) for _ in range(layers)]
+    ids = torch.from_numpy(np.stack([a for a, _ in routes])).to(dev)
+    wts = torch.from_numpy(np.stack([b for _, b in routes])).to(dev)
+    xin = {i_: torch.randn((1, i_), device=dev) for _, i_ in projs}
+    xin[D] = torch.randn((1, D), device=dev)
+    outs = {o: torch.empty((1, o), device=dev) for o, _ in projs}
+    mo = torch.empty((1, D), device=dev)
+    wsb = coli.coli_moe_workspace_bytes(pool, 1, K, F, D, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def one_pass():
+        st = torch.cuda.current_stream()
+        for l in range(layers):
+            P, TP, mg, mu, md, tg, tu, td, sg, su, sdn = L[l]
+            for T, (o, i_) in zip(TP, projs):
+                coli.check(coli.coli_qmatmul(T, xin[i_], outs[o], 1, st))
+            coli.check(coli.coli_moe_block(tg, tu, td, xin[D], 1, ids[l], wts[l], K, sg, su, sdn,
+                                           mo, ws, wsb, st))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    a.record(st)
+    for _ in range(passes):
+        graph.replay()
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / passes
+    attn = sum(qbytes(4, o, i_, gs) + (o + i_) * 4 for o, i_ in projs)
+    moe = 9 * (2 * qbytes(4, F, D, gs) + qbytes(4, D, F, gs)) + 2 * D * 4
+    per_layer = attn + moe
+    gbs = layers * per_layer / (ms * 1e-3) / 1e9
+    resident = sum(sum(t.numel() * t.element_size() for t in (x[0], x[1]))
+                   for l in L for x in (*l[0], l[2], l[3], l[4]))
+    log(f"layer stream: {ms * 1e3:.0f} us/pass  {ms * 1e3 / layers:.1f} us/layer  {gbs:.0f} GB/s  "
+        f"resident {resident / 1e9:.1f} GB")
+    res = {"layer_stream_75": {"us_per_pass": ms * 1e3, "us_per_layer": ms * 1e3 / layers,
+                               "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                               "bytes_per_layer": per_layer, "resident_GB": resident / 1e9,
+                               "launches_per_layer": 4 + 3}}
+    del graph, L
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(coli, sd, np, torch, gq, gsc, uq, usc, dq, dsc, x, routes, block_bytes,
