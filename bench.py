@@ -118,6 +118,8 @@ def main():
     tg = coli.QTensor(4, gq, gsc, F, D, GS)
     tu = coli.QTensor(4, uq, usc, F, D, GS)
     td = coli.QTensor(4, dq, dsc, D, F, GS)
+    for t in (tg, tu, td):  # upload-time repack for the matrix-core decode kernels
+        t.pack()
     r = sd.rng(0)
     x = sd.gen_x(r, 1, D)
     NR = 64
@@ -228,6 +230,7 @@ def side_measurements(coli, sd, np, torch, log):
     # config 1: one matrix, back-to-back launches (cache-resident; latency)
     q, s = sd.pool_on_device(7, 4, 1, 1024, 2048, 64)
     T = coli.QTensor(4, q, s, 1024, 2048, 64)
+    T.pack()
     x = torch.randn((1, 2048), device=dev)
     y = torch.empty((1, 1024), device=dev)
     us = timed(lambda i: coli.coli_qmatmul(T, x, y, 1, st), 200)
@@ -241,6 +244,8 @@ def side_measurements(coli, sd, np, torch, log):
             ncopy = max(2, -(-(1 << 30) // mb))
             q, s = sd.pool_on_device(11 + fmt, fmt, ncopy, 6144, 6144, gs)
             Ts = [coli.QTensor(fmt, q[c], s[c], 6144, 6144, gs, n=1) for c in range(ncopy)]
+            for t in Ts:
+                t.pack()
             x = torch.randn((S, 6144), device=dev)
             y = torch.empty((S, 6144), device=dev)
             us = timed(lambda i: coli.coli_qmatmul(Ts[i % ncopy], x, y, S, st), 4 * ncopy)
@@ -324,6 +329,8 @@ def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):
     for l in range(layers):
         P = [sd.pool_on_device(1000 + 10 * l + i, 4, 1, o, i_, gs) for i, (o, i_) in enumerate(projs)]
         TP = [coli.QTensor(4, q[0], s[0], o, i_, gs, n=1) for (q, s), (o, i_) in zip(P, projs)]
+        for t in TP:
+            t.pack()
         mg = sd.pool_on_device(5000 + 4 * l, 4, pool + 1, F, D, gs)
         mu = sd.pool_on_device(5001 + 4 * l, 4, pool + 1, F, D, gs)
         md = sd.pool_on_device(5002 + 4 * l, 4, pool + 1, D, F, gs)
@@ -333,6 +340,8 @@ def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):
         sg = coli.QTensor(4, mg[0][pool], mg[1][pool], F, D, gs, n=1)
         su = coli.QTensor(4, mu[0][pool], mu[1][pool], F, D, gs, n=1)
         sdn = coli.QTensor(4, md[0][pool], md[1][pool], D, F, gs, n=1)
+        for t in (tg, tu, td, sg, su, sdn):
+            t.pack()
         L.append((P, TP, mg, mu, md, tg, tu, td, sg, su, sdn))
     r = sd.rng(75)
     routes = [sd.gen_routing_uniform(r, 1, K, pool) for _ in range(layers)]

@@ -23,7 +23,8 @@ class coli_qtensor(C.Structure):
     _fields_ = [("fmt", C.c_int32), ("n", C.c_int32), ("O", C.c_int32), ("I", C.c_int32),
                 ("gs", C.c_int32), ("ng", C.c_int32), ("row_bytes", C.c_int64),
                 ("q_stride", C.c_int64), ("s_stride", C.c_int64), ("q", C.c_void_p),
-                ("s", C.c_void_p), ("magic", C.c_uint32), ("flags", C.c_uint32)]
+                ("s", C.c_void_p), ("magic", C.c_uint32), ("flags", C.c_uint32),
+                ("pk", C.c_void_p), ("pk_stride", C.c_int64), ("pk_scale_off", C.c_int64)]
 
 
 _lib = None
@@ -50,8 +51,11 @@ def _load():
     sig = {
         "coli_tensor_upload": (i32, [QP, i32, i32, i32, i32, i32, i32, vp, vp]),
         "coli_qmatmul": (i32, [QP, vp, vp, i32, vp]),
+        "coli_packed_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "coli_tensor_pack": (i32, [QP, vp, sz, vp]),
         "coli_gemv_max_rows": (i32, []),
         "coli_set_gemv_max_rows": (i32, [i32]),
+        "coli_set_decode_kernel": (i32, [i32]),
         "coli_dequantize": (i32, [QP, vp, vp]),
         "coli_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "coli_moe_block": (i32, [QP, QP, QP, vp, i32, vp, vp, i32, QP, QP, QP, vp, vp, sz, vp]),
@@ -77,7 +81,8 @@ def _load():
 
 def exported_symbols():
     """Names the binding expects libcoli to export."""
-    return ["coli_tensor_upload", "coli_qmatmul", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
+    return ["coli_tensor_upload", "coli_packed_bytes", "coli_tensor_pack", "coli_qmatmul", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
+            "coli_set_decode_kernel",
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
@@ -115,6 +120,14 @@ def coli_tensor_upload(desc: coli_qtensor, fmt, n, O, I, gs, ng, q, s) -> int:
     return _load().coli_tensor_upload(C.byref(desc), fmt, n, O, I, gs, ng, _ptr(q), _ptr(s))
 
 
+def coli_packed_bytes(fmt, n, O, I, gs) -> int:
+    return _load().coli_packed_bytes(fmt, n, O, I, gs)
+
+
+def coli_tensor_pack(W, packed, nbytes, stream=None) -> int:
+    return _load().coli_tensor_pack(_qp(W), _ptr(packed), nbytes, _stream(stream))
+
+
 def coli_qmatmul(W, x, y, S, stream=None) -> int:
     return _load().coli_qmatmul(_qp(W), _ptr(x), _ptr(y), S, _stream(stream))
 
@@ -125,6 +138,10 @@ def coli_gemv_max_rows() -> int:
 
 def coli_set_gemv_max_rows(s: int) -> int:
     return _load().coli_set_gemv_max_rows(s)
+
+
+def coli_set_decode_kernel(mode: int) -> int:
+    return _load().coli_set_decode_kernel(mode)
 
 
 def coli_dequantize(W, w_out, stream=None) -> int:
@@ -219,6 +236,18 @@ class QTensor:
     @property
     def fmt(self):
         return self.desc.fmt
+
+    def pack(self, stream=None) -> bool:
+        """Attach a packed copy (allocated here with torch) when the format has
+        one; returns whether it did."""
+        import torch
+        d = self.desc
+        nb = coli_packed_bytes(d.fmt, d.n, d.O, d.I, d.gs)
+        if nb == 0:
+            return False
+        self.packed = torch.empty(nb, dtype=torch.uint8, device=self.q.device)
+        check(coli_tensor_pack(self, self.packed, nb, stream), "coli_tensor_pack")
+        return True
 
 
 def check(rc: int, what: str = "call") -> None:

@@ -25,6 +25,19 @@ static thread_local char g_error[512];
 static std::atomic<uint64_t> g_calls{0}, g_declined{0}, g_launches{0};
 static std::atomic<int64_t> g_fail_after{-2};  // -2: not read from env yet
 static std::atomic<int> g_gemv_max{0};
+static std::atomic<int> g_decode_mode{-1};
+
+int decode_kernel_mode() {
+    int v = g_decode_mode.load();
+    if (v < 0) {
+        const char *e = getenv("COLI_DECODE_KERNEL");
+        v = (e && strcmp(e, "valu") == 0) ? 1 : 0;
+        int z = -1;
+        g_decode_mode.compare_exchange_strong(z, v);
+        v = g_decode_mode.load();
+    }
+    return v;
+}
 static int g_notice = -1;
 
 static void notice(const char *what, const char *msg) {
@@ -174,6 +187,14 @@ int coli_gemv_max_rows(void) {
     return v;
 }
 
+int coli_set_decode_kernel(int mode) {
+    if (mode != 0 && mode != 1)
+        return -1;
+    const int old = decode_kernel_mode();
+    g_decode_mode.store(mode);
+    return old;
+}
+
 int coli_set_gemv_max_rows(int s) {
     if (s < 1 || s > 4)
         return 0;
@@ -278,6 +299,28 @@ int coli_tensor_upload(coli_qtensor *t, int fmt, int n, int O, int I, int gs, in
     }
     *t = r;
     return COLI_OK;
+}
+
+size_t coli_packed_bytes(int fmt, int n, int O, int I, int gs) {
+    return packed_bytes(fmt, n, O, I, gs);
+}
+
+int coli_tensor_pack(coli_qtensor *t, void *packed, size_t bytes, void *stream) {
+    if (check_qt(t, "tensor_pack") != COLI_OK)
+        return COLI_DECLINED;
+    const size_t need = packed_bytes(t->fmt, t->n, t->O, t->I, t->gs);
+    if (need == 0)
+        return decline("tensor_pack: no packed form for fmt %d, I=%d, gs=%d (needs fmt 2/4, "
+                       "I %% 32 == 0, gs 32, 64 or a multiple of 128)", t->fmt, t->I, t->gs);
+    if (!(t->flags & QF_FAST))
+        return decline("tensor_pack: codes not 16-byte aligned");
+    if (!packed || !dev_aligned(packed, 256))
+        return decline("tensor_pack: packed buffer NULL or not 256-byte aligned");
+    if (bytes < need)
+        return decline("tensor_pack: packed buffer %zu bytes < %zu needed", bytes, need);
+    if (!gate_call())
+        return COLI_DECLINED;
+    return launch_pack(t, packed, (hipStream_t)stream);
 }
 
 int coli_dequantize(const coli_qtensor *W, float *w_out, void *stream) {

@@ -34,6 +34,7 @@ enum : uint32_t {
     QF_FAST = 1u,     // packet loads allowed: aligned rows, row_bytes % packet == 0
     QF_GROUP32 = 2u,  // fmt 4: gs % 32 == 0 (one scale per 32-input packet)
     QF_GROUP16 = 4u,  // fmt 4: gs % 16 == 0 but not 32 (two scales per packet)
+    QF_PACKED = 8u,   // carries a packed copy (coli_tensor_pack)
 };
 
 constexpr uint32_t QT_MAGIC = 0xC0117E45u;
@@ -68,6 +69,14 @@ struct MoeArgs {
 int launch_moe_decode(const MoeArgs &a);
 int launch_moe_prefill(const MoeArgs &a);
 size_t moe_decode_ws_bytes(int S, int K, int F, int D, int has_shared);
+// matrix-core decode kernels (mgemv.hip); return 1 done, 0 not taken, <0 error
+bool mgemv_ok(const coli_qtensor *W);
+size_t packed_bytes(int fmt, int n, int O, int I, int gs);
+int launch_pack(coli_qtensor *t, void *packed, hipStream_t st);
+int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
+int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp);
+// 0: matrix-core decode kernels where the layout allows, 1: vector-ALU kernels only
+int decode_kernel_mode();
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared);
 
 // ---------------------------------------------------------------------------

@@ -393,6 +393,9 @@ __global__ __launch_bounds__(256) void k_rowdot(RowDotArgs a) {
     }
 }
 
+#ifndef COLI_VALU_WANT_WGS
+#define COLI_VALU_WANT_WGS 1024
+#endif
 // LDS budget for the staged inputs of one workgroup.
 constexpr int LDS_X_BYTES = 32 * 1024;
 
@@ -485,6 +488,13 @@ int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStrea
                            W->row_bytes, W->ng, W->gs > 0 ? W->gs : 1, S);
         return after_launch("gemv_any");
     }
+    if (S <= 4 && decode_kernel_mode() == 0) {
+        const int r = launch_mgemv(W, x, y, S, st);
+        if (r == 1)
+            return COLI_OK;
+        if (r < 0)
+            return COLI_HIP_ERROR;
+    }
     for (int t0 = 0; t0 < S; t0 += 4) {
         const int ns = (S - t0) < 4 ? (S - t0) : 4;
         const float *xb = x + (int64_t)t0 * W->I;
@@ -576,7 +586,7 @@ static int moe_decode_t(const MoeArgs &a, float *h, float *yp) {
         r.S = a.S; r.K = a.K; r.E = a.E;
         r.x_by_pair = 0;
         r.out = h;
-        r.rows_per_wg = rows_per_wg(a.F, P, R, 1024);
+        r.rows_per_wg = rows_per_wg(a.F, P, R, COLI_VALU_WANT_WGS);
         ProfScope ps("moe_gateup_decode", a.st);
         launch_rowdot<FMT, GM, 1, R, 2, EPI_SILU>(r, P, a.st);
         int rc = after_launch("moe_gateup_decode");
@@ -601,13 +611,15 @@ static int moe_decode_t(const MoeArgs &a, float *h, float *yp) {
         if (rc != COLI_OK)
             return rc;
     }
-    {
-        ProfScope ps("moe_combine", a.st);
-        hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((a.D + 255) / 256), (unsigned)a.S),
-                           dim3(256), 0, a.st, yp, a.ids, a.w, a.S, a.K, a.E, a.D, has_sh ? 1 : 0,
-                           a.out);
-        return after_launch("moe_combine");
-    }
+    return COLI_OK;
+}
+
+static int moe_combine(const MoeArgs &a, const float *yp) {
+    ProfScope ps("moe_combine", a.st);
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((a.D + 255) / 256), (unsigned)a.S),
+                       dim3(256), 0, a.st, yp, a.ids, a.w, a.S, a.K, a.E, a.D,
+                       a.sg != nullptr ? 1 : 0, a.out);
+    return after_launch("moe_combine");
 }
 
 int launch_moe_decode(const MoeArgs &a) {
@@ -616,14 +628,26 @@ int launch_moe_decode(const MoeArgs &a) {
     float *h = a.h_out ? a.h_out : (float *)a.ws;
     float *yp = (float *)((char *)a.ws + ((P * a.F * sizeof(float) + 255) / 256) * 256);
     const coli_qtensor *all[6] = {a.gate, a.up, a.down, a.sg, a.su, a.sd};
-    switch (a.gate->fmt) {
-    case 1: return moe_decode_t<1, 0>(a, h, yp);
-    case 2: return moe_decode_t<2, 0>(a, h, yp);
-    case 3: return moe_decode_t<3, 0>(a, h, yp);
-    default:
-        return group_mode(all, 6) == 1 ? moe_decode_t<4, 1>(a, h, yp)
-                                       : moe_decode_t<4, 2>(a, h, yp);
+    int rc = 0;
+    if (decode_kernel_mode() == 0)
+        rc = launch_mgemv_moe(a, h, yp);  // matrix-core kernels where they apply
+    if (rc < 0)
+        return COLI_HIP_ERROR;
+    if (rc == 0) {
+        switch (a.gate->fmt) {
+        case 1: rc = moe_decode_t<1, 0>(a, h, yp); break;
+        case 2: rc = moe_decode_t<2, 0>(a, h, yp); break;
+        case 3: rc = moe_decode_t<3, 0>(a, h, yp); break;
+        default:
+            rc = group_mode(all, 6) == 1 ? moe_decode_t<4, 1>(a, h, yp)
+                                         : moe_decode_t<4, 2>(a, h, yp);
+        }
+        if (rc != COLI_OK)
+            return rc;
     }
+    if (a.out == nullptr || a.down == nullptr)
+        return COLI_OK;
+    return moe_combine(a, yp);
 }
 
 }  // namespace coli

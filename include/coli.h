@@ -87,6 +87,11 @@ typedef struct coli_qtensor {
     const float *s;    /* device scales                                     */
     uint32_t magic;    /* set by coli_tensor_upload                         */
     uint32_t flags;    /* internal: which kernel paths the layout allows    */
+    /* Optional repacked copy (coli_tensor_pack); NULL until packed.  The
+     * matrix-core decode kernels read it instead of q/s. */
+    const void *pk;    /* device: packed codes and scales                   */
+    int64_t pk_stride; /* bytes between matrices in the packed copy         */
+    int64_t pk_scale_off; /* byte offset of the packed scales within pk     */
 } coli_qtensor;
 
 /*
@@ -107,6 +112,32 @@ int coli_tensor_upload(coli_qtensor *t, int fmt, int n, int O, int I, int gs, in
                        const void *q_dev, const float *s_dev);
 
 /*
+ * coli_packed_bytes -- device bytes the repacked copy of a tensor of this
+ * shape needs (0 when the format / layout has no packed form: packing needs
+ * fmt 2 or 4, I % 32 == 0, and for fmt 4 gs of 32, 64 or a multiple of 128).
+ */
+size_t coli_packed_bytes(int fmt, int n, int O, int I, int gs);
+
+/*
+ * coli_tensor_pack -- write a repacked copy of the tensor's codes (and fmt-4
+ * scales) into caller-owned device memory and attach it to the record; an
+ * upload-time layout conversion in the spirit of the pages' upload-time
+ * offset_to_signed_s4 (colibri PR #298, CUDA fmt=4 commit).  Layout: every
+ * 16-row x 128-input tile becomes one contiguous 1 KiB block in the order the
+ * matrix-core decode kernels load it (so each wavefront load is one 1 KiB
+ * request), the tile's group scales follow in 16-row runs; rows and inputs
+ * past O and I are padded with zero-valued codes.  The values are unchanged.
+ *   t         record from coli_tensor_upload (updated on success)
+ *   packed    device buffer of at least coli_packed_bytes(...) bytes, 256-byte
+ *             aligned, owned by the caller, kept alive while t is used
+ * The original q/s must stay valid too (other kernels read them).  Packing is
+ * enqueued on `stream`; calls on other streams must be ordered after it.
+ * Returns COLI_OK, COLI_DECLINED (no packed form, small or misaligned buffer)
+ * or COLI_HIP_ERROR.
+ */
+int coli_tensor_pack(coli_qtensor *t, void *packed, size_t bytes, void *stream);
+
+/*
  * coli_qmatmul -- y = W x for every matrix of the stack
  * (colibri PR #298 commits: fmt 4 folds the group scale in per group, fmt 1-3
  * scale once per row; colibri-strix "route large row-batch matmul_qt GEMMs to
@@ -125,6 +156,13 @@ int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *s
 int coli_gemv_max_rows(void);
 /* Set it (1..4); returns the previous value, or 0 if the value is refused. */
 int coli_set_gemv_max_rows(int s);
+
+/* Kernel family of the fp32 decode path: 0 (default) uses the matrix-core
+ * decode kernels for tensors that carry a packed copy (coli_tensor_pack) and
+ * the vector-ALU kernels elsewhere; 1 uses the vector-ALU kernels everywhere.  Both meet the same 1e-5 * sum |w||x| bound.
+ * Environment: COLI_DECODE_KERNEL=valu.  Returns the previous mode, -1 if
+ * `mode` is refused. */
+int coli_set_decode_kernel(int mode);
 
 /*
  * coli_dequantize -- w_out[e][o][i] = (float)(s * v), the exact product

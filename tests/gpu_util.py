@@ -4,6 +4,8 @@ magnitude-relative tolerances (colibri PR #298, matmul_i4_grouped test
 commit: error is judged against the sum of |terms|, not |result|)."""
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,16 @@ TOL_BF16 = 4e-3   # bf16 matrix-core path: |y - y_ref| <= 4e-3 * sum_i |w||x|
 DEV = "cuda"
 
 
+@contextlib.contextmanager
+def decode_kernels(mode):
+    """Run with the matrix-core (0) or vector-ALU (1) decode kernels."""
+    old = coli.coli_set_decode_kernel(mode)
+    try:
+        yield
+    finally:
+        coli.coli_set_decode_kernel(old)
+
+
 def need_gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU test run without a visible GPU")
@@ -29,12 +41,16 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def qtensor(W: QMat) -> coli.QTensor:
-    """Upload a host QMat (single matrix or stack) and describe it."""
+def qtensor(W: QMat, pack: bool = False) -> coli.QTensor:
+    """Upload a host QMat (single matrix or stack) and describe it; with
+    pack=True also attach the packed copy the matrix-core kernels read."""
     q = to_dev(W.q.view(np.uint8))
     s = to_dev(W.s.astype(np.float32))
     n = W.q.shape[0] if W.q.ndim == 3 else 1
-    return coli.QTensor(W.fmt, q, s, W.O, W.I, W.gs if W.fmt == 4 else 0, n=n)
+    T = coli.QTensor(W.fmt, q, s, W.O, W.I, W.gs if W.fmt == 4 else 0, n=n)
+    if pack:
+        T.pack()
+    return T
 
 
 def gpu_qmatmul(T: coli.QTensor, x: np.ndarray, n: int = 1) -> np.ndarray:

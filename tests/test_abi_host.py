@@ -203,3 +203,30 @@ def test_moe_hidden_validation(lib):
     assert "shared" in coli.coli_last_reason()
     assert coli.coli_moe_hidden(g, u, FAKE_S, 1, FAKE_S, 2, sg, su, None, FAKE_Q, ws, 0) == 0
     assert "h_out" in coli.coli_last_reason(), coli.coli_last_reason()
+
+
+@pytest.mark.parametrize("fmt,O,I,gs,expect", [
+    (4, 2048, 6144, 64, 2048 // 16 * 48 * (1024 + 2 * 64)),
+    (4, 6144, 2048, 128, 6144 // 16 * 16 * (1024 + 64)),
+    (4, 33, 4160, 32, 3 * 33 * (1024 + 4 * 64)),
+    (2, 100, 256, 0, ((7 * 2 * 1024 + 255) // 256) * 256),
+    (4, 16, 96, 48, 0), (4, 16, 96, 16, 0), (1, 16, 128, 0, 0), (3, 16, 128, 0, 0),
+    (4, 16, 100, 64, 0),
+])
+def test_packed_bytes(lib, fmt, O, I, gs, expect):
+    assert coli.coli_packed_bytes(fmt, 1, O, I, gs) == expect
+    assert coli.coli_packed_bytes(fmt, 3, O, I, gs) == 3 * expect
+
+
+def test_pack_declines_before_device(lib):
+    _, _, l0 = coli.coli_stats()
+    rc, W = upload(4, 1, 64, 96, 48, 2)
+    assert coli.coli_tensor_pack(W, FAKE_Q, 1 << 20, 0) == 0 and "packed form" in coli.coli_last_reason()
+    rc, W = upload(4, 1, 64, 256, 64, 4)
+    need = coli.coli_packed_bytes(4, 1, 64, 256, 64)
+    assert coli.coli_tensor_pack(W, FAKE_Q, need - 1, 0) == 0 and "bytes" in coli.coli_last_reason()
+    assert coli.coli_tensor_pack(W, FAKE_Q + 64, need, 0) == 0 and "aligned" in coli.coli_last_reason()
+    rc, W = upload(4, 1, 64, 256, 64, 4, q=FAKE_Q + 8)
+    assert coli.coli_tensor_pack(W, FAKE_Q, need, 0) == 0 and "aligned" in coli.coli_last_reason()
+    _, _, l1 = coli.coli_stats()
+    assert l1 == l0

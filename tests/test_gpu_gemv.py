@@ -11,8 +11,8 @@ import torch
 
 import bit_gemv_coli_amd as coli
 import synthdata as sd
-from gpu_util import (TOL_BF16, TOL_FP32, assert_within, gpu_qmatmul, make_case, need_gpu,
-                      qtensor, to_dev)
+from gpu_util import (TOL_BF16, TOL_FP32, assert_within, decode_kernels, gpu_qmatmul, make_case,
+                      need_gpu, qtensor, to_dev)
 from oracle import QMat
 
 pytestmark = pytest.mark.gpu
@@ -60,23 +60,30 @@ def test_dequant_subnormal_and_extreme_scales(orc):
     assert np.array_equal(w.cpu().numpy()[0].view(np.uint32), orc.dequant_f32(W).view(np.uint32))
 
 
+KERNELS = pytest.mark.parametrize("kmode", [0, 1], ids=["mfma", "valu"])
+
+
+@KERNELS
 @pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
-def test_qmatmul_small(orc, case):
+def test_qmatmul_small(orc, case, kmode):
     need_gpu()
     fmt, O, I, gs, S, n = case
     W, x = make_case(fmt, O, I, gs, S, seed=1 + hash(case) % 1000, n=n if n > 1 else None)
-    T = qtensor(W)
-    y = gpu_qmatmul(T, x, n)
+    T = qtensor(W, pack=(kmode == 0))
+    with decode_kernels(kmode):
+        y = gpu_qmatmul(T, x, n)
     tol = TOL_FP32 if S <= coli.coli_gemv_max_rows() else TOL_BF16
     for e in range(n):
         y_ref, A = orc.qmatmul(W.expert(e), x)
         assert_within(y[e], y_ref, A, tol, f"{case} expert {e}")
 
 
-def test_qmatmul_nibble_extremes_and_outliers(orc):
+@KERNELS
+def test_qmatmul_nibble_extremes_and_outliers(orc, kmode):
     """Rows of all 0x00 / all 0xFF bytes (-8 / +7), zero rows (0x88), and
     outlier-heavy rows (one large group scale), S = 1..4."""
     need_gpu()
+    coli.coli_set_decode_kernel(kmode)
     r = sd.rng(77)
     O, I, gs = 8, 2048, 64
     q = sd.gen_codes(r, 4, O, I)
@@ -89,7 +96,7 @@ def test_qmatmul_nibble_extremes_and_outliers(orc):
     s[5, :] = 1e-3
     s[5, 3] = 1e3
     W = QMat(4, O, I, gs, q, s)
-    T = qtensor(W)
+    T = qtensor(W, pack=(kmode == 0))
     for S in (1, 2, 3, 4):
         x = sd.gen_x(r, S, I)
         x[:, 100] = 1e4
@@ -97,19 +104,23 @@ def test_qmatmul_nibble_extremes_and_outliers(orc):
         y_ref, A = orc.qmatmul(W, x)
         assert_within(y, y_ref, A, TOL_FP32, f"extremes S={S}")
         assert np.all(y[:, 2] == 0.0)
+    coli.coli_set_decode_kernel(0)
 
 
+@KERNELS
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
-def test_qmatmul_one_hot_columns_exact(orc, S):
+def test_qmatmul_one_hot_columns_exact(orc, S, kmode):
     """x = e_i picks column i: the GPU result equals s*v exactly."""
     need_gpu()
     W, _ = make_case(4, 64, 2048, 64, 1, seed=5)
-    T = qtensor(W)
+    T = qtensor(W, pack=(kmode == 0))
+    coli.coli_set_decode_kernel(kmode)
     cols = [0, 31, 32, 1000, 2047][:S]
     x = np.zeros((S, 2048), np.float32)
     for t, c in enumerate(cols):
         x[t, c] = 1.0
     y = gpu_qmatmul(T, x)[0]
+    coli.coli_set_decode_kernel(0)
     w = orc.dequant_f32(W)
     for t, c in enumerate(cols):
         assert np.array_equal(y[t], w[:, c]), (S, c)
@@ -127,23 +138,26 @@ def test_qmatmul_config1_full(orc):
 SWEEP = [(1, 0), (2, 0), (3, 0), (4, 64), (4, 128)]
 
 
+@KERNELS
 @pytest.mark.parametrize("fmt,gs", SWEEP, ids=[f"fmt{f}-gs{g}" for f, g in SWEEP])
 @pytest.mark.parametrize("S", [1, 4])
-def test_qmatmul_format_sweep_full(orc, fmt, gs, S):
+def test_qmatmul_format_sweep_full(orc, fmt, gs, S, kmode):
     """Format sweep at full size: O = I = 6144, S in {1, 4}."""
     need_gpu()
     W, x = make_case(fmt, 6144, 6144, gs, S, seed=10 + fmt + gs + S)
-    y = gpu_qmatmul(qtensor(W), x)[0]
+    with decode_kernels(kmode):
+        y = gpu_qmatmul(qtensor(W, pack=(kmode == 0)), x)[0]
     y_ref, A = orc.qmatmul(W, x)
     assert_within(y, y_ref, A, TOL_FP32, f"sweep fmt {fmt} gs {gs} S {S}")
 
 
+@pytest.mark.parametrize("pack", [True, False], ids=["packed", "plain"])
 @pytest.mark.parametrize("O,I", [(1536, 6144), (16384, 1536), (576, 6144), (6144, 16384)])
-def test_qmatmul_attention_projection_shapes(orc, O, I):
+def test_qmatmul_attention_projection_shapes(orc, O, I, pack):
     """The decode layer's projections (q_a, q_b, kv_a, o_proj), fmt 4 g64."""
     need_gpu()
     W, x = make_case(4, O, I, 64, 1, seed=O + I)
-    y = gpu_qmatmul(qtensor(W), x)[0]
+    y = gpu_qmatmul(qtensor(W, pack=pack), x)[0]
     y_ref, A = orc.qmatmul(W, x)
     assert_within(y, y_ref, A, TOL_FP32, f"proj {O}x{I}")
 
@@ -151,7 +165,7 @@ def test_qmatmul_attention_projection_shapes(orc, O, I):
 def test_qmatmul_repeatable_bitwise(orc):
     need_gpu()
     W, x = make_case(4, 3000, 6144, 64, 3, seed=9)
-    T = qtensor(W)
+    T = qtensor(W, pack=True)
     a = gpu_qmatmul(T, x)
     b = gpu_qmatmul(T, x)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
@@ -191,3 +205,19 @@ def test_fault_injection_writes_nothing(orc):
         assert torch.all(y == 123.0)
     finally:
         coli.coli_set_fail_after(-1)
+
+
+def test_pack_leaves_other_paths_unchanged(orc):
+    """A packed tensor still serves the prefill GEMM and the vector-ALU kernels
+    from its original codes; results with and without the packed copy agree
+    with the oracle."""
+    need_gpu()
+    W, x = make_case(4, 100, 1024, 128, 9, seed=12)
+    T = qtensor(W, pack=True)
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(gpu_qmatmul(T, x)[0], y_ref, A, TOL_BF16, "prefill on a packed tensor")
+    for S in (1, 3):
+        yr, Ar = orc.qmatmul(W, x[:S])
+        with decode_kernels(1):
+            assert_within(gpu_qmatmul(T, x[:S])[0], yr, Ar, TOL_FP32, "valu on a packed tensor")
+        assert_within(gpu_qmatmul(T, x[:S])[0], yr, Ar, TOL_FP32, "mfma on a packed tensor")

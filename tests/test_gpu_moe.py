@@ -16,7 +16,7 @@ import torch
 
 import bit_gemv_coli_amd as coli
 import synthdata as sd
-from gpu_util import TOL_BF16, TOL_FP32, assert_within, need_gpu, qtensor, to_dev
+from gpu_util import TOL_BF16, TOL_FP32, assert_within, decode_kernels, need_gpu, qtensor, to_dev
 from oracle import QMat
 
 pytestmark = pytest.mark.gpu
@@ -43,11 +43,11 @@ def _moe_inputs(seed, fmt, S, K, E, D, F, gs, shared, routing="uniform"):
     return G, U, Dn, sh, x, ids, w
 
 
-def _run_gpu(G, U, Dn, sh, x, ids, w, hidden=True):
+def _run_gpu(G, U, Dn, sh, x, ids, w, hidden=True, pack=True):
     S, K = ids.shape
     E, F, D = G.n, G.O, G.I
-    tg, tu, td = qtensor(G), qtensor(U), qtensor(Dn)
-    ts = [qtensor(m) for m in sh] if sh is not None else [None, None, None]
+    tg, tu, td = qtensor(G, pack), qtensor(U, pack), qtensor(Dn, pack)
+    ts = [qtensor(m, pack) for m in sh] if sh is not None else [None, None, None]
     xd, idd, wd = to_dev(x), to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32))
     ws_bytes = coli.coli_moe_workspace_bytes(E, S, K, F, D, sh is not None)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -137,16 +137,19 @@ DECODE = [  # (fmt, S, K, E, D, F, gs, shared)
 ]
 
 
+@pytest.mark.parametrize("kmode", [0, 1], ids=["mfma", "valu"])
 @pytest.mark.parametrize("case", DECODE, ids=["fmt{}-S{}-K{}-E{}-D{}-F{}-gs{}-sh{}".format(*c) for c in DECODE])
-def test_moe_decode_small(orc, case):
+def test_moe_decode_small(orc, case, kmode):
     need_gpu()
     fmt, S, K, E, D, F, gs, shared = case
     G, U, Dn, sh, x, ids, w = _moe_inputs(hash(case) % 997, fmt, S, K, E, D, F, gs, shared)
-    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    with decode_kernels(kmode):
+        out, h = _run_gpu(G, U, Dn, sh, x, ids, w, pack=(kmode == 0))
     _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
 
 
-def test_moe_decode_duplicates_invalid_and_zero_weights(orc):
+@pytest.mark.parametrize("kmode", [0, 1], ids=["mfma", "valu"])
+def test_moe_decode_duplicates_invalid_and_zero_weights(orc, kmode):
     need_gpu()
     G, U, Dn, sh, x, ids, w = _moe_inputs(31, 4, 3, 4, 8, 128, 64, 64, True)
     ids = ids.copy()
@@ -155,7 +158,8 @@ def test_moe_decode_duplicates_invalid_and_zero_weights(orc):
     ids[1, 2] = 8              # out of range: left out
     ids[2, 0] = -5             # out of range: left out
     w[2, 3] = 0.0              # zero weight
-    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    with decode_kernels(kmode):
+        out, h = _run_gpu(G, U, Dn, sh, x, ids, w, pack=(kmode == 0))
     _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
 
 
@@ -184,6 +188,8 @@ def test_moe_decode_config2_full(orc):
     tg = coli.QTensor(4, gq, gsc, F, D, gs)
     tu = coli.QTensor(4, uq, usc, F, D, gs)
     td = coli.QTensor(4, dq, dsc, D, F, gs)
+    for t in (tg, tu, td):
+        assert t.pack()
     xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
     ws_bytes = coli.coli_moe_workspace_bytes(E, 1, K, F, D, 0)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
