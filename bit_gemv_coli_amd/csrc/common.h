@@ -74,7 +74,7 @@ bool mgemv_ok(const coli_qtensor *W);
 size_t packed_bytes(int fmt, int n, int O, int I, int gs);
 int launch_pack(coli_qtensor *t, void *packed, hipStream_t st);
 int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
-int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp);
+int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt);
 // 0: matrix-core decode kernels where the layout allows, 1: vector-ALU kernels only
 int decode_kernel_mode();
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared);

@@ -530,6 +530,7 @@ int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStrea
 //   launch 2  yp[p] = D_e h[p]
 //   launch 3  out[s] = sum_k w[s][k] yp[s*K+k] (+ yp[shared s]), ascending k,
 //             one thread per output, no atomics: reruns are bit-identical.
+//             (The matrix-core path folds launch 3 into launch 2.)
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ yp,
@@ -541,12 +542,23 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ y
     const int o = blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= D)
         return;
+    // all K loads of a chunk are issued before the sums (ascending k)
     float acc = 0.f;
-    for (int k = 0; k < K; ++k) {
-        const int64_t p = (int64_t)s * K + k;
-        const int e = ids[p];
-        if (e >= 0 && e < E)
-            acc = fmaf(w[p], yp[p * D + o], acc);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        float v[8], wk[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = min(k0 + u, K - 1);
+            const int64_t p = (int64_t)s * K + k;
+            const int e = ids[p];
+            ok[u] = (k0 + u < K) && e >= 0 && e < E;
+            wk[u] = w[p];
+            v[u] = yp[p * D + o];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc = ok[u] ? fmaf(wk[u], v[u], acc) : acc;
     }
     if (has_shared)
         acc += yp[((int64_t)S * K + s) * D + o];
@@ -557,7 +569,8 @@ size_t moe_decode_ws_bytes(int S, int K, int F, int D, int has_shared) {
     const size_t P = (size_t)S * K + (has_shared ? S : 0);
     const size_t hb = ((P * F * sizeof(float) + 255) / 256) * 256;
     const size_t yb = ((P * D * sizeof(float) + 255) / 256) * 256;
-    return hb + yb;
+    const size_t cb = (((size_t)(D + 15) / 16 * sizeof(int) + 255) / 256) * 256;  // counters
+    return hb + yb + cb;
 }
 
 static void fill_pair_args(RowDotArgs &a, const coli_qtensor *m0, const coli_qtensor *m1,
@@ -627,13 +640,16 @@ int launch_moe_decode(const MoeArgs &a) {
     const size_t P = (size_t)a.S * a.K + (has_sh ? a.S : 0);
     float *h = a.h_out ? a.h_out : (float *)a.ws;
     float *yp = (float *)((char *)a.ws + ((P * a.F * sizeof(float) + 255) / 256) * 256);
+    int *cnt = (int *)((char *)yp + ((P * a.D * sizeof(float) + 255) / 256) * 256);
     const coli_qtensor *all[6] = {a.gate, a.up, a.down, a.sg, a.su, a.sd};
     int rc = 0;
     if (decode_kernel_mode() == 0)
-        rc = launch_mgemv_moe(a, h, yp);  // matrix-core kernels where they apply
+        rc = launch_mgemv_moe(a, h, yp, cnt);  // matrix-core kernels, combine folded in
     if (rc < 0)
         return COLI_HIP_ERROR;
-    if (rc == 0) {
+    if (rc == 1)
+        return COLI_OK;
+    {
         switch (a.gate->fmt) {
         case 1: rc = moe_decode_t<1, 0>(a, h, yp); break;
         case 2: rc = moe_decode_t<2, 0>(a, h, yp); break;

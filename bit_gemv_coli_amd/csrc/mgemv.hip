@@ -93,7 +93,71 @@ struct MgArgs {
     int Sy;
     int kseg;   // inputs per LDS segment (multiple of 128)
     int nseg;
+    // MoE down with the top-k combine folded in (cnt != nullptr): arrival
+    // counters per workgroup column, routing weights, final output [S][O]
+    int *cnt;
+    int ncnt;   // counters the gate/up launch clears
+    const float *wts;
+    float *yfin;
+    int has_sh;
 };
+
+// Partial rows that another workgroup sums are stored and loaded with
+// device-scope relaxed atomics: those go to the point of coherence shared by
+// all XCDs (their L2s are not coherent with each other for plain accesses), so
+// no cache-wide write-back or invalidate is needed.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After a workgroup has stored its partial rows of one 16*TPW-row column, it
+// counts itself in; the last of the column's gridDim.y workgroups writes
+// out[s][row] = sum_k w[s][k] * yp[s*K+k][row] (+ yp[shared s][row]) for the
+// column: k ascending, ids outside [0,E) skipped, one thread per output.
+// Arrival order only decides which workgroup sums, never the order of the
+// sum, so reruns are bit-identical.
+template <int TPW>
+__device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(a.cnt + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.y - 1;
+    __syncthreads();
+    if (!last)
+        return;
+    constexpr int ROWS = 16 * TPW;
+    const int O = a.O, K = a.K;
+    for (int idx = threadIdx.x; idx < ROWS * a.S; idx += 256) {
+        const int s = idx / ROWS, row = blockIdx.x * ROWS + idx % ROWS;
+        if (row >= O)
+            continue;
+        float acc = 0.f;
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float v[8], wk[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = min(k0 + u, K - 1);
+                const int64_t p = (int64_t)s * K + k;
+                const int e = gload<int32_t>(a.ids + p);
+                ok[u] = (k0 + u < K) && e >= 0 && e < a.E;
+                wk[u] = gload<float>(a.wts + p);
+                v[u] = load_coherent(a.out + p * O + row);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                acc = ok[u] ? fmaf(wk[u], v[u], acc) : acc;
+        }
+        if (a.has_sh)
+            acc += load_coherent(a.out + ((int64_t)a.S * K + s) * O + row);
+        a.yfin[(int64_t)s * O + row] = acc;
+    }
+}
 
 #ifndef COLI_MG_NBK
 #define COLI_MG_NBK 4
@@ -164,9 +228,18 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     }
     const int tile = blockIdx.x * TPW + tile_w;
     const int row0 = tile * 16;
+    if constexpr (EPI == MG_SILU) {
+        if (a.cnt != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+            for (int i = tid; i < a.ncnt; i += 256)
+                __hip_atomic_store(a.cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (!valid) {
         if (EPI == MG_SILU && ks == 0 && lane < 16 && row0 + lane < O)
             a.out[p * O + row0 + lane] = 0.f;
+        if constexpr (EPI == MG_PART) {
+            if (a.cnt != nullptr)
+                mg_combine_tail<TPW>(a);
+        }
         return;
     }
 
@@ -177,12 +250,15 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     const int lg = (CB == 1) ? 0 : (CB == 2 ? (j >> 1) : j);
     const bool aact = (ar < AROWS) && (acb == lg);
     // this lane's 16 bytes of every packed 1 KiB tile block, and its scale runs
+    // (a wavefront past the last tile of a ragged column reads the last tile
+    // again and writes nothing)
+    const int tile_ld = min(tile, (O + 15) / 16 - 1);
     const uint8_t *qtile[NMAT];
     const float *stile[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-        qtile[m] = pkm[m] + (int64_t)tile * a.nkb * 1024 + 16 * lane;
-        stile[m] = (const float *)(pkm[m] + a.pk_scale_off) + (int64_t)tile * a.nkb * a.cbs * 16 + n;
+        qtile[m] = pkm[m] + (int64_t)tile_ld * a.nkb * 1024 + 16 * lane;
+        stile[m] = (const float *)(pkm[m] + a.pk_scale_off) + (int64_t)tile_ld * a.nkb * a.cbs * 16 + n;
     }
     // C rows of this lane: 4*j .. 4*j+3 (j doubles as the C row quarter)
     const int cr0 = 4 * j;
@@ -359,33 +435,38 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[((wave * NMAT + m) * 16 + cr0 + i) * 16 + n] = acc[m][i];
     __syncthreads();
-    if (ks != 0 || lane >= 16 * NT)
-        return;
     const int t = lane >> 4, nn = lane & 15;
     const int row = row0 + nn;
-    if (row >= O)
-        return;
-    float v[NMAT];
+    if (ks == 0 && lane < 16 * NT && row < O) {
+        float v[NMAT];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        float sum = 0.f;
-        for (int w2 = 0; w2 < KS; ++w2)
+        for (int m = 0; m < NMAT; ++m) {
+            float sum = 0.f;
+            for (int w2 = 0; w2 < KS; ++w2)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-                    sum += red[(((tile_w * KS + w2) * NMAT + m) * 16 + cb * 2 * NT + 2 * t + hl) * 16 + nn];
-        if (!GROUPED)
-            sum *= gload<float>(sc[m] + row);
-        v[m] = sum;
+                    for (int hl = 0; hl < 2; ++hl)
+                        sum += red[(((tile_w * KS + w2) * NMAT + m) * 16 + cb * 2 * NT + 2 * t + hl) * 16 + nn];
+            if (!GROUPED)
+                sum *= gload<float>(sc[m] + row);
+            v[m] = sum;
+        }
+        if constexpr (EPI == MG_SILU) {
+            const float g = v[0], u = v[NMAT - 1];
+            a.out[p * O + row] = (g / (1.0f + expf(-g))) * u;
+        } else if constexpr (EPI == MG_PART) {
+            if (a.cnt != nullptr)
+                store_coherent(a.out + p * O + row, v[0]);
+            else
+                a.out[p * O + row] = v[0];
+        } else {
+            a.out[(p * a.Sy + t) * O + row] = v[0];
+        }
     }
-    if constexpr (EPI == MG_SILU) {
-        const float g = v[0], u = v[NMAT - 1];
-        a.out[p * O + row] = (g / (1.0f + expf(-g))) * u;
-    } else if constexpr (EPI == MG_PART) {
-        a.out[p * O + row] = v[0];
-    } else {
-        a.out[(p * a.Sy + t) * O + row] = v[0];
+    if constexpr (EPI == MG_PART) {
+        if (a.cnt != nullptr)
+            mg_combine_tail<TPW>(a);
     }
 }
 
@@ -604,9 +685,11 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     return after_launch("mgemv") == COLI_OK ? 1 : -1;
 }
 
-// Decode MoE stages on the matrix cores: gate/up + SiLU (dual) and down per
-// pair.  Returns 0 when not taken.
-int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp) {
+// Decode MoE block on the matrix cores: gate/up + SiLU (dual), then down per
+// pair with the weighted top-k combine done by the last workgroup of each row
+// column (cnt: one arrival counter per column, cleared by the gate/up launch).
+// Returns 1 when the whole block was launched, 0 when not taken.
+int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
     const coli_qtensor *all[6] = {m.gate, m.up, m.down, m.sg, m.su, m.sd};
     for (const coli_qtensor *t : all)
         if (t && !mgemv_ok(t))
@@ -629,6 +712,10 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp) {
         a.ids = m.ids;
         a.S = m.S; a.K = m.K; a.E = m.E;
         a.out = h;
+        if (m.out != nullptr && m.down != nullptr) {
+            a.cnt = cnt;
+            a.ncnt = (m.D + 15) / 16;
+        }
         ProfScope ps("moe_gateup_decode", m.st);
         if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP>(cb, a, P, m.st)
                 : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP>(cb, a, P, m.st)))
@@ -649,6 +736,10 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp) {
         a.ids = m.ids;
         a.S = m.S; a.K = m.K; a.E = m.E;
         a.out = yp;
+        a.cnt = cnt;
+        a.wts = m.w;
+        a.yfin = m.out;
+        a.has_sh = has_sh ? 1 : 0;
         ProfScope ps("moe_down_decode", m.st);
         if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN>(cb, a, P, m.st)
                 : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN>(cb, a, P, m.st)))

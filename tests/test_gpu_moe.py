@@ -134,6 +134,8 @@ DECODE = [  # (fmt, S, K, E, D, F, gs, shared)
     (1, 3, 2, 4, 160, 64, 0, True),
     (3, 2, 4, 6, 128, 64, 0, True),
     (3, 4, 2, 3, 96, 160, 0, False),
+    (2, 3, 4, 6, 224, 64, 0, True),    # 14 down tiles: a ragged last row column
+    (4, 2, 5, 7, 352, 96, 64, True),   # 22 down tiles
 ]
 
 
