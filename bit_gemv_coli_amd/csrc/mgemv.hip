@@ -8,26 +8,32 @@
 //
 // Why matrix cores for a bandwidth-bound GEMV: at 8 TB/s an int4 GEMV has to
 // retire ~14e12 weights/s, and converting codes to floats one by one on the
-// vector ALUs costs ~2.5-3.5 instructions per weight -- close to all of the
-// VALU issue budget.  Here each 32-bit word of 8 codes becomes four packed
-// fp16 pairs of the exact integers (q-8) or 16*(q-8) in 9 VALU instructions
-// (one shift, four v_and_or_b32 with the 1024 magic exponent, four
-// v_pk_add_f16), and v_mfma_f32_16x16x32_f16 does the multiply-add.
-//
-// Precision: the inputs are split as x * 2^e = hi + lo with hi, lo in fp16
-// (e a per-input-row power of two putting max|x| just below 2^15), so the
-// represented input is within 2^-22 of x relative; products with the exact
-// integer weights are exact, accumulation is fp32, the group scale is applied
-// in fp32 once per 128 inputs.  The error stays far inside 1e-5 * sum |w||x|.
+// vector ALUs takes most of the VALU issue budget.  Here the products are
+// exact integer products on v_mfma_i32_16x16x64_i8:
+//   weights  the packed copy holds each code as the two's-complement nibble
+//            v = q - 8 (the pages' upload-time offset_to_signed_s4).  For a
+//            word of 8 nibbles, w & 0xF0F0F0F0 is 16*v of the odd inputs as
+//            four int8 and (w << 4) & 0xF0F0F0F0 is 16*v of the even inputs:
+//            two 16-byte B operands from 12 VALU instructions per 32 codes.
+//   inputs   per (input row, 128-input block) a power of two 2^e brings
+//            max|x| into [2^29, 2^30); X = trunc(x * 2^e) is an int32 within
+//            2^-29 max|x| 2^e of x 2^e, and X = d0 + 2^8 d1 + 2^16 d2 + 2^24 d3
+//            with signed byte digits: the bytes of (X + 0x808080) XOR
+//            0x808080.  The digits, moved into one row per digit, are the
+//            int8 A operand.
+//   sums     exact in int32 per 128-input block (|sum| < 2^22); the group
+//            scale, 2^-e, the digit weight and 1/16 are applied in fp32.
+// The error stays far inside 1e-5 * sum |w||x|.
 //
 // Layout of one matrix-core step (16 weight rows x 128 inputs):
 //   lane l: weight row n = l % 16, input quarter j = l / 16; it loads the 16
-//   code bytes of row n at inputs [32j, 32j+32) of the block (one fully used
-//   64-byte segment per row and 4 lanes).  Its 4 words feed 4 MFMAs (word m
-//   covers inputs 32j+8m .. +8).  The MFMA's B operand is those weights; the
-//   A operand rows are (group-in-block, input row, hi/lo) combinations of the
-//   inputs read from LDS, zero where the lane's inputs belong to another
-//   group, so one MFMA sums each group separately into its own output row.
+//   code bytes of row n at inputs [32j, 32j+32) of the block (one 1 KiB
+//   request per wavefront in the packed copy).  Its even and odd inputs form
+//   the B operands of two MFMAs.  A row r of a set = (combination c of group-
+//   in-block and input row, digit r % 4) with c = 4 * set + r / 4; an A lane
+//   whose inputs belong to another group than its row's reads zeros, so each
+//   group's sum lands in its own output rows.  C rows 4j .. 4j+3 of a lane are
+//   the four digits of combination 4 * set + j.
 #include <string.h>
 
 #include <algorithm>
@@ -36,39 +42,31 @@
 
 namespace coli {
 
-typedef _Float16 f16_t;
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4m __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-    return r;
+// 16*v of the odd / even inputs of a word of 8 two's-complement nibbles
+__device__ __forceinline__ uint32_t odd_x16(uint32_t w) { return w & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t even_x16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+
+// int32 -> four signed byte digits, X = d0 + 2^8 d1 + 2^16 d2 + 2^24 d3
+// (|X| < 2^30): byte i of (X + 0x808080) is d_i + 128 for i < 3
+__device__ __forceinline__ uint32_t digits_of(float xs) {
+    return ((uint32_t)(int)xs + 0x808080u) ^ 0x808080u;
 }
 
-// 8 codes (one word; inputs 0..7, low nibble first) -> B operand slots
-// [i0, i4, i1, i5, i2, i6, i3, i7] holding q-8 (even slots of pairs 0 and 2)
-// and 16*(q-8) (pairs 1 and 3).
-__device__ __forceinline__ f16x8 codes_to_f16(uint32_t w, uint32_t magic) {
-    const uint32_t w8 = w >> 8;
-    const uint32_t p0 = and_or(w, 0x000F000Fu, magic);
-    const uint32_t p1 = and_or(w, 0x00F000F0u, magic);
-    const uint32_t p2 = and_or(w8, 0x000F000Fu, magic);
-    const uint32_t p3 = and_or(w8, 0x00F000F0u, magic);
-    const f16x2 o1 = {(f16_t)-1032.0f, (f16_t)-1032.0f};   // 1024 + 8
-    const f16x2 o16 = {(f16_t)-1152.0f, (f16_t)-1152.0f};  // 1024 + 16*8
-    const f16x2 h0 = __builtin_bit_cast(f16x2, p0) + o1;
-    const f16x2 h1 = __builtin_bit_cast(f16x2, p1) + o16;
-    const f16x2 h2 = __builtin_bit_cast(f16x2, p2) + o1;
-    const f16x2 h3 = __builtin_bit_cast(f16x2, p3) + o16;
-    return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+// 4x4 byte transpose: out[d] byte b = byte d of in[b]
+__device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                           uint32_t out[4]) {
+    // v_perm_b32 selects bytes of {S0 (bytes 4-7), S1 (bytes 0-3)}
+    const uint32_t ab0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+    const uint32_t ab1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+    const uint32_t cd0 = __builtin_amdgcn_perm(d, c, 0x05010400u);
+    const uint32_t cd1 = __builtin_amdgcn_perm(d, c, 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(cd0, ab0, 0x05040100u);  // a0 b0 c0 d0
+    out[1] = __builtin_amdgcn_perm(cd0, ab0, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(cd1, ab1, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(cd1, ab1, 0x07060302u);
 }
-
-// Input slot of element w (0..7) of an 8-block, and whether its weight comes
-// out multiplied by 16 (then the input is stored divided by 16).
-__device__ __forceinline__ int slot_of(int w) { return w < 4 ? 2 * w : 2 * (w - 4) + 1; }
-__device__ __forceinline__ bool times16(int w) { return (w & 1) != 0; }
 
 enum { MG_Y = 0, MG_SILU = 1, MG_PART = 2 };
 
@@ -159,9 +157,6 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
     }
 }
 
-#ifndef COLI_MG_NBK
-#define COLI_MG_NBK 4
-#endif
 #ifndef COLI_MG_KS_GATEUP
 #define COLI_MG_KS_GATEUP 2
 #endif
@@ -171,8 +166,14 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 #ifndef COLI_MG_KS_DENSE
 #define COLI_MG_KS_DENSE 4
 #endif
-constexpr int MG_NBK = COLI_MG_NBK;  // 128-input blocks requested together per wavefront
-constexpr int MG_ZERO_BYTES = MG_NBK * 256 + 64;
+// 128-input blocks requested together per wavefront: one quad, whose group
+// scales sit together in the packed copy
+constexpr int MG_NBK = 4;
+// zero A operand (32 bytes) for lanes whose inputs belong to another group
+constexpr int MG_ZERO_BYTES = 64;
+
+// LDS bytes of one k_mgemv launch (digits, zero block, reduction, factors)
+__host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3) / 4; }
 
 // NT input rows per tile (1..4); CB groups per 128-input block (1, 2, 4);
 // KS wavefronts share one 16-row tile along the inputs; NMAT matrices (gate
@@ -180,19 +181,21 @@ constexpr int MG_ZERO_BYTES = MG_NBK * 256 + 64;
 template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS>
 __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     constexpr int TPW = 4 / KS;
-    constexpr int AROWS = CB * 2 * NT;  // live A rows (<= 16)
-    static_assert(AROWS <= 16, "too many A rows");
+    constexpr int NCOMBO = CB * NT;          // (group-in-block, input row) combinations
+    constexpr int NSET = mg_nset(CB, NT);    // A-row sets of 4 combinations x 4 digits
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile_w = wave / KS, ks = wave % KS;
     const int I = a.I, O = a.O;
     const int KSEG = a.kseg;
 
-    // LDS: [NT][2][KSEG] fp16 inputs | zero block | reduction [4][NMAT][16][16] f32 | misc
-    f16_t *xs = (f16_t *)smem;
-    char *zero = smem + (size_t)NT * 2 * KSEG * 2;
+    // LDS: digits [NT][4][KSEG] int8 | zero block | reduction [4][NMAT][NSET][16][16] f32 |
+    //      exponent factors [NT][KSEG/128]
+    char *xs = smem;
+    char *zero = smem + (size_t)NT * 4 * KSEG;
     float *red = (float *)(zero + MG_ZERO_BYTES);
-    float *misc = red + 4 * NMAT * 256;
+    float *xfac = red + 4 * NMAT * NSET * 256;
+    const int fstride = KSEG / 128;
 
     // --- which matrix, which inputs ---------------------------------------
     const int64_t p = blockIdx.y;
@@ -244,86 +247,109 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     }
 
     // --- lane roles ----------------------------------------------------------
-    const int n = lane & 15, j = lane >> 4;         // B: weight row, input quarter
-    const int ar = lane & 15;                        // A row
-    const int acb = ar / (2 * NT), at = (ar % (2 * NT)) / 2, ahl = ar & 1;
-    const int lg = (CB == 1) ? 0 : (CB == 2 ? (j >> 1) : j);
-    const bool aact = (ar < AROWS) && (acb == lg);
+    const int n = lane & 15, j = lane >> 4;                   // B: weight row, input quarter
+    const int lg = (CB == 1) ? 0 : (CB == 2 ? (j >> 1) : j);  // group slot of the lane's inputs
+    // A row n of set st: combination c = 4*st + n/4 = (slot c / NT, input row
+    // c % NT), digit n % 4; inactive lanes read the zero block (step 0)
+    int aoff[NSET], astep[NSET];
+    // C rows 4j .. 4j+3: the digits of combination 4*st + j
+    int ccb[NSET], ct[NSET];
+#pragma unroll
+    for (int st = 0; st < NSET; ++st) {
+        const int c = st * 4 + (n >> 2);
+        const bool act = c < NCOMBO && c / NT == lg;
+        aoff[st] = act ? (((c % NT) * 4 + (n & 3)) * KSEG + 32 * j) : (int)(zero - xs);
+        astep[st] = act ? 128 : 0;
+        const int cr = min(st * 4 + j, NCOMBO - 1);
+        ccb[st] = cr / NT;
+        ct[st] = cr % NT;
+    }
     // this lane's 16 bytes of every packed 1 KiB tile block, and its scale runs
     // (a wavefront past the last tile of a ragged column reads the last tile
     // again and writes nothing)
     const int tile_ld = min(tile, (O + 15) / 16 - 1);
+    const int nkq = (a.nkb + 3) / 4;
     const uint8_t *qtile[NMAT];
-    const float *stile[NMAT];
+    const float *squad[NMAT];  // row n's scales of quad 0: 4 blocks x CB groups
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
         qtile[m] = pkm[m] + (int64_t)tile_ld * a.nkb * 1024 + 16 * lane;
-        stile[m] = (const float *)(pkm[m] + a.pk_scale_off) + (int64_t)tile_ld * a.nkb * a.cbs * 16 + n;
+        squad[m] = (const float *)(pkm[m] + a.pk_scale_off) + ((int64_t)tile_ld * nkq * 16 + n) * 4 * CB;
     }
-    // C rows of this lane: 4*j .. 4*j+3 (j doubles as the C row quarter)
-    const int cr0 = 4 * j;
-    const int ccb0 = min(cr0, AROWS - 1) / (2 * NT);
-    const int ccb1 = min(cr0 + 2, AROWS - 1) / (2 * NT);
     const int kpad = (I + 127) / 128 * 128;
-    const uint32_t magic = 0x64006400u;
 
-    float acc[NMAT][4];
+    float acc[NSET][NMAT][4];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int st = 0; st < NSET; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][i] = 0.f;
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[st][m][q] = 0.f;
 
-    // exponent factors 2^-e per (input row, 128-input block) of the segment
-    float *xfac = misc;  // [NT][kseg/128]
-    const int fstride = KSEG / 128;
-
-    // requests for one batch of 128-input blocks (codes and group scales);
+    // requests for one quad of 128-input blocks (codes and group scales);
     // two batches alternate so one is in flight while the other is computed
     struct Batch {
         u32x4 cw[MG_NBK][NMAT];
-        float s0[MG_NBK][NMAT], s1[MG_NBK][NMAT];
+        f32x4 sq[NMAT][GROUPED ? CB : 1];  // scales of the quad, [block][group] order
     };
     Batch bA, bB;
+    // kbg: first block of a quad (a multiple of 4)
     auto load_batch = [&](Batch &bt, int kbg, int kb_last) {
-        auto &cw = bt.cw;
-        auto &s0 = bt.s0;
-        auto &s1 = bt.s1;
 #pragma unroll
         for (int i = 0; i < MG_NBK; ++i) {
             const int kglob = min(kbg + i, kb_last);
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                cw[i][m] = __builtin_nontemporal_load(
+            for (int m = 0; m < NMAT; ++m)
+                bt.cw[i][m] = __builtin_nontemporal_load(
                     (const COLI_GLOBAL u32x4 *)(qtile[m] + (int64_t)kglob * 1024));
-                if constexpr (GROUPED) {
-                    const float *sb = stile[m] + (int64_t)kglob * a.cbs * 16;
-                    s0[i][m] = gload<float>(sb + ccb0 * 16);
-                    s1[i][m] = (((2 * NT) % 4) == 0) ? s0[i][m] : gload<float>(sb + ccb1 * 16);
-                } else {
-                    s0[i][m] = s1[i][m] = 1.0f;
-                }
-            }
         }
+        if constexpr (GROUPED) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int c = 0; c < CB; ++c)
+                    bt.sq[m][c] = gload<f32x4>(squad[m] + (int64_t)(kbg / 4) * 64 * CB + 4 * c);
+        }
+    };
+    // group scale of block i of the quad, group slot cb (0 .. CB-1)
+    auto pick = [&](const Batch &bt, int m, int i, int cb) -> float {
+        if constexpr (!GROUPED) {
+            return 1.0f;
+        } else if constexpr (CB == 1) {
+            return bt.sq[m][0][i];
+        } else if constexpr (CB == 2) {
+            const f32x4 v = bt.sq[m][i / 2];
+            return cb ? v[2 * (i % 2) + 1] : v[2 * (i % 2)];
+        } else {
+            const f32x4 v = bt.sq[m][i];
+            return cb >= 2 ? (cb == 3 ? v[3] : v[2]) : (cb == 1 ? v[1] : v[0]);
+        }
+    };
+    // blocks [kb_beg, kb_end) of a segment of nkbs blocks for wavefront ks:
+    // whole quads split evenly over the KS wavefronts
+    auto share = [&](int nkbs, int &kb_beg, int &kb_end) {
+        const int nq = (nkbs + 3) / 4;
+        kb_beg = 4 * ((ks * nq) / KS);
+        kb_end = min(4 * (((ks + 1) * nq) / KS), nkbs);
     };
 
     // the first batch is requested before the inputs are staged
-    int seg0_beg, seg0_end;
     {
-        const int klen = min(KSEG, kpad);
-        const int nkb = klen / 128;
-        seg0_beg = (ks * nkb) / KS;
-        seg0_end = ((ks + 1) * nkb) / KS;
-        if (seg0_beg < seg0_end)
-            load_batch(bA, seg0_beg, seg0_end - 1);
+        int b0, e0;
+        share(min(KSEG, kpad) / 128, b0, e0);
+        if (b0 < e0)
+            load_batch(bA, b0, e0 - 1);
     }
 
     for (int sgi = 0; sgi < a.nseg; ++sgi) {
         const int k0 = sgi * KSEG;
         const int klen = min(KSEG, kpad - k0);
         const int nkb = klen / 128;
-        // ---- stage this segment's inputs: hi / lo fp16 in slot order, one
-        //      power-of-two exponent per (input row, 128-input block): 16
-        //      consecutive threads own one block, each 8 inputs -------------
+        // ---- stage this segment's inputs as four int8 digits under one power
+        //      of two per (input row, 128-input block): 16 consecutive threads
+        //      own one block, each 8 inputs (one word of a 32-input quarter);
+        //      digit row d holds, per quarter, the even inputs' bytes then the
+        //      odd inputs' bytes ---------------------------------------------
         __syncthreads();
         {
             constexpr int UN = 4;
@@ -347,29 +373,42 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
                 for (int u = 0; u < UN; ++u) {
                     const int idx = base + u * 256 + tid;
                     float mx = 0.f;
+                    bool bad = false;  // NaN or beyond 3e38 (fmaxf would drop a NaN)
 #pragma unroll
-                    for (int w = 0; w < 8; ++w) mx = fmaxf(mx, fabsf(v[u][w]));
+                    for (int w = 0; w < 8; ++w) {
+                        mx = fmaxf(mx, fabsf(v[u][w]));
+                        bad |= !(fabsf(v[u][w]) <= 3.0e38f);
+                    }
+                    if (bad)
+                        mx = __builtin_inff();
 #pragma unroll
                     for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+                    // 2^e2 * max|x| in [2^29, 2^30) (tiny blocks: e2 <= 126 keeps
+                    // 2^-e2 normal); non-finite blocks give a NaN factor
                     int e2 = 0;
                     if (mx > 0.f && mx <= 3.0e38f) {
                         (void)frexpf(mx, &e2);  // mx < 2^e2
-                        e2 = 15 - e2;
+                        e2 = min(30 - e2, 126);
                     }
                     if (idx < NT * nb8) {
                         const int t = idx / nb8, b8 = idx % nb8;
-                        f16x8 hv, lv;
+                        uint32_t wd[8];
 #pragma unroll
-                        for (int w = 0; w < 8; ++w) {
-                            const float vs = ldexpf(v[u][w], e2 - (times16(w) ? 4 : 0));
-                            const f16_t h = (f16_t)vs;
-                            hv[slot_of(w)] = h;
-                            lv[slot_of(w)] = (f16_t)(vs - (float)h);
+                        for (int w = 0; w < 8; ++w)
+                            wd[w] = (mx <= 3.0e38f) ? digits_of(ldexpf(v[u][w], e2)) : 0u;
+                        // byte b of the even word: input 2b of the 8; odd word: 2b+1
+                        uint32_t ev[4], od[4];
+                        transpose4(wd[0], wd[2], wd[4], wd[6], ev);
+                        transpose4(wd[1], wd[3], wd[5], wd[7], od);
+                        char *dst = xs + t * 4 * KSEG + (b8 >> 2) * 32 + (b8 & 3) * 4;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            *reinterpret_cast<uint32_t *>(dst + d * KSEG) = ev[d];
+                            *reinterpret_cast<uint32_t *>(dst + d * KSEG + 16) = od[d];
                         }
-                        *reinterpret_cast<f16x8 *>(&xs[(t * 2 + 0) * KSEG + b8 * 8]) = hv;
-                        *reinterpret_cast<f16x8 *>(&xs[(t * 2 + 1) * KSEG + b8 * 8]) = lv;
                         if ((b8 & 15) == 0)
-                            xfac[t * fstride + b8 / 16] = ldexpf(1.0f, -e2);
+                            xfac[t * fstride + b8 / 16] =
+                                (mx <= 3.0e38f) ? ldexpf(1.0f, -e2) : __builtin_nanf("");
                     }
                 }
             }
@@ -379,38 +418,39 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
         __syncthreads();
 
         // ---- this wavefront's share of the segment's 128-input blocks ------
-        const int kb_beg = (ks * nkb) / KS, kb_end = ((ks + 1) * nkb) / KS;
-        const char *abase = (const char *)&xs[(at * 2 + ahl) * KSEG + 32 * j];
-        // token of each of this lane's C rows (rows cr0, cr0+1 / cr0+2, cr0+3)
-        const int ct0 = (min(cr0, AROWS - 1) % (2 * NT)) / 2;
-        const int ct1 = (min(cr0 + 2, AROWS - 1) % (2 * NT)) / 2;
+        int kb_beg, kb_end;
+        share(nkb, kb_beg, kb_end);
 
         auto compute_batch = [&](Batch &bt, int kb) {
-            // inactive lanes read the zero block (it covers a whole batch)
-            const char *ap = aact ? abase + kb * 256 : zero;
 #pragma unroll
             for (int i = 0; i < MG_NBK; ++i) {
                 if (kb + i >= kb_end)
                     break;
-                f16x8 av[4];
+                i32x4 a0[NSET], a1[NSET];
+                float f[NSET];
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm)
-                    av[mm] = *reinterpret_cast<const f16x8 *>(ap + i * 256 + 16 * mm);
-                const float f0 = xfac[ct0 * fstride + kb + i];
-                const float f1 = xfac[ct1 * fstride + kb + i];
+                for (int st = 0; st < NSET; ++st) {
+                    const char *ap = xs + aoff[st] + (kb + i) * astep[st];
+                    a0[st] = *reinterpret_cast<const i32x4 *>(ap);
+                    a1[st] = *reinterpret_cast<const i32x4 *>(ap + 16);
+                    f[st] = xfac[ct[st] * fstride + kb + i];
+                }
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
                     const u32x4 w = bt.cw[i][m];
-                    f32x4m c = {0.f, 0.f, 0.f, 0.f};
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[0], codes_to_f16(w.x, magic), c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[1], codes_to_f16(w.y, magic), c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[2], codes_to_f16(w.z, magic), c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[3], codes_to_f16(w.w, magic), c, 0, 0, 0);
-                    const float g0 = bt.s0[i][m] * f0, g1 = bt.s1[i][m] * f1;
-                    acc[m][0] = fmaf(g0, c[0], acc[m][0]);
-                    acc[m][1] = fmaf(g0, c[1], acc[m][1]);
-                    acc[m][2] = fmaf(g1, c[2], acc[m][2]);
-                    acc[m][3] = fmaf(g1, c[3], acc[m][3]);
+                    const i32x4 be = {(int)even_x16(w.x), (int)even_x16(w.y), (int)even_x16(w.z),
+                                      (int)even_x16(w.w)};
+                    const i32x4 bo = {(int)odd_x16(w.x), (int)odd_x16(w.y), (int)odd_x16(w.z),
+                                      (int)odd_x16(w.w)};
+#pragma unroll
+                    for (int st = 0; st < NSET; ++st) {
+                        i32x4 c = {0, 0, 0, 0};
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[st], be, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[st], bo, c, 0, 0, 0);
+                        const float g = pick(bt, m, i, ccb[st]) * f[st];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[st][m][q] = fmaf(g, (float)c[q], acc[st][m][q]);
+                    }
                 }
             }
         };
@@ -429,11 +469,14 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
         }
     }
 
-    // --- reduce: KS wavefronts x (group, hi/lo) rows -> one value per (row, input row)
+    // --- reduce: KS wavefronts x group slots x digits -> one value per (row, input row)
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int st = 0; st < NSET; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[((wave * NMAT + m) * 16 + cr0 + i) * 16 + n] = acc[m][i];
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red[(((wave * NMAT + m) * NSET + st) * 16 + 4 * j + q) * 16 + n] = acc[st][m][q];
     __syncthreads();
     const int t = lane >> 4, nn = lane & 15;
     const int row = row0 + nn;
@@ -444,10 +487,13 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
             float sum = 0.f;
             for (int w2 = 0; w2 < KS; ++w2)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int hl = 0; hl < 2; ++hl)
-                        sum += red[(((tile_w * KS + w2) * NMAT + m) * 16 + cb * 2 * NT + 2 * t + hl) * 16 + nn];
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int c = cb * NT + t;
+                    const float *rr =
+                        &red[(((tile_w * KS + w2) * NMAT + m) * NSET + c / 4) * 256 + (c % 4) * 64 + nn];
+                    sum += ((rr[0] + rr[16] * 0x1p8f) + rr[32] * 0x1p16f) + rr[48] * 0x1p24f;
+                }
+            sum *= 0.0625f;  // the weights entered as 16 * (q - 8)
             if (!GROUPED)
                 sum *= gload<float>(sc[m] + row);
             v[m] = sum;
@@ -503,7 +549,8 @@ static PackGeom pack_geom(int fmt, int O, int I, int gs) {
     g.cbs = cbs_of(fmt, gs);
     g.code_bytes = (int64_t)g.rt * g.nkb * 1024;
     g.scale_off = g.code_bytes;
-    const int64_t sb = (fmt == 4) ? (int64_t)g.rt * g.nkb * g.cbs * 16 * 4 : 0;
+    const int64_t nkq = (g.nkb + 3) / 4;
+    const int64_t sb = (fmt == 4) ? (int64_t)g.rt * nkq * 16 * 4 * g.cbs * 4 : 0;
     g.stride = (g.code_bytes + sb + 255) / 256 * 256;
     return g;
 }
@@ -515,7 +562,8 @@ size_t packed_bytes(int fmt, int n, int O, int I, int gs) {
 }
 
 // packed codes: tile block (e, rt, kb) = 1 KiB, lane l = 16*j + r holds row
-// 16*rt + r, inputs kb*128 + 32*j .. +32 (16 bytes); padding codes 0x88 (= 0)
+// 16*rt + r, inputs kb*128 + 32*j .. +32 (16 bytes) as two's-complement
+// nibbles q - 8 (code XOR 8); padding 0
 __global__ __launch_bounds__(256) void k_pack_codes(const uint8_t *__restrict__ q, int64_t rb,
                                                     int64_t q_stride, int n, int O, int I, int rt,
                                                     int nkb, int64_t stride,
@@ -532,37 +580,45 @@ __global__ __launch_bounds__(256) void k_pack_codes(const uint8_t *__restrict__ 
         const int r = l & 15, j = l >> 4;
         const int row = tr * 16 + r;
         const int k = kb * 128 + 32 * j;
-        u32x4 v = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-        if (row < O && k < I)
-            v = gload<u32x4>(q + (int64_t)e * q_stride + (int64_t)row * rb + k / 2);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < O && k < I) {
+            const u32x4 c = gload<u32x4>(q + (int64_t)e * q_stride + (int64_t)row * rb + k / 2);
+            v = u32x4{c.x ^ 0x88888888u, c.y ^ 0x88888888u, c.z ^ 0x88888888u, c.w ^ 0x88888888u};
+        }
         *reinterpret_cast<u32x4 *>(pk + (int64_t)e * stride + ((int64_t)tr * nkb + kb) * 1024 + 16 * l) = v;
     }
 }
 
-// packed fmt-4 scales: for (e, rt, kb) a run of cbs x 16 floats: slot cb, row r
-// holds s[16*rt + r][group of the 128-input block's slot cb]; padding 0
+// packed fmt-4 scales: for (e, rt, quad kq of 4 blocks, row r) a run of
+// 4 x cbs floats, [block i][slot cb] = s[16*rt + r][group of slot cb of block
+// 4*kq + i]; one lane reads its row's run for a whole quad.  Padding 0.
 __global__ __launch_bounds__(256) void k_pack_scales(const float *__restrict__ s, int64_t s_stride,
                                                      int ng, int gs, int n, int O, int rt, int nkb,
                                                      int cbs, int64_t stride, int64_t scale_off,
                                                      uint8_t *__restrict__ pk) {
-    const int64_t total = (int64_t)n * rt * nkb * cbs * 16;
+    const int nkq = (nkb + 3) / 4;
+    const int64_t total = (int64_t)n * rt * nkq * 16 * 4 * cbs;
     for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total;
          c += (int64_t)gridDim.x * 256) {
-        const int r = (int)(c % 16);
-        int64_t t = c / 16;
+        int64_t t = c;
         const int cb = (int)(t % cbs);
         t /= cbs;
-        const int kb = (int)(t % nkb);
-        t /= nkb;
+        const int i = (int)(t % 4);
+        t /= 4;
+        const int r = (int)(t % 16);
+        t /= 16;
+        const int kq = (int)(t % nkq);
+        t /= nkq;
         const int tr = (int)(t % rt);
         const int e = (int)(t / rt);
         const int row = tr * 16 + r;
+        const int kb = 4 * kq + i;
         const int g = (cbs == 1) ? (kb * 128) / gs : kb * cbs + cb;
         float v = 0.f;
-        if (row < O && g < ng)
+        if (row < O && kb < nkb && g < ng)
             v = gload<float>(s + (int64_t)e * s_stride + (int64_t)row * ng + g);
         float *dst = (float *)(pk + (int64_t)e * stride + scale_off);
-        dst[(((int64_t)tr * nkb + kb) * cbs + cb) * 16 + r] = v;
+        dst[c - (int64_t)e * ((int64_t)rt * nkq * 16 * 4 * cbs)] = v;
     }
 }
 
@@ -579,7 +635,7 @@ int launch_pack(coli_qtensor *t, void *packed, hipStream_t st) {
         if (rc != COLI_OK) return rc;
     }
     if (t->fmt == 4) {
-        const int64_t total = (int64_t)t->n * g.rt * g.nkb * g.cbs * 16;
+        const int64_t total = (int64_t)t->n * g.rt * ((g.nkb + 3) / 4) * 16 * 4 * g.cbs;
         const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
         ProfScope ps("pack", st);
         hipLaunchKernelGGL(k_pack_scales, dim3(blocks), dim3(256), 0, st, t->s, t->s_stride, t->ng,
@@ -602,13 +658,13 @@ bool mgemv_ok(const coli_qtensor *W) {
 
 static int cb_of(const coli_qtensor *W) { return cbs_of(W->fmt, W->gs); }
 
-static void plan_lds(int NT, int NMAT, int I, int &kseg, int &nseg, size_t &bytes) {
+static void plan_lds(int NT, int CB, int NMAT, int I, int &kseg, int &nseg, size_t &bytes) {
     const int kpad = (I + 127) / 128 * 128;
-    const int cap = (48 * 1024) / (NT * 2 * 2);          // inputs per segment
-    kseg = cap / 128 * 128;
+    const int cap = (48 * 1024) / (NT * 4);  // inputs per segment (4 digit bytes each)
+    kseg = cap / 512 * 512;
     if (kseg > kpad) kseg = kpad;
-    nseg = (kpad + kseg - 1) / kseg;
-    bytes = (size_t)NT * 2 * kseg * 2 + MG_ZERO_BYTES + 4 * NMAT * 256 * 4 +
+    nseg = (kpad + kseg - 1) / kseg;  // segments hold whole quads (kseg % 512 == 0)
+    bytes = (size_t)NT * 4 * kseg + MG_ZERO_BYTES + (size_t)4 * NMAT * mg_nset(CB, NT) * 256 * 4 +
             (size_t)NT * (kseg / 128) * 4 + 64;
 }
 
@@ -634,7 +690,7 @@ static MgArgs mg_args_for(const coli_qtensor *W) {
 template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS>
 static void mg_launch(MgArgs a, int groups, hipStream_t st) {
     size_t lds;
-    plan_lds(NT, NMAT, a.I, a.kseg, a.nseg, lds);
+    plan_lds(NT, CB, NMAT, a.I, a.kseg, a.nseg, lds);
     constexpr int TPW = 4 / KS;
     const int tiles = (a.O + 15) / 16;
     const dim3 grid((unsigned)((tiles + TPW - 1) / TPW), (unsigned)groups);
@@ -645,12 +701,8 @@ template <int NT, bool GROUPED, int NMAT, int EPI, int KS>
 static int mg_dispatch_cb(int cb, const MgArgs &a, int groups, hipStream_t st) {
     switch (cb) {
     case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1;
-    case 2:
-        if constexpr (NT <= 4) { mg_launch<NT, 2, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1; }
-        return 0;
-    default:
-        if constexpr (NT <= 2) { mg_launch<NT, 4, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1; }
-        return 0;
+    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1;
+    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1;
     }
 }
 
@@ -660,8 +712,6 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     if (!mgemv_ok(W) || S < 1 || S > 4)
         return 0;
     const int cb = cb_of(W);
-    if (cb * 2 * S > 16)
-        return 0;
     MgArgs a = mg_args_for(W);
     a.x = x;
     a.ldx = W->I;

@@ -125,8 +125,10 @@ size_t coli_packed_bytes(int fmt, int n, int O, int I, int gs);
  * offset_to_signed_s4 (colibri PR #298, CUDA fmt=4 commit).  Layout: every
  * 16-row x 128-input tile becomes one contiguous 1 KiB block in the order the
  * matrix-core decode kernels load it (so each wavefront load is one 1 KiB
- * request), the tile's group scales follow in 16-row runs; rows and inputs
- * past O and I are padded with zero-valued codes.  The values are unchanged.
+ * request) holding the codes as two's-complement nibbles q - 8; the group
+ * scales follow, one run per (tile, 4 blocks, row) so a lane fetches a whole
+ * batch's scales at once; rows and inputs past O and I are padded with zero
+ * weights.  The represented weights are unchanged.
  *   t         record from coli_tensor_upload (updated on success)
  *   packed    device buffer of at least coli_packed_bytes(...) bytes, 256-byte
  *             aligned, owned by the caller, kept alive while t is used

@@ -208,7 +208,7 @@ def test_moe_hidden_validation(lib):
 @pytest.mark.parametrize("fmt,O,I,gs,expect", [
     (4, 2048, 6144, 64, 2048 // 16 * 48 * (1024 + 2 * 64)),
     (4, 6144, 2048, 128, 6144 // 16 * 16 * (1024 + 64)),
-    (4, 33, 4160, 32, 3 * 33 * (1024 + 4 * 64)),
+    (4, 33, 4160, 32, 3 * 33 * 1024 + 3 * 9 * 16 * 4 * 4 * 4),  # scales in whole quads
     (2, 100, 256, 0, ((7 * 2 * 1024 + 255) // 256) * 256),
     (4, 16, 96, 48, 0), (4, 16, 96, 16, 0), (1, 16, 128, 0, 0), (3, 16, 128, 0, 0),
     (4, 16, 100, 64, 0),

@@ -221,3 +221,19 @@ def test_pack_leaves_other_paths_unchanged(orc):
         with decode_kernels(1):
             assert_within(gpu_qmatmul(T, x[:S])[0], yr, Ar, TOL_FP32, "valu on a packed tensor")
         assert_within(gpu_qmatmul(T, x[:S])[0], yr, Ar, TOL_FP32, "mfma on a packed tensor")
+
+
+@KERNELS
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")], ids=["nan", "inf"])
+def test_qmatmul_nonfinite_input_propagates(orc, kmode, bad):
+    """A NaN or inf input makes every output of its input row non-finite (as
+    in the oracle, where NaN*w and inf*0 are NaN); other rows stay exact."""
+    need_gpu()
+    W, x = make_case(4, 40, 512, 64, 2, seed=21)
+    x[0, 300] = bad
+    with decode_kernels(kmode):
+        y = gpu_qmatmul(qtensor(W, pack=(kmode == 0)), x)[0]
+    y_ref, A = orc.qmatmul(W, x)
+    assert not np.isfinite(y_ref[0]).any()
+    assert not np.isfinite(y[0]).any()
+    assert_within(y[1], y_ref[1], A[1], TOL_FP32, "finite row")
