@@ -48,7 +48,7 @@ def src_hash(paths):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = ["bit_gemv_coli_amd/csrc/gemv.hip", "bit_gemv_coli_amd/csrc/common.h"]
+KERNEL_SOURCES = ["bit_gemv_coli_amd/csrc/mgemv.hip", "bit_gemv_coli_amd/csrc/common.h"]
 
 
 def traffic_from_profiles(kernel_tag):

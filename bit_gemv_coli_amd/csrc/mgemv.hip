@@ -119,6 +119,7 @@ __device__ __forceinline__ float load_coherent(const float *p) {
 // sum, so reruns are bit-identical.
 template <int TPW>
 __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
+    const int nth = blockDim.x;
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
     __syncthreads();
@@ -130,7 +131,7 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
         return;
     constexpr int ROWS = 16 * TPW;
     const int O = a.O, K = a.K;
-    for (int idx = threadIdx.x; idx < ROWS * a.S; idx += 256) {
+    for (int idx = threadIdx.x; idx < ROWS * a.S; idx += nth) {
         const int s = idx / ROWS, row = blockIdx.x * ROWS + idx % ROWS;
         if (row >= O)
             continue;
@@ -157,20 +158,35 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
     }
 }
 
+// launch shapes: KS wavefronts along the inputs of one 16-row tile, NW
+// wavefronts per workgroup (NW / KS tiles); measured best for the decode MoE
+// block: gate/up 2 x 4, down 1 x 4
 #ifndef COLI_MG_KS_GATEUP
 #define COLI_MG_KS_GATEUP 2
+#endif
+#ifndef COLI_MG_NW_GATEUP
+#define COLI_MG_NW_GATEUP 4
 #endif
 #ifndef COLI_MG_KS_DOWN
 #define COLI_MG_KS_DOWN 1
 #endif
+#ifndef COLI_MG_NW_DOWN
+#define COLI_MG_NW_DOWN 4
+#endif
 #ifndef COLI_MG_KS_DENSE
 #define COLI_MG_KS_DENSE 4
+#endif
+#ifndef COLI_MG_NW_DENSE
+#define COLI_MG_NW_DENSE 4
 #endif
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
 constexpr int MG_NBK = 4;
-// zero A operand (32 bytes) for lanes whose inputs belong to another group
-constexpr int MG_ZERO_BYTES = 64;
+// buffer resource word 3 for raw (untyped) buffer loads; reads past
+// num_records return zeros
+constexpr int MG_RSRC_W3 = 0x00020000;
+// load aux bits: nontemporal (streamed once)
+constexpr int MG_AUX_NT = 2;
 
 // LDS bytes of one k_mgemv launch (digits, zero block, reduction, factors)
 __host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3) / 4; }
@@ -178,24 +194,27 @@ __host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3)
 // NT input rows per tile (1..4); CB groups per 128-input block (1, 2, 4);
 // KS wavefronts share one 16-row tile along the inputs; NMAT matrices (gate
 // and up share their rows).
-template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS>
-__global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
-    constexpr int TPW = 4 / KS;
+template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW>
+__global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
+    static_assert(NW % KS == 0, "whole tiles per workgroup");
+    constexpr int TPW = NW / KS;
+    constexpr int NTH = NW * 64;
     constexpr int NCOMBO = CB * NT;          // (group-in-block, input row) combinations
     constexpr int NSET = mg_nset(CB, NT);    // A-row sets of 4 combinations x 4 digits
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile_w = wave / KS, ks = wave % KS;
     const int I = a.I, O = a.O;
     const int KSEG = a.kseg;
 
-    // LDS: digits [NT][4][KSEG] int8 | zero block | reduction [4][NMAT][NSET][16][16] f32 |
+    // LDS: digits [NT][4][KSEG] int8 | zero row [KSEG] | reduction [4][NMAT][NSET][16][16] f32 |
     //      exponent factors [NT][KSEG/128]
     char *xs = smem;
     char *zero = smem + (size_t)NT * 4 * KSEG;
-    float *red = (float *)(zero + MG_ZERO_BYTES);
-    float *xfac = red + 4 * NMAT * NSET * 256;
-    const int fstride = KSEG / 128;
+    float *red = (float *)(zero + KSEG);
+    float *xfac = red + NW * NMAT * NSET * 256;
+    const int fstride = (KSEG / 128 + 3) & ~3;  // whole quads: one 16-byte read per batch
 
     // --- which matrix, which inputs ---------------------------------------
     const int64_t p = blockIdx.y;
@@ -233,7 +252,7 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     const int row0 = tile * 16;
     if constexpr (EPI == MG_SILU) {
         if (a.cnt != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
-            for (int i = tid; i < a.ncnt; i += 256)
+            for (int i = tid; i < a.ncnt; i += NTH)
                 __hip_atomic_store(a.cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (!valid) {
@@ -250,8 +269,8 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     const int n = lane & 15, j = lane >> 4;                   // B: weight row, input quarter
     const int lg = (CB == 1) ? 0 : (CB == 2 ? (j >> 1) : j);  // group slot of the lane's inputs
     // A row n of set st: combination c = 4*st + n/4 = (slot c / NT, input row
-    // c % NT), digit n % 4; inactive lanes read the zero block (step 0)
-    int aoff[NSET], astep[NSET];
+    // c % NT), digit n % 4; inactive lanes read the zero row
+    int aoff[NSET];
     // C rows 4j .. 4j+3: the digits of combination 4*st + j
     int ccb[NSET], ct[NSET];
 #pragma unroll
@@ -259,7 +278,6 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
         const int c = st * 4 + (n >> 2);
         const bool act = c < NCOMBO && c / NT == lg;
         aoff[st] = act ? (((c % NT) * 4 + (n & 3)) * KSEG + 32 * j) : (int)(zero - xs);
-        astep[st] = act ? 128 : 0;
         const int cr = min(st * 4 + j, NCOMBO - 1);
         ccb[st] = cr / NT;
         ct[st] = cr % NT;
@@ -269,13 +287,20 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     // again and writes nothing)
     const int tile_ld = min(tile, (O + 15) / 16 - 1);
     const int nkq = (a.nkb + 3) / 4;
-    const uint8_t *qtile[NMAT];
-    const float *squad[NMAT];  // row n's scales of quad 0: 4 blocks x CB groups
+    // codes and scales of the matrix as buffer resources; per lane a fixed
+    // byte offset, per request a wave-uniform one
+    __amdgpu_buffer_rsrc_t qrs[NMAT], srs[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-        qtile[m] = pkm[m] + (int64_t)tile_ld * a.nkb * 1024 + 16 * lane;
-        squad[m] = (const float *)(pkm[m] + a.pk_scale_off) + ((int64_t)tile_ld * nkq * 16 + n) * 4 * CB;
+        qrs[m] = __builtin_amdgcn_make_buffer_rsrc((void *)pkm[m], (short)0, (int)a.pk_scale_off,
+                                                   MG_RSRC_W3);
+        srs[m] = __builtin_amdgcn_make_buffer_rsrc((void *)(pkm[m] + a.pk_scale_off), (short)0,
+                                                   (int)(a.pk_stride - a.pk_scale_off), MG_RSRC_W3);
     }
+    const int qoff = tile_ld * a.nkb * 1024 + 16 * lane;  // this lane's bytes of block 0
+    int soff[NSET];  // row n's 4 scales (one per block) of its C rows' group slot, quad 0
+#pragma unroll
+    for (int st = 0; st < NSET; ++st) soff[st] = ((tile_ld * nkq * 16 + n) * CB + ccb[st]) * 16;
     const int kpad = (I + 127) / 128 * 128;
 
     float acc[NSET][NMAT][4];
@@ -290,39 +315,28 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
     // two batches alternate so one is in flight while the other is computed
     struct Batch {
         u32x4 cw[MG_NBK][NMAT];
-        f32x4 sq[NMAT][GROUPED ? CB : 1];  // scales of the quad, [block][group] order
+        f32x4 sq[NMAT][GROUPED ? NSET : 1];  // the quad's 4 scales of each set's group slot
     };
     Batch bA, bB;
-    // kbg: first block of a quad (a multiple of 4)
+    // kbg: first block of a quad (a multiple of 4); blocks past kb_last
+    // re-read kb_last
     auto load_batch = [&](Batch &bt, int kbg, int kb_last) {
 #pragma unroll
         for (int i = 0; i < MG_NBK; ++i) {
-            const int kglob = min(kbg + i, kb_last);
+            const int kglob = __builtin_amdgcn_readfirstlane(min(kbg + i, kb_last));
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
-                bt.cw[i][m] = __builtin_nontemporal_load(
-                    (const COLI_GLOBAL u32x4 *)(qtile[m] + (int64_t)kglob * 1024));
+                bt.cw[i][m] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs[m], qoff, kglob * 1024, MG_AUX_NT));
         }
         if constexpr (GROUPED) {
+            const int sq0 = __builtin_amdgcn_readfirstlane((kbg / 4) * 16 * CB * 16);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int c = 0; c < CB; ++c)
-                    bt.sq[m][c] = gload<f32x4>(squad[m] + (int64_t)(kbg / 4) * 64 * CB + 4 * c);
-        }
-    };
-    // group scale of block i of the quad, group slot cb (0 .. CB-1)
-    auto pick = [&](const Batch &bt, int m, int i, int cb) -> float {
-        if constexpr (!GROUPED) {
-            return 1.0f;
-        } else if constexpr (CB == 1) {
-            return bt.sq[m][0][i];
-        } else if constexpr (CB == 2) {
-            const f32x4 v = bt.sq[m][i / 2];
-            return cb ? v[2 * (i % 2) + 1] : v[2 * (i % 2)];
-        } else {
-            const f32x4 v = bt.sq[m][i];
-            return cb >= 2 ? (cb == 3 ? v[3] : v[2]) : (cb == 1 ? v[1] : v[0]);
+                for (int st = 0; st < NSET; ++st)
+                    bt.sq[m][st] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs[m], soff[st], sq0, 0));
         }
     };
     // blocks [kb_beg, kb_end) of a segment of nkbs blocks for wavefront ks:
@@ -354,11 +368,11 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
         {
             constexpr int UN = 4;
             const int nb8 = klen / 8;
-            for (int base = 0; base < NT * nb8; base += UN * 256) {
+            for (int base = 0; base < NT * nb8; base += UN * NTH) {
                 float v[UN][8];
 #pragma unroll
                 for (int u = 0; u < UN; ++u) {
-                    const int idx = min(base + u * 256 + tid, NT * nb8 - 1);
+                    const int idx = min(base + u * NTH + tid, NT * nb8 - 1);
                     const int t = idx / nb8, b8 = idx % nb8;
                     const int k = k0 + b8 * 8;
                     const float *xr = a.x + (int64_t)xrow[t] * a.ldx + min(k, I - 8);
@@ -371,7 +385,7 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
                 }
 #pragma unroll
                 for (int u = 0; u < UN; ++u) {
-                    const int idx = base + u * 256 + tid;
+                    const int idx = base + u * NTH + tid;
                     float mx = 0.f;
                     bool bad = false;  // NaN or beyond 3e38 (fmaxf would drop a NaN)
 #pragma unroll
@@ -412,8 +426,9 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
                     }
                 }
             }
-            for (int idx = tid; idx < MG_ZERO_BYTES / 16; idx += 256)
-                reinterpret_cast<u32x4 *>(zero)[idx] = u32x4{0u, 0u, 0u, 0u};
+            if (sgi == 0)
+                for (int idx = tid; idx < KSEG / 16; idx += NTH)
+                    reinterpret_cast<u32x4 *>(zero)[idx] = u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
 
@@ -422,18 +437,20 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
         share(nkb, kb_beg, kb_end);
 
         auto compute_batch = [&](Batch &bt, int kb) {
+            f32x4 fq[NSET];  // 2^-e of the quad's blocks for each set's input row
+#pragma unroll
+            for (int st = 0; st < NSET; ++st)
+                fq[st] = *reinterpret_cast<const f32x4 *>(&xfac[ct[st] * fstride + kb]);
 #pragma unroll
             for (int i = 0; i < MG_NBK; ++i) {
                 if (kb + i >= kb_end)
                     break;
                 i32x4 a0[NSET], a1[NSET];
-                float f[NSET];
 #pragma unroll
                 for (int st = 0; st < NSET; ++st) {
-                    const char *ap = xs + aoff[st] + (kb + i) * astep[st];
+                    const char *ap = xs + aoff[st] + (kb + i) * 128;
                     a0[st] = *reinterpret_cast<const i32x4 *>(ap);
                     a1[st] = *reinterpret_cast<const i32x4 *>(ap + 16);
-                    f[st] = xfac[ct[st] * fstride + kb + i];
                 }
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
@@ -447,7 +464,7 @@ __global__ __launch_bounds__(256) void k_mgemv(MgArgs a) {
                         i32x4 c = {0, 0, 0, 0};
                         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[st], be, c, 0, 0, 0);
                         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[st], bo, c, 0, 0, 0);
-                        const float g = pick(bt, m, i, ccb[st]) * f[st];
+                        const float g = (GROUPED ? bt.sq[m][st][i] : 1.0f) * fq[st][i];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) acc[st][m][q] = fmaf(g, (float)c[q], acc[st][m][q]);
                     }
@@ -589,9 +606,9 @@ __global__ __launch_bounds__(256) void k_pack_codes(const uint8_t *__restrict__ 
     }
 }
 
-// packed fmt-4 scales: for (e, rt, quad kq of 4 blocks, row r) a run of
-// 4 x cbs floats, [block i][slot cb] = s[16*rt + r][group of slot cb of block
-// 4*kq + i]; one lane reads its row's run for a whole quad.  Padding 0.
+// packed fmt-4 scales: for (e, rt, quad kq of 4 blocks, row r, group slot cb)
+// a run of 4 floats, block i: s[16*rt + r][group of slot cb of block 4*kq + i];
+// one lane reads the run of its row and slot for a whole quad.  Padding 0.
 __global__ __launch_bounds__(256) void k_pack_scales(const float *__restrict__ s, int64_t s_stride,
                                                      int ng, int gs, int n, int O, int rt, int nkb,
                                                      int cbs, int64_t stride, int64_t scale_off,
@@ -601,10 +618,10 @@ __global__ __launch_bounds__(256) void k_pack_scales(const float *__restrict__ s
     for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total;
          c += (int64_t)gridDim.x * 256) {
         int64_t t = c;
-        const int cb = (int)(t % cbs);
-        t /= cbs;
         const int i = (int)(t % 4);
         t /= 4;
+        const int cb = (int)(t % cbs);
+        t /= cbs;
         const int r = (int)(t % 16);
         t /= 16;
         const int kq = (int)(t % nkq);
@@ -652,20 +669,22 @@ int launch_pack(coli_qtensor *t, void *packed, hipStream_t st) {
 }
 
 // The matrix-core GEMV runs on tensors that carry a packed copy.
+// (Buffer resources address one packed matrix with 32-bit byte offsets.)
 bool mgemv_ok(const coli_qtensor *W) {
-    return (W->flags & QF_PACKED) && W->pk != nullptr && packable(W->fmt, W->I, W->gs);
+    return (W->flags & QF_PACKED) && W->pk != nullptr && packable(W->fmt, W->I, W->gs) &&
+           W->pk_stride < ((int64_t)1 << 31);
 }
 
 static int cb_of(const coli_qtensor *W) { return cbs_of(W->fmt, W->gs); }
 
-static void plan_lds(int NT, int CB, int NMAT, int I, int &kseg, int &nseg, size_t &bytes) {
+static void plan_lds(int NT, int CB, int NMAT, int NW, int I, int &kseg, int &nseg, size_t &bytes) {
     const int kpad = (I + 127) / 128 * 128;
-    const int cap = (48 * 1024) / (NT * 4);  // inputs per segment (4 digit bytes each)
+    const int cap = (48 * 1024) / (NT * 4 + 1);  // inputs per segment: 4 digit bytes each + zero row
     kseg = cap / 512 * 512;
     if (kseg > kpad) kseg = kpad;
     nseg = (kpad + kseg - 1) / kseg;  // segments hold whole quads (kseg % 512 == 0)
-    bytes = (size_t)NT * 4 * kseg + MG_ZERO_BYTES + (size_t)4 * NMAT * mg_nset(CB, NT) * 256 * 4 +
-            (size_t)NT * (kseg / 128) * 4 + 64;
+    bytes = (size_t)NT * 4 * kseg + kseg + (size_t)NW * NMAT * mg_nset(CB, NT) * 256 * 4 +
+            (size_t)NT * ((kseg / 128 + 3) & ~3) * 4 + 64;
 }
 
 static MgArgs mg_args_for(const coli_qtensor *W) {
@@ -687,22 +706,22 @@ static MgArgs mg_args_for(const coli_qtensor *W) {
     return a;
 }
 
-template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS>
+template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW>
 static void mg_launch(MgArgs a, int groups, hipStream_t st) {
     size_t lds;
-    plan_lds(NT, CB, NMAT, a.I, a.kseg, a.nseg, lds);
-    constexpr int TPW = 4 / KS;
+    plan_lds(NT, CB, NMAT, NW, a.I, a.kseg, a.nseg, lds);
+    constexpr int TPW = NW / KS;
     const int tiles = (a.O + 15) / 16;
     const dim3 grid((unsigned)((tiles + TPW - 1) / TPW), (unsigned)groups);
-    hipLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS>), grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW>), grid, dim3(NW * 64), lds, st, a);
 }
 
-template <int NT, bool GROUPED, int NMAT, int EPI, int KS>
+template <int NT, bool GROUPED, int NMAT, int EPI, int KS, int NW>
 static int mg_dispatch_cb(int cb, const MgArgs &a, int groups, hipStream_t st) {
     switch (cb) {
-    case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1;
-    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1;
-    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS>(a, groups, st); return 1;
+    case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS, NW>(a, groups, st); return 1;
+    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS, NW>(a, groups, st); return 1;
+    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS, NW>(a, groups, st); return 1;
     }
 }
 
@@ -721,8 +740,8 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     ProfScope ps("mgemv", st);
     int ok;
 #define MG_CASE(NTV)                                                                          \
-    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE>(cb, a, W->n, st)            \
-           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE>(cb, a, W->n, st)
+    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st) \
+           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st)
     switch (S) {
     case 1: MG_CASE(1); break;
     case 2: MG_CASE(2); break;
@@ -767,8 +786,8 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
             a.ncnt = (m.D + 15) / 16;
         }
         ProfScope ps("moe_gateup_decode", m.st);
-        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP>(cb, a, P, m.st)
-                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP>(cb, a, P, m.st)))
+        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st)
+                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st)))
             return 0;
         int rc = after_launch("moe_gateup_decode");
         if (rc != COLI_OK) return rc;
@@ -791,8 +810,8 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
         a.yfin = m.out;
         a.has_sh = has_sh ? 1 : 0;
         ProfScope ps("moe_down_decode", m.st);
-        if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN>(cb, a, P, m.st)
-                : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN>(cb, a, P, m.st)))
+        if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st)
+                : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st)))
             return 0;
         int rc = after_launch("moe_down_decode");
         if (rc != COLI_OK) return rc;
