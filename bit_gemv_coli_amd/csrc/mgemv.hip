@@ -248,6 +248,29 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) xrow[t] = t;
     }
+    // inputs of one staging step: UN groups of 8 per thread.  The first step's
+    // loads are issued here, ahead of every weight request (loads complete in
+    // order), so the staging overlaps the first weight batches.
+    constexpr int UN = 4;
+    const int kpad = (I + 127) / 128 * 128;
+    float xv[UN][8];
+    auto stage_load = [&](int k0, int nb8, int base) {
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int idx = min(base + u * NTH + tid, NT * nb8 - 1);
+            const int t = idx / nb8, b8 = idx % nb8;
+            const int k = k0 + b8 * 8;
+            const float *xr = a.x + (int64_t)xrow[t] * a.ldx + min(k, I - 8);
+            const f32x4 p0 = gload<f32x4>(xr), p1 = gload<f32x4>(xr + 4);
+            const bool in = k < I;
+            xv[u][0] = in ? p0.x : 0.f; xv[u][1] = in ? p0.y : 0.f;
+            xv[u][2] = in ? p0.z : 0.f; xv[u][3] = in ? p0.w : 0.f;
+            xv[u][4] = in ? p1.x : 0.f; xv[u][5] = in ? p1.y : 0.f;
+            xv[u][6] = in ? p1.z : 0.f; xv[u][7] = in ? p1.w : 0.f;
+        }
+    };
+    stage_load(0, min(KSEG, kpad) / 8, 0);
+
     const int tile = blockIdx.x * TPW + tile_w;
     const int row0 = tile * 16;
     if constexpr (EPI == MG_SILU) {
@@ -301,7 +324,6 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     int soff[NSET];  // row n's 4 scales (one per block) of its C rows' group slot, quad 0
 #pragma unroll
     for (int st = 0; st < NSET; ++st) soff[st] = ((tile_ld * nkq * 16 + n) * CB + ccb[st]) * 16;
-    const int kpad = (I + 127) / 128 * 128;
 
     float acc[NSET][NMAT][4];
 #pragma unroll
@@ -319,18 +341,19 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     };
     Batch bA, bB;
     // kbg: first block of a quad (a multiple of 4); blocks past kb_last
-    // re-read kb_last
+    // re-read kb_last (requests are unconditional, so the compiler's load
+    // counting sees straight-line code and waits for one batch at a time)
     auto load_batch = [&](Batch &bt, int kbg, int kb_last) {
 #pragma unroll
         for (int i = 0; i < MG_NBK; ++i) {
-            const int kglob = __builtin_amdgcn_readfirstlane(min(kbg + i, kb_last));
+            const int kglob = __builtin_amdgcn_readfirstlane(max(min(kbg + i, kb_last), 0));
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
                 bt.cw[i][m] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs[m], qoff, kglob * 1024, MG_AUX_NT));
         }
         if constexpr (GROUPED) {
-            const int sq0 = __builtin_amdgcn_readfirstlane((kbg / 4) * 16 * CB * 16);
+            const int sq0 = __builtin_amdgcn_readfirstlane((max(min(kbg, kb_last), 0) / 4) * 16 * CB * 16);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -347,143 +370,152 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         kb_end = min(4 * (((ks + 1) * nq) / KS), nkbs);
     };
 
-    // the first batch is requested before the inputs are staged
-    {
-        int b0, e0;
-        share(min(KSEG, kpad) / 128, b0, e0);
-        if (b0 < e0)
-            load_batch(bA, b0, e0 - 1);
-    }
-
-    for (int sgi = 0; sgi < a.nseg; ++sgi) {
-        const int k0 = sgi * KSEG;
-        const int klen = min(KSEG, kpad - k0);
-        const int nkb = klen / 128;
-        // ---- stage this segment's inputs as four int8 digits under one power
-        //      of two per (input row, 128-input block): 16 consecutive threads
-        //      own one block, each 8 inputs (one word of a 32-input quarter);
-        //      digit row d holds, per quarter, the even inputs' bytes then the
-        //      odd inputs' bytes ---------------------------------------------
-        __syncthreads();
-        {
-            constexpr int UN = 4;
-            const int nb8 = klen / 8;
-            for (int base = 0; base < NT * nb8; base += UN * NTH) {
-                float v[UN][8];
+    // ---- staging of one step of inputs as four int8 digits under one power
+    //      of two per (input row, 128-input block): 16 consecutive threads
+    //      own one block, each 8 inputs (one word of a 32-input quarter);
+    //      digit row d holds, per quarter, the even inputs' bytes then the odd
+    //      inputs' bytes
+    auto stage_store = [&](int nb8, int base) {
+        auto &v = xv;
 #pragma unroll
-                for (int u = 0; u < UN; ++u) {
-                    const int idx = min(base + u * NTH + tid, NT * nb8 - 1);
-                    const int t = idx / nb8, b8 = idx % nb8;
-                    const int k = k0 + b8 * 8;
-                    const float *xr = a.x + (int64_t)xrow[t] * a.ldx + min(k, I - 8);
-                    const f32x4 p0 = gload<f32x4>(xr), p1 = gload<f32x4>(xr + 4);
-                    const bool in = k < I;
-                    v[u][0] = in ? p0.x : 0.f; v[u][1] = in ? p0.y : 0.f;
-                    v[u][2] = in ? p0.z : 0.f; v[u][3] = in ? p0.w : 0.f;
-                    v[u][4] = in ? p1.x : 0.f; v[u][5] = in ? p1.y : 0.f;
-                    v[u][6] = in ? p1.z : 0.f; v[u][7] = in ? p1.w : 0.f;
-                }
+        for (int u = 0; u < UN; ++u) {
+            const int idx = base + u * NTH + tid;
+            float mx = 0.f;
+            bool bad = false;  // NaN or beyond 3e38 (fmaxf would drop a NaN)
 #pragma unroll
-                for (int u = 0; u < UN; ++u) {
-                    const int idx = base + u * NTH + tid;
-                    float mx = 0.f;
-                    bool bad = false;  // NaN or beyond 3e38 (fmaxf would drop a NaN)
-#pragma unroll
-                    for (int w = 0; w < 8; ++w) {
-                        mx = fmaxf(mx, fabsf(v[u][w]));
-                        bad |= !(fabsf(v[u][w]) <= 3.0e38f);
-                    }
-                    if (bad)
-                        mx = __builtin_inff();
-#pragma unroll
-                    for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-                    // 2^e2 * max|x| in [2^29, 2^30) (tiny blocks: e2 <= 126 keeps
-                    // 2^-e2 normal); non-finite blocks give a NaN factor
-                    int e2 = 0;
-                    if (mx > 0.f && mx <= 3.0e38f) {
-                        (void)frexpf(mx, &e2);  // mx < 2^e2
-                        e2 = min(30 - e2, 126);
-                    }
-                    if (idx < NT * nb8) {
-                        const int t = idx / nb8, b8 = idx % nb8;
-                        uint32_t wd[8];
-#pragma unroll
-                        for (int w = 0; w < 8; ++w)
-                            wd[w] = (mx <= 3.0e38f) ? digits_of(ldexpf(v[u][w], e2)) : 0u;
-                        // byte b of the even word: input 2b of the 8; odd word: 2b+1
-                        uint32_t ev[4], od[4];
-                        transpose4(wd[0], wd[2], wd[4], wd[6], ev);
-                        transpose4(wd[1], wd[3], wd[5], wd[7], od);
-                        char *dst = xs + t * 4 * KSEG + (b8 >> 2) * 32 + (b8 & 3) * 4;
-#pragma unroll
-                        for (int d = 0; d < 4; ++d) {
-                            *reinterpret_cast<uint32_t *>(dst + d * KSEG) = ev[d];
-                            *reinterpret_cast<uint32_t *>(dst + d * KSEG + 16) = od[d];
-                        }
-                        if ((b8 & 15) == 0)
-                            xfac[t * fstride + b8 / 16] =
-                                (mx <= 3.0e38f) ? ldexpf(1.0f, -e2) : __builtin_nanf("");
-                    }
-                }
+            for (int w = 0; w < 8; ++w) {
+                mx = fmaxf(mx, fabsf(v[u][w]));
+                bad |= !(fabsf(v[u][w]) <= 3.0e38f);
             }
-            if (sgi == 0)
-                for (int idx = tid; idx < KSEG / 16; idx += NTH)
-                    reinterpret_cast<u32x4 *>(zero)[idx] = u32x4{0u, 0u, 0u, 0u};
+            if (bad)
+                mx = __builtin_inff();
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+            // 2^e2 * max|x| in [2^29, 2^30) (tiny blocks: e2 <= 126 keeps
+            // 2^-e2 normal); non-finite blocks give a NaN factor
+            int e2 = 0;
+            if (mx > 0.f && mx <= 3.0e38f) {
+                (void)frexpf(mx, &e2);  // mx < 2^e2
+                e2 = min(30 - e2, 126);
+            }
+            if (idx < NT * nb8) {
+                const int t = idx / nb8, b8 = idx % nb8;
+                uint32_t wd[8];
+#pragma unroll
+                for (int w = 0; w < 8; ++w)
+                    wd[w] = (mx <= 3.0e38f) ? digits_of(ldexpf(v[u][w], e2)) : 0u;
+                // byte b of the even word: input 2b of the 8; odd word: 2b+1
+                uint32_t ev[4], od[4];
+                transpose4(wd[0], wd[2], wd[4], wd[6], ev);
+                transpose4(wd[1], wd[3], wd[5], wd[7], od);
+                char *dst = xs + t * 4 * KSEG + (b8 >> 2) * 32 + (b8 & 3) * 4;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    *reinterpret_cast<uint32_t *>(dst + d * KSEG) = ev[d];
+                    *reinterpret_cast<uint32_t *>(dst + d * KSEG + 16) = od[d];
+                }
+                if ((b8 & 15) == 0)
+                    xfac[t * fstride + b8 / 16] =
+                        (mx <= 3.0e38f) ? ldexpf(1.0f, -e2) : __builtin_nanf("");
+            }
         }
-        __syncthreads();
-
-        // ---- this wavefront's share of the segment's 128-input blocks ------
-        int kb_beg, kb_end;
-        share(nkb, kb_beg, kb_end);
-
-        auto compute_batch = [&](Batch &bt, int kb) {
-            f32x4 fq[NSET];  // 2^-e of the quad's blocks for each set's input row
+    };
+    // one quad (segment blocks kb .. kb+3); blocks at or past kb_end add
+    // nothing (zero factor), so every quad runs the same straight-line code
+    auto compute_batch = [&](Batch &bt, int kb, int kb_end) {
+        f32x4 fq[NSET];  // 2^-e of the quad's blocks for each set's input row
 #pragma unroll
-            for (int st = 0; st < NSET; ++st)
-                fq[st] = *reinterpret_cast<const f32x4 *>(&xfac[ct[st] * fstride + kb]);
+        for (int st = 0; st < NSET; ++st)
+            fq[st] = *reinterpret_cast<const f32x4 *>(&xfac[ct[st] * fstride + kb]);
 #pragma unroll
-            for (int i = 0; i < MG_NBK; ++i) {
-                if (kb + i >= kb_end)
-                    break;
-                i32x4 a0[NSET], a1[NSET];
+        for (int i = 0; i < MG_NBK; ++i) {
+            const bool live = kb + i < kb_end;
+            i32x4 a0[NSET], a1[NSET];
+#pragma unroll
+            for (int st = 0; st < NSET; ++st) {
+                const char *ap = xs + aoff[st] + (kb + i) * 128;
+                a0[st] = *reinterpret_cast<const i32x4 *>(ap);
+                a1[st] = *reinterpret_cast<const i32x4 *>(ap + 16);
+            }
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const u32x4 w = bt.cw[i][m];
+                const i32x4 be = {(int)even_x16(w.x), (int)even_x16(w.y), (int)even_x16(w.z),
+                                  (int)even_x16(w.w)};
+                const i32x4 bo = {(int)odd_x16(w.x), (int)odd_x16(w.y), (int)odd_x16(w.z),
+                                  (int)odd_x16(w.w)};
 #pragma unroll
                 for (int st = 0; st < NSET; ++st) {
-                    const char *ap = xs + aoff[st] + (kb + i) * 128;
-                    a0[st] = *reinterpret_cast<const i32x4 *>(ap);
-                    a1[st] = *reinterpret_cast<const i32x4 *>(ap + 16);
-                }
+                    i32x4 c = {0, 0, 0, 0};
+                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[st], be, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[st], bo, c, 0, 0, 0);
+                    const float g = live ? (GROUPED ? bt.sq[m][st][i] : 1.0f) * fq[st][i] : 0.0f;
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                    const u32x4 w = bt.cw[i][m];
-                    const i32x4 be = {(int)even_x16(w.x), (int)even_x16(w.y), (int)even_x16(w.z),
-                                      (int)even_x16(w.w)};
-                    const i32x4 bo = {(int)odd_x16(w.x), (int)odd_x16(w.y), (int)odd_x16(w.z),
-                                      (int)odd_x16(w.w)};
-#pragma unroll
-                    for (int st = 0; st < NSET; ++st) {
-                        i32x4 c = {0, 0, 0, 0};
-                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[st], be, c, 0, 0, 0);
-                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[st], bo, c, 0, 0, 0);
-                        const float g = (GROUPED ? bt.sq[m][st][i] : 1.0f) * fq[st][i];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[st][m][q] = fmaf(g, (float)c[q], acc[st][m][q]);
-                    }
+                    for (int q = 0; q < 4; ++q) acc[st][m][q] = fmaf(g, (float)c[q], acc[st][m][q]);
                 }
             }
-        };
-        const int kg0 = k0 / 128;
-        if (sgi > 0 && kb_beg < kb_end)
-            load_batch(bA, kg0 + kb_beg, kg0 + kb_end - 1);
-        for (int kb = kb_beg; kb < kb_end; kb += 2 * MG_NBK) {
-            const bool hasB = kb + MG_NBK < kb_end;
-            if (hasB)
-                load_batch(bB, kg0 + kb + MG_NBK, kg0 + kb_end - 1);
-            compute_batch(bA, kb);
-            if (kb + 2 * MG_NBK < kb_end)
-                load_batch(bA, kg0 + kb + 2 * MG_NBK, kg0 + kb_end - 1);
-            if (hasB)
-                compute_batch(bB, kb + MG_NBK);
         }
+    };
+    // LDS hand-over between the wavefronts (no wait on outstanding loads)
+    auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    // ---- segment 0: its first staging step's inputs are already requested;
+    //      the first two weight batches go out before the staging uses them
+    int kb_beg, kb_end;
+    {
+        const int klen = min(KSEG, kpad);
+        const int nb8 = klen / 8;
+        share(klen / 128, kb_beg, kb_end);
+        load_batch(bA, kb_beg, kb_end - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_batch(bB, kb_beg + MG_NBK, kb_end - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_store(nb8, 0);
+        for (int base = UN * NTH; base < NT * nb8; base += UN * NTH) {
+            stage_load(0, nb8, base);
+            stage_store(nb8, base);
+        }
+        for (int idx = tid; idx < KSEG / 16; idx += NTH)
+            reinterpret_cast<u32x4 *>(zero)[idx] = u32x4{0u, 0u, 0u, 0u};
+        lds_barrier();
+    }
+    for (int sgi = 0;;) {
+        const int kg0 = sgi * (KSEG / 128);
+        // A and B are in flight; each is re-requested as soon as it is consumed
+        const int nq = (kb_end - kb_beg + 3) / 4;
+        int kb = kb_beg;
+        // (scheduling fences keep each batch's use after the other's request,
+        // so the wait before a batch never covers the batch behind it)
+        for (int q = 0; q + 2 < nq; q += 2, kb += 2 * MG_NBK) {
+            compute_batch(bA, kb, kb_end);
+            __builtin_amdgcn_sched_barrier(0);
+            load_batch(bA, kg0 + kb + 2 * MG_NBK, kg0 + kb_end - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(bB, kb + MG_NBK, kb_end);
+            __builtin_amdgcn_sched_barrier(0);
+            load_batch(bB, kg0 + kb + 3 * MG_NBK, kg0 + kb_end - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        compute_batch(bA, kb, kb_end);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch(bB, kb + MG_NBK, kb_end);
+        if (++sgi >= a.nseg)
+            break;
+        // ---- next segment: restage the inputs, then its first two batches
+        const int k0 = sgi * KSEG;
+        const int klen = min(KSEG, kpad - k0);
+        const int nb8 = klen / 8;
+        lds_barrier();  // every wavefront is done with the previous digits
+        for (int base = 0; base < NT * nb8; base += UN * NTH) {
+            stage_load(k0, nb8, base);
+            stage_store(nb8, base);
+        }
+        lds_barrier();
+        share(klen / 128, kb_beg, kb_end);
+        load_batch(bA, k0 / 128 + kb_beg, k0 / 128 + kb_end - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_batch(bB, k0 / 128 + kb_beg + MG_NBK, k0 / 128 + kb_end - 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // --- reduce: KS wavefronts x group slots x digits -> one value per (row, input row)
