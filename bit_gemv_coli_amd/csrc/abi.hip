@@ -97,7 +97,7 @@ static hipEvent_t take_event() {
     return e;
 }
 
-ProfScope::ProfScope(const char *tag, hipStream_t s) : slot(-1), stream(s) {
+ProfScope::ProfScope(const char *tag, hipStream_t s, bool ext_) : slot(-1), stream(s), ext(ext_) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on)
         return;
@@ -110,17 +110,28 @@ ProfScope::ProfScope(const char *tag, hipStream_t s) : slot(-1), stream(s) {
     bool known = false;
     for (auto &t : g_tags) known |= (t == r.tag);
     if (!known) g_tags.push_back(r.tag);
-    (void)hipEventRecord(r.a, s);
+    if (!ext)
+        (void)hipEventRecord(r.a, s);
     slot = (int)g_prof.size();
     g_prof.push_back(r);
 }
 
 ProfScope::~ProfScope() {
-    if (slot < 0)
+    if (slot < 0 || ext)
         return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (slot < (int)g_prof.size())
         (void)hipEventRecord(g_prof[slot].b, stream);
+}
+
+hipEvent_t ProfScope::start() const {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    return (ext && slot >= 0 && slot < (int)g_prof.size()) ? g_prof[slot].a : nullptr;
+}
+
+hipEvent_t ProfScope::stop() const {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    return (ext && slot >= 0 && slot < (int)g_prof.size()) ? g_prof[slot].b : nullptr;
 }
 
 static bool gate_call() {

@@ -25,8 +25,13 @@ int after_launch(const char *tag);
 struct ProfScope {
     int slot;
     hipStream_t stream;
-    ProfScope(const char *tag, hipStream_t s);
+    bool ext;
+    // ext: the launch records the events itself (hipExtLaunchKernelGGL start
+    // and stop events, stamped by the dispatch), which times the kernel alone
+    ProfScope(const char *tag, hipStream_t s, bool ext = false);
     ~ProfScope();
+    hipEvent_t start() const;  // nullptr unless profiling (ext mode)
+    hipEvent_t stop() const;
 };
 
 // Flags stored in coli_qtensor::flags by coli_tensor_upload.

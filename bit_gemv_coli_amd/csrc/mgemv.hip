@@ -38,6 +38,8 @@
 
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace coli {
@@ -227,7 +229,9 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         int e = 0, s;
         if (!shared) {
             s = (int)(p / a.K);
-            e = gload<int32_t>(a.ids + p);
+            // scalar load: the scalar cache path does not queue behind this
+            // CU's vector weight requests
+            e = *(const __attribute__((address_space(4))) int32_t *)(a.ids + p);
             valid = (e >= 0 && e < a.E);
             if (!valid) e = 0;
         } else {
@@ -739,21 +743,22 @@ static MgArgs mg_args_for(const coli_qtensor *W) {
 }
 
 template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW>
-static void mg_launch(MgArgs a, int groups, hipStream_t st) {
+static void mg_launch(MgArgs a, int groups, hipStream_t st, const ProfScope &ps) {
     size_t lds;
     plan_lds(NT, CB, NMAT, NW, a.I, a.kseg, a.nseg, lds);
     constexpr int TPW = NW / KS;
     const int tiles = (a.O + 15) / 16;
     const dim3 grid((unsigned)((tiles + TPW - 1) / TPW), (unsigned)groups);
-    hipLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW>), grid, dim3(NW * 64), lds, st, a);
+    hipExtLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW>), grid, dim3(NW * 64),
+                          (uint32_t)lds, st, ps.start(), ps.stop(), 0, a);
 }
 
 template <int NT, bool GROUPED, int NMAT, int EPI, int KS, int NW>
-static int mg_dispatch_cb(int cb, const MgArgs &a, int groups, hipStream_t st) {
+static int mg_dispatch_cb(int cb, const MgArgs &a, int groups, hipStream_t st, const ProfScope &ps) {
     switch (cb) {
-    case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS, NW>(a, groups, st); return 1;
-    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS, NW>(a, groups, st); return 1;
-    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS, NW>(a, groups, st); return 1;
+    case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS, NW>(a, groups, st, ps); return 1;
+    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS, NW>(a, groups, st, ps); return 1;
+    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS, NW>(a, groups, st, ps); return 1;
     }
 }
 
@@ -769,11 +774,11 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     a.out = y;
     a.Sy = S;
     const bool g = W->fmt == 4;
-    ProfScope ps("mgemv", st);
+    ProfScope ps("mgemv", st, true);
     int ok;
 #define MG_CASE(NTV)                                                                          \
-    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st) \
-           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st)
+    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st, ps) \
+           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st, ps)
     switch (S) {
     case 1: MG_CASE(1); break;
     case 2: MG_CASE(2); break;
@@ -817,9 +822,9 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
             a.cnt = cnt;
             a.ncnt = (m.D + 15) / 16;
         }
-        ProfScope ps("moe_gateup_decode", m.st);
-        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st)
-                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st)))
+        ProfScope ps("moe_gateup_decode", m.st, true);
+        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st, ps)
+                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st, ps)))
             return 0;
         int rc = after_launch("moe_gateup_decode");
         if (rc != COLI_OK) return rc;
@@ -841,9 +846,9 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
         a.wts = m.w;
         a.yfin = m.out;
         a.has_sh = has_sh ? 1 : 0;
-        ProfScope ps("moe_down_decode", m.st);
-        if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st)
-                : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st)))
+        ProfScope ps("moe_down_decode", m.st, true);
+        if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st, ps)
+                : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st, ps)))
             return 0;
         int rc = after_launch("moe_down_decode");
         if (rc != COLI_OK) return rc;
