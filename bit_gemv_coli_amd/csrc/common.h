@@ -80,6 +80,10 @@ size_t packed_bytes(int fmt, int n, int O, int I, int gs);
 int launch_pack(coli_qtensor *t, void *packed, hipStream_t st);
 int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
 int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt);
+// prefill GEMM on the matrix cores for the int4 formats (pgemm.hip); 1 done,
+// 0 not taken, <0 error
+bool pgemm_ok(const coli_qtensor *W);
+int launch_pgemm_dense(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
 // 0: matrix-core decode kernels where the layout allows, 1: vector-ALU kernels only
 int decode_kernel_mode();
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared);

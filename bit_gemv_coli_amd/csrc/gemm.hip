@@ -324,6 +324,9 @@ static void launch_dense_t(const coli_qtensor *W, const float *x, float *y, int 
 int launch_gemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws, size_t ws_bytes,
                 hipStream_t st) {
     (void)ws; (void)ws_bytes;
+    const int pr = launch_pgemm_dense(W, x, y, S, st);  // int4 formats
+    if (pr != 0)
+        return pr > 0 ? COLI_OK : COLI_HIP_ERROR;
     if (!mfma_ok(W) || (uintptr_t)x % 16 != 0)
         return launch_gemv(W, x, y, S, st);  // exact fp32 path for other layouts
     ProfScope ps("gemm_dense", st);
