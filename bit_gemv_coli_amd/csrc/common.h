@@ -84,6 +84,16 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt);
 // 0 not taken, <0 error
 bool pgemm_ok(const coli_qtensor *W);
 int launch_pgemm_dense(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
+// prefill MoE on the matrix cores: routed tiles of pgemm_moe_rows(m) rows
+// (0: neither kernel takes these tensors; tile list, counts and offsets from
+// launch_route), bf16 gathered inputs xg, bf16 SiLU products hg, f32 down
+// rows y (skipped when y is null)
+constexpr int PG_MOE_ROWS = 64;         // producer/consumer kernel
+constexpr int PG_MOE_ROWS_PACKED = 32;  // weight-streaming kernel (packed copies)
+int pgemm_moe_rows(const MoeArgs &m);
+int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float *y,
+                     const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,
+                     const int32_t *offsets, int max_tiles);
 // 0: matrix-core decode kernels where the layout allows, 1: vector-ALU kernels only
 int decode_kernel_mode();
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared);

@@ -451,18 +451,40 @@ __global__ __launch_bounds__(256) void k_hidden_out(const bf16_t *__restrict__ h
         h[(int64_t)p * F + j] = pos < 0 ? 0.f : (float)hg[(int64_t)pos * F + j];
 }
 
+static int moe_gather(const MoeArgs &a, const PrefillWs &w) {
+    const bool has_sh = a.sg != nullptr;
+    const int SK = a.S * a.K;
+    const int R = SK + (has_sh ? a.S : 0);
+    ProfScope ps("moe_gather", a.st);
+    hipLaunchKernelGGL(k_gather_x, dim3((unsigned)R), dim3(256), 0, a.st, a.x, a.D, a.K, SK, a.S,
+                       has_sh ? 1 : 0, w.perm, w.offsets, a.E, w.xg);
+    return after_launch("moe_gather");
+}
+
+static int moe_hidden_out(const MoeArgs &a, const PrefillWs &w) {
+    const int SK = a.S * a.K;
+    const int R = SK + (a.sg != nullptr ? a.S : 0);
+    ProfScope ps("moe_hidden_out", a.st);
+    hipLaunchKernelGGL(k_hidden_out, dim3((unsigned)R), dim3(256), 0, a.st, w.hg, w.inv, SK, a.F,
+                       a.h_out);
+    return after_launch("moe_hidden_out");
+}
+
+static int moe_combine(const MoeArgs &a, const PrefillWs &w) {
+    ProfScope ps("moe_prefill_combine", a.st);
+    hipLaunchKernelGGL(k_prefill_combine, dim3((unsigned)((a.D / 4 + 255) / 256), (unsigned)a.S),
+                       dim3(256), 0, a.st, w.y, w.inv, a.w, a.S, a.K, a.D,
+                       a.sg != nullptr ? 1 : 0, a.out);
+    return after_launch("moe_prefill_combine");
+}
+
 template <int FMT>
 static int moe_prefill_t(const MoeArgs &a, const PrefillWs &w) {
     const bool has_sh = a.sg != nullptr;
     const int SK = a.S * a.K;
-    const int R = SK + (has_sh ? a.S : 0);
-    {
-        ProfScope ps("moe_gather", a.st);
-        hipLaunchKernelGGL(k_gather_x, dim3((unsigned)R), dim3(256), 0, a.st, a.x, a.D, a.K, SK,
-                           a.S, has_sh ? 1 : 0, w.perm, w.offsets, a.E, w.xg);
-        int rc = after_launch("moe_gather");
-        if (rc != COLI_OK) return rc;
-    }
+    int rc = moe_gather(a, w);
+    if (rc != COLI_OK)
+        return rc;
     {
         GemmArgs g = gemm_args_for(a.gate);
         g.q[1] = (const uint8_t *)a.up->q;
@@ -484,12 +506,8 @@ static int moe_prefill_t(const MoeArgs &a, const PrefillWs &w) {
         int rc = after_launch("moe_gateup_gemm");
         if (rc != COLI_OK) return rc;
     }
-    if (a.h_out) {
-        ProfScope ps("moe_hidden_out", a.st);
-        hipLaunchKernelGGL(k_hidden_out, dim3((unsigned)R), dim3(256), 0, a.st, w.hg, w.inv, SK,
-                           a.F, a.h_out);
-        return after_launch("moe_hidden_out");
-    }
+    if (a.h_out)
+        return moe_hidden_out(a, w);
     {
         GemmArgs g = gemm_args_for(a.down);
         g.sq[0] = g.sq[1] = has_sh ? (const uint8_t *)a.sd->q : g.q[0];
@@ -507,13 +525,23 @@ static int moe_prefill_t(const MoeArgs &a, const PrefillWs &w) {
         int rc = after_launch("moe_down_gemm");
         if (rc != COLI_OK) return rc;
     }
-    {
-        ProfScope ps("moe_prefill_combine", a.st);
-        hipLaunchKernelGGL(k_prefill_combine, dim3((unsigned)((a.D / 4 + 255) / 256), (unsigned)a.S),
-                           dim3(256), 0, a.st, w.y, w.inv, a.w, a.S, a.K, a.D, has_sh ? 1 : 0,
-                           a.out);
-        return after_launch("moe_prefill_combine");
-    }
+    return moe_combine(a, w);
+}
+
+// the int4 formats on the newer matrix-core kernels (routed tiles of `rows`)
+static int moe_prefill_pg(const MoeArgs &a, const PrefillWs &w, int rows) {
+    const bool has_sh = a.sg != nullptr;
+    const size_t SK = (size_t)a.S * a.K;
+    const int max_tiles = (int)(std::min<size_t>((size_t)a.E, SK) + (SK + rows - 1) / rows +
+                                (has_sh ? ((size_t)a.S + rows - 1) / rows : 0));
+    int rc = moe_gather(a, w);
+    if (rc != COLI_OK)
+        return rc;
+    rc = launch_pgemm_moe(a, rows, w.xg, w.hg, a.h_out ? nullptr : w.y, w.tiles, w.n_tiles,
+                          w.counts, w.offsets, max_tiles);
+    if (rc != COLI_OK)
+        return rc;
+    return a.h_out ? moe_hidden_out(a, w) : moe_combine(a, w);
 }
 
 int launch_moe_prefill(const MoeArgs &a) {
@@ -530,10 +558,13 @@ int launch_moe_prefill(const MoeArgs &a) {
     const PrefillWs w = prefill_layout(a.ws, a.E, a.S, a.K, a.F, a.D, has_sh);
     if (w.bytes > a.ws_bytes)
         return decline("moe_block: workspace %zu bytes < %zu needed", a.ws_bytes, w.bytes);
+    const int pg_rows = (uintptr_t)a.ws % 16 == 0 ? pgemm_moe_rows(a) : 0;
     int rc = launch_route(a.ids, a.S, a.K, a.E, w.counts, w.offsets, w.perm, w.n_bad, w.inv,
-                          w.tiles, w.n_tiles, MOE_BM, has_sh ? a.S : 0, a.st);
+                          w.tiles, w.n_tiles, pg_rows ? pg_rows : MOE_BM, has_sh ? a.S : 0, a.st);
     if (rc != COLI_OK)
         return rc;
+    if (pg_rows)
+        return moe_prefill_pg(a, w, pg_rows);
     switch (a.gate->fmt) {
     case 1: return moe_prefill_t<1>(a, w);
     case 2: return moe_prefill_t<2>(a, w);

@@ -49,6 +49,15 @@ struct PgArgs {
     int M, K;
     const uint8_t *q[2];
     const float *s[2];
+    // routed (MoE) tiles: tile t = (expert tiles[2t], first row tiles[2t+1]);
+    // expert E is the shared expert (rows SK ..); weights of expert e at
+    // q[m] + e * q_stride
+    const uint8_t *sq[2];
+    const float *ss[2];
+    int64_t q_stride, s_stride;
+    const int32_t *tiles, *n_tiles, *counts, *offsets;
+    int E, SK, S;
+    int nkb, nkq, cbs, rtn;  // packed copy: blocks per row, quads, scale slots, 16-row tiles
     int64_t rb;     // code bytes per weight row
     int ng, gshift, N;  // groups per row (fmt 4), log2 of the group size, weight rows
     int fmt;
@@ -63,7 +72,7 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
     return r;
 }
 
-template <int BM, int NMAT, int EPI, bool AF32>
+template <int BM, int NMAT, int EPI, bool AF32, bool MOE>
 __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
     static_assert(BM == 64 || BM == 128, "tile rows");
     constexpr int MBK = BM / 64;       // 32-row blocks per consumer wavefront
@@ -78,7 +87,16 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
     // dispatch); give each XCD a contiguous run of tiles in M-major order so
     // its L2 holds the input rows of at most two M tiles
     int mt, nt;
-    {
+    if (MOE) {
+        // routed tiles (gridDim.x a multiple of 8): tile mt runs on XCD mt % 8
+        // -- unused tiles at the end of the list spread over all XCDs -- and
+        // each XCD takes its tiles one after the other with all their
+        // weight-row tiles together, so a tile's input rows stay in that L2
+        const int w = blockIdx.y * gridDim.x + blockIdx.x, ntn = gridDim.y;
+        const int xcd = w % 8, idx = w / 8;
+        mt = 8 * (idx / ntn) + xcd;
+        nt = idx % ntn;
+    } else {
         const int ntm = gridDim.x, ntn = gridDim.y, tiles = ntm * ntn;
         const int w = blockIdx.y * ntm + blockIdx.x;
         const int per = (tiles + 7) / 8;
@@ -89,7 +107,33 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
         mt = t / ntn;
         nt = t % ntn;
     }
-    const int m0 = mt * BM;
+    // rows of this tile: X rows xr0 .. xr0 + mcount - 1 (routing order for
+    // MoE), weights of expert e
+    int xr0, mcount;
+    const uint8_t *wq[NMAT];
+    const float *wsc[NMAT];
+    if (MOE) {
+        if (mt >= gload<int32_t>(a.n_tiles))
+            return;  // whole workgroup: the tile list is shorter than the grid
+        const int e = gload<int32_t>(a.tiles + 2 * mt);
+        const int r0 = gload<int32_t>(a.tiles + 2 * mt + 1);
+        const bool shared = e >= a.E;
+        xr0 = (shared ? a.SK : gload<int32_t>(a.offsets + e)) + r0;
+        mcount = min(BM, (shared ? a.S : gload<int32_t>(a.counts + e)) - r0);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            wq[m] = shared ? a.sq[m] : a.q[m] + (int64_t)e * a.q_stride;
+            wsc[m] = shared ? a.ss[m] : a.s[m] + (int64_t)e * a.s_stride;
+        }
+    } else {
+        xr0 = mt * BM;
+        mcount = min(BM, a.M - xr0);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            wq[m] = a.q[m];
+            wsc[m] = a.s[m];
+        }
+    }
     const int n0 = nt * NPM;
     const int K = a.K;
     const int nsteps = (K + PG_BK - 1) / PG_BK;
@@ -106,8 +150,8 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
         const int rB = pt >> 1, pB = pt & 1;
         const int mat = rB / NPM;
         const int nrow = min(n0 + rB % NPM, a.N - 1);
-        const uint8_t *qrow = a.q[mat] + (int64_t)nrow * a.rb;
-        const float *srow = a.s[mat] + (a.fmt == 4 ? (int64_t)nrow * a.ng : (int64_t)nrow);
+        const uint8_t *qrow = wq[mat] + (int64_t)nrow * a.rb;
+        const float *srow = wsc[mat] + (a.fmt == 4 ? (int64_t)nrow * a.ng : (int64_t)nrow);
         // inputs: request i of a lane covers 16 bytes of input row
         // aro + ARI * i + lane / LPR at input column acol, so that LPR
         // consecutive lanes read one row's step slice (coalesced)
@@ -119,11 +163,10 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
         const int pw = pt >> 6, pl = pt & 63;
         const int aro = pw * (BM / 4) + pl / LPR;  // first row of this lane
         const int acol = EPL * (pl % LPR);
-        const int64_t xoff0 = (int64_t)min(m0 + aro, a.M - 1) * a.ldx;
-        int64_t xstep[NA];  // row offset of request i (rows clamped to M-1)
+        int64_t xstep[NA];  // row offset of request i (rows past the tile clamped)
 #pragma unroll
-        for (int i = 0; i < NA; ++i) xstep[i] = (int64_t)min(m0 + aro + ARI * i, a.M - 1) * a.ldx;
-        (void)xoff0;
+        for (int i = 0; i < NA; ++i)
+            xstep[i] = (int64_t)(xr0 + min(aro + ARI * i, mcount - 1)) * a.ldx;
 
         struct Stage {
             u32x4 c;              // 32 codes
@@ -246,7 +289,42 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
 
     // ---- epilogue: C row (8 * (r / 4) + 4 * (l / 32) + r % 4), column l % 32
     const int ccol = lane & 31, crow = 4 * (lane >> 5);
-    if constexpr (EPI == PG_Y) {
+    if constexpr (EPI == PG_SILU) {
+        // gate values sit in the wn = 0 wavefronts, up values of the same
+        // outputs in wn = 1: up goes through LDS (the producers have ended)
+        float *ex = reinterpret_cast<float *>(&Bs[0][0]);  // [BM][64] f32
+        if (wn == 1) {
+#pragma unroll
+            for (int i = 0; i < MBK; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = wm * (BM / 2) + 32 * i + 8 * (r / 4) + crow + (r % 4);
+                        ex[m * 64 + 32 * j + ccol] = acc[i][j][r];
+                    }
+        }
+        lds_barrier();
+        if (wn == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + 32 * j + ccol;
+                if (n >= a.N)
+                    continue;
+#pragma unroll
+                for (int i = 0; i < MBK; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = wm * (BM / 2) + 32 * i + 8 * (r / 4) + crow + (r % 4);
+                        if (m < mcount) {
+                            const float g = acc[i][j][r], u = ex[m * 64 + 32 * j + ccol];
+                            ((pg_bf16 *)a.y)[(int64_t)(xr0 + m) * a.ldy + n] =
+                                (pg_bf16)((g / (1.0f + expf(-g))) * u);
+                        }
+                    }
+            }
+        }
+    } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + 64 * wn + 32 * j + ccol;
@@ -256,9 +334,296 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
             for (int i = 0; i < MBK; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (r / 4) + crow + (r % 4);
-                    if (m < a.M)
-                        ((float *)a.y)[(int64_t)m * a.ldy + n] = acc[i][j][r];
+                    const int m = wm * (BM / 2) + 32 * i + 8 * (r / 4) + crow + (r % 4);
+                    if (m < mcount)
+                        ((float *)a.y)[(int64_t)(xr0 + m) * a.ldy + n] = acc[i][j][r];
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming GEMM for short row tiles (the routed MoE experts), on the
+// packed copy of the weights: 16-row tiles of 128-input blocks, 1 KiB each,
+// lane l = 16 j + r holding row r, inputs 32 j .. 32 j + 31 as
+// two's-complement nibbles, plus per (tile, 4 blocks, row, group slot) runs
+// of 4 scales.  Every wavefront streams its own tiles straight into registers
+// (one contiguous KiB per tile and block, four blocks in flight, scale runs
+// once per four blocks), turns the nibbles into bf16 there and runs
+// v_mfma_f32_16x16x32_bf16 against the input rows, which the workgroup
+// stages through LDS one block ahead (one barrier per block).  No weight
+// passes through LDS.
+//
+// Inputs inside a block: lane (n = l % 16, g = l / 16) holds inputs
+// 32 g .. 32 g + 31 of weight row n; MFMA slice s (0..3) takes inputs
+// 32 g + 8 s .. + 8 from each lane, and the input rows are read from LDS at the
+// same columns, so every slice sums 32 distinct inputs and the four slices
+// cover the block.
+//
+// Scales: with groups of >= 128 inputs (and the per-row format) a block lies
+// inside one group; the exact weights 16 (q - 8) accumulate per group and the
+// group's scale / 16 is applied once to the group sum in fp32 (SF = false).
+// Groups of 32 or 64 fold the scale into the bf16 weights (SF = true): each
+// lane's 32 inputs lie in one group.
+constexpr int SG_KC = 128;         // inputs per block
+constexpr int SG_LDA = SG_KC + 8;  // LDS row stride of the input tile (bf16 elements)
+constexpr int SG_NB = 4;           // blocks in flight (= blocks per scale run)
+
+typedef float sg_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int MB, int NCT, int NMAT, int EPI, bool MOE, bool SF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sg(PgArgs a) {
+    constexpr int TM = 16 * MB;       // input rows per tile
+    constexpr int TPM = NCT / NMAT;   // 16-row weight tiles per matrix per wavefront
+    constexpr int WCOL = 16 * TPM;    // output columns per wavefront
+    static_assert(NCT % NMAT == 0, "tiles per matrix");
+    __shared__ __attribute__((aligned(16))) pg_bf16 As[2][TM * SG_LDA];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int mt, nt;
+    {
+        // XCD-aware order (gridDim.x a multiple of 8 for routed tiles): row
+        // tile mt runs on XCD mt % 8 with all its column tiles together
+        const int w = blockIdx.y * gridDim.x + blockIdx.x, ntn = gridDim.y;
+        if (gridDim.x % 8 == 0) {
+            const int idx = w / 8;
+            mt = 8 * (idx / ntn) + w % 8;
+            nt = idx % ntn;
+        } else {
+            mt = blockIdx.x;
+            nt = blockIdx.y;
+        }
+    }
+    int xr0, mcount;
+    const uint8_t *wq[NMAT];  // packed codes of the matrix
+    const float *wsc[NMAT];   // its packed scale runs (fmt 4) or row scales (fmt 2)
+    if (MOE) {
+        if (mt >= gload<int32_t>(a.n_tiles))
+            return;  // whole workgroup: the tile list is shorter than the grid
+        const int e = gload<int32_t>(a.tiles + 2 * mt);
+        const int r0 = gload<int32_t>(a.tiles + 2 * mt + 1);
+        const bool shared = e >= a.E;
+        xr0 = (shared ? a.SK : gload<int32_t>(a.offsets + e)) + r0;
+        mcount = min(TM, (shared ? a.S : gload<int32_t>(a.counts + e)) - r0);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            wq[m] = shared ? a.sq[m] : a.q[m] + (int64_t)e * a.q_stride;
+            wsc[m] = shared ? a.ss[m] : a.s[m] + (int64_t)e * a.s_stride;
+        }
+    } else {
+        xr0 = mt * TM;
+        mcount = min(TM, a.M - xr0);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            wq[m] = a.q[m];
+            wsc[m] = a.s[m];
+        }
+    }
+    const int K = a.K;
+    const int nch = a.nkb;  // blocks (the last one zero-padded past K)
+    const int npad = (nch + SG_NB - 1) / SG_NB * SG_NB;
+    const int ln = lane & 15, lg = lane >> 4;
+    const int c0 = nt * (4 * WCOL) + wave * WCOL;  // first output column of this wavefront
+
+    // ---- weight tiles of this wavefront (tiles past the matrix clamped; their
+    // outputs are dropped): code and scale-run offsets within the matrix
+    int qoff[NCT], soff[NCT];
+    float rsc[NCT];  // per-row scale (fmt 2)
+    const int cb = SF ? (lg >> (a.gshift - 5)) : 0;  // this lane's group slot in a block
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+        const int tile = min((c0 + 16 * (t % TPM)) >> 4, a.rtn - 1);
+        qoff[t] = tile * a.nkb * 1024 + 16 * lane;
+        soff[t] = ((tile * a.nkq * 16 + ln) * a.cbs + cb) * 4;
+        rsc[t] = a.fmt == 4 ? 0.f : gload<float>(wsc[t / TPM] + min(c0 + 16 * (t % TPM) + ln, a.N - 1));
+    }
+    struct BSlot {
+        u32x4 c[NCT];
+    };
+    // unconditional requests at clamped addresses: blocks past the last one
+    // meet zero inputs (the LDS tile is zero there)
+    auto bload = [&](BSlot &b, int c) {
+        const int cc = min(c, nch - 1);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) b.c[t] = gload<u32x4>(wq[t / TPM] + (qoff[t] + cc * 1024));
+    };
+    auto rload = [&](sg_f32x4 *run, int kq) {
+        const int kqc = min(kq, a.nkq - 1);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+            run[t] = a.fmt == 4 ? gload<sg_f32x4>(wsc[t / TPM] + (soff[t] + kqc * 64 * a.cbs))
+                                : sg_f32x4{rsc[t], rsc[t], rsc[t], rsc[t]};
+    };
+
+    // ---- input rows: 8 bf16 per 16-byte request, 16 lanes per row
+    constexpr int ALPR = SG_KC / 8;
+    constexpr int AROWS = 256 / ALPR;
+    constexpr int NAQ = TM / AROWS;
+    static_assert(NAQ >= 1, "tile rows");
+    const int arow0 = tid / ALPR, acol = 8 * (tid % ALPR);
+    int64_t aoff[NAQ];
+#pragma unroll
+    for (int i = 0; i < NAQ; ++i)
+        aoff[i] = (int64_t)(xr0 + min(arow0 + AROWS * i, mcount - 1)) * a.ldx;
+    struct ASlot {
+        u32x4 v[NAQ];
+    };
+    auto aload = [&](ASlot &sl, int c) {
+        const int kk = min(min(c, nch - 1) * SG_KC + acol, K - 8);
+#pragma unroll
+        for (int i = 0; i < NAQ; ++i)
+            sl.v[i] = gload<u32x4>((const pg_bf16 *)a.x + (aoff[i] + kk));
+    };
+    // inputs of block c to LDS; columns past K (and blocks past the last) as zeros
+    auto astore = [&](ASlot &sl, int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < NAQ; ++i) asm volatile("" : "+v"(sl.v[i]));
+        const bool zero = c * SG_KC + acol >= K;
+#pragma unroll
+        for (int i = 0; i < NAQ; ++i)
+            *reinterpret_cast<u32x4 *>(&As[stage][(arow0 + AROWS * i) * SG_LDA + acol]) =
+                zero ? u32x4{0u, 0u, 0u, 0u} : sl.v[i];
+    };
+    auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    // ---- accumulators: C tile (i, t), lane holds rows 4 (l / 16) + r, column l % 16
+    sg_f32x4 acc[MB][NCT], accg[MB][NCT];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+            acc[i][t] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
+            accg[i][t] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    // a group ends after block c when c + 1 is a multiple of the blocks per
+    // group (never inside a row for the per-row format) or at the last block
+    const int gblk = a.ng;
+
+    // block c = 4 kq + u with the scale runs of quad kq
+    auto compute = [&](BSlot &b, const sg_f32x4 *run, int u, int stage, int c) {
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) asm volatile("" : "+v"(b.c[t]));
+        float f[NCT];
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) f[t] = run[t][u] * 0.0625f;  // the signed bytes below hold 16 (q - 8)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            pg_bf16x8 afr[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                afr[i] = *reinterpret_cast<const pg_bf16x8 *>(
+                    &As[stage][(16 * i + ln) * SG_LDA + 32 * lg + 8 * s]);
+#pragma unroll
+            for (int t = 0; t < NCT; ++t) {
+                const uint32_t w = b.c[t][s];
+                const uint32_t ev = (w << 4) & 0xF0F0F0F0u;  // inputs 0, 2, 4, 6
+                const uint32_t od = w & 0xF0F0F0F0u;         // inputs 1, 3, 5, 7
+                u32x4 bw;
+                if constexpr (SF) {
+                    const float sc = f[t];
+                    bw = u32x4{pk_bf16(sbyte<0>(ev) * sc, sbyte<0>(od) * sc),
+                               pk_bf16(sbyte<1>(ev) * sc, sbyte<1>(od) * sc),
+                               pk_bf16(sbyte<2>(ev) * sc, sbyte<2>(od) * sc),
+                               pk_bf16(sbyte<3>(ev) * sc, sbyte<3>(od) * sc)};
+                } else {
+                    bw = u32x4{pk_bf16(sbyte<0>(ev), sbyte<0>(od)), pk_bf16(sbyte<1>(ev), sbyte<1>(od)),
+                               pk_bf16(sbyte<2>(ev), sbyte<2>(od)), pk_bf16(sbyte<3>(ev), sbyte<3>(od))};
+                }
+                const pg_bf16x8 bfr = __builtin_bit_cast(pg_bf16x8, bw);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    accg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr, accg[i][t], 0, 0, 0);
+            }
+        }
+        if (!SF && c < nch && ((c + 1) % gblk == 0 || c + 1 == nch)) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int t = 0; t < NCT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[i][t][r] = fmaf(f[t], accg[i][t][r], acc[i][t][r]);
+                        accg[i][t][r] = 0.f;
+                    }
+        }
+    };
+
+    // ---- pipeline: the codes and inputs of block c are requested SG_NB blocks
+    // earlier (inputs first), the scale runs of a quad one quad earlier, the
+    // inputs go to LDS at the end of block c - 1.  Requests complete in order,
+    // so waiting for the inputs of block c + 1 only forces code requests of
+    // blocks up to c + 1.
+    BSlot bs[SG_NB];
+    ASlot as[SG_NB];
+    sg_f32x4 run[NCT], runn[NCT];
+#pragma unroll
+    for (int u = 0; u < SG_NB; ++u) {
+        aload(as[u], u);
+        bload(bs[u], u);
+    }
+    rload(runn, 0);
+    astore(as[0], 0, 0);
+    lds_barrier();  // block 0 in LDS
+    for (int base = 0; base < npad; base += SG_NB) {
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+            asm volatile("" : "+v"(runn[t]));
+            run[t] = runn[t];
+        }
+        rload(runn, base / SG_NB + 1);
+#pragma unroll
+        for (int u = 0; u < SG_NB; ++u) {
+            const int c = base + u;
+            aload(as[u], c + SG_NB);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(bs[u], run, u, u % 2, c);
+            __builtin_amdgcn_sched_barrier(0);
+            bload(bs[u], c + SG_NB);
+            __builtin_amdgcn_sched_barrier(0);
+            astore(as[(u + 1) % SG_NB], (u + 1) % 2, c + 1);
+            lds_barrier();
+        }
+    }
+    if (SF) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int t = 0; t < NCT; ++t) acc[i][t] = accg[i][t];
+    }
+
+    // ---- epilogue
+    if constexpr (EPI == PG_SILU) {
+#pragma unroll
+        for (int t = 0; t < TPM; ++t) {
+            const int n = c0 + 16 * t + ln;
+            if (n >= a.N)
+                continue;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * i + 4 * lg + r;
+                    if (m < mcount) {
+                        const float g = acc[i][t][r], u = acc[i][t + TPM][r];
+                        ((pg_bf16 *)a.y)[(int64_t)(xr0 + m) * a.ldy + n] =
+                            (pg_bf16)((g / (1.0f + expf(-g))) * u);
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+            const int n = c0 + 16 * t + ln;
+            if (n >= a.N)
+                continue;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * i + 4 * lg + r;
+                    if (m < mcount)
+                        ((float *)a.y)[(int64_t)(xr0 + m) * a.ldy + n] = acc[i][t][r];
                 }
         }
     }
@@ -300,13 +665,132 @@ int launch_pgemm_dense(const coli_qtensor *W, const float *x, float *y, int S, h
         a.ldy = W->O;
         if (S > 64) {
             const dim3 grid((unsigned)((S + 127) / 128), (unsigned)((W->O + PG_BN - 1) / PG_BN));
-            hipLaunchKernelGGL((k_pg<128, 1, PG_Y, true>), grid, dim3(512), 0, st, a);
+            hipLaunchKernelGGL((k_pg<128, 1, PG_Y, true, false>), grid, dim3(512), 0, st, a);
         } else {
             const dim3 grid((unsigned)((S + 63) / 64), (unsigned)((W->O + PG_BN - 1) / PG_BN));
-            hipLaunchKernelGGL((k_pg<64, 1, PG_Y, true>), grid, dim3(512), 0, st, a);
+            hipLaunchKernelGGL((k_pg<64, 1, PG_Y, true, false>), grid, dim3(512), 0, st, a);
         }
     }
     return after_launch("gemm_dense") == COLI_OK ? 1 : -1;
+}
+
+// ---- prefill MoE stages over the routed tile list (gridDim.x = max_tiles
+// rounded up to 8): gate/up + SiLU into bf16 h (routing order), down into f32
+// rows.  Tensors with a packed copy run the weight-streaming kernel on 32-row
+// tiles, the others the producer/consumer kernel on 64-row tiles.
+
+static bool moe_all(const MoeArgs &m, bool (*ok)(const coli_qtensor *)) {
+    const coli_qtensor *all[6] = {m.gate, m.up, m.down, m.sg, m.su, m.sd};
+    for (const coli_qtensor *t : all)
+        if (t && !ok(t))
+            return false;
+    return true;
+}
+
+int pgemm_moe_rows(const MoeArgs &m) {
+    if (m.D % 32 != 0 || m.F % 32 != 0)
+        return 0;
+    if (moe_all(m, mgemv_ok))
+        return PG_MOE_ROWS_PACKED;
+    if (moe_all(m, pgemm_ok))
+        return PG_MOE_ROWS;
+    return 0;
+}
+
+// operands of one projection (matrix index mi of the pair) for either kernel
+static void pg_operand(PgArgs &a, int mi, const coli_qtensor *T, const coli_qtensor *Sh, bool packed) {
+    if (packed) {
+        a.q[mi] = (const uint8_t *)T->pk;
+        a.s[mi] = T->fmt == 4 ? (const float *)((const uint8_t *)T->pk + T->pk_scale_off) : T->s;
+        a.q_stride = T->pk_stride;
+        a.s_stride = T->fmt == 4 ? T->pk_stride / 4 : T->s_stride;
+        const coli_qtensor *H = Sh ? Sh : T;
+        a.sq[mi] = Sh ? (const uint8_t *)H->pk : a.q[mi];
+        a.ss[mi] = Sh ? (H->fmt == 4 ? (const float *)((const uint8_t *)H->pk + H->pk_scale_off) : H->s)
+                      : a.s[mi];
+        a.nkb = (T->I + 127) / 128;
+        a.nkq = (a.nkb + 3) / 4;
+        a.cbs = (T->fmt != 4 || T->gs % 128 == 0) ? 1 : 128 / T->gs;
+        a.rtn = (T->O + 15) / 16;
+        // blocks per scale group (the per-row format: never inside a row)
+        a.ng = T->fmt == 4 ? std::max(1, T->gs / 128) : a.nkb + 1;
+        a.gshift = (T->fmt == 4 && T->gs < 128) ? __builtin_ctz((unsigned)T->gs) : 0;
+    } else {
+        a.q[mi] = (const uint8_t *)T->q;
+        a.s[mi] = T->s;
+        a.q_stride = T->q_stride;
+        a.s_stride = T->s_stride;
+        a.sq[mi] = Sh ? (const uint8_t *)Sh->q : a.q[mi];
+        a.ss[mi] = Sh ? Sh->s : a.s[mi];
+        a.ng = T->ng;
+        a.gshift = T->fmt == 4 ? __builtin_ctz((unsigned)T->gs) : 0;
+    }
+    a.rb = T->row_bytes;
+    a.N = T->O;
+    a.fmt = T->fmt;
+}
+
+template <bool SF>
+static void sg_launch(const PgArgs &a, unsigned gx, bool down, hipStream_t st) {
+    constexpr int MB = PG_MOE_ROWS_PACKED / 16;
+    if (!down)
+        hipLaunchKernelGGL((k_sg<MB, 4, 2, PG_SILU, true, SF>), dim3(gx, (unsigned)((a.N + 127) / 128)),
+                           dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_sg<MB, 4, 1, PG_PART, true, SF>), dim3(gx, (unsigned)((a.N + 255) / 256)),
+                           dim3(256), 0, st, a);
+}
+
+static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, const coli_qtensor *T,
+                         hipStream_t st) {
+    if (packed) {
+        if (T->fmt == 4 && T->gs < 128) sg_launch<true>(a, gx, down, st);
+        else sg_launch<false>(a, gx, down, st);
+    } else if (!down) {
+        hipLaunchKernelGGL((k_pg<PG_MOE_ROWS, 2, PG_SILU, false, true>),
+                           dim3(gx, (unsigned)((a.N + 63) / 64)), dim3(512), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((k_pg<PG_MOE_ROWS, 1, PG_PART, false, true>),
+                           dim3(gx, (unsigned)((a.N + 127) / 128)), dim3(512), 0, st, a);
+    }
+}
+
+int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float *y,
+                     const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,
+                     const int32_t *offsets, int max_tiles) {
+    const bool packed = rows == PG_MOE_ROWS_PACKED;
+    const unsigned gx = (unsigned)((max_tiles + 7) / 8 * 8);
+    PgArgs a;
+    memset(&a, 0, sizeof a);
+    a.tiles = tiles; a.n_tiles = n_tiles; a.counts = counts; a.offsets = offsets;
+    a.E = m.E; a.SK = m.S * m.K; a.S = m.S;
+    {
+        pg_operand(a, 0, m.gate, m.sg, packed);
+        pg_operand(a, 1, m.up, m.su, packed);
+        a.x = xg;
+        a.ldx = m.D;
+        a.K = m.D;
+        a.y = hg;
+        a.ldy = m.F;
+        ProfScope ps("moe_gateup_gemm", m.st);
+        pg_moe_stage(a, gx, false, packed, m.gate, m.st);
+        int rc = after_launch("moe_gateup_gemm");
+        if (rc != COLI_OK) return rc;
+    }
+    if (y == nullptr)
+        return COLI_OK;
+    {
+        pg_operand(a, 0, m.down, m.sd, packed);
+        pg_operand(a, 1, m.down, m.sd, packed);
+        a.x = hg;
+        a.ldx = m.F;
+        a.K = m.F;
+        a.y = y;
+        a.ldy = m.D;
+        ProfScope ps("moe_down_gemm", m.st);
+        pg_moe_stage(a, gx, true, packed, m.down, m.st);
+        return after_launch("moe_down_gemm");
+    }
 }
 
 }  // namespace coli

@@ -70,15 +70,22 @@ PREFILL = [  # (fmt, S, K, E, D, F, gs, shared)
     (2, 12, 2, 5, 128, 64, 0, True),
     (1, 7, 3, 4, 96, 64, 0, False),
     (3, 20, 2, 6, 128, 96, 0, True),
+    (4, 24, 4, 6, 768, 384, 384, True),   # groups of 3 blocks
+    (4, 70, 2, 5, 512, 256, 256, False),  # groups of 2 blocks, experts with several tiles
+    (2, 45, 3, 4, 160, 96, 0, False),     # K not a multiple of the 128-input block
 ]
 
 
+@pytest.mark.parametrize("pack", [True, False], ids=["packed", "unpacked"])
 @pytest.mark.parametrize("case", PREFILL, ids=["fmt{}-S{}-K{}-E{}-D{}-F{}-gs{}-sh{}".format(*c) for c in PREFILL])
-def test_moe_prefill_small(orc, case):
+def test_moe_prefill_small(orc, case, pack):
+    """Packed copies take the weight-streaming kernel (32-row tiles), plain
+    int4 tensors the producer/consumer kernel (64-row tiles), the other
+    formats the generic matrix-core GEMM."""
     need_gpu()
     fmt, S, K, E, D, F, gs, shared = case
     G, U, Dn, sh, x, ids, w = _moe_inputs(300 + hash(case) % 997, fmt, S, K, E, D, F, gs, shared)
-    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w, pack=pack)
     _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_BF16)
 
 
@@ -103,7 +110,8 @@ def test_moe_prefill_repeatable_bitwise(orc):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def test_moe_prefill_config4_full(orc):
+@pytest.mark.parametrize("pack", [True, False], ids=["packed", "unpacked"])
+def test_moe_prefill_config4_full(orc, pack):
     """Prefill MoE at its real shape: S = 544 tokens, 256 experts, top-8 with
     Zipf(1.1) popularity, gate/up 2048x6144 and down 6144x2048 fmt 4 gs 128.
     The pool is drawn on the device; the oracle evaluates 6 sampled tokens
@@ -120,6 +128,9 @@ def test_moe_prefill_config4_full(orc):
     tg = coli.QTensor(4, gq, gsc, F, D, gs)
     tu = coli.QTensor(4, uq, usc, F, D, gs)
     td = coli.QTensor(4, dq, dsc, D, F, gs)
+    if pack:
+        for t in (tg, tu, td):
+            t.pack()
     xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
     ws_bytes = coli.coli_moe_workspace_bytes(E, S, K, F, D, 0)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
