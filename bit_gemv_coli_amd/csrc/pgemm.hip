@@ -360,18 +360,26 @@ __global__ __launch_bounds__(512) void k_pg(PgArgs a) {
 // same columns, so every slice sums 32 distinct inputs and the four slices
 // cover the block.
 //
-// Scales: with groups of >= 128 inputs (and the per-row format) a block lies
-// inside one group; the exact weights 16 (q - 8) accumulate per group and the
-// group's scale / 16 is applied once to the group sum in fp32 (SF = false).
-// Groups of 32 or 64 fold the scale into the bf16 weights (SF = true): each
-// lane's 32 inputs lie in one group.
+// Scales and conversion (SM): with groups of >= 128 inputs (and the
+// per-row format) a block lies inside one group.  There the code q becomes
+// the bf16 number 2 + q / 8 by placing its bits in the mantissa (two shifts,
+// two masks and four byte permutes per 8 codes), so that
+// sum (q - 8) x = 8 (sum (2 + q / 8) x - 3 sum x); a fifth MFMA per row block
+// adds -3 sum x (a constant -3 weight row), and the group's scale times 8 is
+// applied once to the group sum in fp32 (SM_GRP1: groups of one block, the
+// group sum starts from zero in the MFMA; SM_GRPN: longer groups; SM_ROW: the
+// per-row format, one group per row).  The byte permutes pair inputs 0-2, 4-6, 1-3, 5-7, so the
+// input rows are stored in LDS in that order within every 8 inputs.  Groups
+// of 32 or 64 (SM_FOLD) fold the scale into the bf16 weights instead, each
+// lane's 32 inputs lying in one group.
 constexpr int SG_KC = 128;         // inputs per block
 constexpr int SG_LDA = SG_KC + 8;  // LDS row stride of the input tile (bf16 elements)
 constexpr int SG_NB = 4;           // blocks in flight (= blocks per scale run)
 
 typedef float sg_f32x4 __attribute__((ext_vector_type(4)));
+enum { SM_FOLD = 0, SM_GRP1 = 1, SM_GRPN = 2, SM_ROW = 3 };
 
-template <int MB, int NCT, int NMAT, int EPI, bool MOE, bool SF>
+template <int MB, int NCT, int NMAT, int EPI, bool MOE, int SM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sg(PgArgs a) {
     constexpr int TM = 16 * MB;       // input rows per tile
     constexpr int TPM = NCT / NMAT;   // 16-row weight tiles per matrix per wavefront
@@ -429,14 +437,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // ---- weight tiles of this wavefront (tiles past the matrix clamped; their
     // outputs are dropped): code and scale-run offsets within the matrix
     int qoff[NCT], soff[NCT];
-    float rsc[NCT];  // per-row scale (fmt 2)
+    float rsc[NCT];  // per-row scale (SM_ROW)
+    constexpr bool SF = SM == SM_FOLD;
     const int cb = SF ? (lg >> (a.gshift - 5)) : 0;  // this lane's group slot in a block
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
         const int tile = min((c0 + 16 * (t % TPM)) >> 4, a.rtn - 1);
         qoff[t] = tile * a.nkb * 1024 + 16 * lane;
         soff[t] = ((tile * a.nkq * 16 + ln) * a.cbs + cb) * 4;
-        rsc[t] = a.fmt == 4 ? 0.f : gload<float>(wsc[t / TPM] + min(c0 + 16 * (t % TPM) + ln, a.N - 1));
+        if (SM == SM_ROW)
+            rsc[t] = gload<float>(wsc[t / TPM] + min(c0 + 16 * (t % TPM) + ln, a.N - 1));
     }
     struct BSlot {
         u32x4 c[NCT];
@@ -450,10 +460,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     auto rload = [&](sg_f32x4 *run, int kq) {
         const int kqc = min(kq, a.nkq - 1);
+        if constexpr (SM != SM_ROW)
 #pragma unroll
-        for (int t = 0; t < NCT; ++t)
-            run[t] = a.fmt == 4 ? gload<sg_f32x4>(wsc[t / TPM] + (soff[t] + kqc * 64 * a.cbs))
-                                : sg_f32x4{rsc[t], rsc[t], rsc[t], rsc[t]};
+            for (int t = 0; t < NCT; ++t) run[t] = gload<sg_f32x4>(wsc[t / TPM] + (soff[t] + kqc * 64 * a.cbs));
     };
 
     // ---- input rows: 8 bf16 per 16-byte request, 16 lanes per row
@@ -475,27 +484,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int i = 0; i < NAQ; ++i)
             sl.v[i] = gload<u32x4>((const pg_bf16 *)a.x + (aoff[i] + kk));
     };
-    // inputs of block c to LDS; columns past K (and blocks past the last) as zeros
+    // inputs of block c to LDS, every 8 in the order 0 2 4 6 1 3 5 7; columns
+    // past K (and blocks past the last) as zeros
     auto astore = [&](ASlot &sl, int stage, int c) {
 #pragma unroll
         for (int i = 0; i < NAQ; ++i) asm volatile("" : "+v"(sl.v[i]));
         const bool zero = c * SG_KC + acol >= K;
 #pragma unroll
-        for (int i = 0; i < NAQ; ++i)
+        for (int i = 0; i < NAQ; ++i) {
+            const u32x4 v = sl.v[i];
+            const u32x4 o = {__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                             __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
             *reinterpret_cast<u32x4 *>(&As[stage][(arow0 + AROWS * i) * SG_LDA + acol]) =
-                zero ? u32x4{0u, 0u, 0u, 0u} : sl.v[i];
+                zero ? u32x4{0u, 0u, 0u, 0u} : o;
+        }
     };
     auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
     // ---- accumulators: C tile (i, t), lane holds rows 4 (l / 16) + r, column l % 16
-    sg_f32x4 acc[MB][NCT], accg[MB][NCT];
+    const sg_f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    sg_f32x4 acc[MB][NCT], accg[MB][NCT], corr[MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i) {
+        corr[i] = zero4;
 #pragma unroll
         for (int t = 0; t < NCT; ++t) {
-            acc[i][t] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
-            accg[i][t] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[i][t] = zero4;
+            accg[i][t] = zero4;
         }
+    }
+    // bf16 -3 in every element: the weight row that adds -3 sum x
+    const pg_bf16x8 neg3 = __builtin_bit_cast(pg_bf16x8, u32x4{0xC040C040u, 0xC040C040u, 0xC040C040u, 0xC040C040u});
     // a group ends after block c when c + 1 is a multiple of the blocks per
     // group (never inside a row for the per-row format) or at the last block
     const int gblk = a.ng;
@@ -506,7 +525,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int t = 0; t < NCT; ++t) asm volatile("" : "+v"(b.c[t]));
         float f[NCT];
 #pragma unroll
-        for (int t = 0; t < NCT; ++t) f[t] = run[t][u] * 0.0625f;  // the signed bytes below hold 16 (q - 8)
+        for (int t = 0; t < NCT; ++t)  // SM_FOLD weights hold 16 (q - 8), the others (q - 8) / 8
+            f[t] = (SM == SM_ROW ? rsc[t] : run[t][u]) * (SF ? 0.0625f : 8.0f);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             pg_bf16x8 afr[MB];
@@ -514,38 +534,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int i = 0; i < MB; ++i)
                 afr[i] = *reinterpret_cast<const pg_bf16x8 *>(
                     &As[stage][(16 * i + ln) * SG_LDA + 32 * lg + 8 * s]);
+            const bool fresh = SM == SM_GRP1 && s == 0;  // the group sum starts here
+            if constexpr (!SF) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    corr[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], neg3, fresh ? zero4 : corr[i], 0, 0, 0);
+            }
 #pragma unroll
             for (int t = 0; t < NCT; ++t) {
-                const uint32_t w = b.c[t][s];
-                const uint32_t ev = (w << 4) & 0xF0F0F0F0u;  // inputs 0, 2, 4, 6
-                const uint32_t od = w & 0xF0F0F0F0u;         // inputs 1, 3, 5, 7
+                const uint32_t w = b.c[t][s];  // two's-complement nibbles q - 8
                 u32x4 bw;
                 if constexpr (SF) {
+                    const uint32_t ev = (w << 4) & 0xF0F0F0F0u;  // 16 (q - 8) of inputs 0, 2, 4, 6
+                    const uint32_t od = w & 0xF0F0F0F0u;         // of inputs 1, 3, 5, 7
                     const float sc = f[t];
-                    bw = u32x4{pk_bf16(sbyte<0>(ev) * sc, sbyte<0>(od) * sc),
-                               pk_bf16(sbyte<1>(ev) * sc, sbyte<1>(od) * sc),
-                               pk_bf16(sbyte<2>(ev) * sc, sbyte<2>(od) * sc),
-                               pk_bf16(sbyte<3>(ev) * sc, sbyte<3>(od) * sc)};
+                    bw = u32x4{pk_bf16(sbyte<0>(ev) * sc, sbyte<1>(ev) * sc),
+                               pk_bf16(sbyte<2>(ev) * sc, sbyte<3>(ev) * sc),
+                               pk_bf16(sbyte<0>(od) * sc, sbyte<1>(od) * sc),
+                               pk_bf16(sbyte<2>(od) * sc, sbyte<3>(od) * sc)};
                 } else {
-                    bw = u32x4{pk_bf16(sbyte<0>(ev), sbyte<0>(od)), pk_bf16(sbyte<1>(ev), sbyte<1>(od)),
-                               pk_bf16(sbyte<2>(ev), sbyte<2>(od)), pk_bf16(sbyte<3>(ev), sbyte<3>(od))};
+                    // q << 3 in the low mantissa byte of bf16 0x40nn: 2 + q / 8
+                    const uint32_t lo = ((w << 3) & 0x78787878u) ^ 0x40404040u;  // inputs 0, 2, 4, 6
+                    const uint32_t hi = ((w >> 1) & 0x78787878u) ^ 0x40404040u;  // inputs 1, 3, 5, 7
+                    bw = u32x4{__builtin_amdgcn_perm(0x40404040u, lo, 0x05010400u),
+                               __builtin_amdgcn_perm(0x40404040u, lo, 0x05030402u),
+                               __builtin_amdgcn_perm(0x40404040u, hi, 0x05010400u),
+                               __builtin_amdgcn_perm(0x40404040u, hi, 0x05030402u)};
                 }
                 const pg_bf16x8 bfr = __builtin_bit_cast(pg_bf16x8, bw);
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
-                    accg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr, accg[i][t], 0, 0, 0);
+                    accg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr, fresh ? zero4 : accg[i][t], 0, 0, 0);
             }
         }
-        if (!SF && c < nch && ((c + 1) % gblk == 0 || c + 1 == nch)) {
+        const bool gend = SM == SM_GRP1 || (SM == SM_GRPN && (c + 1) % gblk == 0) || c + 1 == nch;
+        if (!SF && c < nch && gend) {
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int t = 0; t < NCT; ++t)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        acc[i][t][r] = fmaf(f[t], accg[i][t][r], acc[i][t][r]);
-                        accg[i][t][r] = 0.f;
+                        acc[i][t][r] = fmaf(f[t], accg[i][t][r] + corr[i][r], acc[i][t][r]);
+                        if (SM != SM_GRP1)
+                            accg[i][t][r] = 0.f;
                     }
+            if (SM != SM_GRP1)
+#pragma unroll
+                for (int i = 0; i < MB; ++i) corr[i] = zero4;
         }
     };
 
@@ -730,22 +766,24 @@ static void pg_operand(PgArgs &a, int mi, const coli_qtensor *T, const coli_qten
     a.fmt = T->fmt;
 }
 
-template <bool SF>
+template <int SM>
 static void sg_launch(const PgArgs &a, unsigned gx, bool down, hipStream_t st) {
     constexpr int MB = PG_MOE_ROWS_PACKED / 16;
     if (!down)
-        hipLaunchKernelGGL((k_sg<MB, 4, 2, PG_SILU, true, SF>), dim3(gx, (unsigned)((a.N + 127) / 128)),
+        hipLaunchKernelGGL((k_sg<MB, 4, 2, PG_SILU, true, SM>), dim3(gx, (unsigned)((a.N + 127) / 128)),
                            dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_sg<MB, 4, 1, PG_PART, true, SF>), dim3(gx, (unsigned)((a.N + 255) / 256)),
+        hipLaunchKernelGGL((k_sg<MB, 4, 1, PG_PART, true, SM>), dim3(gx, (unsigned)((a.N + 255) / 256)),
                            dim3(256), 0, st, a);
 }
 
 static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, const coli_qtensor *T,
                          hipStream_t st) {
     if (packed) {
-        if (T->fmt == 4 && T->gs < 128) sg_launch<true>(a, gx, down, st);
-        else sg_launch<false>(a, gx, down, st);
+        if (T->fmt == 4 && T->gs < 128) sg_launch<SM_FOLD>(a, gx, down, st);
+        else if (T->fmt == 4 && T->gs == 128) sg_launch<SM_GRP1>(a, gx, down, st);
+        else if (T->fmt == 4) sg_launch<SM_GRPN>(a, gx, down, st);
+        else sg_launch<SM_ROW>(a, gx, down, st);
     } else if (!down) {
         hipLaunchKernelGGL((k_pg<PG_MOE_ROWS, 2, PG_SILU, false, true>),
                            dim3(gx, (unsigned)((a.N + 63) / 64)), dim3(512), 0, st, a);
