@@ -11,7 +11,9 @@ block touches does not sit in the 256 MB last-level cache.
 value = algorithmic HBM bytes per block / block time (GB/s).  Per-kernel
 durations come from HIP events the library records on the launch stream
 around each kernel inside the timed region.  Side measurements ("extra")
-cover the single fmt-4 GEMV and the 6144x6144 format sweep.
+cover the single fmt-4 GEMV, the 6144x6144 format sweep, the ceilings a
+streaming read and a matrix-core loop reach on this part, the S=544 prefill
+GEMM and MoE block, and the 75-layer decode stream.
 
 Prints ONE JSON line.  N > 1 GPUs is not supported (one-GPU build).
 """
@@ -255,6 +257,7 @@ def side_measurements(coli, sd, np, torch, log):
             log(f"sweep {key}: {us:.2f} us  {gbs:.0f} GB/s")
             del Ts, q, s
     out["gemv_6144x6144_ring"] = sweep
+    out.update(ceiling_probes(coli, torch, log))
     out.update(prefill_measurements(coli, sd, np, torch, log, timed))
     out.update(layer_stream(coli, sd, np, torch, log))
     return out
@@ -262,8 +265,9 @@ def side_measurements(coli, sd, np, torch, log):
 
 def prefill_measurements(coli, sd, np, torch, log, timed):
     """S = 544 prefill: the dense 6144x6144 fmt-4 GEMM (compute-bound) and the
-    Zipf(1.1)-routed 256-expert MoE block with gs 128 (HBM-bound: the routed
-    union covers ~250 experts)."""
+    256-expert MoE block with gs 128 on packed experts, routed by Zipf(1.1)
+    popularity (HBM-bound: the union covers ~250 experts) and, as a labelled
+    variant, Zipf(2.5) (union ~95, head experts with hundreds of rows)."""
     out = {}
     dev = "cuda"
     st = torch.cuda.current_stream()
@@ -281,38 +285,89 @@ def prefill_measurements(coli, sd, np, torch, log, timed):
         del T, q, s
 
     gs = 128
-    r = sd.rng(4)
-    xh = sd.gen_x(r, S, D)
-    ids, w = sd.gen_routing_zipf(r, S, K, E, 1.1)
     gq, gsc = sd.pool_on_device(200, 4, E, F, D, gs)
     uq, usc = sd.pool_on_device(201, 4, E, F, D, gs)
     dq, dsc = sd.pool_on_device(202, 4, E, D, F, gs)
     tg = coli.QTensor(4, gq, gsc, F, D, gs)
     tu = coli.QTensor(4, uq, usc, F, D, gs)
     td = coli.QTensor(4, dq, dsc, D, F, gs)
-    xd = torch.from_numpy(xh).to(dev)
-    idd = torch.from_numpy(ids).to(dev)
-    wd = torch.from_numpy(w).to(dev)
-    outb = torch.empty((S, D), device=dev)
+    for t in (tg, tu, td):  # upload-time repack: the prefill kernels stream the packed blocks
+        t.pack()
     wsb = coli.coli_moe_workspace_bytes(E, S, K, F, D, 0)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    us = timed(lambda i: coli.check(coli.coli_moe_block(tg, tu, td, xd, S, idd, wd, K, None, None,
-                                                        None, outb, ws, wsb, st)), 10)
-    union = int(np.unique(ids).size)
-    flops = 2.0 * S * K * 3 * F * D
-    nbytes = union * (2 * qbytes(4, F, D, gs) + qbytes(4, D, F, gs)) + 2 * S * D * 4 + S * K * 8
-    tf = flops / (us * 1e-6) / 1e12
-    gbs = nbytes / (us * 1e-6) / 1e9
-    ideal_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)) * 1e6
-    out["prefill_moe_544_zipf1.1_g128"] = {
-        "us": us, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "GBps": gbs,
-        "frac_hbm": gbs / HBM_PEAK_GBS, "union_experts": union, "roofline_us": ideal_us,
-        "frac_roofline": ideal_us / us}
-    log(f"prefill MoE 544 zipf: {us:.1f} us  {tf:.1f} TFLOP/s  {gbs:.0f} GB/s  union {union}  "
-        f"({100 * ideal_us / us:.1f}% of max(F/P, B/BW))")
+    outb = torch.empty((S, D), device=dev)
+    for zs, key in ((1.1, "prefill_moe_544_zipf1.1_g128"), (2.5, "prefill_moe_544_zipf2.5_g128_variant")):
+        r = sd.rng(4)
+        xh = sd.gen_x(r, S, D)
+        ids, w = sd.gen_routing_zipf(r, S, K, E, zs)
+        xd = torch.from_numpy(xh).to(dev)
+        idd = torch.from_numpy(ids).to(dev)
+        wd = torch.from_numpy(w).to(dev)
+
+        def blk(i):
+            coli.check(coli.coli_moe_block(tg, tu, td, xd, S, idd, wd, K, None, None, None, outb,
+                                           ws, wsb, st))
+        us = timed(blk, 10)
+        coli.coli_prof_reset()
+        coli.coli_prof_enable(True)
+        for i in range(5):
+            blk(i)
+        torch.cuda.synchronize()
+        coli.coli_prof_enable(False)
+        kern = {}
+        for tag in coli.coli_prof_tags():
+            n, tot = coli.coli_prof_read(tag)
+            if n > 0 and not tag.startswith("probe") and tag != "pack":
+                kern[tag] = tot / n * 1e3
+        cnt = np.bincount(ids.ravel(), minlength=E)
+        union = int((cnt > 0).sum())
+        flops = 2.0 * S * K * 3 * F * D
+        nbytes = union * (2 * qbytes(4, F, D, gs) + qbytes(4, D, F, gs)) + 2 * S * D * 4 + S * K * 8
+        tf = flops / (us * 1e-6) / 1e12
+        gbs = nbytes / (us * 1e-6) / 1e9
+        ideal_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)) * 1e6
+        out[key] = {
+            "us": us, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "GBps": gbs,
+            "frac_hbm": gbs / HBM_PEAK_GBS, "union_experts": union, "max_rows": int(cnt.max()),
+            "experts_ge64_rows": int((cnt >= 64).sum()), "roofline_us": ideal_us,
+            "frac_roofline": ideal_us / us, "kernels_us": kern}
+        log(f"prefill MoE 544 zipf{zs}: {us:.1f} us  {tf:.1f} TFLOP/s  {gbs:.0f} GB/s  union {union}  "
+            f"({100 * ideal_us / us:.1f}% of max(F/P, B/BW) = {ideal_us:.0f} us)  {kern}")
     del tg, tu, td, gq, gsc, uq, usc, dq, dsc, ws
     torch.cuda.empty_cache()
     return out
+
+
+def ceiling_probes(coli, torch, log):
+    """What trivial kernels reach on this part: a streaming read of 4 GiB and a
+    loop of independent bf16 32x32x16 matrix-core products."""
+    st = torch.cuda.current_stream()
+    sink = torch.zeros(1, device="cuda")
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(n):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3  # s
+
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    t = timed(lambda: coli.check(coli.coli_probe_read(buf, sink, st), "coli_probe_read"), 5)
+    read_gbs = buf.numel() / t / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    wg, it = 2048, 1000
+    t = timed(lambda: coli.check(coli.coli_probe_mfma(wg, it, sink, st), "coli_probe_mfma"), 3)
+    mfma_tf = wg * it * coli.PROBE_MFMA_FLOPS_PER_WG_ITER / t / 1e12
+    log(f"ceilings: streaming read {read_gbs:.0f} GB/s ({100 * read_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), "
+        f"bf16 MFMA loop {mfma_tf:.0f} TFLOP/s ({100 * mfma_tf / BF16_PEAK_TFLOPS:.1f}% of 2.5 PFLOP/s)")
+    return {"measured_ceilings": {"stream_read_GBps": read_gbs, "mfma_bf16_TFLOPs": mfma_tf,
+                                  "stream_read_frac_spec": read_gbs / HBM_PEAK_GBS,
+                                  "mfma_bf16_frac_spec": mfma_tf / BF16_PEAK_TFLOPS}}
 
 
 def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):

@@ -70,6 +70,8 @@ def _load():
         "coli_prof_read": (i64, [C.c_char_p, vp]),
         "coli_prof_tag": (C.c_char_p, [i32]),
         "coli_version": (C.c_char_p, []),
+        "coli_probe_read": (i32, [vp, sz, vp, vp]),
+        "coli_probe_mfma": (i32, [i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -86,7 +88,7 @@ def exported_symbols():
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
-            "coli_prof_tag", "coli_version"]
+            "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma"]
 
 
 def _ptr(t):
@@ -187,6 +189,20 @@ def coli_stats():
 
 def coli_set_fail_after(n: int) -> None:
     _load().coli_set_fail_after(n)
+
+
+def coli_probe_read(buf, sink, stream=None) -> int:
+    """Stream the bytes of device tensor `buf` once (HBM read probe)."""
+    return _load().coli_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                   _stream(stream))
+
+
+def coli_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> int:
+    """workgroups x 4 wavefronts x 8 x iters bf16 32x32x16 products."""
+    return _load().coli_probe_mfma(int(workgroups), int(iters), _ptr(sink), _stream(stream))
+
+
+PROBE_MFMA_FLOPS_PER_WG_ITER = 4 * 8 * 2 * 32 * 32 * 16
 
 
 def coli_prof_enable(on: bool) -> None:

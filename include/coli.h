@@ -258,6 +258,19 @@ int64_t coli_prof_read(const char *tag, double *total_ms);
 /* Tag of the i-th distinct kernel seen by the profiler (NULL past the end). */
 const char *coli_prof_tag(int i);
 
+/* Ceilings of this GPU measured by trivial kernels (diagnostics; not part
+ * of the matmul path), timed by the caller around the call on `stream`:
+ *   coli_probe_read   streams `bytes` (a multiple of 16) of the device buffer
+ *                     `buf` (16-byte aligned) once through the vector loads;
+ *   coli_probe_mfma   runs `workgroups` x 4 wavefronts, each issuing
+ *                     8 * iters independent v_mfma_f32_32x32x16_bf16
+ *                     (32768 flops each) -- the bf16 matrix-core rate.
+ * `sink` is one device float that is written only in a case the inputs make
+ * impossible.  Returns COLI_OK, COLI_DECLINED on bad arguments, or
+ * COLI_HIP_ERROR. */
+int coli_probe_read(const void *buf, size_t bytes, float *sink, void *stream);
+int coli_probe_mfma(int workgroups, int iters, float *sink, void *stream);
+
 /* Library version string. */
 const char *coli_version(void);
 
