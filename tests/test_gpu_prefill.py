@@ -24,15 +24,20 @@ GEMM = [
     (2, 100, 256, 0, 7, 1), (2, 64, 96, 0, 129, 1),
     (1, 90, 128, 0, 12, 1), (1, 33, 96, 0, 70, 2),
     (3, 77, 256, 0, 6, 1), (3, 128, 160, 0, 40, 1),
+    # > 64 rows: packed fmt-4 tensors with gs <= 128 take the weight-streaming
+    # kernel (128 x 128 tiles; ragged rows, columns and a partial last block)
+    (4, 300, 384, 128, 200, 1), (4, 130, 256, 32, 130, 2), (4, 96, 160, 32, 77, 1),
+    (4, 272, 1024, 64, 129, 1),
 ]
 
 
+@pytest.mark.parametrize("pack", [False, True], ids=["plain", "packed"])
 @pytest.mark.parametrize("case", GEMM, ids=["fmt{}-O{}-I{}-gs{}-S{}-n{}".format(*c) for c in GEMM])
-def test_qmatmul_prefill(orc, case):
+def test_qmatmul_prefill(orc, case, pack):
     need_gpu()
     fmt, O, I, gs, S, n = case
     W, x = make_case(fmt, O, I, gs, S, seed=200 + hash(case) % 1000, n=n if n > 1 else None)
-    T = qtensor(W)
+    T = qtensor(W, pack=pack and coli.coli_packed_bytes(fmt, n, O, I, gs) > 0)
     y = gpu_qmatmul(T, x, n)
     for e in range(n):
         y_ref, A = orc.qmatmul(W.expert(e), x)
@@ -50,12 +55,13 @@ def test_qmatmul_prefill_fallback_layouts(orc):
         assert_within(y, y_ref, A, TOL_BF16, f"fallback {fmt} {I} {gs}")
 
 
+@pytest.mark.parametrize("pack", [False, True], ids=["plain", "packed"])
 @pytest.mark.parametrize("gs", [64, 128])
-def test_qmatmul_prefill_dense_544_full(orc, gs):
+def test_qmatmul_prefill_dense_544_full(orc, gs, pack):
     """S = 544 x 6144 x 6144 fmt 4: every output of 24 sampled input rows."""
     need_gpu()
     W, x = make_case(4, 6144, 6144, gs, 544, seed=544 + gs)
-    y = gpu_qmatmul(qtensor(W), x)[0]
+    y = gpu_qmatmul(qtensor(W, pack=pack), x)[0]
     rows = np.sort(sd.rng(1).choice(544, 24, replace=False))
     y_ref, A = orc.qmatmul(W, x[rows])
     assert_within(y[rows], y_ref, A, TOL_BF16, f"dense 544 g{gs}")
