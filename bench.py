@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the S=544 prefill measurements (dense GEMM and MoE block); prints "
+                         "their JSON (for profiling those kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (reference for the "
                          "HBM byte counters)")
@@ -111,6 +114,10 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.prefill_only:
+        print(json.dumps(prefill_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
+        return
 
     # ---- inputs ----------------------------------------------------------
     log("drawing the 256-expert fmt-4 pool on the device")
@@ -210,11 +217,9 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def side_measurements(coli, sd, np, torch, log):
-    """Single fmt-4 GEMV (1024x2048, latency) and the 6144x6144 format sweep
-    (ring of distinct copies >= 1 GiB so each launch streams from HBM)."""
-    out = {}
-    dev = "cuda"
+def make_timed(torch):
+    """timed(fn, n): 3 untimed calls fn(i), then the mean us of n calls, by
+    events on the current stream."""
     st = torch.cuda.current_stream()
 
     def timed(fn, n):
@@ -228,6 +233,16 @@ def side_measurements(coli, sd, np, torch, log):
         b.record(st)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n * 1e3  # us
+    return timed
+
+
+def side_measurements(coli, sd, np, torch, log):
+    """Single fmt-4 GEMV (1024x2048, latency) and the 6144x6144 format sweep
+    (ring of distinct copies >= 1 GiB so each launch streams from HBM)."""
+    out = {}
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    timed = make_timed(torch)
 
     # config 1: one matrix, back-to-back launches (cache-resident; latency)
     q, s = sd.pool_on_device(7, 4, 1, 1024, 2048, 64)
