@@ -162,7 +162,9 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 
 // launch shapes: KS wavefronts along the inputs of one 16-row tile, NW
 // wavefronts per workgroup (NW / KS tiles); measured best for the decode MoE
-// block: gate/up 2 x 4, down 1 x 4
+// block: gate/up 2 x 4, down 1 x 4; for one 6144 x 6144 matrix 3 x 6 (two
+// tiles share a workgroup's input staging: 7.7 us at S = 1 against 8.5 us
+// for 4 x 4, 18.7 against 22.8 us at S = 4)
 #ifndef COLI_MG_KS_GATEUP
 #define COLI_MG_KS_GATEUP 2
 #endif
@@ -176,10 +178,10 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 #define COLI_MG_NW_DOWN 4
 #endif
 #ifndef COLI_MG_KS_DENSE
-#define COLI_MG_KS_DENSE 4
+#define COLI_MG_KS_DENSE 3
 #endif
 #ifndef COLI_MG_NW_DENSE
-#define COLI_MG_NW_DENSE 4
+#define COLI_MG_NW_DENSE 6
 #endif
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
