@@ -27,6 +27,9 @@ SMALL = [
     (1, 4, 70, 0, 3, 1), (1, 2, 5, 0, 1, 1), (1, 33, 1040, 0, 2, 1), (1, 8, 4096, 0, 4, 2),
     (3, 5, 130, 0, 2, 1), (3, 3, 7, 0, 1, 1), (3, 2, 66, 0, 1, 1), (3, 19, 2080, 0, 4, 1),
     (3, 12, 64, 0, 3, 2),
+    # more inputs than one LDS segment holds at S = 4 (6656): the matrix-core
+    # kernel restages the inputs between segments
+    (4, 150, 8320, 64, 4, 1), (2, 40, 13312 + 32, 0, 4, 1),
 ]
 
 
