@@ -183,6 +183,10 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 #ifndef COLI_MG_NW_DENSE
 #define COLI_MG_NW_DENSE 6
 #endif
+// quads of blocks in flight per wavefront in the dense GEMV
+#ifndef COLI_MG_NBQ_DENSE
+#define COLI_MG_NBQ_DENSE 2
+#endif
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
 constexpr int MG_NBK = 4;
@@ -197,8 +201,8 @@ __host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3)
 
 // NT input rows per tile (1..4); CB groups per 128-input block (1, 2, 4);
 // KS wavefronts share one 16-row tile along the inputs; NMAT matrices (gate
-// and up share their rows).
-template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW>
+// and up share their rows); NBQ quads of blocks in flight per wavefront.
+template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ = 2>
 __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     static_assert(NW % KS == 0, "whole tiles per workgroup");
     constexpr int TPW = NW / KS;
@@ -340,12 +344,12 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
             for (int q = 0; q < 4; ++q) acc[st][m][q] = 0.f;
 
     // requests for one quad of 128-input blocks (codes and group scales);
-    // two batches alternate so one is in flight while the other is computed
+    // NBQ batches rotate: each is re-requested as soon as it is computed
     struct Batch {
         u32x4 cw[MG_NBK][NMAT];
         f32x4 sq[NMAT][GROUPED ? NSET : 1];  // the quad's 4 scales of each set's group slot
     };
-    Batch bA, bB;
+    Batch bq[NBQ];
     // kbg: first block of a quad (a multiple of 4); blocks past kb_last
     // re-read kb_last (requests are unconditional, so the compiler's load
     // counting sees straight-line code and waits for one batch at a time)
@@ -472,10 +476,11 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         const int klen = min(KSEG, kpad);
         const int nb8 = klen / 8;
         share(klen / 128, kb_beg, kb_end);
-        load_batch(bA, kb_beg, kb_end - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_batch(bB, kb_beg + MG_NBK, kb_end - 1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < NBQ; ++u) {
+            load_batch(bq[u], kb_beg + u * MG_NBK, kb_end - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         stage_store(nb8, 0);
         for (int base = UN * NTH; base < NT * nb8; base += UN * NTH) {
             stage_load(0, nb8, base);
@@ -487,24 +492,26 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     }
     for (int sgi = 0;;) {
         const int kg0 = sgi * (KSEG / 128);
-        // A and B are in flight; each is re-requested as soon as it is consumed
+        // all NBQ batches are in flight; each is re-requested as soon as it
+        // is consumed
         const int nq = (kb_end - kb_beg + 3) / 4;
         int kb = kb_beg;
         // (scheduling fences keep each batch's use after the other's request,
         // so the wait before a batch never covers the batch behind it)
-        for (int q = 0; q + 2 < nq; q += 2, kb += 2 * MG_NBK) {
-            compute_batch(bA, kb, kb_end);
-            __builtin_amdgcn_sched_barrier(0);
-            load_batch(bA, kg0 + kb + 2 * MG_NBK, kg0 + kb_end - 1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_batch(bB, kb + MG_NBK, kb_end);
-            __builtin_amdgcn_sched_barrier(0);
-            load_batch(bB, kg0 + kb + 3 * MG_NBK, kg0 + kb_end - 1);
+        for (int q = 0; q + NBQ < nq; q += NBQ, kb += NBQ * MG_NBK) {
+#pragma unroll
+            for (int u = 0; u < NBQ; ++u) {
+                compute_batch(bq[u], kb + u * MG_NBK, kb_end);
+                __builtin_amdgcn_sched_barrier(0);
+                load_batch(bq[u], kg0 + kb + (u + NBQ) * MG_NBK, kg0 + kb_end - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NBQ; ++u) {
+            compute_batch(bq[u], kb + u * MG_NBK, kb_end);
             __builtin_amdgcn_sched_barrier(0);
         }
-        compute_batch(bA, kb, kb_end);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_batch(bB, kb + MG_NBK, kb_end);
         if (++sgi >= a.nseg)
             break;
         // ---- next segment: restage the inputs, then its first two batches
@@ -518,10 +525,11 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         }
         lds_barrier();
         share(klen / 128, kb_beg, kb_end);
-        load_batch(bA, k0 / 128 + kb_beg, k0 / 128 + kb_end - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_batch(bB, k0 / 128 + kb_beg + MG_NBK, k0 / 128 + kb_end - 1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < NBQ; ++u) {
+            load_batch(bq[u], k0 / 128 + kb_beg + u * MG_NBK, k0 / 128 + kb_end - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // --- reduce: KS wavefronts x group slots x digits -> one value per (row, input row)
@@ -747,23 +755,23 @@ static MgArgs mg_args_for(const coli_qtensor *W) {
     return a;
 }
 
-template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW>
+template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ>
 static void mg_launch(MgArgs a, int groups, hipStream_t st, const ProfScope &ps) {
     size_t lds;
     plan_lds(NT, CB, NMAT, NW, a.I, a.kseg, a.nseg, lds);
     constexpr int TPW = NW / KS;
     const int tiles = (a.O + 15) / 16;
     const dim3 grid((unsigned)((tiles + TPW - 1) / TPW), (unsigned)groups);
-    hipExtLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW>), grid, dim3(NW * 64),
+    hipExtLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW, NBQ>), grid, dim3(NW * 64),
                           (uint32_t)lds, st, ps.start(), ps.stop(), 0, a);
 }
 
-template <int NT, bool GROUPED, int NMAT, int EPI, int KS, int NW>
+template <int NT, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ = 2>
 static int mg_dispatch_cb(int cb, const MgArgs &a, int groups, hipStream_t st, const ProfScope &ps) {
     switch (cb) {
-    case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS, NW>(a, groups, st, ps); return 1;
-    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS, NW>(a, groups, st, ps); return 1;
-    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS, NW>(a, groups, st, ps); return 1;
+    case 1: mg_launch<NT, 1, GROUPED, NMAT, EPI, KS, NW, NBQ>(a, groups, st, ps); return 1;
+    case 2: mg_launch<NT, 2, GROUPED, NMAT, EPI, KS, NW, NBQ>(a, groups, st, ps); return 1;
+    default: mg_launch<NT, 4, GROUPED, NMAT, EPI, KS, NW, NBQ>(a, groups, st, ps); return 1;
     }
 }
 
@@ -782,8 +790,8 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     ProfScope ps("mgemv", st, true);
     int ok;
 #define MG_CASE(NTV)                                                                          \
-    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st, ps) \
-           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE>(cb, a, W->n, st, ps)
+    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
+           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps)
     switch (S) {
     case 1: MG_CASE(1); break;
     case 2: MG_CASE(2); break;
