@@ -254,6 +254,19 @@ def side_measurements(coli, sd, np, torch, log):
     out["gemv_1024x2048_g64_us"] = us
     log(f"gemv 1024x2048 g64: {us:.2f} us/call")
 
+    # what a trivial streaming read of one matrix-sized buffer reaches per
+    # launch (same ring discipline): the per-launch ceiling at this size
+    sink = torch.zeros(1, device=dev)
+    mb21 = qbytes(4, 6144, 6144, 64)
+    nring = max(2, -(-(1 << 30) // mb21))
+    bufs = [torch.empty(mb21 // 16 * 16, dtype=torch.uint8, device=dev) for _ in range(nring)]
+    us_probe = timed(lambda i: coli.check(coli.coli_probe_read(bufs[i % nring], sink, st), "probe"), 4 * nring)
+    probe_gbs = bufs[0].numel() / (us_probe * 1e-6) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    out["stream_read_one_matrix"] = {"bytes": mb21, "us": us_probe, "GBps": probe_gbs}
+    log(f"streaming read of one {mb21 / 1e6:.1f} MB matrix per launch: {us_probe:.2f} us ({probe_gbs:.0f} GB/s)")
+
     sweep = {}
     for fmt, gs in ((4, 64), (4, 128), (2, 0), (1, 0), (3, 0)):
         for S in (1, 4):
@@ -268,7 +281,9 @@ def side_measurements(coli, sd, np, torch, log):
             us = timed(lambda i: coli.coli_qmatmul(Ts[i % ncopy], x, y, S, st), 4 * ncopy)
             gbs = (mb + S * 6144 * 8) / (us * 1e-6) / 1e9
             key = f"fmt{fmt}" + (f"_g{gs}" if fmt == 4 else "") + f"_S{S}"
-            sweep[key] = {"us": us, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+            sweep[key] = {"us": us, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                          "frac_stream_read_same_launch_size":
+                              gbs / probe_gbs if abs(mb - mb21) < 0.2 * mb21 else None}
             log(f"sweep {key}: {us:.2f} us  {gbs:.0f} GB/s")
             del Ts, q, s
     out["gemv_6144x6144_ring"] = sweep
