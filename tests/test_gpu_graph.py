@@ -1,0 +1,90 @@
+"""The expert block and the matmul inside a captured HIP graph (the pages'
+"full decode layer in ONE command buffer": a block is one submission).  Each
+graph is replayed several times with eager library work and host
+synchronisations between the replays, and every replay must reproduce the
+eager result bit for bit (the kernels are deterministic; nothing in the
+library records a memset or an allocation)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_gemv_coli_amd as coli
+from gpu_util import make_case, need_gpu, qtensor, to_dev
+from test_gpu_moe import _moe_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(run, outs, reps=3, between=None):
+    """Capture run() (which writes the tensors in outs), compare every replay
+    with the eager values."""
+    run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for o in outs:
+            o.fill_(float("nan"))
+        if between is not None:
+            between()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, ref):
+            assert torch.equal(o.view(torch.int32), e.view(torch.int32)), f"replay {r} differs"
+    del g
+
+
+def _block(S, pack, seed):
+    G, U, Dn, sh, x, ids, w = _moe_inputs(seed, 4, S, 4, 8, 256, 128, 64 if S <= 4 else 128, True)
+    tg, tu, td = qtensor(G, pack), qtensor(U, pack), qtensor(Dn, pack)
+    ts = [qtensor(m, pack) for m in sh]
+    xd, idd, wd = to_dev(x), to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32))
+    ws_bytes = coli.coli_moe_workspace_bytes(8, S, 4, 128, 256, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((S, 256), device="cuda")
+
+    def run():
+        coli.check(coli.coli_moe_block(tg, tu, td, xd, S, idd, wd, 4, ts[0], ts[1], ts[2], out, ws,
+                                       ws_bytes, torch.cuda.current_stream()), "coli_moe_block")
+    return run, out, (tg, tu, td, ts, xd, idd, wd, ws)
+
+
+@pytest.mark.parametrize("S,pack", [(1, True), (3, True), (1, False), (40, True), (40, False)],
+                         ids=["decode-S1-packed", "decode-S3-packed", "decode-S1-plain",
+                              "prefill-S40-packed", "prefill-S40-plain"])
+def test_moe_block_graph_replays(S, pack):
+    need_gpu()
+    run, out, keep = _block(S, pack, 900 + S)
+    # eager work between replays: another block on the same stream
+    run2, out2, keep2 = _block(2, True, 7)
+    _replays_match(run, [out], between=run2)
+
+
+@pytest.mark.parametrize("S", [1, 4, 96])
+def test_qmatmul_graph_replays(S):
+    need_gpu()
+    W, x = make_case(4, 640, 1024, 64, S, seed=31 + S)
+    T = qtensor(W, pack=True)
+    xd = to_dev(x.astype(np.float32))
+    y = torch.empty((S, 640), device="cuda")
+    W2, x2 = make_case(4, 64, 256, 64, 2, seed=5)
+    T2 = qtensor(W2, pack=True)
+    x2d = to_dev(x2.astype(np.float32))
+    y2 = torch.empty((2, 64), device="cuda")
+
+    def run():
+        coli.check(coli.coli_qmatmul(T, xd, y, S, torch.cuda.current_stream()), "coli_qmatmul")
+
+    def between():
+        coli.check(coli.coli_qmatmul(T2, x2d, y2, 2), "coli_qmatmul")
+    _replays_match(run, [y], between=between)
