@@ -1,5 +1,8 @@
 // pgemm.hip -- prefill GEMM (S > 4 input rows) for the int4 formats on the
-// gfx950 matrix cores: Y[m][n] = sum_k w(n, k) * X[m][k].
+// gfx950 matrix cores: Y[m][n] = sum_k w(n, k) * X[m][k].  Two kernels:
+//   k_pg  producer/consumer wavefronts with a double-buffered LDS tile for
+//         both operands (dense rows; plain int4 experts in the MoE block);
+//   k_sg  weight streaming for packed experts in the MoE block (further down).
 //
 // What is computed (colibri PR #298, CUDA fmt=4 commit: w = scale(n, k/gs) *
 // (q - 8), the group scale applied inline; colibri-strix "route large
