@@ -203,6 +203,8 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(coli, sd, np, torch, gq, gsc, uq, usc, dq, dsc, x, routes,
                            block_bytes, args.cpu_seconds, log)
+        if not args.no_extra:
+            extra["oracle_timings"] = oracle_timings(sd, np, log)
 
     res = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -512,6 +514,66 @@ def cpu_baseline(coli, sd, np, torch, gq, gsc, uq, usc, dq, dsc, x, routes, bloc
             "sample": f"{done} decode MoE blocks (S=1, 8 routed experts, full shapes), "
                       f"{spent:.1f} s of oracle time; OpenMP over the 8 routed pairs",
             "us_per_block": spent / done * 1e6}
+
+
+def oracle_timings(sd, np, log):
+    """The oracle on bounded samples of the other workloads, for context
+    beside the GPU figures: the 6144x6144 fmt-4 g64 GEMV at S=1 (one and all
+    host threads) and the S=544 Zipf(1.1) prefill MoE block on 4 of its
+    tokens (each token's output depends only on its own row and routing),
+    scaled to 544 tokens."""
+    import oracle
+    from oracle import QMat
+    nthreads = len(os.sched_getaffinity(0))
+    out = {"host_threads": nthreads, "cpu_model": _cpu_model()}
+    r = sd.rng(3)
+    x = sd.gen_x(r, 1, 6144)
+    q, s = sd.gen_matrix(r, 4, 6144, 6144, 64)
+    W = QMat(4, 6144, 6144, 64, q, s)
+    for nt in (1, nthreads):
+        orc = oracle.get(nthreads=nt)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 2.0:
+            orc.qmatmul(W, x)
+            n += 1
+        us = (time.perf_counter() - t0) / n * 1e6
+        out[f"gemv_6144x6144_g64_S1_threads{nt}_us"] = us
+        log(f"oracle gemv 6144^2 g64 S=1, {nt} threads: {us:.0f} us")
+    # prefill MoE: 4 tokens of the S=544 Zipf(1.1) draw, their experts only
+    S, gs = 544, 128
+    r = sd.rng(4)
+    xh = sd.gen_x(r, S, D)
+    ids, w = sd.gen_routing_zipf(r, S, K, E, 1.1)
+    toks = np.arange(4)
+    used = np.unique(ids[toks])
+    remap = {int(e): i for i, e in enumerate(used)}
+    rq = sd.rng(77)
+    mats = [sd.gen_matrix(rq, 4, F, D, gs, n=len(used)), sd.gen_matrix(rq, 4, F, D, gs, n=len(used)),
+            sd.gen_matrix(rq, 4, D, F, gs, n=len(used))]
+    G = QMat(4, F, D, gs, *mats[0])
+    U = QMat(4, F, D, gs, *mats[1])
+    Dn = QMat(4, D, F, gs, *mats[2])
+    local = np.vectorize(remap.get)(ids[toks]).astype(np.int32)
+    orc = oracle.get(nthreads=nthreads)
+    t0 = time.perf_counter()
+    orc.moe_block(G, U, Dn, xh[toks], local, w[toks])
+    sec = time.perf_counter() - t0
+    out["prefill_moe_544_zipf1.1_4_tokens_s"] = sec
+    out["prefill_moe_544_zipf1.1_scaled_to_544_tokens_s"] = sec * S / len(toks)
+    log(f"oracle prefill MoE, 4 of 544 tokens ({nthreads} threads): {sec:.2f} s "
+        f"-> ~{sec * S / len(toks):.0f} s for 544 tokens")
+    return out
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
