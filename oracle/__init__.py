@@ -114,6 +114,7 @@ class Oracle:
         L.oracle_silu.argtypes = [dbl]
         L.oracle_moe_route.restype = i64
         L.oracle_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+        L.oracle_moe_router.argtypes = [vp, i64, i64, vp, vp, i64, i64, dbl, i32, dbl, vp, vp, vp]
         L.oracle_moe_block.restype = i64
         L.oracle_moe_block.argtypes = [C.POINTER(OracleQT)] * 3 + [
             i64, vp, i64, vp, vp, i64] + [C.POINTER(OracleQT)] * 3 + [
@@ -177,6 +178,24 @@ class Oracle:
         perm = np.full(S * K, -1, dtype=np.int32)
         bad = self.lib.oracle_moe_route(_p(ids), S, K, E, _p(counts), _p(offsets), _p(perm))
         return counts, offsets, perm, int(bad)
+
+    def moe_router(self, x: np.ndarray, R: np.ndarray, bias, K: int, topp: float = 0.0,
+                   norm_topk: bool = True, routed_scale: float = 1.0):
+        """Router logits, sigmoid, greedy top-K over sigmoid + bias (ties to the
+        smaller index), top-p, norm_topk, routed_scale (coli_oracle.c states
+        the readings).  Returns ids [S][K] int32, w [S][K] f64, z [S][E] f64."""
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+        R = np.ascontiguousarray(R, dtype=np.float32)
+        S, D = x.shape
+        E = R.shape[0]
+        assert R.shape[1] == D and 1 <= K <= E
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        ids = np.zeros((S, K), dtype=np.int32)
+        w = np.zeros((S, K), dtype=np.float64)
+        z = np.zeros((S, E), dtype=np.float64)
+        self.lib.oracle_moe_router(_p(x), S, D, _p(R), _p(b), E, K, float(topp),
+                                   int(bool(norm_topk)), float(routed_scale), _p(ids), _p(w), _p(z))
+        return ids, w, z
 
     def moe_block(self, gate: QMat, up: QMat, down: QMat, x: np.ndarray,
                   ids: np.ndarray, w: np.ndarray, shared=None, rows=None,

@@ -29,6 +29,11 @@
  *   [P3-shared] colibri-strix commit log, commit "zero-copy attention weights +
  *               fuse shared expert into GPU block": the shared expert is an
  *               extra expert with routing weight 1.0 over every row.
+ *   [P3-layer]  colibri-strix commit log, commit "metal: full decode layer in
+ *               ONE command buffer": the router is a matvec followed by a
+ *               sigmoid, then an exact top-K phase: greedy argmax over the
+ *               sigmoid score plus a per-expert bias with the CPU's tie order,
+ *               top-p truncation, norm_topk and routed_scale.
  *
  * Readings where the pages are silent (each also listed with the design notes):
  *   - element 2j of a byte pair is the LOW nibble, 2j+1 the high nibble;
@@ -378,4 +383,88 @@ int64_t oracle_moe_block(const oracle_qt *gate, const oracle_qt *up, const oracl
     free(valid);
     free(ybuf);
     return bad;
+}
+
+/* ------------------------------------------------------------------ */
+/* Router and exact top-K ([P3-layer])                                 */
+/* ------------------------------------------------------------------ */
+
+/* For every input row s (readings where the one-line description is silent):
+ *   z[e] = sum_d R[e][d] * x[s][d] in f64 (exact products, sequential sum);
+ *   p[e] = 1 / (1 + exp(-z[e]));  selection key c[e] = p[e] + bias[e];
+ *   K greedy rounds, each taking the not yet chosen expert with the largest
+ *   key, the smallest index among equal keys (a scan keeping its first
+ *   maximum);
+ *   top-p (0 < topp < 1): the picks, in pick order, are kept up to and
+ *   including the first at which the running sum of p reaches
+ *   topp * (sum of p over all K picks); later slots become id -1, weight 0;
+ *   topp <= 0 or >= 1 keeps all K;
+ *   weight of a kept pick = its p (the bias steers the choice only); with
+ *   norm_topk the kept weights are divided by their sum; finally every weight
+ *   is multiplied by routed_scale.
+ * ids[s][K], w[s][K] (f64); z_out[s][E] the logits when not NULL.
+ * bias may be NULL (all zero). */
+void oracle_moe_router(const float *x, int64_t S, int64_t D, const float *R,
+                       const float *bias, int64_t E, int64_t K, double topp,
+                       int norm_topk, double routed_scale, int32_t *ids, double *w,
+                       double *z_out)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+    double *c = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+    double *pr = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+    char *taken = (char *)malloc((size_t)(E > 0 ? E : 1));
+    for (int64_t s = 0; s < S; s++) {
+        for (int64_t e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; d++)
+                acc += (double)R[e * D + d] * (double)x[s * D + d];
+            z[e] = acc;
+            pr[e] = 1.0 / (1.0 + exp(-acc));
+            c[e] = pr[e] + (bias ? (double)bias[e] : 0.0);
+            taken[e] = 0;
+            if (z_out)
+                z_out[s * E + e] = acc;
+        }
+        /* greedy picks */
+        double total = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++)
+                if (!taken[e] && (best < 0 || c[e] > c[best]))
+                    best = e;
+            taken[best] = 1;
+            ids[s * K + k] = (int32_t)best;
+            w[s * K + k] = pr[best];
+            total += pr[best];
+        }
+        /* top-p truncation */
+        int64_t keep = K;
+        if (topp > 0.0 && topp < 1.0) {
+            double run = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                run += w[s * K + k];
+                if (run >= topp * total) {
+                    keep = k + 1;
+                    break;
+                }
+            }
+        }
+        for (int64_t k = keep; k < K; k++) {
+            ids[s * K + k] = -1;
+            w[s * K + k] = 0.0;
+        }
+        if (norm_topk) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < keep; k++)
+                sum += w[s * K + k];
+            for (int64_t k = 0; k < keep; k++)
+                w[s * K + k] /= sum;
+        }
+        for (int64_t k = 0; k < keep; k++)
+            w[s * K + k] *= routed_scale;
+    }
+    free(taken);
+    free(pr);
+    free(c);
+    free(z);
 }

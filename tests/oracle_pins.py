@@ -384,4 +384,97 @@ def pin_moe_intermediates(orc):
         assert np.all(np.abs(inter["h"][p] - h_ref) <= tol)
 
 
+# ---------------------------------------------------------------------------
+# Router and exact top-K (colibri-strix commit log, "metal: full decode layer
+# in ONE command buffer": router matvec + sigmoid, greedy argmax over sigmoid
+# + bias with the CPU's tie order, top-p truncation, norm_topk, routed_scale)
+# ---------------------------------------------------------------------------
+
+def ref_router(x, R, bias, K, topp, norm_topk, scale):
+    """Independent statement: numpy's f64 matmul, scipy's logistic function, a
+    stable sort by (-key, index) for the greedy picks, a cumulative sum for
+    top-p."""
+    z = np.asarray(x, np.float64) @ np.asarray(R, np.float64).T
+    p = expit(z)
+    c = p + (0.0 if bias is None else np.asarray(bias, np.float64)[None, :])
+    S, E = z.shape
+    ids = np.full((S, K), -1, np.int64)
+    w = np.zeros((S, K))
+    for s in range(S):
+        order = sorted(range(E), key=lambda e: (-c[s, e], e))[:K]
+        pw = p[s, order]
+        keep = K
+        if 0.0 < topp < 1.0:
+            keep = int(np.argmax(np.cumsum(pw) >= topp * pw.sum())) + 1
+        ww = pw[:keep]
+        if norm_topk:
+            ww = ww / ww.sum()
+        ids[s, :keep] = order[:keep]
+        w[s, :keep] = ww * scale
+    return ids, w, z
+
+
+def pin_router_bruteforce(orc):
+    r = np.random.default_rng(11)
+    for (S, D, E, K, topp, norm, scale, bs) in [(3, 40, 10, 4, 0.0, True, 1.0, 0.05),
+                                                (5, 17, 33, 8, 0.6, True, 2.5, 0.05),
+                                                (2, 64, 8, 8, 0.0, False, 1.0, 0.05),
+                                                (4, 9, 16, 3, 0.9, False, 0.5, 0.05),
+                                                (8, 20, 24, 6, 0.5, True, 1.0, 0.4)]:
+        x = r.standard_normal((S, D)).astype(np.float32)
+        R = (r.standard_normal((E, D)) * 0.3).astype(np.float32)
+        b = (r.standard_normal(E) * bs).astype(np.float32)
+        ids, w, z = orc.moe_router(x, R, b, K, topp, norm, scale)
+        ri, rw, rz = ref_router(x, R, b, K, topp, norm, scale)
+        A = np.abs(x).astype(np.float64) @ np.abs(R).astype(np.float64).T
+        assert np.all(np.abs(z - rz) <= 1e-13 * A), "router logits"
+        assert np.array_equal(ids, ri), (ids, ri)
+        assert np.allclose(w, rw, rtol=1e-12, atol=0), "router weights"
+
+
+def pin_router_ties_bias_topp(orc):
+    """x = 0: every logit is 0 and every sigmoid 1/2 exactly, so the keys are
+    1/2 + bias and the ties are exact."""
+    E, K, D = 12, 5, 7
+    x = np.zeros((1, D), np.float32)
+    R = np.ones((E, D), np.float32)
+    # no bias: all keys equal -> picks 0, 1, 2, 3, 4 (smaller index first)
+    ids, w, _ = orc.moe_router(x, R, None, K, 0.0, True, 3.0)
+    assert ids.tolist() == [[0, 1, 2, 3, 4]] and np.allclose(w, 3.0 / K, rtol=1e-15, atol=0)
+    # bias 1 on expert 9, 0.5 on experts 7 and 4 (tied): 9 first, then 4, 7
+    b = np.zeros(E, np.float32)
+    b[9], b[7], b[4] = 1.0, 0.5, 0.5
+    ids, w, _ = orc.moe_router(x, R, b, K, 0.0, False, 1.0)
+    assert ids.tolist() == [[9, 4, 7, 0, 1]] and np.all(w == 0.5)  # weights ignore the bias
+    # top-p: 4 picks of 1/2 each, total 2; topp = 1/4 -> the first pick alone
+    # reaches 1/2 = topp * total exactly and ends the list
+    ids, w, _ = orc.moe_router(x, R, None, 4, 0.25, True, 1.0)
+    assert ids.tolist() == [[0, -1, -1, -1]] and w.tolist() == [[1.0, 0.0, 0.0, 0.0]]
+    ids, w, _ = orc.moe_router(x, R, None, 4, 0.5, False, 2.0)   # 1 = topp * 2 after two picks
+    assert ids.tolist() == [[0, 1, -1, -1]] and w.tolist() == [[1.0, 1.0, 0.0, 0.0]]
+
+
+def pin_router_invariants(orc):
+    r = np.random.default_rng(12)
+    S, D, E, K = 4, 24, 20, 6
+    x = r.standard_normal((S, D)).astype(np.float32)
+    R = (r.standard_normal((E, D)) * 0.4).astype(np.float32)
+    b = (r.standard_normal(E) * 0.1).astype(np.float32)
+    ids, w, z = orc.moe_router(x, R, b, K, 0.0, True, 1.0)
+    # relabelling the experts relabels the picks
+    perm = r.permutation(E)
+    ids2, w2, _ = orc.moe_router(x, R[perm], b[perm], K, 0.0, True, 1.0)
+    assert np.array_equal(perm[ids2], ids) and np.allclose(w2, w, rtol=1e-15)
+    # norm_topk: weights sum to routed_scale; routed_scale is a plain factor
+    ids3, w3, _ = orc.moe_router(x, R, b, K, 0.0, True, 2.75)
+    assert np.array_equal(ids3, ids) and np.allclose(w3.sum(axis=1), 2.75, rtol=1e-14)
+    assert np.allclose(w3, 2.75 * w, rtol=1e-15)
+    # a single-row problem equals the same row inside a batch
+    i1, w1, _ = orc.moe_router(x[2:3], R, b, K, 0.0, True, 1.0)
+    assert np.array_equal(i1[0], ids[2]) and np.array_equal(w1[0], w[2])
+    # without norm_topk the weights are the picks' sigmoids, in pick order
+    i4, w4, z4 = orc.moe_router(x, R, b, K, 0.0, False, 1.0)
+    assert np.allclose(w4, expit(np.take_along_axis(z4, i4.astype(np.int64), axis=1)), rtol=1e-15)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -24,6 +24,12 @@ MUTATIONS = {
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "combine_ignores_w": ("acc += (double)w[p] * ybuf[p * nout + r];", "acc += ybuf[p * nout + r];"),
     "up_gets_silu": ("h[j] = oracle_silu(g[j]) * u[j];", "h[j] = g[j] * oracle_silu(u[j]);"),
+    "router_ties_to_larger_index": ("if (!taken[e] && (best < 0 || c[e] > c[best]))",
+                                    "if (!taken[e] && (best < 0 || c[e] >= c[best]))"),
+    "router_weight_includes_bias": ("w[s * K + k] = pr[best];", "w[s * K + k] = c[best];"),
+    "router_topp_strict": ("if (run >= topp * total) {", "if (run > topp * total) {"),
+    "router_no_sigmoid": ("pr[e] = 1.0 / (1.0 + exp(-acc));", "pr[e] = acc;"),
+    "router_topp_on_biased_keys": ("run += w[s * K + k];", "run += c[ids[s * K + k]];"),
     "route_unstable": ("for (int64_t p = 0; p < S * K; p++) {\n            int32_t e = ids[p];\n            if (e >= 0 && e < E)\n                perm",
                        "for (int64_t p = S * K - 1; p >= 0; p--) {\n            int32_t e = ids[p];\n            if (e >= 0 && e < E)\n                perm"),
 }
