@@ -290,6 +290,7 @@ def side_measurements(coli, sd, np, torch, log):
             del Ts, q, s
     out["gemv_6144x6144_ring"] = sweep
     out.update(ceiling_probes(coli, torch, log))
+    out.update(router_measurements(coli, sd, np, torch, log, timed))
     out.update(prefill_measurements(coli, sd, np, torch, log, timed))
     out.update(layer_stream(coli, sd, np, torch, log))
     return out
@@ -367,6 +368,29 @@ def prefill_measurements(coli, sd, np, torch, log, timed):
             f"({100 * ideal_us / us:.1f}% of max(F/P, B/BW) = {ideal_us:.0f} us)  {kern}")
     del tg, tu, td, gq, gsc, uq, usc, dq, dsc, ws
     torch.cuda.empty_cache()
+    return out
+
+
+def router_measurements(coli, sd, np, torch, log, timed):
+    """The router and exact top-K at the block's shape (E 256, D 6144, K 8)
+    for one decode row and the S=544 prefill batch."""
+    dev = "cuda"
+    st = torch.cuda.current_stream()
+    r = sd.rng(9)
+    R = torch.from_numpy((r.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)).to(dev)
+    bias = torch.from_numpy((r.standard_normal(E) * 0.05).astype(np.float32)).to(dev)
+    out = {}
+    for S in (1, 544):
+        x = torch.randn((S, D), device=dev)
+        ids = torch.empty((S, K), dtype=torch.int32, device=dev)
+        w = torch.empty((S, K), device=dev)
+        wsb = coli.coli_moe_router_workspace_bytes(S, E)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        us = timed(lambda i: coli.check(coli.coli_moe_router(x, S, D, R, bias, E, K, 0.0, 1, 2.5, ids, w,
+                                                             ws, wsb, st), "router"), 50)
+        nbytes = E * D * 4 + S * D * 4
+        out[f"router_S{S}_E{E}_D{D}_K{K}"] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
+        log(f"router S={S}: {us:.2f} us ({nbytes / (us * 1e-6) / 1e9:.0f} GB/s of router weights + inputs)")
     return out
 
 

@@ -70,6 +70,9 @@ def _load():
         "coli_prof_read": (i64, [C.c_char_p, vp]),
         "coli_prof_tag": (C.c_char_p, [i32]),
         "coli_version": (C.c_char_p, []),
+        "coli_moe_router_workspace_bytes": (sz, [i32, i32]),
+        "coli_moe_router": (i32, [vp, i32, i32, vp, vp, i32, i32, C.c_float, i32, C.c_float, vp, vp,
+                                  vp, sz, vp]),
         "coli_probe_read": (i32, [vp, sz, vp, vp]),
         "coli_probe_mfma": (i32, [i32, i32, vp, vp]),
     }
@@ -88,7 +91,8 @@ def exported_symbols():
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
-            "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma"]
+            "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma",
+            "coli_moe_router_workspace_bytes", "coli_moe_router"]
 
 
 def _ptr(t):
@@ -189,6 +193,17 @@ def coli_stats():
 
 def coli_set_fail_after(n: int) -> None:
     _load().coli_set_fail_after(n)
+
+
+def coli_moe_router_workspace_bytes(S: int, E: int) -> int:
+    return _load().coli_moe_router_workspace_bytes(S, E)
+
+
+def coli_moe_router(x, S, D, R, bias, E, K, topp, norm_topk, routed_scale, ids, w, workspace,
+                    ws_bytes, stream=None) -> int:
+    return _load().coli_moe_router(_ptr(x), S, D, _ptr(R), _ptr(bias), E, K, float(topp),
+                                   int(bool(norm_topk)), float(routed_scale), _ptr(ids), _ptr(w),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def coli_probe_read(buf, sink, stream=None) -> int:

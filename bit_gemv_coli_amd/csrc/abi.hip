@@ -374,6 +374,32 @@ int coli_moe_route(const int32_t *ids, int S, int K, int E, int32_t *counts, int
                         0, (hipStream_t)stream);
 }
 
+size_t coli_moe_router_workspace_bytes(int S, int E) {
+    if (S < 1 || E < 1)
+        return 0;
+    return router_ws_bytes(S, E);
+}
+
+int coli_moe_router(const float *x, int S, int D, const float *R, const float *bias, int E, int K,
+                    float topp, int norm_topk, float routed_scale, int32_t *ids, float *w,
+                    void *workspace, size_t ws_bytes, void *stream) {
+    if (!x || !R || !ids || !w || !workspace)
+        return decline("moe_router: NULL pointer (only bias may be NULL)");
+    if (S < 1 || D < 1 || E < 1 || E > 512 || K < 1 || K > 16 || K > E)
+        return decline("moe_router: bad S=%d D=%d E=%d K=%d (E 1..512, K 1..min(16,E))", S, D, E, K);
+    if (!(topp >= 0.0f && topp <= 1.0f) || !(routed_scale == routed_scale))
+        return decline("moe_router: topp must lie in [0,1] and routed_scale must be a number");
+    if ((uintptr_t)workspace % 8 != 0 || ws_bytes < router_ws_bytes(S, E))
+        return decline("moe_router: workspace %zu bytes (8-byte aligned) < %zu needed", ws_bytes,
+                       router_ws_bytes(S, E));
+    if ((int64_t)S * D > INT32_MAX || (int64_t)E * D > INT32_MAX)
+        return decline("moe_router: S*D or E*D too large");
+    if (!gate_call())
+        return COLI_DECLINED;
+    return launch_router(x, S, D, R, bias, E, K, topp, norm_topk, routed_scale, ids, w, workspace,
+                         (hipStream_t)stream);
+}
+
 size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shared) {
     if (E < 1 || S < 1 || K < 1 || F < 1 || Dm < 1)
         return 0;

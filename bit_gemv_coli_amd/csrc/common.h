@@ -73,6 +73,11 @@ struct MoeArgs {
 };
 int launch_moe_decode(const MoeArgs &a);
 int launch_moe_prefill(const MoeArgs &a);
+// router logits (f64, into ws) and exact top-K (router.hip)
+size_t router_ws_bytes(int S, int E);
+int launch_router(const float *x, int S, int D, const float *R, const float *bias, int E, int K,
+                  float topp, int norm_topk, float routed_scale, int32_t *ids, float *w, void *ws,
+                  hipStream_t st);
 size_t moe_decode_ws_bytes(int S, int K, int F, int D, int has_shared);
 // matrix-core decode kernels (mgemv.hip); return 1 done, 0 not taken, <0 error
 bool mgemv_ok(const coli_qtensor *W);

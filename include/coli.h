@@ -238,6 +238,31 @@ size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shar
 /* loud).                                                                   */
 /* ---------------------------------------------------------------------- */
 
+/*
+ * coli_moe_router -- the router in front of the expert block and its exact
+ * top-K selection (colibri-strix commit log, "metal: full decode layer in ONE
+ * command buffer": router matvec + sigmoid, greedy argmax over sigmoid + bias
+ * with the CPU's tie order, top-p truncation, norm_topk, routed_scale).
+ *   x    f32 [S][D] input rows;  R  f32 [E][D] router weights (row-major);
+ *   bias f32 [E] added to the sigmoid score for the choice only (NULL: none);
+ *   for each row: z = R x (exact f64 products, f64 sums), p = 1/(1+exp(-z)),
+ *   K greedy picks of the largest p + bias, the smaller expert index among
+ *   equal keys; 0 < topp < 1 keeps the picks up to and including the first at
+ *   which the running sum of p reaches topp times the sum over the K picks
+ *   (topp 0 or 1 keeps all); weights = p of the kept picks, divided by their
+ *   sum when norm_topk != 0, times routed_scale;
+ *   ids i32 [S][K] in pick order (dropped slots -1), w f32 [S][K] (dropped 0);
+ *   workspace: device memory of coli_moe_router_workspace_bytes(S, E) bytes,
+ *   8-byte aligned, caller-owned, contents undefined between calls.
+ * ids and w feed coli_moe_block directly.  Limits: 1 <= E <= 512,
+ * 1 <= K <= min(16, E).  Returns COLI_OK, COLI_DECLINED (bad sizes, NULL
+ * pointers, small workspace, topp outside [0,1]) or COLI_HIP_ERROR.
+ */
+size_t coli_moe_router_workspace_bytes(int S, int E);
+int coli_moe_router(const float *x, int S, int D, const float *R, const float *bias, int E, int K,
+                    float topp, int norm_topk, float routed_scale, int32_t *ids, float *w,
+                    void *workspace, size_t ws_bytes, void *stream);
+
 /* Why the last call on this thread returned COLI_DECLINED ("" if none). */
 const char *coli_last_reason(void);
 /* Last HIP error text on this thread ("" if none). */
