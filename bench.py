@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the S=544 prefill measurements (dense GEMM and MoE block); prints "
                          "their JSON (for profiling those kernels)")
+    ap.add_argument("--router-only", action="store_true",
+                    help="only the router and top-K timings (S=1 and S=544); prints their JSON "
+                         "(for profiling those kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (reference for the "
                          "HBM byte counters)")
@@ -117,6 +120,9 @@ def main():
 
     if args.prefill_only:
         print(json.dumps(prefill_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
+        return
+    if args.router_only:
+        print(json.dumps(router_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
         return
 
     # ---- inputs ----------------------------------------------------------
@@ -373,9 +379,10 @@ def prefill_measurements(coli, sd, np, torch, log, timed):
 
 def router_measurements(coli, sd, np, torch, log, timed):
     """The router and exact top-K at the block's shape (E 256, D 6144, K 8)
-    for one decode row and the S=544 prefill batch."""
+    for one decode row and the S=544 prefill batch.  Device time per call
+    from a graph of 20 calls replayed 10 times (a call from Python costs more
+    than the kernels at S=1); the host-loop figure beside it."""
     dev = "cuda"
-    st = torch.cuda.current_stream()
     r = sd.rng(9)
     R = torch.from_numpy((r.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)).to(dev)
     bias = torch.from_numpy((r.standard_normal(E) * 0.05).astype(np.float32)).to(dev)
@@ -386,11 +393,28 @@ def router_measurements(coli, sd, np, torch, log, timed):
         w = torch.empty((S, K), device=dev)
         wsb = coli.coli_moe_router_workspace_bytes(S, E)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        us = timed(lambda i: coli.check(coli.coli_moe_router(x, S, D, R, bias, E, K, 0.0, 1, 2.5, ids, w,
-                                                             ws, wsb, st), "router"), 50)
+
+        def call(i=0):
+            coli.check(coli.coli_moe_router(x, S, D, R, bias, E, K, 0.0, 1, 2.5, ids, w, ws, wsb,
+                                            torch.cuda.current_stream()), "router")
+        us_loop = timed(call, 50)
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            call()
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                call()
+        us = timed(lambda i: g.replay(), 10) / 20
+        del g
         nbytes = E * D * 4 + S * D * 4
-        out[f"router_S{S}_E{E}_D{D}_K{K}"] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
-        log(f"router S={S}: {us:.2f} us ({nbytes / (us * 1e-6) / 1e9:.0f} GB/s of router weights + inputs)")
+        out[f"router_S{S}_E{E}_D{D}_K{K}"] = {"us": us, "us_host_loop": us_loop,
+                                              "GBps": nbytes / (us * 1e-6) / 1e9}
+        log(f"router S={S}: {us:.2f} us per call in a graph ({us_loop:.2f} us from a host loop; "
+            f"{nbytes / (us * 1e-6) / 1e9:.0f} GB/s of router weights + inputs)")
     return out
 
 

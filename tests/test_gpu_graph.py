@@ -33,7 +33,7 @@ def _replays_match(run, outs, reps=3, between=None):
     torch.cuda.synchronize()
     for r in range(reps):
         for o in outs:
-            o.fill_(float("nan"))
+            o.fill_(float("nan") if o.is_floating_point() else -7)
         if between is not None:
             between()
         torch.cuda.synchronize()
@@ -88,3 +88,25 @@ def test_qmatmul_graph_replays(S):
     def between():
         coli.check(coli.coli_qmatmul(T2, x2d, y2, 2), "coli_qmatmul")
     _replays_match(run, [y], between=between)
+
+
+@pytest.mark.parametrize("S", [1, 4, 96])
+def test_router_graph_replays(S):
+    """The router and top-K (decode rows, and many rows through the split
+    matrix-core logits) replayed from a graph."""
+    need_gpu()
+    import synthdata as sd
+    E, D, K = 64, 512, 6
+    r = sd.rng(300 + S)
+    x = to_dev(sd.gen_x(r, S, D))
+    R = to_dev((r.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32))
+    bias = to_dev((r.standard_normal(E) * 0.05).astype(np.float32))
+    ids = torch.empty((S, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((S, K), device="cuda")
+    wsb = coli.coli_moe_router_workspace_bytes(S, E)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def run():
+        coli.check(coli.coli_moe_router(x, S, D, R, bias, E, K, 0.7, 1, 2.5, ids, w, ws, wsb,
+                                        torch.cuda.current_stream()), "coli_moe_router")
+    _replays_match(run, [ids, w], between=lambda: ws.fill_(0xFF))

@@ -92,6 +92,16 @@ def test_router_exact_ties(orc):
     bias[[7, 19, 33]] = 0.25
     _check(orc, x, R, bias, K, 0.0, True, 1.0)
     _check(orc, x, R, None, K, 0.25, False, 1.0)  # at x = 0 the first pick reaches topp exactly
+    # the same ties where the logits go through the matrix-core path with
+    # the inputs split over several workgroups (partial sums added in order)
+    S, D = 40, 1024
+    x = sd.gen_x(r, S, D)
+    x[[0, 17, 39]] = 0.0
+    R = (r.standard_normal((E, D)) / 32).astype(np.float32)
+    R[5] = R[30]
+    R[12] = R[30]
+    R[2] = R[39]
+    _check(orc, x, R, bias, K, 0.0, True, 1.0)
 
 
 def test_router_feeds_block(orc):
