@@ -115,6 +115,7 @@ class Oracle:
         L.oracle_moe_route.restype = i64
         L.oracle_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.oracle_moe_router.argtypes = [vp, i64, i64, vp, vp, i64, i64, dbl, i32, dbl, vp, vp, vp]
+        L.oracle_rmsnorm.argtypes = [vp, i64, i64, vp, dbl, vp]
         L.oracle_moe_block.restype = i64
         L.oracle_moe_block.argtypes = [C.POINTER(OracleQT)] * 3 + [
             i64, vp, i64, vp, vp, i64] + [C.POINTER(OracleQT)] * 3 + [
@@ -196,6 +197,32 @@ class Oracle:
         self.lib.oracle_moe_router(_p(x), S, D, _p(R), _p(b), E, K, float(topp),
                                    int(bool(norm_topk)), float(routed_scale), _p(ids), _p(w), _p(z))
         return ids, w, z
+
+    def rmsnorm(self, x: np.ndarray, w, eps: float) -> np.ndarray:
+        """Per-row RMSNorm with a per-feature weight (coli_oracle.c states the
+        reading).  Returns y [S][D] f64."""
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+        S, D = x.shape
+        wf = None if w is None else np.ascontiguousarray(w, dtype=np.float32)
+        assert wf is None or wf.shape == (D,)
+        y = np.zeros((S, D), dtype=np.float64)
+        self.lib.oracle_rmsnorm(_p(x), S, D, _p(wf), float(eps), _p(y))
+        return y
+
+    def moe_layer(self, h: np.ndarray, ln_w, eps: float, R: np.ndarray, bias, K: int,
+                  topp: float, norm_topk: bool, routed_scale: float, gate: QMat, up: QMat,
+                  down: QMat, shared=None):
+        """The expert half of a decode layer (colibri-strix commit log, "metal:
+        full decode layer in ONE command buffer"): xn = RMSNorm(h), stored as
+        f32; router and exact top-K on xn; the expert block on xn with the
+        routed weights as f32; out = h + block.  Each step is one of the
+        functions above, called in that order.  Returns out [S][D] f64 and a
+        dict with xn (f32), ids, w (f64) and the block output y (f64)."""
+        h = np.ascontiguousarray(np.atleast_2d(h), dtype=np.float32)
+        xn = self.rmsnorm(h, ln_w, eps).astype(np.float32)
+        ids, w, _ = self.moe_router(xn, R, bias, K, topp, norm_topk, routed_scale)
+        y = self.moe_block(gate, up, down, xn, ids, w.astype(np.float32), shared=shared)
+        return h.astype(np.float64) + y, {"xn": xn, "ids": ids, "w": w, "y": y}
 
     def moe_block(self, gate: QMat, up: QMat, down: QMat, x: np.ndarray,
                   ids: np.ndarray, w: np.ndarray, shared=None, rows=None,

@@ -468,3 +468,25 @@ void oracle_moe_router(const float *x, int64_t S, int64_t D, const float *R,
     free(c);
     free(z);
 }
+
+/* ------------------------------------------------------------------ */
+
+/* RMSNorm of each row (colibri-strix commit log, "metal: full decode layer
+ * in ONE command buffer": the post-attention norm in front of the expert
+ * half of the layer).  The pages name the step only; the reading taken is
+ * the usual root-mean-square norm with a per-feature weight:
+ *   ms      = (sum_d x[s][d]^2) / D          (f64, sequential sum)
+ *   y[s][d] = x[s][d] / sqrt(ms + eps) * w[d] (f64)
+ * w may be NULL (all ones). */
+void oracle_rmsnorm(const float *x, int64_t S, int64_t D, const float *w, double eps, double *y)
+{
+    for (int64_t s = 0; s < S; s++) {
+        const float *xr = x + s * D;
+        double ss = 0.0;
+        for (int64_t d = 0; d < D; d++)
+            ss += (double)xr[d] * (double)xr[d];
+        const double inv = 1.0 / sqrt(ss / (double)D + eps);
+        for (int64_t d = 0; d < D; d++)
+            y[s * D + d] = (double)xr[d] * inv * (w ? (double)w[d] : 1.0);
+    }
+}

@@ -477,4 +477,46 @@ def pin_router_invariants(orc):
     assert np.allclose(w4, expit(np.take_along_axis(z4, i4.astype(np.int64), axis=1)), rtol=1e-15)
 
 
+def pin_rmsnorm_closed_forms(orc):
+    """RMSNorm (the post-attention norm of the layer): a hand-worked row,
+    constant rows, the weight as a per-feature factor, scale invariance."""
+    # x = (3, 4): mean of squares 12.5, so y = (3, 4) / sqrt(12.5)
+    y = orc.rmsnorm(np.array([[3.0, 4.0]], np.float32), None, 0.0)
+    assert np.allclose(y[0], [0.8485281374238571, 1.1313708498984762], rtol=1e-15, atol=0)
+    # constant rows c: y = c / sqrt(c^2 + eps) * w
+    D = 96
+    r = np.random.default_rng(3)
+    w = r.uniform(0.5, 2.0, D).astype(np.float32)
+    for c, eps in ((2.0, 1e-6), (-0.5, 0.25), (1e-3, 1e-6)):
+        y = orc.rmsnorm(np.full((1, D), c, np.float32), w, eps)
+        want = np.float64(np.float32(c)) / np.sqrt(np.float64(np.float32(c)) ** 2 + eps) * w
+        assert np.allclose(y[0], want, rtol=1e-14, atol=0), (c, eps)
+    # weight = per-feature factor on the unweighted result, rows independent
+    x = r.standard_normal((5, D)).astype(np.float32)
+    y0 = orc.rmsnorm(x, None, 1e-5)
+    yw = orc.rmsnorm(x, w, 1e-5)
+    assert np.array_equal(yw, y0 * w.astype(np.float64))
+    assert np.array_equal(orc.rmsnorm(x[2:3], None, 1e-5), y0[2:3])
+    # eps = 0: mean of squares of the output is 1, and x -> 4x changes nothing
+    y1 = orc.rmsnorm(x, None, 0.0)
+    assert np.allclose(np.mean(y1 ** 2, axis=1), 1.0, rtol=1e-13)
+    assert np.array_equal(orc.rmsnorm(4 * x, None, 0.0), y1)
+
+
+def pin_moe_layer_zero_norm_weight(orc):
+    """The layer with an all-zero norm weight: the normed rows are zero, every
+    logit is 0 and every key 1/2 + bias, so the picks are the K largest
+    biases (smaller index on ties), the block adds exactly zero and out = h."""
+    S, K, E, D, F = 3, 3, 8, 64, 32
+    G, U, Dn, x, _, _, sh = _moe_case(41, S, K, E, D, F, shared=True)
+    R = np.random.default_rng(5).standard_normal((E, D)).astype(np.float32)
+    bias = np.array([0.1, 0.3, 0.3, -0.2, 0.0, 0.3, 0.05, 0.2], np.float32)
+    out, st = orc.moe_layer(x, np.zeros(D, np.float32), 1e-6, R, bias, K, 0.0, True, 1.0,
+                            G, U, Dn, shared=sh)
+    assert np.array_equal(st["xn"], np.zeros((S, D), np.float32))
+    assert np.array_equal(st["ids"], np.tile(np.array([1, 2, 5], np.int32), (S, 1)))
+    assert np.allclose(st["w"], 1.0 / 3.0, rtol=1e-15)
+    assert np.array_equal(out, x.astype(np.float64))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

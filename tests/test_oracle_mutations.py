@@ -30,6 +30,12 @@ MUTATIONS = {
     "router_topp_strict": ("if (run >= topp * total) {", "if (run > topp * total) {"),
     "router_no_sigmoid": ("pr[e] = 1.0 / (1.0 + exp(-acc));", "pr[e] = acc;"),
     "router_topp_on_biased_keys": ("run += w[s * K + k];", "run += c[ids[s * K + k]];"),
+    "rmsnorm_sum_not_mean": ("const double inv = 1.0 / sqrt(ss / (double)D + eps);",
+                             "const double inv = 1.0 / sqrt(ss + eps);"),
+    "rmsnorm_eps_outside_sqrt": ("const double inv = 1.0 / sqrt(ss / (double)D + eps);",
+                                 "const double inv = 1.0 / (sqrt(ss / (double)D) + eps);"),
+    "rmsnorm_weight_dropped": ("y[s * D + d] = (double)xr[d] * inv * (w ? (double)w[d] : 1.0);",
+                               "y[s * D + d] = (double)xr[d] * inv;"),
     "route_unstable": ("for (int64_t p = 0; p < S * K; p++) {\n            int32_t e = ids[p];\n            if (e >= 0 && e < E)\n                perm",
                        "for (int64_t p = S * K - 1; p >= 0; p--) {\n            int32_t e = ids[p];\n            if (e >= 0 && e < E)\n                perm"),
 }
