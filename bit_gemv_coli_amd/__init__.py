@@ -73,6 +73,10 @@ def _load():
         "coli_moe_router_workspace_bytes": (sz, [i32, i32]),
         "coli_moe_router": (i32, [vp, i32, i32, vp, vp, i32, i32, C.c_float, i32, C.c_float, vp, vp,
                                   vp, sz, vp]),
+        "coli_rmsnorm": (i32, [vp, i32, i32, vp, C.c_float, vp, vp]),
+        "coli_moe_layer_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "coli_moe_layer": (i32, [QP, QP, QP, vp, i32, vp, C.c_float, vp, vp, i32, C.c_float, i32,
+                                 C.c_float, QP, QP, QP, vp, vp, sz, vp]),
         "coli_probe_read": (i32, [vp, sz, vp, vp]),
         "coli_probe_mfma": (i32, [i32, i32, vp, vp]),
     }
@@ -92,7 +96,8 @@ def exported_symbols():
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
             "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma",
-            "coli_moe_router_workspace_bytes", "coli_moe_router"]
+            "coli_moe_router_workspace_bytes", "coli_moe_router", "coli_rmsnorm",
+            "coli_moe_layer_workspace_bytes", "coli_moe_layer"]
 
 
 def _ptr(t):
@@ -204,6 +209,23 @@ def coli_moe_router(x, S, D, R, bias, E, K, topp, norm_topk, routed_scale, ids, 
     return _load().coli_moe_router(_ptr(x), S, D, _ptr(R), _ptr(bias), E, K, float(topp),
                                    int(bool(norm_topk)), float(routed_scale), _ptr(ids), _ptr(w),
                                    _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def coli_rmsnorm(x, S, D, w, eps, y, stream=None) -> int:
+    return _load().coli_rmsnorm(_ptr(x), S, D, _ptr(w), float(eps), _ptr(y), _stream(stream))
+
+
+def coli_moe_layer_workspace_bytes(E, S, K, F, D, has_shared) -> int:
+    return _load().coli_moe_layer_workspace_bytes(E, S, K, F, D, int(bool(has_shared)))
+
+
+def coli_moe_layer(gate, up, down, h, S, ln_w, eps, R, bias, K, topp, norm_topk, routed_scale,
+                   sh_gate, sh_up, sh_down, out, workspace, ws_bytes, stream=None) -> int:
+    return _load().coli_moe_layer(_qp(gate), _qp(up), _qp(down), _ptr(h), S, _ptr(ln_w),
+                                  float(eps), _ptr(R), _ptr(bias), K, float(topp),
+                                  int(bool(norm_topk)), float(routed_scale), _qp(sh_gate),
+                                  _qp(sh_up), _qp(sh_down), _ptr(out), _ptr(workspace), ws_bytes,
+                                  _stream(stream))
 
 
 def coli_probe_read(buf, sink, stream=None) -> int:

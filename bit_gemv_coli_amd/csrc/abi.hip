@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "common.h"
+#include "layer.h"
 
 namespace coli {
 
@@ -520,6 +521,98 @@ int coli_moe_hidden(const coli_qtensor *gate, const coli_qtensor *up, const floa
     if (S <= coli_gemv_max_rows())
         return launch_moe_decode(a);
     return launch_moe_prefill(a);
+}
+
+int coli_rmsnorm(const float *x, int S, int D, const float *w, float eps, float *y, void *stream) {
+    if (!x || !y)
+        return decline("rmsnorm: NULL x or y");
+    if (S < 1 || D < 1 || (int64_t)S * D > INT32_MAX)
+        return decline("rmsnorm: bad S=%d D=%d", S, D);
+    if (!(eps >= 0.0f) || eps == __builtin_huge_valf())
+        return decline("rmsnorm: eps must be finite and >= 0");
+    if (!gate_call())
+        return COLI_DECLINED;
+    return launch_rmsnorm(x, S, D, w, (double)eps, y, (hipStream_t)stream);
+}
+
+static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+// workspace of coli_moe_layer: xn | ids | w | router | block output | block
+struct LayerWs {
+    size_t xn, ids, w, rt, y, blk, total;
+};
+static LayerWs layer_ws(int E, int S, int K, int F, int D, int has_shared) {
+    LayerWs l{};
+    const size_t blk = coli_moe_workspace_bytes(E, S, K, F, D, has_shared);
+    if (blk == 0)
+        return l;
+    l.xn = 0;
+    l.ids = l.xn + al256((size_t)S * D * sizeof(float));
+    l.w = l.ids + al256((size_t)S * K * sizeof(int32_t));
+    l.rt = l.w + al256((size_t)S * K * sizeof(float));
+    l.y = l.rt + al256(router_ws_bytes(S, E));
+    l.blk = l.y + al256((size_t)S * D * sizeof(float));
+    l.total = l.blk + blk;
+    return l;
+}
+
+size_t coli_moe_layer_workspace_bytes(int E, int S, int K, int F, int D, int has_shared) {
+    if (E < 1 || S < 1 || K < 1 || F < 1 || D < 1)
+        return 0;
+    return layer_ws(E, S, K, F, D, has_shared).total;
+}
+
+int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                   const float *h, int S, const float *ln_w, float eps, const float *R,
+                   const float *bias, int K, float topp, int norm_topk, float routed_scale,
+                   const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                   const coli_qtensor *sh_down, float *out, void *workspace, size_t ws_bytes,
+                   void *stream) {
+    if (!h || !R || !out || !workspace)
+        return decline("moe_layer: NULL h, R, out or workspace (ln_w, bias and the shared "
+                       "expert may be NULL)");
+    if (!dev_aligned(workspace, 256))
+        return decline("moe_layer: workspace not 256-byte aligned");
+    // the routing lands in the workspace; any non-NULL ids pointer passes here
+    if (check_moe(gate, up, down, h, S, (const int32_t *)workspace, K, sh_gate, sh_up, sh_down,
+                  "moe_layer") != COLI_OK)
+        return COLI_DECLINED;
+    if (!down)
+        return decline("moe_layer: NULL down tensor");
+    const int E = gate->n, F = gate->O, D = gate->I;
+    if (E > 512 || K > 16 || K > E)
+        return decline("moe_layer: E=%d K=%d (router: E 1..512, K 1..min(16,E))", E, K);
+    if (!(topp >= 0.0f && topp <= 1.0f) || !(routed_scale == routed_scale))
+        return decline("moe_layer: topp must lie in [0,1] and routed_scale must be a number");
+    if (!(eps >= 0.0f) || eps == __builtin_huge_valf())
+        return decline("moe_layer: eps must be finite and >= 0");
+    if ((int64_t)S * D > INT32_MAX || (int64_t)E * D > INT32_MAX)
+        return decline("moe_layer: S*D or E*D too large");
+    const int has_sh = sh_gate != nullptr;
+    const LayerWs l = layer_ws(E, S, K, F, D, has_sh);
+    if (l.total == 0 || ws_bytes < l.total)
+        return decline("moe_layer: workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    if (!gate_call())
+        return COLI_DECLINED;
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *xn = (float *)(ws + l.xn);
+    int32_t *ids = (int32_t *)(ws + l.ids);
+    float *w = (float *)(ws + l.w);
+    float *y = (float *)(ws + l.y);
+    int rc = launch_rmsnorm(h, S, D, ln_w, (double)eps, xn, st);
+    if (rc != COLI_OK) return rc;
+    rc = launch_router(xn, S, D, R, bias, E, K, topp, norm_topk, routed_scale, ids, w, ws + l.rt, st);
+    if (rc != COLI_OK) return rc;
+    MoeArgs a;
+    a.gate = gate; a.up = up; a.down = down;
+    a.sg = sh_gate; a.su = sh_up; a.sd = sh_down;
+    a.x = xn; a.S = S; a.K = K; a.E = E; a.F = F; a.D = D;
+    a.ids = ids; a.w = w; a.out = y; a.h_out = nullptr;
+    a.ws = ws + l.blk; a.ws_bytes = ws_bytes - l.blk; a.st = st;
+    rc = S <= coli_gemv_max_rows() ? launch_moe_decode(a) : launch_moe_prefill(a);
+    if (rc != COLI_OK) return rc;
+    return launch_residual_add(h, y, out, (int64_t)S * D, st);
 }
 
 }  // extern "C"

@@ -1,0 +1,13 @@
+// layer.h -- launchers of the decode-layer steps around the expert block
+// (layer.hip): the per-row RMSNorm and the residual add.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coli {
+
+int launch_rmsnorm(const float *x, int S, int D, const float *w, double eps, float *y,
+                   hipStream_t st);
+int launch_residual_add(const float *h, const float *y, float *out, int64_t n, hipStream_t st);
+
+}  // namespace coli

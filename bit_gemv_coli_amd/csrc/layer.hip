@@ -1,0 +1,93 @@
+// layer.hip -- the steps of a decode layer around the expert block
+// (colibri-strix commit log, "metal: full decode layer in ONE command
+// buffer": the post-attention RMSNorm in front of the shared expert, router
+// and experts, and the residual add after them).
+//   k_rmsnorm       one workgroup per row: f64 sum of squares (each thread a
+//                   strided share, wavefront sums, then the four wavefronts in
+//                   order), inv = 1 / sqrt(ms + eps) in f64, every output the
+//                   f32 rounding of x * inv * w computed in f64;
+//   k_residual_add  out = h + y elementwise (out may be h).
+#include "common.h"
+#include "layer.h"
+
+namespace coli {
+
+__device__ __forceinline__ double ly_shfl_xor(double v, int m) {
+    const int2 p = __builtin_bit_cast(int2, v);
+    int2 q;
+    q.x = __shfl_xor(p.x, m);
+    q.y = __shfl_xor(p.y, m);
+    return __builtin_bit_cast(double, q);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, int D,
+                                                 const float *__restrict__ w, double eps,
+                                                 float *__restrict__ y) {
+    __shared__ double part[4];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const float *xr = x + (int64_t)blockIdx.x * D;
+    float *yr = y + (int64_t)blockIdx.x * D;
+    double ss = 0.0;
+    if constexpr (VEC) {
+        for (int d = 4 * t; d < D; d += 1024) {
+            const f32x4 v = gload<f32x4>(xr + d);
+            ss = fma((double)v.x, (double)v.x, ss);
+            ss = fma((double)v.y, (double)v.y, ss);
+            ss = fma((double)v.z, (double)v.z, ss);
+            ss = fma((double)v.w, (double)v.w, ss);
+        }
+    } else {
+        for (int d = t; d < D; d += 256) ss = fma((double)xr[d], (double)xr[d], ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += ly_shfl_xor(ss, m);
+    if (lane == 0)
+        part[wv] = ss;
+    __syncthreads();
+    const double tot = ((part[0] + part[1]) + part[2]) + part[3];
+    const double inv = 1.0 / sqrt(tot / (double)D + eps);
+    if constexpr (VEC) {
+        for (int d = 4 * t; d < D; d += 1024) {
+            const f32x4 v = gload<f32x4>(xr + d);
+            const f32x4 g = w ? gload<f32x4>(w + d) : f32x4{1.f, 1.f, 1.f, 1.f};
+            f32x4 o;
+            o.x = (float)((double)v.x * inv * (double)g.x);
+            o.y = (float)((double)v.y * inv * (double)g.y);
+            o.z = (float)((double)v.z * inv * (double)g.z);
+            o.w = (float)((double)v.w * inv * (double)g.w);
+            *(f32x4 *)(yr + d) = o;
+        }
+    } else {
+        for (int d = t; d < D; d += 256)
+            yr[d] = (float)((double)xr[d] * inv * (w ? (double)w[d] : 1.0));
+    }
+}
+
+__global__ __launch_bounds__(256) void k_residual_add(const float *h, const float *__restrict__ y,
+                                                      float *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        out[i] = h[i] + y[i];
+}
+
+int launch_rmsnorm(const float *x, int S, int D, const float *w, double eps, float *y,
+                   hipStream_t st) {
+    ProfScope ps("rmsnorm", st);
+    const bool vec = D % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0 &&
+                     (uintptr_t)w % 16 == 0;
+    if (vec)
+        hipLaunchKernelGGL(k_rmsnorm<true>, dim3((unsigned)S), dim3(256), 0, st, x, D, w, eps, y);
+    else
+        hipLaunchKernelGGL(k_rmsnorm<false>, dim3((unsigned)S), dim3(256), 0, st, x, D, w, eps, y);
+    return after_launch("rmsnorm");
+}
+
+int launch_residual_add(const float *h, const float *y, float *out, int64_t n, hipStream_t st) {
+    ProfScope ps("residual_add", st);
+    hipLaunchKernelGGL(k_residual_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, h, y,
+                       out, n);
+    return after_launch("residual_add");
+}
+
+}  // namespace coli

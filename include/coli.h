@@ -263,6 +263,49 @@ int coli_moe_router(const float *x, int S, int D, const float *R, const float *b
                     float topp, int norm_topk, float routed_scale, int32_t *ids, float *w,
                     void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * coli_rmsnorm -- per-row RMSNorm (colibri-strix commit log, "metal: full
+ * decode layer in ONE command buffer": the post-attention norm in front of
+ * the shared expert and the router; the pages name the step only, the usual
+ * root-mean-square norm with a per-feature weight is taken):
+ *   y[s][d] = x[s][d] / sqrt(mean_d x[s][d]^2 + eps) * w[d]
+ * with the mean of squares and the product in f64 and one rounding to f32.
+ *   x, y  f32 [S][D] device rows (y may equal x); w f32 [D] or NULL (ones);
+ *   eps   finite, >= 0.
+ * Returns COLI_OK, COLI_DECLINED (NULL x/y, bad sizes, bad eps) or
+ * COLI_HIP_ERROR.
+ */
+int coli_rmsnorm(const float *x, int S, int D, const float *w, float eps, float *y, void *stream);
+
+/*
+ * coli_moe_layer -- the expert half of a decode layer in one submission
+ * (colibri-strix commit log, "metal: full decode layer in ONE command
+ * buffer": post-attention norm, shared expert, router with the exact top-K,
+ * routed experts, then the residual add), for S >= 1 rows:
+ *   xn      = coli_rmsnorm(h, ln_w, eps)                   (kept in workspace)
+ *   ids, w  = coli_moe_router(xn, R, bias, K, topp, norm_topk, routed_scale)
+ *   out     = h + coli_moe_block(xn, ids, w; shared expert if given)
+ * Arguments as in those calls: gate/up/down are the expert stacks (E = gate's
+ * matrix count, F its rows, D its columns), R f32 [E][D], h and out f32
+ * [S][D] (out may equal h: the add is elementwise and last).  ln_w, bias and
+ * the shared expert (all three or none) may be NULL.  Limits: the block's
+ * (one fmt and gs, whole 16-byte packets) and the router's (E <= 512,
+ * K <= min(16, E)).
+ *   workspace: device memory of coli_moe_layer_workspace_bytes(E, S, K, F, D,
+ *   has_shared) bytes, 256-byte aligned, caller-owned, contents undefined
+ *   between calls.  Everything is validated before the first launch; nothing
+ *   is allocated and the host never waits, so the call can be captured in a
+ *   graph.
+ * Returns COLI_OK, COLI_DECLINED or COLI_HIP_ERROR.
+ */
+size_t coli_moe_layer_workspace_bytes(int E, int S, int K, int F, int D, int has_shared);
+int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                   const float *h, int S, const float *ln_w, float eps, const float *R,
+                   const float *bias, int K, float topp, int norm_topk, float routed_scale,
+                   const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                   const coli_qtensor *sh_down, float *out, void *workspace, size_t ws_bytes,
+                   void *stream);
+
 /* Why the last call on this thread returned COLI_DECLINED ("" if none). */
 const char *coli_last_reason(void);
 /* Last HIP error text on this thread ("" if none). */

@@ -110,3 +110,29 @@ def test_router_graph_replays(S):
         coli.check(coli.coli_moe_router(x, S, D, R, bias, E, K, 0.7, 1, 2.5, ids, w, ws, wsb,
                                         torch.cuda.current_stream()), "coli_moe_router")
     _replays_match(run, [ids, w], between=lambda: ws.fill_(0xFF))
+
+
+def test_moe_layer_graph_replays():
+    """Norm, router, top-K, shared + routed experts and the residual add of
+    the expert half of a layer, replayed from one graph (in place on a copy
+    of h restored before each replay)."""
+    need_gpu()
+    import synthdata as sd
+    S, K, E, D, F = 1, 8, 16, 256, 128
+    G, U, Dn, sh, x, _, _ = _moe_inputs(808, 4, S, K, E, D, F, 64, True)
+    r = sd.rng(809)
+    tg, tu, td = qtensor(G, True), qtensor(U, True), qtensor(Dn, True)
+    ts = [qtensor(m, True) for m in sh]
+    h0 = to_dev(x)
+    h = h0.clone()
+    lnw = to_dev(r.uniform(0.5, 1.5, D).astype(np.float32))
+    R = to_dev((r.standard_normal((E, D)) / 16).astype(np.float32))
+    wsb = coli.coli_moe_layer_workspace_bytes(E, S, K, F, D, True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(h)
+
+    def run():
+        coli.check(coli.coli_moe_layer(tg, tu, td, h, S, lnw, 1e-6, R, None, K, 0.0, 1, 2.5,
+                                       ts[0], ts[1], ts[2], out, ws, wsb,
+                                       torch.cuda.current_stream()), "coli_moe_layer")
+    _replays_match(run, [out], between=lambda: ws.fill_(0x7F))
