@@ -275,7 +275,7 @@ def side_measurements(coli, sd, np, torch, log):
     out["stream_read_one_matrix"] = {"bytes": mb21, "us": us_probe, "GBps": probe_gbs}
     log(f"streaming read of one {mb21 / 1e6:.1f} MB matrix per launch: {us_probe:.2f} us ({probe_gbs:.0f} GB/s)")
 
-    sweep = {}
+    sweep, stack = {}, {}
     for fmt, gs in ((4, 64), (4, 128), (2, 0), (1, 0), (3, 0)):
         for S in (1, 4):
             mb = qbytes(fmt, 6144, 6144, gs)
@@ -293,8 +293,24 @@ def side_measurements(coli, sd, np, torch, log):
                           "frac_stream_read_same_launch_size":
                               gbs / probe_gbs if abs(mb - mb21) < 0.2 * mb21 else None}
             log(f"sweep {key}: {us:.2f} us  {gbs:.0f} GB/s")
-            del Ts, q, s
+            # the same ring, NST distinct matrices per launch (a stack sharing
+            # x, the pages' batched-expert form): the per-launch start-up is
+            # paid once per NST matrices
+            NST = 8
+            nst = ncopy // NST
+            Tst = [coli.QTensor(fmt, q[c * NST:(c + 1) * NST], s[c * NST:(c + 1) * NST], 6144,
+                                6144, gs, n=NST) for c in range(nst)]
+            for t in Tst:
+                t.pack()
+            ys = torch.empty((NST, S, 6144), device=dev)
+            us = timed(lambda i: coli.coli_qmatmul(Tst[i % nst], x, ys, S, st), 4 * nst)
+            gbs = NST * (mb + S * 6144 * 8) / (us * 1e-6) / 1e9
+            stack[key] = {"matrices_per_launch": NST, "us_per_launch": us,
+                          "us_per_matrix": us / NST, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+            log(f"sweep {key} x{NST} per launch: {us / NST:.2f} us/matrix  {gbs:.0f} GB/s")
+            del Ts, Tst, q, s
     out["gemv_6144x6144_ring"] = sweep
+    out["gemv_6144x6144_ring_stacked"] = stack
     out.update(ceiling_probes(coli, torch, log))
     out.update(router_measurements(coli, sd, np, torch, log, timed))
     out.update(prefill_measurements(coli, sd, np, torch, log, timed))

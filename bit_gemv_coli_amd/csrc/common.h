@@ -94,7 +94,10 @@ int launch_pgemm_dense(const coli_qtensor *W, const float *x, float *y, int S, h
 // launch_route), bf16 gathered inputs xg, bf16 SiLU products hg, f32 down
 // rows y (skipped when y is null)
 constexpr int PG_MOE_ROWS = 64;         // producer/consumer kernel
-constexpr int PG_MOE_ROWS_PACKED = 32;  // weight-streaming kernel (packed copies)
+#ifndef COLI_SG_ROWS
+#define COLI_SG_ROWS 32
+#endif
+constexpr int PG_MOE_ROWS_PACKED = COLI_SG_ROWS;  // weight-streaming kernel (packed copies)
 int pgemm_moe_rows(const MoeArgs &m);
 int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float *y,
                      const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,

@@ -183,9 +183,19 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 #ifndef COLI_MG_NW_DENSE
 #define COLI_MG_NW_DENSE 6
 #endif
-// quads of blocks in flight per wavefront in the dense GEMV
+// weight requests after the first input staging instead of before it
+#ifndef COLI_MG_STAGE_FIRST
+#define COLI_MG_STAGE_FIRST 0
+#endif
+// quads of blocks in flight per wavefront in the dense GEMV and the MoE block
 #ifndef COLI_MG_NBQ_DENSE
 #define COLI_MG_NBQ_DENSE 2
+#endif
+#ifndef COLI_MG_NBQ_GATEUP
+#define COLI_MG_NBQ_GATEUP 2
+#endif
+#ifndef COLI_MG_NBQ_DOWN
+#define COLI_MG_NBQ_DOWN 2
 #endif
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
@@ -476,11 +486,13 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         const int klen = min(KSEG, kpad);
         const int nb8 = klen / 8;
         share(klen / 128, kb_beg, kb_end);
+#if !COLI_MG_STAGE_FIRST
 #pragma unroll
         for (int u = 0; u < NBQ; ++u) {
             load_batch(bq[u], kb_beg + u * MG_NBK, kb_end - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
+#endif
         stage_store(nb8, 0);
         for (int base = UN * NTH; base < NT * nb8; base += UN * NTH) {
             stage_load(0, nb8, base);
@@ -489,6 +501,13 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         for (int idx = tid; idx < KSEG / 16; idx += NTH)
             reinterpret_cast<u32x4 *>(zero)[idx] = u32x4{0u, 0u, 0u, 0u};
         lds_barrier();
+#if COLI_MG_STAGE_FIRST
+#pragma unroll
+        for (int u = 0; u < NBQ; ++u) {
+            load_batch(bq[u], kb_beg + u * MG_NBK, kb_end - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#endif
     }
     for (int sgi = 0;;) {
         const int kg0 = sgi * (KSEG / 128);
@@ -836,8 +855,8 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
             a.ncnt = (m.D + 15) / 16;
         }
         ProfScope ps("moe_gateup_decode", m.st, true);
-        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st, ps)
-                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP>(cb, a, P, m.st, ps)))
+        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, COLI_MG_NBQ_GATEUP>(cb, a, P, m.st, ps)
+                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, COLI_MG_NBQ_GATEUP>(cb, a, P, m.st, ps)))
             return 0;
         int rc = after_launch("moe_gateup_decode");
         if (rc != COLI_OK) return rc;
@@ -860,8 +879,8 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
         a.yfin = m.out;
         a.has_sh = has_sh ? 1 : 0;
         ProfScope ps("moe_down_decode", m.st, true);
-        if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st, ps)
-                : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN>(cb, a, P, m.st, ps)))
+        if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN, COLI_MG_NBQ_DOWN>(cb, a, P, m.st, ps)
+                : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN, COLI_MG_NBQ_DOWN>(cb, a, P, m.st, ps)))
             return 0;
         int rc = after_launch("moe_down_decode");
         if (rc != COLI_OK) return rc;

@@ -769,15 +769,24 @@ static void pg_operand(PgArgs &a, int mi, const coli_qtensor *T, const coli_qten
     a.fmt = T->fmt;
 }
 
+// 16-row weight tiles per wavefront in the weight-streaming kernel (measured:
+// 2 instead of 4 is 8% slower on the Zipf(1.1) S=544 block; 64-row input
+// tiles, which need 2 to fit the registers, 1.5x slower)
+#ifndef COLI_SG_NCT
+#define COLI_SG_NCT 4
+#endif
+
 template <int SM>
 static void sg_launch(const PgArgs &a, unsigned gx, bool down, hipStream_t st) {
     constexpr int MB = PG_MOE_ROWS_PACKED / 16;
+    constexpr int NCT = COLI_SG_NCT;
+    // output columns per workgroup: 4 wavefronts x 16 NCT / NMAT
     if (!down)
-        hipLaunchKernelGGL((k_sg<MB, 4, 2, PG_SILU, true, SM>), dim3(gx, (unsigned)((a.N + 127) / 128)),
-                           dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_sg<MB, NCT, 2, PG_SILU, true, SM>),
+                           dim3(gx, (unsigned)((a.N + 32 * NCT - 1) / (32 * NCT))), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_sg<MB, 4, 1, PG_PART, true, SM>), dim3(gx, (unsigned)((a.N + 255) / 256)),
-                           dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_sg<MB, NCT, 1, PG_PART, true, SM>),
+                           dim3(gx, (unsigned)((a.N + 64 * NCT - 1) / (64 * NCT))), dim3(256), 0, st, a);
 }
 
 static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, const coli_qtensor *T,
@@ -799,7 +808,7 @@ static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, c
 int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float *y,
                      const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,
                      const int32_t *offsets, int max_tiles) {
-    const bool packed = rows == PG_MOE_ROWS_PACKED;
+    const bool packed = rows > 0 && moe_all(m, mgemv_ok);
     const unsigned gx = (unsigned)((max_tiles + 7) / 8 * 8);
     PgArgs a;
     memset(&a, 0, sizeof a);
