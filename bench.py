@@ -506,47 +506,65 @@ def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def one_pass():
+    # the four projections take independent inputs here, so they go out as
+    # one grouped submission; the second variant launches them one by one
+    xs = [xin[i_] for _, i_ in projs]
+    ys = [outs[o] for o, _ in projs]
+
+    def one_pass(grouped):
         st = torch.cuda.current_stream()
         for l in range(layers):
             P, TP, mg, mu, md, tg, tu, td, sg, su, sdn = L[l]
-            for T, (o, i_) in zip(TP, projs):
-                coli.check(coli.coli_qmatmul(T, xin[i_], outs[o], 1, st))
+            if grouped:
+                coli.check(coli.coli_qmatmul_group(TP, xs, ys, 1, st))
+            else:
+                for T, (o, i_) in zip(TP, projs):
+                    coli.check(coli.coli_qmatmul(T, xin[i_], outs[o], 1, st))
             coli.check(coli.coli_moe_block(tg, tu, td, xin[D], 1, ids[l], wts[l], K, sg, su, sdn,
                                            mo, ws, wsb, st))
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        one_pass()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        one_pass()
-    graph.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st = torch.cuda.current_stream()
-    a.record(st)
-    for _ in range(passes):
+    def timed_graph(grouped):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_pass(grouped)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_pass(grouped)
         graph.replay()
-    b.record(st)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / passes
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        a.record(st)
+        for _ in range(passes):
+            graph.replay()
+        b.record(st)
+        torch.cuda.synchronize()
+        del graph
+        return a.elapsed_time(b) / passes
+
     attn = sum(qbytes(4, o, i_, gs) + (o + i_) * 4 for o, i_ in projs)
     moe = 9 * (2 * qbytes(4, F, D, gs) + qbytes(4, D, F, gs)) + 2 * D * 4
     per_layer = attn + moe
-    gbs = layers * per_layer / (ms * 1e-3) / 1e9
     resident = sum(sum(t.numel() * t.element_size() for t in (x[0], x[1]))
                    for l in L for x in (*l[0], l[2], l[3], l[4]))
-    log(f"layer stream: {ms * 1e3:.0f} us/pass  {ms * 1e3 / layers:.1f} us/layer  {gbs:.0f} GB/s  "
-        f"resident {resident / 1e9:.1f} GB")
-    res = {"layer_stream_75": {"us_per_pass": ms * 1e3, "us_per_layer": ms * 1e3 / layers,
-                               "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                               "bytes_per_layer": per_layer, "resident_GB": resident / 1e9,
-                               "launches_per_layer": 4 + 3}}
-    del graph, L
+    res = {}
+    for grouped, key in ((True, "layer_stream_75"),
+                         (False, "layer_stream_75_one_launch_per_projection")):
+        n0 = coli.coli_stats()[2]
+        one_pass(grouped)
+        torch.cuda.synchronize()
+        launches = (coli.coli_stats()[2] - n0) / layers
+        ms = timed_graph(grouped)
+        gbs = layers * per_layer / (ms * 1e-3) / 1e9
+        log(f"{key}: {ms * 1e3:.0f} us/pass  {ms * 1e3 / layers:.1f} us/layer  {gbs:.0f} GB/s  "
+            f"resident {resident / 1e9:.1f} GB")
+        res[key] = {"us_per_pass": ms * 1e3, "us_per_layer": ms * 1e3 / layers, "GBps": gbs,
+                    "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": per_layer,
+                    "resident_GB": resident / 1e9, "launches_per_layer": launches}
+    del L
     torch.cuda.empty_cache()
     return res
 

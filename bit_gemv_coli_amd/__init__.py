@@ -51,6 +51,7 @@ def _load():
     sig = {
         "coli_tensor_upload": (i32, [QP, i32, i32, i32, i32, i32, i32, vp, vp]),
         "coli_qmatmul": (i32, [QP, vp, vp, i32, vp]),
+        "coli_qmatmul_group": (i32, [i32, vp, vp, vp, i32, vp]),
         "coli_packed_bytes": (sz, [i32, i32, i32, i32, i32]),
         "coli_tensor_pack": (i32, [QP, vp, sz, vp]),
         "coli_gemv_max_rows": (i32, []),
@@ -90,7 +91,8 @@ def _load():
 
 def exported_symbols():
     """Names the binding expects libcoli to export."""
-    return ["coli_tensor_upload", "coli_packed_bytes", "coli_tensor_pack", "coli_qmatmul", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
+    return ["coli_tensor_upload", "coli_packed_bytes", "coli_tensor_pack", "coli_qmatmul",
+            "coli_qmatmul_group", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
             "coli_set_decode_kernel",
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
@@ -141,6 +143,21 @@ def coli_tensor_pack(W, packed, nbytes, stream=None) -> int:
 
 def coli_qmatmul(W, x, y, S, stream=None) -> int:
     return _load().coli_qmatmul(_qp(W), _ptr(x), _ptr(y), S, _stream(stream))
+
+
+COLI_GROUP_MAX = 8
+
+
+def coli_qmatmul_group(Ws, xs, ys, S, stream=None) -> int:
+    """y[g] = W[g] x[g] for the members of one group (lists of equal length)."""
+    n = len(Ws)
+    if not (len(xs) == n and len(ys) == n):
+        raise ValueError("coli_qmatmul_group: W, x and y lists differ in length")
+    descs = (C.POINTER(coli_qtensor) * max(n, 1))(
+        *[C.pointer(w.desc if isinstance(w, QTensor) else w) for w in Ws])
+    xp = (C.c_void_p * max(n, 1))(*[_ptr(x) for x in xs])
+    yp = (C.c_void_p * max(n, 1))(*[_ptr(y) for y in ys])
+    return _load().coli_qmatmul_group(n, descs, xp, yp, S, _stream(stream))
 
 
 def coli_gemv_max_rows() -> int:

@@ -361,6 +361,40 @@ int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *s
     return launch_gemm(W, x, y, S, nullptr, 0, (hipStream_t)stream);
 }
 
+int coli_qmatmul_group(int n, const coli_qtensor *const *W, const float *const *x,
+                       float *const *y, int S, void *stream) {
+    if (n < 1 || n > COLI_GROUP_MAX || !W || !x || !y)
+        return decline("qmatmul_group: n=%d outside 1..%d or NULL array", n, COLI_GROUP_MAX);
+    if (S < 1)
+        return decline("qmatmul_group: S=%d < 1", S);
+    for (int g = 0; g < n; ++g) {
+        if (check_qt(W[g], "qmatmul_group") != COLI_OK)
+            return COLI_DECLINED;
+        if (!x[g] || !y[g])
+            return decline("qmatmul_group: NULL x or y of member %d", g);
+        if (!dev_aligned(x[g], 4) || !dev_aligned(y[g], 4))
+            return decline("qmatmul_group: x or y of member %d not 4-byte aligned", g);
+    }
+    if (!gate_call())
+        return COLI_DECLINED;
+    const hipStream_t st = (hipStream_t)stream;
+    if (S <= coli_gemv_max_rows() && decode_kernel_mode() == 0) {
+        const int r = launch_mgemv_group(n, W, x, y, S, st);
+        if (r == 1)
+            return COLI_OK;
+        if (r < 0)
+            return COLI_HIP_ERROR;
+    }
+    // not one launch (format mix, no packed copy, stacks, S > 4): member by member
+    for (int g = 0; g < n; ++g) {
+        const int rc = S <= coli_gemv_max_rows() ? launch_gemv(W[g], x[g], y[g], S, st)
+                                                 : launch_gemm(W[g], x[g], y[g], S, nullptr, 0, st);
+        if (rc != COLI_OK)
+            return rc;
+    }
+    return COLI_OK;
+}
+
 int coli_moe_route(const int32_t *ids, int S, int K, int E, int32_t *counts, int32_t *offsets,
                    int32_t *perm, int32_t *n_bad, void *stream) {
     if (!ids || !counts || !offsets || !perm || !n_bad)

@@ -84,6 +84,8 @@ bool mgemv_ok(const coli_qtensor *W);
 size_t packed_bytes(int fmt, int n, int O, int I, int gs);
 int launch_pack(coli_qtensor *t, void *packed, hipStream_t st);
 int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
+int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *x,
+                       float *const *y, int S, hipStream_t st);
 int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt);
 // prefill GEMM on the matrix cores for the int4 formats (pgemm.hip); 1 done,
 // 0 not taken, <0 error

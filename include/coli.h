@@ -154,6 +154,29 @@ int coli_tensor_pack(coli_qtensor *t, void *packed, size_t bytes, void *stream);
  */
 int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *stream);
 
+/*
+ * coli_qmatmul_group -- y[g] = W[g] x[g] for n independent matrices in one
+ * submission (colibri-strix commit log, "metal: full decode layer in ONE
+ * command buffer": the projections of a layer go to the GPU together, not one
+ * dispatch each).  Each member is computed exactly as coli_qmatmul computes it
+ * (same kernels, same bounds, bit-identical results); members need not share
+ * shapes.
+ *   n      1 .. COLI_GROUP_MAX members
+ *   W[g]   tensor from coli_tensor_upload (for one launch: a single matrix
+ *          with a packed copy, all members the same fmt, fmt-4 members with
+ *          the same scale slots per 128 inputs; otherwise the members run one
+ *          launch each, still in this call)
+ *   x[g]   device f32 [S][I_g]      y[g]   device f32 [n_g][S][O_g]
+ *   S      >= 1 input rows, the same for all members
+ * The host arrays W, x, y are read during the call only.  Members' outputs
+ * must not overlap each other or any input.  Every member is validated
+ * before anything is enqueued.  Returns COLI_OK / COLI_DECLINED /
+ * COLI_HIP_ERROR.
+ */
+#define COLI_GROUP_MAX 8
+int coli_qmatmul_group(int n, const coli_qtensor *const *W, const float *const *x,
+                       float *const *y, int S, void *stream);
+
 /* Largest S served by the fp32 GEMV path (env COLI_GEMV_MAX_ROWS, 1..4). */
 int coli_gemv_max_rows(void);
 /* Set it (1..4); returns the previous value, or 0 if the value is refused. */
