@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the S=544 prefill measurements (dense GEMM and MoE block); prints "
                          "their JSON (for profiling those kernels)")
+    ap.add_argument("--layer-stream-only", action="store_true",
+                    help="only the 75-layer decode stream (grouped and one launch per projection)")
     ap.add_argument("--router-only", action="store_true",
                     help="only the router and top-K timings (S=1 and S=544); prints their JSON "
                          "(for profiling those kernels)")
@@ -120,6 +122,9 @@ def main():
 
     if args.prefill_only:
         print(json.dumps(prefill_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
+        return
+    if args.layer_stream_only:
+        print(json.dumps(layer_stream(coli, sd, np, torch, log)), flush=True)
         return
     if args.router_only:
         print(json.dumps(router_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
