@@ -56,7 +56,8 @@ int launch_gemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws
 size_t gemm_workspace_bytes(int S, int I);
 int launch_route(const int32_t *ids, int S, int K, int E, int32_t *counts, int32_t *offsets,
                  int32_t *perm, int32_t *n_bad, int32_t *inv, int32_t *tiles, int32_t *n_tiles,
-                 int bm, int shared_rows, hipStream_t st);
+                 int bm, int shared_rows, hipStream_t st, int32_t *tiles_s = nullptr,
+                 int32_t *n_tiles_s = nullptr, int bm_s = 0);
 
 struct MoeArgs {
     const coli_qtensor *gate, *up, *down;
@@ -100,10 +101,17 @@ constexpr int PG_MOE_ROWS = 64;         // producer/consumer kernel
 #define COLI_SG_ROWS 32
 #endif
 constexpr int PG_MOE_ROWS_PACKED = COLI_SG_ROWS;  // weight-streaming kernel (packed copies)
+// experts with 1 .. PG_MOE_ROWS_SHORT rows take one tile of that many rows in
+// the weight-streaming kernel instead of a PG_MOE_ROWS_PACKED-row tile (0: off)
+#ifndef COLI_SG_SHORT_ROWS
+#define COLI_SG_SHORT_ROWS 16
+#endif
+constexpr int PG_MOE_ROWS_SHORT = COLI_SG_SHORT_ROWS;
 int pgemm_moe_rows(const MoeArgs &m);
 int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float *y,
                      const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,
-                     const int32_t *offsets, int max_tiles);
+                     const int32_t *offsets, int max_tiles, const int32_t *tiles_s = nullptr,
+                     const int32_t *n_tiles_s = nullptr, int max_short = 0);
 // 0: matrix-core decode kernels where the layout allows, 1: vector-ALU kernels only
 int decode_kernel_mode();
 size_t moe_prefill_ws_bytes(int E, int S, int K, int F, int D, int has_shared);

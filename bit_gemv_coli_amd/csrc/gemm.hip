@@ -346,11 +346,11 @@ int launch_gemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws
 constexpr int MOE_BM = 32, MOE_BN = 128;
 
 struct PrefillWs {
-    int32_t *counts, *offsets, *perm, *n_bad, *inv, *tiles, *n_tiles;
+    int32_t *counts, *offsets, *perm, *n_bad, *inv, *tiles, *n_tiles, *tiles_s, *n_tiles_s;
     bf16_t *xg, *hg;
     float *y;
     size_t bytes;
-    int max_tiles;
+    int max_tiles, max_short;
 };
 
 static size_t al(size_t b) { return (b + 255) / 256 * 256; }
@@ -370,6 +370,9 @@ static PrefillWs prefill_layout(void *base, int E, int S, int K, int F, int D, i
     w.inv = (int32_t *)take(sizeof(int32_t) * std::max<size_t>(SK, 1));
     w.tiles = (int32_t *)take(sizeof(int32_t) * 2 * w.max_tiles);
     w.n_tiles = (int32_t *)take(sizeof(int32_t));
+    w.max_short = (int)std::min<size_t>((size_t)E, SK);
+    w.tiles_s = (int32_t *)take(sizeof(int32_t) * 2 * std::max(w.max_short, 1));
+    w.n_tiles_s = (int32_t *)take(sizeof(int32_t));
     w.xg = (bf16_t *)take(sizeof(bf16_t) * R * D);
     w.hg = (bf16_t *)take(sizeof(bf16_t) * R * F);
     w.y = (float *)take(sizeof(float) * R * D);
@@ -537,8 +540,10 @@ static int moe_prefill_pg(const MoeArgs &a, const PrefillWs &w, int rows) {
     int rc = moe_gather(a, w);
     if (rc != COLI_OK)
         return rc;
+    const bool short_tiles = rows == PG_MOE_ROWS_PACKED && PG_MOE_ROWS_SHORT > 0;
     rc = launch_pgemm_moe(a, rows, w.xg, w.hg, a.h_out ? nullptr : w.y, w.tiles, w.n_tiles,
-                          w.counts, w.offsets, max_tiles);
+                          w.counts, w.offsets, max_tiles, short_tiles ? w.tiles_s : nullptr,
+                          short_tiles ? w.n_tiles_s : nullptr, short_tiles ? w.max_short : 0);
     if (rc != COLI_OK)
         return rc;
     return a.h_out ? moe_hidden_out(a, w) : moe_combine(a, w);
@@ -559,8 +564,10 @@ int launch_moe_prefill(const MoeArgs &a) {
     if (w.bytes > a.ws_bytes)
         return decline("moe_block: workspace %zu bytes < %zu needed", a.ws_bytes, w.bytes);
     const int pg_rows = (uintptr_t)a.ws % 16 == 0 ? pgemm_moe_rows(a) : 0;
+    const int bm_s = pg_rows == PG_MOE_ROWS_PACKED ? PG_MOE_ROWS_SHORT : 0;
     int rc = launch_route(a.ids, a.S, a.K, a.E, w.counts, w.offsets, w.perm, w.n_bad, w.inv,
-                          w.tiles, w.n_tiles, pg_rows ? pg_rows : MOE_BM, has_sh ? a.S : 0, a.st);
+                          w.tiles, w.n_tiles, pg_rows ? pg_rows : MOE_BM, has_sh ? a.S : 0, a.st,
+                          bm_s ? w.tiles_s : nullptr, bm_s ? w.n_tiles_s : nullptr, bm_s);
     if (rc != COLI_OK)
         return rc;
     if (pg_rows)

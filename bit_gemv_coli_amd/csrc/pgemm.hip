@@ -776,9 +776,8 @@ static void pg_operand(PgArgs &a, int mi, const coli_qtensor *T, const coli_qten
 #define COLI_SG_NCT 4
 #endif
 
-template <int SM>
+template <int SM, int MB>
 static void sg_launch(const PgArgs &a, unsigned gx, bool down, hipStream_t st) {
-    constexpr int MB = PG_MOE_ROWS_PACKED / 16;
     constexpr int NCT = COLI_SG_NCT;
     // output columns per workgroup: 4 wavefronts x 16 NCT / NMAT
     if (!down)
@@ -789,13 +788,31 @@ static void sg_launch(const PgArgs &a, unsigned gx, bool down, hipStream_t st) {
                            dim3(gx, (unsigned)((a.N + 64 * NCT - 1) / (64 * NCT))), dim3(256), 0, st, a);
 }
 
+template <int MB>
+static void sg_stage(const PgArgs &a, unsigned gx, bool down, const coli_qtensor *T, hipStream_t st) {
+    if (T->fmt == 4 && T->gs < 128) sg_launch<SM_FOLD, MB>(a, gx, down, st);
+    else if (T->fmt == 4 && T->gs == 128) sg_launch<SM_GRP1, MB>(a, gx, down, st);
+    else if (T->fmt == 4) sg_launch<SM_GRPN, MB>(a, gx, down, st);
+    else sg_launch<SM_ROW, MB>(a, gx, down, st);
+}
+
+// one projection stage over the routed tiles; packed experts: the row tiles
+// of PG_MOE_ROWS_PACKED rows, then (gx_s > 0) the short tiles of experts with
+// at most PG_MOE_ROWS_SHORT rows, which halve the matrix-core and input work
+// of the many lightly routed experts
 static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, const coli_qtensor *T,
-                         hipStream_t st) {
+                         hipStream_t st, const int32_t *tiles_s, const int32_t *n_tiles_s,
+                         unsigned gx_s) {
     if (packed) {
-        if (T->fmt == 4 && T->gs < 128) sg_launch<SM_FOLD>(a, gx, down, st);
-        else if (T->fmt == 4 && T->gs == 128) sg_launch<SM_GRP1>(a, gx, down, st);
-        else if (T->fmt == 4) sg_launch<SM_GRPN>(a, gx, down, st);
-        else sg_launch<SM_ROW>(a, gx, down, st);
+        sg_stage<PG_MOE_ROWS_PACKED / 16>(a, gx, down, T, st);
+        if constexpr (PG_MOE_ROWS_SHORT > 0) {
+            if (gx_s > 0) {
+                PgArgs b = a;
+                b.tiles = tiles_s;
+                b.n_tiles = n_tiles_s;
+                sg_stage<PG_MOE_ROWS_SHORT / 16>(b, gx_s, down, T, st);
+            }
+        }
     } else if (!down) {
         hipLaunchKernelGGL((k_pg<PG_MOE_ROWS, 2, PG_SILU, false, true>),
                            dim3(gx, (unsigned)((a.N + 63) / 64)), dim3(512), 0, st, a);
@@ -807,9 +824,12 @@ static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, c
 
 int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float *y,
                      const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,
-                     const int32_t *offsets, int max_tiles) {
+                     const int32_t *offsets, int max_tiles, const int32_t *tiles_s,
+                     const int32_t *n_tiles_s, int max_short) {
     const bool packed = rows > 0 && moe_all(m, mgemv_ok);
     const unsigned gx = (unsigned)((max_tiles + 7) / 8 * 8);
+    const unsigned gx_s = (packed && tiles_s && n_tiles_s && max_short > 0)
+                              ? (unsigned)((max_short + 7) / 8 * 8) : 0u;
     PgArgs a;
     memset(&a, 0, sizeof a);
     a.tiles = tiles; a.n_tiles = n_tiles; a.counts = counts; a.offsets = offsets;
@@ -823,7 +843,7 @@ int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float
         a.y = hg;
         a.ldy = m.F;
         ProfScope ps("moe_gateup_gemm", m.st);
-        pg_moe_stage(a, gx, false, packed, m.gate, m.st);
+        pg_moe_stage(a, gx, false, packed, m.gate, m.st, tiles_s, n_tiles_s, gx_s);
         int rc = after_launch("moe_gateup_gemm");
         if (rc != COLI_OK) return rc;
     }
@@ -838,7 +858,7 @@ int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float
         a.y = y;
         a.ldy = m.D;
         ProfScope ps("moe_down_gemm", m.st);
-        pg_moe_stage(a, gx, true, packed, m.down, m.st);
+        pg_moe_stage(a, gx, true, packed, m.down, m.st, tiles_s, n_tiles_s, gx_s);
         return after_launch("moe_down_gemm");
     }
 }

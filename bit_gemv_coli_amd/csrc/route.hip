@@ -57,7 +57,9 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(const int32_t *__restrict_
                                                       int32_t *__restrict__ inv,
                                                       int32_t *__restrict__ tiles,
                                                       int32_t *__restrict__ n_tiles, int bm,
-                                                      int shared_rows) {
+                                                      int shared_rows,
+                                                      int32_t *__restrict__ tiles_s,
+                                                      int32_t *__restrict__ n_tiles_s, int bm_s) {
     // seg[w][e]: pairs of segment w routed to e, then that segment's cursor
     __shared__ int seg[RT_WAVES * RT_EMAX];
     __shared__ int sbuf[RT_WAVES];
@@ -84,7 +86,9 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(const int32_t *__restrict_
     __syncthreads();
 
     // 2. totals, exclusive offsets, per-segment cursors; tile counts
-    int carry = 0, tcarry = 0;
+    // (with bm_s > 0, an expert of 1 .. bm_s rows gets one short tile in the
+    // second list instead of row tiles of bm in the first)
+    int carry = 0, tcarry = 0, scarry = 0;
     for (int e0 = 0; e0 < E; e0 += RT_THREADS) {
         const int e = e0 + tid;
         int c = 0;
@@ -93,9 +97,16 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(const int32_t *__restrict_
             for (int w = 0; w < RT_WAVES; ++w) c += seg[w * E + e];
         int tot;
         const int ex = block_exclusive_scan(c, sbuf, &tot) + carry;
-        const int nt = (bm > 0) ? (c + bm - 1) / bm : 0;
+        const bool small = bm_s > 0 && c >= 1 && c <= bm_s;
+        const int nt = (bm > 0 && !small) ? (c + bm - 1) / bm : 0;
         int ttot;
         const int tex = block_exclusive_scan(nt, sbuf, &ttot) + tcarry;
+        int stot;
+        const int sex = block_exclusive_scan(small ? 1 : 0, sbuf, &stot) + scarry;
+        if (tiles_s && small) {
+            tiles_s[2 * sex] = e;
+            tiles_s[2 * sex + 1] = 0;
+        }
         if (e < E) {
             counts[e] = c;
             offsets[e] = ex;
@@ -114,6 +125,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(const int32_t *__restrict_
         }
         carry += tot;
         tcarry += ttot;
+        scarry += stot;
     }
     if (tid == 0) {
         offsets[E] = carry;
@@ -128,6 +140,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(const int32_t *__restrict_
             }
         }
         if (n_tiles) n_tiles[0] = nt;
+        if (n_tiles_s) n_tiles_s[0] = scarry;
     }
     __syncthreads();
 
@@ -168,12 +181,13 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(const int32_t *__restrict_
 
 int launch_route(const int32_t *ids, int S, int K, int E, int32_t *counts, int32_t *offsets,
                  int32_t *perm, int32_t *n_bad, int32_t *inv, int32_t *tiles, int32_t *n_tiles,
-                 int bm, int shared_rows, hipStream_t st) {
+                 int bm, int shared_rows, hipStream_t st, int32_t *tiles_s, int32_t *n_tiles_s,
+                 int bm_s) {
     if (E < 1 || E > RT_EMAX)
         return decline("route: E=%d outside 1..%d", E, RT_EMAX);
     ProfScope ps("route", st);
     hipLaunchKernelGGL(k_route, dim3(1), dim3(RT_THREADS), 0, st, ids, S * K, E, counts, offsets,
-                       perm, n_bad, inv, tiles, n_tiles, bm, shared_rows);
+                       perm, n_bad, inv, tiles, n_tiles, bm, shared_rows, tiles_s, n_tiles_s, bm_s);
     return after_launch("route");
 }
 
