@@ -95,6 +95,32 @@ def test_moe_prefill_small(orc, case, pack):
     _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_BF16)
 
 
+def _routing_with_counts(counts, S, K):
+    """ids [S][K] in which expert e is routed exactly counts[e] times, never
+    twice to one token (every count <= S): the sorted labels fill slot k of
+    tokens 0..S-1 in turn."""
+    labels = np.repeat(np.arange(len(counts)), counts)
+    assert labels.size == S * K and max(counts) <= S
+    return labels.reshape(K, S).T.astype(np.int32).copy()
+
+
+@pytest.mark.parametrize("counts,shared", [
+    ([1, 15, 16, 17, 0, 31], False),
+    ([32, 33, 15, 0, 0, 0], True),
+], ids=["1-15-16-17-0-31", "32-33-15-shared"])
+def test_moe_prefill_tile_boundaries(orc, counts, shared):
+    """Experts with 1..16 routed rows take one 16-row tile, larger ones 32-row
+    tiles (packed experts): counts on both sides of both boundaries."""
+    need_gpu()
+    S, K = 40, 2
+    G, U, Dn, sh, x, _, w = _moe_inputs(77 + len(counts), 4, S, K, len(counts), 256, 128, 64,
+                                        shared)
+    ids = _routing_with_counts(counts, S, K)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=len(counts)), counts)
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_BF16)
+
+
 def test_moe_prefill_ragged_zipf_invalid(orc):
     """Zipf-skewed routing (some experts with many rows, many with one or
     none), out-of-range ids and duplicates."""
