@@ -61,6 +61,7 @@ struct PgArgs {
     const int32_t *tiles, *n_tiles, *counts, *offsets;
     int E, SK, S;
     int nkb, nkq, cbs, rtn;  // packed copy: blocks per row, quads, scale slots, 16-row tiles
+    int mchunk;              // weight-streaming kernel: row tiles run together on one XCD
     int64_t rb;     // code bytes per weight row
     int ng, gshift, N;  // groups per row (fmt 4), log2 of the group size, weight rows
     int fmt;
@@ -394,13 +395,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int mt, nt;
     {
-        // XCD-aware order (gridDim.x a multiple of 8 for routed tiles): row
-        // tile mt runs on XCD mt % 8 with all its column tiles together
+        // XCD-aware order (workgroup w runs on XCD w % 8; gridDim.x a multiple
+        // of 8 L): runs of L = mchunk consecutive row tiles go to one XCD,
+        // which takes their column tiles one by one with the L row tiles of
+        // each side by side, so the L tiles (usually one expert's) read every
+        // weight slice together and share it through that XCD's L2, while
+        // their input rows stay there too.  L = 1: row tile mt on XCD mt % 8
+        // with all its column tiles together.
         const int w = blockIdx.y * gridDim.x + blockIdx.x, ntn = gridDim.y;
-        if (gridDim.x % 8 == 0) {
-            const int idx = w / 8;
-            mt = 8 * (idx / ntn) + w % 8;
-            nt = idx % ntn;
+        const int L = a.mchunk > 0 ? a.mchunk : 1;
+        if (gridDim.x % (8 * L) == 0) {
+            const int xcd = w % 8, j = w / 8, per = L * ntn;
+            const int r = j / per, q = j % per;
+            nt = q / L;
+            mt = (r * 8 + xcd) * L + q % L;
         } else {
             mt = blockIdx.x;
             nt = blockIdx.y;
@@ -800,14 +808,25 @@ static void sg_stage(const PgArgs &a, unsigned gx, bool down, const coli_qtensor
 // of PG_MOE_ROWS_PACKED rows, then (gx_s > 0) the short tiles of experts with
 // at most PG_MOE_ROWS_SHORT rows, which halve the matrix-core and input work
 // of the many lightly routed experts
+// row tiles of one XCD run (see k_sg) in the pass over the longer tiles
+// (measured on the S=544 Zipf(1.1) / Zipf(2.5) blocks: 1, 2, 4 within noise
+// of each other, 8 slower on Zipf(2.5); the repeated weight reads of the
+// multi-tile experts are served by the last-level cache either way)
+#ifndef COLI_SG_MCHUNK
+#define COLI_SG_MCHUNK 2
+#endif
+
 static void pg_moe_stage(const PgArgs &a, unsigned gx, bool down, bool packed, const coli_qtensor *T,
                          hipStream_t st, const int32_t *tiles_s, const int32_t *n_tiles_s,
                          unsigned gx_s) {
     if (packed) {
-        sg_stage<PG_MOE_ROWS_PACKED / 16>(a, gx, down, T, st);
+        PgArgs b = a;
+        b.mchunk = COLI_SG_MCHUNK;
+        const unsigned g8 = 8u * COLI_SG_MCHUNK;
+        sg_stage<PG_MOE_ROWS_PACKED / 16>(b, (gx + g8 - 1) / g8 * g8, down, T, st);
         if constexpr (PG_MOE_ROWS_SHORT > 0) {
             if (gx_s > 0) {
-                PgArgs b = a;
+                b.mchunk = 1;
                 b.tiles = tiles_s;
                 b.n_tiles = n_tiles_s;
                 sg_stage<PG_MOE_ROWS_SHORT / 16>(b, gx_s, down, T, st);
