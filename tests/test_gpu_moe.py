@@ -165,6 +165,22 @@ def test_moe_decode_duplicates_invalid_and_zero_weights(orc, kmode):
     _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
 
 
+def test_moe_decode_single_row_shared_invalid_ids(orc):
+    """S = 1, K = 7 plus the shared expert (8 pairs) on the matrix-core
+    kernels, with an out-of-range id, a negative id, a duplicate and a zero
+    weight."""
+    need_gpu()
+    G, U, Dn, sh, x, ids, w = _moe_inputs(33, 4, 1, 7, 8, 224, 96, 32, True)
+    ids = ids.copy()
+    w = w.copy()
+    ids[0, 1] = 8
+    ids[0, 2] = -1
+    ids[0, 4] = ids[0, 3]
+    w[0, 5] = 0.0
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
+
+
 def test_moe_decode_repeatable_bitwise(orc):
     need_gpu()
     G, U, Dn, sh, x, ids, w = _moe_inputs(5, 4, 4, 8, 16, 512, 256, 64, True)
