@@ -123,6 +123,31 @@ def test_compute_entries_decline_before_device(lib):
     assert launch1 == launch0  # nothing was launched
 
 
+def test_qmatmul_group_declines_before_device(lib):
+    """Every member is validated before anything is enqueued: bad counts,
+    NULL arrays or members, S < 1, misaligned pointers and tensors never
+    uploaded all decline with no launch."""
+    rc, W = upload(4, 1, 4, 64, 64, 1)
+    assert rc == coli.COLI_OK
+    _, _, launch0 = coli.coli_stats()
+    g = coli.coli_qmatmul_group
+    assert g([], [], [], 1, 0) == coli.COLI_DECLINED
+    assert g([W] * 9, [FAKE_S] * 9, [FAKE_S] * 9, 1, 0) == coli.COLI_DECLINED
+    assert "1..8" in coli.coli_last_reason()
+    assert g([W, W], [FAKE_S, None], [FAKE_S, FAKE_S], 1, 0) == coli.COLI_DECLINED
+    assert "member 1" in coli.coli_last_reason()
+    assert g([W], [FAKE_S], [FAKE_S], 0, 0) == coli.COLI_DECLINED
+    assert g([W, W], [FAKE_S, FAKE_S], [FAKE_S, FAKE_S + 2], 1, 0) == coli.COLI_DECLINED
+    assert g([W, coli.coli_qtensor()], [FAKE_S] * 2, [FAKE_S] * 2, 1, 0) == coli.COLI_DECLINED
+    assert "coli_tensor_upload" in coli.coli_last_reason()
+    L = coli._load()
+    assert L.coli_qmatmul_group(1, None, None, None, 1, None) == coli.COLI_DECLINED
+    with pytest.raises(ValueError):
+        g([W], [FAKE_S, FAKE_S], [FAKE_S], 1, 0)
+    _, _, launch1 = coli.coli_stats()
+    assert launch1 == launch0
+
+
 def _moe_tensors(fmt=4, E=4, F=64, D=128, gs=64):
     ng_g = -(-D // gs) if fmt == 4 else 1
     ng_d = -(-F // gs) if fmt == 4 else 1
