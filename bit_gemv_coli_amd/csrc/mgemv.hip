@@ -213,6 +213,21 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 #ifndef COLI_MG_STAGE_FIRST
 #define COLI_MG_STAGE_FIRST 0
 #endif
+// stacks of matrices with enough rows for at least COLI_MG_WIDE_MIN_WG
+// workgroups of 16 * NW_WIDE / KS_WIDE rows take the wider shape (measured on
+// a ring of 6144 x 6144 fmt-4 stacks of 8: 3 x 12 against 3 x 6 is 8.84 ->
+// 5.65 us per matrix at S = 4 and 4.11 -> 3.96 at S = 1; one matrix per
+// launch is slower with it: 96 workgroups for 256 compute units).  Not for
+// 4 scale slots per block (gs 32), whose S >= 3 kernels would spill.
+#ifndef COLI_MG_KS_WIDE
+#define COLI_MG_KS_WIDE 3
+#endif
+#ifndef COLI_MG_NW_WIDE
+#define COLI_MG_NW_WIDE 12
+#endif
+#ifndef COLI_MG_WIDE_MIN_WG
+#define COLI_MG_WIDE_MIN_WG 512
+#endif
 // quads of blocks in flight per wavefront in the dense GEMV and the MoE block
 #ifndef COLI_MG_NBQ_DENSE
 #define COLI_MG_NBQ_DENSE 2
@@ -860,11 +875,17 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     a.out = y;
     a.Sy = S;
     const bool g = W->fmt == 4;
+    constexpr int ROWS_WIDE = 16 * (COLI_MG_NW_WIDE / COLI_MG_KS_WIDE);
+    const bool wide = cb <= 2 && (int64_t)W->n * ((W->O + ROWS_WIDE - 1) / ROWS_WIDE) >= COLI_MG_WIDE_MIN_WG;
     ProfScope ps("mgemv", st, true);
     int ok;
 #define MG_CASE(NTV)                                                                          \
-    ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
-           : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps)
+    if (wide)                                                                                 \
+        ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
+               : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps); \
+    else                                                                                      \
+        ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
+               : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps)
     switch (S) {
     case 1: MG_CASE(1); break;
     case 2: MG_CASE(2); break;

@@ -240,3 +240,26 @@ def test_qmatmul_nonfinite_input_propagates(orc, kmode, bad):
     assert not np.isfinite(y_ref[0]).any()
     assert not np.isfinite(y[0]).any()
     assert_within(y[1], y_ref[1], A[1], TOL_FP32, "finite row")
+
+
+@pytest.mark.parametrize("fmt,O,I,gs,S", [(4, 4160, 512, 64, 1), (4, 4160, 640, 64, 4),
+                                          (4, 4096, 384, 128, 3), (2, 4112, 256, 0, 2)])
+def test_qmatmul_wide_stack(orc, fmt, O, I, gs, S):
+    """Stacks with enough rows for 512 or more 64-row workgroups take the
+    wider launch shape: every matrix against the oracle, and bit-identical to
+    the same matrix run alone (the narrower shape; both split the inputs
+    three ways per tile)."""
+    need_gpu()
+    n = 8
+    W, x = make_case(fmt, O, I, gs, S, seed=4000 + O + I + S, n=n)
+    T = qtensor(W, pack=True)
+    y = gpu_qmatmul(T, x, n)
+    xd = to_dev(x.astype(np.float32))
+    for e in range(n):
+        y_ref, A = orc.qmatmul(W.expert(e), x)
+        assert_within(y[e], y_ref, A, TOL_FP32, f"stack matrix {e}")
+        Te = qtensor(W.expert(e), pack=True)
+        alone = torch.full((1, S, O), float("nan"), device="cuda")
+        coli.check(coli.coli_qmatmul(Te, xd, alone, S), "coli_qmatmul")
+        torch.cuda.synchronize()
+        assert np.array_equal(alone.cpu().numpy()[0].view(np.uint32), y[e].view(np.uint32)), e
