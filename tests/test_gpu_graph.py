@@ -136,3 +136,29 @@ def test_moe_layer_graph_replays():
                                        ts[0], ts[1], ts[2], out, ws, wsb,
                                        torch.cuda.current_stream()), "coli_moe_layer")
     _replays_match(run, [out], between=lambda: ws.fill_(0x7F))
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_graph_grouped_gemv(S):
+    """coli_qmatmul_group (one launch for independent matrices, the way the
+    layer stream captures a layer's projections) replayed from a graph, with
+    single-matrix calls on other data between the replays."""
+    need_gpu()
+    shapes = [(1536, 640), (1024, 1536), (576, 640), (640, 2048)]
+    Ts, xs, ys = [], [], []
+    for j, (O, I) in enumerate(shapes):
+        W, x = make_case(4, O, I, 64, S, seed=60 + j)
+        Ts.append(qtensor(W, pack=True))
+        xs.append(to_dev(x))
+        ys.append(torch.empty((1, S, O), device="cuda"))
+    Wb, xb = make_case(4, 512, 1024, 64, S, seed=70)
+    Tb, xbd = qtensor(Wb, pack=True), to_dev(xb)
+    yb = torch.empty((1, S, 512), device="cuda")
+
+    def run():
+        coli.check(coli.coli_qmatmul_group(Ts, xs, ys, S), "coli_qmatmul_group")
+
+    def between():
+        coli.check(coli.coli_qmatmul(Tb, xbd, yb, S), "coli_qmatmul")
+
+    _replays_match(run, ys, between=between)
