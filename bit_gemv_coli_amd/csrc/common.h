@@ -82,6 +82,7 @@ int launch_router(const float *x, int S, int D, const float *R, const float *bia
 size_t moe_decode_ws_bytes(int S, int K, int F, int D, int has_shared);
 // matrix-core decode kernels (mgemv.hip); return 1 done, 0 not taken, <0 error
 bool mgemv_ok(const coli_qtensor *W);
+bool mgemv_int4_ok(const coli_qtensor *W);
 size_t packed_bytes(int fmt, int n, int O, int I, int gs);
 int launch_pack(coli_qtensor *t, void *packed, hipStream_t st);
 int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);

@@ -253,9 +253,15 @@ __host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3)
 // NT input rows per tile (1..4); CB groups per 128-input block (1, 2, 4);
 // KS wavefronts share one 16-row tile along the inputs; NMAT matrices (gate
 // and up share their rows); NBQ quads of blocks in flight per wavefront.
-template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ = 2>
+// QB: bits per code in the packed copy -- 4 (fmt 2 / 4: nibbles, B bytes
+// 16 v), 8 (fmt 1: int8 codes, B bytes v), 2 (fmt 3: 2-bit codes moved to the
+// top of each byte, B bytes 64 v).
+template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ = 2, int QB = 4>
 __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     static_assert(NW % KS == 0, "whole tiles per workgroup");
+    static_assert(QB == 4 || ((QB == 8 || QB == 2) && !GROUPED && EPI == MG_Y), "code width");
+    constexpr int LB = 4 * QB;   // code bytes per lane and 128-input block
+    constexpr int BLK = 64 * LB; // bytes per 16-row x 128-input tile block
     constexpr int TPW = NW / KS;
     constexpr int NTH = NW * 64;
     constexpr int NCOMBO = CB * NT;          // (group-in-block, input row) combinations
@@ -409,7 +415,7 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         srs[m] = __builtin_amdgcn_make_buffer_rsrc((void *)(pkm[m] + a.pk_scale_off), (short)0,
                                                    (int)(a.pk_stride - a.pk_scale_off), MG_RSRC_W3);
     }
-    const int qoff = tile_ld * a.nkb * 1024 + 16 * lane;  // this lane's bytes of block 0
+    const int qoff = tile_ld * a.nkb * BLK + LB * lane;  // this lane's bytes of block 0
     int soff[NSET];  // row n's 4 scales (one per block) of its C rows' group slot, quad 0
 #pragma unroll
     for (int st = 0; st < NSET; ++st) soff[st] = ((tile_ld * nkq * 16 + n) * CB + ccb[st]) * 16;
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     // requests for one quad of 128-input blocks (codes and group scales);
     // NBQ batches rotate: each is re-requested as soon as it is computed
     struct Batch {
-        u32x4 cw[MG_NBK][NMAT];
+        u32x4 cw[MG_NBK][NMAT][QB == 8 ? 2 : 1];  // (QB 2: 8 bytes in .x, .y)
         f32x4 sq[NMAT][GROUPED ? NSET : 1];  // the quad's 4 scales of each set's group slot
     };
     Batch bq[NBQ];
@@ -437,9 +443,19 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         for (int i = 0; i < MG_NBK; ++i) {
             const int kglob = __builtin_amdgcn_readfirstlane(max(min(kbg + i, kb_last), 0));
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-                bt.cw[i][m] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs[m], qoff, kglob * 1024, MG_AUX_NT));
+            for (int m = 0; m < NMAT; ++m) {
+                if constexpr (QB == 2) {
+                    const u32x2 v = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs[m], qoff, kglob * BLK, MG_AUX_NT));
+                    bt.cw[i][m][0] = u32x4{v.x, v.y, 0u, 0u};
+                } else {
+#pragma unroll
+                    for (int h = 0; h < (QB == 8 ? 2 : 1); ++h)
+                        bt.cw[i][m][h] = __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs[m], qoff + 16 * h, kglob * BLK,
+                                                                         MG_AUX_NT));
+                }
+            }
         }
         if constexpr (GROUPED) {
             const int sq0 = __builtin_amdgcn_readfirstlane((max(min(kbg, kb_last), 0) / 4) * 16 * CB * 16);
@@ -528,11 +544,22 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
             }
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                const u32x4 w = bt.cw[i][m];
-                const i32x4 be = {(int)even_x16(w.x), (int)even_x16(w.y), (int)even_x16(w.z),
-                                  (int)even_x16(w.w)};
-                const i32x4 bo = {(int)odd_x16(w.x), (int)odd_x16(w.y), (int)odd_x16(w.z),
-                                  (int)odd_x16(w.w)};
+                const u32x4 w = bt.cw[i][m][0];
+                i32x4 be, bo;  // B operands: the lane's even inputs, its odd inputs
+                if constexpr (QB == 4) {
+                    be = i32x4{(int)even_x16(w.x), (int)even_x16(w.y), (int)even_x16(w.z),
+                               (int)even_x16(w.w)};
+                    bo = i32x4{(int)odd_x16(w.x), (int)odd_x16(w.y), (int)odd_x16(w.z),
+                               (int)odd_x16(w.w)};
+                } else if constexpr (QB == 8) {
+                    be = __builtin_bit_cast(i32x4, w);
+                    bo = __builtin_bit_cast(i32x4, bt.cw[i][m][QB == 8 ? 1 : 0]);
+                } else {
+                    be = i32x4{(int)((w.x << 6) & 0xC0C0C0C0u), (int)((w.x << 4) & 0xC0C0C0C0u),
+                               (int)((w.x << 2) & 0xC0C0C0C0u), (int)(w.x & 0xC0C0C0C0u)};
+                    bo = i32x4{(int)((w.y << 6) & 0xC0C0C0C0u), (int)((w.y << 4) & 0xC0C0C0C0u),
+                               (int)((w.y << 2) & 0xC0C0C0C0u), (int)(w.y & 0xC0C0C0C0u)};
+                }
 #pragma unroll
                 for (int st = 0; st < NSET; ++st) {
                     i32x4 c = {0, 0, 0, 0};
@@ -644,7 +671,8 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
                         &red[(((tile_w * KS + w2) * NMAT + m) * NSET + c / 4) * 256 + (c % 4) * 64 + nn];
                     sum += ((rr[0] + rr[16] * 0x1p8f) + rr[32] * 0x1p16f) + rr[48] * 0x1p24f;
                 }
-            sum *= 0.0625f;  // the weights entered as 16 * (q - 8)
+            // the weights entered as 16 v (int4), v (int8) or 64 v (int2)
+            sum *= (QB == 4) ? 0.0625f : (QB == 2 ? 0.015625f : 1.0f);
             if (!GROUPED)
                 sum *= gload<float>(sc[m] + row);
             v[m] = sum;
@@ -674,7 +702,7 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
 // Which layouts have a packed form: int4 codes in whole 32-input packets, and
 // for fmt 4 a group size of 32, 64 or a multiple of 128.
 static bool packable(int fmt, int I, int gs) {
-    if (fmt != 2 && fmt != 4)
+    if (fmt < 1 || fmt > 4)
         return false;
     if (I % 32 != 0 || I < 32)
         return false;
@@ -693,12 +721,15 @@ struct PackGeom {
     int64_t code_bytes, scale_off, stride;
 };
 
+// code bytes of one lane in one 128-input block of a packed tile (32 inputs)
+static int lane_bytes(int fmt) { return fmt == 1 ? 32 : (fmt == 3 ? 8 : 16); }
+
 static PackGeom pack_geom(int fmt, int O, int I, int gs) {
     PackGeom g;
     g.rt = (O + 15) / 16;
     g.nkb = (I + 127) / 128;
     g.cbs = cbs_of(fmt, gs);
-    g.code_bytes = (int64_t)g.rt * g.nkb * 1024;
+    g.code_bytes = (int64_t)g.rt * g.nkb * 64 * lane_bytes(fmt);
     g.scale_off = g.code_bytes;
     const int64_t nkq = (g.nkb + 3) / 4;
     const int64_t sb = (fmt == 4) ? (int64_t)g.rt * nkq * 16 * 4 * g.cbs * 4 : 0;
@@ -737,6 +768,52 @@ __global__ __launch_bounds__(256) void k_pack_codes(const uint8_t *__restrict__ 
             v = u32x4{c.x ^ 0x88888888u, c.y ^ 0x88888888u, c.z ^ 0x88888888u, c.w ^ 0x88888888u};
         }
         *reinterpret_cast<u32x4 *>(pk + (int64_t)e * stride + ((int64_t)tr * nkb + kb) * 1024 + 16 * l) = v;
+    }
+}
+
+// packed fmt-1 / fmt-3 codes: tile block (e, rt, kb) of 64 lanes x LB bytes,
+// lane l = 16*j + r holding row 16*rt + r, inputs kb*128 + 32*j .. +32, ordered
+// for the two B operands (even inputs, odd inputs): fmt 1 (LB 32) the 16
+// even inputs' int8 codes, then the 16 odd ones'; fmt 3 (LB 8) two words, word
+// 0 for the even inputs, word 1 for the odd ones, whose byte b bits 2k, 2k+1
+// hold v = code - 2 (two's complement) of the input at position 4k + b of
+// that list.  Padding 0.
+__global__ __launch_bounds__(256) void k_pack_codes_row(int fmt, const uint8_t *__restrict__ q,
+                                                        int64_t rb, int64_t q_stride, int n, int O,
+                                                        int I, int rt, int nkb, int64_t stride,
+                                                        uint8_t *__restrict__ pk) {
+    const int LB = fmt == 1 ? 32 : 8;
+    const int64_t total = (int64_t)n * rt * nkb * 64;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * 256) {
+        const int l = (int)(c % 64);
+        const int64_t blk = c / 64;
+        const int kb = (int)(blk % nkb);
+        const int64_t t2 = blk / nkb;
+        const int tr = (int)(t2 % rt);
+        const int e = (int)(t2 / rt);
+        const int r = l & 15, j = l >> 4;
+        const int row = tr * 16 + r;
+        const int k0 = kb * 128 + 32 * j;
+        uint8_t out[32];
+        for (int i = 0; i < 32; ++i) out[i] = 0;
+        if (row < O) {
+            const uint8_t *src = q + (int64_t)e * q_stride + (int64_t)row * rb;
+            for (int i = 0; i < 32; ++i) {
+                const int k = k0 + i;
+                if (k >= I)
+                    break;
+                const int half = i & 1, m = i >> 1;  // odd / even list, position in it
+                if (fmt == 1) {
+                    out[half * 16 + m] = src[k];
+                } else {
+                    const int v = ((src[k >> 2] >> (2 * (k & 3))) & 3) - 2;
+                    out[half * 4 + (m & 3)] |= (uint8_t)((v & 3) << (2 * (m >> 2)));
+                }
+            }
+        }
+        uint8_t *dst = pk + (int64_t)e * stride + ((int64_t)tr * nkb + kb) * 64 * LB + (int64_t)LB * l;
+        for (int i = 0; i < LB; ++i) dst[i] = out[i];
     }
 }
 
@@ -779,9 +856,14 @@ int launch_pack(coli_qtensor *t, void *packed, hipStream_t st) {
         const int64_t total = (int64_t)t->n * g.rt * g.nkb * 64;
         const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
         ProfScope ps("pack", st);
-        hipLaunchKernelGGL(k_pack_codes, dim3(blocks), dim3(256), 0, st, (const uint8_t *)t->q,
-                           t->row_bytes, t->q_stride, t->n, t->O, t->I, g.rt, g.nkb, g.stride,
-                           (uint8_t *)packed);
+        if (t->fmt == 1 || t->fmt == 3)
+            hipLaunchKernelGGL(k_pack_codes_row, dim3(blocks), dim3(256), 0, st, t->fmt,
+                               (const uint8_t *)t->q, t->row_bytes, t->q_stride, t->n, t->O, t->I,
+                               g.rt, g.nkb, g.stride, (uint8_t *)packed);
+        else
+            hipLaunchKernelGGL(k_pack_codes, dim3(blocks), dim3(256), 0, st, (const uint8_t *)t->q,
+                               t->row_bytes, t->q_stride, t->n, t->O, t->I, g.rt, g.nkb, g.stride,
+                               (uint8_t *)packed);
         int rc = after_launch("pack");
         if (rc != COLI_OK) return rc;
     }
@@ -807,6 +889,11 @@ int launch_pack(coli_qtensor *t, void *packed, hipStream_t st) {
 bool mgemv_ok(const coli_qtensor *W) {
     return (W->flags & QF_PACKED) && W->pk != nullptr && packable(W->fmt, W->I, W->gs) &&
            W->pk_stride < ((int64_t)1 << 31);
+}
+
+// the int4 formats, which the MoE block, grouped GEMV and prefill kernels take
+bool mgemv_int4_ok(const coli_qtensor *W) {
+    return mgemv_ok(W) && (W->fmt == 2 || W->fmt == 4);
 }
 
 static int cb_of(const coli_qtensor *W) { return cbs_of(W->fmt, W->gs); }
@@ -843,14 +930,14 @@ static MgArgs mg_args_for(const coli_qtensor *W) {
     return a;
 }
 
-template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ>
+template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ, int QB = 4>
 static void mg_launch(MgArgs a, int groups, hipStream_t st, const ProfScope &ps) {
     size_t lds;
     plan_lds(NT, CB, NMAT, NW, a.I, a.kseg, a.nseg, lds);
     constexpr int TPW = NW / KS;
     const int tiles = (a.O + 15) / 16;
     const dim3 grid((unsigned)((tiles + TPW - 1) / TPW), (unsigned)groups);
-    hipExtLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW, NBQ>), grid, dim3(NW * 64),
+    hipExtLaunchKernelGGL((k_mgemv<NT, CB, GROUPED, NMAT, EPI, KS, NW, NBQ, QB>), grid, dim3(NW * 64),
                           (uint32_t)lds, st, ps.start(), ps.stop(), 0, a);
 }
 
@@ -879,8 +966,15 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     const bool wide = cb <= 2 && (int64_t)W->n * ((W->O + ROWS_WIDE - 1) / ROWS_WIDE) >= COLI_MG_WIDE_MIN_WG;
     ProfScope ps("mgemv", st, true);
     int ok;
+#define MG_ROWFMT(NTV, QBV)                                                                   \
+    (wide ? (mg_launch<NTV, 1, false, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE, QBV>(a, W->n, st, ps), 1) \
+          : (mg_launch<NTV, 1, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE, QBV>(a, W->n, st, ps), 1))
 #define MG_CASE(NTV)                                                                          \
-    if (wide)                                                                                 \
+    if (W->fmt == 1)                                                                          \
+        ok = MG_ROWFMT(NTV, 8);                                                               \
+    else if (W->fmt == 3)                                                                     \
+        ok = MG_ROWFMT(NTV, 2);                                                               \
+    else if (wide)                                                                            \
         ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
                : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps); \
     else                                                                                      \
@@ -893,6 +987,7 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     default: MG_CASE(4); break;
     }
 #undef MG_CASE
+#undef MG_ROWFMT
     if (!ok)
         return 0;
     return after_launch("mgemv") == COLI_OK ? 1 : -1;
@@ -907,7 +1002,7 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
     if (n < 1 || n > MG_MAXGRP || S < 1 || S > 4)
         return 0;
     for (int g = 0; g < n; ++g)
-        if (!mgemv_ok(W[g]) || W[g]->n != 1 || W[g]->fmt != W[0]->fmt || cb_of(W[g]) != cb_of(W[0]))
+        if (!mgemv_int4_ok(W[g]) || W[g]->n != 1 || W[g]->fmt != W[0]->fmt || cb_of(W[g]) != cb_of(W[0]))
             return 0;
     constexpr int TPW = COLI_MG_NW_DENSE / COLI_MG_KS_DENSE;
     MgArgs a = mg_args_for(W[0]);
@@ -978,7 +1073,7 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
 int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
     const coli_qtensor *all[6] = {m.gate, m.up, m.down, m.sg, m.su, m.sd};
     for (const coli_qtensor *t : all)
-        if (t && !mgemv_ok(t))
+        if (t && !mgemv_int4_ok(t))
             return 0;
     const int cb = cb_of(m.gate);
     const bool g = m.gate->fmt == 4;

@@ -737,7 +737,7 @@ static bool moe_all(const MoeArgs &m, bool (*ok)(const coli_qtensor *)) {
 int pgemm_moe_rows(const MoeArgs &m) {
     if (m.D % 32 != 0 || m.F % 32 != 0)
         return 0;
-    if (moe_all(m, mgemv_ok))
+    if (moe_all(m, mgemv_int4_ok))
         return PG_MOE_ROWS_PACKED;
     if (moe_all(m, pgemm_ok))
         return PG_MOE_ROWS;
@@ -845,7 +845,7 @@ int launch_pgemm_moe(const MoeArgs &m, int rows, const void *xg, void *hg, float
                      const int32_t *tiles, const int32_t *n_tiles, const int32_t *counts,
                      const int32_t *offsets, int max_tiles, const int32_t *tiles_s,
                      const int32_t *n_tiles_s, int max_short) {
-    const bool packed = rows > 0 && moe_all(m, mgemv_ok);
+    const bool packed = rows > 0 && moe_all(m, mgemv_int4_ok);
     const unsigned gx = (unsigned)((max_tiles + 7) / 8 * 8);
     const unsigned gx_s = (packed && tiles_s && n_tiles_s && max_short > 0)
                               ? (unsigned)((max_short + 7) / 8 * 8) : 0u;

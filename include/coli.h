@@ -114,7 +114,7 @@ int coli_tensor_upload(coli_qtensor *t, int fmt, int n, int O, int I, int gs, in
 /*
  * coli_packed_bytes -- device bytes the repacked copy of a tensor of this
  * shape needs (0 when the format / layout has no packed form: packing needs
- * fmt 2 or 4, I % 32 == 0, and for fmt 4 gs of 32, 64 or a multiple of 128).
+ * I % 32 == 0, and for fmt 4 gs of 32, 64 or a multiple of 128).
  */
 size_t coli_packed_bytes(int fmt, int n, int O, int I, int gs);
 
@@ -123,12 +123,17 @@ size_t coli_packed_bytes(int fmt, int n, int O, int I, int gs);
  * scales) into caller-owned device memory and attach it to the record; an
  * upload-time layout conversion in the spirit of the pages' upload-time
  * offset_to_signed_s4 (colibri PR #298, CUDA fmt=4 commit).  Layout: every
- * 16-row x 128-input tile becomes one contiguous 1 KiB block in the order the
- * matrix-core decode kernels load it (so each wavefront load is one 1 KiB
- * request) holding the codes as two's-complement nibbles q - 8; the group
- * scales follow, one run per (tile, 4 blocks, row) so a lane fetches a whole
- * batch's scales at once; rows and inputs past O and I are padded with zero
- * weights.  The represented weights are unchanged.
+ * 16-row x 128-input tile becomes one contiguous block in the order the
+ * matrix-core decode kernels load it (so each wavefront load is one request):
+ * fmt 2 / 4 1 KiB of two's-complement nibbles q - 8; fmt 1 2 KiB of the int8
+ * codes, each lane's 32 inputs as the 16 even ones then the 16 odd ones;
+ * fmt 3 512 bytes of two's-complement 2-bit values q - 2 in the same
+ * even / odd split.  The fmt-4 group scales follow, one run per (tile, 4
+ * blocks, row) so a lane fetches a whole batch's scales at once (per-row
+ * scales stay in the original s); rows and inputs past O and I are padded
+ * with zero weights.  The represented weights are unchanged.  Only fmt 2 / 4
+ * packed copies serve the MoE block, the grouped GEMV and the prefill
+ * kernels; fmt 1 / 3 packed copies serve coli_qmatmul at S <= 4.
  *   t         record from coli_tensor_upload (updated on success)
  *   packed    device buffer of at least coli_packed_bytes(...) bytes, 256-byte
  *             aligned, owned by the caller, kept alive while t is used

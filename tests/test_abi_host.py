@@ -235,7 +235,9 @@ def test_moe_hidden_validation(lib):
     (4, 6144, 2048, 128, 6144 // 16 * 16 * (1024 + 64)),
     (4, 33, 4160, 32, 3 * 33 * 1024 + 3 * 9 * 16 * 4 * 4 * 4),  # scales in whole quads
     (2, 100, 256, 0, ((7 * 2 * 1024 + 255) // 256) * 256),
-    (4, 16, 96, 48, 0), (4, 16, 96, 16, 0), (1, 16, 128, 0, 0), (3, 16, 128, 0, 0),
+    (1, 16, 128, 0, 2048), (1, 40, 4096 + 32, 0, 3 * 33 * 2048),   # int8: 2 KiB tile blocks
+    (3, 16, 128, 0, 512), (3, 40, 4096 + 32, 0, 3 * 33 * 512),     # int2: 512-byte tile blocks
+    (4, 16, 96, 48, 0), (4, 16, 96, 16, 0), (1, 16, 100, 0, 0), (3, 16, 66, 0, 0),
     (4, 16, 100, 64, 0),
 ])
 def test_packed_bytes(lib, fmt, O, I, gs, expect):

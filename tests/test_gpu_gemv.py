@@ -243,7 +243,9 @@ def test_qmatmul_nonfinite_input_propagates(orc, kmode, bad):
 
 
 @pytest.mark.parametrize("fmt,O,I,gs,S", [(4, 4160, 512, 64, 1), (4, 4160, 640, 64, 4),
-                                          (4, 4096, 384, 128, 3), (2, 4112, 256, 0, 2)])
+                                          (4, 4096, 384, 128, 3), (2, 4112, 256, 0, 2),
+                                          (1, 4160, 512, 0, 1), (1, 4096, 384, 0, 4),
+                                          (3, 4112, 640, 0, 2), (3, 4096, 256, 0, 4)])
 def test_qmatmul_wide_stack(orc, fmt, O, I, gs, S):
     """Stacks with enough rows for 512 or more 64-row workgroups take the
     wider launch shape: every matrix against the oracle, and bit-identical to
@@ -263,3 +265,32 @@ def test_qmatmul_wide_stack(orc, fmt, O, I, gs, S):
         coli.check(coli.coli_qmatmul(Te, xd, alone, S), "coli_qmatmul")
         torch.cuda.synchronize()
         assert np.array_equal(alone.cpu().numpy()[0].view(np.uint32), y[e].view(np.uint32)), e
+
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+@pytest.mark.parametrize("fmt", [1, 3])
+def test_qmatmul_per_row_packed_extremes(orc, fmt, S):
+    """fmt 1 and fmt 3 on the matrix cores (packed copy): int8 codes -128 and
+    127 side by side, every 2-bit code, rows of a single repeated code, a
+    ragged last tile (O = 37) and inputs past the last whole block
+    (I = 416), against the oracle."""
+    need_gpu()
+    O, I = 37, 416
+    r = sd.rng(90 + fmt + S)
+    x = sd.gen_x(r, S, I)
+    q, s = sd.gen_matrix(r, fmt, O, I, 0)
+    q = q.copy()
+    if fmt == 1:
+        q[0, 0::2], q[0, 1::2] = 0x80, 0x7F   # -128, 127
+        q[1, :] = 0x80
+        q[2, :] = 0x7F
+    else:
+        q[0, :] = 0b11100100                  # codes 0, 1, 2, 3 in every byte
+        q[1, :] = 0x00                        # every weight -2
+        q[2, :] = 0xFF                        # every weight +1
+    W = QMat(fmt, O, I, 0, q, s)
+    T = qtensor(W, pack=True)
+    assert T.desc.flags & 8, "the packed copy should be attached"
+    y = gpu_qmatmul(T, x)[0]
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(y, y_ref, A, TOL_FP32, f"fmt {fmt} S {S}")
