@@ -266,6 +266,33 @@ def side_measurements(coli, sd, np, torch, log):
     us = timed(lambda i: coli.coli_qmatmul(T, x, y, 1, st), 200)
     out["gemv_1024x2048_g64_us"] = us
     log(f"gemv 1024x2048 g64: {us:.2f} us/call")
+    del T, q, s
+    # the same shape from a >= 1 GiB ring of distinct copies (HBM, not the
+    # last-level cache): one matrix per launch, and stacks of 64 per launch
+    mb1 = qbytes(4, 1024, 2048, 64)
+    ncopy = -(-(1 << 30) // mb1) // 64 * 64 + 64
+    q, s = sd.pool_on_device(8, 4, ncopy, 1024, 2048, 64)
+    Ts = [coli.QTensor(4, q[c], s[c], 1024, 2048, 64, n=1) for c in range(ncopy)]
+    for t in Ts:
+        t.pack()
+    us1 = timed(lambda i: coli.coli_qmatmul(Ts[i % ncopy], x, y, 1, st), 2 * ncopy)
+    del Ts
+    NST = 64
+    Tst = [coli.QTensor(4, q[c * NST:(c + 1) * NST], s[c * NST:(c + 1) * NST], 1024, 2048, 64, n=NST)
+           for c in range(ncopy // NST)]
+    for t in Tst:
+        t.pack()
+    ys = torch.empty((NST, 1, 1024), device=dev)
+    usn = timed(lambda i: coli.coli_qmatmul(Tst[i % len(Tst)], x, ys, 1, st), 4 * len(Tst))
+    per = mb1 + 2048 * 4 + 1024 * 4
+    out["gemv_1024x2048_g64_ring"] = {
+        "copies": ncopy, "one_per_launch": {"us": us1, "GBps": per / (us1 * 1e-6) / 1e9},
+        f"{NST}_per_launch": {"us_per_matrix": usn / NST, "GBps": NST * per / (usn * 1e-6) / 1e9,
+                              "frac_hbm": NST * per / (usn * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+    log(f"gemv 1024x2048 g64 ring of {ncopy}: {us1:.2f} us per launch of one; "
+        f"{usn / NST:.3f} us per matrix in launches of {NST} ({NST * per / (usn * 1e-6) / 1e9:.0f} GB/s)")
+    del Tst, q, s
+    torch.cuda.empty_cache()
 
     # what a trivial streaming read of one matrix-sized buffer reaches per
     # launch (same ring discipline): the per-launch ceiling at this size

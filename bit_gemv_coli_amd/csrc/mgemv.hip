@@ -225,6 +225,18 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
 #ifndef COLI_MG_NW_WIDE
 #define COLI_MG_NW_WIDE 12
 #endif
+// ... and at S = 1 two wavefronts along the inputs x 4 tiles (8 wavefronts):
+// stacked 6144 x 6144 fmt 4 g64 3.97 -> 3.58 us per matrix, 1024 x 2048
+// stacks of 64 0.42 -> 0.27 us (2048 inputs are 4 quads: no uneven 3-way
+// split); slower than 3 x 12 at S = 4 (5.61 -> 5.89 us)
+#ifndef COLI_MG_KS_WIDE1
+#define COLI_MG_KS_WIDE1 2
+#endif
+#ifndef COLI_MG_NW_WIDE1
+#define COLI_MG_NW_WIDE1 8
+#endif
+static_assert(COLI_MG_NW_WIDE / COLI_MG_KS_WIDE == COLI_MG_NW_WIDE1 / COLI_MG_KS_WIDE1,
+              "both wide shapes cover the same rows per workgroup");
 #ifndef COLI_MG_WIDE_MIN_WG
 #define COLI_MG_WIDE_MIN_WG 512
 #endif
@@ -966,8 +978,10 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     const bool wide = cb <= 2 && (int64_t)W->n * ((W->O + ROWS_WIDE - 1) / ROWS_WIDE) >= COLI_MG_WIDE_MIN_WG;
     ProfScope ps("mgemv", st, true);
     int ok;
+#define MG_KSW(NTV) ((NTV) == 1 ? COLI_MG_KS_WIDE1 : COLI_MG_KS_WIDE)
+#define MG_NWW(NTV) ((NTV) == 1 ? COLI_MG_NW_WIDE1 : COLI_MG_NW_WIDE)
 #define MG_ROWFMT(NTV, QBV)                                                                   \
-    (wide ? (mg_launch<NTV, 1, false, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE, QBV>(a, W->n, st, ps), 1) \
+    (wide ? (mg_launch<NTV, 1, false, 1, MG_Y, MG_KSW(NTV), MG_NWW(NTV), COLI_MG_NBQ_DENSE, QBV>(a, W->n, st, ps), 1) \
           : (mg_launch<NTV, 1, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE, QBV>(a, W->n, st, ps), 1))
 #define MG_CASE(NTV)                                                                          \
     if (W->fmt == 1)                                                                          \
@@ -975,8 +989,8 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     else if (W->fmt == 3)                                                                     \
         ok = MG_ROWFMT(NTV, 2);                                                               \
     else if (wide)                                                                            \
-        ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
-               : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_WIDE, COLI_MG_NW_WIDE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps); \
+        ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, MG_KSW(NTV), MG_NWW(NTV), COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
+               : mg_dispatch_cb<NTV, false, 1, MG_Y, MG_KSW(NTV), MG_NWW(NTV), COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps); \
     else                                                                                      \
         ok = g ? mg_dispatch_cb<NTV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps) \
                : mg_dispatch_cb<NTV, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps)
@@ -988,6 +1002,8 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     }
 #undef MG_CASE
 #undef MG_ROWFMT
+#undef MG_KSW
+#undef MG_NWW
     if (!ok)
         return 0;
     return after_launch("mgemv") == COLI_OK ? 1 : -1;
