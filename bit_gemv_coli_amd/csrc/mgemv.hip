@@ -247,8 +247,10 @@ static_assert(COLI_MG_NW_WIDE / COLI_MG_KS_WIDE == COLI_MG_NW_WIDE1 / COLI_MG_KS
 #ifndef COLI_MG_NBQ_GATEUP
 #define COLI_MG_NBQ_GATEUP 2
 #endif
+// (down: one quad; measured 13.6 against 14.1 us per down launch with two,
+// 16.5 with four, in the 8-of-256-expert block)
 #ifndef COLI_MG_NBQ_DOWN
-#define COLI_MG_NBQ_DOWN 2
+#define COLI_MG_NBQ_DOWN 1
 #endif
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
@@ -1009,6 +1011,15 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     return after_launch("mgemv") == COLI_OK ? 1 : -1;
 }
 
+// launch shape of the grouped GEMV (75-layer stream with the four projections
+// grouped: 3 x 6 64.0-64.7 us per layer, 2 x 4 64.9-65.2, 2 x 8 66.8-68.2)
+#ifndef COLI_MG_KS_GROUP
+#define COLI_MG_KS_GROUP COLI_MG_KS_DENSE
+#endif
+#ifndef COLI_MG_NW_GROUP
+#define COLI_MG_NW_GROUP COLI_MG_NW_DENSE
+#endif
+
 // Grouped GEMV: n independent single matrices (same format class, each with a
 // packed copy) with their own inputs x[g] [S][I_g] and outputs y[g] [S][O_g],
 // one launch.  Returns 0 when the group is not taken (the caller then runs
@@ -1020,7 +1031,7 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
     for (int g = 0; g < n; ++g)
         if (!mgemv_int4_ok(W[g]) || W[g]->n != 1 || W[g]->fmt != W[0]->fmt || cb_of(W[g]) != cb_of(W[0]))
             return 0;
-    constexpr int TPW = COLI_MG_NW_DENSE / COLI_MG_KS_DENSE;
+    constexpr int TPW = COLI_MG_NW_GROUP / COLI_MG_KS_GROUP;
     MgArgs a = mg_args_for(W[0]);
     a.Sy = S;
     a.ngrp = n;
@@ -1044,7 +1055,7 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
         m.O = W[g]->O;
         m.I = W[g]->I;
         size_t lds;
-        plan_lds(S, cb_of(W[g]), 1, COLI_MG_NW_DENSE, m.I, m.kseg, m.nseg, lds);
+        plan_lds(S, cb_of(W[g]), 1, COLI_MG_NW_GROUP, m.I, m.kseg, m.nseg, lds);
         lds_max = std::max(lds_max, lds);
         m.wg0 = wg;
         wg += ((m.O + 15) / 16 + TPW - 1) / TPW;
@@ -1054,14 +1065,14 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
     ProfScope ps("mgemv_group", st, true);
     int ok = 1;
 #define MG_G(NTV, CBV)                                                                             \
-    hipExtLaunchKernelGGL((k_mgemv<NTV, CBV, true, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE,    \
+    hipExtLaunchKernelGGL((k_mgemv<NTV, CBV, true, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP,    \
                                    COLI_MG_NBQ_DENSE>),                                            \
-                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_DENSE * 64), (uint32_t)lds_max, st, \
+                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
                           ps.start(), ps.stop(), 0, a)
 #define MG_R(NTV)                                                                                  \
-    hipExtLaunchKernelGGL((k_mgemv<NTV, 1, false, 1, MG_Y, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE,     \
+    hipExtLaunchKernelGGL((k_mgemv<NTV, 1, false, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP,     \
                                    COLI_MG_NBQ_DENSE>),                                            \
-                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_DENSE * 64), (uint32_t)lds_max, st, \
+                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
                           ps.start(), ps.stop(), 0, a)
 #define MG_NT(NTV)                                   \
     if (!grouped) { MG_R(NTV); }                     \
