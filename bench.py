@@ -217,6 +217,9 @@ def main():
         if not args.no_extra:
             extra["oracle_timings"] = oracle_timings(sd, np, log)
 
+    if not args.no_extra:
+        extra["summary"] = summary(extra, value, roofline)
+
     res = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -228,6 +231,31 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(res), flush=True)
+
+
+def summary(e, value, roofline):
+    """One line per workload: the figure and its fraction of the bound that
+    applies (HBM 8 TB/s for decode, max(flops/bf16 peak, bytes/HBM) for the
+    prefill MoE block, bf16 peak for the dense prefill GEMM)."""
+    out = {"decode_moe_block_S1": {"GBps": value, "frac_hbm": value / HBM_PEAK_GBS},
+           "decode_moe_gateup_kernel": {"GBps": roofline.get("achieved"), "frac_hbm": roofline.get("frac")}}
+    st = e.get("gemv_6144x6144_ring_stacked", {})
+    for k in ("fmt4_g64_S1", "fmt4_g64_S4", "fmt4_g128_S1", "fmt2_S1", "fmt1_S1", "fmt3_S1"):
+        if k in st:
+            out[f"gemv_6144x6144_{k}_x8_per_launch"] = {"GBps": st[k]["GBps"], "frac_hbm": st[k]["frac_hbm"]}
+    one = e.get("gemv_6144x6144_ring", {}).get("fmt4_g64_S1")
+    if one:
+        out["gemv_6144x6144_fmt4_g64_S1_one_per_launch"] = {"GBps": one["GBps"], "frac_hbm": one["frac_hbm"]}
+    ls = e.get("layer_stream_75")
+    if ls:
+        out["layer_stream_75"] = {"us_per_layer": ls["us_per_layer"], "frac_hbm": ls["frac_hbm"]}
+    pm = e.get("prefill_moe_544_zipf1.1_g128")
+    if pm:
+        out["prefill_moe_544_zipf1.1"] = {"us": pm["us"], "TFLOPs": pm["TFLOPs"], "frac_roofline": pm["frac_roofline"]}
+    pd = e.get("prefill_dense_544x6144x6144_g128")
+    if pd:
+        out["prefill_dense_544x6144x6144"] = {"TFLOPs": pd["TFLOPs"], "frac_bf16_peak": pd["frac_bf16_peak"]}
+    return out
 
 
 def make_timed(torch):
