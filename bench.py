@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the S=544 prefill measurements (dense GEMM and MoE block); prints "
                          "their JSON (for profiling those kernels)")
+    ap.add_argument("--gemv-only", action="store_true",
+                    help="only the GEMV measurements (1024x2048 latency and ring, 6144x6144 format "
+                         "sweep one and eight matrices per launch)")
     ap.add_argument("--layer-stream-only", action="store_true",
                     help="only the 75-layer decode stream (grouped and one launch per projection)")
     ap.add_argument("--router-only", action="store_true",
@@ -122,6 +125,9 @@ def main():
 
     if args.prefill_only:
         print(json.dumps(prefill_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
+        return
+    if args.gemv_only:
+        print(json.dumps(gemv_measurements(coli, sd, np, torch, log)), flush=True)
         return
     if args.layer_stream_only:
         print(json.dumps(layer_stream(coli, sd, np, torch, log)), flush=True)
@@ -278,8 +284,21 @@ def make_timed(torch):
 
 
 def side_measurements(coli, sd, np, torch, log):
-    """Single fmt-4 GEMV (1024x2048, latency) and the 6144x6144 format sweep
-    (ring of distinct copies >= 1 GiB so each launch streams from HBM)."""
+    """The GEMV measurements, the ceiling probes, the router, the S=544
+    prefill and the 75-layer stream."""
+    timed = make_timed(torch)
+    out = gemv_measurements(coli, sd, np, torch, log)
+    out.update(ceiling_probes(coli, torch, log))
+    out.update(router_measurements(coli, sd, np, torch, log, timed))
+    out.update(prefill_measurements(coli, sd, np, torch, log, timed))
+    out.update(layer_stream(coli, sd, np, torch, log))
+    return out
+
+
+def gemv_measurements(coli, sd, np, torch, log):
+    """Single fmt-4 GEMV (1024x2048, latency and a >= 1 GiB ring) and the
+    6144x6144 format sweep (ring of distinct copies >= 1 GiB so each launch
+    streams from HBM), one and eight matrices per launch."""
     out = {}
     dev = "cuda"
     st = torch.cuda.current_stream()
@@ -371,10 +390,6 @@ def side_measurements(coli, sd, np, torch, log):
             del Ts, Tst, q, s
     out["gemv_6144x6144_ring"] = sweep
     out["gemv_6144x6144_ring_stacked"] = stack
-    out.update(ceiling_probes(coli, torch, log))
-    out.update(router_measurements(coli, sd, np, torch, log, timed))
-    out.update(prefill_measurements(coli, sd, np, torch, log, timed))
-    out.update(layer_stream(coli, sd, np, torch, log))
     return out
 
 
