@@ -213,6 +213,23 @@ def main():
     # ---- side measurements --------------------------------------------------
     extra = {"block_us": ms * 1e3, "kernels": kern, "wall_s_timed": wall}
     if not args.no_extra:
+        # the same blocks in two submissions (begin: resident slots; end: the
+        # late ones), half of the 8 slots late
+        late = torch.from_numpy((np.arange(K) % 2).astype(np.int32).reshape(1, K)).to(dev)
+        wsb2 = coli.coli_moe_block_two_phase_workspace_bytes(E, 1, K, F, D, 0)
+        ws2 = torch.empty(wsb2, dtype=torch.uint8, device=dev)
+
+        def step2(i):
+            j = i % NR
+            coli.check(coli.coli_moe_block_begin(tg, tu, td, x_d, 1, ids_d[j], w_d[j], K, late, None,
+                                                 None, None, out, ws2, wsb2, stream), "begin")
+            coli.check(coli.coli_moe_block_end(tg, tu, td, x_d, 1, w_d[j], K, 0, out, ws2, wsb2,
+                                               stream), "end")
+        us2 = make_timed(torch)(step2, args.steps)
+        extra["two_phase_block_us"] = {"begin_plus_end": us2, "one_submission": ms * 1e3,
+                                       "late_slots": K // 2}
+        log(f"two-phase block (4 of 8 slots late): {us2:.2f} us against {ms * 1e3:.2f} us in one")
+        del ws2
         extra.update(side_measurements(coli, sd, np, torch, log))
 
     # ---- CPU oracle baseline -------------------------------------------------

@@ -52,6 +52,9 @@ def _load():
         "coli_tensor_upload": (i32, [QP, i32, i32, i32, i32, i32, i32, vp, vp]),
         "coli_qmatmul": (i32, [QP, vp, vp, i32, vp]),
         "coli_qmatmul_group": (i32, [i32, vp, vp, vp, i32, vp]),
+        "coli_moe_block_two_phase_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "coli_moe_block_begin": (i32, [QP, QP, QP, vp, i32, vp, vp, i32, vp, QP, QP, QP, vp, vp, sz, vp]),
+        "coli_moe_block_end": (i32, [QP, QP, QP, vp, i32, vp, i32, i32, vp, vp, sz, vp]),
         "coli_packed_bytes": (sz, [i32, i32, i32, i32, i32]),
         "coli_tensor_pack": (i32, [QP, vp, sz, vp]),
         "coli_gemv_max_rows": (i32, []),
@@ -93,6 +96,8 @@ def exported_symbols():
     """Names the binding expects libcoli to export."""
     return ["coli_tensor_upload", "coli_packed_bytes", "coli_tensor_pack", "coli_qmatmul",
             "coli_qmatmul_group", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
+            "coli_moe_block_two_phase_workspace_bytes", "coli_moe_block_begin",
+            "coli_moe_block_end",
             "coli_set_decode_kernel",
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
@@ -146,6 +151,25 @@ def coli_qmatmul(W, x, y, S, stream=None) -> int:
 
 
 COLI_GROUP_MAX = 8
+
+
+def coli_moe_block_two_phase_workspace_bytes(E, S, K, F, D, has_shared) -> int:
+    return _load().coli_moe_block_two_phase_workspace_bytes(E, S, K, F, D, int(bool(has_shared)))
+
+
+def coli_moe_block_begin(gate, up, down, x, S, ids, w, K, late, sh_gate, sh_up, sh_down, out,
+                         workspace, ws_bytes, stream=None) -> int:
+    return _load().coli_moe_block_begin(_qp(gate), _qp(up), _qp(down), _ptr(x), S, _ptr(ids),
+                                        _ptr(w), K, _ptr(late), _qp(sh_gate), _qp(sh_up),
+                                        _qp(sh_down), _ptr(out), _ptr(workspace), ws_bytes,
+                                        _stream(stream))
+
+
+def coli_moe_block_end(gate, up, down, x, S, w, K, has_shared, out, workspace, ws_bytes,
+                       stream=None) -> int:
+    return _load().coli_moe_block_end(_qp(gate), _qp(up), _qp(down), _ptr(x), S, _ptr(w), K,
+                                      int(bool(has_shared)), _ptr(out), _ptr(workspace), ws_bytes,
+                                      _stream(stream))
 
 
 def coli_qmatmul_group(Ws, xs, ys, S, stream=None) -> int:

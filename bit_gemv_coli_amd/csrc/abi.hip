@@ -527,6 +527,92 @@ int coli_moe_block(const coli_qtensor *gate, const coli_qtensor *up, const coli_
     return launch_moe_prefill(a);
 }
 
+// two-phase block workspace: [block][resident ids][late ids][late experts' output]
+struct TwoPhaseWs {
+    size_t blk, ida, idb, y, total;
+};
+static TwoPhaseWs two_phase_ws(int E, int S, int K, int F, int D, int has_sh) {
+    TwoPhaseWs t;
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    t.blk = 0;
+    const size_t b = coli_moe_workspace_bytes(E, S, K, F, D, has_sh);
+    t.ida = al(b);
+    t.idb = t.ida + al(sizeof(int32_t) * (size_t)S * K);
+    t.y = t.idb + al(sizeof(int32_t) * (size_t)S * K);
+    t.total = b == 0 ? 0 : t.y + al(sizeof(float) * (size_t)S * D);
+    return t;
+}
+
+size_t coli_moe_block_two_phase_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shared) {
+    if (E < 1 || S < 1 || K < 1 || F < 1 || Dm < 1)
+        return 0;
+    return two_phase_ws(E, S, K, F, Dm, has_shared ? 1 : 0).total;
+}
+
+static int moe_run(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                   const float *x, int S, const int32_t *ids, const float *w, int K,
+                   const coli_qtensor *sg, const coli_qtensor *su, const coli_qtensor *sd, float *out,
+                   void *ws, size_t ws_bytes, hipStream_t st) {
+    MoeArgs a;
+    a.gate = gate; a.up = up; a.down = down;
+    a.sg = sg; a.su = su; a.sd = sd;
+    a.x = x; a.S = S; a.K = K; a.E = gate->n; a.F = gate->O; a.D = gate->I;
+    a.ids = ids; a.w = w; a.out = out; a.h_out = nullptr;
+    a.ws = ws; a.ws_bytes = ws_bytes; a.st = st;
+    return S <= coli_gemv_max_rows() ? launch_moe_decode(a) : launch_moe_prefill(a);
+}
+
+int coli_moe_block_begin(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                         const float *x, int S, const int32_t *ids, const float *w, int K,
+                         const int32_t *late, const coli_qtensor *sh_gate,
+                         const coli_qtensor *sh_up, const coli_qtensor *sh_down, float *out,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    if (check_moe(gate, up, down, x, S, ids, K, sh_gate, sh_up, sh_down, "moe_block_begin") != COLI_OK)
+        return COLI_DECLINED;
+    if (!down || !w || !out || !late)
+        return decline("moe_block_begin: NULL down, w, out or late");
+    if (!workspace || !dev_aligned(workspace, 256))
+        return decline("moe_block_begin: workspace NULL or not 256-byte aligned");
+    if ((int64_t)S * K > INT32_MAX / 2)
+        return decline("moe_block_begin: S*K too large");
+    const TwoPhaseWs t = two_phase_ws(gate->n, S, K, gate->O, gate->I, sh_gate != nullptr);
+    if (t.total == 0 || ws_bytes < t.total)
+        return decline("moe_block_begin: workspace %zu bytes < %zu needed", ws_bytes, t.total);
+    if (!gate_call())
+        return COLI_DECLINED;
+    const hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    int32_t *ida = (int32_t *)(ws + t.ida), *idb = (int32_t *)(ws + t.idb);
+    int rc = launch_split_ids(ids, late, S * K, ida, idb, st);
+    if (rc != COLI_OK) return rc;
+    return moe_run(gate, up, down, x, S, ida, w, K, sh_gate, sh_up, sh_down, out, ws, t.ida, st);
+}
+
+int coli_moe_block_end(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                       const float *x, int S, const float *w, int K, int has_shared, float *out,
+                       void *workspace, size_t ws_bytes, void *stream) {
+    if (!workspace || !dev_aligned(workspace, 256))
+        return decline("moe_block_end: workspace NULL or not 256-byte aligned");
+    // the late routing sits in the workspace; any non-NULL ids pointer passes here
+    if (check_moe(gate, up, down, x, S, (const int32_t *)workspace, K, nullptr, nullptr, nullptr,
+                  "moe_block_end") != COLI_OK)
+        return COLI_DECLINED;
+    if (!down || !w || !out)
+        return decline("moe_block_end: NULL down, w or out");
+    const TwoPhaseWs t = two_phase_ws(gate->n, S, K, gate->O, gate->I, has_shared ? 1 : 0);
+    const int32_t *idb = (const int32_t *)((char *)workspace + t.idb);
+    if (t.total == 0 || ws_bytes < t.total)
+        return decline("moe_block_end: workspace %zu bytes < %zu needed", ws_bytes, t.total);
+    if (!gate_call())
+        return COLI_DECLINED;
+    const hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *y = (float *)(ws + t.y);
+    int rc = moe_run(gate, up, down, x, S, idb, w, K, nullptr, nullptr, nullptr, y, ws, t.ida, st);
+    if (rc != COLI_OK) return rc;
+    return launch_residual_add(out, y, out, (int64_t)S * gate->I, st);
+}
+
 int coli_moe_hidden(const coli_qtensor *gate, const coli_qtensor *up, const float *x, int S,
                     const int32_t *ids, int K, const coli_qtensor *sh_gate,
                     const coli_qtensor *sh_up, float *h_out, void *workspace, size_t ws_bytes,

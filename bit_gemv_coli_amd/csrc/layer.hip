@@ -71,6 +71,30 @@ __global__ __launch_bounds__(256) void k_residual_add(const float *h, const floa
         out[i] = h[i] + y[i];
 }
 
+// The two routings of a two-phase block: slot i keeps its expert in ida when
+// it is resident (late[i] == 0) and in idb when it is late; the other list
+// holds -1 there, which the block skips.
+__global__ __launch_bounds__(256) void k_split_ids(const int32_t *__restrict__ ids,
+                                                   const int32_t *__restrict__ late, int n,
+                                                   int32_t *__restrict__ ida,
+                                                   int32_t *__restrict__ idb) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+        const int32_t e = ids[i];
+        const bool l = late[i] != 0;
+        ida[i] = l ? -1 : e;
+        idb[i] = l ? e : -1;
+    }
+}
+
+int launch_split_ids(const int32_t *ids, const int32_t *late, int n, int32_t *ida, int32_t *idb,
+                     hipStream_t st) {
+    ProfScope ps("split_ids", st);
+    hipLaunchKernelGGL(k_split_ids, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, late,
+                       n, ida, idb);
+    return after_launch("split_ids");
+}
+
 int launch_rmsnorm(const float *x, int S, int D, const float *w, double eps, float *y,
                    hipStream_t st) {
     ProfScope ps("rmsnorm", st);

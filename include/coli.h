@@ -260,6 +260,38 @@ int coli_moe_hidden(const coli_qtensor *gate, const coli_qtensor *up, const floa
 /* Workspace bytes coli_moe_block / coli_moe_hidden need (0 on bad input). */
 size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shared);
 
+/*
+ * coli_moe_block_begin / coli_moe_block_end -- the expert block in two
+ * submissions (colibri-strix commit log, "metal: overlap disk loads with GPU
+ * compute inside the layer": the resident experts and the shared expert go
+ * to the GPU first, the experts still being loaded follow in a second submit
+ * once they are in place).  Here a slot (s, k) is late when late[s][k] != 0:
+ * begin computes out = the block over the resident slots (+ the shared
+ * expert); end, enqueued once the late experts' weights are in the stacks,
+ * adds the block over the late slots:
+ *     out[s] = (sum_{k resident} w y + shared) + (sum_{k late} w y)
+ * each sum in ascending k (deterministic; the same value as coli_moe_block up
+ * to the order of that one extra addition, within the same bounds).
+ *   begin: arguments as coli_moe_block plus late, device int32 [S][K];
+ *   end:   the same tensors, x, S, w, K, whether begin had a shared expert,
+ *          and out as written by begin.
+ *   workspace: device memory of coli_moe_block_two_phase_workspace_bytes(E,
+ *   S, K, F, D, has_shared) bytes, 256-byte aligned, the same buffer for both
+ *   calls (begin leaves the late slots' routing in it) and not used by
+ *   anything else in between.  Both calls on one stream, or ordered.
+ * Returns COLI_OK, COLI_DECLINED (as coli_moe_block, NULL late) or
+ * COLI_HIP_ERROR.
+ */
+size_t coli_moe_block_two_phase_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shared);
+int coli_moe_block_begin(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                         const float *x, int S, const int32_t *ids, const float *w, int K,
+                         const int32_t *late, const coli_qtensor *sh_gate,
+                         const coli_qtensor *sh_up, const coli_qtensor *sh_down, float *out,
+                         void *workspace, size_t ws_bytes, void *stream);
+int coli_moe_block_end(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                       const float *x, int S, const float *w, int K, int has_shared, float *out,
+                       void *workspace, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Diagnostics (colibri PR #298, HIP single-source merge: a fault-injection */
 /* control proves GPU calls really executed; issue #585: fallbacks must be  */

@@ -123,6 +123,30 @@ def test_compute_entries_decline_before_device(lib):
     assert launch1 == launch0  # nothing was launched
 
 
+def test_two_phase_block_declines_before_device(lib):
+    """begin / end validate like coli_moe_block, need the late flags, and size
+    their workspace for both calls; nothing is launched on a decline."""
+    g, u, d = _moe_tensors()
+    _, _, launch0 = coli.coli_stats()
+    need = coli.coli_moe_block_two_phase_workspace_bytes(4, 2, 2, 64, 128, False)
+    assert need > coli.coli_moe_workspace_bytes(4, 2, 2, 64, 128, False)
+    assert coli.coli_moe_block_two_phase_workspace_bytes(0, 2, 2, 64, 128, False) == 0
+    ws = FAKE_Q // 256 * 256 + 256
+    b = coli.coli_moe_block_begin
+    assert b(g, u, d, FAKE_S, 2, FAKE_S, FAKE_S, 2, None, None, None, None, FAKE_S, ws, need, 0) == 0
+    assert "late" in coli.coli_last_reason()
+    assert b(g, u, d, FAKE_S, 2, FAKE_S, FAKE_S, 2, FAKE_S, None, None, None, FAKE_S, ws, need - 1,
+             0) == 0
+    assert b(g, u, d, FAKE_S, 2, FAKE_S, FAKE_S, 2, FAKE_S, None, None, None, FAKE_S, ws + 8, need,
+             0) == 0
+    e = coli.coli_moe_block_end
+    assert e(g, u, d, FAKE_S, 2, FAKE_S, 2, False, FAKE_S, None, need, 0) == 0
+    assert e(g, u, d, FAKE_S, 2, FAKE_S, 2, False, None, ws, need, 0) == 0
+    assert e(coli.coli_qtensor(), u, d, FAKE_S, 2, FAKE_S, 2, False, FAKE_S, ws, need, 0) == 0
+    _, _, launch1 = coli.coli_stats()
+    assert launch1 == launch0
+
+
 def test_qmatmul_group_declines_before_device(lib):
     """Every member is validated before anything is enqueued: bad counts,
     NULL arrays or members, S < 1, misaligned pointers and tensors never

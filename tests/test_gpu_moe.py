@@ -262,3 +262,80 @@ def _route_compare(orc, ids, E):
     assert np.array_equal(offsets.cpu().numpy(), o_ref)
     assert np.array_equal(perm.cpu().numpy()[:S * K], p_ref)
     assert int(bad.item()) == b_ref
+
+
+TWO_PHASE = [  # (fmt, S, K, E, D, F, gs, shared, late pattern)
+    (4, 1, 8, 16, 256, 128, 64, True, "half"),
+    (4, 1, 8, 16, 256, 128, 64, False, "all"),
+    (4, 3, 4, 9, 192, 96, 32, True, "half"),
+    (2, 2, 3, 7, 128, 96, 0, True, "none"),
+    (4, 40, 4, 12, 256, 128, 128, True, "half"),   # S > 4: the prefill kernels
+    (4, 24, 2, 6, 256, 128, 64, False, "all"),
+]
+
+
+def _late(pattern, S, K, seed):
+    if pattern == "none":
+        return np.zeros((S, K), np.int32)
+    if pattern == "all":
+        return np.ones((S, K), np.int32)
+    return (sd.rng(seed).random((S, K)) < 0.5).astype(np.int32)
+
+
+def _two_phase(G, U, Dn, sh, x, ids, w, late, pack=True):
+    S, K = ids.shape
+    E, F, D = G.n, G.O, G.I
+    tg, tu, td = qtensor(G, pack), qtensor(U, pack), qtensor(Dn, pack)
+    ts = [qtensor(m, pack) for m in sh] if sh is not None else [None, None, None]
+    xd, idd, wd = to_dev(x), to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32))
+    ld = to_dev(late.astype(np.int32))
+    wsb = coli.coli_moe_block_two_phase_workspace_bytes(E, S, K, F, D, sh is not None)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.full((S, D), float("nan"), device="cuda")
+    coli.check(coli.coli_moe_block_begin(tg, tu, td, xd, S, idd, wd, K, ld, ts[0], ts[1], ts[2], out,
+                                         ws, wsb), "coli_moe_block_begin")
+    coli.check(coli.coli_moe_block_end(tg, tu, td, xd, S, wd, K, sh is not None, out, ws, wsb),
+               "coli_moe_block_end")
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", TWO_PHASE,
+                         ids=["fmt{}-S{}-K{}-E{}-D{}-F{}-gs{}-sh{}-{}".format(*c) for c in TWO_PHASE])
+def test_moe_two_phase_matches_oracle(orc, case):
+    """Resident slots (and the shared expert) in begin, late slots in end: the
+    sum equals the whole block within its end-to-end bound; with no late slot
+    it equals coli_moe_block itself."""
+    need_gpu()
+    fmt, S, K, E, D, F, gs, shared, pattern = case
+    G, U, Dn, sh, x, ids, w = _moe_inputs(700 + S + K + E, fmt, S, K, E, D, F, gs, shared)
+    late = _late(pattern, S, K, seed=S * K)
+    out = _two_phase(G, U, Dn, sh, x, ids, w, late)
+    tau = TOL_FP32 if S <= coli.coli_gemv_max_rows() else TOL_BF16
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, None, tau)
+    if pattern == "none":
+        whole, _ = _run_gpu(G, U, Dn, sh, x, ids, w, hidden=False)
+        assert np.array_equal(out, whole)
+
+
+def test_moe_two_phase_repeatable_and_declines(orc):
+    need_gpu()
+    G, U, Dn, sh, x, ids, w = _moe_inputs(77, 4, 1, 8, 16, 256, 128, 64, True)
+    late = _late("half", 1, 8, seed=3)
+    a = _two_phase(G, U, Dn, sh, x, ids, w, late)
+    b = _two_phase(G, U, Dn, sh, x, ids, w, late)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    tg, tu, td = qtensor(G, True), qtensor(U, True), qtensor(Dn, True)
+    xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+    wsb = coli.coli_moe_block_two_phase_workspace_bytes(16, 1, 8, 128, 256, False)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.full((1, 256), 5.0, device="cuda")
+    assert coli.coli_moe_block_begin(tg, tu, td, xd, 1, idd, wd, 8, None, None, None, None, out,
+                                     ws, wsb) == coli.COLI_DECLINED
+    assert "late" in coli.coli_last_reason()
+    assert coli.coli_moe_block_begin(tg, tu, td, xd, 1, idd, wd, 8, idd, None, None, None, out,
+                                     ws, wsb - 256) == coli.COLI_DECLINED
+    assert coli.coli_moe_block_end(tg, tu, td, xd, 1, wd, 8, False, out, ws, wsb - 256) == \
+        coli.COLI_DECLINED
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)
