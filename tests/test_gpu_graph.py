@@ -162,3 +162,37 @@ def test_graph_grouped_gemv(S):
         coli.check(coli.coli_qmatmul(Tb, xbd, yb, S), "coli_qmatmul")
 
     _replays_match(run, ys, between=between)
+
+
+@pytest.mark.parametrize("S", [1, 40])
+def test_graph_two_phase_block(S):
+    """coli_moe_block_begin and coli_moe_block_end captured together and
+    replayed, with a one-submission block on other data between replays."""
+    need_gpu()
+    K, E, D, F = 4, 8, 256, 128
+    gs = 64 if S <= 4 else 128
+    G, U, Dn, sh, x, ids, w = _moe_inputs(90 + S, 4, S, K, E, D, F, gs, True)
+    tg, tu, td = qtensor(G, True), qtensor(U, True), qtensor(Dn, True)
+    ts = [qtensor(m, True) for m in sh]
+    xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+    late = to_dev((np.arange(S * K).reshape(S, K) % 3 == 1).astype(np.int32))
+    wsb = coli.coli_moe_block_two_phase_workspace_bytes(E, S, K, F, D, True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((S, D), device="cuda")
+    G2, U2, D2, sh2, x2, ids2, w2 = _moe_inputs(91 + S, 4, S, K, E, D, F, gs, False)
+    t2 = [qtensor(m, True) for m in (G2, U2, D2)]
+    x2d, ids2d, w2d = to_dev(x2), to_dev(ids2), to_dev(w2)
+    wsb2 = coli.coli_moe_workspace_bytes(E, S, K, F, D, 0)
+    ws2 = torch.empty(wsb2, dtype=torch.uint8, device="cuda")
+    out2 = torch.empty((S, D), device="cuda")
+
+    def run():
+        coli.check(coli.coli_moe_block_begin(tg, tu, td, xd, S, idd, wd, K, late, ts[0], ts[1], ts[2],
+                                             out, ws, wsb), "begin")
+        coli.check(coli.coli_moe_block_end(tg, tu, td, xd, S, wd, K, True, out, ws, wsb), "end")
+
+    def between():
+        coli.check(coli.coli_moe_block(t2[0], t2[1], t2[2], x2d, S, ids2d, w2d, K, None, None, None,
+                                       out2, ws2, wsb2), "coli_moe_block")
+
+    _replays_match(run, [out], between=between)
