@@ -905,7 +905,7 @@ bool mgemv_ok(const coli_qtensor *W) {
            W->pk_stride < ((int64_t)1 << 31);
 }
 
-// the int4 formats, which the MoE block, grouped GEMV and prefill kernels take
+// the int4 formats, which the MoE block and prefill kernels take
 bool mgemv_int4_ok(const coli_qtensor *W) {
     return mgemv_ok(W) && (W->fmt == 2 || W->fmt == 4);
 }
@@ -1029,7 +1029,7 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
     if (n < 1 || n > MG_MAXGRP || S < 1 || S > 4)
         return 0;
     for (int g = 0; g < n; ++g)
-        if (!mgemv_int4_ok(W[g]) || W[g]->n != 1 || W[g]->fmt != W[0]->fmt || cb_of(W[g]) != cb_of(W[0]))
+        if (!mgemv_ok(W[g]) || W[g]->n != 1 || W[g]->fmt != W[0]->fmt || cb_of(W[g]) != cb_of(W[0]))
             return 0;
     constexpr int TPW = COLI_MG_NW_GROUP / COLI_MG_KS_GROUP;
     MgArgs a = mg_args_for(W[0]);
@@ -1074,8 +1074,15 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
                                    COLI_MG_NBQ_DENSE>),                                            \
                           dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
                           ps.start(), ps.stop(), 0, a)
+#define MG_Q(NTV, QBV)                                                                             \
+    hipExtLaunchKernelGGL((k_mgemv<NTV, 1, false, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP,     \
+                                   COLI_MG_NBQ_DENSE, QBV>),                                       \
+                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
+                          ps.start(), ps.stop(), 0, a)
 #define MG_NT(NTV)                                   \
-    if (!grouped) { MG_R(NTV); }                     \
+    if (W[0]->fmt == 1) { MG_Q(NTV, 8); }            \
+    else if (W[0]->fmt == 3) { MG_Q(NTV, 2); }       \
+    else if (!grouped) { MG_R(NTV); }                \
     else if (cb == 1) { MG_G(NTV, 1); }              \
     else if (cb == 2) { MG_G(NTV, 2); }              \
     else { MG_G(NTV, 4); }
@@ -1086,6 +1093,7 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
     default: MG_NT(4); break;
     }
 #undef MG_NT
+#undef MG_Q
 #undef MG_R
 #undef MG_G
     if (!ok)

@@ -132,8 +132,8 @@ size_t coli_packed_bytes(int fmt, int n, int O, int I, int gs);
  * blocks, row) so a lane fetches a whole batch's scales at once (per-row
  * scales stay in the original s); rows and inputs past O and I are padded
  * with zero weights.  The represented weights are unchanged.  Only fmt 2 / 4
- * packed copies serve the MoE block, the grouped GEMV and the prefill
- * kernels; fmt 1 / 3 packed copies serve coli_qmatmul at S <= 4.
+ * packed copies serve the MoE block and the prefill kernels; fmt 1 / 3
+ * packed copies serve coli_qmatmul and coli_qmatmul_group at S <= 4.
  *   t         record from coli_tensor_upload (updated on success)
  *   packed    device buffer of at least coli_packed_bytes(...) bytes, 256-byte
  *             aligned, owned by the caller, kept alive while t is used

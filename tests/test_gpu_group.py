@@ -22,6 +22,8 @@ GROUPS = [
     [(4, 70, 1024, 128), (4, 300, 2560, 256), (4, 17, 6144, 128)],
     [(4, 40, 96, 32), (4, 9, 4096, 32)],
     [(2, 41, 2080, 0), (2, 9, 64, 0), (2, 500, 1536, 0)],
+    [(1, 37, 1056, 0), (1, 300, 640, 0), (1, 16, 8320, 0)],
+    [(3, 37, 1056, 0), (3, 300, 640, 0), (3, 16, 8320, 0)],
 ]
 
 
