@@ -208,7 +208,10 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS if achieved else None,
                 "traffic": traffic_from_profiles(dom),
-                "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": dom_us}
+                "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": dom_us,
+                # the whole block (both launches and the gap between them), for
+                # reading beside the dominant kernel's fraction
+                "block_GBps": value, "block_frac": value / HBM_PEAK_GBS}
 
     # ---- side measurements --------------------------------------------------
     extra = {"block_us": ms * 1e3, "kernels": kern, "wall_s_timed": wall}
@@ -553,9 +556,32 @@ def ceiling_probes(coli, torch, log):
     mfma_tf = wg * it * coli.PROBE_MFMA_FLOPS_PER_WG_ITER / t / 1e12
     log(f"ceilings: streaming read {read_gbs:.0f} GB/s ({100 * read_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), "
         f"bf16 MFMA loop {mfma_tf:.0f} TFLOP/s ({100 * mfma_tf / BF16_PEAK_TFLOPS:.1f}% of 2.5 PFLOP/s)")
+    # launch floor: an empty kernel back to back on the stream, and the same
+    # launches replayed from a HIP graph (256 and 1024 workgroups)
+    floor = {}
+    for wg in (256, 1024):
+        n = 2000
+        t = timed(lambda: coli.check(coli.coli_probe_launch(wg, sink, st), "probe_launch"), n)
+        floor[f"eager_{wg}wg_us"] = t * 1e6
+        g = torch.cuda.CUDAGraph()
+        gs_ = torch.cuda.Stream()
+        with torch.cuda.stream(gs_):
+            for _ in range(3):
+                coli.check(coli.coli_probe_launch(wg, sink, gs_), "probe_launch")
+            gs_.synchronize()
+            g.capture_begin()
+            for _ in range(100):
+                coli.check(coli.coli_probe_launch(wg, sink, gs_), "probe_launch")
+            g.capture_end()
+        torch.cuda.synchronize()
+        tg = timed(lambda: g.replay(), 20)
+        floor[f"graph_{wg}wg_us"] = tg * 1e6 / 100
+        del g
+    log(f"launch floor (empty kernel): {floor}")
     return {"measured_ceilings": {"stream_read_GBps": read_gbs, "mfma_bf16_TFLOPs": mfma_tf,
                                   "stream_read_frac_spec": read_gbs / HBM_PEAK_GBS,
-                                  "mfma_bf16_frac_spec": mfma_tf / BF16_PEAK_TFLOPS}}
+                                  "mfma_bf16_frac_spec": mfma_tf / BF16_PEAK_TFLOPS,
+                                  "launch_floor_us": floor}}
 
 
 def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):
@@ -685,6 +711,7 @@ def cpu_baseline(coli, sd, np, torch, gq, gsc, uq, usc, dq, dsc, x, routes, bloc
     gbs = done * block_bytes / spent / 1e9
     log(f"cpu oracle: {done} blocks in {spent:.1f} s -> {gbs:.3f} GB/s ({min(nthreads, K)} threads)")
     return {"value": gbs, "unit": "GB/s", "cores": min(nthreads, K), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{done} decode MoE blocks (S=1, 8 routed experts, full shapes), "
                       f"{spent:.1f} s of oracle time; OpenMP over the 8 routed pairs",
             "us_per_block": spent / done * 1e6}
@@ -741,13 +768,24 @@ def oracle_timings(sd, np, log):
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name plus family /
+    model / stepping (a virtual machine may shorten the name), and how many
+    logical CPUs this process may use."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (t.strip() for t in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    fam = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    mhz = info.get("cpu MHz")
+    extra = f"; {fam}" if fam else ""
+    extra += f"; {mhz} MHz" if mhz else ""
+    return (f"{name}{extra}; {len(os.sched_getaffinity(0))} logical CPUs usable of "
+            f"{os.cpu_count()}")
 
 
 if __name__ == "__main__":

@@ -83,6 +83,7 @@ def _load():
                                  C.c_float, QP, QP, QP, vp, vp, sz, vp]),
         "coli_probe_read": (i32, [vp, sz, vp, vp]),
         "coli_probe_mfma": (i32, [i32, i32, vp, vp]),
+        "coli_probe_launch": (i32, [i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -102,7 +103,7 @@ def exported_symbols():
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
             "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
-            "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma",
+            "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma", "coli_probe_launch",
             "coli_moe_router_workspace_bytes", "coli_moe_router", "coli_rmsnorm",
             "coli_moe_layer_workspace_bytes", "coli_moe_layer"]
 
@@ -278,6 +279,11 @@ def coli_probe_read(buf, sink, stream=None) -> int:
 def coli_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> int:
     """workgroups x 4 wavefronts x 8 x iters bf16 32x32x16 products."""
     return _load().coli_probe_mfma(int(workgroups), int(iters), _ptr(sink), _stream(stream))
+
+
+def coli_probe_launch(workgroups: int, sink, stream=None) -> int:
+    """One launch of an empty kernel (the launch floor)."""
+    return _load().coli_probe_launch(int(workgroups), _ptr(sink), _stream(stream))
 
 
 PROBE_MFMA_FLOPS_PER_WG_ITER = 4 * 8 * 2 * 32 * 32 * 16

@@ -1,6 +1,6 @@
 // abi.hip -- the extern "C" entry points of libcoli: validation, dispatch,
 // diagnostics.  Conventions (colibri PR #298, commit making the CUDA ABI return
-// 0 for fmt=4: "a fallback, never a wrong answer"; issue #585 thread: silent
+// 0 for fmt=4: a declined call is a fallback, not a wrong result; issue #585 thread: silent
 // fallbacks mislead, so every refusal names its reason; colibri PR #298, HIP
 // single-source merge: a fault-injection control proves GPU calls executed):
 //   * every entry validates everything it can see on the host before enqueuing

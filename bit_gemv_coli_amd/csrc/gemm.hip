@@ -3,8 +3,8 @@
 //
 // What is computed (colibri PR #298, CUDA fmt=4 commit: the group scale is
 // applied to each group's partial sum during accumulation; colibri-strix
-// commit log, "route large row-batch matmul_qt GEMMs to the GPU": large row
-// batches take a GEMM path; "metal: batched moe_block": per-row ragged
+// commit log, prefill GEMM routing commit: large row
+// batches take a GEMM path; batched expert-block commit: per-row ragged
 // routing, gate/up -> SiLU -> down, weighted scatter-add):
 //     Y[m][n] = sum_g scale(n, g) * sum_{k in g} v(n, k) * X[m][k]
 //

@@ -522,7 +522,7 @@ int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStrea
 // Decode MoE block (S <= 4)
 //
 // colibri-strix "batched moe_block": per expert gate/up -> SiLU -> down, then
-// the weighted scatter-add; "fuse shared expert": the shared expert is one
+// the weighted scatter-add; shared-expert fusion commit: the shared expert is one
 // more expert with weight 1 on every row.  Here, per routed pair p = s*K+k
 // (then one pair per token for the shared expert):
 //   launch 1  h[p]  = silu(G_e x_s) * (U_e x_s)   gate row j and up row j in

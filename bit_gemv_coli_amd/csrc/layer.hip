@@ -1,6 +1,5 @@
 // layer.hip -- the steps of a decode layer around the expert block
-// (colibri-strix commit log, "metal: full decode layer in ONE command
-// buffer": the post-attention RMSNorm in front of the shared expert, router
+// (colibri-strix commit log, full decode layer commit: the post-attention RMSNorm in front of the shared expert, router
 // and experts, and the residual add after them).
 //   k_rmsnorm       one workgroup per row: f64 sum of squares (each thread a
 //                   strided share, wavefront sums, then the four wavefronts in

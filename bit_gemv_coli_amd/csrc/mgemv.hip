@@ -23,7 +23,13 @@
 //            int8 A operand.
 //   sums     exact in int32 per 128-input block (|sum| < 2^22); the group
 //            scale, 2^-e, the digit weight and 1/16 are applied in fp32.
-// The error stays far inside 1e-5 * sum |w||x|.
+// Accuracy: the represented input is within 2^-e <= 2^-29 max|x| of its
+// block (2^-126 for blocks below 2^-96), so an output moves by at most
+// 2^-29 * sum_b max_b|x| * sum_{i in b} |w_i| on top of the fp32 rounding
+// (1e-5 * sum |w||x|).  For activations of similar magnitude that term is
+// ~1e-8 of sum |w||x|; one input far above the rest of its block where the
+// weights are zero makes it dominate (the vector-ALU kernels have no such
+// term).
 //
 // Layout of one matrix-core step (16 weight rows x 128 inputs):
 //   lane l: weight row n = l % 16, input quarter j = l / 16; it loads the 16
@@ -123,6 +129,24 @@ struct MgArgs {
 // device-scope relaxed atomics: those go to the point of coherence shared by
 // all XCDs (their L2s are not coherent with each other for plain accesses), so
 // no cache-wide write-back or invalidate is needed.
+//
+// What orders them (the combine tail below): the HIP memory model gives a
+// relaxed atomic no ordering against another, so the order rests on the gfx9
+// (CDNA4) ISA, not on the source-level model:
+//   * agent-scope relaxed atomic loads and stores are emitted as global
+//     loads / stores with the sc1 bit, which the L2 of each XCD serves
+//     write-through / miss-always, i.e. at the memory-side coherence point;
+//   * on gfx9 the vector memory counter (vmcnt) counts stores as well as
+//     loads, and a store leaves it only once the memory side has acknowledged
+//     it, so `s_waitcnt vmcnt(0)` (inside s_waitcnt(0)) returns after this
+//     wave's partial rows are at the coherence point;
+//   * the counter add is issued after that wait and the workgroup barrier,
+//     and the last workgroup issues its sc1 loads only after the add has
+//     returned -- so they observe every partial row counted before it.
+// A release/acquire pair would say the same thing in the source model, but
+// agent-scope release on gfx950 writes back the whole L2 of the XCD
+// (measured: about five times this kernel's time); the tests check the
+// combined rows against the oracle and their bit-repeatability.
 __device__ __forceinline__ void store_coherent(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -5,8 +5,7 @@
 //   k_sg  weight streaming for packed experts in the MoE block (further down).
 //
 // What is computed (colibri PR #298, CUDA fmt=4 commit: w = scale(n, k/gs) *
-// (q - 8), the group scale applied inline; colibri-strix "route large
-// row-batch matmul_qt GEMMs to the GPU": large row batches take a GEMM path).
+// (q - 8), the group scale applied inline; colibri-strix prefill GEMM routing commit: large row batches take a GEMM path).
 //
 // Precision (the bf16 envelope): every weight is dequantized once per
 // workgroup to bf16(s * (q - 8)) -- one rounding of the exact product -- and

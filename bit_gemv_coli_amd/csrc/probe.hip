@@ -1,8 +1,9 @@
-// probe.hip -- two diagnostic kernels that measure this GPU's own ceilings,
+// probe.hip -- diagnostic kernels that measure this GPU's own ceilings,
 // so that measured throughput can be stated against both the data-sheet
 // peaks and what a trivial kernel reaches on the same part: a streaming read
 // of a device buffer (HBM) and a loop of independent bf16 matrix-core
-// products (v_mfma_f32_32x32x16_bf16).  Neither is part of the matmul path.
+// products (v_mfma_f32_32x32x16_bf16), and an empty kernel for the launch
+// floor.  None is part of the matmul path.
 #include "common.h"
 
 namespace coli {
@@ -59,6 +60,13 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float never, floa
         sink[0] = s;
 }
 
+// a kernel that does nothing: the launch floor of this GPU and runtime
+// (back-to-back launches on one stream, or replayed from a graph)
+__global__ __launch_bounds__(256) void k_probe_empty(float never, float *sink) {
+    if (threadIdx.x == 1024)  // never: blocks have 256 threads
+        sink[0] = never;
+}
+
 }  // namespace coli
 
 using namespace coli;
@@ -78,4 +86,12 @@ extern "C" int coli_probe_mfma(int workgroups, int iters, float *sink, void *str
     hipLaunchKernelGGL(k_probe_mfma, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream,
                        iters, -1.2345e30f, sink);
     return after_launch("probe_mfma");
+}
+
+extern "C" int coli_probe_launch(int workgroups, float *sink, void *stream) {
+    if (!sink || workgroups < 1)
+        return decline("probe_launch: need workgroups >= 1 and a sink");
+    hipLaunchKernelGGL(k_probe_empty, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream,
+                       -1.2345e30f, sink);
+    return after_launch("probe_launch");
 }

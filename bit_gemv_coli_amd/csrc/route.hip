@@ -1,5 +1,5 @@
 // route.hip -- the MoE routing table on the GPU (colibri-strix commit log,
-// "metal: batched moe_block": per-row ragged expert routing; the CPU then did
+// batched expert-block commit: per-row ragged expert routing; the CPU then did
 // the weighted scatter-add -- here the table drives gathers and a
 // deterministic combine instead).
 //

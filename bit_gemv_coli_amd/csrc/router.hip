@@ -1,6 +1,5 @@
 // router.hip -- the MoE router and its exact top-K selection on the GPU
-// (colibri-strix commit log, "metal: full decode layer in ONE command
-// buffer": router matvec + sigmoid, then greedy argmax over sigmoid + bias
+// (colibri-strix commit log, full decode layer commit: router matvec + sigmoid, then greedy argmax over sigmoid + bias
 // with the CPU's tie order, top-p truncation, norm_topk, routed_scale).
 //
 // Decisions are taken on f64 numbers: every logit is a sum of exact f64

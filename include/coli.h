@@ -14,13 +14,12 @@
  *   colibri PR #298, commit adding fmt=4 to the Metal mm_gemv -- fmt 1-3 scale
  *       once per row after the dot product; fmt 4 per group.
  *   colibri PR #298, commit making the CUDA ABI return 0 for fmt=4 -- an entry
- *       that cannot honour its input returns 0: a fallback, never a wrong answer.
- *   colibri-strix commit log, "metal: batched moe_block + zero-copy slab
- *       registry" -- gate/up -> SiLU -> down for a whole expert block in one
+ *       that cannot honour its input returns 0: a declined call is a fallback, not a wrong result.
+ *   colibri-strix commit log, batched expert-block commit -- gate/up -> SiLU -> down for a whole expert block in one
  *       submission, ragged per-row routing, weighted scatter-add.
- *   colibri-strix commit log, "fuse shared expert into GPU block" -- the shared
+ *   colibri-strix commit log, shared-expert fusion commit -- the shared
  *       expert joins the block as an extra expert with weight 1.0 on every row.
- *   colibri-strix commit log, "route large row-batch matmul_qt GEMMs to the GPU"
+ *   colibri-strix commit log, prefill GEMM routing commit
  *       -- large row batches (prefill) take a GEMM path, small ones a GEMV.
  *
  * Conventions shared by every entry point
@@ -147,22 +146,34 @@ int coli_tensor_pack(coli_qtensor *t, void *packed, size_t bytes, void *stream);
 /*
  * coli_qmatmul -- y = W x for every matrix of the stack
  * (colibri PR #298 commits: fmt 4 folds the group scale in per group, fmt 1-3
- * scale once per row; colibri-strix "route large row-batch matmul_qt GEMMs to
- * the GPU": large row batches take the GEMM path).
+ * scale once per row; colibri-strix prefill GEMM routing commit: large row batches take the GEMM path).
  *   W   tensor from coli_tensor_upload (n matrices [O][I])
  *   x   device f32 [S][I]          y   device f32 [n][S][O]
  *   S   >= 1 input rows.  S <= coli_gemv_max_rows() (default 4) runs the
- *       fp32 GEMV kernels (error <= 1e-5 * sum_i |w||x| per output); larger S
- *       runs the bf16 matrix-core GEMM (weights and x rounded to bf16, fp32
- *       accumulation; error <= 4e-3 * sum_i |w||x|).
+ *       fp32 GEMV kernels; larger S runs the bf16 matrix-core GEMM (weights
+ *       and x rounded to bf16, fp32 accumulation; error <= 4e-3 * A per
+ *       output, A = sum_i |w_i||x_i|).
+ *       Decode error (S <= 4), per output:
+ *         vector-ALU kernels (no packed copy, or coli_set_decode_kernel(1)):
+ *           <= 1e-5 * A -- they multiply the f32 inputs themselves;
+ *         matrix-core kernels (tensors with a packed copy):
+ *           <= 1e-5 * A + 2^-29 * Ahat,
+ *           Ahat = sum over the 128-input blocks b of the row of
+ *                  max(max_{i in b} |x_i|, 2^-97) * sum_{i in b} |w_i|.
+ *         The matrix-core kernels hold each (input row, 128-input block) as
+ *         integers under one power of two, so an input's resolution is
+ *         2^-29 of its block's largest |x|.  For activations like the
+ *         workloads' N(0,1) inputs Ahat is a few times A and the term is
+ *         ~1e-8 A; an input ~1e6 times larger than the rest of its block at
+ *         a column whose weights are zero makes it exceed 1e-5 A.  Callers
+ *         whose inputs have such outliers take the vector-ALU kernels.
  * x and y must not overlap.  Returns COLI_OK / COLI_DECLINED / COLI_HIP_ERROR.
  */
 int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *stream);
 
 /*
  * coli_qmatmul_group -- y[g] = W[g] x[g] for n independent matrices in one
- * submission (colibri-strix commit log, "metal: full decode layer in ONE
- * command buffer": the projections of a layer go to the GPU together, not one
+ * submission (colibri-strix commit log, full decode layer commit: the projections of a layer go to the GPU together, not one
  * dispatch each).  Each member is computed exactly as coli_qmatmul computes it
  * (same kernels, same bounds, bit-identical results); members need not share
  * shapes.
@@ -189,7 +200,9 @@ int coli_set_gemv_max_rows(int s);
 
 /* Kernel family of the fp32 decode path: 0 (default) uses the matrix-core
  * decode kernels for tensors that carry a packed copy (coli_tensor_pack) and
- * the vector-ALU kernels elsewhere; 1 uses the vector-ALU kernels everywhere.  Both meet the same 1e-5 * sum |w||x| bound.
+ * the vector-ALU kernels elsewhere; 1 uses the vector-ALU kernels everywhere
+ * (error <= 1e-5 * A whatever the inputs' spread; the matrix-core kernels add
+ * up to 2^-29 * Ahat, see coli_qmatmul).
  * Environment: COLI_DECODE_KERNEL=valu.  Returns the previous mode, -1 if
  * `mode` is refused. */
 int coli_set_decode_kernel(int mode);
@@ -219,7 +232,7 @@ int coli_moe_route(const int32_t *ids, int S, int K, int E, int32_t *counts,
 /*
  * coli_moe_block -- the batched MoE expert block in one submission
  * (colibri-strix "batched moe_block": gate/up -> SiLU -> down per expert, then
- * the weighted combine; "fuse shared expert": the shared expert adds with
+ * the weighted combine; shared-expert fusion commit: the shared expert adds with
  * weight 1.0 on every row):
  *   out[s] = sum_k w[s][k] * D_e (silu(G_e x_s) * (U_e x_s)),  e = ids[s][k]
  *            + D_sh (silu(G_sh x_s) * (U_sh x_s))            (if given)
@@ -235,7 +248,9 @@ int coli_moe_route(const int32_t *ids, int S, int K, int E, int32_t *counts,
  * outside [0,E) contribute nothing (their count is reported by
  * coli_moe_route); duplicate ids in a row are independent terms.  The combine
  * adds k in ascending order with no atomics, so reruns are bit-identical.
- * S <= coli_gemv_max_rows() runs fp32 GEMV kernels; larger S runs bf16
+ * S <= coli_gemv_max_rows() runs fp32 GEMV kernels (packed stacks: the
+ * matrix-core kernels, each GEMV within the coli_qmatmul bound, with x as the
+ * input of gate/up and h as the input of down); larger S runs bf16
  * matrix-core grouped GEMMs over the routing table.
  * Limits: 1 <= E <= 4096, 1 <= K <= 64, S >= 1.
  */
@@ -262,8 +277,7 @@ size_t coli_moe_workspace_bytes(int E, int S, int K, int F, int Dm, int has_shar
 
 /*
  * coli_moe_block_begin / coli_moe_block_end -- the expert block in two
- * submissions (colibri-strix commit log, "metal: overlap disk loads with GPU
- * compute inside the layer": the resident experts and the shared expert go
+ * submissions (colibri-strix commit log, disk/GPU overlap commit: the resident experts and the shared expert go
  * to the GPU first, the experts still being loaded follow in a second submit
  * once they are in place).  Here a slot (s, k) is late when late[s][k] != 0:
  * begin computes out = the block over the resident slots (+ the shared
@@ -300,8 +314,7 @@ int coli_moe_block_end(const coli_qtensor *gate, const coli_qtensor *up, const c
 
 /*
  * coli_moe_router -- the router in front of the expert block and its exact
- * top-K selection (colibri-strix commit log, "metal: full decode layer in ONE
- * command buffer": router matvec + sigmoid, greedy argmax over sigmoid + bias
+ * top-K selection (colibri-strix commit log, full decode layer commit: router matvec + sigmoid, greedy argmax over sigmoid + bias
  * with the CPU's tie order, top-p truncation, norm_topk, routed_scale).
  *   x    f32 [S][D] input rows;  R  f32 [E][D] router weights (row-major);
  *   bias f32 [E] added to the sigmoid score for the choice only (NULL: none);
@@ -324,8 +337,7 @@ int coli_moe_router(const float *x, int S, int D, const float *R, const float *b
                     void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * coli_rmsnorm -- per-row RMSNorm (colibri-strix commit log, "metal: full
- * decode layer in ONE command buffer": the post-attention norm in front of
+ * coli_rmsnorm -- per-row RMSNorm (colibri-strix commit log, full decode layer commit: the post-attention norm in front of
  * the shared expert and the router; the pages name the step only, the usual
  * root-mean-square norm with a per-feature weight is taken):
  *   y[s][d] = x[s][d] / sqrt(mean_d x[s][d]^2 + eps) * w[d]
@@ -339,8 +351,7 @@ int coli_rmsnorm(const float *x, int S, int D, const float *w, float eps, float 
 
 /*
  * coli_moe_layer -- the expert half of a decode layer in one submission
- * (colibri-strix commit log, "metal: full decode layer in ONE command
- * buffer": post-attention norm, shared expert, router with the exact top-K,
+ * (colibri-strix commit log, full decode layer commit: post-attention norm, shared expert, router with the exact top-K,
  * routed experts, then the residual add), for S >= 1 rows:
  *   xn      = coli_rmsnorm(h, ln_w, eps)                   (kept in workspace)
  *   ids, w  = coli_moe_router(xn, R, bias, K, topp, norm_topk, routed_scale)
@@ -398,6 +409,10 @@ const char *coli_prof_tag(int i);
  * COLI_HIP_ERROR. */
 int coli_probe_read(const void *buf, size_t bytes, float *sink, void *stream);
 int coli_probe_mfma(int workgroups, int iters, float *sink, void *stream);
+/* coli_probe_launch: one launch of an empty kernel of `workgroups` x 256
+ * threads -- the launch floor (back to back on a stream, or from a graph).
+ * `sink` as above.  Returns COLI_OK, COLI_DECLINED or COLI_HIP_ERROR. */
+int coli_probe_launch(int workgroups, float *sink, void *stream);
 
 /* Library version string. */
 const char *coli_version(void);

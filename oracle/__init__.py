@@ -212,8 +212,7 @@ class Oracle:
     def moe_layer(self, h: np.ndarray, ln_w, eps: float, R: np.ndarray, bias, K: int,
                   topp: float, norm_topk: bool, routed_scale: float, gate: QMat, up: QMat,
                   down: QMat, shared=None):
-        """The expert half of a decode layer (colibri-strix commit log, "metal:
-        full decode layer in ONE command buffer"): xn = RMSNorm(h), stored as
+        """The expert half of a decode layer (colibri-strix commit log, full decode layer commit): xn = RMSNorm(h), stored as
         f32; router and exact top-K on xn; the expert block on xn with the
         routed weights as f32; out = h + block.  Each step is one of the
         functions above, called in that order.  Returns out [S][D] f64 and a

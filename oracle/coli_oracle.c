@@ -23,14 +23,11 @@
  *   [P4-addrow] colibri PR #298, commit making qt_addrow/qt_matvec_rows refuse
  *               unknown formats: fmt=1 raw bytes, fmt=3 row stride (I+3)/4,
  *               one scale per row for fmt 1/2/3.
- *   [P3-moe]    colibri-strix commit log, commit "metal: batched moe_block +
- *               zero-copy slab registry": gate/up -> SiLU -> down per expert,
+ *   [P3-moe]    colibri-strix commit log, batched expert-block commit: gate/up -> SiLU -> down per expert,
  *               per-row ragged routing, weighted scatter-add of the results.
- *   [P3-shared] colibri-strix commit log, commit "zero-copy attention weights +
- *               fuse shared expert into GPU block": the shared expert is an
+ *   [P3-shared] colibri-strix commit log, shared-expert fusion commit: the shared expert is an
  *               extra expert with routing weight 1.0 over every row.
- *   [P3-layer]  colibri-strix commit log, commit "metal: full decode layer in
- *               ONE command buffer": the router is a matvec followed by a
+ *   [P3-layer]  colibri-strix commit log, full decode layer commit: the router is a matvec followed by a
  *               sigmoid, then an exact top-K phase: greedy argmax over the
  *               sigmoid score plus a per-expert bias with the CPU's tie order,
  *               top-p truncation, norm_topk and routed_scale.
@@ -471,8 +468,7 @@ void oracle_moe_router(const float *x, int64_t S, int64_t D, const float *R,
 
 /* ------------------------------------------------------------------ */
 
-/* RMSNorm of each row (colibri-strix commit log, "metal: full decode layer
- * in ONE command buffer": the post-attention norm in front of the expert
+/* RMSNorm of each row (colibri-strix commit log, full decode layer commit: the post-attention norm in front of the expert
  * half of the layer).  The pages name the step only; the reading taken is
  * the usual root-mean-square norm with a per-feature weight:
  *   ms      = (sum_d x[s][d]^2) / D          (f64, sequential sum)

@@ -62,17 +62,41 @@ def gpu_qmatmul(T: coli.QTensor, x: np.ndarray, n: int = 1) -> np.ndarray:
     return y.cpu().numpy()
 
 
-def assert_within(y_gpu, y_ref, A, tol, what=""):
+def assert_within(y_gpu, y_ref, A, tol, what="", extra=None):
+    """|y_gpu - y_ref| <= tol * A (+ extra, an absolute allowance per output,
+    e.g. the matrix-core decode kernels' 2^-29 * Ahat input-resolution term)."""
     y_gpu = np.asarray(y_gpu, dtype=np.float64)
     err = np.abs(y_gpu - y_ref)
-    bound = tol * A
+    bound = tol * A if extra is None else tol * A + extra
     bad = ~(err <= bound)  # NaN counts as bad
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        ratio = np.nanmax(err / np.maximum(A, 1e-300))
-        raise AssertionError(f"{what}: {int(bad.sum())} outputs outside {tol:g}*A; "
-                             f"max err/A = {ratio:.3e}; first bad {idx.tolist()}")
+        ratio = np.nanmax(err / np.maximum(bound, 1e-300))
+        raise AssertionError(f"{what}: {int(bad.sum())} outputs outside {tol:g}*A"
+                             f"{'' if extra is None else ' + extra'}; "
+                             f"max err/bound = {ratio:.3e}; first bad {idx.tolist()}")
     return float(np.max(err / np.maximum(A, 1e-300))) if err.size else 0.0
+
+
+def rep_allowance(orc, W: QMat, x) -> np.ndarray:
+    """2^-29 * Ahat per output: how far the matrix-core decode kernels' input
+    representation (one power of two per input row and 128-input block) may
+    move each output of W x."""
+    from digit_model import REP_BOUND, block_magnitude
+    return REP_BOUND * block_magnitude(np.abs(orc.dequant_f64(W)), x)
+
+
+def zero_column(q: np.ndarray, fmt: int, col: int) -> None:
+    """Set the codes of input column `col` to the format's zero in every row
+    (q: uint8 [O][row_bytes], modified in place)."""
+    if fmt in (2, 4):
+        b = col // 2
+        q[:, b] = (q[:, b] & 0x0F) | 0x80 if col % 2 else (q[:, b] & 0xF0) | 0x08
+    elif fmt == 3:
+        b, sh = col // 4, 2 * (col % 4)
+        q[:, b] = (q[:, b] & np.uint8(~(3 << sh) & 0xFF)) | np.uint8(2 << sh)
+    else:
+        q[:, col] = 0
 
 
 def make_case(fmt, O, I, gs, S, seed, n=None):

@@ -385,8 +385,7 @@ def pin_moe_intermediates(orc):
 
 
 # ---------------------------------------------------------------------------
-# Router and exact top-K (colibri-strix commit log, "metal: full decode layer
-# in ONE command buffer": router matvec + sigmoid, greedy argmax over sigmoid
+# Router and exact top-K (colibri-strix commit log, full decode layer commit: router matvec + sigmoid, greedy argmax over sigmoid
 # + bias with the CPU's tie order, top-p truncation, norm_topk, routed_scale)
 # ---------------------------------------------------------------------------
 

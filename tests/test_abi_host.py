@@ -1,7 +1,7 @@
 """Host-side checks of the C ABI (no GPU): the library loads, exports every
 symbol include/coli.h declares, and its validation declines bad input before
 touching the device (colibri PR #298: an entry that cannot honour its input
-returns 0 -- a fallback, never a wrong answer)."""
+returns 0 -- a declined call is a fallback, not a wrong result)."""
 import ctypes as C
 import os
 import re

@@ -12,7 +12,7 @@ import torch
 import bit_gemv_coli_amd as coli
 import synthdata as sd
 from gpu_util import (TOL_BF16, TOL_FP32, assert_within, decode_kernels, gpu_qmatmul, make_case,
-                      need_gpu, qtensor, to_dev)
+                      need_gpu, qtensor, rep_allowance, to_dev, zero_column)
 from oracle import QMat
 
 pytestmark = pytest.mark.gpu
@@ -129,13 +129,49 @@ def test_qmatmul_one_hot_columns_exact(orc, S, kmode):
         assert np.array_equal(y[t], w[:, c]), (S, c)
 
 
-def test_qmatmul_config1_full(orc):
-    """Single fmt-4 GEMV: O=1024, I=2048, gs=64, S=1, seed 0."""
+@KERNELS
+def test_qmatmul_config1_full(orc, kmode):
+    """Single fmt-4 GEMV: O=1024, I=2048, gs=64, S=1, seed 0, on the packed
+    matrix-core path (the one the benchmark times) and the vector-ALU path."""
     need_gpu()
     W, x = make_case(4, 1024, 2048, 64, 1, seed=0)
-    y = gpu_qmatmul(qtensor(W), x)[0]
+    with decode_kernels(kmode):
+        y = gpu_qmatmul(qtensor(W, pack=(kmode == 0)), x)[0]
     y_ref, A = orc.qmatmul(W, x)
     assert_within(y, y_ref, A, TOL_FP32, "config 1")
+
+
+ZW = [(4, 64), (4, 128), (2, 0), (1, 0), (3, 0)]
+
+
+@KERNELS
+@pytest.mark.parametrize("fmt,gs", ZW, ids=[f"fmt{f}-gs{g}" for f, g in ZW])
+def test_qmatmul_zero_weight_outliers(orc, fmt, gs, kmode):
+    """Huge inputs at columns whose weights are zero in every row, among
+    N(0,1) inputs (S = 1..4, 1e7 .. 1e30).  The matrix-core kernels give every
+    (input row, 128-input block) one power of two, so such a block loses
+    resolution: they must stay within 1e-5 A + 2^-29 Ahat.  The vector-ALU
+    kernels multiply the floats themselves and hold the plain 1e-5 A."""
+    need_gpu()
+    O, I = 272, 2176
+    r = sd.rng(300 + fmt + gs)
+    q, s = sd.gen_matrix(r, fmt, O, I, gs)
+    cols = (5, 700, 2100)
+    for c in cols:
+        zero_column(q, fmt, c)
+    W = QMat(fmt, O, I, gs if fmt == 4 else 0, q, s)
+    assert np.all(orc.dequant_f64(W)[:, list(cols)] == 0.0)
+    T = qtensor(W, pack=(kmode == 0))
+    for S in (1, 2, 3, 4):
+        for mag in (1e7, 1e12, 1e30):
+            x = sd.gen_x(r, S, I)
+            for t in range(S):
+                x[t, cols[t % 3]] = mag if t % 2 == 0 else -mag
+            with decode_kernels(kmode):
+                y = gpu_qmatmul(T, x)[0]
+            y_ref, A = orc.qmatmul(W, x)
+            extra = rep_allowance(orc, W, x) if kmode == 0 else None
+            assert_within(y, y_ref, A, TOL_FP32, f"fmt {fmt} S {S} outlier {mag:g}", extra)
 
 
 SWEEP = [(1, 0), (2, 0), (3, 0), (4, 64), (4, 128)]

@@ -1,5 +1,5 @@
 """The expert block and the matmul inside a captured HIP graph (the pages'
-"full decode layer in ONE command buffer": a block is one submission).  Each
+full decode layer commit: a block is one submission).  Each
 graph is replayed several times with eager library work and host
 synchronisations between the replays, and every replay must reproduce the
 eager result bit for bit (the kernels are deterministic; nothing in the

@@ -1,5 +1,5 @@
 """GPU parity of the steps around the expert block (colibri-strix commit
-log, "metal: full decode layer in ONE command buffer": post-attention
+log, full decode layer commit: post-attention
 RMSNorm, router with the exact top-K, shared + routed experts, residual add)
 against the oracle.
 

@@ -1,6 +1,6 @@
 """GPU parity of the MoE routing table (bit-exact) and the expert block
-(colibri-strix commit log, "metal: batched moe_block": gate/up -> SiLU ->
-down per routed expert, weighted combine; "fuse shared expert": the shared
+(colibri-strix commit log, batched expert-block commit: gate/up -> SiLU ->
+down per routed expert, weighted combine; shared-expert fusion commit: the shared
 expert adds with weight 1.0 on every row) against the oracle.
 
 Checks per case:
@@ -16,7 +16,9 @@ import torch
 
 import bit_gemv_coli_amd as coli
 import synthdata as sd
-from gpu_util import TOL_BF16, TOL_FP32, assert_within, decode_kernels, need_gpu, qtensor, to_dev
+from digit_model import REP_BOUND, block_magnitude
+from gpu_util import (TOL_BF16, TOL_FP32, assert_within, decode_kernels, need_gpu, qtensor, to_dev,
+                      zero_column)
 from oracle import QMat
 
 pytestmark = pytest.mark.gpu
@@ -65,7 +67,9 @@ def _run_gpu(G, U, Dn, sh, x, ids, w, hidden=True, pack=True):
     return out.cpu().numpy(), h
 
 
-def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None):
+def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None, rep=False):
+    """rep=True adds the matrix-core decode kernels' input-resolution term
+    2^-29 * Ahat to each stage's bound (gate/up on x, down on the GPU's h)."""
     S, K = ids.shape
     E = G.n
     D = Dn.O
@@ -78,6 +82,21 @@ def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None):
     P = S * K + (S if sh is not None else 0)
     valid = np.ones(P, bool)
     valid[:S * K] = (ids.reshape(-1) >= 0) & (ids.reshape(-1) < E)
+
+    def pair(p):
+        if p < S * K:
+            e = int(ids.flat[p])
+            return p // K, float(w.flat[p]), G.expert(e), U.expert(e), Dn.expert(e)
+        return p - S * K, 1.0, sh[0], sh[1], sh[2]
+
+    if rep:
+        for p in range(P):
+            if valid[p]:
+                s_, _, Gm, Um, _ = pair(p)
+                xs = x[s_:s_ + 1]
+                rg = REP_BOUND * block_magnitude(np.abs(orc.dequant_f64(Gm)), xs)[0]
+                ru = REP_BOUND * block_magnitude(np.abs(orc.dequant_f64(Um)), xs)[0]
+                eps[p] += 1.1 * np.abs(u[p]) * rg + np.abs(sil[p]) * ru
     # 1. hidden vectors
     if h_gpu is not None:
         err = np.abs(h_gpu.astype(np.float64) - h)
@@ -90,33 +109,33 @@ def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None):
         sel = np.arange(D) if rows is None else np.asarray(rows)
         y_st = np.zeros((S, len(sel)))
         A_st = np.zeros((S, len(sel)))
+        R_st = np.zeros((S, len(sel)))
         for p in range(P):
             if not valid[p]:
                 continue
-            if p < S * K:
-                s, wk, Dm = p // K, float(w.flat[p]), Dn.expert(int(ids.flat[p]))
-            else:
-                s, wk, Dm = p - S * K, 1.0, sh[2]
+            s, wk, _, _, Dm = pair(p)
             Dsel = QMat(Dm.fmt, len(sel), Dm.I, Dm.gs, np.ascontiguousarray(Dm.q[sel]),
                         np.ascontiguousarray(Dm.s[sel]))
-            yk, Ak = orc.qmatmul(Dsel, h_gpu[p:p + 1].astype(np.float32))
+            hp = h_gpu[p:p + 1].astype(np.float32)
+            yk, Ak = orc.qmatmul(Dsel, hp)
             y_st[s] += wk * yk[0]
             A_st[s] += abs(wk) * Ak[0]
-        assert_within(out_rows, y_st, A_st, tau, "stagewise down+combine")
+            if rep:
+                R_st[s] += abs(wk) * REP_BOUND * block_magnitude(np.abs(orc.dequant_f64(Dsel)), hp)[0]
+        assert_within(out_rows, y_st, A_st, tau, "stagewise down+combine", R_st if rep else None)
     # 3. end to end
     sel = np.arange(D) if rows is None else np.asarray(rows)
     bound = np.zeros((S, len(sel)))
     for p in range(P):
         if not valid[p]:
             continue
-        if p < S * K:
-            s, wk, Dm = p // K, float(w.flat[p]), Dn.expert(int(ids.flat[p]))
-        else:
-            s, wk, Dm = p - S * K, 1.0, sh[2]
+        s, wk, _, _, Dm = pair(p)
         Dsel = QMat(Dm.fmt, len(sel), Dm.I, Dm.gs, np.ascontiguousarray(Dm.q[sel]),
                     np.ascontiguousarray(Dm.s[sel]))
         Dabs = np.abs(orc.dequant_f64(Dsel))
         bound[s] += abs(wk) * (Dabs @ eps[p] + tau * (Dabs @ (np.abs(h[p]) + eps[p])))
+        if rep and h_gpu is not None:
+            bound[s] += abs(wk) * REP_BOUND * block_magnitude(Dabs, h_gpu[p:p + 1])[0]
     err = np.abs(out_rows.astype(np.float64) - out_ref)
     assert np.all(err <= bound + 1e-30), f"end to end: max err/bound = {np.max(err / bound):.3e}"
 
@@ -181,6 +200,32 @@ def test_moe_decode_single_row_shared_invalid_ids(orc):
     _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
 
 
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_moe_decode_zero_weight_outlier_in_h(orc, S):
+    """One hidden unit j0 of every expert is driven to ~1e13 (its gate and up
+    rows have all codes +7 and scales 1e3, on inputs whose first block is
+    positive) while the down matrices' column j0 is zero in every row: the
+    down kernel's first 128-input block of h then has a huge maximum and no
+    weight on it.  Every stage stays within its bound plus the matrix-core
+    decode kernels' 2^-29 * Ahat term (gate/up from x, down from the GPU's h)."""
+    need_gpu()
+    E, D, F, K, gs, j0 = 4, 512, 256, 2, 64, 100
+    G, U, Dn, sh, x, ids, w = _moe_inputs(800 + S, 4, S, K, E, D, F, gs, True)
+    for m in (G, U, sh[0], sh[1]):
+        q = m.q if m.q.ndim == 3 else m.q[None]
+        sc = m.s if m.s.ndim == 3 else m.s[None]
+        q[:, j0, :] = 0xFF
+        sc[:, j0, :] = 1e3
+    for m in (Dn, sh[2]):
+        q = m.q if m.q.ndim == 3 else m.q[None]
+        for e in range(q.shape[0]):
+            zero_column(q[e], 4, j0)
+    x[:, :128] = 5.0
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    assert np.min(np.abs(h[:, j0])) > 1e12
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32, rep=True)
+
+
 def test_moe_decode_repeatable_bitwise(orc):
     need_gpu()
     G, U, Dn, sh, x, ids, w = _moe_inputs(5, 4, 4, 8, 16, 512, 256, 64, True)
@@ -193,8 +238,8 @@ def test_moe_decode_config2_full(orc):
     """Decode MoE block at its real shape: hidden 6144, 256 experts with gate/up
     2048x6144 and down 6144x2048, fmt 4 gs 64, 8 routed experts chosen
     uniformly, softmax weights.  The expert pool is drawn on the device with a
-    seeded generator; the 8 routed experts are copied back for the oracle;
-    the oracle evaluates 384 sampled output rows."""
+    seeded generator; the 8 routed experts are copied back for the oracle,
+    which evaluates every one of the 6144 output rows."""
     need_gpu()
     E, D, F, gs, K = 256, 6144, 2048, 64, 8
     r = sd.rng(2)
@@ -223,9 +268,7 @@ def test_moe_decode_config2_full(orc):
     U = QMat(4, F, D, gs, uq[sel].cpu().numpy(), usc[sel].cpu().numpy())
     Dn = QMat(4, D, F, gs, dq[sel].cpu().numpy(), dsc[sel].cpu().numpy())
     local = np.arange(K, dtype=np.int32)[None, :]
-    rows = np.sort(sd.rng(3).choice(D, 384, replace=False)).astype(np.int32)
-    _check_moe(orc, G, U, Dn, None, x, local, w, out.cpu().numpy(), h.cpu().numpy(), TOL_FP32,
-               rows=rows)
+    _check_moe(orc, G, U, Dn, None, x, local, w, out.cpu().numpy(), h.cpu().numpy(), TOL_FP32)
 
 
 ROUTE = [(1, 8, 256), (3, 2, 5), (7, 3, 4), (16, 4, 64), (5, 1, 1), (544, 8, 256),

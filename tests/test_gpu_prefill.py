@@ -1,8 +1,7 @@
 """GPU parity of the prefill path (S > 4 input rows): the bf16 matrix-core
 GEMM for coli_qmatmul and the ragged MoE block (routing table, gathered
 inputs, dual gate/up + SiLU, down, combine), against the oracle with the
-bf16 tolerance 4e-3 * sum |w||x| (colibri-strix commit log, "route large
-row-batch matmul_qt GEMMs to the GPU": prefill-sized row batches take a GEMM
+bf16 tolerance 4e-3 * sum |w||x| (colibri-strix commit log, prefill GEMM routing commit: prefill-sized row batches take a GEMM
 path)."""
 import numpy as np
 import pytest

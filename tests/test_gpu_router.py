@@ -1,5 +1,4 @@
-"""GPU router and exact top-K (colibri-strix commit log, "metal: full decode
-layer in ONE command buffer": router matvec + sigmoid, greedy argmax over
+"""GPU router and exact top-K (colibri-strix commit log, full decode layer commit: router matvec + sigmoid, greedy argmax over
 sigmoid + bias with the CPU's tie order, top-p truncation, norm_topk,
 routed_scale) against the oracle: the picks bit-exact (both sides decide on
 f64 keys), the f32 weights within the rounding of an f64 value."""
