@@ -65,6 +65,7 @@ def _load():
         "coli_moe_block": (i32, [QP, QP, QP, vp, i32, vp, vp, i32, QP, QP, QP, vp, vp, sz, vp]),
         "coli_moe_hidden": (i32, [QP, QP, vp, i32, vp, i32, QP, QP, vp, vp, sz, vp]),
         "coli_moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "coli_moe_block_noalloc": (i32, [QP, QP, QP, vp, i32, vp, vp, i32, QP, QP, QP, vp, vp]),
         "coli_last_reason": (C.c_char_p, []),
         "coli_last_error": (C.c_char_p, []),
         "coli_stats": (None, [vp, vp, vp]),
@@ -101,7 +102,7 @@ def exported_symbols():
             "coli_moe_block_end",
             "coli_set_decode_kernel",
             "coli_dequantize", "coli_moe_route", "coli_moe_block", "coli_moe_hidden",
-            "coli_moe_workspace_bytes", "coli_last_reason", "coli_last_error", "coli_stats",
+            "coli_moe_workspace_bytes", "coli_moe_block_noalloc", "coli_last_reason", "coli_last_error", "coli_stats",
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
             "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma", "coli_probe_launch",
             "coli_moe_router_workspace_bytes", "coli_moe_router", "coli_rmsnorm",
@@ -211,6 +212,16 @@ def coli_moe_block(gate, up, down, x, S, ids, w, K, sh_gate, sh_up, sh_down, out
     return _load().coli_moe_block(_qp(gate), _qp(up), _qp(down), _ptr(x), S, _ptr(ids), _ptr(w),
                                   K, _qp(sh_gate), _qp(sh_up), _qp(sh_down), _ptr(out),
                                   _ptr(workspace), ws_bytes, _stream(stream))
+
+
+COLI_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def coli_moe_block_noalloc(gate, up, down, x, S, ids, w, K, sh_gate, sh_up, sh_down, out,
+                           stream=None) -> int:
+    return _load().coli_moe_block_noalloc(_qp(gate), _qp(up), _qp(down), _ptr(x), S, _ptr(ids),
+                                          _ptr(w), K, _qp(sh_gate), _qp(sh_up), _qp(sh_down),
+                                          _ptr(out), _stream(stream))
 
 
 def coli_moe_hidden(gate, up, x, S, ids, K, sh_gate, sh_up, h_out, workspace, ws_bytes,

@@ -167,6 +167,40 @@ static int check_qt(const coli_qtensor *t, const char *name) {
 
 static bool dev_aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Device scratch of coli_moe_block_noalloc: one array per GPU (every device
+// the library runs on holds its own copy until the process ends).  The host
+// name `scratch` is a host-side stand-in, not a device address; the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[COLI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// COLI_OK with *out = this device's scratch address, or the decline / error
+static int scratch_on_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return decline("moe_block_noalloc: device %d beyond the %d the scratch table covers", dev,
+                       SCRATCH_MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr)
+            return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return COLI_OK;
+}
+
 }  // namespace coli
 
 using namespace coli;
@@ -733,6 +767,33 @@ int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_
     rc = S <= coli_gemv_max_rows() ? launch_moe_decode(a) : launch_moe_prefill(a);
     if (rc != COLI_OK) return rc;
     return launch_residual_add(h, y, out, (int64_t)S * D, st);
+}
+
+// ---------------------------------------------------------------------------
+// coli_moe_block_noalloc: the expert block with the library's own device
+// scratch instead of a caller workspace (for callers that cannot allocate).
+// ---------------------------------------------------------------------------
+
+int coli_moe_block_noalloc(const coli_qtensor *gate, const coli_qtensor *up,
+                           const coli_qtensor *down, const float *x, int S, const int32_t *ids,
+                           const float *w, int K, const coli_qtensor *sh_gate,
+                           const coli_qtensor *sh_up, const coli_qtensor *sh_down, float *out,
+                           void *stream) {
+    if (check_moe(gate, up, down, x, S, ids, K, sh_gate, sh_up, sh_down, "moe_block_noalloc") !=
+        COLI_OK)
+        return COLI_DECLINED;
+    const size_t need =
+        coli_moe_workspace_bytes(gate->n, S, K, gate->O, gate->I, sh_gate != nullptr);
+    if (need == 0 || need > (size_t)COLI_NOALLOC_SCRATCH_BYTES)
+        return decline("moe_block_noalloc: this block needs %zu bytes of scratch; the library's "
+                       "static scratch holds %zu (use coli_moe_block with a workspace)",
+                       need, (size_t)COLI_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    const int rc = scratch_on_current_device(&ws);
+    if (rc != COLI_OK)
+        return rc;
+    return coli_moe_block(gate, up, down, x, S, ids, w, K, sh_gate, sh_up, sh_down, out, ws,
+                          (size_t)COLI_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -306,6 +306,32 @@ int coli_moe_block_end(const coli_qtensor *gate, const coli_qtensor *up, const c
                        const float *x, int S, const float *w, int K, int has_shared, float *out,
                        void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * coli_moe_block_noalloc -- coli_moe_block for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same block, same kernels and results, with the
+ * library's own static device scratch in place of the caller's workspace.
+ * Arguments as coli_moe_block without workspace / ws_bytes; the caller still
+ * passes x, ids, w and out.
+ *   Limit: blocks whose coli_moe_workspace_bytes(...) exceeds
+ *   COLI_NOALLOC_SCRATCH_BYTES are declined (COLI_DECLINED, nothing written;
+ *   the decode shapes of the pages' model -- S <= 4, K = 8, F = 2048,
+ *   D = 6144, shared expert -- need about 1.2 MB).
+ *   The scratch is one static array per GPU, held by every GPU the library
+ *   runs on until the process ends; it keeps the last call's contents (the
+ *   block clears what must start at zero itself).  Calls that may overlap on
+ *   one GPU (other streams, other threads) race on it: serialise them.
+ *   Allocates nothing (no hipMalloc / hipFree; the scratch address is looked
+ *   up once per device on the first call there).
+ * Returns COLI_OK, COLI_DECLINED or COLI_HIP_ERROR.
+ */
+#define COLI_NOALLOC_SCRATCH_BYTES (8u << 20)
+int coli_moe_block_noalloc(const coli_qtensor *gate, const coli_qtensor *up,
+                           const coli_qtensor *down, const float *x, int S, const int32_t *ids,
+                           const float *w, int K, const coli_qtensor *sh_gate,
+                           const coli_qtensor *sh_up, const coli_qtensor *sh_down, float *out,
+                           void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Diagnostics (colibri PR #298, HIP single-source merge: a fault-injection */
 /* control proves GPU calls really executed; issue #585: fallbacks must be  */
