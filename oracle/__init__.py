@@ -116,6 +116,15 @@ class Oracle:
         L.oracle_moe_route.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.oracle_moe_router.argtypes = [vp, i64, i64, vp, vp, i64, i64, dbl, i32, dbl, vp, vp, vp]
         L.oracle_rmsnorm.argtypes = [vp, i64, i64, vp, dbl, vp]
+        QP = C.POINTER(OracleQT)
+        L.oracle_rope.argtypes = [vp, i64, i64, dbl, vp]
+        L.oracle_mla_qabs.argtypes = [QP, i64, i64, i64, i64, vp, i64, vp, vp]
+        L.oracle_mla_scores.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, vp, vp]
+        L.oracle_mla_softmax.argtypes = [vp, i64, i64, i64, i64, vp]
+        L.oracle_mla_clat.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp]
+        L.oracle_mla_ctx.argtypes = [QP, i64, i64, i64, vp, i64, vp, vp]
+        L.oracle_mla_decode.argtypes = [QP, vp, QP, QP, vp, QP, QP, i64, i64, i64, i64, dbl, dbl,
+                                        vp, i64, i64, vp, vp, vp, C.POINTER(C.c_void_p), i32]
         L.oracle_moe_block.restype = i64
         L.oracle_moe_block.argtypes = [C.POINTER(OracleQT)] * 3 + [
             i64, vp, i64, vp, vp, i64] + [C.POINTER(OracleQT)] * 3 + [
@@ -253,6 +262,123 @@ class Oracle:
             inter["bad"] = int(bad)
             return out, inter
         return out
+
+
+    # --- MLA decode attention (coli_oracle.c states the passages and readings)
+    def rope(self, v: np.ndarray, pos: int, theta: float) -> np.ndarray:
+        """RoPE of rotary vectors v [..., d_rope] (f64) at one position."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        dr = v.shape[-1]
+        flat = v.reshape(-1, dr)
+        out = np.zeros_like(flat)
+        for i in range(flat.shape[0]):
+            self.lib.oracle_rope(_p(flat[i]), dr // 2, int(pos), float(theta), _p(out[i]))
+        return out.reshape(v.shape)
+
+    def mla_qabs(self, kv_b: QMat, H, dn, dr, dv, q):
+        """(qabs [S][H][L], A) from q [S][H*(dn+dr)] (key absorption)."""
+        q = np.ascontiguousarray(np.atleast_2d(q), dtype=np.float64)
+        S, L = q.shape[0], kv_b.I
+        qa = np.zeros((S, H, L))
+        A = np.zeros((S, H, L))
+        t = kv_b.qt()
+        self.lib.oracle_mla_qabs(C.pointer(t), H, dn, dr, dv, _p(q), S, _p(qa), _p(A))
+        return qa, A
+
+    def mla_scores(self, qabs, qpe, Lc, Rc, pos_base, scale):
+        """(scores [S][H][pos_base+S], A): scaled q.k over t <= pos_base+s."""
+        qabs = np.ascontiguousarray(qabs, dtype=np.float64)
+        qpe = np.ascontiguousarray(qpe, dtype=np.float64)
+        Lc = np.ascontiguousarray(Lc, dtype=np.float32)
+        Rc = np.ascontiguousarray(Rc, dtype=np.float32)
+        S, H, L = qabs.shape
+        dr = qpe.shape[2]
+        Ts = pos_base + S
+        sc = np.zeros((S, H, Ts))
+        A = np.zeros((S, H, Ts))
+        self.lib.oracle_mla_scores(_p(qabs), _p(qpe), _p(Lc), _p(Rc), S, H, L, dr, pos_base, Ts,
+                                   float(scale), _p(sc), _p(A))
+        return sc, A
+
+    def mla_softmax(self, scores, pos_base):
+        scores = np.ascontiguousarray(scores, dtype=np.float64)
+        S, H, Ts = scores.shape
+        p = np.zeros_like(scores)
+        self.lib.oracle_mla_softmax(_p(scores), S, H, pos_base, Ts, _p(p))
+        return p
+
+    def mla_clat(self, p, Lc, pos_base):
+        p = np.ascontiguousarray(p, dtype=np.float64)
+        Lc = np.ascontiguousarray(Lc, dtype=np.float32)
+        S, H, Ts = p.shape
+        L = Lc.shape[1]
+        cl = np.zeros((S, H, L))
+        A = np.zeros((S, H, L))
+        self.lib.oracle_mla_clat(_p(p), _p(Lc), S, H, L, pos_base, Ts, _p(cl), _p(A))
+        return cl, A
+
+    def mla_ctx(self, kv_b: QMat, H, dn, dv, clat):
+        clat = np.ascontiguousarray(clat, dtype=np.float64)
+        S = clat.shape[0]
+        ctx = np.zeros((S, H * dv))
+        A = np.zeros((S, H * dv))
+        t = kv_b.qt()
+        self.lib.oracle_mla_ctx(C.pointer(t), H, dn, dv, _p(clat), S, _p(ctx), _p(A))
+        return ctx, A
+
+    def mla_decode(self, W: "MlaWeights", x, pos_base: int, Lc, Rc):
+        """The decode attention of S rows at positions pos_base.. (every step
+        in order, f64).  Lc [T][L] / Rc [T][dr] f32 are copied; the copies get
+        this call's rows.  Returns out [S][D] f64, the stages (dict) and the
+        new caches."""
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+        S = x.shape[0]
+        H, dn, dr, dv = W.H, W.dn, W.dr, W.dv
+        L, qr = W.kv_b.I, W.q_a.O
+        Lc = np.array(Lc, dtype=np.float32, order="C", copy=True)
+        Rc = np.array(Rc, dtype=np.float32, order="C", copy=True)
+        assert Lc.shape[0] >= pos_base + S and Rc.shape[0] >= pos_base + S
+        Ts = pos_base + S
+        shapes = [(S, qr), (S, L + dr), (S, qr), (S, H * (dn + dr)), (S, H, L), (S, H, dr),
+                  (S, H, Ts), (S, H, Ts), (S, H, L), (S, H * dv)]
+        names = ["cq_raw", "ckv_raw", "cq", "q", "qabs", "qpe", "scores", "p", "clat", "ctx"]
+        st = {n: np.zeros(sh) for n, sh in zip(names, shapes)}
+        ptrs = (C.c_void_p * 10)(*[st[n].ctypes.data for n in names])
+        out = np.zeros((S, W.o_proj.O))
+        ts = [m.qt() for m in (W.q_a, W.q_b, W.kv_a, W.kv_b, W.o_proj)]
+        qn = None if W.q_norm is None else np.ascontiguousarray(W.q_norm, dtype=np.float32)
+        kn = None if W.kv_norm is None else np.ascontiguousarray(W.kv_norm, dtype=np.float32)
+        self.lib.oracle_mla_decode(C.pointer(ts[0]), _p(qn), C.pointer(ts[1]), C.pointer(ts[2]),
+                                   _p(kn), C.pointer(ts[3]), C.pointer(ts[4]), H, dn, dr, dv,
+                                   float(W.eps), float(W.theta), _p(x), S, pos_base, _p(Lc),
+                                   _p(Rc), _p(out), ptrs, self.nthreads)
+        self._keep = ts
+        return out, st, Lc, Rc
+
+
+@dataclass
+class MlaWeights:
+    """One decode attention layer's weights and hyper-parameters (the
+    readings in coli_oracle.c): q_a [qr][D], q_b [H(dn+dr)][qr], kv_a
+    [L+dr][D], kv_b [H(dn+dv)][L], o_proj [D][H dv]; q_norm [qr] and
+    kv_norm [L] f32 (None: ones)."""
+    q_a: QMat
+    q_norm: np.ndarray | None
+    q_b: QMat
+    kv_a: QMat
+    kv_norm: np.ndarray | None
+    kv_b: QMat
+    o_proj: QMat
+    H: int
+    dn: int
+    dr: int
+    dv: int
+    eps: float = 1e-6
+    theta: float = 10000.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.dn + self.dr))
 
 
 _default: Oracle | None = None

@@ -486,3 +486,283 @@ void oracle_rmsnorm(const float *x, int64_t S, int64_t D, const float *w, double
             y[s * D + d] = (double)xr[d] * inv * (w ? (double)w[d] : 1.0);
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* MLA decode attention                                                */
+/* ------------------------------------------------------------------ */
+/*
+ * Sources (colibri-strix commit log):
+ *   [P3-attn]   fused decode attention commit (Phase 2): one decode attention
+ *               layer is q_a -> RMSNorm -> q_b -> RoPE on the query path;
+ *               kv_a -> RMSNorm of the latent and RoPE of the rotary key at
+ *               the token's position, both written to the latent / rotary
+ *               caches (Lc, Rc); the MLA absorption core (qabs, score,
+ *               softmax, clat, ctx); then o_proj.
+ *   [P3-attnS4] fused attention for S <= 4 (MTP verify): every core step
+ *               gains a query-row dimension; query row s attends the keys
+ *               [0, pos_base + s].
+ *   [P3-attnT]  standalone fused-attention regression tests: the CPU chain
+ *               per head is qabs, score, softmax, clat, ctx; checked at
+ *               S = 1/3/4 and pos_base 0/12/37 including the cache rows.
+ *   [P1]        issue #585 thread: kv_b, the MLA absorption weight, is
+ *               grouped int4 (fmt 4) on the fused path.
+ *
+ * Readings where the pages are silent (each also in the design notes):
+ *   - dimensions: H heads, each query head has d_nope "no position" and
+ *     d_rope rotary components (q_b rows h*(d_nope+d_rope) + j, the no-
+ *     position ones first); kv_a gives the latent (kv_rank) then the shared
+ *     rotary key (d_rope); kv_b rows h*(d_nope+d_v) + j hold head h's key
+ *     absorption rows (j < d_nope) then its value rows; ctx is [h*d_v + v];
+ *   - RoPE rotates consecutive pairs (2i, 2i+1) of a rotary vector by
+ *     pos * theta^(-2i/d_rope);
+ *   - RMSNorm as oracle_rmsnorm (eps inside the square root, per-feature
+ *     weight), on the query latent and on the kv latent;
+ *   - the softmax scale is 1/sqrt(d_nope + d_rope);
+ *   - the caches store f32 (the rows this call writes are rounded to f32
+ *     before any score reads them).
+ * Absorption: score = q . k with k = [W_UK Lc, Rc] equals
+ * (W_UK^T q_nope) . Lc + q_rope . Rc, and sum_t p_t W_UV Lc_t equals
+ * W_UV (sum_t p_t Lc_t); the pins check this against the expanded form.
+ */
+
+/* RoPE of one rotary vector of 2*npair components at position pos. */
+void oracle_rope(const double *in, int64_t npair, int64_t pos, double theta, double *out)
+{
+    for (int64_t i = 0; i < npair; i++) {
+        double ang = (double)pos * pow(theta, -(double)(2 * i) / (double)(2 * npair));
+        double c = cos(ang), s = sin(ang);
+        double a = in[2 * i], b = in[2 * i + 1];
+        out[2 * i] = a * c - b * s;
+        out[2 * i + 1] = a * s + b * c;
+    }
+}
+
+/* RMSNorm of one f64 vector (the oracle_rmsnorm formula). */
+static void rms_f64(const double *x, int64_t n, const float *w, double eps, double *y)
+{
+    double ss = 0.0;
+    for (int64_t d = 0; d < n; d++)
+        ss += x[d] * x[d];
+    const double inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t d = 0; d < n; d++)
+        y[d] = x[d] * inv * (w ? (double)w[d] : 1.0);
+}
+
+/* One weight of matrix 0 of a stack. */
+static double qt_w(const oracle_qt *t, int64_t o, int64_t i)
+{
+    return weight_value(t->fmt, t->q, t->s, oracle_row_bytes(t->fmt, t->I), t->ng, t->gs, o, i);
+}
+
+/* qabs[s][h][c] = sum_{j < dn} q[s][h*(dn+dr)+j] * kv_b[h*(dn+dv)+j][c]
+ * (the key absorption); A the matching sum of |terms|.  q: [S][H*(dn+dr)]. */
+void oracle_mla_qabs(const oracle_qt *kv_b, int64_t H, int64_t dn, int64_t dr, int64_t dv,
+                     const double *q, int64_t S, double *qabs, double *A)
+{
+    const int64_t L = kv_b->I;
+    for (int64_t s = 0; s < S; s++)
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (int64_t h = 0; h < H; h++)
+            for (int64_t c = 0; c < L; c++) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t j = 0; j < dn; j++) {
+                    double w = qt_w(kv_b, h * (dn + dv) + j, c);
+                    double v = q[s * H * (dn + dr) + h * (dn + dr) + j];
+                    acc += v * w;
+                    mag += fabs(v) * fabs(w);
+                }
+                qabs[(s * H + h) * L + c] = acc;
+                if (A)
+                    A[(s * H + h) * L + c] = mag;
+            }
+}
+
+/* scores[s][h][t] = scale * (qabs[s][h] . Lc[t] + qpe[s][h] . Rc[t]) for
+ * t <= pos_base + s; entries past it are set to 0 (never read).  Ts = the
+ * row stride of scores (>= pos_base + S).  A: the sum of |terms| times scale. */
+void oracle_mla_scores(const double *qabs, const double *qpe, const float *Lc, const float *Rc,
+                       int64_t S, int64_t H, int64_t L, int64_t dr, int64_t pos_base, int64_t Ts,
+                       double scale, double *scores, double *A)
+{
+    for (int64_t s = 0; s < S; s++)
+        for (int64_t h = 0; h < H; h++) {
+            const double *qa = qabs + (s * H + h) * L, *qp = qpe + (s * H + h) * dr;
+            for (int64_t t = 0; t < Ts; t++) {
+                double acc = 0.0, mag = 0.0;
+                if (t <= pos_base + s) {
+                    for (int64_t c = 0; c < L; c++) {
+                        acc += qa[c] * (double)Lc[t * L + c];
+                        mag += fabs(qa[c]) * fabs((double)Lc[t * L + c]);
+                    }
+                    for (int64_t r = 0; r < dr; r++) {
+                        acc += qp[r] * (double)Rc[t * dr + r];
+                        mag += fabs(qp[r]) * fabs((double)Rc[t * dr + r]);
+                    }
+                }
+                scores[(s * H + h) * Ts + t] = acc * scale;
+                if (A)
+                    A[(s * H + h) * Ts + t] = mag * scale;
+            }
+        }
+}
+
+/* p[s][h][t] = exp(z_t - max) / sum over t <= pos_base + s; 0 past it. */
+void oracle_mla_softmax(const double *scores, int64_t S, int64_t H, int64_t pos_base, int64_t Ts,
+                        double *p)
+{
+    for (int64_t s = 0; s < S; s++)
+        for (int64_t h = 0; h < H; h++) {
+            const double *z = scores + (s * H + h) * Ts;
+            double *pr = p + (s * H + h) * Ts;
+            const int64_t n = pos_base + s + 1;
+            double mx = z[0];
+            for (int64_t t = 1; t < n; t++)
+                mx = z[t] > mx ? z[t] : mx;
+            double sum = 0.0;
+            for (int64_t t = 0; t < n; t++)
+                sum += exp(z[t] - mx);
+            for (int64_t t = 0; t < Ts; t++)
+                pr[t] = t < n ? exp(z[t] - mx) / sum : 0.0;
+        }
+}
+
+/* clat[s][h][c] = sum_{t <= pos_base+s} p[s][h][t] * Lc[t][c]; A its sum of
+ * |terms|. */
+void oracle_mla_clat(const double *p, const float *Lc, int64_t S, int64_t H, int64_t L,
+                     int64_t pos_base, int64_t Ts, double *clat, double *A)
+{
+    for (int64_t s = 0; s < S; s++)
+        for (int64_t h = 0; h < H; h++)
+            for (int64_t c = 0; c < L; c++) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t t = 0; t <= pos_base + s; t++) {
+                    double v = p[(s * H + h) * Ts + t] * (double)Lc[t * L + c];
+                    acc += v;
+                    mag += fabs(v);
+                }
+                clat[(s * H + h) * L + c] = acc;
+                if (A)
+                    A[(s * H + h) * L + c] = mag;
+            }
+}
+
+/* ctx[s][h*dv+v] = sum_c kv_b[h*(dn+dv)+dn+v][c] * clat[s][h][c] (the value
+ * absorption); A its sum of |terms|. */
+void oracle_mla_ctx(const oracle_qt *kv_b, int64_t H, int64_t dn, int64_t dv, const double *clat,
+                    int64_t S, double *ctx, double *A)
+{
+    const int64_t L = kv_b->I;
+    for (int64_t s = 0; s < S; s++)
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (int64_t h = 0; h < H; h++)
+            for (int64_t v = 0; v < dv; v++) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t c = 0; c < L; c++) {
+                    double w = qt_w(kv_b, h * (dn + dv) + dn + v, c);
+                    double z = clat[(s * H + h) * L + c];
+                    acc += w * z;
+                    mag += fabs(w) * fabs(z);
+                }
+                ctx[s * H * dv + h * dv + v] = acc;
+                if (A)
+                    A[s * H * dv + h * dv + v] = mag;
+            }
+}
+
+/* One matrix of a stack times f64 rows: y[s][o] = sum_i w(o,i) x[s][i]. */
+static void qt_gemv(const oracle_qt *t, const double *x, int64_t S, double *y, int nthreads)
+{
+    (void)nthreads;
+    for (int64_t s = 0; s < S; s++)
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+        for (int64_t o = 0; o < t->O; o++) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < t->I; i++)
+                acc += qt_w(t, o, i) * x[s * t->I + i];
+            y[s * t->O + o] = acc;
+        }
+}
+
+/* The whole decode attention for S rows at positions pos_base .. pos_base+S-1
+ * ([P3-attn], [P3-attnS4]), every step above in order:
+ *   cq_raw = q_a x;  cq = RMSNorm(cq_raw) * q_norm;  q = q_b cq
+ *   ckv_raw = kv_a x;  Lc[pos] = f32(RMSNorm(latent) * kv_norm);
+ *   Rc[pos] = f32(RoPE(rotary key, pos))                  (pos = pos_base+s)
+ *   qpe = RoPE(q rotary part, pos);  qabs;  scores;  p;  clat;  ctx;
+ *   out = o_proj ctx
+ * x f32 [S][D]; Lc f32 [>= pos_base+S][kv_rank], Rc f32 [..][d_rope]: rows
+ * below pos_base are inputs, rows pos_base.. are written.  out f64 [S][D].
+ * st (optional, NULL entries skipped) receives the stages in f64:
+ * 0 cq_raw [S][qr], 1 ckv_raw [S][L+dr], 2 cq [S][qr], 3 q [S][H(dn+dr)],
+ * 4 qabs [S][H][L], 5 qpe [S][H][dr], 6 scores [S][H][pos_base+S],
+ * 7 p [same], 8 clat [S][H][L], 9 ctx [S][H dv].  nthreads: OpenMP threads
+ * over the output rows of the four projections (no change to the arithmetic). */
+void oracle_mla_decode(const oracle_qt *q_a, const float *q_norm, const oracle_qt *q_b,
+                       const oracle_qt *kv_a, const float *kv_norm, const oracle_qt *kv_b,
+                       const oracle_qt *o_proj, int64_t H, int64_t dn, int64_t dr, int64_t dv,
+                       double eps, double theta, const float *x, int64_t S, int64_t pos_base,
+                       float *Lc, float *Rc, double *out, double **st, int nthreads)
+{
+    const int64_t D = q_a->I, qr = q_a->O, L = kv_b->I, Ts = pos_base + S;
+    const int64_t nq = H * (dn + dr);
+    double *xd = (double *)calloc((size_t)(S * D), sizeof(double));
+    double *cq_raw = (double *)calloc((size_t)(S * qr), sizeof(double));
+    double *ckv = (double *)calloc((size_t)(S * (L + dr)), sizeof(double));
+    double *cq = (double *)calloc((size_t)(S * qr), sizeof(double));
+    double *q = (double *)calloc((size_t)(S * nq), sizeof(double));
+    double *qabs = (double *)calloc((size_t)(S * H * L), sizeof(double));
+    double *qpe = (double *)calloc((size_t)(S * H * dr), sizeof(double));
+    double *sc = (double *)calloc((size_t)(S * H * Ts), sizeof(double));
+    double *p = (double *)calloc((size_t)(S * H * Ts), sizeof(double));
+    double *clat = (double *)calloc((size_t)(S * H * L), sizeof(double));
+    double *ctx = (double *)calloc((size_t)(S * H * dv), sizeof(double));
+    double *tmp = (double *)calloc((size_t)(L > dr ? L : dr), sizeof(double));
+
+    for (int64_t i = 0; i < S * D; i++)
+        xd[i] = (double)x[i];
+    /* query path */
+    qt_gemv(q_a, xd, S, cq_raw, nthreads);
+    for (int64_t s = 0; s < S; s++)
+        rms_f64(cq_raw + s * qr, qr, q_norm, eps, cq + s * qr);
+    qt_gemv(q_b, cq, S, q, nthreads);
+    /* kv path: cache rows of this call's positions */
+    qt_gemv(kv_a, xd, S, ckv, nthreads);
+    for (int64_t s = 0; s < S; s++) {
+        const int64_t pos = pos_base + s;
+        rms_f64(ckv + s * (L + dr), L, kv_norm, eps, tmp);
+        for (int64_t c = 0; c < L; c++)
+            Lc[pos * L + c] = (float)tmp[c];
+        oracle_rope(ckv + s * (L + dr) + L, dr / 2, pos, theta, tmp);
+        for (int64_t r = 0; r < dr; r++)
+            Rc[pos * dr + r] = (float)tmp[r];
+    }
+    /* absorption core */
+    for (int64_t s = 0; s < S; s++)
+        for (int64_t h = 0; h < H; h++)
+            oracle_rope(q + s * nq + h * (dn + dr) + dn, dr / 2, pos_base + s, theta,
+                        qpe + (s * H + h) * dr);
+    oracle_mla_qabs(kv_b, H, dn, dr, dv, q, S, qabs, NULL);
+    oracle_mla_scores(qabs, qpe, Lc, Rc, S, H, L, dr, pos_base, Ts, 1.0 / sqrt((double)(dn + dr)),
+                      sc, NULL);
+    oracle_mla_softmax(sc, S, H, pos_base, Ts, p);
+    oracle_mla_clat(p, Lc, S, H, L, pos_base, Ts, clat, NULL);
+    oracle_mla_ctx(kv_b, H, dn, dv, clat, S, ctx, NULL);
+    qt_gemv(o_proj, ctx, S, out, nthreads);
+
+    if (st) {
+        const double *src[10] = {cq_raw, ckv, cq, q, qabs, qpe, sc, p, clat, ctx};
+        const int64_t n[10] = {S * qr, S * (L + dr), S * qr, S * nq, S * H * L, S * H * dr,
+                               S * H * Ts, S * H * Ts, S * H * L, S * H * dv};
+        for (int k = 0; k < 10; k++)
+            if (st[k])
+                memcpy(st[k], src[k], sizeof(double) * (size_t)n[k]);
+    }
+    free(xd); free(cq_raw); free(ckv); free(cq); free(q); free(qabs); free(qpe);
+    free(sc); free(p); free(clat); free(ctx); free(tmp);
+}

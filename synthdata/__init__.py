@@ -129,3 +129,26 @@ def pool_on_device(seed: int, fmt: int, n: int, O: int, I: int, gs: int, device=
     s = torch.empty(shape, device=device, dtype=torch.float32)
     s.uniform_(SCALE_LO, SCALE_HI, generator=g)
     return q, s
+
+
+# ---------------------------------------------------------------------------
+# Decode attention layer (MLA): weights, norm weights and prior cache rows
+# ---------------------------------------------------------------------------
+
+def gen_mla(r: np.random.Generator, D: int, qr: int, L: int, H: int, dn: int, dr: int, dv: int,
+            gs: int = 64, T: int = 64, pos_base: int = 0):
+    """Weights of one decode attention layer, all fmt 4 with group size gs:
+    q_a [qr][D], q_b [H(dn+dr)][qr], kv_a [L+dr][D], kv_b [H(dn+dv)][L],
+    o_proj [D][H dv] as (codes, scales); norm weights q_norm [qr], kv_norm [L]
+    uniform in [0.5, 1.5]; caches Lc [T][L], Rc [T][dr] whose rows below
+    pos_base hold N(0,1) draws (earlier tokens) and the rest zeros."""
+    shapes = {"q_a": (qr, D), "q_b": (H * (dn + dr), qr), "kv_a": (L + dr, D),
+              "kv_b": (H * (dn + dv), L), "o_proj": (D, H * dv)}
+    mats = {k: gen_matrix(r, 4, o, i, gs) for k, (o, i) in shapes.items()}
+    q_norm = r.uniform(0.5, 1.5, size=qr).astype(np.float32)
+    kv_norm = r.uniform(0.5, 1.5, size=L).astype(np.float32)
+    Lc = np.zeros((T, L), np.float32)
+    Rc = np.zeros((T, dr), np.float32)
+    Lc[:pos_base] = r.standard_normal((pos_base, L), dtype=np.float32)
+    Rc[:pos_base] = r.standard_normal((pos_base, dr), dtype=np.float32)
+    return mats, shapes, q_norm, kv_norm, Lc, Rc

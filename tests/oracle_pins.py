@@ -519,3 +519,139 @@ def pin_moe_layer_zero_norm_weight(orc):
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+# ---------------------------------------------------------------------------
+# MLA decode attention (colibri-strix commit log, fused decode attention
+# commits): RoPE closed forms, the absorbed core against the expanded
+# textbook attention, the one-key case, row equivalence, causality.
+# ---------------------------------------------------------------------------
+
+def pin_rope_closed_forms(orc):
+    # one pair: a rotation of the plane by the position itself
+    for pos in (0, 1, 7, 123):
+        a, b = 0.3, -1.7
+        got = orc.rope(np.array([a, b]), pos, 10000.0)
+        c, s = np.cos(pos), np.sin(pos)
+        assert np.allclose(got, [a * c - b * s, a * s + b * c], rtol=0, atol=1e-14)
+    # second pair of four: frequency theta^(-2/4) = 0.1 for theta = 100
+    got = orc.rope(np.array([0.0, 0.0, 1.0, 0.0]), 10, 100.0)
+    assert np.allclose(got, [0.0, 0.0, np.cos(1.0), np.sin(1.0)], rtol=0, atol=1e-14)
+    # position 0 is the identity, pair norms are kept, rotations compose
+    v = np.random.default_rng(5).standard_normal(64)
+    assert np.array_equal(orc.rope(v, 0, 10000.0), v)
+    r1 = orc.rope(v, 37, 10000.0)
+    assert np.allclose(np.hypot(r1[0::2], r1[1::2]), np.hypot(v[0::2], v[1::2]), atol=1e-13)
+    assert np.allclose(orc.rope(orc.rope(v, 12, 10000.0), 25, 10000.0), r1, atol=1e-12)
+
+
+def _mla_case(seed, S, pos_base, D=64, qr=32, L=48, H=3, dn=8, dr=4, dv=6, gs=16, T=None):
+    from oracle import MlaWeights
+    r = sd.rng(seed)
+    T = T or pos_base + S + 3
+    mats, shapes, qn, kn, Lc, Rc = sd.gen_mla(r, D, qr, L, H, dn, dr, dv, gs, T, pos_base)
+    Q = {k: QMat(4, o, i, gs, *mats[k]) for k, (o, i) in shapes.items()}
+    W = MlaWeights(Q["q_a"], qn, Q["q_b"], Q["kv_a"], kn, Q["kv_b"], Q["o_proj"], H, dn, dr, dv,
+                   eps=1e-6, theta=50.0)
+    x = sd.gen_x(r, S, D)
+    return W, x, Lc, Rc
+
+
+def _naive_mla(W, x, pos_base, Lc0, Rc0):
+    """Textbook multi-head attention with K and V expanded from the latent
+    cache, every weight from the independent decoder (ref_dense), RoPE and
+    RMSNorm written out with numpy."""
+    S = x.shape[0]
+    H, dn, dr, dv, L = W.H, W.dn, W.dr, W.dv, W.kv_b.I
+    Wqa, Wqb, Wkva, Wkvb, Wo = (ref_dense(m) for m in (W.q_a, W.q_b, W.kv_a, W.kv_b, W.o_proj))
+
+    def rms(v, w):
+        return v / np.sqrt(np.mean(v * v) + W.eps) * w.astype(np.float64)
+
+    def rot(v, pos):
+        f = W.theta ** (-np.arange(0, dr, 2) / dr)
+        c, s_ = np.cos(pos * f), np.sin(pos * f)
+        o = np.empty_like(v)
+        o[0::2] = v[0::2] * c - v[1::2] * s_
+        o[1::2] = v[0::2] * s_ + v[1::2] * c
+        return o
+
+    xd = x.astype(np.float64)
+    Lc, Rc = Lc0.copy(), Rc0.copy()
+    for s in range(S):
+        ckv = Wkva @ xd[s]
+        Lc[pos_base + s] = rms(ckv[:L], W.kv_norm).astype(np.float32)
+        Rc[pos_base + s] = rot(ckv[L:], pos_base + s).astype(np.float32)
+    blocks = Wkvb.reshape(H, dn + dv, L)
+    out, ctx = np.zeros((S, W.o_proj.O)), np.zeros((S, H * dv))
+    for s in range(S):
+        q = (Wqb @ rms(Wqa @ xd[s], W.q_norm)).reshape(H, dn + dr)
+        T = pos_base + s + 1
+        Lt, Rt = Lc[:T].astype(np.float64), Rc[:T].astype(np.float64)
+        for h in range(H):
+            Kh = np.concatenate([Lt @ blocks[h, :dn].T, Rt], axis=1)      # [T][dn+dr]
+            Vh = Lt @ blocks[h, dn:].T                                      # [T][dv]
+            qh = np.concatenate([q[h, :dn], rot(q[h, dn:], pos_base + s)])
+            z = Kh @ qh / np.sqrt(dn + dr)
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            ctx[s, h * dv:(h + 1) * dv] = p @ Vh
+        out[s] = Wo @ ctx[s]
+    return out, ctx, Lc, Rc
+
+
+def pin_mla_absorbed_equals_expanded(orc):
+    for seed, S, pb in ((1, 1, 0), (2, 3, 5), (3, 4, 9), (4, 2, 1)):
+        W, x, Lc, Rc = _mla_case(seed, S, pb)
+        out, st, Lc1, Rc1 = orc.mla_decode(W, x, pb, Lc, Rc)
+        nout, nctx, nLc, nRc = _naive_mla(W, x, pb, Lc, Rc)
+        assert np.array_equal(Lc1[:pb + S], nLc[:pb + S]) or \
+            np.allclose(Lc1, nLc, rtol=2 ** -23, atol=0), "latent cache rows"
+        assert np.allclose(Rc1, nRc, rtol=2 ** -23, atol=1e-30), "rotary cache rows"
+        mag_ctx = np.abs(nctx).max() + 1e-30
+        assert np.max(np.abs(st["ctx"] - nctx)) <= 1e-11 * mag_ctx, "ctx"
+        mag = np.abs(ref_dense(W.o_proj)) @ np.abs(nctx[0])
+        assert np.max(np.abs(out - nout)) <= 1e-11 * (mag.max() + 1e-30), "out"
+
+
+def pin_mla_one_key(orc):
+    """pos_base 0, one row: the single key takes probability 1, so the
+    context of head h is its value rows times the new latent row."""
+    W, x, Lc, Rc = _mla_case(11, 1, 0)
+    out, st, Lc1, _ = orc.mla_decode(W, x, 0, Lc, Rc)
+    assert np.all(st["p"][:, :, 0] == 1.0)
+    H, dn, dv, L = W.H, W.dn, W.dv, W.kv_b.I
+    Wv = ref_dense(W.kv_b).reshape(H, dn + dv, L)[:, dn:]
+    want = np.concatenate([Wv[h] @ Lc1[0].astype(np.float64) for h in range(H)])
+    assert np.allclose(st["ctx"][0], want, rtol=1e-13, atol=1e-15)
+
+
+def pin_mla_rows_equal_single_calls(orc):
+    """Row s of an S-row call is the single-row call at pos_base + s made
+    after the rows before it (the caches carry the earlier rows)."""
+    W, x, Lc, Rc = _mla_case(21, 4, 6)
+    out, _, Lc4, Rc4 = orc.mla_decode(W, x, 6, Lc, Rc)
+    Lcs, Rcs = Lc.copy(), Rc.copy()
+    for s in range(4):
+        o1, _, Lcs, Rcs = orc.mla_decode(W, x[s:s + 1], 6 + s, Lcs, Rcs)
+        assert np.array_equal(o1[0], out[s]), s
+    assert np.array_equal(Lcs, Lc4) and np.array_equal(Rcs, Rc4)
+
+
+def pin_mla_causal(orc):
+    """Cache rows past the last position never matter; earlier rows do."""
+    W, x, Lc, Rc = _mla_case(31, 3, 4, T=12)
+    out, _, _, _ = orc.mla_decode(W, x, 4, Lc, Rc)
+    Lf, Rf = Lc.copy(), Rc.copy()
+    Lf[7:] = 9.0
+    Rf[7:] = -9.0
+    out2, _, _, _ = orc.mla_decode(W, x, 4, Lf, Rf)
+    assert np.array_equal(out, out2)
+    Lp = Lc.copy()
+    Lp[2] += 1.0
+    out3, _, _, _ = orc.mla_decode(W, x, 4, Lp, Rc)
+    assert not np.allclose(out, out3)
+
+
+ALL_PINS += [pin_rope_closed_forms, pin_mla_absorbed_equals_expanded, pin_mla_one_key,
+             pin_mla_rows_equal_single_calls, pin_mla_causal]

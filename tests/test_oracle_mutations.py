@@ -38,6 +38,24 @@ MUTATIONS = {
                                "y[s * D + d] = (double)xr[d] * inv;"),
     "route_unstable": ("for (int64_t p = 0; p < S * K; p++) {\n            int32_t e = ids[p];\n            if (e >= 0 && e < E)\n                perm",
                        "for (int64_t p = S * K - 1; p >= 0; p--) {\n            int32_t e = ids[p];\n            if (e >= 0 && e < E)\n                perm"),
+    # MLA decode attention
+    "rope_sign": ("out[2 * i] = a * c - b * s;", "out[2 * i] = a * c + b * s;"),
+    "rope_frequency": ("pow(theta, -(double)(2 * i) / (double)(2 * npair))",
+                       "pow(theta, -(double)(i) / (double)(2 * npair))"),
+    "causal_exclusive": ("if (t <= pos_base + s) {", "if (t < pos_base + s) {"),
+    "mla_scale_nope_only": ("1.0 / sqrt((double)(dn + dr))", "1.0 / sqrt((double)dn)"),
+    "kvb_value_rows_first": ("double w = qt_w(kv_b, h * (dn + dv) + j, c);",
+                             "double w = qt_w(kv_b, h * (dn + dv) + dv + j, c);"),
+    "latent_norm_weight_dropped": ("rms_f64(ckv + s * (L + dr), L, kv_norm, eps, tmp);",
+                                   "rms_f64(ckv + s * (L + dr), L, NULL, eps, tmp);"),
+    "rotary_key_not_rotated": ("oracle_rope(ckv + s * (L + dr) + L, dr / 2, pos, theta, tmp);",
+                               "oracle_rope(ckv + s * (L + dr) + L, dr / 2, 0, theta, tmp);"),
+    "query_rotary_from_nope_part": ("oracle_rope(q + s * nq + h * (dn + dr) + dn, dr / 2,",
+                                    "oracle_rope(q + s * nq + h * (dn + dr), dr / 2,"),
+    "softmax_sum_misses_last_key": ("for (int64_t t = 0; t < n; t++)\n                sum += exp(z[t] - mx);",
+                                    "for (int64_t t = 0; t + 1 < n; t++)\n                sum += exp(z[t] - mx);"),
+    "clat_unweighted": ("double v = p[(s * H + h) * Ts + t] * (double)Lc[t * L + c];",
+                        "double v = (double)Lc[t * L + c];"),
 }
 
 
