@@ -18,6 +18,15 @@ LIB_PATH = os.path.join(HERE, "libcoli.so")
 COLI_OK, COLI_DECLINED, COLI_HIP_ERROR = 1, 0, -1
 
 
+class coli_mla_layer(C.Structure):
+    """Mirror of ``coli_mla_layer`` in include/coli.h."""
+    _fields_ = [("q_a", C.c_void_p), ("q_b", C.c_void_p), ("kv_a", C.c_void_p),
+                ("kv_b", C.c_void_p), ("o_proj", C.c_void_p), ("q_norm", C.c_void_p),
+                ("kv_norm", C.c_void_p), ("H", C.c_int32), ("d_nope", C.c_int32),
+                ("d_rope", C.c_int32), ("d_v", C.c_int32), ("eps", C.c_float),
+                ("rope_theta", C.c_float)]
+
+
 class coli_qtensor(C.Structure):
     """Mirror of ``coli_qtensor`` in include/coli.h."""
     _fields_ = [("fmt", C.c_int32), ("n", C.c_int32), ("O", C.c_int32), ("I", C.c_int32),
@@ -85,6 +94,11 @@ def _load():
         "coli_probe_read": (i32, [vp, sz, vp, vp]),
         "coli_probe_mfma": (i32, [i32, i32, vp, vp]),
         "coli_probe_launch": (i32, [i32, vp, vp]),
+        "coli_mla_workspace_bytes": (sz, [C.POINTER(coli_mla_layer), i32, i32]),
+        "coli_mla_workspace_layout": (sz, [C.POINTER(coli_mla_layer), i32, i32,
+                                           C.POINTER(C.c_size_t)]),
+        "coli_mla_decode": (i32, [C.POINTER(coli_mla_layer), vp, i32, i32, vp, vp, i32, vp, vp, sz,
+                                  vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -106,7 +120,8 @@ def exported_symbols():
             "coli_set_fail_after", "coli_prof_enable", "coli_prof_reset", "coli_prof_read",
             "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma", "coli_probe_launch",
             "coli_moe_router_workspace_bytes", "coli_moe_router", "coli_rmsnorm",
-            "coli_moe_layer_workspace_bytes", "coli_moe_layer"]
+            "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_mla_workspace_bytes",
+            "coli_mla_workspace_layout", "coli_mla_decode"]
 
 
 def _ptr(t):
@@ -290,6 +305,39 @@ def coli_probe_read(buf, sink, stream=None) -> int:
 def coli_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> int:
     """workgroups x 4 wavefronts x 8 x iters bf16 32x32x16 products."""
     return _load().coli_probe_mfma(int(workgroups), int(iters), _ptr(sink), _stream(stream))
+
+
+MLA_STAGES = ["cq_raw", "ckv_raw", "cq", "q", "qabs", "qpe", "scores", "p", "clat", "ctx"]
+
+
+class MlaLayer:
+    """A coli_mla_layer record plus the QTensors and norm weights it refers to
+    (kept alive)."""
+
+    def __init__(self, q_a, q_b, kv_a, kv_b, o_proj, q_norm, kv_norm, H, d_nope, d_rope, d_v,
+                 eps=1e-6, rope_theta=10000.0):
+        self.mats = (q_a, q_b, kv_a, kv_b, o_proj)
+        self.norms = (q_norm, kv_norm)
+        self.desc = coli_mla_layer(
+            *[C.addressof(m.desc) for m in self.mats], _ptr(q_norm), _ptr(kv_norm), H, d_nope,
+            d_rope, d_v, float(eps), float(rope_theta))
+
+
+def coli_mla_workspace_bytes(layer, S, T_cap) -> int:
+    return _load().coli_mla_workspace_bytes(C.byref(layer.desc), S, T_cap)
+
+
+def coli_mla_workspace_layout(layer, S, T_cap):
+    """(total bytes, {stage name: byte offset})."""
+    off = (C.c_size_t * len(MLA_STAGES))()
+    tot = _load().coli_mla_workspace_layout(C.byref(layer.desc), S, T_cap, off)
+    return tot, dict(zip(MLA_STAGES, list(off)))
+
+
+def coli_mla_decode(layer, x, S, pos_base, Lc, Rc, T_cap, out, workspace, ws_bytes,
+                    stream=None) -> int:
+    return _load().coli_mla_decode(C.byref(layer.desc), _ptr(x), S, pos_base, _ptr(Lc), _ptr(Rc),
+                                   T_cap, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def coli_probe_launch(workgroups: int, sink, stream=None) -> int:

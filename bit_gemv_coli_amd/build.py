@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoli.so")
-SOURCES = ["abi.hip", "gemv.hip", "mgemv.hip", "gemm.hip", "pgemm.hip", "route.hip", "router.hip", "layer.hip", "probe.hip"]
+SOURCES = ["abi.hip", "gemv.hip", "mgemv.hip", "gemm.hip", "pgemm.hip", "route.hip", "router.hip", "layer.hip", "mla.hip", "probe.hip"]
 ARCH = os.environ.get("COLI_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

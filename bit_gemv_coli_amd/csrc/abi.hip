@@ -18,6 +18,7 @@
 
 #include "common.h"
 #include "layer.h"
+#include "mla.h"
 
 namespace coli {
 
@@ -767,6 +768,104 @@ int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_
     rc = S <= coli_gemv_max_rows() ? launch_moe_decode(a) : launch_moe_prefill(a);
     if (rc != COLI_OK) return rc;
     return launch_residual_add(h, y, out, (int64_t)S * D, st);
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention (MLA)
+// ---------------------------------------------------------------------------
+
+// shapes and limits of a coli_mla_layer; fills the layout for S rows and
+// T_cap cache rows
+static int check_mla(const coli_mla_layer *m, int S, int T_cap, MlaLayout *lay, const char *who) {
+    if (!m)
+        return decline("%s: NULL layer", who);
+    const coli_qtensor *ts[5] = {m->q_a, m->q_b, m->kv_a, m->kv_b, m->o_proj};
+    const char *nm[5] = {"q_a", "q_b", "kv_a", "kv_b", "o_proj"};
+    for (int i = 0; i < 5; ++i) {
+        if (check_qt(ts[i], nm[i]) != COLI_OK)
+            return decline("%s: %s not filled by coli_tensor_upload", who, nm[i]);
+        if (ts[i]->n != 1)
+            return decline("%s: %s must be a single matrix", who, nm[i]);
+    }
+    const int H = m->H, dn = m->d_nope, dr = m->d_rope, dv = m->d_v;
+    if (H < 1 || H > 256 || dn < 1 || dn > 1024 || dr < 2 || dr > 256 || dr % 2 || dv < 1 ||
+        dv > 1024)
+        return decline("%s: bad heads/dims H=%d d_nope=%d d_rope=%d d_v=%d (H 1..256, d_nope "
+                       "1..1024, d_rope even 2..256, d_v 1..1024)", who, H, dn, dr, dv);
+    const int D = m->q_a->I, qr = m->q_a->O, L = m->kv_b->I;
+    if (m->q_b->I != qr || m->q_b->O != H * (dn + dr))
+        return decline("%s: q_b is [%d][%d], expected [%d][%d]", who, m->q_b->O, m->q_b->I,
+                       H * (dn + dr), qr);
+    if (m->kv_a->I != D || m->kv_a->O != L + dr)
+        return decline("%s: kv_a is [%d][%d], expected [%d][%d]", who, m->kv_a->O, m->kv_a->I,
+                       L + dr, D);
+    if (m->kv_b->O != H * (dn + dv))
+        return decline("%s: kv_b has %d rows, expected %d", who, m->kv_b->O, H * (dn + dv));
+    if (m->o_proj->O != D || m->o_proj->I != H * dv)
+        return decline("%s: o_proj is [%d][%d], expected [%d][%d]", who, m->o_proj->O,
+                       m->o_proj->I, D, H * dv);
+    const coli_qtensor *kb = m->kv_b;
+    if (!(kb->fmt == COLI_FMT_I4_ROW || (kb->fmt == COLI_FMT_I4_GRP && kb->gs % 8 == 0)))
+        return decline("%s: kv_b must be fmt 2, or fmt 4 with gs %% 8 == 0 (fmt %d gs %d)", who,
+                       kb->fmt, kb->gs);
+    if (L % 8 != 0 || L > 4096 || !dev_aligned(kb->q, 4))
+        return decline("%s: latent width %d must be a multiple of 8 up to 4096 with 4-byte "
+                       "aligned kv_b codes", who, L);
+    if (S < 1 || S > 4)
+        return decline("%s: S=%d outside 1..4 (decode rows)", who, S);
+    if (T_cap < S || (int64_t)T_cap * (L + dr) > INT32_MAX)
+        return decline("%s: bad T_cap=%d", who, T_cap);
+    if (!(m->eps >= 0.0f) || m->eps == __builtin_huge_valf() ||
+        !(m->rope_theta > 0.0f) || m->rope_theta == __builtin_huge_valf())
+        return decline("%s: eps must be finite >= 0 and rope_theta finite > 0", who);
+    *lay = mla_layout(S, H, dn, dr, dv, qr, L, T_cap);
+    return COLI_OK;
+}
+
+size_t coli_mla_workspace_layout(const coli_mla_layer *layer, int S, int T_cap,
+                                 size_t offsets[COLI_MLA_STAGES]) {
+    MlaLayout l;
+    if (check_mla(layer, S, T_cap, &l, "mla_workspace_layout") != COLI_OK)
+        return 0;
+    if (offsets)
+        for (int i = 0; i < MLA_NSTAGE; ++i) offsets[i] = l.off[i];
+    return l.total;
+}
+
+size_t coli_mla_workspace_bytes(const coli_mla_layer *layer, int S, int T_cap) {
+    return coli_mla_workspace_layout(layer, S, T_cap, nullptr);
+}
+
+int coli_mla_decode(const coli_mla_layer *layer, const float *x, int S, int pos_base, float *Lc,
+                    float *Rc, int T_cap, float *out, void *workspace, size_t ws_bytes,
+                    void *stream) {
+    MlaLayout l;
+    if (check_mla(layer, S, T_cap, &l, "mla_decode") != COLI_OK)
+        return COLI_DECLINED;
+    if (!x || !Lc || !Rc || !out)
+        return decline("mla_decode: NULL x, Lc, Rc or out");
+    if (!dev_aligned(x, 16) || !dev_aligned(out, 4) || !dev_aligned(Lc, 4) || !dev_aligned(Rc, 4))
+        return decline("mla_decode: x must be 16-byte aligned (out, Lc, Rc 4-byte)");
+    if (pos_base < 0 || pos_base > T_cap - S)
+        return decline("mla_decode: pos_base=%d with S=%d outside a cache of %d rows", pos_base, S,
+                       T_cap);
+    if (!workspace || !dev_aligned(workspace, 256) || ws_bytes < l.total)
+        return decline("mla_decode: workspace NULL, not 256-byte aligned or %zu < %zu bytes",
+                       ws_bytes, l.total);
+    if (!gate_call())
+        return COLI_DECLINED;
+    MlaArgs a;
+    a.layer = layer;
+    a.x = x;
+    a.S = S;
+    a.pos_base = pos_base;
+    a.T_cap = T_cap;
+    a.Lc = Lc;
+    a.Rc = Rc;
+    a.out = out;
+    a.ws = workspace;
+    a.st = (hipStream_t)stream;
+    return launch_mla_decode(a);
 }
 
 // ---------------------------------------------------------------------------

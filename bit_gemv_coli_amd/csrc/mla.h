@@ -1,0 +1,41 @@
+// mla.h -- the decode attention launcher (mla.hip) and its workspace layout.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/coli.h"
+
+namespace coli {
+
+// stage buffers inside the workspace, in this order (offsets are public via
+// coli_mla_workspace_layout)
+enum { MLA_CQ_RAW = 0, MLA_CKV_RAW, MLA_CQ, MLA_Q, MLA_QABS, MLA_QPE, MLA_SCORES, MLA_P, MLA_CLAT,
+       MLA_CTX, MLA_NSTAGE };
+static_assert(MLA_NSTAGE == COLI_MLA_STAGES, "stage count");
+
+struct MlaLayout {
+    size_t off[MLA_NSTAGE];
+    size_t total;
+};
+MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap);
+
+// kv_b's codes and scales as the absorption kernels read them
+struct MlaKvb {
+    const uint8_t *q;
+    const float *s;
+    int64_t rb;  // bytes per row
+    int ng, gs;  // fmt 4 groups per row and group size (fmt 2: 1, 1)
+};
+
+struct MlaArgs {
+    const coli_mla_layer *layer;
+    const float *x;
+    int S, pos_base, T_cap;
+    float *Lc, *Rc, *out;
+    void *ws;
+    hipStream_t st;
+};
+int launch_mla_decode(const MlaArgs &a);
+
+}  // namespace coli

@@ -403,6 +403,68 @@ int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_
                    const coli_qtensor *sh_down, float *out, void *workspace, size_t ws_bytes,
                    void *stream);
 
+/*
+ * Decode attention of one MLA layer (colibri-strix commit log: the fused
+ * decode attention commit (Phase 2) runs q_a -> RMSNorm -> q_b -> RoPE, kv_a ->
+ * RMSNorm of the latent and RoPE of the rotary key written to the latent and
+ * rotary caches, the absorption core (qabs, score, softmax, clat, ctx) and
+ * o_proj in one submission; the S <= 4 commit after it gives every step a
+ * query-row dimension, row s attending keys [0, pos_base + s]; issue #585
+ * thread: kv_b is grouped int4 on that path).
+ *
+ * Dimensions (the pages compile them in without printing them; the reading
+ * here takes them from the layer's projection shapes): D hidden, qr = q_a
+ * rows, L latent width, H heads of d_nope + d_rope query components and d_v
+ * value components:
+ *   q_a [qr][D]   q_b [H (d_nope + d_rope)][qr], head h's rows h (d_nope +
+ *                 d_rope) + j, the d_nope position-free ones first
+ *   kv_a [L + d_rope][D]: the latent, then the rotary key shared by all heads
+ *   kv_b [H (d_nope + d_v)][L]: head h's d_nope key rows, then its d_v value
+ *                 rows                       o_proj [D][H d_v]
+ *   q_norm [qr], kv_norm [L]: f32 RMSNorm weights (NULL: ones)
+ * RoPE turns consecutive pairs (2i, 2i+1) by pos * rope_theta^(-2i/d_rope);
+ * RMSNorm is x / sqrt(mean x^2 + eps) * w; the softmax scale is
+ * 1/sqrt(d_nope + d_rope).  All five matrices are single coli_qtensors (any
+ * format for the projections; kv_b fmt 4 with gs % 8 == 0, or fmt 2).
+ */
+typedef struct coli_mla_layer {
+    const coli_qtensor *q_a, *q_b, *kv_a, *kv_b, *o_proj;
+    const float *q_norm, *kv_norm;
+    int32_t H, d_nope, d_rope, d_v;
+    float eps, rope_theta;
+} coli_mla_layer;
+
+#define COLI_MLA_STAGES 10
+/* Workspace bytes of coli_mla_decode for S rows and caches of T_cap rows
+ * (0 on bad input). */
+size_t coli_mla_workspace_bytes(const coli_mla_layer *layer, int S, int T_cap);
+/* Where each step leaves its result in that workspace (for inspection after
+ * the call): byte offsets of f32 arrays, in order cq_raw [S][qr], ckv_raw
+ * [S][L + d_rope], cq [S][qr], q [S][H (d_nope + d_rope)], qabs [S][H][L],
+ * qpe [S][H][d_rope] (rotated), scores [S][H][T_cap] (scaled, keys 0 ..
+ * pos_base + s), p [S][H][T_cap], clat [S][H][L], ctx [S][H d_v].  Returns
+ * the total bytes (0 on bad input). */
+size_t coli_mla_workspace_layout(const coli_mla_layer *layer, int S, int T_cap,
+                                 size_t offsets[COLI_MLA_STAGES]);
+/*
+ * coli_mla_decode -- the decode attention for S = 1..4 rows x [S][D] at
+ * positions pos_base .. pos_base + S - 1:
+ *   writes cache rows Lc[pos_base + s] (f32 [T_cap][L]) and Rc[pos_base + s]
+ *   (f32 [T_cap][d_rope]); reads rows 0 .. pos_base + s for row s (rows below
+ *   pos_base are the earlier tokens', supplied by the caller);
+ *   out f32 [S][D] = o_proj ctx.
+ * Requires pos_base >= 0 and pos_base + S <= T_cap.  The projections run the
+ * decode GEMV kernels (coli_qmatmul's bounds); the core is fp32.  Nothing is
+ * allocated and the host never waits (graph-capturable).  x, out, Lc, Rc and
+ * the workspace must not overlap.
+ *   workspace: coli_mla_workspace_bytes(layer, S, T_cap) bytes, 256-byte
+ *   aligned, caller-owned; its stage arrays hold this call's intermediates.
+ * Returns COLI_OK, COLI_DECLINED or COLI_HIP_ERROR.
+ */
+int coli_mla_decode(const coli_mla_layer *layer, const float *x, int S, int pos_base, float *Lc,
+                    float *Rc, int T_cap, float *out, void *workspace, size_t ws_bytes,
+                    void *stream);
+
 /* Why the last call on this thread returned COLI_DECLINED ("" if none). */
 const char *coli_last_reason(void);
 /* Last HIP error text on this thread ("" if none). */
