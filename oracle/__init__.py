@@ -356,6 +356,29 @@ class Oracle:
         return out, st, Lc, Rc
 
 
+def _layer_decode(self, x, in_ln, eps, attn: "MlaWeights", pos_base, Lc, Rc, post_ln, R, bias, K,
+                  topp, norm_topk, routed_scale, gate, up, down, shared=None):
+    """One decode layer (colibri-strix commit log, full decode layer commit:
+    in_ln RMSNorm -> fused attention -> residual add -> post_ln RMSNorm ->
+    shared expert, router with the exact top-K, routed experts -> residual
+    add), each step one of the functions above, called in that order; the
+    values handed from one step to the next are f32 (as stored):
+      xn = rmsnorm(x, in_ln);  a = mla_decode(xn);  h = f32(x + a);
+      out = moe_layer(h, post_ln)                       (its own residual add)
+    Returns out [S][D] f64, a dict of the intermediates, and the new caches."""
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    xn = self.rmsnorm(x, in_ln, eps).astype(np.float32)
+    a, st, Lc1, Rc1 = self.mla_decode(attn, xn, pos_base, Lc, Rc)
+    h = (x.astype(np.float64) + a).astype(np.float32)
+    out, inter = self.moe_layer(h, post_ln, eps, R, bias, K, topp, norm_topk, routed_scale,
+                                gate, up, down, shared=shared)
+    inter.update({"xn": xn, "attn": a, "h": h, "attn_stages": st, "xn_moe": inter["xn"]})
+    return out, inter, Lc1, Rc1
+
+
+Oracle.layer_decode = _layer_decode
+
+
 @dataclass
 class MlaWeights:
     """One decode attention layer's weights and hyper-parameters (the

@@ -655,3 +655,44 @@ def pin_mla_causal(orc):
 
 ALL_PINS += [pin_rope_closed_forms, pin_mla_absorbed_equals_expanded, pin_mla_one_key,
              pin_mla_rows_equal_single_calls, pin_mla_causal]
+
+
+# ---------------------------------------------------------------------------
+# Full decode layer (colibri-strix commit log, full decode layer commit): the
+# composition, checked through cases that reduce it to one half.
+# ---------------------------------------------------------------------------
+
+def _layer_case(seed, S, pb, D=64, E=6, F=32, K=2, gs=16):
+    W, x, Lc, Rc = _mla_case(seed, S, pb, D=D, gs=gs)
+    r = sd.rng(seed + 1000)
+    G, U, Dn, _, _, _, sh = _moe_case(seed + 2000, S, K, E, D, F, gs=gs, shared=True)
+    R = r.standard_normal((E, D)).astype(np.float32)
+    bias = r.uniform(-0.1, 0.1, E).astype(np.float32)
+    in_ln = r.uniform(0.5, 1.5, D).astype(np.float32)
+    post_ln = r.uniform(0.5, 1.5, D).astype(np.float32)
+    return W, x, Lc, Rc, G, U, Dn, sh, R, bias, in_ln, post_ln
+
+
+def pin_layer_reduces_to_its_halves(orc):
+    from oracle import QMat as QM
+    W, x, Lc, Rc, G, U, Dn, sh, R, bias, in_ln, post_ln = _layer_case(41, 3, 4)
+    args = (R, bias, 2, 0.0, True, 1.0, G, U, Dn)
+    # attention output projection zero: h = x, the layer is the expert half on x
+    Wz = W.__class__(**{**W.__dict__, "o_proj": QM(4, W.o_proj.O, W.o_proj.I, W.o_proj.gs,
+                                                  W.o_proj.q, np.zeros_like(W.o_proj.s))})
+    out, it, _, _ = orc.layer_decode(x, in_ln, 1e-6, Wz, 4, Lc, Rc, post_ln, *args, shared=sh)
+    assert np.array_equal(it["h"], x)
+    ref, _ = orc.moe_layer(x, post_ln, 1e-6, *args, shared=sh)
+    assert np.array_equal(out, ref)
+    # every down projection zero: the layer is x + attention(in_ln(x))
+    Dz = QM(4, Dn.O, Dn.I, Dn.gs, Dn.q, np.zeros_like(Dn.s))
+    shz = (sh[0], sh[1], QM(4, sh[2].O, sh[2].I, sh[2].gs, sh[2].q, np.zeros_like(sh[2].s)))
+    out, it, Lc1, _ = orc.layer_decode(x, in_ln, 1e-6, W, 4, Lc, Rc, post_ln, R, bias, 2, 0.0,
+                                       True, 1.0, G, U, Dz, shared=shz)
+    xn = orc.rmsnorm(x, in_ln, 1e-6).astype(np.float32)
+    a, _, Lc2, _ = orc.mla_decode(W, xn, 4, Lc, Rc)
+    assert np.array_equal(out, (x.astype(np.float64) + a).astype(np.float32).astype(np.float64))
+    assert np.array_equal(Lc1, Lc2)
+
+
+ALL_PINS += [pin_layer_reduces_to_its_halves]
