@@ -99,6 +99,13 @@ def _load():
                                            C.POINTER(C.c_size_t)]),
         "coli_mla_decode": (i32, [C.POINTER(coli_mla_layer), vp, i32, i32, vp, vp, i32, vp, vp, sz,
                                   vp]),
+        "coli_layer_decode_workspace_bytes": (sz, [C.POINTER(coli_mla_layer), QP, i32, i32, i32,
+                                                   i32]),
+        "coli_layer_decode_workspace_layout": (sz, [C.POINTER(coli_mla_layer), QP, i32, i32, i32,
+                                                    i32, C.POINTER(C.c_size_t)]),
+        "coli_layer_decode": (i32, [C.POINTER(coli_mla_layer), vp, QP, QP, QP, vp, vp, vp, i32,
+                                    C.c_float, i32, C.c_float, QP, QP, QP, C.c_float, vp, i32, i32,
+                                    vp, vp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -121,7 +128,8 @@ def exported_symbols():
             "coli_prof_tag", "coli_version", "coli_probe_read", "coli_probe_mfma", "coli_probe_launch",
             "coli_moe_router_workspace_bytes", "coli_moe_router", "coli_rmsnorm",
             "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_mla_workspace_bytes",
-            "coli_mla_workspace_layout", "coli_mla_decode"]
+            "coli_mla_workspace_layout", "coli_mla_decode", "coli_layer_decode_workspace_bytes",
+            "coli_layer_decode_workspace_layout", "coli_layer_decode"]
 
 
 def _ptr(t):
@@ -338,6 +346,32 @@ def coli_mla_decode(layer, x, S, pos_base, Lc, Rc, T_cap, out, workspace, ws_byt
                     stream=None) -> int:
     return _load().coli_mla_decode(C.byref(layer.desc), _ptr(x), S, pos_base, _ptr(Lc), _ptr(Rc),
                                    T_cap, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+
+
+LAYER_STAGES = ["xn", "attn", "h", "attn_ws", "moe_ws"]
+
+
+def coli_layer_decode_workspace_bytes(attn, gate, S, K, T_cap, has_shared) -> int:
+    return _load().coli_layer_decode_workspace_bytes(C.byref(attn.desc), _qp(gate), S, K, T_cap,
+                                                     int(bool(has_shared)))
+
+
+def coli_layer_decode_workspace_layout(attn, gate, S, K, T_cap, has_shared):
+    """(total bytes, {stage name: byte offset})."""
+    off = (C.c_size_t * len(LAYER_STAGES))()
+    tot = _load().coli_layer_decode_workspace_layout(C.byref(attn.desc), _qp(gate), S, K, T_cap,
+                                                     int(bool(has_shared)), off)
+    return tot, dict(zip(LAYER_STAGES, list(off)))
+
+
+def coli_layer_decode(attn, in_ln, gate, up, down, post_ln, R, bias, K, topp, norm_topk,
+                      routed_scale, sh_gate, sh_up, sh_down, eps, x, S, pos_base, Lc, Rc, T_cap,
+                      out, workspace, ws_bytes, stream=None) -> int:
+    return _load().coli_layer_decode(
+        C.byref(attn.desc), _ptr(in_ln), _qp(gate), _qp(up), _qp(down), _ptr(post_ln), _ptr(R),
+        _ptr(bias), K, float(topp), int(bool(norm_topk)), float(routed_scale), _qp(sh_gate),
+        _qp(sh_up), _qp(sh_down), float(eps), _ptr(x), S, pos_base, _ptr(Lc), _ptr(Rc), T_cap,
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def coli_probe_launch(workgroups: int, sink, stream=None) -> int:

@@ -717,40 +717,41 @@ size_t coli_moe_layer_workspace_bytes(int E, int S, int K, int F, int D, int has
     return layer_ws(E, S, K, F, D, has_shared).total;
 }
 
-int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
-                   const float *h, int S, const float *ln_w, float eps, const float *R,
-                   const float *bias, int K, float topp, int norm_topk, float routed_scale,
-                   const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
-                   const coli_qtensor *sh_down, float *out, void *workspace, size_t ws_bytes,
-                   void *stream) {
-    if (!h || !R || !out || !workspace)
-        return decline("moe_layer: NULL h, R, out or workspace (ln_w, bias and the shared "
-                       "expert may be NULL)");
-    if (!dev_aligned(workspace, 256))
-        return decline("moe_layer: workspace not 256-byte aligned");
+// validation of the expert half of a layer (everything but the workspace)
+static int check_moe_layer(const coli_qtensor *gate, const coli_qtensor *up,
+                           const coli_qtensor *down, const float *h, int S, float eps,
+                           const float *R, int K, float topp, float routed_scale,
+                           const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                           const coli_qtensor *sh_down, const void *ids_probe, const char *who) {
+    if (!h || !R)
+        return decline("%s: NULL input rows or router weights", who);
     // the routing lands in the workspace; any non-NULL ids pointer passes here
-    if (check_moe(gate, up, down, h, S, (const int32_t *)workspace, K, sh_gate, sh_up, sh_down,
-                  "moe_layer") != COLI_OK)
+    if (check_moe(gate, up, down, h, S, (const int32_t *)ids_probe, K, sh_gate, sh_up, sh_down,
+                  who) != COLI_OK)
         return COLI_DECLINED;
     if (!down)
-        return decline("moe_layer: NULL down tensor");
-    const int E = gate->n, F = gate->O, D = gate->I;
+        return decline("%s: NULL down tensor", who);
+    const int E = gate->n, D = gate->I;
     if (E > 512 || K > 16 || K > E)
-        return decline("moe_layer: E=%d K=%d (router: E 1..512, K 1..min(16,E))", E, K);
+        return decline("%s: E=%d K=%d (router: E 1..512, K 1..min(16,E))", who, E, K);
     if (!(topp >= 0.0f && topp <= 1.0f) || !(routed_scale == routed_scale))
-        return decline("moe_layer: topp must lie in [0,1] and routed_scale must be a number");
+        return decline("%s: topp must lie in [0,1] and routed_scale must be a number", who);
     if (!(eps >= 0.0f) || eps == __builtin_huge_valf())
-        return decline("moe_layer: eps must be finite and >= 0");
+        return decline("%s: eps must be finite and >= 0", who);
     if ((int64_t)S * D > INT32_MAX || (int64_t)E * D > INT32_MAX)
-        return decline("moe_layer: S*D or E*D too large");
-    const int has_sh = sh_gate != nullptr;
-    const LayerWs l = layer_ws(E, S, K, F, D, has_sh);
-    if (l.total == 0 || ws_bytes < l.total)
-        return decline("moe_layer: workspace %zu bytes < %zu needed", ws_bytes, l.total);
-    if (!gate_call())
-        return COLI_DECLINED;
-    hipStream_t st = (hipStream_t)stream;
-    char *ws = (char *)workspace;
+        return decline("%s: S*D or E*D too large", who);
+    return COLI_OK;
+}
+
+// the expert half's launches: norm, router, block (shared expert included),
+// residual add
+static int launch_moe_layer(const coli_qtensor *gate, const coli_qtensor *up,
+                            const coli_qtensor *down, const float *h, int S, const float *ln_w,
+                            float eps, const float *R, const float *bias, int K, float topp,
+                            int norm_topk, float routed_scale, const coli_qtensor *sh_gate,
+                            const coli_qtensor *sh_up, const coli_qtensor *sh_down, float *out,
+                            char *ws, size_t ws_bytes, const LayerWs &l, hipStream_t st) {
+    const int E = gate->n, F = gate->O, D = gate->I;
     float *xn = (float *)(ws + l.xn);
     int32_t *ids = (int32_t *)(ws + l.ids);
     float *w = (float *)(ws + l.w);
@@ -768,6 +769,30 @@ int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_
     rc = S <= coli_gemv_max_rows() ? launch_moe_decode(a) : launch_moe_prefill(a);
     if (rc != COLI_OK) return rc;
     return launch_residual_add(h, y, out, (int64_t)S * D, st);
+}
+
+int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_qtensor *down,
+                   const float *h, int S, const float *ln_w, float eps, const float *R,
+                   const float *bias, int K, float topp, int norm_topk, float routed_scale,
+                   const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                   const coli_qtensor *sh_down, float *out, void *workspace, size_t ws_bytes,
+                   void *stream) {
+    if (!h || !R || !out || !workspace)
+        return decline("moe_layer: NULL h, R, out or workspace (ln_w, bias and the shared "
+                       "expert may be NULL)");
+    if (!dev_aligned(workspace, 256))
+        return decline("moe_layer: workspace not 256-byte aligned");
+    if (check_moe_layer(gate, up, down, h, S, eps, R, K, topp, routed_scale, sh_gate, sh_up,
+                        sh_down, workspace, "moe_layer") != COLI_OK)
+        return COLI_DECLINED;
+    const LayerWs l = layer_ws(gate->n, S, K, gate->O, gate->I, sh_gate != nullptr);
+    if (l.total == 0 || ws_bytes < l.total)
+        return decline("moe_layer: workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    if (!gate_call())
+        return COLI_DECLINED;
+    return launch_moe_layer(gate, up, down, h, S, ln_w, eps, R, bias, K, topp, norm_topk,
+                            routed_scale, sh_gate, sh_up, sh_down, out, (char *)workspace,
+                            ws_bytes, l, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -866,6 +891,114 @@ int coli_mla_decode(const coli_mla_layer *layer, const float *x, int S, int pos_
     a.ws = workspace;
     a.st = (hipStream_t)stream;
     return launch_mla_decode(a);
+}
+
+// ---------------------------------------------------------------------------
+// Full decode layer: in_ln -> attention -> residual -> expert half
+// ---------------------------------------------------------------------------
+
+struct FullLayerWs {
+    size_t off[COLI_LAYER_STAGES];  // xn, attn, h, attention workspace, expert-half workspace
+    size_t mla_bytes, moe_bytes, total;
+};
+
+static int full_layer_ws(const coli_mla_layer *attn, const coli_qtensor *gate, int S, int K,
+                         int T_cap, int has_shared, FullLayerWs *f, const char *who) {
+    MlaLayout ml;
+    if (check_mla(attn, S, T_cap, &ml, who) != COLI_OK)
+        return COLI_DECLINED;
+    if (check_qt(gate, "gate") != COLI_OK)
+        return COLI_DECLINED;
+    const int D = attn->q_a->I;
+    if (gate->I != D)
+        return decline("%s: experts take %d inputs, the attention's hidden size is %d", who,
+                       gate->I, D);
+    const LayerWs l = layer_ws(gate->n, S, K, gate->O, D, has_shared);
+    if (l.total == 0)
+        return decline("%s: bad expert-half sizes", who);
+    const size_t rows = al256((size_t)S * D * sizeof(float));
+    f->off[0] = 0;
+    f->off[1] = rows;
+    f->off[2] = 2 * rows;
+    f->off[3] = 3 * rows;
+    f->off[4] = 3 * rows + ml.total;
+    f->mla_bytes = ml.total;
+    f->moe_bytes = l.total;
+    f->total = f->off[4] + l.total;
+    return COLI_OK;
+}
+
+size_t coli_layer_decode_workspace_layout(const coli_mla_layer *attn, const coli_qtensor *gate,
+                                          int S, int K, int T_cap, int has_shared,
+                                          size_t offsets[COLI_LAYER_STAGES]) {
+    FullLayerWs f;
+    if (full_layer_ws(attn, gate, S, K, T_cap, has_shared ? 1 : 0, &f, "layer_decode_workspace") !=
+        COLI_OK)
+        return 0;
+    if (offsets)
+        for (int i = 0; i < COLI_LAYER_STAGES; ++i) offsets[i] = f.off[i];
+    return f.total;
+}
+
+size_t coli_layer_decode_workspace_bytes(const coli_mla_layer *attn, const coli_qtensor *gate,
+                                         int S, int K, int T_cap, int has_shared) {
+    return coli_layer_decode_workspace_layout(attn, gate, S, K, T_cap, has_shared, nullptr);
+}
+
+int coli_layer_decode(const coli_mla_layer *attn, const float *in_ln, const coli_qtensor *gate,
+                      const coli_qtensor *up, const coli_qtensor *down, const float *post_ln,
+                      const float *R, const float *bias, int K, float topp, int norm_topk,
+                      float routed_scale, const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                      const coli_qtensor *sh_down, float eps, const float *x, int S, int pos_base,
+                      float *Lc, float *Rc, int T_cap, float *out, void *workspace,
+                      size_t ws_bytes, void *stream) {
+    const char *who = "layer_decode";
+    FullLayerWs f;
+    if (full_layer_ws(attn, gate, S, K, T_cap, sh_gate != nullptr, &f, who) != COLI_OK)
+        return COLI_DECLINED;
+    if (!x || !Lc || !Rc || !out || !workspace)
+        return decline("%s: NULL x, Lc, Rc, out or workspace", who);
+    if (!dev_aligned(x, 16) || !dev_aligned(out, 4) || !dev_aligned(Lc, 4) || !dev_aligned(Rc, 4))
+        return decline("%s: x must be 16-byte aligned (out, Lc, Rc 4-byte)", who);
+    if (pos_base < 0 || pos_base > T_cap - S)
+        return decline("%s: pos_base=%d with S=%d outside a cache of %d rows", who, pos_base, S,
+                       T_cap);
+    if (!dev_aligned(workspace, 256) || ws_bytes < f.total)
+        return decline("%s: workspace not 256-byte aligned or %zu < %zu bytes", who, ws_bytes,
+                       f.total);
+    char *ws = (char *)workspace;
+    const float *h = (const float *)(ws + f.off[2]);
+    if (check_moe_layer(gate, up, down, h, S, eps, R, K, topp, routed_scale, sh_gate, sh_up,
+                        sh_down, ws, who) != COLI_OK)
+        return COLI_DECLINED;
+    if (!gate_call())
+        return COLI_DECLINED;
+    const hipStream_t st = (hipStream_t)stream;
+    const int D = attn->q_a->I;
+    float *xn = (float *)(ws + f.off[0]);
+    float *a = (float *)(ws + f.off[1]);
+    float *hh = (float *)(ws + f.off[2]);
+    int rc = launch_rmsnorm(x, S, D, in_ln, (double)eps, xn, st);
+    if (rc != COLI_OK) return rc;
+    MlaArgs m;
+    m.layer = attn;
+    m.x = xn;
+    m.S = S;
+    m.pos_base = pos_base;
+    m.T_cap = T_cap;
+    m.Lc = Lc;
+    m.Rc = Rc;
+    m.out = a;
+    m.ws = ws + f.off[3];
+    m.st = st;
+    rc = launch_mla_decode(m);
+    if (rc != COLI_OK) return rc;
+    rc = launch_residual_add(x, a, hh, (int64_t)S * D, st);
+    if (rc != COLI_OK) return rc;
+    const LayerWs l = layer_ws(gate->n, S, K, gate->O, D, sh_gate != nullptr);
+    return launch_moe_layer(gate, up, down, hh, S, post_ln, eps, R, bias, K, topp, norm_topk,
+                            routed_scale, sh_gate, sh_up, sh_down, out, ws + f.off[4], f.moe_bytes,
+                            l, st);
 }
 
 // ---------------------------------------------------------------------------

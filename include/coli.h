@@ -465,6 +465,40 @@ int coli_mla_decode(const coli_mla_layer *layer, const float *x, int S, int pos_
                     float *Rc, int T_cap, float *out, void *workspace, size_t ws_bytes,
                     void *stream);
 
+/*
+ * coli_layer_decode -- a whole decode layer in one submission (colibri-strix
+ * commit log, full decode layer commit: in_ln RMSNorm -> fused attention ->
+ * residual add -> post_ln RMSNorm -> shared expert, router with the exact
+ * top-K, routed experts -> residual add):
+ *   xn  = coli_rmsnorm(x, in_ln, eps)
+ *   a   = coli_mla_decode(attn, xn, pos_base; caches Lc, Rc)
+ *   h   = x + a                                               (f32)
+ *   out = coli_moe_layer(h, post_ln, eps, R, bias, K, topp, norm_topk,
+ *                        routed_scale; experts gate/up/down, shared expert)
+ * Arguments as in those calls (S = 1..4; in_ln, post_ln, bias and the shared
+ * expert may be NULL); out may equal x.  Everything is validated before the
+ * first launch; nothing is allocated and the host never waits.
+ *   workspace: coli_layer_decode_workspace_bytes(attn, gate, S, K, T_cap,
+ *   has_shared) bytes, 256-byte aligned.  coli_layer_decode_workspace_layout
+ *   gives the byte offsets of xn [S][D], a [S][D], h [S][D], the attention's
+ *   workspace (coli_mla_workspace_layout applies from there) and the expert
+ *   half's workspace.
+ * Returns COLI_OK, COLI_DECLINED or COLI_HIP_ERROR.
+ */
+#define COLI_LAYER_STAGES 5
+size_t coli_layer_decode_workspace_bytes(const coli_mla_layer *attn, const coli_qtensor *gate,
+                                         int S, int K, int T_cap, int has_shared);
+size_t coli_layer_decode_workspace_layout(const coli_mla_layer *attn, const coli_qtensor *gate,
+                                          int S, int K, int T_cap, int has_shared,
+                                          size_t offsets[COLI_LAYER_STAGES]);
+int coli_layer_decode(const coli_mla_layer *attn, const float *in_ln, const coli_qtensor *gate,
+                      const coli_qtensor *up, const coli_qtensor *down, const float *post_ln,
+                      const float *R, const float *bias, int K, float topp, int norm_topk,
+                      float routed_scale, const coli_qtensor *sh_gate, const coli_qtensor *sh_up,
+                      const coli_qtensor *sh_down, float eps, const float *x, int S, int pos_base,
+                      float *Lc, float *Rc, int T_cap, float *out, void *workspace,
+                      size_t ws_bytes, void *stream);
+
 /* Why the last call on this thread returned COLI_DECLINED ("" if none). */
 const char *coli_last_reason(void);
 /* Last HIP error text on this thread ("" if none). */
