@@ -88,6 +88,9 @@ def main():
                          "sweep one and eight matrices per launch)")
     ap.add_argument("--layer-stream-only", action="store_true",
                     help="only the 75-layer decode stream (grouped and one launch per projection)")
+    ap.add_argument("--layer-decode-only", action="store_true",
+                    help="only the 75 whole decode layers (attention + expert half) and the "
+                         "attention alone")
     ap.add_argument("--router-only", action="store_true",
                     help="only the router and top-K timings (S=1 and S=544); prints their JSON "
                          "(for profiling those kernels)")
@@ -131,6 +134,9 @@ def main():
         return
     if args.layer_stream_only:
         print(json.dumps(layer_stream(coli, sd, np, torch, log)), flush=True)
+        return
+    if args.layer_decode_only:
+        print(json.dumps(full_layer_stream(coli, sd, np, torch, log)), flush=True)
         return
     if args.router_only:
         print(json.dumps(router_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
@@ -272,6 +278,9 @@ def summary(e, value, roofline):
     one = e.get("gemv_6144x6144_ring", {}).get("fmt4_g64_S1")
     if one:
         out["gemv_6144x6144_fmt4_g64_S1_one_per_launch"] = {"GBps": one["GBps"], "frac_hbm": one["frac_hbm"]}
+    for k in ("layer_decode_75", "mla_decode_75"):
+        if k in e:
+            out[k] = {"us_per_layer": e[k]["us_per_layer"], "frac_hbm": e[k]["frac_hbm"]}
     ls = e.get("layer_stream_75")
     if ls:
         out["layer_stream_75"] = {"us_per_layer": ls["us_per_layer"], "frac_hbm": ls["frac_hbm"]}
@@ -312,6 +321,7 @@ def side_measurements(coli, sd, np, torch, log):
     out.update(router_measurements(coli, sd, np, torch, log, timed))
     out.update(prefill_measurements(coli, sd, np, torch, log, timed))
     out.update(layer_stream(coli, sd, np, torch, log))
+    out.update(full_layer_stream(coli, sd, np, torch, log))
     return out
 
 
@@ -582,6 +592,137 @@ def ceiling_probes(coli, torch, log):
                                   "stream_read_frac_spec": read_gbs / HBM_PEAK_GBS,
                                   "mfma_bf16_frac_spec": mfma_tf / BF16_PEAK_TFLOPS,
                                   "launch_floor_us": floor}}
+
+
+def full_layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=5, pos=544,
+                      T_cap=1024):
+    """75 whole decode layers (S = 1) back to back in one HIP graph, each one
+    coli_layer_decode: in_ln RMSNorm, MLA attention at position 544 (64 heads
+    of 192 + 64 / 256, latent 512 + 64, caches of 1024 rows holding 544
+    earlier tokens; q_a 1536x6144, q_b 16384x1536, kv_a 576x6144, kv_b
+    28672x512, o_proj 6144x16384), residual, post_ln RMSNorm, router with the
+    exact top-8 over a resident pool of 20 experts, 8 routed + 1 shared
+    expert (gate/up 2048x6144, down 6144x2048), residual -- all fmt 4 gs 64.
+    Also the attention alone (75 coli_mla_decode calls in a graph) and, from
+    one eager pass with the library's per-launch events, each kernel's
+    average time."""
+    dev = "cuda"
+    gs, H, dn, dr, dv, qr, Lat = 64, 64, 192, 64, 256, 1536, 512
+    log(f"full layer stream: drawing {layers} layers")
+    shapes = [(qr, D), (H * (dn + dr), qr), (Lat + dr, D), (H * (dn + dv), Lat), (D, H * dv)]
+    Ls = []
+    for l in range(layers):
+        P = [sd.pool_on_device(20000 + 10 * l + i, 4, 1, o, i_, gs) for i, (o, i_) in enumerate(shapes)]
+        TP = [coli.QTensor(4, q[0], s_[0], o, i_, gs, n=1) for (q, s_), (o, i_) in zip(P, shapes)]
+        for t in TP[:3] + TP[4:]:
+            t.pack()
+        qn = torch.rand(qr, device=dev) + 0.5
+        kn = torch.rand(Lat, device=dev) + 0.5
+        layer = coli.MlaLayer(*TP, qn, kn, H, dn, dr, dv, 1e-6, 10000.0)
+        Lc = torch.zeros((T_cap, Lat), device=dev)
+        Rc = torch.zeros((T_cap, dr), device=dev)
+        Lc[:pos].normal_()
+        Rc[:pos].normal_()
+        mg = sd.pool_on_device(30000 + 4 * l, 4, pool + 1, F, D, gs)
+        mu = sd.pool_on_device(30001 + 4 * l, 4, pool + 1, F, D, gs)
+        md = sd.pool_on_device(30002 + 4 * l, 4, pool + 1, D, F, gs)
+        tg = coli.QTensor(4, mg[0][:pool], mg[1][:pool], F, D, gs)
+        tu = coli.QTensor(4, mu[0][:pool], mu[1][:pool], F, D, gs)
+        td = coli.QTensor(4, md[0][:pool], md[1][:pool], D, F, gs)
+        sg = coli.QTensor(4, mg[0][pool], mg[1][pool], F, D, gs, n=1)
+        su = coli.QTensor(4, mu[0][pool], mu[1][pool], F, D, gs, n=1)
+        sdn = coli.QTensor(4, md[0][pool], md[1][pool], D, F, gs, n=1)
+        for t in (tg, tu, td, sg, su, sdn):
+            t.pack()
+        R = torch.randn((pool, D), device=dev) / D ** 0.5
+        bias = torch.randn(pool, device=dev) * 0.05
+        ln = (torch.rand(D, device=dev) + 0.5, torch.rand(D, device=dev) + 0.5)
+        Ls.append((P, TP, layer, qn, kn, Lc, Rc, mg, mu, md, tg, tu, td, sg, su, sdn, R, bias, ln))
+    x = torch.randn((1, D), device=dev)
+    out = torch.empty((1, D), device=dev)
+    a_out = torch.empty((1, D), device=dev)
+    wsb = coli.coli_layer_decode_workspace_bytes(Ls[0][2], Ls[0][10], 1, K, T_cap, True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    mwsb = coli.coli_mla_workspace_bytes(Ls[0][2], 1, T_cap)
+    mws = torch.empty(mwsb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def layer_pass():
+        st = torch.cuda.current_stream()
+        for l in range(layers):
+            (P, TP, layer, qn, kn, Lc, Rc, mg, mu, md, tg, tu, td, sg, su, sdn, R, bias,
+             ln) = Ls[l]
+            coli.check(coli.coli_layer_decode(layer, ln[0], tg, tu, td, ln[1], R, bias, K, 0.0, 1,
+                                              2.5, sg, su, sdn, 1e-6, x, 1, pos, Lc, Rc, T_cap,
+                                              out, ws, wsb, st), "coli_layer_decode")
+
+    def attn_pass():
+        st = torch.cuda.current_stream()
+        for l in range(layers):
+            layer, Lc, Rc = Ls[l][2], Ls[l][5], Ls[l][6]
+            coli.check(coli.coli_mla_decode(layer, x, 1, pos, Lc, Rc, T_cap, a_out, mws, mwsb, st),
+                       "coli_mla_decode")
+
+    def timed_graph(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        a.record(st)
+        for _ in range(passes):
+            graph.replay()
+        b.record(st)
+        torch.cuda.synchronize()
+        del graph
+        return a.elapsed_time(b) / passes
+
+    attn_w = sum(qbytes(4, o, i_, gs) for o, i_ in shapes)
+    cache = (pos + 1) * (Lat + dr) * 4          # every key row read once
+    attn_bytes = attn_w + cache + 2 * D * 4 + qr * 4 + Lat * 4
+    moe_bytes = 9 * (2 * qbytes(4, F, D, gs) + qbytes(4, D, F, gs)) + pool * D * 4 + 3 * D * 4
+    per_layer = attn_bytes + moe_bytes
+    res = {}
+    ms = timed_graph(layer_pass)
+    gbs = layers * per_layer / (ms * 1e-3) / 1e9
+    log(f"full decode layer x{layers}: {ms * 1e3 / layers:.1f} us/layer, {gbs:.0f} GB/s "
+        f"({per_layer / 1e6:.1f} MB/layer)")
+    res["layer_decode_75"] = {"us_per_layer": ms * 1e3 / layers, "GBps": gbs,
+                              "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": per_layer,
+                              "pos": pos, "launches_per_layer": None}
+    ms = timed_graph(attn_pass)
+    gbs = layers * attn_bytes / (ms * 1e-3) / 1e9
+    log(f"MLA decode attention x{layers}: {ms * 1e3 / layers:.1f} us/layer, {gbs:.0f} GB/s "
+        f"({attn_bytes / 1e6:.1f} MB)")
+    res["mla_decode_75"] = {"us_per_layer": ms * 1e3 / layers, "GBps": gbs,
+                            "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": attn_bytes,
+                            "pos": pos}
+    # per-kernel averages from one eager pass of whole layers
+    n0 = coli.coli_stats()[2]
+    coli.coli_prof_reset()
+    coli.coli_prof_enable(True)
+    layer_pass()
+    torch.cuda.synchronize()
+    coli.coli_prof_enable(False)
+    res["layer_decode_75"]["launches_per_layer"] = (coli.coli_stats()[2] - n0) / layers
+    kern = {}
+    for tag in coli.coli_prof_tags():
+        n, tot = coli.coli_prof_read(tag)
+        if n > 0:
+            kern[tag] = {"launches": n, "avg_us": tot / n * 1e3}
+    res["layer_decode_75"]["kernels_eager"] = kern
+    log(f"full layer kernels (eager, events per launch): {kern}")
+    del Ls
+    torch.cuda.empty_cache()
+    return res
 
 
 def layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=10):

@@ -196,3 +196,61 @@ def test_graph_two_phase_block(S):
                                        out2, ws2, wsb2), "coli_moe_block")
 
     _replays_match(run, [out], between=between)
+
+
+def test_layer_decode_graph_replays():
+    """A whole decode layer (attention with its cache writes, residual, expert
+    half) captured as one graph: every replay reproduces the eager output and
+    cache rows bit for bit, with an eager layer on other buffers between the
+    replays."""
+    need_gpu()
+    from test_gpu_mla import SMALL, _setup as setup_attention
+    S, pb, E, F, K = 3, 6, 8, 64, 4
+    D = SMALL["D"]
+
+    def make(seed):
+        W, layer, x, Lc, Rc, T = setup_attention(seed, S, pb, SMALL)
+        G, U, Dn, sh, _, _, _ = _moe_inputs(seed + 1, 4, S, K, E, D, F, 32, True)
+        R = (np.random.default_rng(seed).standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)
+        tg, tu, td = qtensor(G, True), qtensor(U, True), qtensor(Dn, True)
+        ts = [qtensor(m, True) for m in sh]
+        total = coli.coli_layer_decode_workspace_bytes(layer, tg, S, K, T, True)
+        ws = torch.empty(total, dtype=torch.uint8, device="cuda")
+        xd, Rd, Lc_d, Rc_d = to_dev(x), to_dev(R), to_dev(Lc), to_dev(Rc)
+        out = torch.empty((S, D), device="cuda")
+
+        def run():
+            coli.check(coli.coli_layer_decode(layer, None, tg, tu, td, None, Rd, None, K, 0.0, 1,
+                                              1.0, ts[0], ts[1], ts[2], 1e-6, xd, S, pb, Lc_d,
+                                              Rc_d, T, out, ws, total,
+                                              torch.cuda.current_stream()), "coli_layer_decode")
+        return run, [out, Lc_d, Rc_d], (layer, tg, tu, td, ts, ws, xd, Rd)
+    run, outs, keep = make(950)
+    run2, _, keep2 = make(960)
+    out, Lc_d, Rc_d = outs
+    # the caches are inputs too (rows below pb): only this call's rows are
+    # cleared before each replay
+    run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        Lc_d[pb:pb + S].fill_(float("nan"))
+        Rc_d[pb:pb + S].fill_(float("nan"))
+        run2()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, ref):
+            assert torch.equal(o.view(torch.int32), e.view(torch.int32)), f"replay {r} differs"
+    del g
