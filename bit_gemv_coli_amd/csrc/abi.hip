@@ -833,8 +833,8 @@ static int check_mla(const coli_mla_layer *m, int S, int T_cap, MlaLayout *lay, 
     if (!(kb->fmt == COLI_FMT_I4_ROW || (kb->fmt == COLI_FMT_I4_GRP && kb->gs % 8 == 0)))
         return decline("%s: kv_b must be fmt 2, or fmt 4 with gs %% 8 == 0 (fmt %d gs %d)", who,
                        kb->fmt, kb->gs);
-    if (L % 8 != 0 || L > 4096 || !dev_aligned(kb->q, 4))
-        return decline("%s: latent width %d must be a multiple of 8 up to 4096 with 4-byte "
+    if (L % 32 != 0 || L > 4096 || !dev_aligned(kb->q, 16))
+        return decline("%s: latent width %d must be a multiple of 32 up to 4096 with 16-byte "
                        "aligned kv_b codes", who, L);
     if (S < 1 || S > 4)
         return decline("%s: S=%d outside 1..4 (decode rows)", who, S);

@@ -14,8 +14,15 @@ enum { MLA_CQ_RAW = 0, MLA_CKV_RAW, MLA_CQ, MLA_Q, MLA_QABS, MLA_QPE, MLA_SCORES
        MLA_CTX, MLA_NSTAGE };
 static_assert(MLA_NSTAGE == COLI_MLA_STAGES, "stage count");
 
+// key-absorption row splits per head (their partial sums sit in the workspace
+// after the public stages)
+constexpr int MLA_QA_SPLIT = 4;
+// score splits over the L + d_rope components
+constexpr int MLA_SC_SPLIT = 3;
+
 struct MlaLayout {
     size_t off[MLA_NSTAGE];
+    size_t qabs_part, sc_part, cl_part;  // partial sums (internal)
     size_t total;
 };
 MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap);

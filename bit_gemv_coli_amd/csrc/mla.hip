@@ -22,19 +22,21 @@
 //                     f32 rounding of x * inv * w in f64; the kv workgroup
 //                     also rotates the rotary key (cos / sin in f64) and
 //                     writes both cache rows
-//   k_mla_qabs        one workgroup per (head, 512-column slab): each lane
-//                     owns 8 columns (one word of codes per kv_b row), the
-//                     8 wavefronts take every 8th key row, then sum in LDS in
-//                     wavefront order; workgroup 0 of each head rotates the
-//                     query's rotary part
-//   k_mla_scores      one workgroup per (64 keys, head, row): qabs and qpe in
-//                     LDS, a wavefront per 16 keys, lanes across the latent
-//                     (coalesced cache rows), wavefront sums
-//   k_mla_softmax_clat one workgroup per (row, head, 256 latent columns): max
-//                     and sum by fixed-order LDS trees, p by exp and one
-//                     division, then clat with the probabilities staged in LDS
-//   k_mla_ctx         one workgroup per (head, 16 value rows): lanes own 8
-//                     latent columns, wavefront sums
+//   k_mla_qabs        4 workgroups per head, each summing a quarter of its
+//                     key rows (lanes own 8 columns, 8 rows in flight per
+//                     wavefront) into a partial; workgroup 0 of each head
+//                     rotates the query's rotary part
+//   k_mla_scores      partial scores over a third of the L + d_rope components:
+//                     4 heads x 64 keys per workgroup, LDS chunks double-
+//                     buffered; adds the qabs partials while staging
+//   k_mla_softmax_clat per 64-key chunk: the softmax statistics of each
+//                     wavefront's head over all keys, then the chunk's share
+//                     of clat (4 heads x 64 columns per workgroup)
+//   k_mla_ctx         16 value rows per wavefront, 4 lanes per row with
+//                     16-byte code loads; clat (the chunks' shares added in
+//                     order) in LDS
+// Every partial sum is added in a fixed order by the next kernel, so reruns
+// are bit-identical.
 #include "common.h"
 #include "mla.h"
 
@@ -92,56 +94,80 @@ __global__ __launch_bounds__(256) void k_mla_norm_rope(const float *__restrict__
 }
 
 // ---- key absorption and the query's rotary part ----------------------------
+// grid (head, QA_SPLIT row splits): each workgroup sums its share of the
+// head's d_nope key rows into its own partial (qabs_part[split]); the scores
+// kernel adds the QA_SPLIT partials in split order.  A lane owns 8 columns
+// (one word of codes per row); the 8 wavefronts take every 8th row of the
+// split, all of a wavefront's rows requested before any is used.
 constexpr int QA_NW = 8;      // wavefronts per workgroup
-constexpr int QA_COLS = 512;  // latent columns per workgroup (8 per lane)
+constexpr int QA_COLS = 512;  // latent columns per pass (8 per lane)
+constexpr int QA_RB = 8;      // rows per wavefront in flight
 
 template <int S, bool GRP>
 __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int dn, int dr, int dv,
                                                          int L, const float *__restrict__ q,
                                                          int pos_base, double theta,
-                                                         float *__restrict__ qabs,
+                                                         float *__restrict__ part,
                                                          float *__restrict__ qpe) {
     __shared__ float red[QA_NW][S][QA_COLS];
-    const int h = blockIdx.x, col0 = blockIdx.y * QA_COLS;
+    const int h = blockIdx.x, split = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nq = H * (dn + dr);
-    const int c0 = col0 + 8 * lane;  // this lane's 8 columns
-    const bool live = c0 < L;
-    float acc[S][8];
+    const int rows = (dn + MLA_QA_SPLIT - 1) / MLA_QA_SPLIT;
+    const int j0 = split * rows, j1 = min(dn, j0 + rows);
+    const float *qh = q + (int64_t)h * (dn + dr);
+    for (int col0 = 0; col0 < L; col0 += QA_COLS) {
+        const int c0 = col0 + 8 * lane;  // this lane's 8 columns
+        const bool live = c0 < L;
+        float acc[S][8];
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+        for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[s][k] = 0.f;
-    for (int j = wave; j < dn; j += QA_NW) {
-        const int64_t row = (int64_t)h * (dn + dv) + j;
-        const float sc = GRP ? (live ? gload<float>(kb.s + row * kb.ng + c0 / kb.gs) : 0.f)
-                             : gload<float>(kb.s + row);
-        const uint32_t wd = live ? gload<uint32_t>(kb.q + row * kb.rb + c0 / 2) : 0x88888888u;
-        float f[8];
-        decode_nib_word(wd, f);  // 16 (nibble - 8)
+            for (int k = 0; k < 8; ++k) acc[s][k] = 0.f;
+        for (int jb = j0 + wave; jb < j1; jb += QA_NW * QA_RB) {
+            uint32_t wd[QA_RB];
+            float sc[QA_RB], qs[QA_RB][S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const float qs = gload<float>(q + (int64_t)s * nq + (int64_t)h * (dn + dr) + j) * sc *
-                             0.0625f;
+            for (int r = 0; r < QA_RB; ++r) {
+                const int j = min(jb + r * QA_NW, j1 - 1);
+                const int64_t row = (int64_t)h * (dn + dv) + j;
+                wd[r] = live ? gload<uint32_t>(kb.q + row * kb.rb + c0 / 2) : 0x88888888u;
+                sc[r] = GRP ? (live ? gload<float>(kb.s + row * kb.ng + c0 / kb.gs) : 0.f)
+                            : gload<float>(kb.s + row);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc[s][k] = fmaf(qs, f[k], acc[s][k]);
+                for (int s = 0; s < S; ++s) qs[r][s] = gload<float>(qh + (int64_t)s * nq + j);
+            }
+#pragma unroll
+            for (int r = 0; r < QA_RB; ++r) {
+                if (jb + r * QA_NW >= j1)
+                    break;
+                float f[8];
+                decode_nib_word(wd[r], f);  // 16 (nibble - 8)
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float w = qs[r][s] * sc[r] * 0.0625f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) acc[s][k] = fmaf(w, f[k], acc[s][k]);
+                }
+            }
         }
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) red[wave][s][8 * lane + k] = acc[s][k];
+        __syncthreads();
+        for (int idx = tid; idx < S * QA_COLS; idx += QA_NW * 64) {
+            const int s = idx / QA_COLS, c = idx % QA_COLS;
+            if (col0 + c < L) {
+                float v = red[0][s][c];
+#pragma unroll
+                for (int w = 1; w < QA_NW; ++w) v += red[w][s][c];
+                part[(((int64_t)split * S + s) * H + h) * L + col0 + c] = v;
+            }
+        }
+        __syncthreads();
     }
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) red[wave][s][8 * lane + k] = acc[s][k];
-    __syncthreads();
-    for (int idx = tid; idx < S * QA_COLS; idx += QA_NW * 64) {
-        const int s = idx / QA_COLS, c = idx % QA_COLS;
-        if (col0 + c >= L)
-            continue;
-        float v = red[0][s][c];
-#pragma unroll
-        for (int w = 1; w < QA_NW; ++w) v += red[w][s][c];
-        qabs[((int64_t)s * H + h) * L + col0 + c] = v;
-    }
-    if (blockIdx.y == 0)
+    if (split == 0)
         for (int idx = tid; idx < S * (dr / 2); idx += QA_NW * 64) {
             const int s = idx / (dr / 2), i = idx % (dr / 2);
             const float *qr = q + (int64_t)s * nq + (int64_t)h * (dn + dr) + dn;
@@ -151,120 +177,230 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
 }
 
 // ---- scores ----------------------------------------------------------------
-constexpr int SC_KEYS = 64;  // keys per workgroup (16 per wavefront)
+// Partial scores over one third of the L + d_rope components (Q = [qabs,
+// qpe], K = [Lc, Rc]): grid (64-key tiles, 4-head groups, row x MLA_SC_SPLIT).
+// A workgroup takes 4 heads (one per wavefront) x 64 keys (one per lane);
+// its components go through LDS in chunks of 64 (keys padded to 65 floats),
+// the next chunk's loads issued before the current one is used; each chunk is
+// summed on its own and then added.  The softmax kernel adds the splits in
+// order and scales.  qabs is the sum of the key-absorption partials, formed
+// while staging; the first key tile stores it.
+constexpr int SC_KEYS = 64;
+constexpr int SC_HEADS = 4;
+constexpr int SC_CH = 64;
 
-__global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ qabs,
+__global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ part,
                                                     const float *__restrict__ qpe,
                                                     const float *__restrict__ Lc,
-                                                    const float *__restrict__ Rc, int H, int L,
-                                                    int dr, int pos_base, int Tcap, float scale,
-                                                    float *__restrict__ scores) {
-    extern __shared__ float sq[];  // [L] qabs then [dr] qpe of this (row, head)
-    const int t0 = blockIdx.x * SC_KEYS, h = blockIdx.y, s = blockIdx.z;
+                                                    const float *__restrict__ Rc, int S, int H,
+                                                    int L, int dr, int pos_base, int Tcap,
+                                                    float *__restrict__ qabs,
+                                                    float *__restrict__ sc_part) {
+    __shared__ float kt[2][SC_KEYS][SC_CH + 1];
+    __shared__ float qt[2][SC_HEADS][SC_CH];
+    const int t0 = blockIdx.x * SC_KEYS, h0 = blockIdx.y * SC_HEADS;
+    const int s = blockIdx.z / MLA_SC_SPLIT, split = blockIdx.z % MLA_SC_SPLIT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int last = pos_base + s;  // keys 0 .. last
     if (t0 > last)
         return;
-    const float *qa = qabs + ((int64_t)s * H + h) * L;
-    const float *qp = qpe + ((int64_t)s * H + h) * dr;
-    for (int c = tid; c < L; c += 256) sq[c] = qa[c];
-    for (int r = tid; r < dr; r += 256) sq[L + r] = qp[r];
-    __syncthreads();
-    float *zrow = scores + ((int64_t)s * H + h) * Tcap;
-    const int tb = t0 + wave * (SC_KEYS / 4);
-    for (int k = 0; k < SC_KEYS / 4; ++k) {
-        const int t = tb + k;
-        if (t > last)
-            break;
-        const float *lr = Lc + (int64_t)t * L;
-        const float *rr = Rc + (int64_t)t * dr;
-        float a = 0.f;
-        for (int c = lane; c < L; c += 64) a = fmaf(sq[c], lr[c], a);
-        for (int r = lane; r < dr; r += 64) a = fmaf(sq[L + r], rr[r], a);
-        a = wave_sum(a);
-        if (lane == 0)
-            zrow[t] = a * scale;
+    const int C = L + dr;
+    const int nch_all = (C + SC_CH - 1) / SC_CH;
+    const int per = (nch_all + MLA_SC_SPLIT - 1) / MLA_SC_SPLIT;
+    const int ch0 = split * per, ch1 = min(nch_all, ch0 + per);
+    const int64_t pstride = (int64_t)S * H * L;
+    float kr[SC_KEYS * SC_CH / 256], qv;
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
+            const int idx = tid + 256 * i, key = idx / SC_CH, cc = idx % SC_CH;
+            const int t = t0 + key, c = c0 + cc;
+            float v = 0.f;
+            if (t <= last && c < C)
+                v = c < L ? Lc[(int64_t)t * L + c] : Rc[(int64_t)t * dr + (c - L)];
+            kr[i] = v;
+        }
+        const int hh = tid / SC_CH, cc = tid % SC_CH;  // 4 heads x 64 components
+        const int h = h0 + hh, c = c0 + cc;
+        float v = 0.f;
+        if (h < H && c < C) {
+            if (c < L) {
+                const float *pp = part + ((int64_t)s * H + h) * L + c;
+                v = pp[0];
+#pragma unroll
+                for (int k = 1; k < MLA_QA_SPLIT; ++k) v += pp[k * pstride];
+            } else {
+                v = qpe[((int64_t)s * H + h) * dr + (c - L)];
+            }
+        }
+        qv = v;
+    };
+    auto store = [&](int buf, int c0) {
+#pragma unroll
+        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
+            const int idx = tid + 256 * i;
+            kt[buf][idx / SC_CH][idx % SC_CH] = kr[i];
+        }
+        const int hh = tid / SC_CH, cc = tid % SC_CH;
+        qt[buf][hh][cc] = qv;
+        if (blockIdx.x == 0 && h0 + hh < H && c0 + cc < L)
+            qabs[((int64_t)s * H + h0 + hh) * L + c0 + cc] = qv;
+    };
+    float tot = 0.f;
+    if (ch0 < ch1) {
+        fetch(ch0 * SC_CH);
+        store(0, ch0 * SC_CH);
     }
+    __syncthreads();
+    for (int ch = ch0; ch < ch1; ++ch) {
+        const int buf = (ch - ch0) & 1;
+        if (ch + 1 < ch1)
+            fetch((ch + 1) * SC_CH);
+        float a = 0.f;
+#pragma unroll 16
+        for (int cc = 0; cc < SC_CH; ++cc) a = fmaf(qt[buf][wave][cc], kt[buf][lane][cc], a);
+        tot += a;
+        if (ch + 1 < ch1)
+            store(buf ^ 1, (ch + 1) * SC_CH);
+        __syncthreads();
+    }
+    const int t = t0 + lane, h = h0 + wave;
+    if (t <= last && h < H)
+        sc_part[(((int64_t)split * S + s) * H + h) * Tcap + t] = tot;
 }
 
 // ---- softmax and the latent context ----------------------------------------
-__device__ __forceinline__ float block_reduce_256(float v, float *buf, bool is_max) {
-    // fixed-order tree over the 256 threads (deterministic)
-    const int tid = threadIdx.x;
-    buf[tid] = v;
-    __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-        if (tid < off)
-            buf[tid] = is_max ? fmaxf(buf[tid], buf[tid + off]) : buf[tid] + buf[tid + off];
-        __syncthreads();
-    }
-    const float r = buf[0];
-    __syncthreads();
-    return r;
+// grid (64-key chunks, 64-column tiles, 4-head groups x rows).  Each wavefront
+// first forms its head's scores z_t = scale * (sum of the score splits in
+// order) over keys 0 .. pos_base + s and their softmax statistics (strided
+// max and sum of exp(z - max), then wavefront shuffles in a fixed order);
+// then its workgroup's chunk: p = exp(z - max) / sum for 64 keys in LDS, the
+// chunk's Lc rows in LDS, and the chunk's share of clat[h][c] = sum_t p Lc[t][c]
+// into its own partial.  The value-absorption kernel adds the partials in
+// chunk order.  Column tile 0 stores the chunk's scores and probabilities.
+constexpr int CL_COLS = 64;
+constexpr int CL_HEADS = 4;
+constexpr int CL_KEYS = 64;
+
+__device__ __forceinline__ float mla_score(const float *__restrict__ sc_part, int64_t sstride,
+                                           int64_t at, float scale) {
+    float z = sc_part[at];
+#pragma unroll
+    for (int k = 1; k < MLA_SC_SPLIT; ++k) z += sc_part[at + k * sstride];
+    return z * scale;
 }
 
-__global__ __launch_bounds__(256) void k_mla_softmax_clat(const float *__restrict__ scores,
-                                                          const float *__restrict__ Lc, int H, int L,
-                                                          int pos_base, int Tcap,
+__global__ __launch_bounds__(256) void k_mla_softmax_clat(const float *__restrict__ sc_part,
+                                                          const float *__restrict__ Lc, int S, int H,
+                                                          int L, int pos_base, int Tcap, float scale,
+                                                          float *__restrict__ scores,
                                                           float *__restrict__ p,
-                                                          float *__restrict__ clat) {
-    __shared__ float buf[256];
-    __shared__ float pl[256];
-    const int sh = blockIdx.x, s = sh / H;
-    const int tid = threadIdx.x;
+                                                          float *__restrict__ cl_part) {
+    __shared__ float lt[CL_KEYS][CL_COLS + 1];
+    __shared__ float pt[CL_HEADS][CL_KEYS];
+    const int chunk = blockIdx.x, t0 = chunk * CL_KEYS, c0 = blockIdx.y * CL_COLS;
+    const int ng = (H + CL_HEADS - 1) / CL_HEADS;
+    const int s = blockIdx.z / ng, h0 = (blockIdx.z % ng) * CL_HEADS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = pos_base + s + 1;
-    const float *z = scores + (int64_t)sh * Tcap;
-    float m = -__builtin_inff();
-    for (int t = tid; t < n; t += 256) m = fmaxf(m, z[t]);
-    m = block_reduce_256(m, buf, true);
-    float e = 0.f;
-    for (int t = tid; t < n; t += 256) e += expf(z[t] - m);
-    const float sum = block_reduce_256(e, buf, false);
-    const int c = blockIdx.y * 256 + tid;
-    float acc = 0.f;
-    for (int tb = 0; tb < n; tb += 256) {
-        const int t = tb + tid;
-        const float pv = t < n ? expf(z[t] - m) / sum : 0.f;
-        pl[tid] = pv;
-        if (blockIdx.y == 0 && t < n)
-            p[(int64_t)sh * Tcap + t] = pv;
-        __syncthreads();
-        if (c < L) {
-            const int nk = min(256, n - tb);
-            for (int k = 0; k < nk; ++k) acc = fmaf(pl[k], Lc[(int64_t)(tb + k) * L + c], acc);
-        }
-        __syncthreads();
+    if (t0 >= n)
+        return;
+    const int64_t sstride = (int64_t)S * H * Tcap;
+    // this chunk's Lc rows: requested first, they do not depend on the scores
+    float lr[CL_KEYS * CL_COLS / 256];
+#pragma unroll
+    for (int i = 0; i < CL_KEYS * CL_COLS / 256; ++i) {
+        const int idx = tid + 256 * i, tt = idx / CL_COLS, c = idx % CL_COLS;
+        const int t = t0 + tt;
+        lr[i] = (t < n && c0 + c < L) ? Lc[(int64_t)t * L + c0 + c] : 0.f;
     }
-    if (c < L)
-        clat[(int64_t)sh * L + c] = acc;
+    // softmax statistics of this wavefront's head
+    const int h = h0 + wave;
+    const int64_t zrow = ((int64_t)s * H + min(h, H - 1)) * Tcap;
+    float m = -__builtin_inff();
+    for (int t = lane; t < n; t += 64) m = fmaxf(m, mla_score(sc_part, sstride, zrow + t, scale));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float e = 0.f;
+    for (int t = lane; t < n; t += 64) e += expf(mla_score(sc_part, sstride, zrow + t, scale) - m);
+    e = wave_sum(e);
+    {
+        const int t = t0 + lane;
+        float pv = 0.f;
+        if (h < H && t < n) {
+            const float z = mla_score(sc_part, sstride, zrow + t, scale);
+            pv = expf(z - m) / e;
+            if (blockIdx.y == 0) {
+                scores[zrow + t] = z;
+                p[zrow + t] = pv;
+            }
+        }
+        pt[wave][lane] = pv;
+    }
+#pragma unroll
+    for (int i = 0; i < CL_KEYS * CL_COLS / 256; ++i) {
+        const int idx = tid + 256 * i;
+        lt[idx / CL_COLS][idx % CL_COLS] = lr[i];
+    }
+    __syncthreads();
+    float a = 0.f;
+#pragma unroll 16
+    for (int tt = 0; tt < CL_KEYS; ++tt) a = fmaf(pt[wave][tt], lt[tt][lane], a);
+    const int c = c0 + lane;
+    if (h < H && c < L)
+        cl_part[(((int64_t)chunk * S + s) * H + h) * L + c] = a;
 }
 
 // ---- value absorption --------------------------------------------------------
-constexpr int CX_ROWS = 16;  // value rows per workgroup (4 per wavefront)
+// ctx[h][v] = sum_c kv_b[h (dn+dv) + dn + v][c] clat[h][c]: a wavefront takes
+// 16 value rows, 4 lanes per row, each lane 16-byte loads (32 columns) of its
+// row at chunks q, q+4, ... (the 4 lanes of a row read 64 contiguous bytes);
+// clat of the head sits in LDS; the 4 lanes' sums are combined by two xor
+// shuffles.  Needs L % 32 == 0.
+constexpr int CX_ROWS = 64;  // value rows per workgroup (16 per wavefront)
 
 template <int S, bool GRP>
 __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int dv, int L,
-                                                 const float *__restrict__ clat,
+                                                 int pos_base, const float *__restrict__ cl_part,
+                                                 float *__restrict__ clat,
                                                  float *__restrict__ ctx) {
+    extern __shared__ __attribute__((aligned(16))) float cl[];  // [S][L]
     const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwd = L / 8;  // words of codes per row
-    for (int r = 0; r < CX_ROWS / 4; ++r) {
-        const int v = blockIdx.y * CX_ROWS + wave * (CX_ROWS / 4) + r;
-        if (v >= dv)
-            break;
-        const int64_t row = (int64_t)h * (dn + dv) + dn + v;
-        float part[S];
+    // clat = the key chunks' partials of row s, added in chunk order; the
+    // first row tile stores it
+    for (int i = tid; i < S * L; i += 256) {
+        const int s = i / L, c = i % L;
+        const int nchunk = (pos_base + s + 1 + CL_KEYS - 1) / CL_KEYS;
+        const float *pp = cl_part + ((int64_t)s * H + h) * L + c;
+        float v = pp[0];
+        for (int k = 1; k < nchunk; ++k) v += pp[(int64_t)k * S * H * L];
+        cl[i] = v;
+        if (blockIdx.y == 0)
+            clat[((int64_t)s * H + h) * L + c] = v;
+    }
+    __syncthreads();
+    const int v = blockIdx.y * CX_ROWS + wave * 16 + (lane >> 2);
+    const int q = lane & 3;
+    const bool live = v < dv;
+    const int64_t row = (int64_t)h * (dn + dv) + dn + min(v, dv - 1);
+    const int nch = L / 32;
+    float part[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) part[s] = 0.f;
-        for (int wd = lane; wd < nwd; wd += 64) {
-            const int c0 = 8 * wd;
-            const float sc = GRP ? gload<float>(kb.s + row * kb.ng + c0 / kb.gs) : 1.f;
+    for (int s = 0; s < S; ++s) part[s] = 0.f;
+    for (int ch = q; ch < nch; ch += 4) {
+        const u32x4 w4 = live ? gload<u32x4>(kb.q + row * kb.rb + 16 * ch)
+                              : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        const uint32_t wds[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = 32 * ch + 8 * k;
+            const float sc = GRP ? gload<float>(kb.s + row * kb.ng + c / kb.gs) : 1.f;
             float f[8];
-            decode_nib_word(gload<uint32_t>(kb.q + row * kb.rb + c0 / 2), f);
+            decode_nib_word(wds[k], f);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const float *cl = clat + ((int64_t)s * H + h) * L + c0;
-                const f32x4 a = gload<f32x4>(cl), b = gload<f32x4>(cl + 4);
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(cl + s * L + c);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(cl + s * L + c + 4);
                 float d = f[0] * a.x;
                 d = fmaf(f[1], a.y, d); d = fmaf(f[2], a.z, d); d = fmaf(f[3], a.w, d);
                 d = fmaf(f[4], b.x, d); d = fmaf(f[5], b.y, d); d = fmaf(f[6], b.z, d);
@@ -272,13 +408,14 @@ __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int d
                 part[s] = fmaf(sc, d, part[s]);
             }
         }
-        const float rs = GRP ? 0.0625f : gload<float>(kb.s + row) * 0.0625f;
+    }
+    const float rs = GRP ? 0.0625f : gload<float>(kb.s + row) * 0.0625f;
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const float tot = wave_sum(part[s]);
-            if (lane == 0)
-                ctx[(int64_t)s * H * dv + (int64_t)h * dv + v] = tot * rs;
-        }
+    for (int s = 0; s < S; ++s) {
+        float t = part[s] + __shfl_xor(part[s], 1, 4);
+        t += __shfl_xor(t, 2, 4);
+        if (q == 0 && live)
+            ctx[(int64_t)s * H * dv + (int64_t)h * dv + v] = t * rs;
     }
 }
 
@@ -304,6 +441,9 @@ MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tc
     l.off[MLA_P] = take((size_t)S * H * Tcap);
     l.off[MLA_CLAT] = take((size_t)S * H * L);
     l.off[MLA_CTX] = take((size_t)S * H * dv);
+    l.qabs_part = take((size_t)MLA_QA_SPLIT * S * H * L);
+    l.sc_part = take((size_t)MLA_SC_SPLIT * S * H * Tcap);
+    l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * S * H * L);
     l.total = o;
     return l;
 }
@@ -345,47 +485,55 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     float *p = (float *)(ws + l.off[MLA_P]);
     float *clat = (float *)(ws + l.off[MLA_CLAT]);
     float *ctx = (float *)(ws + l.off[MLA_CTX]);
+    float *part = (float *)(ws + l.qabs_part);
+    float *sc_part = (float *)(ws + l.sc_part);
+    float *cl_part = (float *)(ws + l.cl_part);
     const double theta = (double)m.rope_theta;
     {
         ProfScope ps("mla_qabs", st);
-        const dim3 grid((unsigned)H, (unsigned)((L + QA_COLS - 1) / QA_COLS));
+        const dim3 grid((unsigned)H, (unsigned)MLA_QA_SPLIT);
         if (grp)
             hipLaunchKernelGGL((k_mla_qabs<S, true>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn, dr,
-                               dv, L, q, a.pos_base, theta, qabs, qpe);
+                               dv, L, q, a.pos_base, theta, part, qpe);
         else
             hipLaunchKernelGGL((k_mla_qabs<S, false>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn,
-                               dr, dv, L, q, a.pos_base, theta, qabs, qpe);
+                               dr, dv, L, q, a.pos_base, theta, part, qpe);
         const int rc = after_launch("mla_qabs");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_scores", st);
         const int nkeys = a.pos_base + S;
-        const dim3 grid((unsigned)((nkeys + SC_KEYS - 1) / SC_KEYS), (unsigned)H, (unsigned)S);
-        const float scale = (float)(1.0 / sqrt((double)(dn + dr)));
-        hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), (size_t)(L + dr) * sizeof(float), st,
-                           (const float *)qabs, (const float *)qpe, (const float *)a.Lc,
-                           (const float *)a.Rc, H, L, dr, a.pos_base, a.T_cap, scale, sc);
+        const dim3 grid((unsigned)((nkeys + SC_KEYS - 1) / SC_KEYS),
+                        (unsigned)((H + SC_HEADS - 1) / SC_HEADS), (unsigned)(S * MLA_SC_SPLIT));
+        hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
+                           (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, S, H, L,
+                           dr, a.pos_base, a.T_cap, qabs, sc_part);
         const int rc = after_launch("mla_scores");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_softmax_clat", st);
-        const dim3 grid((unsigned)(S * H), (unsigned)((L + 255) / 256));
-        hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc,
-                           (const float *)a.Lc, H, L, a.pos_base, a.T_cap, p, clat);
+        const int nkeys = a.pos_base + S;
+        const float scale = (float)(1.0 / sqrt((double)(dn + dr)));
+        const dim3 grid((unsigned)((nkeys + CL_KEYS - 1) / CL_KEYS),
+                        (unsigned)((L + CL_COLS - 1) / CL_COLS),
+                        (unsigned)(S * ((H + CL_HEADS - 1) / CL_HEADS)));
+        hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
+                           (const float *)a.Lc, S, H, L, a.pos_base, a.T_cap, scale, sc, p, cl_part);
         const int rc = after_launch("mla_softmax_clat");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_ctx", st);
         const dim3 grid((unsigned)H, (unsigned)((dv + CX_ROWS - 1) / CX_ROWS));
+        const size_t lds = (size_t)S * L * sizeof(float);
         if (grp)
-            hipLaunchKernelGGL((k_mla_ctx<S, true>), grid, dim3(256), 0, st, kb, H, dn, dv, L,
-                               (const float *)clat, ctx);
+            hipLaunchKernelGGL((k_mla_ctx<S, true>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
+                               a.pos_base, (const float *)cl_part, clat, ctx);
         else
-            hipLaunchKernelGGL((k_mla_ctx<S, false>), grid, dim3(256), 0, st, kb, H, dn, dv, L,
-                               (const float *)clat, ctx);
+            hipLaunchKernelGGL((k_mla_ctx<S, false>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
+                               a.pos_base, (const float *)cl_part, clat, ctx);
         const int rc = after_launch("mla_ctx");
         if (rc != COLI_OK) return rc;
     }

@@ -425,7 +425,8 @@ int coli_moe_layer(const coli_qtensor *gate, const coli_qtensor *up, const coli_
  * RoPE turns consecutive pairs (2i, 2i+1) by pos * rope_theta^(-2i/d_rope);
  * RMSNorm is x / sqrt(mean x^2 + eps) * w; the softmax scale is
  * 1/sqrt(d_nope + d_rope).  All five matrices are single coli_qtensors (any
- * format for the projections; kv_b fmt 4 with gs % 8 == 0, or fmt 2).
+ * format for the projections; kv_b fmt 4 with gs % 8 == 0, or fmt 2, latent
+ * width L a multiple of 32 up to 4096, codes 16-byte aligned).
  */
 typedef struct coli_mla_layer {
     const coli_qtensor *q_a, *q_b, *kv_a, *kv_b, *o_proj;
