@@ -382,3 +382,67 @@ def test_moe_two_phase_repeatable_and_declines(orc):
         coli.COLI_DECLINED
     torch.cuda.synchronize()
     assert torch.all(out == 5.0)
+
+
+def test_moe_two_phase_overlapped_upload(orc):
+    """The two-phase block as the pages use it: the late experts' weights
+    (codes, scales and the packed copy the decode kernels read) are not on the
+    device when begin is enqueued; they are copied from pinned host memory on
+    a second stream while begin runs, and end waits for the copies through an
+    event.  The result is bit-identical to the same two submissions run after
+    the copies have finished, and within the block's bound of the oracle."""
+    need_gpu()
+    S, K, E, D, F, gs = 1, 8, 16, 1024, 512, 64
+    G, U, Dn, sh, x, ids, w = _moe_inputs(931, 4, S, K, E, D, F, gs, True)
+    late = np.zeros((S, K), np.int32)
+    late[0, 1::2] = 1
+    late_e = sorted(set(int(e) for e in ids[0, 1::2]))
+    tg, tu, td = qtensor(G, True), qtensor(U, True), qtensor(Dn, True)
+    ts = [qtensor(m, True) for m in sh]
+    xd, idd, wd = to_dev(x), to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32))
+    ld = to_dev(late)
+    wsb = coli.coli_moe_block_two_phase_workspace_bytes(E, S, K, F, D, True)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    # the late experts' device slices: original codes, scales, packed copy
+    def slices(T):
+        d = T.desc
+        out = []
+        for e in late_e:
+            out.append(T.q[e])
+            out.append(T.s[e])
+            out.append(T.packed[e * d.pk_stride:(e + 1) * d.pk_stride])
+        return out
+    dev_sl = [t for T in (tg, tu, td) for t in slices(T)]
+    host = [torch.empty(t.shape, dtype=t.dtype, pin_memory=True) for t in dev_sl]
+    for h_, d_ in zip(host, dev_sl):
+        h_.copy_(d_)
+    torch.cuda.synchronize()
+
+    def run(overlap):
+        for d_ in dev_sl:   # not loaded yet
+            d_.zero_()
+        out = torch.full((S, D), float("nan"), device="cuda")
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(main)
+        if not overlap:
+            for h_, d_ in zip(host, dev_sl):
+                d_.copy_(h_)
+        coli.check(coli.coli_moe_block_begin(tg, tu, td, xd, S, idd, wd, K, ld, ts[0], ts[1],
+                                             ts[2], out, ws, wsb, main), "begin")
+        if overlap:
+            with torch.cuda.stream(side):
+                for h_, d_ in zip(host, dev_sl):
+                    d_.copy_(h_, non_blocking=True)
+                ev = torch.cuda.Event()
+                ev.record(side)
+            main.wait_event(ev)
+        coli.check(coli.coli_moe_block_end(tg, tu, td, xd, S, wd, K, True, out, ws, wsb, main),
+                   "end")
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+    serial = run(False)
+    overlapped = run(True)
+    assert np.array_equal(serial.view(np.uint32), overlapped.view(np.uint32))
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, overlapped, None, TOL_FP32)
