@@ -140,6 +140,31 @@ def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None, rep=Fal
     assert np.all(err <= bound + 1e-30), f"end to end: max err/bound = {np.max(err / bound):.3e}"
 
 
+# S = 1 with long expert rows (F up to 2048) and every scale-slot count
+DECODE_LONG_F = [  # (fmt, S, K, E, D, F, gs, shared)
+    (4, 1, 8, 16, 256, 512, 64, True),
+    (4, 1, 8, 16, 512, 2048, 64, False),
+    (4, 1, 5, 9, 160, 1024, 32, True),      # gs 32: four scale slots per block
+    (4, 1, 3, 7, 96, 1536, 128, True),      # gs 128: one slot
+    (2, 1, 4, 8, 256, 512, 0, True),        # per-row scales
+    (4, 1, 16, 40, 128, 512, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_LONG_F,
+                         ids=["fmt{}-S{}-K{}-E{}-D{}-F{}-gs{}-sh{}".format(*c) for c in DECODE_LONG_F])
+def test_moe_decode_long_rows_with_bad_ids(orc, case):
+    need_gpu()
+    fmt, S, K, E, D, F, gs, shared = case
+    G, U, Dn, sh, x, ids, w = _moe_inputs(1500 + K + E + F, fmt, S, K, E, D, F, gs, shared)
+    if K >= 5:  # an invalid id and a duplicate among the picks
+        ids = ids.copy()
+        ids[0, 1] = E + 3
+        ids[0, 3] = ids[0, 2]
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_FP32)
+
+
 DECODE = [  # (fmt, S, K, E, D, F, gs, shared)
     (4, 1, 8, 16, 256, 128, 64, False),
     (4, 1, 8, 16, 256, 128, 64, True),
