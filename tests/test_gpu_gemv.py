@@ -201,6 +201,20 @@ def test_qmatmul_attention_projection_shapes(orc, O, I, pack):
     assert_within(y, y_ref, A, TOL_FP32, f"proj {O}x{I}")
 
 
+@pytest.mark.parametrize("fmt,gs,S", [(4, 64, 1), (4, 64, 2), (4, 32, 3), (4, 128, 4), (1, 0, 2),
+                                      (3, 0, 4), (2, 0, 1)])
+def test_qmatmul_long_rows_several_input_segments(orc, fmt, gs, S):
+    """Rows of 17056 inputs (a partial last group at gs 64): the matrix-core
+    kernel stages the inputs in two or three segments, the next segment's
+    first weight requests going out before its restaging."""
+    need_gpu()
+    W, x = make_case(fmt, 200, 17056, gs, S, seed=40 + fmt + gs + S)
+    y = gpu_qmatmul(qtensor(W, pack=True), x)[0]
+    y_ref, A = orc.qmatmul(W, x)
+    assert_within(y, y_ref, A, TOL_FP32, f"long rows fmt {fmt} gs {gs} S {S}",
+                  rep_allowance(orc, W, x))
+
+
 def test_qmatmul_repeatable_bitwise(orc):
     need_gpu()
     W, x = make_case(4, 3000, 6144, 64, 3, seed=9)
