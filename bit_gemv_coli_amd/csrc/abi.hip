@@ -756,9 +756,8 @@ static int launch_moe_layer(const coli_qtensor *gate, const coli_qtensor *up,
     int32_t *ids = (int32_t *)(ws + l.ids);
     float *w = (float *)(ws + l.w);
     float *y = (float *)(ws + l.y);
-    int rc = launch_rmsnorm(h, S, D, ln_w, (double)eps, xn, st);
-    if (rc != COLI_OK) return rc;
-    rc = launch_router(xn, S, D, R, bias, E, K, topp, norm_topk, routed_scale, ids, w, ws + l.rt, st);
+    int rc = launch_norm_router(h, S, D, ln_w, (double)eps, xn, R, bias, E, K, topp, norm_topk,
+                                routed_scale, ids, w, ws + l.rt, st);
     if (rc != COLI_OK) return rc;
     MoeArgs a;
     a.gate = gate; a.up = up; a.down = down;
@@ -766,7 +765,12 @@ static int launch_moe_layer(const coli_qtensor *gate, const coli_qtensor *up,
     a.x = xn; a.S = S; a.K = K; a.E = E; a.F = F; a.D = D;
     a.ids = ids; a.w = w; a.out = y; a.h_out = nullptr;
     a.ws = ws + l.blk; a.ws_bytes = ws_bytes - l.blk; a.st = st;
-    rc = S <= coli_gemv_max_rows() ? launch_moe_decode(a) : launch_moe_prefill(a);
+    if (S <= coli_gemv_max_rows()) {
+        a.resid = h;  // out = h + y in the block's combine
+        a.out_res = out;
+        return launch_moe_decode(a);
+    }
+    rc = launch_moe_prefill(a);
     if (rc != COLI_OK) return rc;
     return launch_residual_add(h, y, out, (int64_t)S * D, st);
 }
@@ -978,11 +982,13 @@ int coli_layer_decode(const coli_mla_layer *attn, const float *in_ln, const coli
     float *xn = (float *)(ws + f.off[0]);
     float *a = (float *)(ws + f.off[1]);
     float *hh = (float *)(ws + f.off[2]);
-    int rc = launch_rmsnorm(x, S, D, in_ln, (double)eps, xn, st);
-    if (rc != COLI_OK) return rc;
     MlaArgs m;
     m.layer = attn;
-    m.x = xn;
+    m.x = x;
+    m.in_norm = true;  // xn = in_ln RMSNorm of x, folded into q_a / kv_a when it can be
+    m.in_norm_w = in_ln;
+    m.in_eps = (double)eps;
+    m.xn = xn;
     m.S = S;
     m.pos_base = pos_base;
     m.T_cap = T_cap;
@@ -991,9 +997,9 @@ int coli_layer_decode(const coli_mla_layer *attn, const float *in_ln, const coli
     m.out = a;
     m.ws = ws + f.off[3];
     m.st = st;
-    rc = launch_mla_decode(m);
-    if (rc != COLI_OK) return rc;
-    rc = launch_residual_add(x, a, hh, (int64_t)S * D, st);
+    m.resid = x;  // h = x + a in o_proj's epilogue
+    m.hsum = hh;
+    const int rc = launch_mla_decode(m);
     if (rc != COLI_OK) return rc;
     const LayerWs l = layer_ws(gate->n, S, K, gate->O, D, sh_gate != nullptr);
     return launch_moe_layer(gate, up, down, hh, S, post_ln, eps, R, bias, K, topp, norm_topk,

@@ -50,7 +50,18 @@ __host__ __device__ constexpr int packet_cols(int fmt) { return fmt == 1 ? 16 : 
 
 // Launchers (defined in gemv.hip / gemm.hip / route.hip).
 int launch_dequant(const coli_qtensor *W, float *w, hipStream_t st);
-int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
+// y = W x; with radd and ysum also ysum = radd + y (a residual add, in the
+// matrix-core kernel's epilogue when that kernel runs)
+int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st,
+                const float *radd = nullptr, float *ysum = nullptr);
+// an RMSNorm applied to a GEMV's input rows as they are staged: x * inv * w
+// (w may be NULL: 1), inv = 1 / sqrt(mean x^2 + eps) per row in f64; the
+// normalised rows [S][I] are written to xn
+struct InNorm {
+    const float *w;
+    double eps;
+    float *xn;
+};
 int launch_gemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws, size_t ws_bytes,
                 hipStream_t st);
 size_t gemm_workspace_bytes(int S, int I);
@@ -71,6 +82,11 @@ struct MoeArgs {
     void *ws;
     size_t ws_bytes;
     hipStream_t st;
+    // decode layer: also out_res = resid + out (the residual add), folded
+    // into the combine when the matrix-core kernels run, else a launch of its
+    // own (S <= 4 only)
+    const float *resid = nullptr;
+    float *out_res = nullptr;
 };
 int launch_moe_decode(const MoeArgs &a);
 int launch_moe_prefill(const MoeArgs &a);
@@ -79,15 +95,20 @@ size_t router_ws_bytes(int S, int E);
 int launch_router(const float *x, int S, int D, const float *R, const float *bias, int E, int K,
                   float topp, int norm_topk, float routed_scale, int32_t *ids, float *w, void *ws,
                   hipStream_t st);
+// RMSNorm (weights lnw, may be NULL) of h into xn, then the router on xn
+int launch_norm_router(const float *h, int S, int D, const float *lnw, double eps, float *xn,
+                       const float *R, const float *bias, int E, int K, float topp, int norm_topk,
+                       float routed_scale, int32_t *ids, float *w, void *ws, hipStream_t st);
 size_t moe_decode_ws_bytes(int S, int K, int F, int D, int has_shared);
 // matrix-core decode kernels (mgemv.hip); return 1 done, 0 not taken, <0 error
 bool mgemv_ok(const coli_qtensor *W);
 bool mgemv_int4_ok(const coli_qtensor *W);
 size_t packed_bytes(int fmt, int n, int O, int I, int gs);
 int launch_pack(coli_qtensor *t, void *packed, hipStream_t st);
-int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
+int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st,
+                 const float *radd = nullptr, float *ysum = nullptr, const InNorm *nrm = nullptr);
 int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *x,
-                       float *const *y, int S, hipStream_t st);
+                       float *const *y, int S, hipStream_t st, const InNorm *nrm = nullptr);
 int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt);
 // prefill GEMM on the matrix cores for the int4 formats (pgemm.hip); 1 done,
 // 0 not taken, <0 error

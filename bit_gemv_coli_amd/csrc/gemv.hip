@@ -23,6 +23,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "layer.h"
 
 namespace coli {
 
@@ -476,7 +477,29 @@ static int group_mode(const coli_qtensor *const *ts, int n) {
 
 // y = W x for S input rows.  Packet kernels take up to 4 input rows per
 // launch (larger S is split into blocks of 4); the fallback takes any S.
-int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st) {
+static int launch_gemv_y(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st);
+
+int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st,
+                const float *radd, float *ysum) {
+    if (ysum == nullptr)
+        return launch_gemv_y(W, x, y, S, st);
+    const bool fast = (W->flags & QF_FAST) &&
+                      (W->fmt != 4 || (W->flags & (QF_GROUP32 | QF_GROUP16))) &&
+                      ((uintptr_t)x % 16 == 0);
+    if (fast && S <= 4 && decode_kernel_mode() == 0) {
+        const int r = launch_mgemv(W, x, y, S, st, radd, ysum);
+        if (r == 1)
+            return COLI_OK;
+        if (r < 0)
+            return COLI_HIP_ERROR;
+    }
+    const int rc = launch_gemv_y(W, x, y, S, st);
+    if (rc != COLI_OK)
+        return rc;
+    return launch_residual_add(radd, y, ysum, (int64_t)S * W->n * W->O, st);
+}
+
+static int launch_gemv_y(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st) {
     const int rows = W->n * W->O;
     const bool fast = (W->flags & QF_FAST) &&
                       (W->fmt != 4 || (W->flags & (QF_GROUP32 | QF_GROUP16))) &&
@@ -648,7 +671,7 @@ int launch_moe_decode(const MoeArgs &a) {
     if (rc < 0)
         return COLI_HIP_ERROR;
     if (rc == 1)
-        return COLI_OK;
+        return COLI_OK;  // (the residual add, if asked for, is in the combine)
     {
         switch (a.gate->fmt) {
         case 1: rc = moe_decode_t<1, 0>(a, h, yp); break;
@@ -663,7 +686,10 @@ int launch_moe_decode(const MoeArgs &a) {
     }
     if (a.out == nullptr || a.down == nullptr)
         return COLI_OK;
-    return moe_combine(a, yp);
+    rc = moe_combine(a, yp);
+    if (rc != COLI_OK || a.resid == nullptr)
+        return rc;
+    return launch_residual_add(a.resid, a.out, a.out_res, (int64_t)a.S * a.D, a.st);
 }
 
 }  // namespace coli

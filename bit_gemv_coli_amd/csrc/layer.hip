@@ -5,61 +5,38 @@
 //                   strided share, wavefront sums, then the four wavefronts in
 //                   order), inv = 1 / sqrt(ms + eps) in f64, every output the
 //                   f32 rounding of x * inv * w computed in f64;
-//   k_residual_add  out = h + y elementwise (out may be h).
+//   k_residual_add  out = h + y elementwise (out may be h) -- where the
+//                   producer of y is not a matrix-core decode kernel, which
+//                   adds the residual in its own epilogue.
 #include "common.h"
 #include "layer.h"
+#include "rms.h"
 
 namespace coli {
-
-__device__ __forceinline__ double ly_shfl_xor(double v, int m) {
-    const int2 p = __builtin_bit_cast(int2, v);
-    int2 q;
-    q.x = __shfl_xor(p.x, m);
-    q.y = __shfl_xor(p.y, m);
-    return __builtin_bit_cast(double, q);
-}
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, int D,
                                                  const float *__restrict__ w, double eps,
                                                  float *__restrict__ y) {
     __shared__ double part[4];
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int t = threadIdx.x;
     const float *xr = x + (int64_t)blockIdx.x * D;
     float *yr = y + (int64_t)blockIdx.x * D;
-    double ss = 0.0;
-    if constexpr (VEC) {
-        for (int d = 4 * t; d < D; d += 1024) {
-            const f32x4 v = gload<f32x4>(xr + d);
-            ss = fma((double)v.x, (double)v.x, ss);
-            ss = fma((double)v.y, (double)v.y, ss);
-            ss = fma((double)v.z, (double)v.z, ss);
-            ss = fma((double)v.w, (double)v.w, ss);
-        }
-    } else {
-        for (int d = t; d < D; d += 256) ss = fma((double)xr[d], (double)xr[d], ss);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += ly_shfl_xor(ss, m);
-    if (lane == 0)
-        part[wv] = ss;
-    __syncthreads();
-    const double tot = ((part[0] + part[1]) + part[2]) + part[3];
-    const double inv = 1.0 / sqrt(tot / (double)D + eps);
+    const double inv = row_rms_inv<VEC>(xr, D, eps, part);
     if constexpr (VEC) {
         for (int d = 4 * t; d < D; d += 1024) {
             const f32x4 v = gload<f32x4>(xr + d);
             const f32x4 g = w ? gload<f32x4>(w + d) : f32x4{1.f, 1.f, 1.f, 1.f};
             f32x4 o;
-            o.x = (float)((double)v.x * inv * (double)g.x);
-            o.y = (float)((double)v.y * inv * (double)g.y);
-            o.z = (float)((double)v.z * inv * (double)g.z);
-            o.w = (float)((double)v.w * inv * (double)g.w);
+            o.x = rms_apply(v.x, inv, g.x);
+            o.y = rms_apply(v.y, inv, g.y);
+            o.z = rms_apply(v.z, inv, g.z);
+            o.w = rms_apply(v.w, inv, g.w);
             *(f32x4 *)(yr + d) = o;
         }
     } else {
         for (int d = t; d < D; d += 256)
-            yr[d] = (float)((double)xr[d] * inv * (w ? (double)w[d] : 1.0));
+            yr[d] = rms_apply(xr[d], inv, w ? w[d] : 1.0f);
     }
 }
 

@@ -47,6 +47,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
+#include "rms.h"
 
 namespace coli {
 
@@ -76,7 +77,9 @@ __device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, u
     out[3] = __builtin_amdgcn_perm(cd1, ab1, 0x07060302u);
 }
 
-enum { MG_Y = 0, MG_SILU = 1, MG_PART = 2 };
+// epilogues: y; SiLU(gate) * up; partial rows for the combine; y with the
+// input rows RMS-normalised as they are staged (MG_YN)
+enum { MG_Y = 0, MG_SILU = 1, MG_PART = 2, MG_YN = 3 };
 
 // one member of a grouped GEMV: a single packed matrix, its input rows and
 // its output rows
@@ -118,6 +121,15 @@ struct MgArgs {
     const float *wts;
     float *yfin;
     int has_sh;
+    // residual add (single-matrix MG_Y, and the combine): yres = radd + y,
+    // same [S][O] layout as the output
+    const float *radd;
+    float *yres;
+    // MG_YN: norm weights (NULL: 1), eps, and where workgroup (0, 0) writes
+    // the normalised input rows [Sy][I]
+    const float *nw;
+    double neps;
+    float *nxo;
     // grouped GEMV (ngrp > 0, MG_Y only): independent matrices with their own
     // inputs and outputs in one launch; workgroups from grp[g].wg0 on belong
     // to member g
@@ -198,6 +210,8 @@ __device__ __forceinline__ void mg_combine_tail(const MgArgs &a) {
         if (a.has_sh)
             acc += load_coherent(a.out + ((int64_t)a.S * K + s) * O + row);
         a.yfin[(int64_t)s * O + row] = acc;
+        if (a.yres != nullptr)
+            a.yres[(int64_t)s * O + row] = a.radd[(int64_t)s * O + row] + acc;
     }
 }
 
@@ -279,6 +293,8 @@ static_assert(COLI_MG_NW_WIDE / COLI_MG_KS_WIDE == COLI_MG_NW_WIDE1 / COLI_MG_KS
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
 constexpr int MG_NBK = 4;
+// groups of 8 inputs per thread in one input staging step
+constexpr int MG_UN = 4;
 // buffer resource word 3 for raw (untyped) buffer loads; reads past
 // num_records return zeros
 constexpr int MG_RSRC_W3 = 0x00020000;
@@ -298,6 +314,7 @@ template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int N
 __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     static_assert(NW % KS == 0, "whole tiles per workgroup");
     static_assert(QB == 4 || ((QB == 8 || QB == 2) && !GROUPED && EPI == MG_Y), "code width");
+    constexpr bool YOUT = EPI == MG_Y || EPI == MG_YN;
     constexpr int LB = 4 * QB;   // code bytes per lane and 128-input block
     constexpr int BLK = 64 * LB; // bytes per 16-row x 128-input tile block
     constexpr int TPW = NW / KS;
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile_w = wave / KS, ks = wave % KS;
     int bx = blockIdx.x;
-    if constexpr (EPI == MG_Y) {
+    if constexpr (YOUT) {
         if (a.ngrp > 0) {
             // this workgroup's member (constant indices only, so the
             // arguments stay in scalar registers)
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     // inputs of one staging step: UN groups of 8 per thread.  The first step's
     // loads are issued here, ahead of every weight request (loads complete in
     // order), so the staging overlaps the first weight batches.
-    constexpr int UN = 4;
+    constexpr int UN = MG_UN;
     const int kpad = (I + 127) / 128 * 128;
     float xv[UN][8];
     auto stage_load = [&](int k0, int nb8, int base) {
@@ -610,6 +627,69 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
             }
         }
     };
+    // MG_YN: the first staging step holds every input of the NT rows (the
+    // host checks NT * nb8 <= UN * NTH and one segment).  Each row's f64 sum
+    // of squares (per thread, wavefront sums, wavefronts in order -- the same
+    // in every workgroup of the launch), then x * inv * w in place;
+    // workgroup (0, 0) also writes the normalised rows out.
+    auto prenorm = [&](int nb8) {
+        double ssq[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) ssq[t] = 0.0;
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int idx = u * NTH + tid;
+            if (idx < NT * nb8) {
+                double s2 = 0.0;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) s2 = fma((double)xv[u][w], (double)xv[u][w], s2);
+                const int t = idx / nb8;
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) ssq[tt] += (tt == t) ? s2 : 0.0;
+            }
+        }
+        double *nred = reinterpret_cast<double *>(red);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            double v = ssq[tt];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) v += rms_shfl_xor(v, m);
+            if (lane == 0)
+                nred[wave * NT + tt] = v;
+        }
+        __syncthreads();
+        double inv[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            double tot = 0.0;
+            for (int w2 = 0; w2 < NW; ++w2) tot += nred[w2 * NT + tt];
+            inv[tt] = 1.0 / sqrt(tot / (double)I + a.neps);
+        }
+        const bool wr = a.nxo != nullptr && blockIdx.x == 0 && blockIdx.y == 0;
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int idx = u * NTH + tid;
+            const int t = idx / nb8, k = (idx % nb8) * 8;
+            if (idx < NT * nb8 && k < I) {  // I % 8 == 0: all 8 inputs are real
+                f32x4 g0{1.f, 1.f, 1.f, 1.f}, g1{1.f, 1.f, 1.f, 1.f};
+                if (a.nw != nullptr) {
+                    g0 = gload<f32x4>(a.nw + k);
+                    g1 = gload<f32x4>(a.nw + k + 4);
+                }
+                double iv = inv[0];
+#pragma unroll
+                for (int tt = 1; tt < NT; ++tt) iv = (tt == t) ? inv[tt] : iv;
+                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+                for (int w = 0; w < 8; ++w) xv[u][w] = rms_apply(xv[u][w], iv, g[w]);
+                if (wr) {
+                    float *o = a.nxo + (int64_t)t * I + k;
+                    *reinterpret_cast<f32x4 *>(o) = f32x4{xv[u][0], xv[u][1], xv[u][2], xv[u][3]};
+                    *reinterpret_cast<f32x4 *>(o + 4) = f32x4{xv[u][4], xv[u][5], xv[u][6], xv[u][7]};
+                }
+            }
+        }
+    };
     // LDS hand-over between the wavefronts (no wait on outstanding loads)
     auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
@@ -627,6 +707,8 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
 #endif
+        if constexpr (EPI == MG_YN)
+            prenorm(nb8);
         stage_store(nb8, 0);
         for (int base = UN * NTH; base < NT * nb8; base += UN * NTH) {
             stage_load(0, nb8, base);
@@ -724,7 +806,10 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
             else
                 a.out[p * O + row] = v[0];
         } else {
-            a.out[(p * a.Sy + t) * O + row] = v[0];
+            const int64_t oi = (p * a.Sy + t) * O + row;
+            a.out[oi] = v[0];
+            if (a.yres != nullptr)
+                a.yres[oi] = a.radd[oi] + v[0];
         }
     }
     if constexpr (EPI == MG_PART) {
@@ -988,10 +1073,28 @@ static int mg_dispatch_cb(int cb, const MgArgs &a, int groups, hipStream_t st, c
     }
 }
 
+// Whether an input RMSNorm folds into a launch of NW-wavefront workgroups on
+// the int4 formats: the S rows fit one staging step of one segment.
+static bool prenorm_fits(const InNorm *nrm, const coli_qtensor *W, int S, int NW) {
+    if (!nrm || !nrm->xn || (uintptr_t)nrm->xn % 16 != 0 || (uintptr_t)nrm->w % 16 != 0 ||
+        W->I % 8 != 0 || !(W->fmt == 2 || W->fmt == 4) || !(nrm->eps >= 0.0))
+        return false;
+    int kseg, nseg;
+    size_t lds;
+    plan_lds(S, cb_of(W), 1, NW, W->I, kseg, nseg, lds);
+    const int kpad = (W->I + 127) / 128 * 128;
+    return nseg == 1 && (int64_t)S * (std::min(kseg, kpad) / 8) <= (int64_t)MG_UN * NW * 64;
+}
+
 // Dense GEMV y[e][t][o] for S <= 4 input rows.  Returns 0 when the layout or
 // (S, gs) combination is not taken (caller falls back to the VALU kernels).
-int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st) {
+// radd / ysum: also ysum = radd + y (one matrix); nrm: the input rows
+// RMS-normalised first (int4 formats, rows that fit one staging step).
+int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st,
+                 const float *radd, float *ysum, const InNorm *nrm) {
     if (!mgemv_ok(W) || S < 1 || S > 4)
+        return 0;
+    if ((radd != nullptr) != (ysum != nullptr) || (ysum != nullptr && W->n != 1))
         return 0;
     const int cb = cb_of(W);
     MgArgs a = mg_args_for(W);
@@ -999,7 +1102,27 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
     a.ldx = W->I;
     a.out = y;
     a.Sy = S;
+    a.radd = radd;
+    a.yres = ysum;
     const bool g = W->fmt == 4;
+    if (nrm != nullptr) {
+        if (!prenorm_fits(nrm, W, S, COLI_MG_NW_DENSE))
+            return 0;
+        a.nw = nrm->w;
+        a.neps = nrm->eps;
+        a.nxo = nrm->xn;
+        ProfScope ps("mgemv", st, true);
+        switch (S) {
+#define MG_NCASE(NTV)                                                                               \
+    case NTV:                                                                                       \
+        if (g) mg_dispatch_cb<NTV, true, 1, MG_YN, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps); \
+        else mg_dispatch_cb<NTV, false, 1, MG_YN, COLI_MG_KS_DENSE, COLI_MG_NW_DENSE, COLI_MG_NBQ_DENSE>(cb, a, W->n, st, ps); \
+        break;
+        MG_NCASE(1) MG_NCASE(2) MG_NCASE(3) default: MG_NCASE(4)
+#undef MG_NCASE
+        }
+        return after_launch("mgemv") == COLI_OK ? 1 : -1;
+    }
     constexpr int ROWS_WIDE = 16 * (COLI_MG_NW_WIDE / COLI_MG_KS_WIDE);
     const bool wide = cb <= 2 && (int64_t)W->n * ((W->O + ROWS_WIDE - 1) / ROWS_WIDE) >= COLI_MG_WIDE_MIN_WG;
     ProfScope ps("mgemv", st, true);
@@ -1049,16 +1172,27 @@ int launch_mgemv(const coli_qtensor *W, const float *x, float *y, int S, hipStre
 // one launch.  Returns 0 when the group is not taken (the caller then runs
 // the members one by one).
 int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *x,
-                       float *const *y, int S, hipStream_t st) {
+                       float *const *y, int S, hipStream_t st, const InNorm *nrm) {
     if (n < 1 || n > MG_MAXGRP || S < 1 || S > 4)
         return 0;
     for (int g = 0; g < n; ++g)
         if (!mgemv_ok(W[g]) || W[g]->n != 1 || W[g]->fmt != W[0]->fmt || cb_of(W[g]) != cb_of(W[0]))
             return 0;
+    // an input norm: every member takes the same rows (normalised in each
+    // workgroup; the first workgroup writes them out)
+    if (nrm != nullptr)
+        for (int g = 0; g < n; ++g)
+            if (x[g] != x[0] || W[g]->I != W[0]->I || !prenorm_fits(nrm, W[g], S, COLI_MG_NW_GROUP))
+                return 0;
     constexpr int TPW = COLI_MG_NW_GROUP / COLI_MG_KS_GROUP;
     MgArgs a = mg_args_for(W[0]);
     a.Sy = S;
     a.ngrp = n;
+    if (nrm != nullptr) {
+        a.nw = nrm->w;
+        a.neps = nrm->eps;
+        a.nxo = nrm->xn;
+    }
     size_t lds_max = 0;
     int wg = 0;
     // members with the longest rows first: their workgroups run longest, so
@@ -1089,12 +1223,20 @@ int launch_mgemv_group(int n, const coli_qtensor *const *W, const float *const *
     ProfScope ps("mgemv_group", st, true);
     int ok = 1;
 #define MG_G(NTV, CBV)                                                                             \
-    hipExtLaunchKernelGGL((k_mgemv<NTV, CBV, true, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP,    \
+    if (nrm) hipExtLaunchKernelGGL((k_mgemv<NTV, CBV, true, 1, MG_YN, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP, \
+                                   COLI_MG_NBQ_DENSE>),                                            \
+                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
+                          ps.start(), ps.stop(), 0, a);                                            \
+    else hipExtLaunchKernelGGL((k_mgemv<NTV, CBV, true, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP, \
                                    COLI_MG_NBQ_DENSE>),                                            \
                           dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
                           ps.start(), ps.stop(), 0, a)
 #define MG_R(NTV)                                                                                  \
-    hipExtLaunchKernelGGL((k_mgemv<NTV, 1, false, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP,     \
+    if (nrm) hipExtLaunchKernelGGL((k_mgemv<NTV, 1, false, 1, MG_YN, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP, \
+                                   COLI_MG_NBQ_DENSE>),                                            \
+                          dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
+                          ps.start(), ps.stop(), 0, a);                                            \
+    else hipExtLaunchKernelGGL((k_mgemv<NTV, 1, false, 1, MG_Y, COLI_MG_KS_GROUP, COLI_MG_NW_GROUP, \
                                    COLI_MG_NBQ_DENSE>),                                            \
                           dim3((unsigned)wg, 1u), dim3(COLI_MG_NW_GROUP * 64), (uint32_t)lds_max, st, \
                           ps.start(), ps.stop(), 0, a)
@@ -1180,6 +1322,8 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
         a.wts = m.w;
         a.yfin = m.out;
         a.has_sh = has_sh ? 1 : 0;
+        a.radd = m.resid;
+        a.yres = m.resid ? m.out_res : nullptr;
         ProfScope ps("moe_down_decode", m.st, true);
         if (!(g ? mg_dispatch_cb<1, true, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN, COLI_MG_NBQ_DOWN>(cb, a, P, m.st, ps)
                 : mg_dispatch_cb<1, false, 1, MG_PART, COLI_MG_KS_DOWN, COLI_MG_NW_DOWN, COLI_MG_NBQ_DOWN>(cb, a, P, m.st, ps)))

@@ -42,6 +42,17 @@ struct MlaArgs {
     float *Lc, *Rc, *out;
     void *ws;
     hipStream_t st;
+    // decode layer: also hsum = resid + out (the residual add after the
+    // attention), in o_proj's epilogue when the matrix-core kernel runs it
+    const float *resid = nullptr;
+    float *hsum = nullptr;
+    // decode layer: x is the layer input; the attention's input is its
+    // RMSNorm with in_norm_w (may be NULL) and in_eps, written to xn --
+    // folded into the q_a / kv_a launch when the matrix-core kernel runs it
+    bool in_norm = false;
+    const float *in_norm_w = nullptr;
+    double in_eps = 0.0;
+    float *xn = nullptr;
 };
 int launch_mla_decode(const MlaArgs &a);
 

@@ -13,19 +13,23 @@
 // The four projections are the library's decode GEMVs (q_a and kv_a share x
 // and go out as one grouped launch); the kernels here are the steps between
 // them.  Every step is a separate launch on one stream, so each reads what the
-// one before wrote; nothing waits on the host.
+// one before wrote; nothing waits on the host.  The query latent's RMSNorm
+// is folded into q_b's input staging when the matrix-core GEMV runs q_b (the
+// layer's input norm likewise into the q_a / kv_a launch), and the key side
+// (latent norm, rotary key, cache rows) runs in the key-absorption launch.
 //
 // Kernels (all HBM- or latency-bound at decode sizes; the weights they read,
 // kv_b's key and value rows, are 64 x 448 x 512 int4 = 8.3 MB for the
 // pages' model):
-//   k_mla_norm_rope   one workgroup per (row, latent): f64 sum of squares,
-//                     f32 rounding of x * inv * w in f64; the kv workgroup
-//                     also rotates the rotary key (cos / sin in f64) and
-//                     writes both cache rows
+//   k_mla_qnorm       (when q_b does not fold it) one workgroup per row: f64
+//                     sum of squares, f32 rounding of x * inv * w in f64
 //   k_mla_qabs        4 workgroups per head, each summing a quarter of its
 //                     key rows (lanes own 8 columns, 8 rows in flight per
 //                     wavefront) into a partial; workgroup 0 of each head
-//                     rotates the query's rotary part
+//                     rotates the query's rotary part; one more column of
+//                     workgroups normalises each new row's latent, rotates
+//                     its rotary key (cos / sin in f64) and writes both
+//                     cache rows
 //   k_mla_scores      partial scores over a third of the L + d_rope components:
 //                     4 heads x 64 keys per workgroup, LDS chunks double-
 //                     buffered; adds the qabs partials while staging
@@ -38,6 +42,7 @@
 // Every partial sum is added in a fixed order by the next kernel, so reruns
 // are bit-identical.
 #include "common.h"
+#include "layer.h"
 #include "mla.h"
 
 namespace coli {
@@ -61,36 +66,38 @@ __device__ __forceinline__ void rope_pair(float a, float b, int i, int dr, int p
 }
 
 // ---- norms, rotary key, cache rows ----------------------------------------
-__global__ __launch_bounds__(256) void k_mla_norm_rope(const float *__restrict__ cq_raw, int qr,
-                                                       const float *__restrict__ qn,
-                                                       const float *__restrict__ ckv, int L, int dr,
-                                                       const float *__restrict__ kn, double eps,
-                                                       double theta, int pos_base,
-                                                       float *__restrict__ cq, float *__restrict__ Lc,
-                                                       float *__restrict__ Rc) {
-    __shared__ double part[4];
-    const int s = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const bool kv = blockIdx.y == 1;
-    const int pos = pos_base + s;
-    const float *xr = kv ? ckv + (int64_t)s * (L + dr) : cq_raw + (int64_t)s * qr;
-    const int n = kv ? L : qr;
-    const float *w = kv ? kn : qn;
-    float *yr = kv ? Lc + (int64_t)pos * L : cq + (int64_t)s * qr;
+// RMSNorm of one row of n inputs by a workgroup of NTH threads: f64 sum of
+// squares (strided per thread, wavefront sums, wavefronts in order), every
+// output the f32 rounding of x * inv * w computed in f64; part: NTH / 64
+// doubles of LDS.  Contains a workgroup barrier.
+template <int NTH>
+__device__ __forceinline__ void mla_row_norm(const float *__restrict__ xr, int n,
+                                             const float *__restrict__ w, double eps,
+                                             float *__restrict__ yr, double *part) {
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     double ss = 0.0;
-    for (int d = t; d < n; d += 256) ss = fma((double)xr[d], (double)xr[d], ss);
+    for (int d = t; d < n; d += NTH) ss = fma((double)xr[d], (double)xr[d], ss);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += mla_shfl_xor(ss, m);
     if (lane == 0)
         part[wv] = ss;
     __syncthreads();
-    const double tot = ((part[0] + part[1]) + part[2]) + part[3];
+    double tot = part[0];
+#pragma unroll
+    for (int i = 1; i < NTH / 64; ++i) tot += part[i];
     const double inv = 1.0 / sqrt(tot / (double)n + eps);
-    for (int d = t; d < n; d += 256)
+    for (int d = t; d < n; d += NTH)
         yr[d] = (float)((double)xr[d] * inv * (w ? (double)w[d] : 1.0));
-    if (kv)
-        for (int i = t; i < dr / 2; i += 256)
-            rope_pair(xr[L + 2 * i], xr[L + 2 * i + 1], i, dr, pos, theta,
-                      Rc + (int64_t)pos * dr + 2 * i, Rc + (int64_t)pos * dr + 2 * i + 1);
+}
+
+// the query latent's norm, one workgroup per row (when the q_b launch does
+// not fold it into its input staging)
+__global__ __launch_bounds__(256) void k_mla_qnorm(const float *__restrict__ cq_raw, int qr,
+                                                   const float *__restrict__ qn, double eps,
+                                                   float *__restrict__ cq) {
+    __shared__ double part[4];
+    const int s = blockIdx.x;
+    mla_row_norm<256>(cq_raw + (int64_t)s * qr, qr, qn, eps, cq + (int64_t)s * qr, part);
 }
 
 // ---- key absorption and the query's rotary part ----------------------------
@@ -103,15 +110,35 @@ constexpr int QA_NW = 8;      // wavefronts per workgroup
 constexpr int QA_COLS = 512;  // latent columns per pass (8 per lane)
 constexpr int QA_RB = 8;      // rows per wavefront in flight
 
+// The extra column of workgroups (blockIdx.x == H) takes the new tokens' key
+// side: workgroup (H, s) normalises row s's latent into cache row
+// pos_base + s of Lc and rotates its rotary key into the same row of Rc.
 template <int S, bool GRP>
 __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int dn, int dr, int dv,
                                                          int L, const float *__restrict__ q,
                                                          int pos_base, double theta,
                                                          float *__restrict__ part,
-                                                         float *__restrict__ qpe) {
+                                                         float *__restrict__ qpe,
+                                                         const float *__restrict__ ckv,
+                                                         const float *__restrict__ kn, double eps,
+                                                         float *__restrict__ Lc,
+                                                         float *__restrict__ Rc) {
     __shared__ float red[QA_NW][S][QA_COLS];
     const int h = blockIdx.x, split = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (h == H) {
+        __shared__ double npart[QA_NW];
+        const int s = split;
+        if (s >= S)
+            return;
+        const int pos = pos_base + s;
+        const float *xr = ckv + (int64_t)s * (L + dr);
+        mla_row_norm<QA_NW * 64>(xr, L, kn, eps, Lc + (int64_t)pos * L, npart);
+        for (int i = tid; i < dr / 2; i += QA_NW * 64)
+            rope_pair(xr[L + 2 * i], xr[L + 2 * i + 1], i, dr, pos, theta,
+                      Rc + (int64_t)pos * dr + 2 * i, Rc + (int64_t)pos * dr + 2 * i + 1);
+        return;
+    }
     const int nq = H * (dn + dr);
     const int rows = (dn + MLA_QA_SPLIT - 1) / MLA_QA_SPLIT;
     const int j0 = split * rows, j1 = min(dn, j0 + rows);
@@ -491,13 +518,18 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     const double theta = (double)m.rope_theta;
     {
         ProfScope ps("mla_qabs", st);
-        const dim3 grid((unsigned)H, (unsigned)MLA_QA_SPLIT);
+        // (one more column of workgroups for the key side of the new rows)
+        static_assert(MLA_QA_SPLIT >= 4, "a workgroup per new row");
+        const dim3 grid((unsigned)H + 1, (unsigned)MLA_QA_SPLIT);
+        const float *ckv = (const float *)(ws + l.off[MLA_CKV_RAW]);
         if (grp)
             hipLaunchKernelGGL((k_mla_qabs<S, true>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn, dr,
-                               dv, L, q, a.pos_base, theta, part, qpe);
+                               dv, L, q, a.pos_base, theta, part, qpe, ckv, m.kv_norm,
+                               (double)m.eps, a.Lc, a.Rc);
         else
             hipLaunchKernelGGL((k_mla_qabs<S, false>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn,
-                               dr, dv, L, q, a.pos_base, theta, part, qpe);
+                               dr, dv, L, q, a.pos_base, theta, part, qpe, ckv, m.kv_norm,
+                               (double)m.eps, a.Lc, a.Rc);
         const int rc = after_launch("mla_qabs");
         if (rc != COLI_OK) return rc;
     }
@@ -553,19 +585,51 @@ int launch_mla_decode(const MlaArgs &a) {
     float *cq = (float *)(ws + l.off[MLA_CQ]);
     float *q = (float *)(ws + l.off[MLA_Q]);
     float *ctx = (float *)(ws + l.off[MLA_CTX]);
-    int rc = gemv_pair(m.q_a, m.kv_a, a.x, cq_raw, ckv, S, st);
-    if (rc != COLI_OK) return rc;
-    {
-        ProfScope ps("mla_norm_rope", st);
-        hipLaunchKernelGGL(k_mla_norm_rope, dim3((unsigned)S, 2), dim3(256), 0, st,
-                           (const float *)cq_raw, qr, m.q_norm, (const float *)ckv, L, dr,
-                           m.kv_norm, (double)m.eps, (double)m.rope_theta, a.pos_base, cq, a.Lc,
-                           a.Rc);
-        rc = after_launch("mla_norm_rope");
+    int rc;
+    // q_a and kv_a (the layer's input norm folded in when the matrix-core
+    // kernel takes it, else a norm launch first)
+    bool done = false;
+    const float *xin = a.x;
+    if (a.in_norm) {
+        if (decode_kernel_mode() == 0) {
+            const coli_qtensor *W[2] = {m.q_a, m.kv_a};
+            const float *xs[2] = {a.x, a.x};
+            float *ys[2] = {cq_raw, ckv};
+            const InNorm nr{a.in_norm_w, a.in_eps, a.xn};
+            const int r = launch_mgemv_group(2, W, xs, ys, S, st, &nr);
+            if (r < 0) return COLI_HIP_ERROR;
+            done = r == 1;
+        }
+        if (!done) {
+            rc = launch_rmsnorm(a.x, S, m.q_a->I, a.in_norm_w, a.in_eps, a.xn, st);
+            if (rc != COLI_OK) return rc;
+            xin = a.xn;
+        }
+    }
+    if (!done) {
+        rc = gemv_pair(m.q_a, m.kv_a, xin, cq_raw, ckv, S, st);
         if (rc != COLI_OK) return rc;
     }
-    rc = launch_gemv(m.q_b, cq, q, S, st);
-    if (rc != COLI_OK) return rc;
+    // q_b on the query latent's norm (folded in the same way); the key
+    // side's norm and rotation run beside the key absorption
+    done = false;
+    if (decode_kernel_mode() == 0) {
+        const InNorm nr{m.q_norm, (double)m.eps, cq};
+        const int r = launch_mgemv(m.q_b, cq_raw, q, S, st, nullptr, nullptr, &nr);
+        if (r < 0) return COLI_HIP_ERROR;
+        done = r == 1;
+    }
+    if (!done) {
+        {
+            ProfScope ps("mla_qnorm", st);
+            hipLaunchKernelGGL(k_mla_qnorm, dim3((unsigned)S), dim3(256), 0, st,
+                               (const float *)cq_raw, qr, m.q_norm, (double)m.eps, cq);
+            rc = after_launch("mla_qnorm");
+            if (rc != COLI_OK) return rc;
+        }
+        rc = launch_gemv(m.q_b, cq, q, S, st);
+        if (rc != COLI_OK) return rc;
+    }
     switch (S) {
         case 1: rc = launch_core<1>(a, l, ws, st); break;
         case 2: rc = launch_core<2>(a, l, ws, st); break;
@@ -573,7 +637,7 @@ int launch_mla_decode(const MlaArgs &a) {
         default: rc = launch_core<4>(a, l, ws, st); break;
     }
     if (rc != COLI_OK) return rc;
-    return launch_gemv(m.o_proj, ctx, a.out, S, st);
+    return launch_gemv(m.o_proj, ctx, a.out, S, st, a.resid, a.hsum);
 }
 
 }  // namespace coli

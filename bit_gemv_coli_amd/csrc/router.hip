@@ -9,7 +9,10 @@
 //   k_router_logits     z[s][e] for up to 4 input rows (decode): a workgroup
 //                       per expert, its wavefronts on quarters of the inputs,
 //                       lanes on 16-byte loads, one f64 FMA per product,
-//                       wavefront sums then quarters added in order;
+//                       wavefront sums then quarters added in order; in a
+//                       decode layer it also applies the RMSNorm in front of
+//                       the router (every workgroup reduces the rows the
+//                       way k_rmsnorm does, the first writes them out);
 //   k_router_logits_mx  z for many rows: f64 16x16x4 matrix-core products
 //                       (f32 operands widened exactly), a 32 x 32 block of
 //                       (rows, experts) per workgroup, the inputs split over
@@ -24,6 +27,8 @@
 #include <algorithm>
 
 #include "common.h"
+#include "layer.h"
+#include "rms.h"
 
 namespace coli {
 
@@ -44,12 +49,21 @@ __device__ __forceinline__ double rt_shfl_xor(double v, int m) {
 // inputs (WS == 4, quarters added in wavefront order).  Every lane takes 4
 // consecutive inputs (one 16-byte load per expert row and input row) of each
 // 256-input stretch, U stretches requested before they are used.
-template <int TT, int TE, int U, bool VEC, int WS>
+// NORM (WS == 4, VEC): x holds the rows before the RMSNorm in front of the
+// router; every workgroup reduces them to 1 / rms exactly as k_rmsnorm does
+// and normalises each input as it loads it (the same f32 values k_rmsnorm
+// writes), and the first workgroup also writes the normalised rows to xn.
+template <int TT, int TE, int U, bool VEC, int WS, bool NORM = false>
 __global__ __launch_bounds__(256) void k_router_logits(const float *__restrict__ x, int S, int D,
                                                        const float *__restrict__ R, int E,
-                                                       double *__restrict__ z) {
+                                                       double *__restrict__ z,
+                                                       const float *__restrict__ lnw = nullptr,
+                                                       double eps = 0.0,
+                                                       float *__restrict__ xn = nullptr) {
     static_assert(WS == 1 || WS == 4, "one or four wavefronts per block of experts");
+    static_assert(!NORM || (WS == 4 && VEC), "the folded norm takes whole workgroups, 16-byte rows");
     __shared__ double sp[WS == 4 ? 3 : 1][TE * TT];
+    __shared__ double npart[NORM ? TT : 1][4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int e0 = (WS == 4 ? (int)blockIdx.x : (int)blockIdx.x * 4 + wv) * TE;
     const int s0 = blockIdx.y * TT;
@@ -65,6 +79,30 @@ __global__ __launch_bounds__(256) void k_router_logits(const float *__restrict__
     for (int i = 0; i < TE; ++i) rr[i] = R + (int64_t)min(e0 + i, E - 1) * D;
 #pragma unroll
     for (int t = 0; t < TT; ++t) xr[t] = x + (int64_t)min(s0 + t, S - 1) * D;
+    double inv[TT];
+    if constexpr (NORM) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) inv[t] = row_rms_inv<true>(xr[t], D, eps, npart[t]);
+        if (blockIdx.x == 0)
+            for (int t = 0; t < TT && s0 + t < S; ++t)
+                for (int d = 4 * (int)threadIdx.x; d < D; d += 1024) {
+                    const f32x4 v = gload<f32x4>(xr[t] + d);
+                    const f32x4 g = lnw ? gload<f32x4>(lnw + d) : f32x4{1.f, 1.f, 1.f, 1.f};
+                    *(f32x4 *)(xn + (int64_t)(s0 + t) * D + d) =
+                        f32x4{rms_apply(v.x, inv[t], g.x), rms_apply(v.y, inv[t], g.y),
+                              rms_apply(v.z, inv[t], g.z), rms_apply(v.w, inv[t], g.w)};
+                }
+    }
+    // the normalised inputs (NORM) of row t at d
+    auto norm4 = [&](f32x4 v, int t, int d) -> f32x4 {
+        if constexpr (NORM) {
+            const f32x4 g = lnw ? gload<f32x4>(lnw + d) : f32x4{1.f, 1.f, 1.f, 1.f};
+            return f32x4{rms_apply(v.x, inv[t], g.x), rms_apply(v.y, inv[t], g.y),
+                         rms_apply(v.z, inv[t], g.z), rms_apply(v.w, inv[t], g.w)};
+        } else {
+            return v;
+        }
+    };
     double acc[TE][TT];
 #pragma unroll
     for (int i = 0; i < TE; ++i)
@@ -81,6 +119,12 @@ __global__ __launch_bounds__(256) void k_router_logits(const float *__restrict__
                 for (int i = 0; i < TE; ++i) rv[u][i] = gload<f32x4>(rr[i] + d);
 #pragma unroll
                 for (int t = 0; t < TT; ++t) xv[u][t] = gload<f32x4>(xr[t] + d);
+            }
+            if constexpr (NORM) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) xv[u][t] = norm4(xv[u][t], t, d0 + 256 * u + 4 * lane);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -100,7 +144,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const float *__restrict__
                 const f32x4 r = gload<f32x4>(rr[i] + d);
 #pragma unroll
                 for (int t = 0; t < TT; ++t) {
-                    const f32x4 v = gload<f32x4>(xr[t] + d);
+                    const f32x4 v = norm4(gload<f32x4>(xr[t] + d), t, d);
                     acc[i][t] = fma((double)r.x, (double)v.x, acc[i][t]);
                     acc[i][t] = fma((double)r.y, (double)v.y, acc[i][t]);
                     acc[i][t] = fma((double)r.z, (double)v.z, acc[i][t]);
@@ -364,6 +408,43 @@ __global__ __launch_bounds__(1024) void k_router_topk(const double *__restrict__
 
 size_t router_ws_bytes(int S, int E) { return (size_t)RT_MAXP * S * E * sizeof(double); }
 
+static int launch_topk(const double *z, int P, int S, int E, const float *bias, int K, float topp,
+                       int norm_topk, float routed_scale, int32_t *ids, float *w, hipStream_t st) {
+    ProfScope ps("router_topk", st);
+    hipLaunchKernelGGL(k_router_topk, dim3((unsigned)S), dim3(1024), 0, st, z, P, S, E, bias, K,
+                       (double)topp, norm_topk, (double)routed_scale, ids, w);
+    return after_launch("router_topk");
+}
+
+// The RMSNorm in front of the router folded into the decode logits kernel
+// (S <= 4 rows, 16-byte aligned rows): one launch fewer; xn gets the same
+// values a separate norm launch writes.  Otherwise the two launches.
+int launch_norm_router(const float *h, int S, int D, const float *lnw, double eps, float *xn,
+                       const float *R, const float *bias, int E, int K, float topp, int norm_topk,
+                       float routed_scale, int32_t *ids, float *w, void *ws, hipStream_t st) {
+    const bool fold = S >= 1 && S <= 4 && D % 4 == 0 && (uintptr_t)h % 16 == 0 &&
+                      (uintptr_t)xn % 16 == 0 && (uintptr_t)lnw % 16 == 0 && (uintptr_t)R % 16 == 0;
+    if (!fold) {
+        const int rc = launch_rmsnorm(h, S, D, lnw, eps, xn, st);
+        if (rc != COLI_OK) return rc;
+        return launch_router(xn, S, D, R, bias, E, K, topp, norm_topk, routed_scale, ids, w, ws, st);
+    }
+    double *z = (double *)ws;
+    {
+        ProfScope ps("router_logits", st);
+        const dim3 grid((unsigned)E, 1u);
+        if (S == 1)
+            hipLaunchKernelGGL((k_router_logits<1, 1, 6, true, 4, true>), grid, dim3(256), 0, st, h, S, D,
+                               R, E, z, lnw, eps, xn);
+        else
+            hipLaunchKernelGGL((k_router_logits<4, 1, 6, true, 4, true>), grid, dim3(256), 0, st, h, S, D,
+                               R, E, z, lnw, eps, xn);
+        const int rc = after_launch("router_logits");
+        if (rc != COLI_OK) return rc;
+    }
+    return launch_topk(z, 1, S, E, bias, K, topp, norm_topk, routed_scale, ids, w, st);
+}
+
 int launch_router(const float *x, int S, int D, const float *R, const float *bias, int E, int K,
                   float topp, int norm_topk, float routed_scale, int32_t *ids, float *w, void *ws,
                   hipStream_t st) {
@@ -398,10 +479,7 @@ int launch_router(const float *x, int S, int D, const float *R, const float *bia
         int rc = after_launch("router_logits");
         if (rc != COLI_OK) return rc;
     }
-    ProfScope ps("router_topk", st);
-    hipLaunchKernelGGL(k_router_topk, dim3((unsigned)S), dim3(1024), 0, st, z, P, S, E, bias, K,
-                       (double)topp, norm_topk, (double)routed_scale, ids, w);
-    return after_launch("router_topk");
+    return launch_topk(z, P, S, E, bias, K, topp, norm_topk, routed_scale, ids, w, st);
 }
 
 }  // namespace coli

@@ -122,6 +122,14 @@ def test_moe_layer_matches_oracle(orc, case):
     xn_g = xn.cpu().numpy()
     assert np.all(np.abs(xn_g - st["xn"]) <= 2.0 ** -24 * np.abs(st["xn"]) * 1.0001)
     assert np.array_equal(ids.cpu().numpy(), st["ids"])
+    # inside the layer call (workspace: normed rows, then the picks) the norm
+    # may be folded into the router: the same bits as the separate steps
+    wsh = ws.cpu().numpy()
+    xn_l = wsh[:S * D * 4].view(np.float32).reshape(S, D)
+    at = (S * D * 4 + 255) // 256 * 256
+    ids_l = wsh[at:at + S * K * 4].view(np.int32).reshape(S, K)
+    assert np.array_equal(xn_l.view(np.uint32), xn_g.view(np.uint32)), "layer's normed rows"
+    assert np.array_equal(ids_l, st["ids"]), "layer's picks"
     y_est = out.cpu().numpy().astype(np.float64) - h.astype(np.float64)
     tau = TOL_FP32 if S <= 4 else TOL_BF16
     # the f32 add of h rounds once more (<= 2^-24 |out|), far inside the bound

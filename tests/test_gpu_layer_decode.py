@@ -14,17 +14,19 @@ import torch
 
 import bit_gemv_coli_amd as coli
 import synthdata as sd
-from gpu_util import TOL_FP32, need_gpu, qtensor, to_dev
+from gpu_util import TOL_FP32, decode_kernels, need_gpu, qtensor, to_dev
 from test_gpu_mla import FULL, SMALL, _check as check_attention, _setup as setup_attention
 from test_gpu_moe import _check_moe, _moe_inputs
 
 pytestmark = pytest.mark.gpu
 
-CASES = [  # (S, pos_base, attention dims, E, F, K, shared, topp)
-    (1, 0, FULL, 16, 1024, 8, True, 0.0),
-    (4, 37, FULL, 16, 1024, 8, True, 0.8),
-    (3, 12, SMALL, 12, 96, 4, True, 0.0),
-    (2, 70, SMALL, 9, 64, 3, False, 0.9),
+CASES = [  # (S, pos_base, attention dims, E, F, K, shared, topp, decode kernels)
+    (1, 0, FULL, 16, 1024, 8, True, 0.0, 0),
+    (4, 37, FULL, 16, 1024, 8, True, 0.8, 0),
+    (3, 12, SMALL, 12, 96, 4, True, 0.0, 0),
+    (2, 70, SMALL, 9, 64, 3, False, 0.9, 0),
+    # the vector-ALU decode kernels: every norm and residual add a launch of its own
+    (2, 33, SMALL, 10, 64, 4, True, 0.0, 1),
 ]
 
 
@@ -32,11 +34,11 @@ def _al256(n):
     return (n + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("case", CASES, ids=["S{}-pos{}-D{}-E{}-F{}-K{}-sh{}-p{}".format(
+@pytest.mark.parametrize("case", CASES, ids=["S{}-pos{}-D{}-E{}-F{}-K{}-sh{}-p{}-k{}".format(
     c[0], c[1], c[2]["D"], *c[3:]) for c in CASES])
 def test_layer_decode_matches_oracle(orc, case):
     need_gpu()
-    S, pb, dims, E, F, K, shared, topp = case
+    S, pb, dims, E, F, K, shared, topp, kmode = case
     D, eps, norm, scale = dims["D"], 1e-6, True, 2.5
     W, layer, x, Lc, Rc, T = setup_attention(500 + S + pb + D, S, pb, dims)
     G, U, Dn, sh, _, _, _ = _moe_inputs(600 + S + E, 4, S, K, E, D, F, 64 if D > 256 else 32,
@@ -54,11 +56,12 @@ def test_layer_decode_matches_oracle(orc, case):
     ws = torch.full((total,), 0xFF, dtype=torch.uint8, device="cuda")
     Lc_d, Rc_d = to_dev(Lc), to_dev(Rc)
     out = torch.full((S, D), float("nan"), device="cuda")
-    coli.check(coli.coli_layer_decode(layer, to_dev(in_ln), tg, tu, td, to_dev(post_ln), to_dev(R),
-                                      to_dev(bias), K, topp, norm, scale, ts[0], ts[1], ts[2], eps,
-                                      to_dev(x), S, pb, Lc_d, Rc_d, T, out, ws, total),
-               "coli_layer_decode")
-    torch.cuda.synchronize()
+    with decode_kernels(kmode):
+        coli.check(coli.coli_layer_decode(layer, to_dev(in_ln), tg, tu, td, to_dev(post_ln),
+                                          to_dev(R), to_dev(bias), K, topp, norm, scale, ts[0],
+                                          ts[1], ts[2], eps, to_dev(x), S, pb, Lc_d, Rc_d, T, out,
+                                          ws, total), "coli_layer_decode")
+        torch.cuda.synchronize()
     wsh = ws.cpu().numpy()
 
     def arr(at, shape, dtype=np.float32):
@@ -76,7 +79,8 @@ def test_layer_decode_matches_oracle(orc, case):
 
     def stage(name, shape):
         return arr(off["attn_ws"] + moff[name], shape)
-    check_attention(orc, W, xn, pb, Lc, Rc, T, a, Lc_d.cpu().numpy(), Rc_d.cpu().numpy(), stage)
+    check_attention(orc, W, xn, pb, Lc, Rc, T, a, Lc_d.cpu().numpy(), Rc_d.cpu().numpy(), stage,
+                    packed=(kmode == 0))
     # 3. residual
     assert np.array_equal(h, (x + a).astype(np.float32)), "h = x + a"
     # 4. the expert half on the GPU's h: picks, then the block
@@ -84,6 +88,8 @@ def test_layer_decode_matches_oracle(orc, case):
                                 shared=sh)
     ids = arr(off["moe_ws"] + _al256(S * D * 4), (S, K), np.int32)
     assert np.array_equal(ids, st["ids"]), (ids, st["ids"])
+    xn2 = arr(off["moe_ws"], (S, D))
+    assert np.all(np.abs(xn2 - st["xn"]) <= 2.0 ** -24 * np.abs(st["xn"]) * 1.0001), "post_ln"
     y_est = out.astype(np.float64) - h.astype(np.float64)
     _check_moe(orc, G, U, Dn, sh, st["xn"], st["ids"], st["w"].astype(np.float32), y_est, None,
                TOL_FP32)
