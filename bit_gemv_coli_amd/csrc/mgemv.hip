@@ -293,8 +293,10 @@ static_assert(COLI_MG_NW_WIDE / COLI_MG_KS_WIDE == COLI_MG_NW_WIDE1 / COLI_MG_KS
 // 128-input blocks requested together per wavefront: one quad, whose group
 // scales sit together in the packed copy
 constexpr int MG_NBK = 4;
-// groups of 8 inputs per thread in one input staging step
+// groups of 8 inputs per thread in one input staging step (with the input
+// norm folded in: fewer, so the norm weights fit beside them)
 constexpr int MG_UN = 4;
+constexpr int MG_UN_YN = 2;
 // buffer resource word 3 for raw (untyped) buffer loads; reads past
 // num_records return zeros
 constexpr int MG_RSRC_W3 = 0x00020000;
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
     // inputs of one staging step: UN groups of 8 per thread.  The first step's
     // loads are issued here, ahead of every weight request (loads complete in
     // order), so the staging overlaps the first weight batches.
-    constexpr int UN = MG_UN;
+    constexpr int UN = EPI == MG_YN ? MG_UN_YN : MG_UN;
     const int kpad = (I + 127) / 128 * 128;
     float xv[UN][8];
     auto stage_load = [&](int k0, int nb8, int base) {
@@ -420,6 +422,25 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         }
     };
     stage_load(0, min(KSEG, kpad) / 8, 0);
+    // MG_YN: the norm weights of the same inputs, requested before the
+    // weights so that the staging does not wait behind them (loads complete
+    // in order)
+    float gv[EPI == MG_YN ? UN : 1][8];
+    if constexpr (EPI == MG_YN) {
+        const int nb8 = min(KSEG, kpad) / 8;
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int idx = min(u * NTH + tid, NT * nb8 - 1);
+            const int k = min((idx % nb8) * 8, I - 8);
+            f32x4 g0{1.f, 1.f, 1.f, 1.f}, g1{1.f, 1.f, 1.f, 1.f};
+            if (a.nw != nullptr) {
+                g0 = gload<f32x4>(a.nw + k);
+                g1 = gload<f32x4>(a.nw + k + 4);
+            }
+            gv[u][0] = g0.x; gv[u][1] = g0.y; gv[u][2] = g0.z; gv[u][3] = g0.w;
+            gv[u][4] = g1.x; gv[u][5] = g1.y; gv[u][6] = g1.z; gv[u][7] = g1.w;
+        }
+    }
 
     const int tile = bx * TPW + tile_w;
     const int row0 = tile * 16;
@@ -628,7 +649,8 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
         }
     };
     // MG_YN: the first staging step holds every input of the NT rows (the
-    // host checks NT * nb8 <= UN * NTH and one segment).  Each row's f64 sum
+    // host checks NT * nb8 <= UN * NTH and one segment); gv holds the norm
+    // weights of the same inputs.  Each row's f64 sum
     // of squares (per thread, wavefront sums, wavefronts in order -- the same
     // in every workgroup of the launch), then x * inv * w in place;
     // workgroup (0, 0) also writes the normalised rows out.
@@ -671,17 +693,11 @@ __global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
             const int idx = u * NTH + tid;
             const int t = idx / nb8, k = (idx % nb8) * 8;
             if (idx < NT * nb8 && k < I) {  // I % 8 == 0: all 8 inputs are real
-                f32x4 g0{1.f, 1.f, 1.f, 1.f}, g1{1.f, 1.f, 1.f, 1.f};
-                if (a.nw != nullptr) {
-                    g0 = gload<f32x4>(a.nw + k);
-                    g1 = gload<f32x4>(a.nw + k + 4);
-                }
                 double iv = inv[0];
 #pragma unroll
                 for (int tt = 1; tt < NT; ++tt) iv = (tt == t) ? inv[tt] : iv;
-                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-                for (int w = 0; w < 8; ++w) xv[u][w] = rms_apply(xv[u][w], iv, g[w]);
+                for (int w = 0; w < 8; ++w) xv[u][w] = rms_apply(xv[u][w], iv, gv[u][w]);
                 if (wr) {
                     float *o = a.nxo + (int64_t)t * I + k;
                     *reinterpret_cast<f32x4 *>(o) = f32x4{xv[u][0], xv[u][1], xv[u][2], xv[u][3]};
@@ -1083,7 +1099,7 @@ static bool prenorm_fits(const InNorm *nrm, const coli_qtensor *W, int S, int NW
     size_t lds;
     plan_lds(S, cb_of(W), 1, NW, W->I, kseg, nseg, lds);
     const int kpad = (W->I + 127) / 128 * 128;
-    return nseg == 1 && (int64_t)S * (std::min(kseg, kpad) / 8) <= (int64_t)MG_UN * NW * 64;
+    return nseg == 1 && (int64_t)S * (std::min(kseg, kpad) / 8) <= (int64_t)MG_UN_YN * NW * 64;
 }
 
 // Dense GEMV y[e][t][o] for S <= 4 input rows.  Returns 0 when the layout or
