@@ -285,6 +285,15 @@ static_assert(COLI_MG_NW_WIDE / COLI_MG_KS_WIDE == COLI_MG_NW_WIDE1 / COLI_MG_KS
 #ifndef COLI_MG_NBQ_GATEUP
 #define COLI_MG_NBQ_GATEUP 2
 #endif
+// gate/up with more workgroups than fit at once with two quads in flight
+// (138 VGPRs + 64 AGPRs: 2 per compute unit, 512 on the chip): one quad in
+// flight compiled for 4 wavefronts per SIMD (116 VGPRs), so e.g. the 9 pairs
+// of 8 routed + 1 shared expert (576 workgroups) start together (measured on
+// the 75-layer stream: 42.0 against 43.1 us per block; the 8-pair block keeps
+// two quads: 35.0 against 35.4 us)
+#ifndef COLI_MG_GATEUP_SLOTS
+#define COLI_MG_GATEUP_SLOTS 512
+#endif
 // (down: one quad; measured 13.6 against 14.1 us per down launch with two,
 // 16.5 with four, in the 8-of-256-expert block)
 #ifndef COLI_MG_NBQ_DOWN
@@ -313,7 +322,7 @@ __host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3)
 // 16 v), 8 (fmt 1: int8 codes, B bytes v), 2 (fmt 3: 2-bit codes moved to the
 // top of each byte, B bytes 64 v).
 template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ = 2, int QB = 4>
-__global__ __launch_bounds__(NW * 64) void k_mgemv(MgArgs a) {
+__global__ __launch_bounds__(NW * 64, (NMAT == 2 && NBQ == 1) ? 4 : 1) void k_mgemv(MgArgs a) {
     static_assert(NW % KS == 0, "whole tiles per workgroup");
     static_assert(QB == 4 || ((QB == 8 || QB == 2) && !GROUPED && EPI == MG_Y), "code width");
     constexpr bool YOUT = EPI == MG_Y || EPI == MG_YN;
@@ -1315,8 +1324,13 @@ int launch_mgemv_moe(const MoeArgs &m, float *h, float *yp, int *cnt) {
             a.ncnt = (m.D + 15) / 16;
         }
         ProfScope ps("moe_gateup_decode", m.st, true);
-        if (!(g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, COLI_MG_NBQ_GATEUP>(cb, a, P, m.st, ps)
-                : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, COLI_MG_NBQ_GATEUP>(cb, a, P, m.st, ps)))
+        constexpr int TPWG = COLI_MG_NW_GATEUP / COLI_MG_KS_GATEUP;
+        const int64_t wgs = (int64_t)P * (((m.F + 15) / 16 + TPWG - 1) / TPWG);
+        const bool many = wgs > COLI_MG_GATEUP_SLOTS;
+        if (!(many ? (g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, 1>(cb, a, P, m.st, ps)
+                        : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, 1>(cb, a, P, m.st, ps))
+                   : (g ? mg_dispatch_cb<1, true, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, COLI_MG_NBQ_GATEUP>(cb, a, P, m.st, ps)
+                        : mg_dispatch_cb<1, false, 2, MG_SILU, COLI_MG_KS_GATEUP, COLI_MG_NW_GATEUP, COLI_MG_NBQ_GATEUP>(cb, a, P, m.st, ps))))
             return 0;
         int rc = after_launch("moe_gateup_decode");
         if (rc != COLI_OK) return rc;

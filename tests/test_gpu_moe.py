@@ -140,7 +140,7 @@ def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None, rep=Fal
     assert np.all(err <= bound + 1e-30), f"end to end: max err/bound = {np.max(err / bound):.3e}"
 
 
-# S = 1 with long expert rows (F up to 2048) and every scale-slot count
+# S = 1 and 2 with long expert rows (F up to 2048) and every scale-slot count
 DECODE_LONG_F = [  # (fmt, S, K, E, D, F, gs, shared)
     (4, 1, 8, 16, 256, 512, 64, True),
     (4, 1, 8, 16, 512, 2048, 64, False),
@@ -148,6 +148,10 @@ DECODE_LONG_F = [  # (fmt, S, K, E, D, F, gs, shared)
     (4, 1, 3, 7, 96, 1536, 128, True),      # gs 128: one slot
     (2, 1, 4, 8, 256, 512, 0, True),        # per-row scales
     (4, 1, 16, 40, 128, 512, 64, True),
+    # more gate/up workgroups than two per compute unit (the one-quad variant)
+    (4, 1, 8, 16, 256, 2048, 64, True),
+    (4, 2, 8, 20, 256, 2048, 128, True),
+    (2, 1, 12, 16, 128, 2048, 0, False),
 ]
 
 
