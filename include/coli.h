@@ -478,7 +478,13 @@ int coli_mla_decode(const coli_mla_layer *layer, const float *x, int S, int pos_
  *                        routed_scale; experts gate/up/down, shared expert)
  * Arguments as in those calls (S = 1..4; in_ln, post_ln, bias and the shared
  * expert may be NULL); out may equal x.  Everything is validated before the
- * first launch; nothing is allocated and the host never waits.
+ * first launch; nothing is allocated and the host never waits.  Where the
+ * matrix-core decode kernels run, the two norms and both residual adds are
+ * folded into neighbouring launches (11 launches per layer instead of 16):
+ * the residual adds and the post_ln norm give the bits the separate steps
+ * give; the in_ln norm sums its squares in another order, so xn may differ
+ * from coli_rmsnorm's in the last place (both within one f32 rounding of the
+ * exact norm).
  *   workspace: coli_layer_decode_workspace_bytes(attn, gate, S, K, T_cap,
  *   has_shared) bytes, 256-byte aligned.  coli_layer_decode_workspace_layout
  *   gives the byte offsets of xn [S][D], a [S][D], h [S][D], the attention's
