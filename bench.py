@@ -8,9 +8,12 @@ dual gate/up + SiLU, down + weighted combine, all inside coli_moe_block.  The
 routing changes every step (64 precomputed uniform draws), so the 170 MB the
 block touches does not sit in the 256 MB last-level cache.
 
-value = algorithmic HBM bytes per block / block time (GB/s).  Per-kernel
-durations come from HIP events the library records on the launch stream
-around each kernel inside the timed region.  Side measurements ("extra")
+value = algorithmic HBM bytes per block / block time (GB/s), the K timed
+blocks captured in one HIP graph and replayed once (one submission, as the
+pages submit a layer's block in one command buffer); the same K blocks
+launched one by one are reported beside it (extra.block_us_eager).  Per-kernel
+durations come from one more pass of K blocks with HIP events the library
+records on the launch stream around each kernel.  Side measurements ("extra")
 cover the single fmt-4 GEMV, the 6144x6144 format sweep, the ceilings a
 streaming read and a matrix-core loop reach on this part, the S=544 prefill
 GEMM and MoE block, and the 75-layer decode stream.
@@ -168,9 +171,9 @@ def main():
     block_bytes = K * expert_bytes + x.nbytes + out.numel() * 4 + K * 8
     gateup_bytes = K * 2 * qbytes(4, F, D, GS) + x.nbytes + K * F * 4
 
-    def step(i):
+    def step(i, st=None):
         rc = coli.coli_moe_block(tg, tu, td, x_d, 1, ids_d[i % NR], w_d[i % NR], K, None, None,
-                                 None, out, ws, wsb, stream)
+                                 None, out, ws, wsb, stream if st is None else st)
         if rc != coli.COLI_OK:
             coli.check(rc, "coli_moe_block")
 
@@ -179,18 +182,44 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # the timed steps as one submission: the K blocks (each with its own
+    # routing) captured in one HIP graph and replayed once -- every kernel of
+    # every block runs; the host's launch calls are out of the timed region
+    log(f"capturing {args.steps} steps in one graph")
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(0, side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cst = torch.cuda.current_stream()
+        for i in range(args.steps):
+            step(args.warmup + i, cst)
+    graph.replay()  # untimed first replay
+    torch.cuda.synchronize()
+
     log(f"timed {args.steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
+    graph.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     value = block_bytes / (ms * 1e-3) / 1e9
+    del graph
+
+    # the same steps launched one by one on the stream (eager), for reference
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / args.steps
 
     # the same steps again with HIP events recorded by the library around
     # every kernel launch (on the launch stream): per-kernel durations
@@ -220,7 +249,9 @@ def main():
                 "block_GBps": value, "block_frac": value / HBM_PEAK_GBS}
 
     # ---- side measurements --------------------------------------------------
-    extra = {"block_us": ms * 1e3, "kernels": kern, "wall_s_timed": wall}
+    extra = {"block_us": ms * 1e3, "block_us_eager": ms_eager * 1e3,
+             "block_GBps_eager": block_bytes / (ms_eager * 1e-3) / 1e9, "kernels": kern,
+             "wall_s_timed": wall}
     if not args.no_extra:
         # the same blocks in two submissions (begin: resident slots; end: the
         # late ones), half of the 8 slots late
