@@ -185,3 +185,59 @@ def test_moe_prefill_config4_full(orc, pack):
     rows = np.sort(sd.rng(6).choice(D, 256, replace=False)).astype(np.int32)
     hsel = h.reshape(S, K, F)[toks].reshape(-1, F)
     _check_moe(orc, G, U, Dn, None, x[toks], local, w[toks], out[toks], hsel, TOL_BF16, rows=rows)
+
+
+ZW = [(4, 128, True), (4, 256, True), (4, 64, True), (4, 32, True), (4, 128, False), (2, 0, True),
+      (2, 0, False)]
+
+
+@pytest.mark.parametrize("fmt,gs,pack", ZW, ids=[f"fmt{f}-gs{g}-{'packed' if p else 'plain'}"
+                                                 for f, g, p in ZW])
+def test_qmatmul_prefill_zero_weights_and_outliers(orc, fmt, gs, pack):
+    """Rows whose codes are all the zero code give exact zeros, and huge
+    inputs at columns whose weights are zero in every row (up to 1e6 times
+    the rest) stay within 4e-3 * sum |w||x|: the bound has no term for the
+    inputs' spread, so a weight that is zero must contribute exactly nothing."""
+    need_gpu()
+    from gpu_util import zero_column
+    O, I, S = 96, 1024, 130
+    r = sd.rng(900 + fmt + gs + pack)
+    q, s = sd.gen_matrix(r, fmt, O, I, gs)
+    q[5] = 0x88          # zero rows
+    q[17] = 0x88
+    cols = (3, 200, 640, 1023)
+    for c in cols:
+        zero_column(q, fmt, c)
+    W = QMat(fmt, O, I, gs if fmt == 4 else 0, q, s)
+    T = qtensor(W, pack=pack)
+    for mag in (1e3, 1e6):
+        x = sd.gen_x(r, S, I)
+        for t in range(S):
+            x[t, cols[t % 4]] = mag if t % 2 else -mag
+        y = gpu_qmatmul(T, x)[0]
+        y_ref, A = orc.qmatmul(W, x)
+        assert np.all(y[:, 5] == 0.0) and np.all(y[:, 17] == 0.0), "zero rows"
+        assert_within(y, y_ref, A, TOL_BF16, f"fmt {fmt} gs {gs} outliers {mag:g}")
+
+
+@pytest.mark.parametrize("gs", [64, 128, 256])
+def test_moe_prefill_zero_weight_outliers(orc, gs):
+    """S = 40 rows, Zipf routing (experts with 1-16 rows and with more), packed
+    experts: inputs up to 1e5 times the rest at hidden columns whose gate and
+    up weights are zero in every expert -- the weight-streaming kernels' group
+    sums (codes as 2 + q/8 with a -3 correction row for gs >= 128) must make
+    those columns contribute nothing, within the staged bf16 bound."""
+    need_gpu()
+    from gpu_util import zero_column
+    E, D, F, K, S = 6, 512, 256, 4, 40
+    G, U, Dn, sh, x, ids, w = _moe_inputs(950 + gs, 4, S, K, E, D, F, gs, True, routing="zipf")
+    cols = (7, 130, 300, 511)
+    for m in (G, U, sh[0], sh[1]):
+        q = m.q if m.q.ndim == 3 else m.q[None]
+        for e in range(q.shape[0]):
+            for c in cols:
+                zero_column(q[e], 4, c)
+    for t in range(S):
+        x[t, cols[t % 4]] = 1e5 if t % 2 else -1e5
+    out, h = _run_gpu(G, U, Dn, sh, x, ids, w)
+    _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h, TOL_BF16)
