@@ -483,6 +483,8 @@ int launch_gemv(const coli_qtensor *W, const float *x, float *y, int S, hipStrea
                 const float *radd, float *ysum) {
     if (ysum == nullptr)
         return launch_gemv_y(W, x, y, S, st);
+    if (W->n != 1 || radd == nullptr)
+        return decline("gemv: a residual add takes one matrix and its addend");
     const bool fast = (W->flags & QF_FAST) &&
                       (W->fmt != 4 || (W->flags & (QF_GROUP32 | QF_GROUP16))) &&
                       ((uintptr_t)x % 16 == 0);
