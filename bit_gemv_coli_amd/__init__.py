@@ -315,6 +315,7 @@ def coli_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> int:
     return _load().coli_probe_mfma(int(workgroups), int(iters), _ptr(sink), _stream(stream))
 
 
+COLI_MLA_MAX_ROWS = 4096  # include/coli.h
 MLA_STAGES = ["cq_raw", "ckv_raw", "cq", "q", "qabs", "qpe", "scores", "p", "clat", "ctx"]
 
 

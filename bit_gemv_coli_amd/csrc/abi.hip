@@ -840,8 +840,8 @@ static int check_mla(const coli_mla_layer *m, int S, int T_cap, MlaLayout *lay, 
     if (L % 32 != 0 || L > 4096 || !dev_aligned(kb->q, 16))
         return decline("%s: latent width %d must be a multiple of 32 up to 4096 with 16-byte "
                        "aligned kv_b codes", who, L);
-    if (S < 1 || S > 4)
-        return decline("%s: S=%d outside 1..4 (decode rows)", who, S);
+    if (S < 1 || S > COLI_MLA_MAX_ROWS)
+        return decline("%s: S=%d outside 1..%d", who, S, COLI_MLA_MAX_ROWS);
     if (T_cap < S || (int64_t)T_cap * (L + dr) > INT32_MAX)
         return decline("%s: bad T_cap=%d", who, T_cap);
     if (!(m->eps >= 0.0f) || m->eps == __builtin_huge_valf() ||

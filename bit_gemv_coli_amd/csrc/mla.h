@@ -19,6 +19,8 @@ static_assert(MLA_NSTAGE == COLI_MLA_STAGES, "stage count");
 constexpr int MLA_QA_SPLIT = 4;
 // score splits over the L + d_rope components
 constexpr int MLA_SC_SPLIT = 3;
+// query rows per run of the core kernels (more rows: several runs in order)
+constexpr int MLA_CHUNK = 4;
 
 struct MlaLayout {
     size_t off[MLA_NSTAGE];

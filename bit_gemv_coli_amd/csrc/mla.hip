@@ -468,9 +468,11 @@ MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tc
     l.off[MLA_P] = take((size_t)S * H * Tcap);
     l.off[MLA_CLAT] = take((size_t)S * H * L);
     l.off[MLA_CTX] = take((size_t)S * H * dv);
-    l.qabs_part = take((size_t)MLA_QA_SPLIT * S * H * L);
-    l.sc_part = take((size_t)MLA_SC_SPLIT * S * H * Tcap);
-    l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * S * H * L);
+    // the core runs on chunks of at most MLA_CHUNK rows: partial sums for one
+    const int Sc = S < MLA_CHUNK ? S : MLA_CHUNK;
+    l.qabs_part = take((size_t)MLA_QA_SPLIT * Sc * H * L);
+    l.sc_part = take((size_t)MLA_SC_SPLIT * Sc * H * Tcap);
+    l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * Sc * H * L);
     l.total = o;
     return l;
 }
@@ -493,8 +495,10 @@ static int gemv_pair(const coli_qtensor *A, const coli_qtensor *B, const float *
     return launch_gemv(B, x, yb, S, st);
 }
 
+// The core for rows r0 .. r0 + S - 1 (S <= MLA_CHUNK) at positions pos_base +
+// r0 ..: stage pointers start at row r0, partial sums are the chunk's own.
 template <int S>
-static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st) {
+static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st, int r0) {
     const coli_mla_layer &m = *a.layer;
     const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v;
     const int L = m.kv_b->I;
@@ -505,13 +509,15 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     kb.rb = m.kv_b->row_bytes;
     kb.ng = m.kv_b->ng;
     kb.gs = grp ? m.kv_b->gs : 1;
-    const float *q = (const float *)(ws + l.off[MLA_Q]);
-    float *qabs = (float *)(ws + l.off[MLA_QABS]);
-    float *qpe = (float *)(ws + l.off[MLA_QPE]);
-    float *sc = (float *)(ws + l.off[MLA_SCORES]);
-    float *p = (float *)(ws + l.off[MLA_P]);
-    float *clat = (float *)(ws + l.off[MLA_CLAT]);
-    float *ctx = (float *)(ws + l.off[MLA_CTX]);
+    const int64_t R = r0;
+    const int pos_base = a.pos_base + r0;
+    const float *q = (const float *)(ws + l.off[MLA_Q]) + R * H * (dn + dr);
+    float *qabs = (float *)(ws + l.off[MLA_QABS]) + R * H * L;
+    float *qpe = (float *)(ws + l.off[MLA_QPE]) + R * H * dr;
+    float *sc = (float *)(ws + l.off[MLA_SCORES]) + R * H * a.T_cap;
+    float *p = (float *)(ws + l.off[MLA_P]) + R * H * a.T_cap;
+    float *clat = (float *)(ws + l.off[MLA_CLAT]) + R * H * L;
+    float *ctx = (float *)(ws + l.off[MLA_CTX]) + R * H * dv;
     float *part = (float *)(ws + l.qabs_part);
     float *sc_part = (float *)(ws + l.sc_part);
     float *cl_part = (float *)(ws + l.cl_part);
@@ -521,38 +527,38 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
         // (one more column of workgroups for the key side of the new rows)
         static_assert(MLA_QA_SPLIT >= 4, "a workgroup per new row");
         const dim3 grid((unsigned)H + 1, (unsigned)MLA_QA_SPLIT);
-        const float *ckv = (const float *)(ws + l.off[MLA_CKV_RAW]);
+        const float *ckv = (const float *)(ws + l.off[MLA_CKV_RAW]) + R * (L + dr);
         if (grp)
             hipLaunchKernelGGL((k_mla_qabs<S, true>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn, dr,
-                               dv, L, q, a.pos_base, theta, part, qpe, ckv, m.kv_norm,
+                               dv, L, q, pos_base, theta, part, qpe, ckv, m.kv_norm,
                                (double)m.eps, a.Lc, a.Rc);
         else
             hipLaunchKernelGGL((k_mla_qabs<S, false>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn,
-                               dr, dv, L, q, a.pos_base, theta, part, qpe, ckv, m.kv_norm,
+                               dr, dv, L, q, pos_base, theta, part, qpe, ckv, m.kv_norm,
                                (double)m.eps, a.Lc, a.Rc);
         const int rc = after_launch("mla_qabs");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_scores", st);
-        const int nkeys = a.pos_base + S;
+        const int nkeys = pos_base + S;
         const dim3 grid((unsigned)((nkeys + SC_KEYS - 1) / SC_KEYS),
                         (unsigned)((H + SC_HEADS - 1) / SC_HEADS), (unsigned)(S * MLA_SC_SPLIT));
         hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
                            (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, S, H, L,
-                           dr, a.pos_base, a.T_cap, qabs, sc_part);
+                           dr, pos_base, a.T_cap, qabs, sc_part);
         const int rc = after_launch("mla_scores");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_softmax_clat", st);
-        const int nkeys = a.pos_base + S;
+        const int nkeys = pos_base + S;
         const float scale = (float)(1.0 / sqrt((double)(dn + dr)));
         const dim3 grid((unsigned)((nkeys + CL_KEYS - 1) / CL_KEYS),
                         (unsigned)((L + CL_COLS - 1) / CL_COLS),
                         (unsigned)(S * ((H + CL_HEADS - 1) / CL_HEADS)));
         hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
-                           (const float *)a.Lc, S, H, L, a.pos_base, a.T_cap, scale, sc, p, cl_part);
+                           (const float *)a.Lc, S, H, L, pos_base, a.T_cap, scale, sc, p, cl_part);
         const int rc = after_launch("mla_softmax_clat");
         if (rc != COLI_OK) return rc;
     }
@@ -562,14 +568,36 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
         const size_t lds = (size_t)S * L * sizeof(float);
         if (grp)
             hipLaunchKernelGGL((k_mla_ctx<S, true>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
-                               a.pos_base, (const float *)cl_part, clat, ctx);
+                               pos_base, (const float *)cl_part, clat, ctx);
         else
             hipLaunchKernelGGL((k_mla_ctx<S, false>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
-                               a.pos_base, (const float *)cl_part, clat, ctx);
+                               pos_base, (const float *)cl_part, clat, ctx);
         const int rc = after_launch("mla_ctx");
         if (rc != COLI_OK) return rc;
     }
     return COLI_OK;
+}
+
+// the core over all S rows, MLA_CHUNK rows per launch set (each chunk's key
+// rows are in the caches before the next chunk's scores read them)
+static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st) {
+    for (int r0 = 0; r0 < a.S; r0 += MLA_CHUNK) {
+        const int n = a.S - r0 < MLA_CHUNK ? a.S - r0 : MLA_CHUNK;
+        int rc;
+        switch (n) {
+            case 1: rc = launch_core<1>(a, l, ws, st, r0); break;
+            case 2: rc = launch_core<2>(a, l, ws, st, r0); break;
+            case 3: rc = launch_core<3>(a, l, ws, st, r0); break;
+            default: rc = launch_core<4>(a, l, ws, st, r0); break;
+        }
+        if (rc != COLI_OK) return rc;
+    }
+    return COLI_OK;
+}
+
+// one projection of S > MLA_CHUNK rows: the prefill GEMM (bf16 matrix cores)
+static int proj_rows(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st) {
+    return launch_gemm(W, x, y, S, nullptr, 0, st);
 }
 
 int launch_mla_decode(const MlaArgs &a) {
@@ -586,6 +614,35 @@ int launch_mla_decode(const MlaArgs &a) {
     float *q = (float *)(ws + l.off[MLA_Q]);
     float *ctx = (float *)(ws + l.off[MLA_CTX]);
     int rc;
+    if (S > MLA_CHUNK) {
+        // prefill rows: the projections on the prefill GEMM, the norms and
+        // the layer's residual add launches of their own, the core in
+        // chunks of rows
+        const float *xin = a.x;
+        if (a.in_norm) {
+            rc = launch_rmsnorm(a.x, S, m.q_a->I, a.in_norm_w, a.in_eps, a.xn, st);
+            if (rc != COLI_OK) return rc;
+            xin = a.xn;
+        }
+        rc = proj_rows(m.q_a, xin, cq_raw, S, st);
+        if (rc != COLI_OK) return rc;
+        rc = proj_rows(m.kv_a, xin, ckv, S, st);
+        if (rc != COLI_OK) return rc;
+        {
+            ProfScope ps("mla_qnorm", st);
+            hipLaunchKernelGGL(k_mla_qnorm, dim3((unsigned)S), dim3(256), 0, st,
+                               (const float *)cq_raw, qr, m.q_norm, (double)m.eps, cq);
+            rc = after_launch("mla_qnorm");
+            if (rc != COLI_OK) return rc;
+        }
+        rc = proj_rows(m.q_b, cq, q, S, st);
+        if (rc != COLI_OK) return rc;
+        rc = launch_core_rows(a, l, ws, st);
+        if (rc != COLI_OK) return rc;
+        rc = proj_rows(m.o_proj, ctx, a.out, S, st);
+        if (rc != COLI_OK || a.hsum == nullptr) return rc;
+        return launch_residual_add(a.resid, a.out, a.hsum, (int64_t)S * m.o_proj->O, st);
+    }
     // q_a and kv_a (the layer's input norm folded in when the matrix-core
     // kernel takes it, else a norm launch first)
     bool done = false;
@@ -630,12 +687,7 @@ int launch_mla_decode(const MlaArgs &a) {
         rc = launch_gemv(m.q_b, cq, q, S, st);
         if (rc != COLI_OK) return rc;
     }
-    switch (S) {
-        case 1: rc = launch_core<1>(a, l, ws, st); break;
-        case 2: rc = launch_core<2>(a, l, ws, st); break;
-        case 3: rc = launch_core<3>(a, l, ws, st); break;
-        default: rc = launch_core<4>(a, l, ws, st); break;
-    }
+    rc = launch_core_rows(a, l, ws, st);
     if (rc != COLI_OK) return rc;
     return launch_gemv(m.o_proj, ctx, a.out, S, st, a.resid, a.hsum);
 }

@@ -436,6 +436,8 @@ typedef struct coli_mla_layer {
 } coli_mla_layer;
 
 #define COLI_MLA_STAGES 10
+/* Most query rows one coli_mla_decode / coli_layer_decode call takes. */
+#define COLI_MLA_MAX_ROWS 4096
 /* Workspace bytes of coli_mla_decode for S rows and caches of T_cap rows
  * (0 on bad input). */
 size_t coli_mla_workspace_bytes(const coli_mla_layer *layer, int S, int T_cap);
@@ -448,14 +450,19 @@ size_t coli_mla_workspace_bytes(const coli_mla_layer *layer, int S, int T_cap);
 size_t coli_mla_workspace_layout(const coli_mla_layer *layer, int S, int T_cap,
                                  size_t offsets[COLI_MLA_STAGES]);
 /*
- * coli_mla_decode -- the decode attention for S = 1..4 rows x [S][D] at
- * positions pos_base .. pos_base + S - 1:
+ * coli_mla_decode -- the attention for S = 1..COLI_MLA_MAX_ROWS rows x [S][D]
+ * at positions pos_base .. pos_base + S - 1 (S <= 4: decode; more rows:
+ * prefill, the same steps for every row, row s attending keys 0 ..
+ * pos_base + s):
  *   writes cache rows Lc[pos_base + s] (f32 [T_cap][L]) and Rc[pos_base + s]
  *   (f32 [T_cap][d_rope]); reads rows 0 .. pos_base + s for row s (rows below
  *   pos_base are the earlier tokens', supplied by the caller);
  *   out f32 [S][D] = o_proj ctx.
- * Requires pos_base >= 0 and pos_base + S <= T_cap.  The projections run the
- * decode GEMV kernels (coli_qmatmul's bounds); the core is fp32.  Nothing is
+ * Requires pos_base >= 0 and pos_base + S <= T_cap.  The projections run
+ * coli_qmatmul's kernels with its bounds (S <= 4: the fp32 decode GEMVs;
+ * more rows: the bf16 prefill GEMMs); the core is fp32, run on chunks of
+ * 4 rows in order (each chunk's cache rows are written before the next
+ * chunk's scores read them).  Nothing is
  * allocated and the host never waits (graph-capturable).  x, out, Lc, Rc and
  * the workspace must not overlap.
  *   workspace: coli_mla_workspace_bytes(layer, S, T_cap) bytes, 256-byte
@@ -476,11 +483,12 @@ int coli_mla_decode(const coli_mla_layer *layer, const float *x, int S, int pos_
  *   h   = x + a                                               (f32)
  *   out = coli_moe_layer(h, post_ln, eps, R, bias, K, topp, norm_topk,
  *                        routed_scale; experts gate/up/down, shared expert)
- * Arguments as in those calls (S = 1..4; in_ln, post_ln, bias and the shared
- * expert may be NULL); out may equal x.  Everything is validated before the
+ * Arguments as in those calls (S = 1..COLI_MLA_MAX_ROWS: S <= 4 decode, more
+ * rows prefill with coli_mla_decode's and coli_moe_layer's prefill kernels;
+ * in_ln, post_ln, bias and the shared expert may be NULL); out may equal x.  Everything is validated before the
  * first launch; nothing is allocated and the host never waits.  Where the
- * matrix-core decode kernels run, the two norms and both residual adds are
- * folded into neighbouring launches (11 launches per layer instead of 16):
+ * matrix-core decode kernels run (S <= 4), the two norms and both residual
+ * adds are folded into neighbouring launches (11 launches per layer instead of 16):
  * the residual adds and the post_ln norm give the bits the separate steps
  * give; the in_ln norm sums its squares in another order, so xn may differ
  * from coli_rmsnorm's in the last place (both within one f32 rounding of the

@@ -20,7 +20,7 @@ import torch
 
 import bit_gemv_coli_amd as coli
 import synthdata as sd
-from gpu_util import TOL_FP32, assert_within, decode_kernels, need_gpu, qtensor, rep_allowance, to_dev
+from gpu_util import TOL_BF16, TOL_FP32, assert_within, decode_kernels, need_gpu, qtensor, rep_allowance, to_dev
 from oracle import MlaWeights, QMat
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +71,10 @@ def _run(layer, x, pb, Lc, Rc, T):
 def _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage, packed=True):
     S = x.shape[0]
     H, dn, dr, dv, L, qr = W.H, W.dn, W.dr, W.dv, W.kv_b.I, W.q_a.O
-    rep = (lambda M, inp: rep_allowance(orc, M, inp)) if packed else (lambda M, inp: None)
+    # more than 4 rows: the projections run the bf16 prefill kernels
+    tol = TOL_FP32 if S <= 4 else TOL_BF16
+    rep = ((lambda M, inp: rep_allowance(orc, M, inp)) if packed and S <= 4
+           else (lambda M, inp: None))
     cq_raw = stage("cq_raw", (S, qr))
     ckv = stage("ckv_raw", (S, L + dr))
     cq = stage("cq", (S, qr))
@@ -85,7 +88,7 @@ def _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage, packed=True):
     # projections from x
     for M, y, nm in ((W.q_a, cq_raw, "q_a"), (W.kv_a, ckv, "kv_a")):
         yr, A = orc.qmatmul(M, x)
-        assert_within(y, yr, A, TOL_FP32, nm, rep(M, x))
+        assert_within(y, yr, A, tol, nm, rep(M, x))
     # norms, rotary key, cache rows
     ref = orc.rmsnorm(cq_raw, W.q_norm, W.eps)
     assert np.all(np.abs(cq - ref) <= 2.0 ** -22 * np.abs(ref) + 1e-30), "q latent norm"
@@ -105,7 +108,7 @@ def _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage, packed=True):
         "cache rows outside this call's positions changed"
     # q_b
     yr, A = orc.qmatmul(W.q_b, cq)
-    assert_within(q, yr, A, TOL_FP32, "q_b", rep(W.q_b, cq))
+    assert_within(q, yr, A, tol, "q_b", rep(W.q_b, cq))
     # rotary part of the query
     qh = q.reshape(S, H, dn + dr)
     for s in range(S):
@@ -140,14 +143,16 @@ def _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage, packed=True):
     ref, A = orc.mla_ctx(W.kv_b, H, dn, dv, clat)
     assert_within(ctx, ref, A, TOL_FP32, "ctx")
     yr, A = orc.qmatmul(W.o_proj, ctx)
-    assert_within(out, yr, A, TOL_FP32, "o_proj", rep(W.o_proj, ctx))
-    # end to end against the oracle's f64 chain: within 1e-4 of the output
-    # projection's magnitude (the sum of the steps' bounds, carried through
-    # the softmax, stays well inside it for these inputs)
+    assert_within(out, yr, A, tol, "o_proj", rep(W.o_proj, ctx))
+    # end to end against the oracle's f64 chain: within 1e-4 (fp32
+    # projections) or 5e-2 (bf16 projections, S > 4) of the output
+    # projection's magnitude -- the sum of the steps' bounds, carried through
+    # the softmax, stays inside it for these inputs
     o_ref, st, Lc_ref, Rc_ref = orc.mla_decode(W, x, pb, Lc, Rc)
     _, A_o = orc.qmatmul(W.o_proj, np.abs(st["ctx"]).astype(np.float32))
     err = np.abs(out - o_ref)
-    assert np.all(err <= 1e-4 * A_o + 1e-30), f"end to end: max err/A {np.max(err / A_o):.3e}"
+    e2e = 1e-4 if S <= 4 else 5e-2
+    assert np.all(err <= e2e * A_o + 1e-30), f"end to end: max err/A {np.max(err / A_o):.3e}"
     return float(np.max(err / A_o))
 
 
@@ -173,6 +178,29 @@ def test_mla_decode_small_dims_long_context(orc, S, pb, T):
     W, layer, x, Lc, Rc, T = _setup(90 + S + pb, S, pb, SMALL, T=T)
     out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
     _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
+
+
+PREFILL = [(5, 0, None), (9, 7, None), (13, 3, 20), (40, 0, 48), (27, 61, 100)]
+
+
+@pytest.mark.parametrize("S,pb,T", PREFILL, ids=[f"S{S}-pos{pb}-T{T}" for S, pb, T in PREFILL])
+def test_mla_prefill_small_dims(orc, S, pb, T):
+    """More than 4 rows (prefill): the projections on the bf16 prefill
+    kernels, the core in chunks of 4 rows, row s attending keys up to
+    pos_base + s -- including chunks whose keys are the earlier chunks' new
+    cache rows."""
+    need_gpu()
+    W, layer, x, Lc, Rc, T = _setup(300 + S + pb, S, pb, SMALL, T=T)
+    out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
+    _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
+
+
+def test_mla_prefill_full_dims(orc):
+    """24 rows at position 37 at the layer's real dimensions."""
+    need_gpu()
+    W, layer, x, Lc, Rc, T = _setup(330, 24, 37, FULL)
+    out, Lc1, Rc1, stage = _run(layer, x, 37, Lc, Rc, T)
+    _check(orc, W, x, 37, Lc, Rc, T, out, Lc1, Rc1, stage)
 
 
 @pytest.mark.parametrize("kmode", [0, 1], ids=["mfma", "valu"])
@@ -205,8 +233,9 @@ def test_mla_decode_rows_match_single_row_calls(orc):
 
 
 def test_mla_decode_declines():
-    """Host-side refusals: positions past the cache, S > 4, a too-small
-    workspace; nothing is launched."""
+    """Host-side refusals: positions past the cache, more rows than the
+    workspace was sized for or than COLI_MLA_MAX_ROWS, a too-small workspace;
+    nothing is launched."""
     need_gpu()
     W, layer, x, Lc, Rc, T = _setup(150, 2, 3, SMALL)
     total = coli.coli_mla_workspace_bytes(layer, 2, T)
@@ -217,4 +246,5 @@ def test_mla_decode_declines():
     assert coli.coli_mla_decode(layer, xd, 2, T - 1, Lc_d, Rc_d, T, out, ws, total) == 0
     assert coli.coli_mla_decode(layer, xd, 5, 0, Lc_d, Rc_d, T, out, ws, total) == 0
     assert coli.coli_mla_decode(layer, xd, 2, 0, Lc_d, Rc_d, T, out, ws, total - 256) == 0
+    assert coli.coli_mla_workspace_bytes(layer, coli.COLI_MLA_MAX_ROWS + 1, 1 << 14) == 0
     assert coli.coli_stats()[2] == n0
