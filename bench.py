@@ -139,7 +139,9 @@ def main():
         print(json.dumps(layer_stream(coli, sd, np, torch, log)), flush=True)
         return
     if args.layer_decode_only:
-        print(json.dumps(full_layer_stream(coli, sd, np, torch, log)), flush=True)
+        out = full_layer_stream(coli, sd, np, torch, log)
+        out.update(attention_prefill(coli, sd, np, torch, log))
+        print(json.dumps(out), flush=True)
         return
     if args.router_only:
         print(json.dumps(router_measurements(coli, sd, np, torch, log, make_timed(torch))), flush=True)
@@ -390,6 +392,9 @@ def summary(e, value, roofline):
     pd = e.get("prefill_dense_544x6144x6144_g128")
     if pd:
         out["prefill_dense_544x6144x6144"] = {"TFLOPs": pd["TFLOPs"], "frac_bf16_peak": pd["frac_bf16_peak"]}
+    ap = e.get("mla_prefill_544")
+    if ap:
+        out["mla_prefill_544"] = {"us_per_layer": ap["us_per_layer"], "TFLOPs": ap["TFLOPs"]}
     return out
 
 
@@ -422,6 +427,7 @@ def side_measurements(coli, sd, np, torch, log):
     out.update(prefill_measurements(coli, sd, np, torch, log, timed))
     out.update(layer_stream(coli, sd, np, torch, log))
     out.update(full_layer_stream(coli, sd, np, torch, log))
+    out.update(attention_prefill(coli, sd, np, torch, log))
     return out
 
 
@@ -692,6 +698,78 @@ def ceiling_probes(coli, torch, log):
                                   "stream_read_frac_spec": read_gbs / HBM_PEAK_GBS,
                                   "mfma_bf16_frac_spec": mfma_tf / BF16_PEAK_TFLOPS,
                                   "launch_floor_us": floor}}
+
+
+def attention_prefill(coli, sd, np, torch, log, S=544, T_cap=1024, passes=5):
+    """One MLA attention layer over a 544-token prompt (S = 544 rows from
+    position 0, caches of 1024 rows): q_a, kv_a, q_b and o_proj on the bf16
+    prefill GEMMs, the fp32 core on chunks of 4 rows; fmt 4 gs 64 at the
+    layer's real dimensions.  FLOPs: the projections 2 S (qr D + (L + dr) D +
+    H (dn + dr) qr + D H dv), the core (causal: row s has s + 1 keys) 2 H
+    (dn L (S rows) + (L + dr) K + L K + L dv (S rows)) with K = the keys
+    summed over the rows."""
+    dev = "cuda"
+    gs, H, dn, dr, dv, qr, Lat = 64, 64, 192, 64, 256, 1536, 512
+    shapes = [(qr, D), (H * (dn + dr), qr), (Lat + dr, D), (H * (dn + dv), Lat), (D, H * dv)]
+    P = [sd.pool_on_device(40000 + i, 4, 1, o, i_, gs) for i, (o, i_) in enumerate(shapes)]
+    TP = [coli.QTensor(4, q[0], s_[0], o, i_, gs, n=1) for (q, s_), (o, i_) in zip(P, shapes)]
+    for t in TP[:3] + TP[4:]:
+        t.pack()
+    qn = torch.rand(qr, device=dev) + 0.5
+    kn = torch.rand(Lat, device=dev) + 0.5
+    layer = coli.MlaLayer(*TP, qn, kn, H, dn, dr, dv, 1e-6, 10000.0)
+    Lc = torch.zeros((T_cap, Lat), device=dev)
+    Rc = torch.zeros((T_cap, dr), device=dev)
+    x = torch.randn((S, D), device=dev)
+    out = torch.empty((S, D), device=dev)
+    wsb = coli.coli_mla_workspace_bytes(layer, S, T_cap)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def call(st):
+        coli.check(coli.coli_mla_decode(layer, x, S, 0, Lc, Rc, T_cap, out, ws, wsb, st),
+                   "coli_mla_decode")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    a.record(st)
+    for _ in range(passes):
+        graph.replay()
+    b.record(st)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / passes * 1e3
+    del graph
+    keys = S * (S + 1) // 2
+    proj = 2.0 * S * (qr * D + (Lat + dr) * D + H * (dn + dr) * qr + D * H * dv)
+    core = 2.0 * H * (dn * Lat * S + (Lat + dr) * keys + Lat * keys + Lat * dv * S)
+    # per-kernel split from one eager call with the library's events
+    coli.coli_prof_reset()
+    coli.coli_prof_enable(True)
+    call(st)
+    torch.cuda.synchronize()
+    coli.coli_prof_enable(False)
+    kern = {}
+    for tag in coli.coli_prof_tags():
+        n, tot = coli.coli_prof_read(tag)
+        if n > 0:
+            kern[tag] = {"launches": n, "total_us": tot * 1e3}
+    log(f"MLA prefill attention S={S}: {us:.0f} us per layer, "
+        f"{(proj + core) / us / 1e6:.1f} TFLOP/s ({proj / 1e9:.1f} GF projections, "
+        f"{core / 1e9:.1f} GF core)")
+    del TP, P, ws
+    torch.cuda.empty_cache()
+    return {"mla_prefill_544": {"us_per_layer": us, "ms_per_75_layers": us * 75 / 1e3,
+                                "TFLOPs": (proj + core) / us / 1e6, "GF_projections": proj / 1e9,
+                                "GF_core": core / 1e9, "kernels_eager": kern}}
 
 
 def full_layer_stream(coli, sd, np, torch, log, layers=75, pool=20, passes=5, pos=544,

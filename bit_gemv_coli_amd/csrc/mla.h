@@ -19,8 +19,14 @@ static_assert(MLA_NSTAGE == COLI_MLA_STAGES, "stage count");
 constexpr int MLA_QA_SPLIT = 4;
 // score splits over the L + d_rope components
 constexpr int MLA_SC_SPLIT = 3;
-// query rows per run of the core kernels (more rows: several runs in order)
+// query rows per workgroup of the absorption kernels, and rows per launch set
+// of the core (more rows: several sets in order; a multiple of MLA_CHUNK)
 constexpr int MLA_CHUNK = 4;
+#ifndef COLI_MLA_GROUP
+#define COLI_MLA_GROUP 64
+#endif
+constexpr int MLA_GROUP = COLI_MLA_GROUP;
+static_assert(MLA_GROUP % MLA_CHUNK == 0, "whole chunks per group");
 
 struct MlaLayout {
     size_t off[MLA_NSTAGE];

@@ -122,10 +122,18 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
                                                          const float *__restrict__ ckv,
                                                          const float *__restrict__ kn, double eps,
                                                          float *__restrict__ Lc,
-                                                         float *__restrict__ Rc) {
+                                                         float *__restrict__ Rc, int nrows,
+                                                         int rbase) {
     __shared__ float red[QA_NW][S][QA_COLS];
     const int h = blockIdx.x, split = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // this workgroup's S rows: rz .. rz + S - 1 of a group of nrows (the
+    // partials' row count), MLA_CHUNK rows per blockIdx.z
+    const int rz = rbase + MLA_CHUNK * (int)blockIdx.z;
+    q += (int64_t)rz * H * (dn + dr);
+    qpe += (int64_t)rz * H * dr;
+    ckv += (int64_t)rz * (L + dr);
+    pos_base += rz;
     if (h == H) {
         __shared__ double npart[QA_NW];
         const int s = split;
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
                 float v = red[0][s][c];
 #pragma unroll
                 for (int w = 1; w < QA_NW; ++w) v += red[w][s][c];
-                part[(((int64_t)split * S + s) * H + h) * L + col0 + c] = v;
+                part[(((int64_t)split * nrows + rz + s) * H + h) * L + col0 + c] = v;
             }
         }
         __syncthreads();
@@ -390,9 +398,15 @@ template <int S, bool GRP>
 __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int dv, int L,
                                                  int pos_base, const float *__restrict__ cl_part,
                                                  float *__restrict__ clat,
-                                                 float *__restrict__ ctx) {
+                                                 float *__restrict__ ctx, int nrows, int rbase) {
     extern __shared__ __attribute__((aligned(16))) float cl[];  // [S][L]
     const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // rows rz .. rz + S - 1 of a group of nrows (the partials' row count)
+    const int rz = rbase + MLA_CHUNK * (int)blockIdx.z;
+    cl_part += (int64_t)rz * H * L;
+    clat += (int64_t)rz * H * L;
+    ctx += (int64_t)rz * H * dv;
+    pos_base += rz;
     // clat = the key chunks' partials of row s, added in chunk order; the
     // first row tile stores it
     for (int i = tid; i < S * L; i += 256) {
@@ -400,7 +414,7 @@ __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int d
         const int nchunk = (pos_base + s + 1 + CL_KEYS - 1) / CL_KEYS;
         const float *pp = cl_part + ((int64_t)s * H + h) * L + c;
         float v = pp[0];
-        for (int k = 1; k < nchunk; ++k) v += pp[(int64_t)k * S * H * L];
+        for (int k = 1; k < nchunk; ++k) v += pp[(int64_t)k * nrows * H * L];
         cl[i] = v;
         if (blockIdx.y == 0)
             clat[((int64_t)s * H + h) * L + c] = v;
@@ -468,8 +482,8 @@ MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tc
     l.off[MLA_P] = take((size_t)S * H * Tcap);
     l.off[MLA_CLAT] = take((size_t)S * H * L);
     l.off[MLA_CTX] = take((size_t)S * H * dv);
-    // the core runs on chunks of at most MLA_CHUNK rows: partial sums for one
-    const int Sc = S < MLA_CHUNK ? S : MLA_CHUNK;
+    // the core runs on groups of at most MLA_GROUP rows: partial sums for one
+    const int Sc = S < MLA_GROUP ? S : MLA_GROUP;
     l.qabs_part = take((size_t)MLA_QA_SPLIT * Sc * H * L);
     l.sc_part = take((size_t)MLA_SC_SPLIT * Sc * H * Tcap);
     l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * Sc * H * L);
@@ -495,10 +509,45 @@ static int gemv_pair(const coli_qtensor *A, const coli_qtensor *B, const float *
     return launch_gemv(B, x, yb, S, st);
 }
 
-// The core for rows r0 .. r0 + S - 1 (S <= MLA_CHUNK) at positions pos_base +
-// r0 ..: stage pointers start at row r0, partial sums are the chunk's own.
-template <int S>
-static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st, int r0) {
+// chunked launch of the key absorption or the value absorption: rows
+// rbase + 4 z .. of a group of nrows, MLA_CHUNK rows per workgroup along z
+template <int SC>
+static void qabs_launch(bool grp, unsigned nz, int rbase, int nrows, const MlaKvb &kb, int H,
+                        int dn, int dr, int dv, int L, const float *q, int pos_base, double theta,
+                        float *part, float *qpe, const float *ckv, const float *kn, double eps,
+                        float *Lc, float *Rc, hipStream_t st) {
+    // (one more column of workgroups for the key side of the new rows)
+    static_assert(MLA_QA_SPLIT >= MLA_CHUNK, "a workgroup per new row of a chunk");
+    const dim3 grid((unsigned)H + 1, (unsigned)MLA_QA_SPLIT, nz);
+    if (grp)
+        hipLaunchKernelGGL((k_mla_qabs<SC, true>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn, dr, dv,
+                           L, q, pos_base, theta, part, qpe, ckv, kn, eps, Lc, Rc, nrows, rbase);
+    else
+        hipLaunchKernelGGL((k_mla_qabs<SC, false>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn, dr,
+                           dv, L, q, pos_base, theta, part, qpe, ckv, kn, eps, Lc, Rc, nrows, rbase);
+}
+
+template <int SC>
+static void ctx_launch(bool grp, unsigned nz, int rbase, int nrows, const MlaKvb &kb, int H,
+                       int dn, int dv, int L, int pos_base, const float *cl_part, float *clat,
+                       float *ctx, hipStream_t st) {
+    const dim3 grid((unsigned)H, (unsigned)((dv + CX_ROWS - 1) / CX_ROWS), nz);
+    const size_t lds = (size_t)SC * L * sizeof(float);
+    if (grp)
+        hipLaunchKernelGGL((k_mla_ctx<SC, true>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
+                           pos_base, cl_part, clat, ctx, nrows, rbase);
+    else
+        hipLaunchKernelGGL((k_mla_ctx<SC, false>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
+                           pos_base, cl_part, clat, ctx, nrows, rbase);
+}
+
+// The core for a group of G rows r0 .. r0 + G - 1 (G <= MLA_GROUP) at
+// positions pos_base + r0 ..: stage pointers start at row r0, the partial
+// sums are the group's own.  The key and value absorptions run MLA_CHUNK rows
+// per workgroup (whole chunks in one launch, a last partial chunk in a second);
+// scores and softmax take the G rows directly.
+static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st, int r0,
+                       int G) {
     const coli_mla_layer &m = *a.layer;
     const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v;
     const int L = m.kv_b->I;
@@ -518,78 +567,80 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     float *p = (float *)(ws + l.off[MLA_P]) + R * H * a.T_cap;
     float *clat = (float *)(ws + l.off[MLA_CLAT]) + R * H * L;
     float *ctx = (float *)(ws + l.off[MLA_CTX]) + R * H * dv;
+    const float *ckv = (const float *)(ws + l.off[MLA_CKV_RAW]) + R * (L + dr);
     float *part = (float *)(ws + l.qabs_part);
     float *sc_part = (float *)(ws + l.sc_part);
     float *cl_part = (float *)(ws + l.cl_part);
     const double theta = (double)m.rope_theta;
+    const double eps = (double)m.eps;
+    const unsigned nfull = (unsigned)(G / MLA_CHUNK);
+    const int rem = G % MLA_CHUNK, rrem = (int)nfull * MLA_CHUNK;
     {
         ProfScope ps("mla_qabs", st);
-        // (one more column of workgroups for the key side of the new rows)
-        static_assert(MLA_QA_SPLIT >= 4, "a workgroup per new row");
-        const dim3 grid((unsigned)H + 1, (unsigned)MLA_QA_SPLIT);
-        const float *ckv = (const float *)(ws + l.off[MLA_CKV_RAW]) + R * (L + dr);
-        if (grp)
-            hipLaunchKernelGGL((k_mla_qabs<S, true>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn, dr,
-                               dv, L, q, pos_base, theta, part, qpe, ckv, m.kv_norm,
-                               (double)m.eps, a.Lc, a.Rc);
-        else
-            hipLaunchKernelGGL((k_mla_qabs<S, false>), grid, dim3(QA_NW * 64), 0, st, kb, H, dn,
-                               dr, dv, L, q, pos_base, theta, part, qpe, ckv, m.kv_norm,
-                               (double)m.eps, a.Lc, a.Rc);
+        if (nfull > 0)
+            qabs_launch<MLA_CHUNK>(grp, nfull, 0, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st);
+        switch (rem) {
+            case 1: qabs_launch<1>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
+            case 2: qabs_launch<2>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
+            case 3: qabs_launch<3>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
+            default: break;
+        }
         const int rc = after_launch("mla_qabs");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_scores", st);
-        const int nkeys = pos_base + S;
+        const int nkeys = pos_base + G;
         const dim3 grid((unsigned)((nkeys + SC_KEYS - 1) / SC_KEYS),
-                        (unsigned)((H + SC_HEADS - 1) / SC_HEADS), (unsigned)(S * MLA_SC_SPLIT));
+                        (unsigned)((H + SC_HEADS - 1) / SC_HEADS), (unsigned)(G * MLA_SC_SPLIT));
         hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
-                           (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, S, H, L,
+                           (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H, L,
                            dr, pos_base, a.T_cap, qabs, sc_part);
         const int rc = after_launch("mla_scores");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_softmax_clat", st);
-        const int nkeys = pos_base + S;
+        const int nkeys = pos_base + G;
         const float scale = (float)(1.0 / sqrt((double)(dn + dr)));
         const dim3 grid((unsigned)((nkeys + CL_KEYS - 1) / CL_KEYS),
                         (unsigned)((L + CL_COLS - 1) / CL_COLS),
-                        (unsigned)(S * ((H + CL_HEADS - 1) / CL_HEADS)));
+                        (unsigned)(G * ((H + CL_HEADS - 1) / CL_HEADS)));
         hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
-                           (const float *)a.Lc, S, H, L, pos_base, a.T_cap, scale, sc, p, cl_part);
+                           (const float *)a.Lc, G, H, L, pos_base, a.T_cap, scale, sc, p, cl_part);
         const int rc = after_launch("mla_softmax_clat");
         if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_ctx", st);
-        const dim3 grid((unsigned)H, (unsigned)((dv + CX_ROWS - 1) / CX_ROWS));
-        const size_t lds = (size_t)S * L * sizeof(float);
-        if (grp)
-            hipLaunchKernelGGL((k_mla_ctx<S, true>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
-                               pos_base, (const float *)cl_part, clat, ctx);
-        else
-            hipLaunchKernelGGL((k_mla_ctx<S, false>), grid, dim3(256), lds, st, kb, H, dn, dv, L,
-                               pos_base, (const float *)cl_part, clat, ctx);
+        if (nfull > 0)
+            ctx_launch<MLA_CHUNK>(grp, nfull, 0, G, kb, H, dn, dv, L, pos_base, cl_part, clat, ctx,
+                                  st);
+        switch (rem) {
+            case 1: ctx_launch<1>(grp, 1, rrem, G, kb, H, dn, dv, L, pos_base, cl_part, clat, ctx,
+                                  st); break;
+            case 2: ctx_launch<2>(grp, 1, rrem, G, kb, H, dn, dv, L, pos_base, cl_part, clat, ctx,
+                                  st); break;
+            case 3: ctx_launch<3>(grp, 1, rrem, G, kb, H, dn, dv, L, pos_base, cl_part, clat, ctx,
+                                  st); break;
+            default: break;
+        }
         const int rc = after_launch("mla_ctx");
         if (rc != COLI_OK) return rc;
     }
     return COLI_OK;
 }
 
-// the core over all S rows, MLA_CHUNK rows per launch set (each chunk's key
-// rows are in the caches before the next chunk's scores read them)
+// the core over all S rows, MLA_GROUP rows per launch set (each group's key
+// rows are in the caches before the next group's scores read them)
 static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st) {
-    for (int r0 = 0; r0 < a.S; r0 += MLA_CHUNK) {
-        const int n = a.S - r0 < MLA_CHUNK ? a.S - r0 : MLA_CHUNK;
-        int rc;
-        switch (n) {
-            case 1: rc = launch_core<1>(a, l, ws, st, r0); break;
-            case 2: rc = launch_core<2>(a, l, ws, st, r0); break;
-            case 3: rc = launch_core<3>(a, l, ws, st, r0); break;
-            default: rc = launch_core<4>(a, l, ws, st, r0); break;
-        }
+    for (int r0 = 0; r0 < a.S; r0 += MLA_GROUP) {
+        const int G = a.S - r0 < MLA_GROUP ? a.S - r0 : MLA_GROUP;
+        const int rc = launch_core(a, l, ws, st, r0, G);
         if (rc != COLI_OK) return rc;
     }
     return COLI_OK;
