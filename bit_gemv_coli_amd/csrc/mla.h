@@ -31,6 +31,7 @@ static_assert(MLA_GROUP % MLA_CHUNK == 0, "whole chunks per group");
 struct MlaLayout {
     size_t off[MLA_NSTAGE];
     size_t qabs_part, sc_part, cl_part;  // partial sums (internal)
+    size_t stats;                        // prefill rows: softmax max and sum per (row, head)
     size_t total;
 };
 MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap);

@@ -212,6 +212,10 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
 }
 
 // ---- scores ----------------------------------------------------------------
+// query rows per workgroup of the prefill scores kernel
+#ifndef COLI_MLA_SCORE_ROWS
+#define COLI_MLA_SCORE_ROWS 4
+#endif
 // Partial scores over one third of the L + d_rope components (Q = [qabs,
 // qpe], K = [Lc, Rc]): grid (64-key tiles, 4-head groups, row x MLA_SC_SPLIT).
 // A workgroup takes 4 heads (one per wavefront) x 64 keys (one per lane);
@@ -304,6 +308,121 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
         sc_part[(((int64_t)split * S + s) * H + h) * Tcap + t] = tot;
 }
 
+// Prefill rows: the same partial scores with R query rows per workgroup, so
+// each key chunk staged in LDS serves R rows x 4 heads.  grid (64-key tiles,
+// 4-head groups, ceil(S / R) row blocks x MLA_SC_SPLIT); rows past S and keys
+// past a row's last position are neither loaded nor stored.  Each thread sums
+// its R products over a chunk four components at a time (one 16-byte
+// broadcast read of every row's query values, four key reads).
+template <int R>
+__global__ __launch_bounds__(256) void k_mla_scores_rows(const float *__restrict__ part,
+                                                         const float *__restrict__ qpe,
+                                                         const float *__restrict__ Lc,
+                                                         const float *__restrict__ Rc, int S,
+                                                         int H, int L, int dr, int pos_base,
+                                                         int Tcap, float *__restrict__ qabs,
+                                                         float *__restrict__ sc_part) {
+    __shared__ float kt[2][SC_KEYS][SC_CH + 1];
+    __shared__ __attribute__((aligned(16))) float qt[2][R][SC_HEADS][SC_CH];
+    const int t0 = blockIdx.x * SC_KEYS, h0 = blockIdx.y * SC_HEADS;
+    const int rb0 = R * (int)(blockIdx.z / MLA_SC_SPLIT), split = blockIdx.z % MLA_SC_SPLIT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nr = min(R, S - rb0);                 // rows of this block
+    const int last_max = pos_base + rb0 + nr - 1;   // keys 0 .. last of its last row
+    if (t0 > last_max)
+        return;
+    const int C = L + dr;
+    const int nch_all = (C + SC_CH - 1) / SC_CH;
+    const int per = (nch_all + MLA_SC_SPLIT - 1) / MLA_SC_SPLIT;
+    const int ch0 = split * per, ch1 = min(nch_all, ch0 + per);
+    const int64_t pstride = (int64_t)S * H * L;
+    constexpr int NQ = R * SC_HEADS * SC_CH / 256;  // query values per thread and chunk
+    float kr[SC_KEYS * SC_CH / 256], qv[NQ];
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
+            const int idx = tid + 256 * i, key = idx / SC_CH, cc = idx % SC_CH;
+            const int t = t0 + key, c = c0 + cc;
+            float v = 0.f;
+            if (t <= last_max && c < C)
+                v = c < L ? Lc[(int64_t)t * L + c] : Rc[(int64_t)t * dr + (c - L)];
+            kr[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx / (SC_HEADS * SC_CH), hh = (idx / SC_CH) % SC_HEADS, cc = idx % SC_CH;
+            const int s = rb0 + r, h = h0 + hh, c = c0 + cc;
+            float v = 0.f;
+            if (r < nr && h < H && c < C) {
+                if (c < L) {
+                    const float *pp = part + ((int64_t)s * H + h) * L + c;
+                    v = pp[0];
+#pragma unroll
+                    for (int k = 1; k < MLA_QA_SPLIT; ++k) v += pp[k * pstride];
+                } else {
+                    v = qpe[((int64_t)s * H + h) * dr + (c - L)];
+                }
+            }
+            qv[i] = v;
+        }
+    };
+    auto store = [&](int buf, int c0) {
+#pragma unroll
+        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
+            const int idx = tid + 256 * i;
+            kt[buf][idx / SC_CH][idx % SC_CH] = kr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx / (SC_HEADS * SC_CH), hh = (idx / SC_CH) % SC_HEADS, cc = idx % SC_CH;
+            qt[buf][r][hh][cc] = qv[i];
+            if (blockIdx.x == 0 && r < nr && h0 + hh < H && c0 + cc < L)
+                qabs[((int64_t)(rb0 + r) * H + h0 + hh) * L + c0 + cc] = qv[i];
+        }
+    };
+    float tot[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) tot[r] = 0.f;
+    if (ch0 < ch1) {
+        fetch(ch0 * SC_CH);
+        store(0, ch0 * SC_CH);
+    }
+    __syncthreads();
+    for (int ch = ch0; ch < ch1; ++ch) {
+        const int buf = (ch - ch0) & 1;
+        if (ch + 1 < ch1)
+            fetch((ch + 1) * SC_CH);
+        float a[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) a[r] = 0.f;
+#pragma unroll 4
+        for (int cc = 0; cc < SC_CH; cc += 4) {
+            const float k0 = kt[buf][lane][cc], k1 = kt[buf][lane][cc + 1];
+            const float k2 = kt[buf][lane][cc + 2], k3 = kt[buf][lane][cc + 3];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const f32x4 qq = *reinterpret_cast<const f32x4 *>(&qt[buf][r][wave][cc]);
+                a[r] = fmaf(qq.x, k0, a[r]);
+                a[r] = fmaf(qq.y, k1, a[r]);
+                a[r] = fmaf(qq.z, k2, a[r]);
+                a[r] = fmaf(qq.w, k3, a[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) tot[r] += a[r];
+        if (ch + 1 < ch1)
+            store(buf ^ 1, (ch + 1) * SC_CH);
+        __syncthreads();
+    }
+    const int t = t0 + lane, h = h0 + wave;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < nr && t <= pos_base + rb0 + r && h < H)
+            sc_part[(((int64_t)split * S + rb0 + r) * H + h) * Tcap + t] = tot[r];
+}
+
 // ---- softmax and the latent context ----------------------------------------
 // grid (64-key chunks, 64-column tiles, 4-head groups x rows).  Each wavefront
 // first forms its head's scores z_t = scale * (sum of the score splits in
@@ -316,6 +435,10 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
 constexpr int CL_COLS = 64;
 constexpr int CL_HEADS = 4;
 constexpr int CL_KEYS = 64;
+// query rows per workgroup of the prefill latent-context kernel
+#ifndef COLI_MLA_CLAT_ROWS
+#define COLI_MLA_CLAT_ROWS 4
+#endif
 
 __device__ __forceinline__ float mla_score(const float *__restrict__ sc_part, int64_t sstride,
                                            int64_t at, float scale) {
@@ -384,6 +507,110 @@ __global__ __launch_bounds__(256) void k_mla_softmax_clat(const float *__restric
     const int c = c0 + lane;
     if (h < H && c < L)
         cl_part[(((int64_t)chunk * S + s) * H + h) * L + c] = a;
+}
+
+// Prefill rows: the softmax statistics once per (row, head) -- the same
+// strided max and sum of exp(z - max) as above, in the same order -- into
+// stats[(s H + h) 2 + {0, 1}]; grid (rows, 4-head groups), a wavefront per head.
+__global__ __launch_bounds__(256) void k_mla_softmax_stats(const float *__restrict__ sc_part,
+                                                           int S, int H, int pos_base, int Tcap,
+                                                           float scale, float *__restrict__ stats) {
+    const int s = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.y * CL_HEADS + wave;
+    if (h >= H)
+        return;  // whole wavefront
+    const int n = pos_base + s + 1;
+    const int64_t sstride = (int64_t)S * H * Tcap;
+    const int64_t zrow = ((int64_t)s * H + h) * Tcap;
+    float m = -__builtin_inff();
+    for (int t = lane; t < n; t += 64) m = fmaxf(m, mla_score(sc_part, sstride, zrow + t, scale));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float e = 0.f;
+    for (int t = lane; t < n; t += 64) e += expf(mla_score(sc_part, sstride, zrow + t, scale) - m);
+    e = wave_sum(e);
+    if (lane == 0) {
+        stats[((int64_t)s * H + h) * 2] = m;
+        stats[((int64_t)s * H + h) * 2 + 1] = e;
+    }
+}
+
+// Prefill rows: probabilities and the latent-context partials with R query
+// rows per workgroup sharing one staged chunk of Lc rows; grid (64-key chunks,
+// 64-column tiles, ceil(S / R) row blocks x 4-head groups).  p and each
+// chunk's sum are formed exactly as in k_mla_softmax_clat (same statistics,
+// same order of the 64 products), so the results are the same bits.
+template <int R>
+__global__ __launch_bounds__(256) void k_mla_clat_rows(const float *__restrict__ sc_part,
+                                                       const float *__restrict__ stats,
+                                                       const float *__restrict__ Lc, int S, int H,
+                                                       int L, int pos_base, int Tcap, float scale,
+                                                       float *__restrict__ scores,
+                                                       float *__restrict__ p,
+                                                       float *__restrict__ cl_part) {
+    __shared__ float lt[CL_KEYS][CL_COLS + 1];
+    __shared__ __attribute__((aligned(16))) float pt[R][CL_HEADS][CL_KEYS];
+    const int chunk = blockIdx.x, t0 = chunk * CL_KEYS, c0 = blockIdx.y * CL_COLS;
+    const int ng = (H + CL_HEADS - 1) / CL_HEADS;
+    const int rb0 = R * (int)(blockIdx.z / ng), h0 = (blockIdx.z % ng) * CL_HEADS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nr = min(R, S - rb0);
+    const int n_max = pos_base + rb0 + nr;  // keys of the block's last row
+    if (t0 >= n_max)
+        return;
+    const int64_t sstride = (int64_t)S * H * Tcap;
+    float lr[CL_KEYS * CL_COLS / 256];
+#pragma unroll
+    for (int i = 0; i < CL_KEYS * CL_COLS / 256; ++i) {
+        const int idx = tid + 256 * i, tt = idx / CL_COLS, c = idx % CL_COLS;
+        const int t = t0 + tt;
+        lr[i] = (t < n_max && c0 + c < L) ? Lc[(int64_t)t * L + c0 + c] : 0.f;
+    }
+    const int h = h0 + wave;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = rb0 + r, t = t0 + lane;
+        const int n = pos_base + s + 1;
+        float pv = 0.f;
+        if (r < nr && h < H && t < n) {
+            const int64_t zrow = ((int64_t)s * H + h) * Tcap;
+            const float m = stats[((int64_t)s * H + h) * 2], e = stats[((int64_t)s * H + h) * 2 + 1];
+            const float z = mla_score(sc_part, sstride, zrow + t, scale);
+            pv = expf(z - m) / e;
+            if (blockIdx.y == 0) {
+                scores[zrow + t] = z;
+                p[zrow + t] = pv;
+            }
+        }
+        pt[r][wave][lane] = pv;
+    }
+#pragma unroll
+    for (int i = 0; i < CL_KEYS * CL_COLS / 256; ++i) {
+        const int idx = tid + 256 * i;
+        lt[idx / CL_COLS][idx % CL_COLS] = lr[i];
+    }
+    __syncthreads();
+    float a[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) a[r] = 0.f;
+#pragma unroll 4
+    for (int tt = 0; tt < CL_KEYS; tt += 4) {
+        const float l0 = lt[tt][lane], l1 = lt[tt + 1][lane], l2 = lt[tt + 2][lane],
+                    l3 = lt[tt + 3][lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const f32x4 pp = *reinterpret_cast<const f32x4 *>(&pt[r][wave][tt]);
+            a[r] = fmaf(pp.x, l0, a[r]);
+            a[r] = fmaf(pp.y, l1, a[r]);
+            a[r] = fmaf(pp.z, l2, a[r]);
+            a[r] = fmaf(pp.w, l3, a[r]);
+        }
+    }
+    const int c = c0 + lane;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < nr && h < H && c < L && t0 < pos_base + rb0 + r + 1)
+            cl_part[(((int64_t)chunk * S + rb0 + r) * H + h) * L + c] = a[r];
 }
 
 // ---- value absorption --------------------------------------------------------
@@ -487,6 +714,7 @@ MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tc
     l.qabs_part = take((size_t)MLA_QA_SPLIT * Sc * H * L);
     l.sc_part = take((size_t)MLA_SC_SPLIT * Sc * H * Tcap);
     l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * Sc * H * L);
+    l.stats = take((size_t)2 * Sc * H);
     l.total = o;
     return l;
 }
@@ -597,9 +825,17 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
         const int nkeys = pos_base + G;
         const dim3 grid((unsigned)((nkeys + SC_KEYS - 1) / SC_KEYS),
                         (unsigned)((H + SC_HEADS - 1) / SC_HEADS), (unsigned)(G * MLA_SC_SPLIT));
-        hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
-                           (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H, L,
-                           dr, pos_base, a.T_cap, qabs, sc_part);
+        if (G > MLA_CHUNK) {
+            constexpr int R = COLI_MLA_SCORE_ROWS;
+            const dim3 gridr(grid.x, grid.y, (unsigned)(((G + R - 1) / R) * MLA_SC_SPLIT));
+            hipLaunchKernelGGL(k_mla_scores_rows<R>, gridr, dim3(256), 0, st, (const float *)part,
+                               (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
+                               L, dr, pos_base, a.T_cap, qabs, sc_part);
+        } else {
+            hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
+                               (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
+                               L, dr, pos_base, a.T_cap, qabs, sc_part);
+        }
         const int rc = after_launch("mla_scores");
         if (rc != COLI_OK) return rc;
     }
@@ -610,8 +846,22 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
         const dim3 grid((unsigned)((nkeys + CL_KEYS - 1) / CL_KEYS),
                         (unsigned)((L + CL_COLS - 1) / CL_COLS),
                         (unsigned)(G * ((H + CL_HEADS - 1) / CL_HEADS)));
-        hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
-                           (const float *)a.Lc, G, H, L, pos_base, a.T_cap, scale, sc, p, cl_part);
+        if (G > MLA_CHUNK) {
+            float *stats = (float *)(ws + l.stats);
+            hipLaunchKernelGGL(k_mla_softmax_stats, dim3((unsigned)G, (unsigned)((H + CL_HEADS - 1) / CL_HEADS)),
+                               dim3(256), 0, st, (const float *)sc_part, G, H, pos_base, a.T_cap,
+                               scale, stats);
+            constexpr int R = COLI_MLA_CLAT_ROWS;
+            const dim3 gridr(grid.x, grid.y,
+                             (unsigned)(((G + R - 1) / R) * ((H + CL_HEADS - 1) / CL_HEADS)));
+            hipLaunchKernelGGL(k_mla_clat_rows<R>, gridr, dim3(256), 0, st, (const float *)sc_part,
+                               (const float *)stats, (const float *)a.Lc, G, H, L, pos_base,
+                               a.T_cap, scale, sc, p, cl_part);
+        } else {
+            hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
+                               (const float *)a.Lc, G, H, L, pos_base, a.T_cap, scale, sc, p,
+                               cl_part);
+        }
         const int rc = after_launch("mla_softmax_clat");
         if (rc != COLI_OK) return rc;
     }
