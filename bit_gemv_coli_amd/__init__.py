@@ -60,6 +60,8 @@ def _load():
     sig = {
         "coli_tensor_upload": (i32, [QP, i32, i32, i32, i32, i32, i32, vp, vp]),
         "coli_qmatmul": (i32, [QP, vp, vp, i32, vp]),
+        "coli_qmatmul_ws": (i32, [QP, vp, vp, i32, vp, sz, vp]),
+        "coli_qmatmul_workspace_bytes": (sz, [QP, i32]),
         "coli_qmatmul_group": (i32, [i32, vp, vp, vp, i32, vp]),
         "coli_moe_block_two_phase_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
         "coli_moe_block_begin": (i32, [QP, QP, QP, vp, i32, vp, vp, i32, vp, QP, QP, QP, vp, vp, sz, vp]),
@@ -118,6 +120,7 @@ def _load():
 def exported_symbols():
     """Names the binding expects libcoli to export."""
     return ["coli_tensor_upload", "coli_packed_bytes", "coli_tensor_pack", "coli_qmatmul",
+            "coli_qmatmul_ws", "coli_qmatmul_workspace_bytes",
             "coli_qmatmul_group", "coli_gemv_max_rows", "coli_set_gemv_max_rows",
             "coli_moe_block_two_phase_workspace_bytes", "coli_moe_block_begin",
             "coli_moe_block_end",
@@ -173,6 +176,15 @@ def coli_tensor_pack(W, packed, nbytes, stream=None) -> int:
 
 def coli_qmatmul(W, x, y, S, stream=None) -> int:
     return _load().coli_qmatmul(_qp(W), _ptr(x), _ptr(y), S, _stream(stream))
+
+
+def coli_qmatmul_ws(W, x, y, S, workspace, ws_bytes, stream=None) -> int:
+    return _load().coli_qmatmul_ws(_qp(W), _ptr(x), _ptr(y), S, _ptr(workspace), ws_bytes,
+                                   _stream(stream))
+
+
+def coli_qmatmul_workspace_bytes(W, S) -> int:
+    return _load().coli_qmatmul_workspace_bytes(_qp(W), S)
 
 
 COLI_GROUP_MAX = 8

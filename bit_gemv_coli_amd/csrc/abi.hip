@@ -18,6 +18,7 @@
 
 #include "common.h"
 #include "layer.h"
+#include "dgemm.h"
 #include "mla.h"
 
 namespace coli {
@@ -393,6 +394,32 @@ int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *s
         return COLI_DECLINED;
     if (S <= coli_gemv_max_rows())
         return launch_gemv(W, x, y, S, (hipStream_t)stream);
+    return launch_gemm(W, x, y, S, nullptr, 0, (hipStream_t)stream);
+}
+
+size_t coli_qmatmul_workspace_bytes(const coli_qtensor *W, int S) {
+    if (!W || S <= coli_gemv_max_rows())
+        return 0;
+    return dgemm_ws_bytes(W, S);
+}
+
+int coli_qmatmul_ws(const coli_qtensor *W, const float *x, float *y, int S, void *workspace,
+                    size_t ws_bytes, void *stream) {
+    if (check_qt(W, "qmatmul_ws") != COLI_OK)
+        return COLI_DECLINED;
+    if (!x || !y)
+        return decline("qmatmul_ws: NULL x or y");
+    if (S < 1)
+        return decline("qmatmul_ws: S=%d < 1", S);
+    if (!dev_aligned(x, 4) || !dev_aligned(y, 4))
+        return decline("qmatmul_ws: x or y not 4-byte aligned");
+    if (!gate_call())
+        return COLI_DECLINED;
+    if (S <= coli_gemv_max_rows())
+        return launch_gemv(W, x, y, S, (hipStream_t)stream);
+    const int r = launch_dgemm(W, x, y, S, workspace, ws_bytes, (hipStream_t)stream);
+    if (r != 0)
+        return r > 0 ? COLI_OK : COLI_HIP_ERROR;
     return launch_gemm(W, x, y, S, nullptr, 0, (hipStream_t)stream);
 }
 

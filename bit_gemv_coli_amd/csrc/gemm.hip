@@ -18,7 +18,8 @@
 //   * v_mfma_f32_16x16x32_bf16 accumulates in fp32; for grouped int4 every
 //     group's partial sum is formed in a fresh accumulator and added to the
 //     output with its f32 scale, so only the inputs are rounded to bf16
-//     (error <= 2^-9 * sum |w||x| plus fp32 accumulation);
+//     (bf16 keeps 8 significant bits: error <= 2^-8 * sum |w||x| plus fp32
+//     accumulation);
 //   * MoE: a routing kernel builds the table and a tile list (expert, first
 //     row); the inputs are gathered to bf16 in routing order once; gate and up
 //     share a workgroup (one pass over the inputs) and write

@@ -172,6 +172,29 @@ int coli_tensor_pack(coli_qtensor *t, void *packed, size_t bytes, void *stream);
 int coli_qmatmul(const coli_qtensor *W, const float *x, float *y, int S, void *stream);
 
 /*
+ * coli_qmatmul_ws -- coli_qmatmul with a caller workspace, for prefill rows
+ * (same pages as coli_qmatmul: large row batches take a GEMM path).
+ *   workspace  device buffer of at least coli_qmatmul_workspace_bytes(W, S)
+ *              bytes, 256-byte aligned, not shared with a call that may run
+ *              at the same time; contents on entry do not matter
+ * For S > coli_gemv_max_rows() on a packed int4 tensor (fmt 2, or fmt 4
+ * with groups of 32, 64 or multiples of 128) the input rows are first
+ * rounded to bf16 into the workspace in the order the matrix cores read
+ * them; then every 144 x 96 output tile runs on one workgroup whose four
+ * wavefronts each sum a quarter of every 128 inputs, the quarters added in a
+ * fixed order.  Same bound as the GEMM of coli_qmatmul (weights bf16(s (q -
+ * 8)), x bf16, fp32 accumulation: error <= 4e-3 * A); results are repeatable
+ * but not bit-identical to coli_qmatmul's (another summation order).  Any
+ * other case -- decode rows, no packed copy, workspace NULL or too small --
+ * runs exactly as coli_qmatmul.  Returns COLI_OK / COLI_DECLINED /
+ * COLI_HIP_ERROR.
+ */
+int coli_qmatmul_ws(const coli_qtensor *W, const float *x, float *y, int S, void *workspace,
+                    size_t ws_bytes, void *stream);
+/* Workspace bytes coli_qmatmul_ws uses for (W, S); 0 when it uses none. */
+size_t coli_qmatmul_workspace_bytes(const coli_qtensor *W, int S);
+
+/*
  * coli_qmatmul_group -- y[g] = W[g] x[g] for n independent matrices in one
  * submission (colibri-strix commit log, full decode layer commit: the projections of a layer go to the GPU together, not one
  * dispatch each).  Each member is computed exactly as coli_qmatmul computes it

@@ -76,7 +76,7 @@ def _check_moe(orc, G, U, Dn, sh, x, ids, w, out, h_gpu, tau, rows=None, rep=Fal
     out_ref, inter = orc.moe_block(G, U, Dn, x, ids, w, shared=sh, rows=rows, intermediates=True)
     g, u, h, Ag, Au = (inter[k] for k in ("g", "u", "h", "Ag", "Au"))
     sil = g / (1.0 + np.exp(-g))
-    # the bf16 path stores h in bf16 (relative rounding <= 2^-9): allow 2^-8
+    # the bf16 path stores h in bf16 (8 significant bits: relative rounding <= 2^-8)
     hround = 2.0 ** -8 if tau > 1e-4 else 1e-6
     eps = tau * (1.1 * np.abs(u) * Ag + np.abs(sil) * Au) + hround * np.abs(h) + 1e-30
     P = S * K + (S if sh is not None else 0)
