@@ -874,7 +874,7 @@ static int check_mla(const coli_mla_layer *m, int S, int T_cap, MlaLayout *lay, 
     if (!(m->eps >= 0.0f) || m->eps == __builtin_huge_valf() ||
         !(m->rope_theta > 0.0f) || m->rope_theta == __builtin_huge_valf())
         return decline("%s: eps must be finite >= 0 and rope_theta finite > 0", who);
-    *lay = mla_layout(S, H, dn, dr, dv, qr, L, T_cap);
+    *lay = mla_layout(S, H, dn, dr, dv, qr, L, T_cap, mla_proj_ws(*m, S));
     return COLI_OK;
 }
 

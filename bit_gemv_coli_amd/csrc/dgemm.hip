@@ -146,22 +146,32 @@ __device__ __forceinline__ void dg_wait_lds() {
 // Fragment block (mb, kb) = 4 KiB at xf + (mb * nkb4 + kb) * 4096 (nkb4: the
 // 128-input blocks rounded up to a multiple of 4): slice s (1 KiB), lane
 // l = 16 j + r holds bf16 of x[16 mb + r][128 kb + 32 j + 8 s .. + 8]; zero
-// past M rows or K inputs.  One workgroup per block: thread t reads
-// row t / 16, inputs 8 (t % 16) .. + 8 (rows read contiguously).
+// past M rows or K inputs.  One workgroup per (mb, 4 blocks): thread t takes
+// row t / 16, inputs 8 (t % 16) .. + 8 of each block (rows read
+// contiguously), all 8 loads issued before the first store.
 __global__ __launch_bounds__(256) void k_dg_xprep(const float *__restrict__ x, int64_t ldx, int M,
                                                   int K, int nkb4, uint8_t *__restrict__ xf) {
-    const int blk = blockIdx.x, mb = blk / nkb4, kb = blk % nkb4;
+    const int mb = blockIdx.x, kb0 = 4 * blockIdx.y;
     const int t = threadIdx.x, r = t >> 4, c8 = t & 15;
-    const int row = 16 * mb + r, k = 128 * kb + 8 * c8;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (row < M && k < K) {
-        const float *p = x + (int64_t)row * ldx + k;
-        a = gload<f32x4>(p);
-        b = gload<f32x4>(p + 4);
+    const int row = 16 * mb + r;
+    f32x4 v[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int k = 128 * (kb0 + j) + 8 * c8;
+        v[j][0] = v[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (row < M && k < K) {
+            const float *p = x + (int64_t)row * ldx + k;
+            v[j][0] = gload<f32x4>(p);
+            v[j][1] = gload<f32x4>(p + 4);
+        }
     }
-    const u32x4 o = {dg_pk(a.x, a.y), dg_pk(a.z, a.w), dg_pk(b.x, b.y), dg_pk(b.z, b.w)};
-    const int j = c8 >> 2, s = c8 & 3;
-    *reinterpret_cast<u32x4 *>(xf + (int64_t)blk * 4096 + s * 1024 + (16 * j + r) * 16) = o;
+    const int j4 = c8 >> 2, s = c8 & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 a = v[j][0], b = v[j][1];
+        const u32x4 o = {dg_pk(a.x, a.y), dg_pk(a.z, a.w), dg_pk(b.x, b.y), dg_pk(b.z, b.w)};
+        *reinterpret_cast<u32x4 *>(xf + ((int64_t)mb * nkb4 + kb0 + j) * 4096 + s * 1024 + (16 * j4 + r) * 16) = o;
+    }
 }
 
 template <int SM>
@@ -374,8 +384,8 @@ int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *w
     const int nkb = (W->I + 127) / 128, nkb4 = (nkb + 3) / 4 * 4;
     const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (W->O + DG_TN - 1) / DG_TN;
     // every matrix of a stack takes the same input rows
-    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB * nkb4)), dim3(256), 0, st, x,
-                       (int64_t)W->I, S, W->I, nkb4, (uint8_t *)ws);
+    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)(nkb4 / 4)), dim3(256), 0, st,
+                       x, (int64_t)W->I, S, W->I, nkb4, (uint8_t *)ws);
     for (int e = 0; e < W->n; ++e) {
         DgArgs a;
         memset(&a, 0, sizeof a);

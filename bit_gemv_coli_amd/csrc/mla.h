@@ -32,9 +32,12 @@ struct MlaLayout {
     size_t off[MLA_NSTAGE];
     size_t qabs_part, sc_part, cl_part;  // partial sums (internal)
     size_t stats;                        // prefill rows: softmax max and sum per (row, head)
+    size_t xprep, xprep_bytes;           // prefill rows: the projections' prepared inputs
     size_t total;
 };
-MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap);
+// proj_ws: bytes the prefill projections' prepared inputs take (mla_proj_ws)
+MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap, size_t proj_ws);
+size_t mla_proj_ws(const coli_mla_layer &m, int S);
 
 // kv_b's codes and scales as the absorption kernels read them
 struct MlaKvb {

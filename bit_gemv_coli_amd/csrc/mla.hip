@@ -41,7 +41,10 @@
 //                     order) in LDS
 // Every partial sum is added in a fixed order by the next kernel, so reruns
 // are bit-identical.
+#include <algorithm>
+
 #include "common.h"
+#include "dgemm.h"
 #include "layer.h"
 #include "mla.h"
 
@@ -691,7 +694,18 @@ __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int d
 // Host side
 // ---------------------------------------------------------------------------
 
-MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap) {
+// prefill rows (S > MLA_CHUNK): the largest input preparation of the four
+// projections (the split-K prefill GEMM on packed tensors), else 0
+size_t mla_proj_ws(const coli_mla_layer &m, int S) {
+    if (S <= MLA_CHUNK)
+        return 0;
+    size_t b = 0;
+    for (const coli_qtensor *W : {m.q_a, m.kv_a, m.q_b, m.o_proj})
+        b = std::max(b, dgemm_ws_bytes(W, S));
+    return b;
+}
+
+MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tcap, size_t proj_ws) {
     MlaLayout l;
     size_t o = 0;
     auto take = [&](size_t floats) {
@@ -715,6 +729,8 @@ MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tc
     l.sc_part = take((size_t)MLA_SC_SPLIT * Sc * H * Tcap);
     l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * Sc * H * L);
     l.stats = take((size_t)2 * Sc * H);
+    l.xprep = take((proj_ws + sizeof(float) - 1) / sizeof(float));
+    l.xprep_bytes = proj_ws;
     l.total = o;
     return l;
 }
@@ -896,8 +912,15 @@ static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipS
     return COLI_OK;
 }
 
-// one projection of S > MLA_CHUNK rows: the prefill GEMM (bf16 matrix cores)
-static int proj_rows(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st) {
+// one projection of S > MLA_CHUNK rows: the prefill GEMM (bf16 matrix cores),
+// the split-K kernel with the inputs prepared in the workspace when it takes W
+static int proj_rows(const coli_qtensor *W, const float *x, float *y, int S, hipStream_t st,
+                     char *ws, const MlaLayout &l) {
+    if (l.xprep_bytes > 0) {
+        const int r = launch_dgemm(W, x, y, S, ws + l.xprep, l.xprep_bytes, st);
+        if (r != 0)
+            return r > 0 ? COLI_OK : COLI_HIP_ERROR;
+    }
     return launch_gemm(W, x, y, S, nullptr, 0, st);
 }
 
@@ -906,7 +929,7 @@ int launch_mla_decode(const MlaArgs &a) {
     const int S = a.S;
     const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v;
     const int qr = m.q_a->O, L = m.kv_b->I;
-    const MlaLayout l = mla_layout(S, H, dn, dr, dv, qr, L, a.T_cap);
+    const MlaLayout l = mla_layout(S, H, dn, dr, dv, qr, L, a.T_cap, mla_proj_ws(m, S));
     char *ws = (char *)a.ws;
     const hipStream_t st = a.st;
     float *cq_raw = (float *)(ws + l.off[MLA_CQ_RAW]);
@@ -925,9 +948,9 @@ int launch_mla_decode(const MlaArgs &a) {
             if (rc != COLI_OK) return rc;
             xin = a.xn;
         }
-        rc = proj_rows(m.q_a, xin, cq_raw, S, st);
+        rc = proj_rows(m.q_a, xin, cq_raw, S, st, ws, l);
         if (rc != COLI_OK) return rc;
-        rc = proj_rows(m.kv_a, xin, ckv, S, st);
+        rc = proj_rows(m.kv_a, xin, ckv, S, st, ws, l);
         if (rc != COLI_OK) return rc;
         {
             ProfScope ps("mla_qnorm", st);
@@ -936,11 +959,11 @@ int launch_mla_decode(const MlaArgs &a) {
             rc = after_launch("mla_qnorm");
             if (rc != COLI_OK) return rc;
         }
-        rc = proj_rows(m.q_b, cq, q, S, st);
+        rc = proj_rows(m.q_b, cq, q, S, st, ws, l);
         if (rc != COLI_OK) return rc;
         rc = launch_core_rows(a, l, ws, st);
         if (rc != COLI_OK) return rc;
-        rc = proj_rows(m.o_proj, ctx, a.out, S, st);
+        rc = proj_rows(m.o_proj, ctx, a.out, S, st, ws, l);
         if (rc != COLI_OK || a.hsum == nullptr) return rc;
         return launch_residual_add(a.resid, a.out, a.hsum, (int64_t)S * m.o_proj->O, st);
     }
