@@ -725,7 +725,7 @@ def attention_prefill(coli, sd, np, torch, log, S=544, T_cap=1024, passes=5):
     shapes = [(qr, D), (H * (dn + dr), qr), (Lat + dr, D), (H * (dn + dv), Lat), (D, H * dv)]
     P = [sd.pool_on_device(40000 + i, 4, 1, o, i_, gs) for i, (o, i_) in enumerate(shapes)]
     TP = [coli.QTensor(4, q[0], s_[0], o, i_, gs, n=1) for (q, s_), (o, i_) in zip(P, shapes)]
-    for t in TP[:3] + TP[4:]:
+    for t in TP:  # (kv_b's packed copy serves the prefill value absorption)
         t.pack()
     qn = torch.rand(qr, device=dev) + 0.5
     kn = torch.rand(Lat, device=dev) + 0.5

@@ -59,6 +59,11 @@ struct DgArgs {
     int M, N, nmt, nnt;
     float *y;
     int64_t ldy;
+    // batches along the grid's y: batch b takes the fragments at byte
+    // b * xf_bstride, weight tiles rt0 + b * rt_bstride + (0 .. rtn - 1) and
+    // outputs at y + b * y_bstride (one batch: all zero)
+    int xf_bstride, rt0, rt_bstride, Otot;
+    int64_t y_bstride;
 };
 
 __device__ __forceinline__ uint32_t dg_pk(float lo, float hi) {
@@ -150,7 +155,11 @@ __device__ __forceinline__ void dg_wait_lds() {
 // row t / 16, inputs 8 (t % 16) .. + 8 of each block (rows read
 // contiguously), all 8 loads issued before the first store.
 __global__ __launch_bounds__(256) void k_dg_xprep(const float *__restrict__ x, int64_t ldx, int M,
-                                                  int K, int nkb4, uint8_t *__restrict__ xf) {
+                                                  int K, int nkb4, uint8_t *__restrict__ xf,
+                                                  int64_t x_bstride, int64_t xf_bstride) {
+    // batch blockIdx.z: inputs at x + z * x_bstride, fragments at xf + z * xf_bstride
+    x += (int64_t)blockIdx.z * x_bstride;
+    xf += (int64_t)blockIdx.z * xf_bstride;
     const int mb = blockIdx.x, kb0 = 4 * blockIdx.y;
     const int t = threadIdx.x, r = t >> 4, c8 = t & 15;
     const int row = 16 * mb + r;
@@ -209,8 +218,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float rsc[DG_NT];
 #pragma unroll
     for (int t = 0; t < DG_NT; ++t) {
-        rt[t] = min(nt * DG_NT + t, a.rtn - 1);
-        rsc[t] = SM == DG_ROW ? gload<float>(a.ps + min(16 * rt[t] + ln, a.N - 1)) : 0.f;
+        rt[t] = a.rt0 + (int)blockIdx.y * a.rt_bstride + min(nt * DG_NT + t, a.rtn - 1);
+        rsc[t] = SM == DG_ROW ? gload<float>(a.ps + min(16 * rt[t] + ln, a.Otot - 1)) : 0.f;
     }
     const int qv = 16 * lane + 4 * wave;
     const int cb = a.cbs == 1 ? 0 : (lg >> (a.gshift - 5));  // group slot of the lane's 32 inputs
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ((mt * 9 + i) * nkb4 + kb) * 4096 + 1024 wave + 16 lane; the blocks past
     // nkb hold zero inputs, so the clamped codes there add nothing
     const int xv = wave * 1024 + 16 * lane;
-    const int xrow = mt * DG_MB * nkb4;
+    const int xrow = mt * DG_MB * nkb4 + (int)blockIdx.y * (a.xf_bstride / 4096);
     const int wofs = wave * DG_SLOT;
     // inputs of block kb (clamped to the padded blocks) into ring slot u
     auto issue = [&](int u, int kb) {
@@ -328,6 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // a share of the fragments over the four arrays and writes them; lane
     // (ln, lg) of fragment (i, t) holds rows 16 i + 4 lg + r, column 16 t + ln
     const int m0 = mt * DG_TM, n0 = nt * DG_TN;
+    float *const yb = a.y + (int64_t)blockIdx.y * a.y_bstride;
     f32x4 *mine = reinterpret_cast<f32x4 *>(ring(wave));
     const f32x4 *p0 = reinterpret_cast<const f32x4 *>(rs0), *p1 = reinterpret_cast<const f32x4 *>(rs1);
     const f32x4 *p2 = reinterpret_cast<const f32x4 *>(rs2), *p3 = reinterpret_cast<const f32x4 *>(rs3);
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int r = 0; r < 4; ++r) {
                     const int gm = m0 + 16 * i + 4 * lg + r;
                     if (gm < a.M)
-                        a.y[(int64_t)gm * a.ldy + gn] = v[r];
+                        yb[(int64_t)gm * a.ldy + gn] = v[r];
                 }
             }
         }
@@ -385,7 +395,7 @@ int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *w
     const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (W->O + DG_TN - 1) / DG_TN;
     // every matrix of a stack takes the same input rows
     hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)(nkb4 / 4)), dim3(256), 0, st,
-                       x, (int64_t)W->I, S, W->I, nkb4, (uint8_t *)ws);
+                       x, (int64_t)W->I, S, W->I, nkb4, (uint8_t *)ws, (int64_t)0, (int64_t)0);
     for (int e = 0; e < W->n; ++e) {
         DgArgs a;
         memset(&a, 0, sizeof a);
@@ -401,6 +411,7 @@ int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *w
         a.cbs = (W->fmt != 4 || W->gs % 128 == 0) ? 1 : 128 / W->gs;
         a.gshift = (W->fmt == 4 && W->gs < 128) ? __builtin_ctz((unsigned)W->gs) : 5;
         a.rtn = (W->O + 15) / 16;
+        a.Otot = W->O;
         a.M = S;
         a.N = W->O;
         a.nmt = nmt;
@@ -414,6 +425,66 @@ int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *w
             hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, a);
     }
     return after_launch("gemm_dense") == COLI_OK ? 1 : -1;
+}
+
+// Per-head products on row ranges of one packed matrix (the MLA value
+// absorption: head h's value rows of kv_b times its latent context).
+size_t dgemm_heads_ws_bytes(const coli_qtensor *W, int S, int nb) {
+    if (nb < 1)
+        return 0;
+    return dgemm_ws_bytes(W, S) * (size_t)nb;
+}
+
+bool dgemm_heads_takes(const coli_qtensor *W, int row0, int row_step, int N, int nb, int S) {
+    const size_t per = dgemm_ws_bytes(W, S);
+    return dg_ok(W) && W->n == 1 && S >= 1 && nb >= 1 && N >= 1 && row0 % 16 == 0 &&
+           row_step % 16 == 0 && row0 + (int64_t)(nb - 1) * row_step + N <= W->O && per > 0 &&
+           per * nb < ((size_t)1 << 31);
+}
+
+int launch_dgemm_heads(const coli_qtensor *W, int row0, int row_step, int N, int nb, const float *x,
+                       int64_t ldx, int64_t x_bstride, float *y, int64_t ldy, int64_t y_bstride, int S,
+                       void *ws, size_t ws_bytes, hipStream_t st) {
+    const size_t per = dgemm_ws_bytes(W, S);
+    if (!dgemm_heads_takes(W, row0, row_step, N, nb, S) || ws == nullptr ||
+        (uintptr_t)ws % 256 != 0 || ws_bytes < per * nb || (uintptr_t)x % 16 != 0 || ldx % 4 != 0 ||
+        x_bstride % 4 != 0)
+        return 0;
+    ProfScope ps("gemm_heads", st);
+    const int nkb = (W->I + 127) / 128, nkb4 = (nkb + 3) / 4 * 4;
+    const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (N + DG_TN - 1) / DG_TN;
+    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)(nkb4 / 4), (unsigned)nb),
+                       dim3(256), 0, st, x, ldx, S, W->I, nkb4, (uint8_t *)ws, x_bstride, (int64_t)per);
+    DgArgs a;
+    memset(&a, 0, sizeof a);
+    a.xf = (const uint8_t *)ws;
+    a.pq = (const uint8_t *)W->pk;
+    a.ps = W->fmt == 4 ? (const float *)((const uint8_t *)W->pk + W->pk_scale_off) : W->s;
+    a.xbytes = (int)(per * nb);
+    a.qbytes = (int)W->pk_scale_off;
+    a.sbytes = W->fmt == 4 ? (int)(W->pk_stride - W->pk_scale_off) : (int)(W->O * sizeof(float));
+    a.nkb = nkb;
+    a.nkq = (nkb + 3) / 4;
+    a.cbs = (W->fmt != 4 || W->gs % 128 == 0) ? 1 : 128 / W->gs;
+    a.gshift = (W->fmt == 4 && W->gs < 128) ? __builtin_ctz((unsigned)W->gs) : 5;
+    a.rtn = (N + 15) / 16;
+    a.Otot = W->O;
+    a.M = S;
+    a.N = N;
+    a.nmt = nmt;
+    a.nnt = nnt;
+    a.y = y;
+    a.ldy = ldy;
+    a.xf_bstride = (int)per;
+    a.rt0 = row0 / 16;
+    a.rt_bstride = row_step / 16;
+    a.y_bstride = y_bstride;
+    const dim3 grid((unsigned)(nmt * nnt), (unsigned)nb);
+    if (W->fmt == 4)
+        hipLaunchKernelGGL(k_dg<DG_GRP>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, a);
+    return after_launch("gemm_heads") == COLI_OK ? 1 : -1;
 }
 
 }  // namespace coli

@@ -616,6 +616,23 @@ __global__ __launch_bounds__(256) void k_mla_clat_rows(const float *__restrict__
             cl_part[(((int64_t)chunk * S + rb0 + r) * H + h) * L + c] = a[r];
 }
 
+// Prefill rows whose value absorption runs on the matrix cores afterwards:
+// clat[s][h][c] = the key chunks' partials of row s added in chunk order
+// (what k_mla_ctx stages); one thread per value.
+__global__ __launch_bounds__(256) void k_mla_clat_sum(const float *__restrict__ cl_part, int S,
+                                                      int H, int L, int pos_base,
+                                                      float *__restrict__ clat) {
+    const int64_t n = (int64_t)S * H * L;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const int s = (int)(i / ((int64_t)H * L));
+    const int nchunk = (pos_base + s + 1 + CL_KEYS - 1) / CL_KEYS;
+    float v = cl_part[i];
+    for (int k = 1; k < nchunk; ++k) v += cl_part[i + (int64_t)k * n];
+    clat[i] = v;
+}
+
 // ---- value absorption --------------------------------------------------------
 // ctx[h][v] = sum_c kv_b[h (dn+dv) + dn + v][c] clat[h][c]: a wavefront takes
 // 16 value rows, 4 lanes per row, each lane 16-byte loads (32 columns) of its
@@ -694,14 +711,23 @@ __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int d
 // Host side
 // ---------------------------------------------------------------------------
 
-// prefill rows (S > MLA_CHUNK): the largest input preparation of the four
-// projections (the split-K prefill GEMM on packed tensors), else 0
+// prefill rows (S > MLA_CHUNK): whether the value absorption of all rows
+// runs as per-head products on the matrix cores (kv_b with a packed int4 copy)
+static bool mla_ctx_on_gemm(const coli_mla_layer &m, int S) {
+    return S > MLA_CHUNK &&
+           dgemm_heads_takes(m.kv_b, m.d_nope, m.d_nope + m.d_v, m.d_v, m.H, S);
+}
+
+// prefill rows: the largest input preparation of the four projections and
+// (when it runs there) the value absorption on the split-K GEMM, else 0
 size_t mla_proj_ws(const coli_mla_layer &m, int S) {
     if (S <= MLA_CHUNK)
         return 0;
     size_t b = 0;
     for (const coli_qtensor *W : {m.q_a, m.kv_a, m.q_b, m.o_proj})
         b = std::max(b, dgemm_ws_bytes(W, S));
+    if (mla_ctx_on_gemm(m, S))
+        b = std::max(b, dgemm_heads_ws_bytes(m.kv_b, S, m.H));
     return b;
 }
 
@@ -791,7 +817,7 @@ static void ctx_launch(bool grp, unsigned nz, int rbase, int nrows, const MlaKvb
 // per workgroup (whole chunks in one launch, a last partial chunk in a second);
 // scores and softmax take the G rows directly.
 static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st, int r0,
-                       int G) {
+                       int G, bool ctx_later) {
     const coli_mla_layer &m = *a.layer;
     const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v;
     const int L = m.kv_b->I;
@@ -883,6 +909,12 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     }
     {
         ProfScope ps("mla_ctx", st);
+        if (ctx_later) {  // the group's clat only; the value absorption follows for all rows
+            const int64_t n = (int64_t)G * H * L;
+            hipLaunchKernelGGL(k_mla_clat_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               (const float *)cl_part, G, H, L, pos_base, clat);
+            return after_launch("mla_ctx");
+        }
         if (nfull > 0)
             ctx_launch<MLA_CHUNK>(grp, nfull, 0, G, kb, H, dn, dv, L, pos_base, cl_part, clat, ctx,
                                   st);
@@ -904,12 +936,22 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
 // the core over all S rows, MLA_GROUP rows per launch set (each group's key
 // rows are in the caches before the next group's scores read them)
 static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st) {
+    const coli_mla_layer &m = *a.layer;
+    const bool ctx_later = mla_ctx_on_gemm(m, a.S) && l.xprep_bytes > 0;
     for (int r0 = 0; r0 < a.S; r0 += MLA_GROUP) {
         const int G = a.S - r0 < MLA_GROUP ? a.S - r0 : MLA_GROUP;
-        const int rc = launch_core(a, l, ws, st, r0, G);
+        const int rc = launch_core(a, l, ws, st, r0, G, ctx_later);
         if (rc != COLI_OK) return rc;
     }
-    return COLI_OK;
+    if (!ctx_later)
+        return COLI_OK;
+    // value absorption of all rows: head h's value rows of kv_b times its
+    // latent context, on the bf16 matrix cores (the prefill precision)
+    const int H = m.H, dn = m.d_nope, dv = m.d_v, L = m.kv_b->I;
+    const int r = launch_dgemm_heads(m.kv_b, dn, dn + dv, dv, H, (const float *)(ws + l.off[MLA_CLAT]),
+                                     (int64_t)H * L, L, (float *)(ws + l.off[MLA_CTX]),
+                                     (int64_t)H * dv, dv, a.S, ws + l.xprep, l.xprep_bytes, st);
+    return r > 0 ? COLI_OK : COLI_HIP_ERROR;  // (shapes checked by mla_ctx_on_gemm)
 }
 
 // one projection of S > MLA_CHUNK rows: the prefill GEMM (bf16 matrix cores),
