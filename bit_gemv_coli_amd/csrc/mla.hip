@@ -440,7 +440,7 @@ constexpr int CL_HEADS = 4;
 constexpr int CL_KEYS = 64;
 // query rows per workgroup of the prefill latent-context kernel
 #ifndef COLI_MLA_CLAT_ROWS
-#define COLI_MLA_CLAT_ROWS 4
+#define COLI_MLA_CLAT_ROWS 8
 #endif
 
 __device__ __forceinline__ float mla_score(const float *__restrict__ sc_part, int64_t sstride,
