@@ -143,44 +143,36 @@ __device__ __forceinline__ void dg_wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// s_waitcnt lgkmcnt(0) only (LDS reads done)
-__device__ __forceinline__ void dg_wait_lds() {
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-}
+// workgroup barrier for LDS hand-overs: waits for this wavefront's LDS
+// accesses only (global stores may still be in flight)
+__device__ __forceinline__ void dg_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Fragment block (mb, kb) = 4 KiB at xf + (mb * nkb4 + kb) * 4096 (nkb4: the
 // 128-input blocks rounded up to a multiple of 4): slice s (1 KiB), lane
 // l = 16 j + r holds bf16 of x[16 mb + r][128 kb + 32 j + 8 s .. + 8]; zero
-// past M rows or K inputs.  One workgroup per (mb, 4 blocks): thread t takes
-// row t / 16, inputs 8 (t % 16) .. + 8 of each block (rows read
-// contiguously), all 8 loads issued before the first store.
+// past M rows or K inputs.  One workgroup per (mb, block): thread t takes
+// row t / 16, inputs 8 (t % 16) .. + 8 (rows read contiguously); a workgroup
+// per block rather than per 4 blocks keeps more loads in flight (measured on
+// the 544 x 6144 x 6144 GEMM: ~2 us less per call).
 __global__ __launch_bounds__(256) void k_dg_xprep(const float *__restrict__ x, int64_t ldx, int M,
                                                   int K, int nkb4, uint8_t *__restrict__ xf,
                                                   int64_t x_bstride, int64_t xf_bstride) {
     // batch blockIdx.z: inputs at x + z * x_bstride, fragments at xf + z * xf_bstride
     x += (int64_t)blockIdx.z * x_bstride;
     xf += (int64_t)blockIdx.z * xf_bstride;
-    const int mb = blockIdx.x, kb0 = 4 * blockIdx.y;
+    const int mb = blockIdx.x, kb = blockIdx.y;
     const int t = threadIdx.x, r = t >> 4, c8 = t & 15;
     const int row = 16 * mb + r;
-    f32x4 v[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int k = 128 * (kb0 + j) + 8 * c8;
-        v[j][0] = v[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (row < M && k < K) {
-            const float *p = x + (int64_t)row * ldx + k;
-            v[j][0] = gload<f32x4>(p);
-            v[j][1] = gload<f32x4>(p + 4);
-        }
+    const int k = 128 * kb + 8 * c8;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+    if (row < M && k < K) {
+        const float *p = x + (int64_t)row * ldx + k;
+        a = gload<f32x4>(p);
+        b = gload<f32x4>(p + 4);
     }
     const int j4 = c8 >> 2, s = c8 & 3;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4 a = v[j][0], b = v[j][1];
-        const u32x4 o = {dg_pk(a.x, a.y), dg_pk(a.z, a.w), dg_pk(b.x, b.y), dg_pk(b.z, b.w)};
-        *reinterpret_cast<u32x4 *>(xf + ((int64_t)mb * nkb4 + kb0 + j) * 4096 + s * 1024 + (16 * j4 + r) * 16) = o;
-    }
+    const u32x4 o = {dg_pk(a.x, a.y), dg_pk(a.z, a.w), dg_pk(b.x, b.y), dg_pk(b.z, b.w)};
+    *reinterpret_cast<u32x4 *>(xf + ((int64_t)mb * nkb4 + kb) * 4096 + s * 1024 + (16 * j4 + r) * 16) = o;
 }
 
 template <int SM>
@@ -335,7 +327,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // tiles at a time: wavefront w stores its 27 fragments (i, t) of the half
     // in slot array w (lane l's 4 values together), then each wavefront sums
     // a share of the fragments over the four arrays and writes them; lane
-    // (ln, lg) of fragment (i, t) holds rows 16 i + 4 lg + r, column 16 t + ln
+    // (ln, lg) of fragment (i, t) holds rows 16 i + 4 lg + r, column 16 t + ln.
+    // The barriers wait for LDS only, so the first half's output stores stay
+    // in flight during the second half (measured: 2-3 us less per call).
     const int m0 = mt * DG_TM, n0 = nt * DG_TN;
     float *const yb = a.y + (int64_t)blockIdx.y * a.y_bstride;
     f32x4 *mine = reinterpret_cast<f32x4 *>(ring(wave));
@@ -348,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 0; i < DG_MB; ++i)
 #pragma unroll
             for (int tt = 0; tt < HT; ++tt) mine[(i * HT + tt) * 64 + lane] = acc[i][h * HT + tt];
-        __syncthreads();
+        dg_lds_barrier();
         for (int f = wave; f < NF; f += 4) {
             const int o = f * 64 + lane;
             const f32x4 v = ((p0[o] + p1[o]) + p2[o]) + p3[o];
@@ -363,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
         }
-        __syncthreads();
+        dg_lds_barrier();
     }
 }
 
@@ -394,7 +388,7 @@ int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *w
     const int nkb = (W->I + 127) / 128, nkb4 = (nkb + 3) / 4 * 4;
     const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (W->O + DG_TN - 1) / DG_TN;
     // every matrix of a stack takes the same input rows
-    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)(nkb4 / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)nkb4), dim3(256), 0, st,
                        x, (int64_t)W->I, S, W->I, nkb4, (uint8_t *)ws, (int64_t)0, (int64_t)0);
     for (int e = 0; e < W->n; ++e) {
         DgArgs a;
@@ -453,7 +447,7 @@ int launch_dgemm_heads(const coli_qtensor *W, int row0, int row_step, int N, int
     ProfScope ps("gemm_heads", st);
     const int nkb = (W->I + 127) / 128, nkb4 = (nkb + 3) / 4 * 4;
     const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (N + DG_TN - 1) / DG_TN;
-    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)(nkb4 / 4), (unsigned)nb),
+    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)nkb4, (unsigned)nb),
                        dim3(256), 0, st, x, ldx, S, W->I, nkb4, (uint8_t *)ws, x_bstride, (int64_t)per);
     DgArgs a;
     memset(&a, 0, sizeof a);
