@@ -31,14 +31,21 @@
 //                     its rotary key (cos / sin in f64) and writes both
 //                     cache rows
 //   k_mla_scores      partial scores over a third of the L + d_rope components:
-//                     4 heads x 64 keys per workgroup, LDS chunks double-
-//                     buffered; adds the qabs partials while staging
+//                     4 heads x 64 keys per workgroup, the split's component
+//                     chunks requested together (16-byte loads) and passed
+//                     through two LDS buffers; adds the qabs partials while
+//                     staging
 //   k_mla_softmax_clat per 64-key chunk: the softmax statistics of each
-//                     wavefront's head over all keys, then the chunk's share
-//                     of clat (4 heads x 64 columns per workgroup)
+//                     wavefront's head over all keys (the first 9 keys per
+//                     lane requested together and kept in registers), then
+//                     the chunk's share of clat (4 heads x 64 columns per
+//                     workgroup)
 //   k_mla_ctx         16 value rows per wavefront, 4 lanes per row with
-//                     16-byte code loads; clat (the chunks' shares added in
-//                     order) in LDS
+//                     16-byte code loads, requested before clat (the chunks'
+//                     shares added in order) is formed in LDS
+// At decode sizes each of these is a few dependent memory round trips of
+// ~2 us each (measured per workgroup), so every kernel requests what it can
+// before its first wait.
 // Every partial sum is added in a fixed order by the next kernel, so reruns
 // are bit-identical.
 #include <algorithm>
@@ -230,13 +237,14 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
 constexpr int SC_KEYS = 64;
 constexpr int SC_HEADS = 4;
 constexpr int SC_CH = 64;
+constexpr int SC_MAXCH = 3;  // component chunks requested together (decode kernel)
 
 __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ part,
                                                     const float *__restrict__ qpe,
                                                     const float *__restrict__ Lc,
                                                     const float *__restrict__ Rc, int S, int H,
                                                     int L, int dr, int pos_base, int Tcap,
-                                                    float *__restrict__ qabs,
+                                                    int lvec, float *__restrict__ qabs,
                                                     float *__restrict__ sc_part) {
     __shared__ float kt[2][SC_KEYS][SC_CH + 1];
     __shared__ float qt[2][SC_HEADS][SC_CH];
@@ -251,59 +259,78 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
     const int per = (nch_all + MLA_SC_SPLIT - 1) / MLA_SC_SPLIT;
     const int ch0 = split * per, ch1 = min(nch_all, ch0 + per);
     const int64_t pstride = (int64_t)S * H * L;
-    float kr[SC_KEYS * SC_CH / 256], qv;
-    auto fetch = [&](int c0) {
+    // key components: thread t takes 4 consecutive components (c4 = 4 (t % 16))
+    // of keys t / 16 + 16 i; the latent part with 16-byte loads (L % 4 == 0,
+    // lvec: Lc 16-byte aligned), the rotary part component by component
+    const int kk = tid >> 4, c4 = 4 * (tid & 15);
+    auto fetch = [&](f32x4 (&kr)[4], float &qv, int c0) {
+        const int c = c0 + c4;
 #pragma unroll
-        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
-            const int idx = tid + 256 * i, key = idx / SC_CH, cc = idx % SC_CH;
-            const int t = t0 + key, c = c0 + cc;
-            float v = 0.f;
-            if (t <= last && c < C)
-                v = c < L ? Lc[(int64_t)t * L + c] : Rc[(int64_t)t * dr + (c - L)];
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + kk + 16 * i;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (t <= last) {
+                if (c + 4 <= L && lvec) {
+                    v = gload<f32x4>(Lc + (int64_t)t * L + c);
+                } else {
+                    float e[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int ck = c + k;
+                        e[k] = ck < L ? Lc[(int64_t)t * L + ck] : (ck < C ? Rc[(int64_t)t * dr + (ck - L)] : 0.f);
+                    }
+                    v = f32x4{e[0], e[1], e[2], e[3]};
+                }
+            }
             kr[i] = v;
         }
-        const int hh = tid / SC_CH, cc = tid % SC_CH;  // 4 heads x 64 components
-        const int h = h0 + hh, c = c0 + cc;
+        const int hh = tid / SC_CH, cq = tid % SC_CH;  // 4 heads x 64 components
+        const int h = h0 + hh, cc = c0 + cq;
         float v = 0.f;
-        if (h < H && c < C) {
-            if (c < L) {
-                const float *pp = part + ((int64_t)s * H + h) * L + c;
+        if (h < H && cc < C) {
+            if (cc < L) {
+                const float *pp = part + ((int64_t)s * H + h) * L + cc;
                 v = pp[0];
 #pragma unroll
                 for (int k = 1; k < MLA_QA_SPLIT; ++k) v += pp[k * pstride];
             } else {
-                v = qpe[((int64_t)s * H + h) * dr + (c - L)];
+                v = qpe[((int64_t)s * H + h) * dr + (cc - L)];
             }
         }
         qv = v;
     };
-    auto store = [&](int buf, int c0) {
+    auto store = [&](int buf, const f32x4 (&kr)[4], float qv, int c0) {
 #pragma unroll
-        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
-            const int idx = tid + 256 * i;
-            kt[buf][idx / SC_CH][idx % SC_CH] = kr[i];
+        for (int i = 0; i < 4; ++i) {
+            float *row = &kt[buf][kk + 16 * i][c4];
+            row[0] = kr[i].x; row[1] = kr[i].y; row[2] = kr[i].z; row[3] = kr[i].w;
         }
-        const int hh = tid / SC_CH, cc = tid % SC_CH;
-        qt[buf][hh][cc] = qv;
-        if (blockIdx.x == 0 && h0 + hh < H && c0 + cc < L)
-            qabs[((int64_t)s * H + h0 + hh) * L + c0 + cc] = qv;
+        const int hh = tid / SC_CH, cq = tid % SC_CH;
+        qt[buf][hh][cq] = qv;
+        if (blockIdx.x == 0 && h0 + hh < H && c0 + cq < L)
+            qabs[((int64_t)s * H + h0 + hh) * L + c0 + cq] = qv;
     };
+    // up to SC_MAXCH chunks are requested together (one memory round trip for
+    // all of them), then go through the two LDS buffers in turn; the chunk
+    // sums are added in chunk order
     float tot = 0.f;
-    if (ch0 < ch1) {
-        fetch(ch0 * SC_CH);
-        store(0, ch0 * SC_CH);
-    }
-    __syncthreads();
-    for (int ch = ch0; ch < ch1; ++ch) {
-        const int buf = (ch - ch0) & 1;
-        if (ch + 1 < ch1)
-            fetch((ch + 1) * SC_CH);
-        float a = 0.f;
+    for (int g0 = ch0; g0 < ch1; g0 += SC_MAXCH) {
+        f32x4 kr[SC_MAXCH][4];
+        float qv[SC_MAXCH];
+#pragma unroll
+        for (int j = 0; j < SC_MAXCH; ++j)
+            fetch(kr[j], qv[j], min(g0 + j, ch1 - 1) * SC_CH);
+#pragma unroll
+        for (int j = 0; j < SC_MAXCH; ++j) {
+            if (g0 + j >= ch1)
+                break;
+            store(j & 1, kr[j], qv[j], (g0 + j) * SC_CH);
+            __syncthreads();
+            float a = 0.f;
 #pragma unroll 16
-        for (int cc = 0; cc < SC_CH; ++cc) a = fmaf(qt[buf][wave][cc], kt[buf][lane][cc], a);
-        tot += a;
-        if (ch + 1 < ch1)
-            store(buf ^ 1, (ch + 1) * SC_CH);
+            for (int cc = 0; cc < SC_CH; ++cc) a = fmaf(qt[j & 1][wave][cc], kt[j & 1][lane][cc], a);
+            tot += a;
+        }
         __syncthreads();
     }
     const int t = t0 + lane, h = h0 + wave;
@@ -438,6 +465,11 @@ __global__ __launch_bounds__(256) void k_mla_scores_rows(const float *__restrict
 constexpr int CL_COLS = 64;
 constexpr int CL_HEADS = 4;
 constexpr int CL_KEYS = 64;
+// keys per lane whose scores are requested together
+#ifndef COLI_MLA_SM_KJ
+#define COLI_MLA_SM_KJ 9
+#endif
+constexpr int SM_KJ = COLI_MLA_SM_KJ;
 // query rows per workgroup of the prefill latent-context kernel
 #ifndef COLI_MLA_CLAT_ROWS
 #define COLI_MLA_CLAT_ROWS 8
@@ -475,21 +507,39 @@ __global__ __launch_bounds__(256) void k_mla_softmax_clat(const float *__restric
         const int t = t0 + tt;
         lr[i] = (t < n && c0 + c < L) ? Lc[(int64_t)t * L + c0 + c] : 0.f;
     }
-    // softmax statistics of this wavefront's head
+    // softmax statistics of this wavefront's head: lane l takes keys l, l + 64,
+    // ...; the first SM_KJ of them are requested together and kept (a key
+    // past n reads as -inf: it moves neither the maximum nor the sum), later
+    // ones are read again for the sum
     const int h = h0 + wave;
     const int64_t zrow = ((int64_t)s * H + min(h, H - 1)) * Tcap;
+    float zk[SM_KJ];
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) {
+        const int t = lane + 64 * j;
+        const float z = mla_score(sc_part, sstride, zrow + min(t, n - 1), scale);
+        zk[j] = t < n ? z : -__builtin_inff();
+    }
     float m = -__builtin_inff();
-    for (int t = lane; t < n; t += 64) m = fmaxf(m, mla_score(sc_part, sstride, zrow + t, scale));
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) m = fmaxf(m, zk[j]);
+    for (int t = lane + 64 * SM_KJ; t < n; t += 64) m = fmaxf(m, mla_score(sc_part, sstride, zrow + t, scale));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float e = 0.f;
-    for (int t = lane; t < n; t += 64) e += expf(mla_score(sc_part, sstride, zrow + t, scale) - m);
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) e += expf(zk[j] - m);
+    for (int t = lane + 64 * SM_KJ; t < n; t += 64) e += expf(mla_score(sc_part, sstride, zrow + t, scale) - m);
     e = wave_sum(e);
     {
         const int t = t0 + lane;
         float pv = 0.f;
         if (h < H && t < n) {
-            const float z = mla_score(sc_part, sstride, zrow + t, scale);
+            float z = zk[0];
+#pragma unroll
+            for (int j = 1; j < SM_KJ; ++j) z = chunk == j ? zk[j] : z;
+            if (chunk >= SM_KJ)
+                z = mla_score(sc_part, sstride, zrow + t, scale);
             pv = expf(z - m) / e;
             if (blockIdx.y == 0) {
                 scores[zrow + t] = z;
@@ -640,6 +690,8 @@ __global__ __launch_bounds__(256) void k_mla_clat_sum(const float *__restrict__ 
 // clat of the head sits in LDS; the 4 lanes' sums are combined by two xor
 // shuffles.  Needs L % 32 == 0.
 constexpr int CX_ROWS = 64;  // value rows per workgroup (16 per wavefront)
+constexpr int CX_CH = 4;     // 32-column chunks per lane whose codes are requested up front
+constexpr int CX_KC = 16;    // key chunks of latent-context partials requested together
 
 template <int S, bool GRP>
 __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int dv, int L,
@@ -654,35 +706,68 @@ __global__ __launch_bounds__(256) void k_mla_ctx(MlaKvb kb, int H, int dn, int d
     clat += (int64_t)rz * H * L;
     ctx += (int64_t)rz * H * dv;
     pos_base += rz;
-    // clat = the key chunks' partials of row s, added in chunk order; the
-    // first row tile stores it
-    for (int i = tid; i < S * L; i += 256) {
-        const int s = i / L, c = i % L;
-        const int nchunk = (pos_base + s + 1 + CL_KEYS - 1) / CL_KEYS;
-        const float *pp = cl_part + ((int64_t)s * H + h) * L + c;
-        float v = pp[0];
-        for (int k = 1; k < nchunk; ++k) v += pp[(int64_t)k * nrows * H * L];
-        cl[i] = v;
-        if (blockIdx.y == 0)
-            clat[((int64_t)s * H + h) * L + c] = v;
-    }
-    __syncthreads();
     const int v = blockIdx.y * CX_ROWS + wave * 16 + (lane >> 2);
     const int q = lane & 3;
     const bool live = v < dv;
     const int64_t row = (int64_t)h * (dn + dv) + dn + min(v, dv - 1);
     const int nch = L / 32;
+    // the value rows' codes and scales of this lane's first CX_CH chunks,
+    // requested before the latent context is summed (one memory round trip
+    // for both)
+    u32x4 wq[CX_CH];
+    float wsc[CX_CH][4];
+#pragma unroll
+    for (int u = 0; u < CX_CH; ++u) {
+        const int ch = min(q + 4 * u, nch - 1);
+        wq[u] = live ? gload<u32x4>(kb.q + row * kb.rb + 16 * ch)
+                     : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            wsc[u][k] = GRP ? gload<float>(kb.s + row * kb.ng + (32 * ch + 8 * k) / kb.gs) : 1.f;
+    }
+    // clat = the key chunks' partials of row s, added in chunk order (the
+    // first CX_KC requested together); the first row tile stores it
+    for (int i = tid; i < S * L; i += 256) {
+        const int s = i / L, c = i % L;
+        const int nchunk = (pos_base + s + 1 + CL_KEYS - 1) / CL_KEYS;
+        const float *pp = cl_part + ((int64_t)s * H + h) * L + c;
+        float pk[CX_KC];
+#pragma unroll
+        for (int k = 0; k < CX_KC; ++k) pk[k] = pp[(int64_t)min(k, nchunk - 1) * nrows * H * L];
+        float v = pk[0];
+#pragma unroll
+        for (int k = 1; k < CX_KC; ++k) v = k < nchunk ? v + pk[k] : v;
+        for (int k = CX_KC; k < nchunk; ++k) v += pp[(int64_t)k * nrows * H * L];
+        cl[i] = v;
+        if (blockIdx.y == 0)
+            clat[((int64_t)s * H + h) * L + c] = v;
+    }
+    __syncthreads();
     float part[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) part[s] = 0.f;
-    for (int ch = q; ch < nch; ch += 4) {
-        const u32x4 w4 = live ? gload<u32x4>(kb.q + row * kb.rb + 16 * ch)
-                              : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+    for (int ch = q, u = 0; ch < nch; ch += 4, ++u) {
+        u32x4 w4 = wq[0];
+        float scu[4] = {wsc[0][0], wsc[0][1], wsc[0][2], wsc[0][3]};
+#pragma unroll
+        for (int j = 1; j < CX_CH; ++j)
+            if (u == j) {
+                w4 = wq[j];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) scu[k] = wsc[j][k];
+            }
+        if (u >= CX_CH) {
+            w4 = live ? gload<u32x4>(kb.q + row * kb.rb + 16 * ch)
+                      : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                scu[k] = GRP ? gload<float>(kb.s + row * kb.ng + (32 * ch + 8 * k) / kb.gs) : 1.f;
+        }
         const uint32_t wds[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int c = 32 * ch + 8 * k;
-            const float sc = GRP ? gload<float>(kb.s + row * kb.ng + c / kb.gs) : 1.f;
+            const float sc = scu[k];
             float f[8];
             decode_nib_word(wds[k], f);
 #pragma unroll
@@ -874,9 +959,10 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
                                (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
                                L, dr, pos_base, a.T_cap, qabs, sc_part);
         } else {
+            const int lvec = (uintptr_t)a.Lc % 16 == 0;
             hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
                                (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
-                               L, dr, pos_base, a.T_cap, qabs, sc_part);
+                               L, dr, pos_base, a.T_cap, lvec, qabs, sc_part);
         }
         const int rc = after_launch("mla_scores");
         if (rc != COLI_OK) return rc;
