@@ -79,6 +79,27 @@ __global__ __launch_bounds__(256) void k_router_logits(const float *__restrict__
     for (int i = 0; i < TE; ++i) rr[i] = R + (int64_t)min(e0 + i, E - 1) * D;
 #pragma unroll
     for (int t = 0; t < TT; ++t) xr[t] = x + (int64_t)min(s0 + t, S - 1) * D;
+    // one batch of U stretches: expert rows, input rows and (NORM) the norm
+    // weights; the first batch is requested before the norm's own loads, so
+    // all of it arrives in the same memory round trip
+    f32x4 rv[U][TE], xv[U][TT], gv[U];
+    const int nfull = VEC ? dlo + (dhi - dlo) / (256 * U) * (256 * U) : dlo;
+    auto load_batch = [&](int d0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int d = d0 + 256 * u + 4 * lane;
+#pragma unroll
+            for (int i = 0; i < TE; ++i) rv[u][i] = gload<f32x4>(rr[i] + d);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) xv[u][t] = gload<f32x4>(xr[t] + d);
+            if constexpr (NORM)
+                gv[u] = lnw ? gload<f32x4>(lnw + d) : f32x4{1.f, 1.f, 1.f, 1.f};
+        }
+    };
+    if constexpr (VEC) {
+        if (dlo < nfull)
+            load_batch(dlo);
+    }
     double inv[TT];
     if constexpr (NORM) {
 #pragma unroll
@@ -109,22 +130,18 @@ __global__ __launch_bounds__(256) void k_router_logits(const float *__restrict__
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[i][t] = 0.0;
     if constexpr (VEC) {
-        const int nfull = dlo + (dhi - dlo) / (256 * U) * (256 * U);
         for (int d0 = dlo; d0 < nfull; d0 += 256 * U) {
-            f32x4 rv[U][TE], xv[U][TT];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int d = d0 + 256 * u + 4 * lane;
-#pragma unroll
-                for (int i = 0; i < TE; ++i) rv[u][i] = gload<f32x4>(rr[i] + d);
-#pragma unroll
-                for (int t = 0; t < TT; ++t) xv[u][t] = gload<f32x4>(xr[t] + d);
-            }
+            if (d0 != dlo)
+                load_batch(d0);
             if constexpr (NORM) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
-                    for (int t = 0; t < TT; ++t) xv[u][t] = norm4(xv[u][t], t, d0 + 256 * u + 4 * lane);
+                    for (int t = 0; t < TT; ++t) {
+                        const f32x4 v = xv[u][t], g = gv[u];
+                        xv[u][t] = f32x4{rms_apply(v.x, inv[t], g.x), rms_apply(v.y, inv[t], g.y),
+                                         rms_apply(v.z, inv[t], g.z), rms_apply(v.w, inv[t], g.w)};
+                    }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
