@@ -321,8 +321,14 @@ __host__ __device__ constexpr int mg_nset(int CB, int NT) { return (CB * NT + 3)
 // QB: bits per code in the packed copy -- 4 (fmt 2 / 4: nibbles, B bytes
 // 16 v), 8 (fmt 1: int8 codes, B bytes v), 2 (fmt 3: 2-bit codes moved to the
 // top of each byte, B bytes 64 v).
+// Occupancy: 4 wavefronts per SIMD for gate/up with one quad in flight, and
+// for one input row with the input norm folded in (122-128 VGPRs): at 3 per
+// SIMD only one 6-wavefront workgroup fits a compute unit (its wavefronts go
+// round-robin over the 4 SIMDs), so q_b's 512 workgroups ran in two rounds
+// (measured: starts spread over 5.7 us).  The other shapes keep the
+// compiler's choice.
 template <int NT, int CB, bool GROUPED, int NMAT, int EPI, int KS, int NW, int NBQ = 2, int QB = 4>
-__global__ __launch_bounds__(NW * 64, (NMAT == 2 && NBQ == 1) ? 4 : 1) void k_mgemv(MgArgs a) {
+__global__ __launch_bounds__(NW * 64, ((NMAT == 2 && NBQ == 1) || (EPI == MG_YN && NT == 1 && CB <= 2)) ? 4 : 1) void k_mgemv(MgArgs a) {
     static_assert(NW % KS == 0, "whole tiles per workgroup");
     static_assert(QB == 4 || ((QB == 8 || QB == 2) && !GROUPED && EPI == MG_Y), "code width");
     constexpr bool YOUT = EPI == MG_Y || EPI == MG_YN;
