@@ -222,10 +222,6 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
 }
 
 // ---- scores ----------------------------------------------------------------
-// query rows per workgroup of the prefill scores kernel
-#ifndef COLI_MLA_SCORE_ROWS
-#define COLI_MLA_SCORE_ROWS 4
-#endif
 // Partial scores over one third of the L + d_rope components (Q = [qabs,
 // qpe], K = [Lc, Rc]): grid (64-key tiles, 4-head groups, row x MLA_SC_SPLIT).
 // A workgroup takes 4 heads (one per wavefront) x 64 keys (one per lane);
@@ -338,119 +334,174 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
         sc_part[(((int64_t)split * S + s) * H + h) * Tcap + t] = tot;
 }
 
-// Prefill rows: the same partial scores with R query rows per workgroup, so
-// each key chunk staged in LDS serves R rows x 4 heads.  grid (64-key tiles,
-// 4-head groups, ceil(S / R) row blocks x MLA_SC_SPLIT); rows past S and keys
-// past a row's last position are neither loaded nor stored.  Each thread sums
-// its R products over a chunk four components at a time (one 16-byte
-// broadcast read of every row's query values, four key reads).
-template <int R>
-__global__ __launch_bounds__(256) void k_mla_scores_rows(const float *__restrict__ part,
-                                                         const float *__restrict__ qpe,
-                                                         const float *__restrict__ Lc,
-                                                         const float *__restrict__ Rc, int S,
-                                                         int H, int L, int dr, int pos_base,
-                                                         int Tcap, float *__restrict__ qabs,
-                                                         float *__restrict__ sc_part) {
-    __shared__ float kt[2][SC_KEYS][SC_CH + 1];
-    __shared__ __attribute__((aligned(16))) float qt[2][R][SC_HEADS][SC_CH];
-    const int t0 = blockIdx.x * SC_KEYS, h0 = blockIdx.y * SC_HEADS;
-    const int rb0 = R * (int)(blockIdx.z / MLA_SC_SPLIT), split = blockIdx.z % MLA_SC_SPLIT;
+// Prefill rows on the fp32 matrix cores: partial scores over one third of
+// the L + d_rope components for one head and the group's rows (up to 64);
+// grid (SX_KW key-tile lanes, heads, MLA_SC_SPLIT): workgroup x takes the
+// 64-key tiles x, x + SX_KW, ...  The query tile of the split (the qabs
+// partials added in split order, then qpe) is summed once into LDS and stays
+// there while the key tiles stream through, component chunk by chunk (64
+// components; the next chunk requested into registers while the current one
+// is multiplied).  Wavefront w takes rows 16 w .. 16 w + 15 against the 64
+// keys of a tile as four 16 x 16 tiles of v_mfma_f32_16x16x4f32 (A lane l =
+// Q[l % 16][k], B lane l = K[k][l % 16] for the product's k index l / 16,
+// result lane l register i = row 4 (l / 16) + i, key l % 16); within each
+// 16-component block, product j gives lane group g = l / 16 component
+// 4 g + j, so a lane reads its four components with one 16-byte LDS read
+// (the sum over the block is the same up to rounding order).  Rows past S, keys past the group's last
+// position and scores past a row's own position are neither loaded nor
+// stored; workgroup x = 0 stores qabs.  A split of more than SX_QCH chunks
+// stages its query chunks again for every key tile.
+constexpr int SX_T = 64;    // rows = keys per tile
+// workgroups per (head, split), along the key tiles
+#ifndef COLI_MLA_SX_KW
+#define COLI_MLA_SX_KW 3
+#endif
+constexpr int SX_KW = COLI_MLA_SX_KW;
+constexpr int SX_QCH = 3;   // query chunks kept in LDS
+constexpr int SX_LD = SC_CH + 4;  // LDS row stride (16-byte rows for the 4-component reads)
+static_assert(MLA_GROUP <= SX_T, "a prefill group's rows fit one tile");
+__global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__ part,
+                                                       const float *__restrict__ qpe,
+                                                       const float *__restrict__ Lc,
+                                                       const float *__restrict__ Rc, int S, int H,
+                                                       int L, int dr, int pos_base, int Tcap,
+                                                       int lvec, float *__restrict__ qabs,
+                                                       float *__restrict__ sc_part) {
+    __shared__ __attribute__((aligned(16))) float qs[SX_QCH][SX_T][SX_LD];
+    __shared__ __attribute__((aligned(16))) float ks[SX_T][SX_LD];
+    const int h = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nr = min(R, S - rb0);                 // rows of this block
-    const int last_max = pos_base + rb0 + nr - 1;   // keys 0 .. last of its last row
-    if (t0 > last_max)
-        return;
+    const int last_max = pos_base + S - 1;  // keys 0 .. last of the last row
+    const int nkt = last_max / SX_T + 1;
     const int C = L + dr;
     const int nch_all = (C + SC_CH - 1) / SC_CH;
     const int per = (nch_all + MLA_SC_SPLIT - 1) / MLA_SC_SPLIT;
+    // (a split with no chunks, when L + d_rope is short, stores zero partials)
     const int ch0 = split * per, ch1 = min(nch_all, ch0 + per);
     const int64_t pstride = (int64_t)S * H * L;
-    constexpr int NQ = R * SC_HEADS * SC_CH / 256;  // query values per thread and chunk
-    float kr[SC_KEYS * SC_CH / 256], qv[NQ];
-    auto fetch = [&](int c0) {
+    // staging: thread t takes 4 consecutive components (4 (t % 16)) of rows /
+    // keys t / 16 + 16 i, i < 4
+    const int rr = tid >> 4, c4 = 4 * (tid & 15);
+    auto qload = [&](f32x4 (&qv)[4], int c0) {
+        const int c = c0 + c4;
 #pragma unroll
-        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
-            const int idx = tid + 256 * i, key = idx / SC_CH, cc = idx % SC_CH;
-            const int t = t0 + key, c = c0 + cc;
-            float v = 0.f;
-            if (t <= last_max && c < C)
-                v = c < L ? Lc[(int64_t)t * L + c] : Rc[(int64_t)t * dr + (c - L)];
-            kr[i] = v;
-        }
+        for (int i = 0; i < 4; ++i) {
+            const int r = rr + 16 * i;
+            f32x4 q = {0.f, 0.f, 0.f, 0.f};
+            if (r < S) {
+                if (c + 4 <= L) {
+                    const float *pp = part + ((int64_t)r * H + h) * L + c;
+                    q = gload<f32x4>(pp);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / (SC_HEADS * SC_CH), hh = (idx / SC_CH) % SC_HEADS, cc = idx % SC_CH;
-            const int s = rb0 + r, h = h0 + hh, c = c0 + cc;
-            float v = 0.f;
-            if (r < nr && h < H && c < C) {
-                if (c < L) {
-                    const float *pp = part + ((int64_t)s * H + h) * L + c;
-                    v = pp[0];
-#pragma unroll
-                    for (int k = 1; k < MLA_QA_SPLIT; ++k) v += pp[k * pstride];
+                    for (int k = 1; k < MLA_QA_SPLIT; ++k) q += gload<f32x4>(pp + k * pstride);
                 } else {
-                    v = qpe[((int64_t)s * H + h) * dr + (c - L)];
+                    float e[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int ck = c + k;
+                        float v = 0.f;
+                        if (ck < L) {
+                            const float *pp = part + ((int64_t)r * H + h) * L + ck;
+                            v = pp[0];
+#pragma unroll
+                            for (int u = 1; u < MLA_QA_SPLIT; ++u) v += pp[u * pstride];
+                        } else if (ck < C) {
+                            v = qpe[((int64_t)r * H + h) * dr + (ck - L)];
+                        }
+                        e[k] = v;
+                    }
+                    q = f32x4{e[0], e[1], e[2], e[3]};
                 }
             }
-            qv[i] = v;
+            qv[i] = q;
         }
     };
-    auto store = [&](int buf, int c0) {
+    auto kload = [&](f32x4 (&kv)[4], int t0, int c0) {
+        const int c = c0 + c4;
 #pragma unroll
-        for (int i = 0; i < SC_KEYS * SC_CH / 256; ++i) {
-            const int idx = tid + 256 * i;
-            kt[buf][idx / SC_CH][idx % SC_CH] = kr[i];
-        }
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + rr + 16 * i;
+            f32x4 k4 = {0.f, 0.f, 0.f, 0.f};
+            if (t <= last_max) {
+                if (c + 4 <= L && lvec) {
+                    k4 = gload<f32x4>(Lc + (int64_t)t * L + c);
+                } else {
+                    float e[4];
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / (SC_HEADS * SC_CH), hh = (idx / SC_CH) % SC_HEADS, cc = idx % SC_CH;
-            qt[buf][r][hh][cc] = qv[i];
-            if (blockIdx.x == 0 && r < nr && h0 + hh < H && c0 + cc < L)
-                qabs[((int64_t)(rb0 + r) * H + h0 + hh) * L + c0 + cc] = qv[i];
+                    for (int k = 0; k < 4; ++k) {
+                        const int ck = c + k;
+                        e[k] = ck < L ? Lc[(int64_t)t * L + ck] : (ck < C ? Rc[(int64_t)t * dr + (ck - L)] : 0.f);
+                    }
+                    k4 = f32x4{e[0], e[1], e[2], e[3]};
+                }
+            }
+            kv[i] = k4;
         }
     };
-    float tot[R];
+    auto put = [&](float (*dst)[SX_LD], const f32x4 (&v)[4]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) tot[r] = 0.f;
-    if (ch0 < ch1) {
-        fetch(ch0 * SC_CH);
-        store(0, ch0 * SC_CH);
-    }
-    __syncthreads();
-    for (int ch = ch0; ch < ch1; ++ch) {
-        const int buf = (ch - ch0) & 1;
-        if (ch + 1 < ch1)
-            fetch((ch + 1) * SC_CH);
-        float a[R];
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(&dst[rr + 16 * i][c4]) = v[i];
+    };
+    const bool qres = ch1 - ch0 <= SX_QCH;  // the split's query chunks stay in LDS
+    const int am = 16 * wave + (lane & 15), bn = lane & 15, g4 = 4 * (lane >> 4);
+    bool qdone = false;
+    for (int kt = blockIdx.x; kt < nkt; kt += gridDim.x) {
+        const int t0 = kt * SX_T;
+        f32x4 acc[4];
 #pragma unroll
-        for (int r = 0; r < R; ++r) a[r] = 0.f;
-#pragma unroll 4
-        for (int cc = 0; cc < SC_CH; cc += 4) {
-            const float k0 = kt[buf][lane][cc], k1 = kt[buf][lane][cc + 1];
-            const float k2 = kt[buf][lane][cc + 2], k3 = kt[buf][lane][cc + 3];
+        for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 qv[4], kv[4];
+        // chunk c's query values (when not resident) and keys are requested
+        // during chunk c - 1
+        auto request = [&](int ch) {
+            if (!qres || !qdone)
+                qload(qv, ch * SC_CH);
+            kload(kv, t0, ch * SC_CH);
+        };
+        if (ch0 < ch1)
+            request(ch0);
+        for (int ch = ch0; ch < ch1; ++ch) {
+            const int qi = qres ? ch - ch0 : 0;
+            __syncthreads();  // the previous chunk's products are done with ks (and qs[qi])
+            if (!qres || !qdone) {
+                put(qs[qi], qv);
+                if (blockIdx.x == 0 && !qdone) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const f32x4 qq = *reinterpret_cast<const f32x4 *>(&qt[buf][r][wave][cc]);
-                a[r] = fmaf(qq.x, k0, a[r]);
-                a[r] = fmaf(qq.y, k1, a[r]);
-                a[r] = fmaf(qq.z, k2, a[r]);
-                a[r] = fmaf(qq.w, k3, a[r]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = rr + 16 * i;
+                        if (r < S && ch * SC_CH + c4 < L)
+                            *reinterpret_cast<f32x4 *>(qabs + ((int64_t)r * H + h) * L + ch * SC_CH + c4) = qv[i];
+                    }
+                }
+            }
+            put(ks, kv);
+            __syncthreads();
+            if (ch + 1 < ch1)
+                request(ch + 1);
+#pragma unroll
+            for (int kb = 0; kb < SC_CH; kb += 16) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&qs[qi][am][kb + g4]);
+                f32x4 b4[4];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    b4[nb] = *reinterpret_cast<const f32x4 *>(&ks[16 * nb + bn][kb + g4]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[j], b4[nb][j], acc[nb], 0, 0, 0);
             }
         }
+        qdone = true;
 #pragma unroll
-        for (int r = 0; r < R; ++r) tot[r] += a[r];
-        if (ch + 1 < ch1)
-            store(buf ^ 1, (ch + 1) * SC_CH);
-        __syncthreads();
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * wave + 4 * (lane >> 4) + i, t = t0 + 16 * nb + (lane & 15);
+                if (r < S && t <= pos_base + r)
+                    sc_part[(((int64_t)split * S + r) * H + h) * Tcap + t] = acc[nb][i];
+            }
     }
-    const int t = t0 + lane, h = h0 + wave;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (r < nr && t <= pos_base + rb0 + r && h < H)
-            sc_part[(((int64_t)split * S + rb0 + r) * H + h) * Tcap + t] = tot[r];
 }
 
 // ---- softmax and the latent context ----------------------------------------
@@ -953,11 +1004,12 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
         const dim3 grid((unsigned)((nkeys + SC_KEYS - 1) / SC_KEYS),
                         (unsigned)((H + SC_HEADS - 1) / SC_HEADS), (unsigned)(G * MLA_SC_SPLIT));
         if (G > MLA_CHUNK) {
-            constexpr int R = COLI_MLA_SCORE_ROWS;
-            const dim3 gridr(grid.x, grid.y, (unsigned)(((G + R - 1) / R) * MLA_SC_SPLIT));
-            hipLaunchKernelGGL(k_mla_scores_rows<R>, gridr, dim3(256), 0, st, (const float *)part,
+            const int lvec = (uintptr_t)a.Lc % 16 == 0;
+            const int nkt = (nkeys + SX_T - 1) / SX_T;
+            const dim3 gridx((unsigned)(nkt < SX_KW ? nkt : SX_KW), (unsigned)H, (unsigned)MLA_SC_SPLIT);
+            hipLaunchKernelGGL(k_mla_scores_mx, gridx, dim3(256), 0, st, (const float *)part,
                                (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
-                               L, dr, pos_base, a.T_cap, qabs, sc_part);
+                               L, dr, pos_base, a.T_cap, lvec, qabs, sc_part);
         } else {
             const int lvec = (uintptr_t)a.Lc % 16 == 0;
             hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
