@@ -521,10 +521,6 @@ constexpr int CL_KEYS = 64;
 #define COLI_MLA_SM_KJ 9
 #endif
 constexpr int SM_KJ = COLI_MLA_SM_KJ;
-// query rows per workgroup of the prefill latent-context kernel
-#ifndef COLI_MLA_CLAT_ROWS
-#define COLI_MLA_CLAT_ROWS 8
-#endif
 
 __device__ __forceinline__ float mla_score(const float *__restrict__ sc_part, int64_t sstride,
                                            int64_t at, float scale) {
@@ -639,82 +635,135 @@ __global__ __launch_bounds__(256) void k_mla_softmax_stats(const float *__restri
     }
 }
 
-// Prefill rows: probabilities and the latent-context partials with R query
-// rows per workgroup sharing one staged chunk of Lc rows; grid (64-key chunks,
-// 64-column tiles, ceil(S / R) row blocks x 4-head groups).  p and each
-// chunk's sum are formed exactly as in k_mla_softmax_clat (same statistics,
-// same order of the 64 products), so the results are the same bits.
-template <int R>
-__global__ __launch_bounds__(256) void k_mla_clat_rows(const float *__restrict__ sc_part,
-                                                       const float *__restrict__ stats,
-                                                       const float *__restrict__ Lc, int S, int H,
-                                                       int L, int pos_base, int Tcap, float scale,
-                                                       float *__restrict__ scores,
-                                                       float *__restrict__ p,
-                                                       float *__restrict__ cl_part) {
-    __shared__ float lt[CL_KEYS][CL_COLS + 1];
-    __shared__ __attribute__((aligned(16))) float pt[R][CL_HEADS][CL_KEYS];
-    const int chunk = blockIdx.x, t0 = chunk * CL_KEYS, c0 = blockIdx.y * CL_COLS;
-    const int ng = (H + CL_HEADS - 1) / CL_HEADS;
-    const int rb0 = R * (int)(blockIdx.z / ng), h0 = (blockIdx.z % ng) * CL_HEADS;
+// Prefill rows on the fp32 matrix cores: one 64-key chunk's share of clat
+// for one head and the group's rows (up to 64); grid (64-key chunks, CX_CW
+// column groups, heads), each workgroup taking every CX_CW-th 64-column
+// tile; the partials k_mla_softmax_clat writes for decode rows
+// (cl_part[chunk][s][h][c] for the chunks that hold keys of row s; column
+// group 0 stores the chunk's scores and probabilities).  p = exp(z - max) /
+// sum (the row's statistics from k_mla_softmax_stats) is formed once into
+// LDS; the column tiles of the chunk's Lc rows follow one another through LDS
+// (transposed, key-contiguous; the next tile requested while the current one
+// is multiplied).  Wavefront w takes rows 16 w .. 16 w + 15 x the 64 columns
+// as four 16 x 16 tiles of v_mfma_f32_16x16x4f32 over the 64 keys, product j
+// giving lane group g = l / 16 key 4 g + j of each 16-key block (16-byte LDS
+// operand reads).
+constexpr int CX_T = 64;               // rows, keys and columns per tile
+constexpr int CX_LD = CX_T + 4;        // LDS row stride
+#ifndef COLI_MLA_CX_CW
+#define COLI_MLA_CX_CW 2
+#endif
+constexpr int CX_CW = COLI_MLA_CX_CW;  // workgroups per (chunk, head), along the column tiles
+static_assert(MLA_GROUP <= CX_T, "a prefill group's rows fit one tile");
+static_assert(CX_T == CL_KEYS, "the partials are per key chunk of CL_KEYS");
+__global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ sc_part,
+                                                     const float *__restrict__ stats,
+                                                     const float *__restrict__ Lc, int S, int H,
+                                                     int L, int pos_base, int Tcap, float scale,
+                                                     int lvec, float *__restrict__ scores,
+                                                     float *__restrict__ p,
+                                                     float *__restrict__ cl_part) {
+    __shared__ __attribute__((aligned(16))) float ps[CX_T][CX_LD];  // [row][key]
+    __shared__ __attribute__((aligned(16))) float lt[CX_T][CX_LD];  // [column][key]
+    const int chunk = blockIdx.x, t0 = chunk * CX_T, h = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nr = min(R, S - rb0);
-    const int n_max = pos_base + rb0 + nr;  // keys of the block's last row
+    const int n_max = pos_base + S;  // keys of the group's last row
     if (t0 >= n_max)
         return;
     const int64_t sstride = (int64_t)S * H * Tcap;
-    float lr[CL_KEYS * CL_COLS / 256];
+    const int rr = tid >> 4, c4 = 4 * (tid & 15);
+    const int nct = (L + CX_T - 1) / CX_T;
+    // the Lc rows of a column tile (keys rr + 16 i, columns c0 + c4 .. + 3)
+    f32x4 lv[4];
+    auto lload = [&](int c0) {
 #pragma unroll
-    for (int i = 0; i < CL_KEYS * CL_COLS / 256; ++i) {
-        const int idx = tid + 256 * i, tt = idx / CL_COLS, c = idx % CL_COLS;
-        const int t = t0 + tt;
-        lr[i] = (t < n_max && c0 + c < L) ? Lc[(int64_t)t * L + c0 + c] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + rr + 16 * i, c = c0 + c4;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (t < n_max) {
+                if (c + 4 <= L && lvec) {
+                    v = gload<f32x4>(Lc + (int64_t)t * L + c);
+                } else {
+                    float e[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) e[k] = c + k < L ? Lc[(int64_t)t * L + c + k] : 0.f;
+                    v = f32x4{e[0], e[1], e[2], e[3]};
+                }
+            }
+            lv[i] = v;
+        }
+    };
+    if (blockIdx.y < nct)
+        lload(blockIdx.y * CX_T);  // requested first: it does not depend on the scores
+    // probabilities of rows rr + 16 i at keys t0 + c4 .. + 3: every score
+    // and statistic requested at once (clamped addresses), masked afterwards
+    float zz[4][4], sm[4], se[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rc = min(rr + 16 * i, S - 1);
+        const int64_t zrow = ((int64_t)rc * H + h) * Tcap;
+        sm[i] = stats[((int64_t)rc * H + h) * 2];
+        se[i] = stats[((int64_t)rc * H + h) * 2 + 1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            zz[i][k] = mla_score(sc_part, sstride, zrow + min(t0 + c4 + k, Tcap - 1), scale);
     }
-    const int h = h0 + wave;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int s = rb0 + r, t = t0 + lane;
-        const int n = pos_base + s + 1;
-        float pv = 0.f;
-        if (r < nr && h < H && t < n) {
-            const int64_t zrow = ((int64_t)s * H + h) * Tcap;
-            const float m = stats[((int64_t)s * H + h) * 2], e = stats[((int64_t)s * H + h) * 2 + 1];
-            const float z = mla_score(sc_part, sstride, zrow + t, scale);
-            pv = expf(z - m) / e;
-            if (blockIdx.y == 0) {
-                scores[zrow + t] = z;
-                p[zrow + t] = pv;
+    for (int i = 0; i < 4; ++i) {
+        const int r = rr + 16 * i;
+        const int64_t zrow = ((int64_t)r * H + h) * Tcap;
+        float pv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = t0 + c4 + k;
+            const bool ok = r < S && t < pos_base + r + 1;
+            pv[k] = ok ? expf(zz[i][k] - sm[i]) / se[i] : 0.f;
+            if (ok && blockIdx.y == 0) {
+                scores[zrow + t] = zz[i][k];
+                p[zrow + t] = pv[k];
             }
         }
-        pt[r][wave][lane] = pv;
+        *reinterpret_cast<f32x4 *>(&ps[r][c4]) = f32x4{pv[0], pv[1], pv[2], pv[3]};
     }
+    const int am = 16 * wave + (lane & 15), bn = lane & 15, g4 = 4 * (lane >> 4);
+    for (int ct = blockIdx.y; ct < nct; ct += gridDim.y) {
+        const int c0 = ct * CX_T;
+        __syncthreads();  // the previous tile's products are done with lt
 #pragma unroll
-    for (int i = 0; i < CL_KEYS * CL_COLS / 256; ++i) {
-        const int idx = tid + 256 * i;
-        lt[idx / CL_COLS][idx % CL_COLS] = lr[i];
-    }
-    __syncthreads();
-    float a[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) a[r] = 0.f;
-#pragma unroll 4
-    for (int tt = 0; tt < CL_KEYS; tt += 4) {
-        const float l0 = lt[tt][lane], l1 = lt[tt + 1][lane], l2 = lt[tt + 2][lane],
-                    l3 = lt[tt + 3][lane];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const f32x4 pp = *reinterpret_cast<const f32x4 *>(&pt[r][wave][tt]);
-            a[r] = fmaf(pp.x, l0, a[r]);
-            a[r] = fmaf(pp.y, l1, a[r]);
-            a[r] = fmaf(pp.z, l2, a[r]);
-            a[r] = fmaf(pp.w, l3, a[r]);
+        for (int i = 0; i < 4; ++i) {
+            const int kk = rr + 16 * i;
+            lt[c4][kk] = lv[i].x;
+            lt[c4 + 1][kk] = lv[i].y;
+            lt[c4 + 2][kk] = lv[i].z;
+            lt[c4 + 3][kk] = lv[i].w;
         }
-    }
-    const int c = c0 + lane;
+        __syncthreads();
+        if (ct + (int)gridDim.y < nct)
+            lload(c0 + (int)gridDim.y * CX_T);
+        f32x4 acc[4];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (r < nr && h < H && c < L && t0 < pos_base + rb0 + r + 1)
-            cl_part[(((int64_t)chunk * S + rb0 + r) * H + h) * L + c] = a[r];
+        for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < CX_T; kb += 16) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&ps[am][kb + g4]);
+            f32x4 b4[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) b4[nb] = *reinterpret_cast<const f32x4 *>(&lt[16 * nb + bn][kb + g4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[j], b4[nb][j], acc[nb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * wave + 4 * (lane >> 4) + i, c = c0 + 16 * nb + (lane & 15);
+                if (r < S && c < L && t0 < pos_base + r + 1)
+                    cl_part[(((int64_t)chunk * S + r) * H + h) * L + c] = acc[nb][i];
+            }
+    }
 }
 
 // Prefill rows whose value absorption runs on the matrix cores afterwards:
@@ -1031,12 +1080,13 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
             hipLaunchKernelGGL(k_mla_softmax_stats, dim3((unsigned)G, (unsigned)((H + CL_HEADS - 1) / CL_HEADS)),
                                dim3(256), 0, st, (const float *)sc_part, G, H, pos_base, a.T_cap,
                                scale, stats);
-            constexpr int R = COLI_MLA_CLAT_ROWS;
-            const dim3 gridr(grid.x, grid.y,
-                             (unsigned)(((G + R - 1) / R) * ((H + CL_HEADS - 1) / CL_HEADS)));
-            hipLaunchKernelGGL(k_mla_clat_rows<R>, gridr, dim3(256), 0, st, (const float *)sc_part,
+            const int lvec = (uintptr_t)a.Lc % 16 == 0;
+            const int nct = (L + CX_T - 1) / CX_T;
+            const dim3 gridx((unsigned)((nkeys + CX_T - 1) / CX_T), (unsigned)(nct < CX_CW ? nct : CX_CW),
+                             (unsigned)H);
+            hipLaunchKernelGGL(k_mla_clat_mx, gridx, dim3(256), 0, st, (const float *)sc_part,
                                (const float *)stats, (const float *)a.Lc, G, H, L, pos_base,
-                               a.T_cap, scale, sc, p, cl_part);
+                               a.T_cap, scale, lvec, sc, p, cl_part);
         } else {
             hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
                                (const float *)a.Lc, G, H, L, pos_base, a.T_cap, scale, sc, p,
