@@ -221,6 +221,131 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
         }
 }
 
+// Prefill rows (a group of up to 64): the key absorption on the fp32 matrix
+// cores, with the key side and the query rotation as other workgroups of the
+// same launch.  Workgroups [0, H * ncol): qabs[s][h][c] = sum_j q[s][h][j]
+// W_UK[h][j][c] for the group's rows x 64 latent columns of head h, over the
+// d_nope key rows in chunks of 64 (query values and kv_b's key rows, the
+// latter decoded to s * (q - 8) exactly as the vector kernel forms them and
+// stored column-major, through LDS; the next chunk requested while the
+// current one is multiplied); wavefront w takes rows 16 w .. 16 w + 15 as
+// four 16 x 16 tiles of v_mfma_f32_16x16x4f32, product j giving lane group
+// g = l / 16 key row 4 g + j of each 16-row block (16-byte LDS operand
+// reads).  The next S workgroups: the key side of row s (latent RMSNorm into
+// cache row pos_base + s of Lc, rotary key into the same row of Rc); the last
+// S: the rotation of row s's query rotary parts into qpe.
+constexpr int QX_T = 64;             // rows, key rows and columns per tile
+constexpr int QX_LD = QX_T + 4;      // LDS row stride
+static_assert(MLA_GROUP <= QX_T, "a prefill group's rows fit one tile");
+template <bool GRP>
+__global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, int dn, int dr,
+                                                     int dv, int L, const float *__restrict__ q,
+                                                     int pos_base, double theta,
+                                                     float *__restrict__ qabs,
+                                                     float *__restrict__ qpe,
+                                                     const float *__restrict__ ckv,
+                                                     const float *__restrict__ kn, double eps,
+                                                     float *__restrict__ Lc,
+                                                     float *__restrict__ Rc) {
+    __shared__ __attribute__((aligned(16))) float qa[QX_T][QX_LD];  // [row][key row]
+    __shared__ __attribute__((aligned(16))) float wt[QX_T][QX_LD];  // [column][key row]
+    __shared__ double npart[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ncol = (L + QX_T - 1) / QX_T;
+    const int nq = H * (dn + dr);
+    int bx = blockIdx.x;
+    if (bx >= H * ncol) {
+        bx -= H * ncol;
+        if (bx < S) {  // key side of row bx
+            const int pos = pos_base + bx;
+            const float *xr = ckv + (int64_t)bx * (L + dr);
+            mla_row_norm<256>(xr, L, kn, eps, Lc + (int64_t)pos * L, npart);
+            for (int i = tid; i < dr / 2; i += 256)
+                rope_pair(xr[L + 2 * i], xr[L + 2 * i + 1], i, dr, pos, theta,
+                          Rc + (int64_t)pos * dr + 2 * i, Rc + (int64_t)pos * dr + 2 * i + 1);
+        } else if (bx < 2 * S) {  // query rotation of row bx - S
+            const int srow = bx - S;
+            for (int idx = tid; idx < H * (dr / 2); idx += 256) {
+                const int h = idx / (dr / 2), i = idx % (dr / 2);
+                const float *qr = q + (int64_t)srow * nq + (int64_t)h * (dn + dr) + dn;
+                float *o = qpe + ((int64_t)srow * H + h) * dr;
+                rope_pair(qr[2 * i], qr[2 * i + 1], i, dr, pos_base + srow, theta, o + 2 * i, o + 2 * i + 1);
+            }
+        }
+        return;
+    }
+    const int h = bx / ncol, c0 = (bx % ncol) * QX_T;
+    const int rr = tid >> 4, j4 = 4 * (tid & 15);  // query staging: rows rr + 16 i, key rows j4 .. + 3
+    const int wr = tid >> 2, w8 = 16 * (tid & 3);  // weight staging: key row wr, columns w8 .. + 15
+    f32x4 qv[4];
+    float wv[16];
+    auto request = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rr + 16 * i, j = j0 + j4;
+            float e[4] = {0.f, 0.f, 0.f, 0.f};
+            if (r < S) {
+                const float *qr = q + (int64_t)r * nq + (int64_t)h * (dn + dr);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) e[k] = j + k < dn ? qr[j + k] : 0.f;
+            }
+            qv[i] = f32x4{e[0], e[1], e[2], e[3]};
+        }
+        const int j = j0 + wr;
+        const int64_t row = (int64_t)h * (dn + dv) + min(j, dn - 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = c0 + w8 + 8 * u;  // 8 columns, one code word
+            uint32_t w = 0x88888888u;
+            float sc = 0.f;
+            if (j < dn && c < L) {
+                w = gload<uint32_t>(kb.q + row * kb.rb + c / 2);
+                sc = GRP ? gload<float>(kb.s + row * kb.ng + c / kb.gs) : gload<float>(kb.s + row);
+            }
+            float f[8];
+            decode_nib_word(w, f);  // 16 (nibble - 8)
+            const float k16 = sc * 0.0625f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) wv[8 * u + k] = f[k] * k16;
+        }
+    };
+    const int am = 16 * wave + (lane & 15), bn = lane & 15, g4 = 4 * (lane >> 4);
+    f32x4 acc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    request(0);
+    for (int j0 = 0; j0 < dn; j0 += QX_T) {
+        __syncthreads();  // the previous chunk's products are done with qa and wt
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(&qa[rr + 16 * i][j4]) = qv[i];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) wt[w8 + k][wr] = wv[k];
+        __syncthreads();
+        if (j0 + QX_T < dn)
+            request(j0 + QX_T);
+#pragma unroll
+        for (int kb4 = 0; kb4 < QX_T; kb4 += 16) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&qa[am][kb4 + g4]);
+            f32x4 b4[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) b4[nb] = *reinterpret_cast<const f32x4 *>(&wt[16 * nb + bn][kb4 + g4]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], b4[nb][jj], acc[nb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wave + 4 * (lane >> 4) + i, c = c0 + 16 * nb + (lane & 15);
+            if (r < S && c < L)
+                qabs[((int64_t)r * H + h) * L + c] = acc[nb][i];
+        }
+}
+
 // ---- scores ----------------------------------------------------------------
 // Partial scores over one third of the L + d_rope components (Q = [qabs,
 // qpe], K = [Lc, Rc]): grid (64-key tiles, 4-head groups, row x MLA_SC_SPLIT).
@@ -337,9 +462,9 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
 // Prefill rows on the fp32 matrix cores: partial scores over one third of
 // the L + d_rope components for one head and the group's rows (up to 64);
 // grid (SX_KW key-tile lanes, heads, MLA_SC_SPLIT): workgroup x takes the
-// 64-key tiles x, x + SX_KW, ...  The query tile of the split (the qabs
-// partials added in split order, then qpe) is summed once into LDS and stays
-// there while the key tiles stream through, component chunk by chunk (64
+// 64-key tiles x, x + SX_KW, ...  The query tile of the split (qabs, then
+// qpe) is staged once into LDS and stays there while the key tiles stream
+// through, component chunk by chunk (64
 // components; the next chunk requested into registers while the current one
 // is multiplied).  Wavefront w takes rows 16 w .. 16 w + 15 against the 64
 // keys of a tile as four 16 x 16 tiles of v_mfma_f32_16x16x4f32 (A lane l =
@@ -349,8 +474,8 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
 // 4 g + j, so a lane reads its four components with one 16-byte LDS read
 // (the sum over the block is the same up to rounding order).  Rows past S, keys past the group's last
 // position and scores past a row's own position are neither loaded nor
-// stored; workgroup x = 0 stores qabs.  A split of more than SX_QCH chunks
-// stages its query chunks again for every key tile.
+// stored.  A split of more than SX_QCH chunks stages its query chunks again
+// for every key tile.
 constexpr int SX_T = 64;    // rows = keys per tile
 // workgroups per (head, split), along the key tiles
 #ifndef COLI_MLA_SX_KW
@@ -360,13 +485,12 @@ constexpr int SX_KW = COLI_MLA_SX_KW;
 constexpr int SX_QCH = 3;   // query chunks kept in LDS
 constexpr int SX_LD = SC_CH + 4;  // LDS row stride (16-byte rows for the 4-component reads)
 static_assert(MLA_GROUP <= SX_T, "a prefill group's rows fit one tile");
-__global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__ part,
+__global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__ qabs,
                                                        const float *__restrict__ qpe,
                                                        const float *__restrict__ Lc,
                                                        const float *__restrict__ Rc, int S, int H,
                                                        int L, int dr, int pos_base, int Tcap,
-                                                       int lvec, float *__restrict__ qabs,
-                                                       float *__restrict__ sc_part) {
+                                                       int lvec, float *__restrict__ sc_part) {
     __shared__ __attribute__((aligned(16))) float qs[SX_QCH][SX_T][SX_LD];
     __shared__ __attribute__((aligned(16))) float ks[SX_T][SX_LD];
     const int h = blockIdx.y, split = blockIdx.z;
@@ -378,7 +502,6 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
     const int per = (nch_all + MLA_SC_SPLIT - 1) / MLA_SC_SPLIT;
     // (a split with no chunks, when L + d_rope is short, stores zero partials)
     const int ch0 = split * per, ch1 = min(nch_all, ch0 + per);
-    const int64_t pstride = (int64_t)S * H * L;
     // staging: thread t takes 4 consecutive components (4 (t % 16)) of rows /
     // keys t / 16 + 16 i, i < 4
     const int rr = tid >> 4, c4 = 4 * (tid & 15);
@@ -390,25 +513,14 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
             f32x4 q = {0.f, 0.f, 0.f, 0.f};
             if (r < S) {
                 if (c + 4 <= L) {
-                    const float *pp = part + ((int64_t)r * H + h) * L + c;
-                    q = gload<f32x4>(pp);
-#pragma unroll
-                    for (int k = 1; k < MLA_QA_SPLIT; ++k) q += gload<f32x4>(pp + k * pstride);
+                    q = gload<f32x4>(qabs + ((int64_t)r * H + h) * L + c);
                 } else {
                     float e[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int ck = c + k;
-                        float v = 0.f;
-                        if (ck < L) {
-                            const float *pp = part + ((int64_t)r * H + h) * L + ck;
-                            v = pp[0];
-#pragma unroll
-                            for (int u = 1; u < MLA_QA_SPLIT; ++u) v += pp[u * pstride];
-                        } else if (ck < C) {
-                            v = qpe[((int64_t)r * H + h) * dr + (ck - L)];
-                        }
-                        e[k] = v;
+                        e[k] = ck < L ? qabs[((int64_t)r * H + h) * L + ck]
+                                      : (ck < C ? qpe[((int64_t)r * H + h) * dr + (ck - L)] : 0.f);
                     }
                     q = f32x4{e[0], e[1], e[2], e[3]};
                 }
@@ -463,17 +575,8 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
         for (int ch = ch0; ch < ch1; ++ch) {
             const int qi = qres ? ch - ch0 : 0;
             __syncthreads();  // the previous chunk's products are done with ks (and qs[qi])
-            if (!qres || !qdone) {
+            if (!qres || !qdone)
                 put(qs[qi], qv);
-                if (blockIdx.x == 0 && !qdone) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = rr + 16 * i;
-                        if (r < S && ch * SC_CH + c4 < L)
-                            *reinterpret_cast<f32x4 *>(qabs + ((int64_t)r * H + h) * L + ch * SC_CH + c4) = qv[i];
-                    }
-                }
-            }
             put(ks, kv);
             __syncthreads();
             if (ch + 1 < ch1)
@@ -1032,20 +1135,33 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     const int rem = G % MLA_CHUNK, rrem = (int)nfull * MLA_CHUNK;
     {
         ProfScope ps("mla_qabs", st);
-        if (nfull > 0)
-            qabs_launch<MLA_CHUNK>(grp, nfull, 0, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
-                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st);
-        switch (rem) {
-            case 1: qabs_launch<1>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
-                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
-            case 2: qabs_launch<2>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
-                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
-            case 3: qabs_launch<3>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
-                                   qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
-            default: break;
+        if (G > MLA_CHUNK) {
+            // prefill group: qabs on the matrix cores, key side and query rotation beside it
+            const unsigned nblk = (unsigned)(H * ((L + QX_T - 1) / QX_T) + 2 * G);
+            if (grp)
+                hipLaunchKernelGGL(k_mla_qabs_mx<true>, dim3(nblk), dim3(256), 0, st, kb, G, H, dn, dr,
+                                   dv, L, q, pos_base, theta, qabs, qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc);
+            else
+                hipLaunchKernelGGL(k_mla_qabs_mx<false>, dim3(nblk), dim3(256), 0, st, kb, G, H, dn, dr,
+                                   dv, L, q, pos_base, theta, qabs, qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc);
+            const int rc = after_launch("mla_qabs");
+            if (rc != COLI_OK) return rc;
+        } else {
+            if (nfull > 0)
+                qabs_launch<MLA_CHUNK>(grp, nfull, 0, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                       qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st);
+            switch (rem) {
+                case 1: qabs_launch<1>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                       qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
+                case 2: qabs_launch<2>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                       qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
+                case 3: qabs_launch<3>(grp, 1, rrem, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
+                                       qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st); break;
+                default: break;
+            }
+            const int rc = after_launch("mla_qabs");
+            if (rc != COLI_OK) return rc;
         }
-        const int rc = after_launch("mla_qabs");
-        if (rc != COLI_OK) return rc;
     }
     {
         ProfScope ps("mla_scores", st);
@@ -1056,9 +1172,9 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
             const int lvec = (uintptr_t)a.Lc % 16 == 0;
             const int nkt = (nkeys + SX_T - 1) / SX_T;
             const dim3 gridx((unsigned)(nkt < SX_KW ? nkt : SX_KW), (unsigned)H, (unsigned)MLA_SC_SPLIT);
-            hipLaunchKernelGGL(k_mla_scores_mx, gridx, dim3(256), 0, st, (const float *)part,
+            hipLaunchKernelGGL(k_mla_scores_mx, gridx, dim3(256), 0, st, (const float *)qabs,
                                (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
-                               L, dr, pos_base, a.T_cap, lvec, qabs, sc_part);
+                               L, dr, pos_base, a.T_cap, lvec, sc_part);
         } else {
             const int lvec = (uintptr_t)a.Lc % 16 == 0;
             hipLaunchKernelGGL(k_mla_scores, grid, dim3(256), 0, st, (const float *)part,
