@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
 constexpr int SX_T = 64;    // rows = keys per tile
 // workgroups per (head, split), along the key tiles
 #ifndef COLI_MLA_SX_KW
-#define COLI_MLA_SX_KW 2
+#define COLI_MLA_SX_KW 4
 #endif
 constexpr int SX_KW = COLI_MLA_SX_KW;
 constexpr int SX_QCH = 3;   // query chunks kept in LDS
