@@ -31,7 +31,6 @@ static_assert(MLA_GROUP % MLA_CHUNK == 0, "whole chunks per group");
 struct MlaLayout {
     size_t off[MLA_NSTAGE];
     size_t qabs_part, sc_part, cl_part;  // partial sums (internal)
-    size_t stats;                        // prefill rows: softmax max and sum per (row, head)
     size_t xprep, xprep_bytes;           // prefill rows: the projections' prepared inputs
     size_t total;
 };

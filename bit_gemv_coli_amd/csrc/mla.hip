@@ -712,12 +712,15 @@ __global__ __launch_bounds__(256) void k_mla_softmax_clat(const float *__restric
         cl_part[(((int64_t)chunk * S + s) * H + h) * L + c] = a;
 }
 
-// Prefill rows: the softmax statistics once per (row, head) -- the same
-// strided max and sum of exp(z - max) as above, in the same order -- into
-// stats[(s H + h) 2 + {0, 1}]; grid (rows, 4-head groups), a wavefront per head.
-__global__ __launch_bounds__(256) void k_mla_softmax_stats(const float *__restrict__ sc_part,
-                                                           int S, int H, int pos_base, int Tcap,
-                                                           float scale, float *__restrict__ stats) {
+// Prefill rows: the softmax of each (row, head) -- the same strided max and
+// sum of exp(z - max) as above, in the same order (the first SM_KJ keys per
+// lane requested together and kept) -- then the row's scores and
+// probabilities p = exp(z - max) / sum for every key; grid (rows, 4-head
+// groups), a wavefront per head.
+__global__ __launch_bounds__(256) void k_mla_softmax_rows(const float *__restrict__ sc_part,
+                                                          int S, int H, int pos_base, int Tcap,
+                                                          float scale, float *__restrict__ scores,
+                                                          float *__restrict__ p) {
     const int s = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.y * CL_HEADS + wave;
     if (h >= H)
@@ -725,16 +728,36 @@ __global__ __launch_bounds__(256) void k_mla_softmax_stats(const float *__restri
     const int n = pos_base + s + 1;
     const int64_t sstride = (int64_t)S * H * Tcap;
     const int64_t zrow = ((int64_t)s * H + h) * Tcap;
+    float zk[SM_KJ];
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) {
+        const int t = lane + 64 * j;
+        const float z = mla_score(sc_part, sstride, zrow + min(t, n - 1), scale);
+        zk[j] = t < n ? z : -__builtin_inff();
+    }
     float m = -__builtin_inff();
-    for (int t = lane; t < n; t += 64) m = fmaxf(m, mla_score(sc_part, sstride, zrow + t, scale));
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) m = fmaxf(m, zk[j]);
+    for (int t = lane + 64 * SM_KJ; t < n; t += 64) m = fmaxf(m, mla_score(sc_part, sstride, zrow + t, scale));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float e = 0.f;
-    for (int t = lane; t < n; t += 64) e += expf(mla_score(sc_part, sstride, zrow + t, scale) - m);
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) e += expf(zk[j] - m);
+    for (int t = lane + 64 * SM_KJ; t < n; t += 64) e += expf(mla_score(sc_part, sstride, zrow + t, scale) - m);
     e = wave_sum(e);
-    if (lane == 0) {
-        stats[((int64_t)s * H + h) * 2] = m;
-        stats[((int64_t)s * H + h) * 2 + 1] = e;
+#pragma unroll
+    for (int j = 0; j < SM_KJ; ++j) {
+        const int t = lane + 64 * j;
+        if (t < n) {
+            scores[zrow + t] = zk[j];
+            p[zrow + t] = expf(zk[j] - m) / e;
+        }
+    }
+    for (int t = lane + 64 * SM_KJ; t < n; t += 64) {
+        const float z = mla_score(sc_part, sstride, zrow + t, scale);
+        scores[zrow + t] = z;
+        p[zrow + t] = expf(z - m) / e;
     }
 }
 
@@ -742,9 +765,8 @@ __global__ __launch_bounds__(256) void k_mla_softmax_stats(const float *__restri
 // for one head and the group's rows (up to 64); grid (64-key chunks, CX_CW
 // column groups, heads), each workgroup taking every CX_CW-th 64-column
 // tile; the partials k_mla_softmax_clat writes for decode rows
-// (cl_part[chunk][s][h][c] for the chunks that hold keys of row s; column
-// group 0 stores the chunk's scores and probabilities).  p = exp(z - max) /
-// sum (the row's statistics from k_mla_softmax_stats) is formed once into
+// (cl_part[chunk][s][h][c] for the chunks that hold keys of row s).  The
+// chunk's probabilities (written by k_mla_softmax_rows) are staged once into
 // LDS; the column tiles of the chunk's Lc rows follow one another through LDS
 // (transposed, key-contiguous; the next tile requested while the current one
 // is multiplied).  Wavefront w takes rows 16 w .. 16 w + 15 x the 64 columns
@@ -759,12 +781,9 @@ constexpr int CX_LD = CX_T + 4;        // LDS row stride
 constexpr int CX_CW = COLI_MLA_CX_CW;  // workgroups per (chunk, head), along the column tiles
 static_assert(MLA_GROUP <= CX_T, "a prefill group's rows fit one tile");
 static_assert(CX_T == CL_KEYS, "the partials are per key chunk of CL_KEYS");
-__global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ sc_part,
-                                                     const float *__restrict__ stats,
+__global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p,
                                                      const float *__restrict__ Lc, int S, int H,
-                                                     int L, int pos_base, int Tcap, float scale,
-                                                     int lvec, float *__restrict__ scores,
-                                                     float *__restrict__ p,
+                                                     int L, int pos_base, int Tcap, int lvec,
                                                      float *__restrict__ cl_part) {
     __shared__ __attribute__((aligned(16))) float ps[CX_T][CX_LD];  // [row][key]
     __shared__ __attribute__((aligned(16))) float lt[CX_T][CX_LD];  // [column][key]
@@ -773,7 +792,6 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ s
     const int n_max = pos_base + S;  // keys of the group's last row
     if (t0 >= n_max)
         return;
-    const int64_t sstride = (int64_t)S * H * Tcap;
     const int rr = tid >> 4, c4 = 4 * (tid & 15);
     const int nct = (L + CX_T - 1) / CX_T;
     // the Lc rows of a column tile (keys rr + 16 i, columns c0 + c4 .. + 3)
@@ -798,34 +816,21 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ s
     };
     if (blockIdx.y < nct)
         lload(blockIdx.y * CX_T);  // requested first: it does not depend on the scores
-    // probabilities of rows rr + 16 i at keys t0 + c4 .. + 3: every score
-    // and statistic requested at once (clamped addresses), masked afterwards
-    float zz[4][4], sm[4], se[4];
+    // probabilities of rows rr + 16 i at keys t0 + c4 .. + 3 (requested at
+    // once at clamped addresses, zero past each row's own position)
+    float pz[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int rc = min(rr + 16 * i, S - 1);
-        const int64_t zrow = ((int64_t)rc * H + h) * Tcap;
-        sm[i] = stats[((int64_t)rc * H + h) * 2];
-        se[i] = stats[((int64_t)rc * H + h) * 2 + 1];
+        const int64_t prow = ((int64_t)min(rr + 16 * i, S - 1) * H + h) * Tcap;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            zz[i][k] = mla_score(sc_part, sstride, zrow + min(t0 + c4 + k, Tcap - 1), scale);
+        for (int k = 0; k < 4; ++k) pz[i][k] = p[prow + min(t0 + c4 + k, Tcap - 1)];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = rr + 16 * i;
-        const int64_t zrow = ((int64_t)r * H + h) * Tcap;
         float pv[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = t0 + c4 + k;
-            const bool ok = r < S && t < pos_base + r + 1;
-            pv[k] = ok ? expf(zz[i][k] - sm[i]) / se[i] : 0.f;
-            if (ok && blockIdx.y == 0) {
-                scores[zrow + t] = zz[i][k];
-                p[zrow + t] = pv[k];
-            }
-        }
+        for (int k = 0; k < 4; ++k) pv[k] = (r < S && t0 + c4 + k < pos_base + r + 1) ? pz[i][k] : 0.f;
         *reinterpret_cast<f32x4 *>(&ps[r][c4]) = f32x4{pv[0], pv[1], pv[2], pv[3]};
     }
     const int am = 16 * wave + (lane & 15), bn = lane & 15, g4 = 4 * (lane >> 4);
@@ -1042,7 +1047,6 @@ MlaLayout mla_layout(int S, int H, int dn, int dr, int dv, int qr, int L, int Tc
     l.qabs_part = take((size_t)MLA_QA_SPLIT * Sc * H * L);
     l.sc_part = take((size_t)MLA_SC_SPLIT * Sc * H * Tcap);
     l.cl_part = take((size_t)((Tcap + CL_KEYS - 1) / CL_KEYS) * Sc * H * L);
-    l.stats = take((size_t)2 * Sc * H);
     l.xprep = take((proj_ws + sizeof(float) - 1) / sizeof(float));
     l.xprep_bytes = proj_ws;
     l.total = o;
@@ -1192,17 +1196,15 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
                         (unsigned)((L + CL_COLS - 1) / CL_COLS),
                         (unsigned)(G * ((H + CL_HEADS - 1) / CL_HEADS)));
         if (G > MLA_CHUNK) {
-            float *stats = (float *)(ws + l.stats);
-            hipLaunchKernelGGL(k_mla_softmax_stats, dim3((unsigned)G, (unsigned)((H + CL_HEADS - 1) / CL_HEADS)),
+            hipLaunchKernelGGL(k_mla_softmax_rows, dim3((unsigned)G, (unsigned)((H + CL_HEADS - 1) / CL_HEADS)),
                                dim3(256), 0, st, (const float *)sc_part, G, H, pos_base, a.T_cap,
-                               scale, stats);
+                               scale, sc, p);
             const int lvec = (uintptr_t)a.Lc % 16 == 0;
             const int nct = (L + CX_T - 1) / CX_T;
             const dim3 gridx((unsigned)((nkeys + CX_T - 1) / CX_T), (unsigned)(nct < CX_CW ? nct : CX_CW),
                              (unsigned)H);
-            hipLaunchKernelGGL(k_mla_clat_mx, gridx, dim3(256), 0, st, (const float *)sc_part,
-                               (const float *)stats, (const float *)a.Lc, G, H, L, pos_base,
-                               a.T_cap, scale, lvec, sc, p, cl_part);
+            hipLaunchKernelGGL(k_mla_clat_mx, gridx, dim3(256), 0, st, (const float *)p,
+                               (const float *)a.Lc, G, H, L, pos_base, a.T_cap, lvec, cl_part);
         } else {
             hipLaunchKernelGGL(k_mla_softmax_clat, grid, dim3(256), 0, st, (const float *)sc_part,
                                (const float *)a.Lc, G, H, L, pos_base, a.T_cap, scale, sc, p,
