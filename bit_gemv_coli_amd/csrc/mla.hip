@@ -776,7 +776,7 @@ __global__ __launch_bounds__(256) void k_mla_softmax_rows(const float *__restric
 constexpr int CX_T = 64;               // rows, keys and columns per tile
 constexpr int CX_LD = CX_T + 4;        // LDS row stride
 #ifndef COLI_MLA_CX_CW
-#define COLI_MLA_CX_CW 2
+#define COLI_MLA_CX_CW 4
 #endif
 constexpr int CX_CW = COLI_MLA_CX_CW;  // workgroups per (chunk, head), along the column tiles
 static_assert(MLA_GROUP <= CX_T, "a prefill group's rows fit one tile");
