@@ -1,4 +1,4 @@
-// mla.hip -- decode attention of one MLA layer for S <= 4 query rows
+// mla.hip -- attention of one MLA layer: decode (S <= 4 query rows) and prefill
 // (colibri-strix commit log, fused decode attention commit (Phase 2) and the
 // S <= 4 commit after it; issue #585 thread: kv_b, the absorption weight, is
 // grouped int4):
@@ -43,6 +43,20 @@
 //   k_mla_ctx         16 value rows per wavefront, 4 lanes per row with
 //                     16-byte code loads, requested before clat (the chunks'
 //                     shares added in order) is formed in LDS
+// Prefill groups (more than 4 rows, up to MLA_GROUP per launch set) run the
+// core on the fp32 matrix cores (v_mfma_f32_16x16x4f32, 64-row tiles):
+//   k_mla_qabs_mx     the group's rows x 64 latent columns of one head per
+//                     workgroup, kv_b's key rows decoded into LDS; more
+//                     workgroups of the same launch do the key side and the
+//                     query rotation
+//   k_mla_scores_mx   the group's queries resident in LDS, 64-key tiles
+//                     streamed; four workgroups per (head, component split)
+//   k_mla_softmax_rows each row's statistics from its scores kept in
+//                     registers; writes every key's score and probability
+//   k_mla_clat_mx     per 64-key chunk and head: probabilities times the
+//                     chunk's latent rows, column tiles through LDS
+//   k_mla_clat_sum    adds the chunks' partials when the value absorption of
+//                     all rows follows on the bf16 GEMM
 // At decode sizes each of these is a few dependent memory round trips of
 // ~2 us each (measured per workgroup), so every kernel requests what it can
 // before its first wait.

@@ -185,27 +185,31 @@ def test_mla_decode_small_dims_long_context(orc, S, pb, T):
     _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
 
 
-PREFILL = [(5, 0, None), (9, 7, None), (13, 3, 20), (40, 0, 48), (27, 61, 100)]
+PREFILL = [(5, 0, None), (9, 7, None), (13, 3, 20), (40, 0, 48), (27, 61, 100),
+           (66, 0, None), (70, 3, 80), (130, 10, 150)]
 
 
 @pytest.mark.parametrize("S,pb,T", PREFILL, ids=[f"S{S}-pos{pb}-T{T}" for S, pb, T in PREFILL])
 def test_mla_prefill_small_dims(orc, S, pb, T):
     """More than 4 rows (prefill): the projections on the bf16 prefill
-    kernels, the core in chunks of 4 rows, row s attending keys up to
-    pos_base + s -- including chunks whose keys are the earlier chunks' new
-    cache rows."""
+    kernels, the core in groups of up to 64 rows, row s attending keys up to
+    pos_base + s -- including groups whose keys are the earlier groups' new
+    cache rows, and a last group of 2 rows (the decode kernels)."""
     need_gpu()
     W, layer, x, Lc, Rc, T = _setup(300 + S + pb, S, pb, SMALL, T=T)
     out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
     _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
 
 
-def test_mla_prefill_full_dims(orc):
-    """24 rows at position 37 at the layer's real dimensions."""
+@pytest.mark.parametrize("S,pb", [(24, 37), (68, 5)], ids=["S24-pos37", "S68-pos5"])
+def test_mla_prefill_full_dims(orc, S, pb):
+    """Prefill rows at the layer's real dimensions: one group of 24 rows, and
+    a group of 64 rows followed by one of 4 (the decode kernels) whose latent
+    context joins the value absorption of all rows on the bf16 matrix cores."""
     need_gpu()
-    W, layer, x, Lc, Rc, T = _setup(330, 24, 37, FULL)
-    out, Lc1, Rc1, stage = _run(layer, x, 37, Lc, Rc, T)
-    _check(orc, W, x, 37, Lc, Rc, T, out, Lc1, Rc1, stage)
+    W, layer, x, Lc, Rc, T = _setup(330 + S, S, pb, FULL)
+    out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
+    _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
 
 
 @pytest.mark.parametrize("kmode", [0, 1], ids=["mfma", "valu"])
