@@ -12,6 +12,11 @@ size_t dgemm_ws_bytes(const coli_qtensor *W, int S);
 // taken (layout, alignment, workspace), <0 error
 int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws, size_t ws_bytes,
                  hipStream_t st);
+// y1 = W1 x and y2 = W2 x (single matrices of the same input count, both
+// grouped int4 or both per-row int4) in one launch after one input
+// preparation; workspace dgemm_ws_bytes(W1, S).  1 done, 0 not taken, <0 error
+int launch_dgemm_pair(const coli_qtensor *W1, const coli_qtensor *W2, const float *x, float *y1,
+                      float *y2, int S, void *ws, size_t ws_bytes, hipStream_t st);
 
 // nb products on row ranges of one packed matrix W (a single matrix): batch
 // b computes y_b[m][n] = sum_k W[row0 + b row_step + n][k] x_b[m][k] for S

@@ -65,6 +65,12 @@ struct DgArgs {
     int xf_bstride, rt0, rt_bstride, Otot;
     int64_t y_bstride;
 };
+// one or two matrices per launch: grid z picks the matrix (two matrices of
+// the same inputs, each with its own tiles; a workgroup past its matrix's
+// tiles ends at once)
+struct DgPair {
+    DgArgs m[2];
+};
 
 __device__ __forceinline__ uint32_t dg_pk(float lo, float hi) {
     uint32_t r;
@@ -176,7 +182,10 @@ __global__ __launch_bounds__(256) void k_dg_xprep(const float *__restrict__ x, i
 }
 
 template <int SM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dg(DgArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dg(DgPair pr) {
+    const DgArgs &a = pr.m[blockIdx.z];
+    if ((int)blockIdx.x >= a.nmt * a.nnt)
+        return;
     // ring slot u (one array each, so the compiler sees the slots apart): the
     // four wavefronts' inputs of one block, DG_SLOT bytes each
     __shared__ __attribute__((aligned(16))) uint8_t rs0[4 * DG_SLOT], rs1[4 * DG_SLOT],
@@ -378,46 +387,85 @@ size_t dgemm_ws_bytes(const coli_qtensor *W, int S) {
     return (size_t)(nmt * DG_MB * nkb4 * 4096);
 }
 
-int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws, size_t ws_bytes,
-                 hipStream_t st) {
-    if (!dg_ok(W) || S < 1 || (uintptr_t)x % 16 != 0 || ws == nullptr ||
-        (uintptr_t)ws % 256 != 0 || ws_bytes < dgemm_ws_bytes(W, S) ||
-        dgemm_ws_bytes(W, S) >= ((size_t)1 << 31))
-        return 0;
-    ProfScope ps("gemm_dense", st);
-    const int nkb = (W->I + 127) / 128, nkb4 = (nkb + 3) / 4 * 4;
-    const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (W->O + DG_TN - 1) / DG_TN;
-    // every matrix of a stack takes the same input rows
+// the arguments for matrix e of W's stack: y = W_e x over S rows, inputs
+// prepared in ws
+static DgArgs dg_args(const coli_qtensor *W, int e, int S, const void *ws, float *y) {
+    const int nkb = (W->I + 127) / 128;
+    DgArgs a;
+    memset(&a, 0, sizeof a);
+    a.xf = (const uint8_t *)ws;
+    a.pq = (const uint8_t *)W->pk + (int64_t)e * W->pk_stride;
+    a.ps = W->fmt == 4 ? (const float *)((const uint8_t *)W->pk + (int64_t)e * W->pk_stride + W->pk_scale_off)
+                       : W->s + (int64_t)e * W->s_stride;
+    a.xbytes = (int)dgemm_ws_bytes(W, S);
+    a.qbytes = (int)W->pk_scale_off;
+    a.sbytes = W->fmt == 4 ? (int)(W->pk_stride - W->pk_scale_off) : (int)(W->O * sizeof(float));
+    a.nkb = nkb;
+    a.nkq = (nkb + 3) / 4;
+    a.cbs = (W->fmt != 4 || W->gs % 128 == 0) ? 1 : 128 / W->gs;
+    a.gshift = (W->fmt == 4 && W->gs < 128) ? __builtin_ctz((unsigned)W->gs) : 5;
+    a.rtn = (W->O + 15) / 16;
+    a.Otot = W->O;
+    a.M = S;
+    a.N = W->O;
+    a.nmt = (S + DG_TM - 1) / DG_TM;
+    a.nnt = (W->O + DG_TN - 1) / DG_TN;
+    a.y = y;
+    a.ldy = W->O;
+    return a;
+}
+
+static bool dg_launch_ok(const coli_qtensor *W, const float *x, int S, const void *ws, size_t ws_bytes) {
+    return dg_ok(W) && S >= 1 && (uintptr_t)x % 16 == 0 && ws != nullptr && (uintptr_t)ws % 256 == 0 &&
+           ws_bytes >= dgemm_ws_bytes(W, S) && dgemm_ws_bytes(W, S) < ((size_t)1 << 31);
+}
+
+static void dg_xprep(const coli_qtensor *W, const float *x, int S, void *ws, hipStream_t st) {
+    const int nkb4 = ((W->I + 127) / 128 + 3) / 4 * 4;
+    const int nmt = (S + DG_TM - 1) / DG_TM;
     hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)nkb4), dim3(256), 0, st,
                        x, (int64_t)W->I, S, W->I, nkb4, (uint8_t *)ws, (int64_t)0, (int64_t)0);
+}
+
+int launch_dgemm(const coli_qtensor *W, const float *x, float *y, int S, void *ws, size_t ws_bytes,
+                 hipStream_t st) {
+    if (!dg_launch_ok(W, x, S, ws, ws_bytes))
+        return 0;
+    ProfScope ps("gemm_dense", st);
+    // every matrix of a stack takes the same input rows
+    dg_xprep(W, x, S, ws, st);
     for (int e = 0; e < W->n; ++e) {
-        DgArgs a;
-        memset(&a, 0, sizeof a);
-        a.xf = (const uint8_t *)ws;
-        a.pq = (const uint8_t *)W->pk + (int64_t)e * W->pk_stride;
-        a.ps = W->fmt == 4 ? (const float *)((const uint8_t *)W->pk + (int64_t)e * W->pk_stride + W->pk_scale_off)
-                           : W->s + (int64_t)e * W->s_stride;
-        a.xbytes = (int)dgemm_ws_bytes(W, S);
-        a.qbytes = (int)W->pk_scale_off;
-        a.sbytes = W->fmt == 4 ? (int)(W->pk_stride - W->pk_scale_off) : (int)(W->O * sizeof(float));
-        a.nkb = nkb;
-        a.nkq = (nkb + 3) / 4;
-        a.cbs = (W->fmt != 4 || W->gs % 128 == 0) ? 1 : 128 / W->gs;
-        a.gshift = (W->fmt == 4 && W->gs < 128) ? __builtin_ctz((unsigned)W->gs) : 5;
-        a.rtn = (W->O + 15) / 16;
-        a.Otot = W->O;
-        a.M = S;
-        a.N = W->O;
-        a.nmt = nmt;
-        a.nnt = nnt;
-        a.y = y + (int64_t)e * S * W->O;
-        a.ldy = W->O;
-        const dim3 grid((unsigned)(nmt * nnt));
+        DgPair pr;
+        pr.m[0] = dg_args(W, e, S, ws, y + (int64_t)e * S * W->O);
+        pr.m[1] = pr.m[0];
+        const dim3 grid((unsigned)(pr.m[0].nmt * pr.m[0].nnt));
         if (W->fmt == 4)
-            hipLaunchKernelGGL(k_dg<DG_GRP>, grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_dg<DG_GRP>, grid, dim3(256), 0, st, pr);
         else
-            hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, pr);
     }
+    return after_launch("gemm_dense") == COLI_OK ? 1 : -1;
+}
+
+int launch_dgemm_pair(const coli_qtensor *W1, const coli_qtensor *W2, const float *x, float *y1,
+                      float *y2, int S, void *ws, size_t ws_bytes, hipStream_t st) {
+    if (!dg_launch_ok(W1, x, S, ws, ws_bytes) || !dg_launch_ok(W2, x, S, ws, ws_bytes) ||
+        W1->n != 1 || W2->n != 1 || W1->I != W2->I || (W1->fmt == 4) != (W2->fmt == 4))
+        return 0;
+    ProfScope ps("gemm_dense", st);
+    dg_xprep(W1, x, S, ws, st);
+    DgPair pr;
+    pr.m[0] = dg_args(W1, 0, S, ws, y1);
+    pr.m[1] = dg_args(W2, 0, S, ws, y2);
+    // the larger tile count rounded to whole XCD rounds, so that workgroup
+    // w of either matrix runs on XCD w % 8
+    const int t1 = pr.m[0].nmt * pr.m[0].nnt, t2 = pr.m[1].nmt * pr.m[1].nnt;
+    const int gx = ((t1 > t2 ? t1 : t2) + 7) / 8 * 8;
+    const dim3 grid((unsigned)gx, 1u, 2u);
+    if (W1->fmt == 4)
+        hipLaunchKernelGGL(k_dg<DG_GRP>, grid, dim3(256), 0, st, pr);
+    else
+        hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, pr);
     return after_launch("gemm_dense") == COLI_OK ? 1 : -1;
 }
 
@@ -474,10 +522,13 @@ int launch_dgemm_heads(const coli_qtensor *W, int row0, int row_step, int N, int
     a.rt_bstride = row_step / 16;
     a.y_bstride = y_bstride;
     const dim3 grid((unsigned)(nmt * nnt), (unsigned)nb);
+    DgPair pr;
+    pr.m[0] = a;
+    pr.m[1] = a;
     if (W->fmt == 4)
-        hipLaunchKernelGGL(k_dg<DG_GRP>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_dg<DG_GRP>, grid, dim3(256), 0, st, pr);
     else
-        hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_dg<DG_ROW>, grid, dim3(256), 0, st, pr);
     return after_launch("gemm_heads") == COLI_OK ? 1 : -1;
 }
 

@@ -1286,6 +1286,19 @@ static int proj_rows(const coli_qtensor *W, const float *x, float *y, int S, hip
     return launch_gemm(W, x, y, S, nullptr, 0, st);
 }
 
+// q_a and kv_a of S > MLA_CHUNK rows (same inputs): one launch of the
+// split-K kernel for both when it takes them, else one projection each
+static int proj_rows_pair(const coli_qtensor *W1, const coli_qtensor *W2, const float *x, float *y1,
+                          float *y2, int S, hipStream_t st, char *ws, const MlaLayout &l) {
+    if (l.xprep_bytes > 0) {
+        const int r = launch_dgemm_pair(W1, W2, x, y1, y2, S, ws + l.xprep, l.xprep_bytes, st);
+        if (r != 0)
+            return r > 0 ? COLI_OK : COLI_HIP_ERROR;
+    }
+    const int rc = proj_rows(W1, x, y1, S, st, ws, l);
+    return rc != COLI_OK ? rc : proj_rows(W2, x, y2, S, st, ws, l);
+}
+
 int launch_mla_decode(const MlaArgs &a) {
     const coli_mla_layer &m = *a.layer;
     const int S = a.S;
@@ -1310,9 +1323,7 @@ int launch_mla_decode(const MlaArgs &a) {
             if (rc != COLI_OK) return rc;
             xin = a.xn;
         }
-        rc = proj_rows(m.q_a, xin, cq_raw, S, st, ws, l);
-        if (rc != COLI_OK) return rc;
-        rc = proj_rows(m.kv_a, xin, ckv, S, st, ws, l);
+        rc = proj_rows_pair(m.q_a, m.kv_a, xin, cq_raw, ckv, S, st, ws, l);
         if (rc != COLI_OK) return rc;
         {
             ProfScope ps("mla_qnorm", st);
