@@ -45,10 +45,11 @@
 //                     shares added in order) is formed in LDS
 // Prefill groups (more than 4 rows, up to MLA_GROUP per launch set) run the
 // core on the fp32 matrix cores (v_mfma_f32_16x16x4f32, 64-row tiles):
-//   k_mla_qabs_mx     the group's rows x 64 latent columns of one head per
+//   k_mla_qabs_mx     once for the rows of all prefill groups, ahead of them:
+//                     a 64-row tile x 64 latent columns of one head per
 //                     workgroup, kv_b's key rows decoded into LDS; more
-//                     workgroups of the same launch do the key side and the
-//                     query rotation
+//                     workgroups of the same launch do the key side (every
+//                     row's cache rows) and the query rotation
 //   k_mla_scores_mx   the group's queries resident in LDS, 64-key tiles
 //                     streamed; four workgroups per (head, component split)
 //   k_mla_softmax_rows each row's statistics from its scores kept in
@@ -235,10 +236,11 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
         }
 }
 
-// Prefill rows (a group of up to 64): the key absorption on the fp32 matrix
-// cores, with the key side and the query rotation as other workgroups of the
-// same launch.  Workgroups [0, H * ncol): qabs[s][h][c] = sum_j q[s][h][j]
-// W_UK[h][j][c] for the group's rows x 64 latent columns of head h, over the
+// Prefill rows (all rows of the prefill groups, before the first group's
+// scores): the key absorption on the fp32 matrix cores, with the key side and
+// the query rotation as other workgroups of the same launch.  Workgroups
+// [0, nrt * H * ncol): qabs[s][h][c] = sum_j q[s][h][j] W_UK[h][j][c] for one
+// 64-row tile x 64 latent columns of head h, over the
 // d_nope key rows in chunks of 64 (query values and kv_b's key rows, the
 // latter decoded to s * (q - 8) exactly as the vector kernel forms them and
 // stored column-major, through LDS; the next chunk requested while the
@@ -250,7 +252,6 @@ __global__ __launch_bounds__(QA_NW * 64) void k_mla_qabs(MlaKvb kb, int H, int d
 // S: the rotation of row s's query rotary parts into qpe.
 constexpr int QX_T = 64;             // rows, key rows and columns per tile
 constexpr int QX_LD = QX_T + 4;      // LDS row stride
-static_assert(MLA_GROUP <= QX_T, "a prefill group's rows fit one tile");
 template <bool GRP>
 __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, int dn, int dr,
                                                      int dv, int L, const float *__restrict__ q,
@@ -266,10 +267,11 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
     __shared__ double npart[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ncol = (L + QX_T - 1) / QX_T;
+    const int nrt = (S + QX_T - 1) / QX_T;
     const int nq = H * (dn + dr);
     int bx = blockIdx.x;
-    if (bx >= H * ncol) {
-        bx -= H * ncol;
+    if (bx >= nrt * H * ncol) {
+        bx -= nrt * H * ncol;
         if (bx < S) {  // key side of row bx
             const int pos = pos_base + bx;
             const float *xr = ckv + (int64_t)bx * (L + dr);
@@ -288,6 +290,12 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
         }
         return;
     }
+    // this workgroup's row tile: rows r0 .. r0 + Sl - 1 of the call
+    const int r0 = (bx / (H * ncol)) * QX_T;
+    bx %= H * ncol;
+    const int Sl = min(QX_T, S - r0);
+    q += (int64_t)r0 * nq;
+    qabs += (int64_t)r0 * H * L;
     const int h = bx / ncol, c0 = (bx % ncol) * QX_T;
     const int rr = tid >> 4, j4 = 4 * (tid & 15);  // query staging: rows rr + 16 i, key rows j4 .. + 3
     const int wr = tid >> 2, w8 = 16 * (tid & 3);  // weight staging: key row wr, columns w8 .. + 15
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
         for (int i = 0; i < 4; ++i) {
             const int r = rr + 16 * i, j = j0 + j4;
             float e[4] = {0.f, 0.f, 0.f, 0.f};
-            if (r < S) {
+            if (r < Sl) {
                 const float *qr = q + (int64_t)r * nq + (int64_t)h * (dn + dr);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) e[k] = j + k < dn ? qr[j + k] : 0.f;
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * wave + 4 * (lane >> 4) + i, c = c0 + 16 * nb + (lane & 15);
-            if (r < S && c < L)
+            if (r < Sl && c < L)
                 qabs[((int64_t)r * H + h) * L + c] = acc[nb][i];
         }
 }
@@ -1117,6 +1125,18 @@ static void ctx_launch(bool grp, unsigned nz, int rbase, int nrows, const MlaKvb
                            pos_base, cl_part, clat, ctx, nrows, rbase);
 }
 
+// kv_b as the absorption kernels read it
+static MlaKvb mla_kvb(const coli_mla_layer &m) {
+    const bool grp = m.kv_b->fmt == COLI_FMT_I4_GRP;
+    MlaKvb kb;
+    kb.q = (const uint8_t *)m.kv_b->q;
+    kb.s = m.kv_b->s;
+    kb.rb = m.kv_b->row_bytes;
+    kb.ng = m.kv_b->ng;
+    kb.gs = grp ? m.kv_b->gs : 1;
+    return kb;
+}
+
 // The core for a group of G rows r0 .. r0 + G - 1 (G <= MLA_GROUP) at
 // positions pos_base + r0 ..: stage pointers start at row r0, the partial
 // sums are the group's own.  The key and value absorptions run MLA_CHUNK rows
@@ -1128,12 +1148,7 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v;
     const int L = m.kv_b->I;
     const bool grp = m.kv_b->fmt == COLI_FMT_I4_GRP;
-    MlaKvb kb;
-    kb.q = (const uint8_t *)m.kv_b->q;
-    kb.s = m.kv_b->s;
-    kb.rb = m.kv_b->row_bytes;
-    kb.ng = m.kv_b->ng;
-    kb.gs = grp ? m.kv_b->gs : 1;
+    const MlaKvb kb = mla_kvb(m);
     const int64_t R = r0;
     const int pos_base = a.pos_base + r0;
     const float *q = (const float *)(ws + l.off[MLA_Q]) + R * H * (dn + dr);
@@ -1151,20 +1166,9 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     const double eps = (double)m.eps;
     const unsigned nfull = (unsigned)(G / MLA_CHUNK);
     const int rem = G % MLA_CHUNK, rrem = (int)nfull * MLA_CHUNK;
-    {
+    if (G <= MLA_CHUNK) {  // (a prefill group's qabs, key side and qpe are formed before the groups)
         ProfScope ps("mla_qabs", st);
-        if (G > MLA_CHUNK) {
-            // prefill group: qabs on the matrix cores, key side and query rotation beside it
-            const unsigned nblk = (unsigned)(H * ((L + QX_T - 1) / QX_T) + 2 * G);
-            if (grp)
-                hipLaunchKernelGGL(k_mla_qabs_mx<true>, dim3(nblk), dim3(256), 0, st, kb, G, H, dn, dr,
-                                   dv, L, q, pos_base, theta, qabs, qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc);
-            else
-                hipLaunchKernelGGL(k_mla_qabs_mx<false>, dim3(nblk), dim3(256), 0, st, kb, G, H, dn, dr,
-                                   dv, L, q, pos_base, theta, qabs, qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc);
-            const int rc = after_launch("mla_qabs");
-            if (rc != COLI_OK) return rc;
-        } else {
+        {
             if (nfull > 0)
                 qabs_launch<MLA_CHUNK>(grp, nfull, 0, G, kb, H, dn, dr, dv, L, q, pos_base, theta, part,
                                        qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc, st);
@@ -1258,6 +1262,31 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
 static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st) {
     const coli_mla_layer &m = *a.layer;
     const bool ctx_later = mla_ctx_on_gemm(m, a.S) && l.xprep_bytes > 0;
+    // the rows of the groups of more than MLA_CHUNK rows (all but a last
+    // group of at most MLA_CHUNK, which takes the decode kernels): their
+    // qabs, key side (cache rows) and qpe in one launch ahead of the groups,
+    // since none of it depends on another row's scores
+    const int last = a.S % MLA_GROUP;
+    const int big = a.S <= MLA_CHUNK ? 0 : (last != 0 && last <= MLA_CHUNK ? a.S - last : a.S);
+    if (big > 0) {
+        ProfScope ps("mla_qabs", st);
+        const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v, L = m.kv_b->I;
+        const MlaKvb kb = mla_kvb(m);
+        const float *q = (const float *)(ws + l.off[MLA_Q]);
+        float *qabs = (float *)(ws + l.off[MLA_QABS]);
+        float *qpe = (float *)(ws + l.off[MLA_QPE]);
+        const float *ckv = (const float *)(ws + l.off[MLA_CKV_RAW]);
+        const double theta = (double)m.rope_theta, eps = (double)m.eps;
+        const unsigned nblk = (unsigned)(((big + QX_T - 1) / QX_T) * H * ((L + QX_T - 1) / QX_T) + 2 * big);
+        if (m.kv_b->fmt == COLI_FMT_I4_GRP)
+            hipLaunchKernelGGL(k_mla_qabs_mx<true>, dim3(nblk), dim3(256), 0, st, kb, big, H, dn, dr, dv,
+                               L, q, a.pos_base, theta, qabs, qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc);
+        else
+            hipLaunchKernelGGL(k_mla_qabs_mx<false>, dim3(nblk), dim3(256), 0, st, kb, big, H, dn, dr, dv,
+                               L, q, a.pos_base, theta, qabs, qpe, ckv, m.kv_norm, eps, a.Lc, a.Rc);
+        const int rc = after_launch("mla_qabs");
+        if (rc != COLI_OK) return rc;
+    }
     for (int r0 = 0; r0 < a.S; r0 += MLA_GROUP) {
         const int G = a.S - r0 < MLA_GROUP ? a.S - r0 : MLA_GROUP;
         const int rc = launch_core(a, l, ws, st, r0, G, ctx_later);
