@@ -176,9 +176,9 @@ __global__ __launch_bounds__(256) void k_dg_xprep(const float *__restrict__ x, i
         a = gload<f32x4>(p);
         b = gload<f32x4>(p + 4);
     }
-    const int j4 = c8 >> 2, s = c8 & 3;
-    const u32x4 o = {dg_pk(a.x, a.y), dg_pk(a.z, a.w), dg_pk(b.x, b.y), dg_pk(b.z, b.w)};
-    *reinterpret_cast<u32x4 *>(xf + ((int64_t)mb * nkb4 + kb) * 4096 + s * 1024 + (16 * j4 + r) * 16) = o;
+    const u32x4 o = {dgemm_bf16x2(a.x, a.y), dgemm_bf16x2(a.z, a.w), dgemm_bf16x2(b.x, b.y),
+                     dgemm_bf16x2(b.z, b.w)};
+    *reinterpret_cast<u32x4 *>(xf + dgemm_frag_offset(row, k, nkb4)) = o;
 }
 
 template <int SM>
@@ -486,17 +486,18 @@ bool dgemm_heads_takes(const coli_qtensor *W, int row0, int row_step, int N, int
 
 int launch_dgemm_heads(const coli_qtensor *W, int row0, int row_step, int N, int nb, const float *x,
                        int64_t ldx, int64_t x_bstride, float *y, int64_t ldy, int64_t y_bstride, int S,
-                       void *ws, size_t ws_bytes, hipStream_t st) {
+                       void *ws, size_t ws_bytes, hipStream_t st, bool prepared) {
     const size_t per = dgemm_ws_bytes(W, S);
     if (!dgemm_heads_takes(W, row0, row_step, N, nb, S) || ws == nullptr ||
-        (uintptr_t)ws % 256 != 0 || ws_bytes < per * nb || (uintptr_t)x % 16 != 0 || ldx % 4 != 0 ||
-        x_bstride % 4 != 0)
+        (uintptr_t)ws % 256 != 0 || ws_bytes < per * nb ||
+        (!prepared && ((uintptr_t)x % 16 != 0 || ldx % 4 != 0 || x_bstride % 4 != 0)))
         return 0;
     ProfScope ps("gemm_heads", st);
     const int nkb = (W->I + 127) / 128, nkb4 = (nkb + 3) / 4 * 4;
     const int nmt = (S + DG_TM - 1) / DG_TM, nnt = (N + DG_TN - 1) / DG_TN;
-    hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)nkb4, (unsigned)nb),
-                       dim3(256), 0, st, x, ldx, S, W->I, nkb4, (uint8_t *)ws, x_bstride, (int64_t)per);
+    if (!prepared)
+        hipLaunchKernelGGL(k_dg_xprep, dim3((unsigned)(nmt * DG_MB), (unsigned)nkb4, (unsigned)nb),
+                           dim3(256), 0, st, x, ldx, S, W->I, nkb4, (uint8_t *)ws, x_bstride, (int64_t)per);
     DgArgs a;
     memset(&a, 0, sizeof a);
     a.xf = (const uint8_t *)ws;

@@ -56,8 +56,9 @@
 //                     registers; writes every key's score and probability
 //   k_mla_clat_mx     per 64-key chunk and head: probabilities times the
 //                     chunk's latent rows, column tiles through LDS
-//   k_mla_clat_sum    adds the chunks' partials when the value absorption of
-//                     all rows follows on the bf16 GEMM
+//   k_mla_clat_sum_frag adds the chunks' partials when the value absorption
+//                     of all rows follows on the bf16 GEMM, writing clat also
+//                     as that GEMM's prepared inputs
 // At decode sizes each of these is a few dependent memory round trips of
 // ~2 us each (measured per workgroup), so every kernel requests what it can
 // before its first wait.
@@ -897,20 +898,38 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p
 }
 
 // Prefill rows whose value absorption runs on the matrix cores afterwards:
-// clat[s][h][c] = the key chunks' partials of row s added in chunk order
-// (what k_mla_ctx stages); one thread per value.
-__global__ __launch_bounds__(256) void k_mla_clat_sum(const float *__restrict__ cl_part, int S,
-                                                      int H, int L, int pos_base,
-                                                      float *__restrict__ clat) {
-    const int64_t n = (int64_t)S * H * L;
+// clat[s][h][c] = the key chunks' partials of row s (one per kpp keys) added
+// in chunk order, written as f32 and as the split-K GEMM's prepared bf16
+// inputs (batch h of the value absorption at xf + h per: row r0 + s, input
+// c; the inputs from L up to nkb4 blocks zero); one thread per 8 values.
+__global__ __launch_bounds__(256) void k_mla_clat_sum_frag(const float *__restrict__ cl_part, int S,
+                                                           int H, int L, int pos_base, int kpp,
+                                                           float *__restrict__ clat, int r0,
+                                                           uint8_t *__restrict__ xf, int64_t per,
+                                                           int nkb4) {
+    const int L8 = nkb4 * 128 / 8;  // 8-input groups per row, padding included
+    const int64_t n8 = (int64_t)S * H * L8;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n)
+    if (i >= n8)
         return;
-    const int s = (int)(i / ((int64_t)H * L));
-    const int nchunk = (pos_base + s + 1 + CL_KEYS - 1) / CL_KEYS;
-    float v = cl_part[i];
-    for (int k = 1; k < nchunk; ++k) v += cl_part[i + (int64_t)k * n];
-    clat[i] = v;
+    const int s = (int)(i / ((int64_t)H * L8));
+    const int h = (int)((i / L8) % H), c = 8 * (int)(i % L8);
+    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+    if (c < L) {
+        const int64_t n = (int64_t)S * H * L, o = ((int64_t)s * H + h) * L + c;
+        const int nchunk = (pos_base + s + 1 + kpp - 1) / kpp;
+        v0 = gload<f32x4>(cl_part + o);
+        v1 = gload<f32x4>(cl_part + o + 4);
+        for (int k = 1; k < nchunk; ++k) {
+            v0 += gload<f32x4>(cl_part + o + (int64_t)k * n);
+            v1 += gload<f32x4>(cl_part + o + (int64_t)k * n + 4);
+        }
+        *reinterpret_cast<f32x4 *>(clat + o) = v0;
+        *reinterpret_cast<f32x4 *>(clat + o + 4) = v1;
+    }
+    const u32x4 b = {dgemm_bf16x2(v0.x, v0.y), dgemm_bf16x2(v0.z, v0.w), dgemm_bf16x2(v1.x, v1.y),
+                     dgemm_bf16x2(v1.z, v1.w)};
+    *reinterpret_cast<u32x4 *>(xf + (int64_t)h * per + dgemm_frag_offset(r0 + s, c, nkb4)) = b;
 }
 
 // ---- value absorption --------------------------------------------------------
@@ -1233,10 +1252,13 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     }
     {
         ProfScope ps("mla_ctx", st);
-        if (ctx_later) {  // the group's clat only; the value absorption follows for all rows
-            const int64_t n = (int64_t)G * H * L;
-            hipLaunchKernelGGL(k_mla_clat_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                               (const float *)cl_part, G, H, L, pos_base, clat);
+        if (ctx_later) {  // the group's clat only, written also as the value absorption's
+                          // prepared inputs; that GEMM follows for all rows
+            const int nkb4 = dgemm_nkb4(m.kv_b);
+            const int64_t n8 = (int64_t)G * H * (nkb4 * 128 / 8);
+            hipLaunchKernelGGL(k_mla_clat_sum_frag, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                               (const float *)cl_part, G, H, L, pos_base, CL_KEYS, clat, r0,
+                               (uint8_t *)(ws + l.xprep), (int64_t)dgemm_ws_bytes(m.kv_b, a.S), nkb4);
             return after_launch("mla_ctx");
         }
         if (nfull > 0)
@@ -1299,7 +1321,8 @@ static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipS
     const int H = m.H, dn = m.d_nope, dv = m.d_v, L = m.kv_b->I;
     const int r = launch_dgemm_heads(m.kv_b, dn, dn + dv, dv, H, (const float *)(ws + l.off[MLA_CLAT]),
                                      (int64_t)H * L, L, (float *)(ws + l.off[MLA_CTX]),
-                                     (int64_t)H * dv, dv, a.S, ws + l.xprep, l.xprep_bytes, st);
+                                     (int64_t)H * dv, dv, a.S, ws + l.xprep, l.xprep_bytes, st,
+                                     true);  // inputs prepared by the groups' clat sums
     return r > 0 ? COLI_OK : COLI_HIP_ERROR;  // (shapes checked by mla_ctx_on_gemm)
 }
 
