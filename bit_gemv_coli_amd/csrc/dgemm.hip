@@ -8,9 +8,11 @@
 //   k_dg_xprep  the input rows once to bf16, in the order the matrix cores
 //               read them (fragments of 16 rows x 8 inputs, 1 KiB per
 //               wavefront request), rows padded to whole tiles with zeros;
-//   k_dg        one workgroup per 144 x 96 output tile: each wavefront takes
-//               one quarter (a 32-input slice) of every 128-input block and
-//               accumulates the whole tile for it, so every weight is turned
+//   k_dg        one workgroup per 144 x 96 output tile (of one matrix, or
+//               of two with the same inputs, the grid's z choosing the
+//               matrix): each wavefront takes one quarter (a 32-input
+//               slice) of every 128-input block and accumulates the whole
+//               tile for it, so every weight is turned
 //               into bf16 once per 144 input rows and no operand passes
 //               between wavefronts; the four partial tiles are added in a
 //               fixed order at the end.
@@ -72,11 +74,6 @@ struct DgPair {
     DgArgs m[2];
 };
 
-__device__ __forceinline__ uint32_t dg_pk(float lo, float hi) {
-    uint32_t r;
-    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-    return r;
-}
 
 // acc += A B on the matrix cores, accumulating in place in acc's registers
 // (the builtin lets the register allocator move the 216 accumulators between
@@ -295,8 +292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float s16 = s16of(bc, 0, 0);
         const uint32_t w = bc.c[0][0];
         const uint32_t ev = (w << 4) & 0xF0F0F0F0u, od = w & 0xF0F0F0F0u;
-        bw = u32x4{dg_pk(sbyte<0>(ev) * s16, sbyte<0>(od) * s16), dg_pk(sbyte<1>(ev) * s16, sbyte<1>(od) * s16),
-                   dg_pk(sbyte<2>(ev) * s16, sbyte<2>(od) * s16), dg_pk(sbyte<3>(ev) * s16, sbyte<3>(od) * s16)};
+        bw = u32x4{dgemm_bf16x2(sbyte<0>(ev) * s16, sbyte<0>(od) * s16), dgemm_bf16x2(sbyte<1>(ev) * s16, sbyte<1>(od) * s16),
+                   dgemm_bf16x2(sbyte<2>(ev) * s16, sbyte<2>(od) * s16), dgemm_bf16x2(sbyte<3>(ev) * s16, sbyte<3>(od) * s16)};
     }
     for (int T = 0; 4 * T < nkb4; ++T) {
         bload(bn, T + 1);
