@@ -23,7 +23,7 @@ constexpr int MLA_SC_SPLIT = 3;
 // of the core (more rows: several sets in order; a multiple of MLA_CHUNK)
 constexpr int MLA_CHUNK = 4;
 #ifndef COLI_MLA_GROUP
-#define COLI_MLA_GROUP 64
+#define COLI_MLA_GROUP 192
 #endif
 constexpr int MLA_GROUP = COLI_MLA_GROUP;
 static_assert(MLA_GROUP % MLA_CHUNK == 0, "whole chunks per group");

@@ -483,8 +483,8 @@ __global__ __launch_bounds__(256) void k_mla_scores(const float *__restrict__ pa
 }
 
 // Prefill rows on the fp32 matrix cores: partial scores over one third of
-// the L + d_rope components for one head and the group's rows (up to 64);
-// grid (SX_KW key-tile lanes, heads, MLA_SC_SPLIT): workgroup x takes the
+// the L + d_rope components for one head and a 64-row tile of the group;
+// grid (SX_KW key-tile lanes, heads, row tiles x MLA_SC_SPLIT): workgroup x takes the
 // 64-key tiles x, x + SX_KW, ...  The query tile of the split (qabs, then
 // qpe) is staged once into LDS and stays there while the key tiles stream
 // through, component chunk by chunk (64
@@ -507,7 +507,6 @@ constexpr int SX_T = 64;    // rows = keys per tile
 constexpr int SX_KW = COLI_MLA_SX_KW;
 constexpr int SX_QCH = 3;   // query chunks kept in LDS
 constexpr int SX_LD = SC_CH + 4;  // LDS row stride (16-byte rows for the 4-component reads)
-static_assert(MLA_GROUP <= SX_T, "a prefill group's rows fit one tile");
 __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__ qabs,
                                                        const float *__restrict__ qpe,
                                                        const float *__restrict__ Lc,
@@ -516,9 +515,11 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
                                                        int lvec, float *__restrict__ sc_part) {
     __shared__ __attribute__((aligned(16))) float qs[SX_QCH][SX_T][SX_LD];
     __shared__ __attribute__((aligned(16))) float ks[SX_T][SX_LD];
-    const int h = blockIdx.y, split = blockIdx.z;
+    // grid z: (row tile, split); this workgroup's rows r0 .. r0 + Sl - 1
+    const int h = blockIdx.y, split = (int)blockIdx.z % MLA_SC_SPLIT;
+    const int r0 = ((int)blockIdx.z / MLA_SC_SPLIT) * SX_T, Sl = min(SX_T, S - r0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int last_max = pos_base + S - 1;  // keys 0 .. last of the last row
+    const int last_max = pos_base + r0 + Sl - 1;  // keys 0 .. last of the tile's last row
     const int nkt = last_max / SX_T + 1;
     const int C = L + dr;
     const int nch_all = (C + SC_CH - 1) / SC_CH;
@@ -534,16 +535,16 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
         for (int i = 0; i < 4; ++i) {
             const int r = rr + 16 * i;
             f32x4 q = {0.f, 0.f, 0.f, 0.f};
-            if (r < S) {
+            if (r < Sl) {
                 if (c + 4 <= L) {
-                    q = gload<f32x4>(qabs + ((int64_t)r * H + h) * L + c);
+                    q = gload<f32x4>(qabs + ((int64_t)(r0 + r) * H + h) * L + c);
                 } else {
                     float e[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int ck = c + k;
-                        e[k] = ck < L ? qabs[((int64_t)r * H + h) * L + ck]
-                                      : (ck < C ? qpe[((int64_t)r * H + h) * dr + (ck - L)] : 0.f);
+                        e[k] = ck < L ? qabs[((int64_t)(r0 + r) * H + h) * L + ck]
+                                      : (ck < C ? qpe[((int64_t)(r0 + r) * H + h) * dr + (ck - L)] : 0.f);
                     }
                     q = f32x4{e[0], e[1], e[2], e[3]};
                 }
@@ -624,8 +625,8 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * wave + 4 * (lane >> 4) + i, t = t0 + 16 * nb + (lane & 15);
-                if (r < S && t <= pos_base + r)
-                    sc_part[(((int64_t)split * S + r) * H + h) * Tcap + t] = acc[nb][i];
+                if (r < Sl && t <= pos_base + r0 + r)
+                    sc_part[(((int64_t)split * S + r0 + r) * H + h) * Tcap + t] = acc[nb][i];
             }
     }
 }
@@ -785,8 +786,8 @@ __global__ __launch_bounds__(256) void k_mla_softmax_rows(const float *__restric
 }
 
 // Prefill rows on the fp32 matrix cores: one 64-key chunk's share of clat
-// for one head and the group's rows (up to 64); grid (64-key chunks, CX_CW
-// column groups, heads), each workgroup taking every CX_CW-th 64-column
+// for one head and a 64-row tile of the group; grid (64-key chunks, CX_CW
+// column groups, row tiles x heads), each workgroup taking every CX_CW-th 64-column
 // tile; the partials k_mla_softmax_clat writes for decode rows
 // (cl_part[chunk][s][h][c] for the chunks that hold keys of row s).  The
 // chunk's probabilities (written by k_mla_softmax_rows) are staged once into
@@ -802,7 +803,6 @@ constexpr int CX_LD = CX_T + 4;        // LDS row stride
 #define COLI_MLA_CX_CW 4
 #endif
 constexpr int CX_CW = COLI_MLA_CX_CW;  // workgroups per (chunk, head), along the column tiles
-static_assert(MLA_GROUP <= CX_T, "a prefill group's rows fit one tile");
 static_assert(CX_T == CL_KEYS, "the partials are per key chunk of CL_KEYS");
 __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p,
                                                      const float *__restrict__ Lc, int S, int H,
@@ -810,9 +810,11 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p
                                                      float *__restrict__ cl_part) {
     __shared__ __attribute__((aligned(16))) float ps[CX_T][CX_LD];  // [row][key]
     __shared__ __attribute__((aligned(16))) float lt[CX_T][CX_LD];  // [column][key]
-    const int chunk = blockIdx.x, t0 = chunk * CX_T, h = blockIdx.z;
+    // grid z: (row tile, head); this workgroup's rows r0 .. r0 + Sl - 1
+    const int chunk = blockIdx.x, t0 = chunk * CX_T, h = (int)blockIdx.z % H;
+    const int r0 = ((int)blockIdx.z / H) * CX_T, Sl = min(CX_T, S - r0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_max = pos_base + S;  // keys of the group's last row
+    const int n_max = pos_base + r0 + Sl;  // keys of the tile's last row
     if (t0 >= n_max)
         return;
     const int rr = tid >> 4, c4 = 4 * (tid & 15);
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p
     float pz[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t prow = ((int64_t)min(rr + 16 * i, S - 1) * H + h) * Tcap;
+        const int64_t prow = ((int64_t)(r0 + min(rr + 16 * i, Sl - 1)) * H + h) * Tcap;
 #pragma unroll
         for (int k = 0; k < 4; ++k) pz[i][k] = p[prow + min(t0 + c4 + k, Tcap - 1)];
     }
@@ -853,7 +855,7 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p
         const int r = rr + 16 * i;
         float pv[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pv[k] = (r < S && t0 + c4 + k < pos_base + r + 1) ? pz[i][k] : 0.f;
+        for (int k = 0; k < 4; ++k) pv[k] = (r < Sl && t0 + c4 + k < pos_base + r0 + r + 1) ? pz[i][k] : 0.f;
         *reinterpret_cast<f32x4 *>(&ps[r][c4]) = f32x4{pv[0], pv[1], pv[2], pv[3]};
     }
     const int am = 16 * wave + (lane & 15), bn = lane & 15, g4 = 4 * (lane >> 4);
@@ -891,8 +893,8 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * wave + 4 * (lane >> 4) + i, c = c0 + 16 * nb + (lane & 15);
-                if (r < S && c < L && t0 < pos_base + r + 1)
-                    cl_part[(((int64_t)chunk * S + r) * H + h) * L + c] = acc[nb][i];
+                if (r < Sl && c < L && t0 < pos_base + r0 + r + 1)
+                    cl_part[(((int64_t)chunk * S + r0 + r) * H + h) * L + c] = acc[nb][i];
             }
     }
 }
@@ -1212,7 +1214,8 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
         if (G > MLA_CHUNK) {
             const int lvec = (uintptr_t)a.Lc % 16 == 0;
             const int nkt = (nkeys + SX_T - 1) / SX_T;
-            const dim3 gridx((unsigned)(nkt < SX_KW ? nkt : SX_KW), (unsigned)H, (unsigned)MLA_SC_SPLIT);
+            const dim3 gridx((unsigned)(nkt < SX_KW ? nkt : SX_KW), (unsigned)H,
+                             (unsigned)(MLA_SC_SPLIT * ((G + SX_T - 1) / SX_T)));
             hipLaunchKernelGGL(k_mla_scores_mx, gridx, dim3(256), 0, st, (const float *)qabs,
                                (const float *)qpe, (const float *)a.Lc, (const float *)a.Rc, G, H,
                                L, dr, pos_base, a.T_cap, lvec, sc_part);
@@ -1239,7 +1242,7 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
             const int lvec = (uintptr_t)a.Lc % 16 == 0;
             const int nct = (L + CX_T - 1) / CX_T;
             const dim3 gridx((unsigned)((nkeys + CX_T - 1) / CX_T), (unsigned)(nct < CX_CW ? nct : CX_CW),
-                             (unsigned)H);
+                             (unsigned)(H * ((G + CX_T - 1) / CX_T)));
             hipLaunchKernelGGL(k_mla_clat_mx, gridx, dim3(256), 0, st, (const float *)p,
                                (const float *)a.Lc, G, H, L, pos_base, a.T_cap, lvec, cl_part);
         } else {
@@ -1279,17 +1282,21 @@ static int launch_core(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream
     return COLI_OK;
 }
 
-// the core over all S rows, MLA_GROUP rows per launch set (each group's key
+// the core over all S rows, at most MLA_GROUP rows per launch set (each group's key
 // rows are in the caches before the next group's scores read them)
 static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipStream_t st) {
     const coli_mla_layer &m = *a.layer;
     const bool ctx_later = mla_ctx_on_gemm(m, a.S) && l.xprep_bytes > 0;
+    // groups of near-equal size, at most MLA_GROUP rows each, whole chunks
+    // of MLA_CHUNK rows but the last
+    const int ngroups = (a.S + MLA_GROUP - 1) / MLA_GROUP;
+    const int gnom = ((a.S + ngroups - 1) / ngroups + MLA_CHUNK - 1) / MLA_CHUNK * MLA_CHUNK;
     // the rows of the groups of more than MLA_CHUNK rows (all but a last
     // group of at most MLA_CHUNK, which takes the decode kernels): their
     // qabs, key side (cache rows) and qpe in one launch ahead of the groups,
     // since none of it depends on another row's scores
-    const int last = a.S % MLA_GROUP;
-    const int big = a.S <= MLA_CHUNK ? 0 : (last != 0 && last <= MLA_CHUNK ? a.S - last : a.S);
+    const int last = a.S - (a.S - 1) / gnom * gnom;  // rows of the last group
+    const int big = a.S <= MLA_CHUNK ? 0 : (last <= MLA_CHUNK ? a.S - last : a.S);
     if (big > 0) {
         ProfScope ps("mla_qabs", st);
         const int H = m.H, dn = m.d_nope, dr = m.d_rope, dv = m.d_v, L = m.kv_b->I;
@@ -1309,8 +1316,8 @@ static int launch_core_rows(const MlaArgs &a, const MlaLayout &l, char *ws, hipS
         const int rc = after_launch("mla_qabs");
         if (rc != COLI_OK) return rc;
     }
-    for (int r0 = 0; r0 < a.S; r0 += MLA_GROUP) {
-        const int G = a.S - r0 < MLA_GROUP ? a.S - r0 : MLA_GROUP;
+    for (int r0 = 0; r0 < a.S; r0 += gnom) {
+        const int G = a.S - r0 < gnom ? a.S - r0 : gnom;
         const int rc = launch_core(a, l, ws, st, r0, G, ctx_later);
         if (rc != COLI_OK) return rc;
     }

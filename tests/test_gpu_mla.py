@@ -186,26 +186,27 @@ def test_mla_decode_small_dims_long_context(orc, S, pb, T):
 
 
 PREFILL = [(5, 0, None), (9, 7, None), (13, 3, 20), (40, 0, 48), (27, 61, 100),
-           (66, 0, None), (70, 3, 80), (130, 10, 150)]
+           (66, 0, None), (70, 3, 80), (130, 10, 150), (200, 3, 210), (389, 7, 400)]
 
 
 @pytest.mark.parametrize("S,pb,T", PREFILL, ids=[f"S{S}-pos{pb}-T{T}" for S, pb, T in PREFILL])
 def test_mla_prefill_small_dims(orc, S, pb, T):
     """More than 4 rows (prefill): the projections on the bf16 prefill
-    kernels, the core in groups of up to 64 rows, row s attending keys up to
-    pos_base + s -- including groups whose keys are the earlier groups' new
-    cache rows, and a last group of 2 rows (the decode kernels)."""
+    kernels, the core in groups of up to 192 rows (64-row tiles inside a
+    group; 200 and 389 rows make two and three groups), row s attending keys
+    up to pos_base + s -- including groups whose keys are the earlier groups'
+    new cache rows."""
     need_gpu()
     W, layer, x, Lc, Rc, T = _setup(300 + S + pb, S, pb, SMALL, T=T)
     out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
     _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
 
 
-@pytest.mark.parametrize("S,pb", [(24, 37), (68, 5)], ids=["S24-pos37", "S68-pos5"])
+@pytest.mark.parametrize("S,pb", [(24, 37), (68, 5), (200, 5)], ids=["S24-pos37", "S68-pos5", "S200-pos5"])
 def test_mla_prefill_full_dims(orc, S, pb):
-    """Prefill rows at the layer's real dimensions: one group of 24 rows, and
-    a group of 64 rows followed by one of 4 (the decode kernels) whose latent
-    context joins the value absorption of all rows on the bf16 matrix cores."""
+    """Prefill rows at the layer's real dimensions: one group of 24 rows, one
+    of 68 (two 64-row tiles), and two groups of 100 rows whose latent
+    contexts feed one value absorption of all rows on the bf16 matrix cores."""
     need_gpu()
     W, layer, x, Lc, Rc, T = _setup(330 + S, S, pb, FULL)
     out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
