@@ -483,11 +483,12 @@ size_t coli_mla_workspace_layout(const coli_mla_layer *layer, int S, int T_cap,
  *   out f32 [S][D] = o_proj ctx.
  * Requires pos_base >= 0 and pos_base + S <= T_cap.  The projections run
  * coli_qmatmul's kernels with its bounds (S <= 4: the fp32 decode GEMVs;
- * more rows: the bf16 prefill GEMMs); the core is fp32, run on chunks of
- * 4 rows in order (each chunk's cache rows are written before the next
- * chunk's scores read them).  Nothing is
- * allocated and the host never waits (graph-capturable).  x, out, Lc, Rc and
- * the workspace must not overlap.
+ * more rows: the bf16 prefill GEMMs).  The core is fp32; for more than 4
+ * rows it runs on the fp32 matrix cores after every row's cache rows are
+ * written, in groups of at most 192 rows, and with a packed kv_b whose head
+ * blocks are whole 16-row tiles the value absorption runs on the bf16
+ * prefill GEMM (its bound).  Nothing is allocated and the host never waits
+ * (graph-capturable).  x, out, Lc, Rc and the workspace must not overlap.
  *   workspace: coli_mla_workspace_bytes(layer, S, T_cap) bytes, 256-byte
  *   aligned, caller-owned; its stage arrays hold this call's intermediates.
  * Returns COLI_OK, COLI_DECLINED or COLI_HIP_ERROR.
