@@ -32,13 +32,17 @@ FULL = dict(D=6144, qr=1536, L=512, H=64, dn=192, dr=64, dv=256, gs=64)
 SMALL = dict(D=256, qr=64, L=96, H=3, dn=16, dr=8, dv=24, gs=32)
 
 
-def _setup(seed, S, pb, dims, T=None, pack=True, kvb_fmt=4, theta=10000.0):
+def _setup(seed, S, pb, dims, T=None, pack=True, kvb_fmt=4, theta=10000.0, kva=None):
     d = dict(dims)
     T = T or pb + S + 5
     r = sd.rng(seed)
     mats, shapes, qn, kn, Lc, Rc = sd.gen_mla(r, d["D"], d["qr"], d["L"], d["H"], d["dn"], d["dr"],
                                               d["dv"], d["gs"], T, pb)
     Q = {k: QMat(4, o, i, d["gs"], *mats[k]) for k, (o, i) in shapes.items()}
+    if kva is not None:  # kv_a drawn again (its own stream) as (fmt, gs)
+        fmt, gs = kva
+        q, s_ = sd.gen_matrix(sd.rng(seed + 7919), fmt, *shapes["kv_a"], gs)
+        Q["kv_a"] = QMat(fmt, *shapes["kv_a"], gs, q, s_)
     if kvb_fmt == 2:  # kv_b with one scale per row: the first group's scale
         q, s = mats["kv_b"]
         Q["kv_b"] = QMat(2, *shapes["kv_b"], 0, q, np.ascontiguousarray(s[:, 0]))
@@ -211,6 +215,17 @@ def test_mla_prefill_full_dims(orc, S, pb):
     W, layer, x, Lc, Rc, T = _setup(330 + S, S, pb, FULL)
     out, Lc1, Rc1, stage = _run(layer, x, pb, Lc, Rc, T)
     _check(orc, W, x, pb, Lc, Rc, T, out, Lc1, Rc1, stage)
+
+
+@pytest.mark.parametrize("kva", [(4, 128), (2, 0)], ids=["kva-g128", "kva-fmt2"])
+def test_mla_prefill_kva_other_layout(orc, kva):
+    """Prefill with kv_a in another layout than q_a (fmt 4 gs 64): gs 128
+    (q_a and kv_a still share one launch of the split-K GEMM, each with its
+    own group geometry) and per-row fmt 2 (two launches)."""
+    need_gpu()
+    W, layer, x, Lc, Rc, T = _setup(360 + kva[1], 24, 37, FULL, kva=kva)
+    out, Lc1, Rc1, stage = _run(layer, x, 37, Lc, Rc, T)
+    _check(orc, W, x, 37, Lc, Rc, T, out, Lc1, Rc1, stage)
 
 
 @pytest.mark.parametrize("kmode", [0, 1], ids=["mfma", "valu"])
