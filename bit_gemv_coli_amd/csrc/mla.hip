@@ -299,6 +299,9 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
     qabs += (int64_t)r0 * H * L;
     const int h = bx / ncol, c0 = (bx % ncol) * QX_T;
     const int rr = tid >> 4, j4 = 4 * (tid & 15);  // query staging: rows rr + 16 i, key rows j4 .. + 3
+    // the query rows' 4-value runs are 16-byte aligned (16-byte aligned q,
+    // head strides a multiple of 4 values)
+    const bool qvec = (uintptr_t)q % 16 == 0 && (dn + dr) % 4 == 0;
     const int wr = tid >> 2, w8 = 16 * (tid & 3);  // weight staging: key row wr, columns w8 .. + 15
     f32x4 qv[4];
     float wv[16];
@@ -306,13 +309,19 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rr + 16 * i, j = j0 + j4;
-            float e[4] = {0.f, 0.f, 0.f, 0.f};
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (r < Sl) {
                 const float *qr = q + (int64_t)r * nq + (int64_t)h * (dn + dr);
+                if (qvec && j + 4 <= dn) {
+                    v = gload<f32x4>(qr + j);  // one 16-byte load
+                } else {
+                    float e[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) e[k] = j + k < dn ? qr[j + k] : 0.f;
+                    for (int k = 0; k < 4; ++k) e[k] = j + k < dn ? qr[j + k] : 0.f;
+                    v = f32x4{e[0], e[1], e[2], e[3]};
+                }
             }
-            qv[i] = f32x4{e[0], e[1], e[2], e[3]};
+            qv[i] = v;
         }
         const int j = j0 + wr;
         const int64_t row = (int64_t)h * (dn + dv) + min(j, dn - 1);
@@ -844,11 +853,17 @@ __global__ __launch_bounds__(256) void k_mla_clat_mx(const float *__restrict__ p
     // probabilities of rows rr + 16 i at keys t0 + c4 .. + 3 (requested at
     // once at clamped addresses, zero past each row's own position)
     float pz[4][4];
+    const bool pvec = (uintptr_t)p % 16 == 0 && Tcap % 4 == 0 && t0 + c4 + 4 <= Tcap;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t prow = ((int64_t)(r0 + min(rr + 16 * i, Sl - 1)) * H + h) * Tcap;
+        if (pvec) {  // one 16-byte load
+            const f32x4 v = gload<f32x4>(p + prow + t0 + c4);
+            pz[i][0] = v.x; pz[i][1] = v.y; pz[i][2] = v.z; pz[i][3] = v.w;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pz[i][k] = p[prow + min(t0 + c4 + k, Tcap - 1)];
+            for (int k = 0; k < 4; ++k) pz[i][k] = p[prow + min(t0 + c4 + k, Tcap - 1)];
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
