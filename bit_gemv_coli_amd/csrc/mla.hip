@@ -533,6 +533,8 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
     const int C = L + dr;
     const int nch_all = (C + SC_CH - 1) / SC_CH;
     const int per = (nch_all + MLA_SC_SPLIT - 1) / MLA_SC_SPLIT;
+    // rotary runs of 4 on 16-byte boundaries (L is a multiple of 32)
+    const bool rvec = lvec && dr % 4 == 0 && (uintptr_t)qpe % 16 == 0 && (uintptr_t)Rc % 16 == 0;
     // (a split with no chunks, when L + d_rope is short, stores zero partials)
     const int ch0 = split * per, ch1 = min(nch_all, ch0 + per);
     // staging: thread t takes 4 consecutive components (4 (t % 16)) of rows /
@@ -547,6 +549,8 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
             if (r < Sl) {
                 if (c + 4 <= L) {
                     q = gload<f32x4>(qabs + ((int64_t)(r0 + r) * H + h) * L + c);
+                } else if (rvec && c >= L && c + 4 <= C) {  // rotary part, 16-byte aligned
+                    q = gload<f32x4>(qpe + ((int64_t)(r0 + r) * H + h) * dr + (c - L));
                 } else {
                     float e[4];
 #pragma unroll
@@ -570,6 +574,8 @@ __global__ __launch_bounds__(256) void k_mla_scores_mx(const float *__restrict__
             if (t <= last_max) {
                 if (c + 4 <= L && lvec) {
                     k4 = gload<f32x4>(Lc + (int64_t)t * L + c);
+                } else if (rvec && c >= L && c + 4 <= C) {  // rotary key, 16-byte aligned
+                    k4 = gload<f32x4>(Rc + (int64_t)t * dr + (c - L));
                 } else {
                     float e[4];
 #pragma unroll
