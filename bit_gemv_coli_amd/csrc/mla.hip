@@ -325,18 +325,29 @@ __global__ __launch_bounds__(256) void k_mla_qabs_mx(MlaKvb kb, int S, int H, in
         }
         const int j = j0 + wr;
         const int64_t row = (int64_t)h * (dn + dv) + min(j, dn - 1);
+        const int c = c0 + w8;  // 16 columns (a multiple of 16, so c < L covers all 16)
+        uint32_t w2[2] = {0x88888888u, 0x88888888u};
+        float sc2[2] = {0.f, 0.f};
+        if (j < dn && c < L) {
+            // both code words in one 8-byte load; one scale when the 16
+            // columns share a group
+            const u32x2 v = gload<u32x2>(kb.q + row * kb.rb + c / 2);
+            w2[0] = v.x;
+            w2[1] = v.y;
+            if (!GRP) {
+                sc2[0] = sc2[1] = gload<float>(kb.s + row);
+            } else if (kb.gs % 16 == 0) {
+                sc2[0] = sc2[1] = gload<float>(kb.s + row * kb.ng + c / kb.gs);
+            } else {
+                sc2[0] = gload<float>(kb.s + row * kb.ng + c / kb.gs);
+                sc2[1] = gload<float>(kb.s + row * kb.ng + (c + 8) / kb.gs);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int c = c0 + w8 + 8 * u;  // 8 columns, one code word
-            uint32_t w = 0x88888888u;
-            float sc = 0.f;
-            if (j < dn && c < L) {
-                w = gload<uint32_t>(kb.q + row * kb.rb + c / 2);
-                sc = GRP ? gload<float>(kb.s + row * kb.ng + c / kb.gs) : gload<float>(kb.s + row);
-            }
             float f[8];
-            decode_nib_word(w, f);  // 16 (nibble - 8)
-            const float k16 = sc * 0.0625f;
+            decode_nib_word(w2[u], f);  // 16 (nibble - 8)
+            const float k16 = sc2[u] * 0.0625f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) wv[8 * u + k] = f[k] * k16;
         }
